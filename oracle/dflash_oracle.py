@@ -1,0 +1,349 @@
+"""CPU oracle for the DFlash KV-injection block drafter.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import or run this module; the library's
+product path never does, and it shares no code with the HIP kernels.
+
+Plain numpy in float64, written from the pages' definition of the method:
+
+  * Eq 2 (page "@mlx-bun/inference 0.0.0-stage -> 1.0.0", dflash.ts header and
+    #buildContext): H_ctx = RMSNorm(W_c [H^l1; ...; H^lm]) over every context
+    row, the m tapped target hidden states concatenated on the feature axis.
+  * Eq 3 (same page, #layer and projectContextRows): every draft layer i
+    normalises BOTH the block and the context with its own attn_norm, forms
+    Q = W_Q n_block, K = [W_K n_ctx ; W_K n_block], V likewise, and runs
+    attention of the block rows over [context ++ block] with no mask (the
+    block is bidirectional; is_causal is false, page "A Refusal Is Not A
+    Failure", section "What the port taught, besides that"). The context is
+    read-only memory re-projected by each layer; it is never updated.
+  * #buildBlock: row 0 of the block is the anchor's embedding (borrowed from
+    the target) through tok_proj plus block_pos[0]; rows k >= 1 are
+    mask_emb[k-1] + block_pos[k].
+  * #layer FFN: H += (act(n2 W_gate) * (n2 W_up)) W_down with n2 = RMSNorm(H;
+    ff_norm); the residual adds follow the attention output projection and
+    the FFN.
+  * #backbone / #baseLogits: Y = RMSNorm(H; out_norm) W_out, cast to the
+    embedding dtype, scored by the borrowed target LM head; forwardRows takes
+    the greedy argmax of each row (row k proposes the (k+1)-th token after
+    the anchor).
+  * Greedy verification (page "Inco Hacks Native: DFlash 2 Speculation",
+    section 3, log lines "accepted=7 committed=8" and "accepted=5
+    committed=6" for block 8): accepted = longest prefix of drafts equal to
+    the target's argmax, committed = accepted + 1.
+
+Readings where the pages are silent (each listed in the design notes):
+  RMSNorm is x * (mean(x^2) + eps)^-1/2 * g with eps = 1e-6; attention scale
+  is hd^-1/2 with no positional rotation; query head h reads kv head
+  h // (hq / hkv); argmax ties resolve to the lowest index; the FFN
+  activation is the tanh-form GELU or SiLU per the workload; the rows
+  appended to the context each round are the `committed` verified rows.
+
+Modes:
+  pure      float64 throughout (the fp32 workloads are compared to this).
+  faithful  float64, but rounded to bfloat16 (nearest-even) at the points
+            the GPU contract rounds: every input of a weight product (the
+            normalised block, context and FFN inputs, the attention output,
+            the FFN product, the out-norm output), the Q/K/V projections, the
+            context K/V cache and the out-projection result Y.
+
+Weights are in the synthetic generator's storage formats: float32 arrays,
+uint16 bfloat16 bit patterns, or 4-bit groups dict(codes, scales, biases)
+with w = scale * q + bias, groups of 64 along the reduction axis, 8 codes
+per uint32 low nibble first. Matrices are [out, in]; a product is x @ W.T.
+"""
+
+import math
+
+import numpy as np
+
+GROUP = 64
+
+
+# ----------------------------------------------------------------------------
+# number formats
+
+
+def bf16(x):
+    """Round float64 values to bfloat16 precision (8 significant bits),
+    nearest with ties to even, returned as float64."""
+    x = np.asarray(x, dtype=np.float64)
+    mant, expo = np.frexp(x)                      # x = mant * 2^expo, 0.5 <= |mant| < 1
+    return np.ldexp(np.rint(mant * 256.0), expo - 8)
+
+
+def decode_bf16(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def dequant_int4(w, rows=None):
+    """4-bit groups -> float64 [N, K] (optionally only the given rows)."""
+    codes, scales, biases = w["codes"], w["scales"], w["biases"]
+    if rows is not None:
+        codes, scales, biases = codes[rows], scales[rows], biases[rows]
+    N, K8 = codes.shape
+    q = np.empty((N, K8, 8), dtype=np.float64)
+    for j in range(8):
+        q[:, :, j] = (codes >> np.uint32(4 * j)) & np.uint32(15)
+    q = q.reshape(N, K8 * 8)
+    s = np.repeat(decode_bf16(scales), GROUP, axis=1)
+    b = np.repeat(decode_bf16(biases), GROUP, axis=1)
+    return s * q + b
+
+
+def dense(w, rows=None):
+    """Any stored weight -> float64 array."""
+    if isinstance(w, dict):
+        return dequant_int4(w, rows)
+    w = np.asarray(w)
+    if rows is not None:
+        w = w[rows]
+    if w.dtype == np.uint16:
+        return decode_bf16(w)
+    return w.astype(np.float64)
+
+
+def n_rows(w):
+    return w["codes"].shape[0] if isinstance(w, dict) else np.asarray(w).shape[0]
+
+
+# ----------------------------------------------------------------------------
+# elementwise pieces
+
+
+def rmsnorm(x, g, eps):
+    """y = x / sqrt(mean(x^2) + eps) * g over the last axis (page 3, the
+    rmsNorm calls in #buildContext, #layer and #backbone)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def gelu_tanh(x):
+    """Tanh-form GELU, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+ACTS = {"gelu_tanh": gelu_tanh, "silu": silu}
+
+
+def _r(x, faithful):
+    return bf16(x) if faithful else x
+
+
+def softmax_rows(s):
+    s = s - s.max(axis=-1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# ----------------------------------------------------------------------------
+# Eq 2: context projection
+
+
+def context_project(taps, W_c, g_ctx, eps):
+    """taps: m arrays [n, H] -> H_ctx [n, d] (page 3, #buildContext, Eq 2)."""
+    X = np.concatenate([dense(t) for t in taps], axis=1)
+    P = X @ dense(W_c).T
+    return rmsnorm(P, dense(g_ctx), eps)
+
+
+# ----------------------------------------------------------------------------
+# Eq 3, context half: per-layer K/V of the context
+
+
+def context_kv(H_ctx, g_attn, W_k, W_v, hkv, hd, eps, faithful):
+    """One layer's context keys/values [n, hkv, hd] (page 3,
+    projectContextRows: the layer's own attn_norm, then its own W_K, W_V)."""
+    n = _r(rmsnorm(H_ctx, dense(g_attn), eps), faithful)
+    K = _r(n @ dense(W_k).T, faithful)
+    V = _r(n @ dense(W_v).T, faithful)
+    rows = H_ctx.shape[0]
+    return K.reshape(rows, hkv, hd), V.reshape(rows, hkv, hd)
+
+
+class Context:
+    """Retained per-layer context K/V of B sequences (page 3: the context
+    projection is independent of the block and is retained across rounds)."""
+
+    def __init__(self, nl, B, hkv, hd):
+        self.k = [[np.zeros((0, hkv, hd)) for _ in range(B)] for _ in range(nl)]
+        self.v = [[np.zeros((0, hkv, hd)) for _ in range(B)] for _ in range(nl)]
+
+    def length(self, b):
+        return self.k[0][b].shape[0]
+
+    def append(self, layer, b, K, V):
+        self.k[layer][b] = np.concatenate([self.k[layer][b], K], axis=0)
+        self.v[layer][b] = np.concatenate([self.v[layer][b], V], axis=0)
+
+    def truncate(self, b, length):
+        for i in range(len(self.k)):
+            self.k[i][b] = self.k[i][b][:length]
+            self.v[i][b] = self.v[i][b][:length]
+
+
+def append_context(ctx, weights, dims, H_ctx, seq_rows, counts, faithful):
+    """Append rows of H_ctx to the retained context. seq_rows[b] is the list
+    of H_ctx row indices proposed for sequence b; only the first counts[b]
+    of them are appended (the verified ones)."""
+    for i in range(dims.nl):
+        for b, rows in enumerate(seq_rows):
+            take = list(rows)[: int(counts[b])]
+            if not take:
+                continue
+            K, V = context_kv(H_ctx[take], weights[f"bb.{i}.attn_norm"], weights[f"bb.{i}.k"],
+                              weights[f"bb.{i}.v"], dims.hkv, dims.hd, dims.eps, faithful)
+            ctx.append(i, b, K, V)
+
+
+# ----------------------------------------------------------------------------
+# the block
+
+
+def block_init(anchor_ids, E_in, W_tok, mask_emb, block_pos, gamma, faithful):
+    """H_d [B, gamma, d] (page 3, #buildBlock; the embedding is the target's)."""
+    e = _r(dense(E_in, rows=np.asarray(anchor_ids, dtype=np.int64)), faithful)   # [B, H]
+    P = dense(block_pos)
+    B = e.shape[0]
+    H = np.empty((B, gamma, P.shape[1]))
+    H[:, 0] = e @ dense(W_tok).T + P[0]
+    if gamma > 1:
+        H[:, 1:] = dense(mask_emb) + P[1:]
+    return H
+
+
+def attention(Q, K, V, scale):
+    """Non-causal attention. Q [R, hq, hd]; K, V [Lk, hkv, hd] -> [R, hq, hd].
+    Query head h reads key/value head h // (hq // hkv)."""
+    R, hq, hd = Q.shape
+    hkv = K.shape[1]
+    group = hq // hkv
+    O = np.empty_like(Q)
+    for h in range(hq):
+        g = h // group
+        S = scale * (Q[:, h] @ K[:, g].T)
+        O[:, h] = softmax_rows(S) @ V[:, g]
+    return O
+
+
+def draft_layer(H_d, ctx, layer, weights, dims, faithful, attn=attention):
+    """One KV-injection layer over all sequences (page 3, #layer, Eq 3).
+    H_d [B, gamma, d] -> new H_d. ctx.k[layer][b] is read, never written."""
+    B, G, d = H_d.shape
+    hq, hkv, hd = dims.hq, dims.hkv, dims.hd
+    w = lambda n: weights[f"bb.{layer}.{n}"]
+    Wq, Wk, Wv, Wo = dense(w("q")), dense(w("k")), dense(w("v")), dense(w("o"))
+    Wg, Wu, Wd = dense(w("gate")), dense(w("up")), dense(w("down"))
+    g_attn, g_ffn = dense(w("attn_norm")), dense(w("ff_norm"))
+    act = ACTS[dims.act]
+    out = np.empty_like(H_d)
+    for b in range(B):
+        x = H_d[b]
+        n = _r(rmsnorm(x, g_attn, dims.eps), faithful)
+        Q = _r(n @ Wq.T, faithful).reshape(G, hq, hd)
+        Kb = _r(n @ Wk.T, faithful).reshape(G, hkv, hd)
+        Vb = _r(n @ Wv.T, faithful).reshape(G, hkv, hd)
+        K = np.concatenate([ctx.k[layer][b], Kb], axis=0)
+        V = np.concatenate([ctx.v[layer][b], Vb], axis=0)
+        O = _r(attn(Q, K, V, hd ** -0.5).reshape(G, hq * hd), faithful)
+        x = x + O @ Wo.T
+        n2 = _r(rmsnorm(x, g_ffn, dims.eps), faithful)
+        A = _r(act(n2 @ Wg.T) * (n2 @ Wu.T), faithful)
+        out[b] = x + A @ Wd.T
+    return out
+
+
+def out_project(H_d, g_out, W_out, eps, faithful):
+    """Y = RMSNorm(H_d; out_norm) W_out, cast to the embedding dtype
+    (page 3, #backbone then #baseLogits)."""
+    y = _r(rmsnorm(H_d, dense(g_out), eps), faithful)
+    return _r(y @ dense(W_out).T, faithful)
+
+
+# ----------------------------------------------------------------------------
+# LM head and argmax
+
+
+def lm_head_argmax(Y, E_out, chunk=16384, want_logits=False):
+    """Greedy ids of Y [M, H] under the borrowed head E_out [V, H]:
+    argmax_v Y . E_out[v], lowest index among equal maxima.
+    Returns (ids [M], max logit [M], logits [M, V] or None)."""
+    Y = np.asarray(Y, dtype=np.float64)
+    M = Y.shape[0]
+    V = n_rows(E_out)
+    best = np.full(M, -np.inf)
+    arg = np.zeros(M, dtype=np.int64)
+    logits = np.empty((M, V)) if want_logits else None
+    for v0 in range(0, V, chunk):
+        rows = np.arange(v0, min(V, v0 + chunk))
+        s = Y @ dense(E_out, rows=rows).T
+        if want_logits:
+            logits[:, rows] = s
+        j = np.argmax(s, axis=1)              # first (lowest) index of the chunk's maximum
+        val = s[np.arange(M), j]
+        better = val > best                   # strictly greater: an earlier chunk keeps ties
+        best = np.where(better, val, best)
+        arg = np.where(better, v0 + j, arg)
+    return arg.astype(np.int32), best, logits
+
+
+def argmax_lowest(x):
+    """Row argmax with ties to the lowest index."""
+    return np.argmax(np.asarray(x), axis=-1).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# greedy verification
+
+
+def verify_greedy(target_logits, draft_ids):
+    """target_logits [B, gamma+1, V], draft_ids [B, gamma] ->
+    accepted [B], committed [B], ids [B, gamma+1] (-1 padded), next anchor [B].
+
+    t[b, j] is the target's greedy token at verify row j; draft k is checked
+    against row k; accepted is the longest agreeing prefix; the committed
+    tokens are t[b, 0..accepted] (the verified drafts plus the target's own
+    next token), so committed = accepted + 1, and t[b, accepted] is the next
+    anchor."""
+    t = argmax_lowest(target_logits)
+    B, G = draft_ids.shape
+    accepted = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        a = 0
+        while a < G and int(draft_ids[b, a]) == int(t[b, a]):
+            a += 1
+        accepted[b] = a
+    committed = accepted + 1
+    ids = np.full((B, G + 1), -1, dtype=np.int32)
+    for b in range(B):
+        ids[b, : committed[b]] = t[b, : committed[b]]
+    nxt = t[np.arange(B), accepted].astype(np.int32)
+    return accepted, committed.astype(np.int32), ids, nxt
+
+
+# ----------------------------------------------------------------------------
+# composition
+
+
+def draft_forward(weights, dims, ctx, anchor_ids, faithful, return_all=False):
+    """Block init, every layer, out projection, LM head argmax (page 3,
+    forwardRows with the retained context). Returns draft ids [B, gamma]
+    (and the intermediates when return_all)."""
+    H = block_init(anchor_ids, weights["E_in"], weights["tok_proj"], weights["mask_emb"],
+                   weights["block_pos"], dims.gamma, faithful)
+    layers = [H]
+    for i in range(dims.nl):
+        H = draft_layer(H, ctx, i, weights, dims, faithful)
+        layers.append(H)
+    Y = out_project(H, weights["out_norm"], weights["out_proj"], dims.eps, faithful)
+    B, G = H.shape[0], dims.gamma
+    ids, best, logits = lm_head_argmax(Y.reshape(B * G, -1), weights["E_out"], want_logits=return_all)
+    ids = ids.reshape(B, G)
+    if return_all:
+        return ids, {"H": layers, "Y": Y, "logits": logits, "max_logit": best.reshape(B, G)}
+    return ids
