@@ -1,0 +1,27 @@
+// Split-K non-causal block attention (see attention.hip).
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace dfl {
+
+struct AttnParams {
+    const float* qkv;      // [B*gamma][qkv_ld]: Q cols [0, hq hd), K_b cols, then V_b cols
+    int64_t qkv_ld;
+    const void* kcache;    // this layer's cache [B][hkv][cap][hd]
+    const void* vcache;
+    const int32_t* len;    // [B] context rows per sequence
+    int B, hq, hkv, hd, gamma, cap, nsplit, kv_f32;
+    float scale;
+    float* part;           // [B][hq][nsplit][gamma][hd+2]  (o, running max, running sum)
+    float* out;            // O [B*gamma][out_ld], head h at columns h*hd
+    int64_t out_ld;
+    int round_out;
+};
+
+hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+int attention_max_rows();
+
+}  // namespace dfl

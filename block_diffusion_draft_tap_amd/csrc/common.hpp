@@ -1,0 +1,116 @@
+// Device helpers shared by the drafter kernels: bf16 bit conversions, bf16
+// dot products, 64-lane wavefront reductions and the FFN activations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfl {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // 4 wavefronts per workgroup
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (inputs are finite)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// c + a.lo*b.lo + a.hi*b.hi on packed bf16 pairs, fp32 accumulate
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Larger value wins; equal values keep the lower index.
+__device__ __forceinline__ void argmax_pick(float& v, int& i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float v2 = __shfl_xor(v, o, kWave);
+        int i2 = __shfl_xor(i, o, kWave);
+        argmax_pick(v, i, v2, i2);
+    }
+}
+
+// Sum NV per-lane values across the wavefront by recursive halving: at each
+// step a lane keeps one half of its values and adds the partner's copy of that
+// half, so the work shrinks with the value count. On return lanes 2v and 2v+1
+// hold the full sum of value v (NV = 32), lanes 4v..4v+3 for NV = 16, and so
+// on; for NV > 32 every lane holds value (lane >> (6 - log2 NV)).
+template <int NV>
+__device__ __forceinline__ float wave_sum_many(float (&v)[NV], int lane) {
+    static_assert((NV & (NV - 1)) == 0 && NV >= 1 && NV <= 64, "power of two");
+    int c = NV;
+    int off = 32;
+#pragma unroll
+    for (int step = 0; step < 6; ++step) {
+        if (c > 1) {
+            const bool up = (lane & off) != 0;
+            const int h = c >> 1;
+#pragma unroll
+            for (int i = 0; i < NV / 2; ++i) {
+                if (i < h) {
+                    float lo = v[i], hi = v[i + h];
+                    float send = up ? lo : hi;
+                    float keep = up ? hi : lo;
+                    v[i] = keep + __shfl_xor(send, off, kWave);
+                }
+            }
+            c = h;
+        } else {
+            v[0] += __shfl_xor(v[0], off, kWave);
+        }
+        off >>= 1;
+    }
+    return v[0];
+}
+// Which value index lane `lane` holds after wave_sum_many<NV>.
+template <int NV>
+__device__ __forceinline__ int wave_sum_many_index(int lane) {
+    int idx = 0, off = 32, c = NV;
+#pragma unroll
+    for (int step = 0; step < 6; ++step) {
+        if (c > 1) {
+            c >>= 1;
+            if (lane & off) idx += c;
+        }
+        off >>= 1;
+    }
+    return idx;
+}
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * x * (1.0f + tanhf(k0 * (x + 0.044715f * x * x * x)));
+}
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+__device__ __forceinline__ float load_gain(const void* g, bool f32, int i) {
+    return f32 ? static_cast<const float*>(g)[i] : bf16_bits_to_f32(static_cast<const uint16_t*>(g)[i]);
+}
+
+}  // namespace dfl

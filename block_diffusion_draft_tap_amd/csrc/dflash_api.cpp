@@ -1,0 +1,556 @@
+// C ABI of libdflash.so (declared in include/dflash.h): argument validation on
+// the host, workspace layout, and the kernel sequence of each call.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/dflash.h"
+#include "attention.hpp"
+#include "gemv.hpp"
+#include "head.hpp"
+
+using namespace dfl;
+
+namespace {
+
+std::atomic<uint64_t> g_invocations{0};
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool kill_switch() {
+    const char* e = std::getenv("DFLASH_DISABLE");
+    return e && e[0] && std::strcmp(e, "0") != 0;
+}
+
+// gfx950 present on the current device (checked per call; the properties
+// query is cached per device id)
+bool device_supported() {
+    static std::mutex mu;
+    static int cached[64];
+    static bool init = false;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!init) {
+        for (int& c : cached) c = -1;
+        init = true;
+    }
+    if (cached[dev] < 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+        cached[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    }
+    return cached[dev] == 1;
+}
+
+int gate() { return (kill_switch() || !device_supported()) ? DFLASH_DECLINED : DFLASH_OK; }
+
+int check_dims(const dflash_dims* d) {
+    if (!d) return DFLASH_EINVAL;
+    if (d->H <= 0 || d->m <= 0 || d->d <= 0 || d->nl < 0 || d->hq <= 0 || d->hkv <= 0 || d->hd <= 0 || d->F <= 0 ||
+        d->V <= 0 || d->gamma <= 0)
+        return DFLASH_EINVAL;
+    if (d->d != d->hq * d->hd || d->hq % d->hkv != 0) return DFLASH_EINVAL;
+    if (!(d->eps >= 0.0f) || d->eps > 1.0f) return DFLASH_EINVAL;
+    if (d->hd != 64 && d->hd != 128) return DFLASH_DECLINED;
+    if (d->wdtype != DFLASH_F32 && d->wdtype != DFLASH_BF16 && d->wdtype != DFLASH_INT4G64) return DFLASH_DECLINED;
+    if (d->act != DFLASH_ACT_GELU_TANH && d->act != DFLASH_ACT_SILU) return DFLASH_DECLINED;
+    if (d->nl > kMaxLayers || d->m > kMaxTaps) return DFLASH_DECLINED;
+    if (d->gamma + 1 > 64) return DFLASH_DECLINED;
+    if ((d->hq / d->hkv) * d->gamma > attention_max_rows()) return DFLASH_DECLINED;
+    const int q = d->wdtype == DFLASH_INT4G64 ? 64 : 8;
+    if (d->H % q || d->d % q || d->F % q) return DFLASH_DECLINED;
+    return DFLASH_OK;
+}
+
+int wtype_of(int dtype) { return dtype == DFLASH_F32 ? W_F32 : (dtype == DFLASH_BF16 ? W_BF16 : W_I4); }
+
+int check_weight(const dflash_weight& w, int rows, int cols, int want_dtype /* -1: any */) {
+    if (!w.data) return DFLASH_EINVAL;
+    if (w.dtype != DFLASH_F32 && w.dtype != DFLASH_BF16 && w.dtype != DFLASH_INT4G64) return DFLASH_EINVAL;
+    if (want_dtype >= 0 && w.dtype != want_dtype) return DFLASH_EINVAL;
+    if (w.rows != rows || w.cols != cols) return DFLASH_EINVAL;
+    if (w.dtype == DFLASH_INT4G64) {
+        if (!w.scales || !w.biases) return DFLASH_EINVAL;
+        if (cols % 64) return DFLASH_DECLINED;
+    } else if (cols % 8) {
+        return DFLASH_DECLINED;
+    }
+    return DFLASH_OK;
+}
+
+#define DFL_TRY(expr)                     \
+    do {                                  \
+        const int rc_ = (expr);           \
+        if (rc_ != DFLASH_OK) return rc_; \
+    } while (0)
+#define DFL_HIP(expr)                                    \
+    do {                                                 \
+        if ((expr) != hipSuccess) return DFLASH_EHIP;    \
+    } while (0)
+
+int check_model(const dflash_model* M) {
+    if (!M) return DFLASH_EINVAL;
+    DFL_TRY(check_dims(&M->dims));
+    const dflash_dims& d = M->dims;
+    const int wd = d.wdtype;
+    if (!M->ctx_norm || !M->block_pos || !M->out_norm || (d.gamma > 1 && !M->mask_emb)) return DFLASH_EINVAL;
+    if (d.nl > 0 && !M->layers) return DFLASH_EINVAL;
+    DFL_TRY(check_weight(M->w_c, d.d, d.m * d.H, wd));
+    DFL_TRY(check_weight(M->tok_proj, d.d, d.H, wd));
+    DFL_TRY(check_weight(M->out_proj, d.H, d.d, wd));
+    DFL_TRY(check_weight(M->embed_in, d.V, d.H, -1));
+    DFL_TRY(check_weight(M->lm_head, d.V, d.H, -1));
+    for (int i = 0; i < d.nl; ++i) {
+        const dflash_layer& L = M->layers[i];
+        if (!L.attn_norm || !L.ffn_norm) return DFLASH_EINVAL;
+        DFL_TRY(check_weight(L.w_qkv, (d.hq + 2 * d.hkv) * d.hd, d.d, wd));
+        DFL_TRY(check_weight(L.w_o, d.d, d.hq * d.hd, wd));
+        DFL_TRY(check_weight(L.w_gate_up, 2 * d.F, d.d, wd));
+        DFL_TRY(check_weight(L.w_down, d.d, d.F, wd));
+    }
+    return DFLASH_OK;
+}
+
+int check_kv(const dflash_kv* kv, const dflash_dims& d, int B) {
+    if (!kv || !kv->k || !kv->v || !kv->len) return DFLASH_EINVAL;
+    if (kv->B < B || B <= 0 || kv->cap <= 0) return DFLASH_EINVAL;
+    const int want = d.wdtype == DFLASH_F32 ? DFLASH_F32 : DFLASH_BF16;
+    if (kv->dtype != want) return DFLASH_EINVAL;
+    return DFLASH_OK;
+}
+
+WeightPtr wptr(const dflash_weight& w) {
+    WeightPtr p;
+    p.data = w.data;
+    p.scales = static_cast<const uint16_t*>(w.scales);
+    p.biases = static_cast<const uint16_t*>(w.biases);
+    return p;
+}
+
+int nsplit_for(int cap, int gamma) {
+    const int T = cap + gamma;
+    int ns = (T + 63) / 64;
+    return ns < 1 ? 1 : (ns > 64 ? 64 : ns);
+}
+
+int rpw_for(int N) { return N >= 16384 ? 4 : (N >= 2048 ? 2 : 1); }
+int lm_nblocks(int V) { return (V + 15) / 16; }  // LM head runs 4 rows per wavefront
+
+struct Ws {
+    float* hd;
+    float* qkv;
+    float* part;
+    float* o;
+    float* a;
+    float* y;
+    float* lmv;
+    int32_t* lmi;
+    size_t total;
+    int nsplit;
+};
+
+Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
+    Ws w{};
+    const size_t rows = (size_t)B * d.gamma;
+    const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
+    w.nsplit = nsplit_for(cap, d.gamma);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    const size_t o_hd = take(rows * d.d * 4);
+    const size_t o_qkv = take(rows * qkv_rows * 4);
+    const size_t o_part = take((size_t)B * d.hq * w.nsplit * d.gamma * (d.hd + 2) * 4);
+    const size_t o_o = take(rows * d.hq * d.hd * 4);
+    const size_t o_a = take(rows * d.F * 4);
+    const size_t o_y = take(rows * d.H * 4);
+    const size_t nb = lm_nblocks(d.V);
+    const size_t o_lmv = take(rows * nb * 4);
+    const size_t o_lmi = take(rows * nb * 4);
+    w.total = off;
+    char* c = static_cast<char*>(base);
+    if (c) {
+        w.hd = reinterpret_cast<float*>(c + o_hd);
+        w.qkv = reinterpret_cast<float*>(c + o_qkv);
+        w.part = reinterpret_cast<float*>(c + o_part);
+        w.o = reinterpret_cast<float*>(c + o_o);
+        w.a = reinterpret_cast<float*>(c + o_a);
+        w.y = reinterpret_cast<float*>(c + o_y);
+        w.lmv = reinterpret_cast<float*>(c + o_lmv);
+        w.lmi = reinterpret_cast<int32_t*>(c + o_lmi);
+    }
+    return w;
+}
+
+// ---------------------------------------------------------------------------
+// GEMV helpers; activation rows are processed in chunks of up to 8 (32 for
+// long row counts of the context projection and append)
+
+GemvParams base_params(const dflash_dims& d) {
+    GemvParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.gain_f32 = d.wdtype == DFLASH_F32 ? 1 : 0;
+    p.eps = d.eps;
+    p.round_out = d.wdtype == DFLASH_F32 ? 0 : 1;
+    return p;
+}
+
+hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStream_t s, int layers = 1,
+                     int maxm_long = 8) {
+    const int maxm = rows > 8 ? maxm_long : 8;
+    for (int r0 = 0; r0 < rows; r0 += maxm) {
+        GemvParams q = p;
+        q.M = rows - r0 < maxm ? rows - r0 : maxm;
+        if (pro == PRO_PLAIN || pro == PRO_NORM) q.x = p.x + (int64_t)r0 * p.x_ld;
+        if (pro == PRO_TAPS) {
+            const size_t esz = p.src_f32 ? 4 : 2;
+            for (int j = 0; j < kMaxTaps; ++j)
+                if (p.taps[j]) q.taps[j] = static_cast<const char*>(p.taps[j]) + (size_t)r0 * p.tap_ld * esz;
+        }
+        if (pro == PRO_GATHER) q.ids = p.ids + r0;
+        if (epi == EPI_STORE || epi == EPI_RESID || epi == EPI_GATED) q.out = p.out + (int64_t)r0 * p.out_ld;
+        if (epi == EPI_KV) q.row_base = p.row_base + r0;
+        if (epi == EPI_BLOCKINIT) q.seq_base = p.seq_base + r0;
+        if (epi == EPI_ARGMAX) {
+            q.part_val = p.part_val + (int64_t)r0 * p.nblocks;
+            q.part_idx = p.part_idx + (int64_t)r0 * p.nblocks;
+        }
+        const hipError_t e = launch_gemv(wtype, pro, epi, maxm, q, layers, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B, const Ws& w, hipStream_t s) {
+    const dflash_dims& d = M->dims;
+    const dflash_layer& L = M->layers[i];
+    const int wt = wtype_of(d.wdtype);
+    const int rows = B * d.gamma;
+    const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
+
+    {  // n = RMSNorm(H; attn_norm); [Q | K_b | V_b] = n W_qkv^T
+        GemvParams p = base_params(d);
+        p.w[0] = wptr(L.w_qkv);
+        p.N = qkv_rows;
+        p.K = d.d;
+        p.rpw = rpw_for(p.N);
+        p.x = h;
+        p.x_ld = d.d;
+        p.gain[0] = L.attn_norm;
+        p.out = w.qkv;
+        p.out_ld = qkv_rows;
+        DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_STORE, p, rows, s));
+    }
+    {  // O = softmax(Q [K_ctx; K_b]^T / sqrt(hd)) [V_ctx; V_b]
+        AttnParams a;
+        std::memset(&a, 0, sizeof(a));
+        a.qkv = w.qkv;
+        a.qkv_ld = qkv_rows;
+        const size_t esz = kv->dtype == DFLASH_F32 ? 4 : 2;
+        const size_t layer_bytes = (size_t)kv->B * d.hkv * kv->cap * d.hd * esz;
+        a.kcache = static_cast<const char*>(kv->k) + (size_t)i * layer_bytes;
+        a.vcache = static_cast<const char*>(kv->v) + (size_t)i * layer_bytes;
+        a.len = kv->len;
+        a.B = B;
+        a.hq = d.hq;
+        a.hkv = d.hkv;
+        a.hd = d.hd;
+        a.gamma = d.gamma;
+        a.cap = kv->cap;
+        a.nsplit = w.nsplit;
+        a.kv_f32 = kv->dtype == DFLASH_F32;
+        a.scale = 1.0f / sqrtf((float)d.hd);
+        a.part = w.part;
+        a.out = w.o;
+        a.out_ld = d.hq * d.hd;
+        a.round_out = d.wdtype == DFLASH_F32 ? 0 : 1;
+        DFL_HIP(launch_attention(a, s));
+    }
+    {  // H += O W_o^T
+        GemvParams p = base_params(d);
+        p.w[0] = wptr(L.w_o);
+        p.N = d.d;
+        p.K = d.hq * d.hd;
+        p.rpw = rpw_for(p.N);
+        p.x = w.o;
+        p.x_ld = d.hq * d.hd;
+        p.out = h;
+        p.out_ld = d.d;
+        DFL_HIP(gemv_rows(wt, PRO_PLAIN, EPI_RESID, p, rows, s));
+    }
+    {  // A = act(n2 W_gate^T) * (n2 W_up^T), n2 = RMSNorm(H; ffn_norm)
+        GemvParams p = base_params(d);
+        p.w[0] = wptr(L.w_gate_up);
+        p.N = 2 * d.F;
+        p.F = d.F;
+        p.K = d.d;
+        p.rpw = d.F >= 8192 ? 4 : 2;
+        p.act = d.act;
+        p.x = h;
+        p.x_ld = d.d;
+        p.gain[0] = L.ffn_norm;
+        p.out = w.a;
+        p.out_ld = d.F;
+        DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_GATED, p, rows, s));
+    }
+    {  // H += A W_down^T
+        GemvParams p = base_params(d);
+        p.w[0] = wptr(L.w_down);
+        p.N = d.d;
+        p.K = d.F;
+        p.rpw = rpw_for(p.N);
+        p.x = w.a;
+        p.x_ld = d.F;
+        p.out = h;
+        p.out_ld = d.d;
+        DFL_HIP(gemv_rows(wt, PRO_PLAIN, EPI_RESID, p, rows, s));
+    }
+    return DFLASH_OK;
+}
+
+int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, int V, int32_t* ids, float* maxl,
+            float* pv, int32_t* pi, hipStream_t s) {
+    GemvParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.w[0] = wptr(E);
+    p.N = V;
+    p.K = H;
+    p.rpw = 4;
+    p.taps[0] = y;
+    p.tap_ld = H;
+    p.H = H;
+    p.src_f32 = y_f32;
+    p.nblocks = lm_nblocks(V);
+    p.part_val = pv;
+    p.part_idx = pi;
+    DFL_HIP(gemv_rows(wtype_of(E.dtype), PRO_TAPS, EPI_ARGMAX, p, rows, s));
+    DFL_HIP(launch_argmax_merge(pv, pi, p.nblocks, rows, ids, maxl, s));
+    return DFLASH_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+
+extern "C" {
+
+size_t dflash_workspace_bytes(const dflash_dims* dims, int32_t B, int32_t cap) {
+    if (check_dims(dims) == DFLASH_EINVAL || B <= 0 || cap < 0) return 0;
+    return ws_layout(*dims, B, cap, nullptr).total;
+}
+
+int dflash_query(const dflash_dims* dims) {
+    DFL_TRY(check_dims(dims));
+    return gate();
+}
+
+const char* dflash_status_string(int status) {
+    switch (status) {
+        case DFLASH_OK: return "ok";
+        case DFLASH_DECLINED: return "declined: request not served by this library (fall back to plain decoding)";
+        case DFLASH_EINVAL: return "invalid argument";
+        case DFLASH_ENOSPC: return "workspace or KV capacity too small";
+        case DFLASH_EHIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+uint64_t dflash_invocations(void) { return g_invocations.load(); }
+
+int dflash_context_project(const dflash_model* M, const void* const* taps, int64_t tap_ld, int32_t n, float* h_ctx,
+                           void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    DFL_TRY(check_model(M));
+    const dflash_dims& d = M->dims;
+    if (n < 0 || !taps || (n > 0 && !h_ctx) || tap_ld < d.H) return DFLASH_EINVAL;
+    for (int j = 0; j < d.m; ++j)
+        if (!taps[j]) return DFLASH_EINVAL;
+    for (int j = 0; j < d.m; ++j)
+        if ((reinterpret_cast<uintptr_t>(taps[j]) & 15) || (tap_ld % 8)) return DFLASH_DECLINED;
+    DFL_TRY(gate());
+    if (n == 0) return DFLASH_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    GemvParams p = base_params(d);
+    p.w[0] = wptr(M->w_c);
+    p.N = d.d;
+    p.K = d.m * d.H;
+    p.rpw = rpw_for(p.N);
+    for (int j = 0; j < d.m; ++j) p.taps[j] = taps[j];
+    p.tap_ld = tap_ld;
+    p.H = d.H;
+    p.src_f32 = d.wdtype == DFLASH_F32;
+    p.out = h_ctx;
+    p.out_ld = d.d;
+    p.round_out = 0;  // P stays fp32; the norm follows
+    DFL_HIP(gemv_rows(wtype_of(d.wdtype), PRO_TAPS, EPI_STORE, p, n, s, 1, 32));
+    DFL_HIP(launch_rownorm(h_ctx, n, d.d, M->ctx_norm, d.wdtype == DFLASH_F32, d.eps, s));
+    g_invocations++;
+    return DFLASH_OK;
+}
+
+int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, const int32_t* row_offsets,
+                         const int32_t* counts, const dflash_kv* kv, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    DFL_TRY(check_model(M));
+    const dflash_dims& d = M->dims;
+    if (n < 0 || (n > 0 && !h_ctx) || !row_offsets || !kv) return DFLASH_EINVAL;
+    DFL_TRY(check_kv(kv, d, kv->B));
+    DFL_TRY(gate());
+    if (n == 0 || d.nl == 0) return DFLASH_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    GemvParams p = base_params(d);
+    for (int i = 0; i < d.nl; ++i) {
+        p.w[i] = wptr(M->layers[i].w_qkv);
+        p.gain[i] = M->layers[i].attn_norm;
+    }
+    p.w_row0 = (int64_t)d.hq * d.hd;  // the K and V rows of the fused QKV matrix
+    p.N = 2 * d.hkv * d.hd;
+    p.K = d.d;
+    p.rpw = rpw_for(p.N);
+    p.x = h_ctx;
+    p.x_ld = d.d;
+    p.kcache = kv->k;
+    p.vcache = kv->v;
+    p.len = kv->len;
+    p.row_offsets = row_offsets;
+    p.counts = counts;
+    p.row_base = 0;
+    p.B = kv->B;
+    p.hkv = d.hkv;
+    p.hd = d.hd;
+    p.cap = kv->cap;
+    p.kv_f32 = kv->dtype == DFLASH_F32;
+    p.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
+    DFL_HIP(gemv_rows(wtype_of(d.wdtype), PRO_NORM, EPI_KV, p, n, s, d.nl, 32));
+    DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
+    g_invocations++;
+    return DFLASH_OK;
+}
+
+int dflash_draft_layer(const dflash_model* M, int32_t layer, float* h_block, const dflash_kv* kv, int32_t B,
+                       void* ws, size_t ws_bytes, void* stream) {
+    DFL_TRY(check_model(M));
+    const dflash_dims& d = M->dims;
+    if (layer < 0 || layer >= d.nl || !h_block || B <= 0) return DFLASH_EINVAL;
+    DFL_TRY(check_kv(kv, d, B));
+    const Ws w = ws_layout(d, B, kv->cap, ws);
+    if (!ws || ws_bytes < w.total) return DFLASH_ENOSPC;
+    DFL_TRY(gate());
+    DFL_TRY(run_layer(M, layer, h_block, kv, B, w, static_cast<hipStream_t>(stream)));
+    g_invocations++;
+    return DFLASH_OK;
+}
+
+int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const dflash_kv* kv, int32_t B,
+                         int32_t* draft_ids, void* y_out, float* max_logit, void* ws, size_t ws_bytes,
+                         void* stream) {
+    DFL_TRY(check_model(M));
+    const dflash_dims& d = M->dims;
+    if (!anchor_ids || !draft_ids || B <= 0) return DFLASH_EINVAL;
+    DFL_TRY(check_kv(kv, d, B));
+    const Ws w = ws_layout(d, B, kv->cap, ws);
+    if (!ws || ws_bytes < w.total) return DFLASH_ENOSPC;
+    DFL_TRY(gate());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int wt = wtype_of(d.wdtype);
+    const int rows = B * d.gamma;
+    {  // block rows: E_in[anchor] tok_proj^T + block_pos[0]; mask_emb[k-1] + block_pos[k]
+        GemvParams p = base_params(d);
+        p.w[0] = wptr(M->tok_proj);
+        p.N = d.d;
+        p.K = d.H;
+        p.rpw = rpw_for(p.N);
+        p.ids = anchor_ids;
+        p.table = wptr(M->embed_in);
+        p.table_type = wtype_of(M->embed_in.dtype);
+        p.table_rows = M->embed_in.rows;
+        p.out = w.hd;
+        p.block_pos = M->block_pos;
+        p.mask_emb = M->mask_emb;
+        p.gamma = d.gamma;
+        p.seq_base = 0;
+        DFL_HIP(gemv_rows(wt, PRO_GATHER, EPI_BLOCKINIT, p, B, s));
+    }
+    for (int i = 0; i < d.nl; ++i) DFL_TRY(run_layer(M, i, w.hd, kv, B, w, s));
+    {  // Y = bf16(bf16(RMSNorm(H; out_norm)) out_proj^T)
+        GemvParams p = base_params(d);
+        p.w[0] = wptr(M->out_proj);
+        p.N = d.H;
+        p.K = d.d;
+        p.rpw = rpw_for(p.N);
+        p.x = w.hd;
+        p.x_ld = d.d;
+        p.gain[0] = M->out_norm;
+        p.out = w.y;
+        p.out_ld = d.H;
+        DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_STORE, p, rows, s));
+    }
+    DFL_TRY(lm_head(M->lm_head, w.y, 1, rows, d.H, d.V, draft_ids, max_logit, w.lmv, w.lmi, s));
+    if (y_out) {
+        if (d.wdtype == DFLASH_F32)
+            DFL_HIP(launch_copy_f32(w.y, static_cast<float*>(y_out), (int64_t)rows * d.H, s));
+        else
+            DFL_HIP(launch_to_bf16(w.y, static_cast<uint16_t*>(y_out), (int64_t)rows * d.H, s));
+    }
+    g_invocations++;
+    return DFLASH_OK;
+}
+
+size_t dflash_lm_head_workspace_bytes(int32_t V, int32_t M) {
+    if (V <= 0 || M <= 0) return 0;
+    return 2 * align_up((size_t)M * lm_nblocks(V) * 4);
+}
+
+int dflash_lm_head_argmax(const dflash_weight* E_out, const void* y, int32_t y_dtype, int32_t M, int32_t* ids,
+                          float* max_logit, void* ws, size_t ws_bytes, void* stream) {
+    if (!E_out || !y || !ids || M <= 0) return DFLASH_EINVAL;
+    if (y_dtype != DFLASH_F32 && y_dtype != DFLASH_BF16) return DFLASH_EINVAL;
+    DFL_TRY(check_weight(*E_out, E_out->rows, E_out->cols, -1));
+    if (E_out->rows <= 0 || E_out->cols <= 0) return DFLASH_EINVAL;
+    if (reinterpret_cast<uintptr_t>(y) & 15) return DFLASH_DECLINED;
+    const size_t need = dflash_lm_head_workspace_bytes(E_out->rows, M);
+    if (!ws || ws_bytes < need) return DFLASH_ENOSPC;
+    DFL_TRY(gate());
+    char* c = static_cast<char*>(ws);
+    float* pv = reinterpret_cast<float*>(c);
+    int32_t* pi = reinterpret_cast<int32_t*>(c + need / 2);
+    DFL_TRY(lm_head(*E_out, y, y_dtype == DFLASH_F32, M, E_out->cols, E_out->rows, ids, max_logit, pv, pi,
+                    static_cast<hipStream_t>(stream)));
+    g_invocations++;
+    return DFLASH_OK;
+}
+
+size_t dflash_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V) {
+    if (B <= 0 || gamma <= 0 || V <= 0) return 0;
+    return 2 * align_up((size_t)B * (gamma + 1) * verify_splits(V) * 4);
+}
+
+int dflash_verify_greedy(const float* target_logits, const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V,
+                         int32_t* accepted, int32_t* committed, int32_t* ids, int32_t* next_anchor, void* ws,
+                         size_t ws_bytes, void* stream) {
+    if (!target_logits || !draft_ids || !accepted || !committed || !ids) return DFLASH_EINVAL;
+    if (B <= 0 || gamma <= 0 || V <= 0) return DFLASH_EINVAL;
+    if (gamma + 1 > 64) return DFLASH_DECLINED;
+    if (reinterpret_cast<uintptr_t>(target_logits) & 15) return DFLASH_DECLINED;
+    const size_t need = dflash_verify_workspace_bytes(B, gamma, V);
+    if (!ws || ws_bytes < need) return DFLASH_ENOSPC;
+    DFL_TRY(gate());
+    char* c = static_cast<char*>(ws);
+    float* pv = reinterpret_cast<float*>(c);
+    int32_t* pi = reinterpret_cast<int32_t*>(c + need / 2);
+    DFL_HIP(launch_verify(target_logits, draft_ids, B, gamma, V, accepted, committed, ids, next_anchor, pv, pi,
+                          static_cast<hipStream_t>(stream)));
+    g_invocations++;
+    return DFLASH_OK;
+}
+
+}  // extern "C"

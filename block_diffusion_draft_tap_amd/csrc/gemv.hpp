@@ -1,0 +1,99 @@
+// Skinny GEMV / small-M GEMM for the drafter's projections:
+//   y[m, n] = sum_k x[m, k] * W[n, k]       (W row-major [N, K], K contiguous)
+// for M <= MAXM activation rows. Each workgroup (4 wavefronts) owns a tile of
+// 4*RPW weight rows and streams them over the whole K range once; every lane
+// reads 16-byte weight chunks, the activations are staged once per workgroup
+// in LDS (in K chunks) in the type the product uses (bf16 for bf16/int4
+// weights, fp32 for fp32 weights), and partial sums are reduced across the
+// wavefront at the end.
+//
+// Prologues build the activation rows while staging them:
+//   PRO_PLAIN   x rows from an fp32 buffer
+//   PRO_NORM    RMSNorm of fp32 rows with a gain: x * (mean x^2 + eps)^-1/2 * g
+//   PRO_TAPS    concatenation of m tap buffers [rows, H] (Eq 2 input)
+//   PRO_GATHER  rows of an embedding table selected by token ids
+// Epilogues consume the reduced sums:
+//   EPI_STORE      out[m, n] = y (optionally rounded to bf16)
+//   EPI_RESID      out[m, n] += y                     (residual stream)
+//   EPI_GATED      out[m, j] = act(y_gate[j]) * y_up[j]  (rows j and F+j)
+//   EPI_KV         K/V rows written to the retained context cache
+//   EPI_BLOCKINIT  block rows: anchor row + block_pos[0], mask rows
+//   EPI_ARGMAX     per-workgroup (max, lowest index) of each row's outputs
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace dfl {
+
+enum WType { W_F32 = 0, W_BF16 = 1, W_I4 = 2 };
+enum { PRO_PLAIN = 0, PRO_NORM = 1, PRO_TAPS = 2, PRO_GATHER = 3 };
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_GATED = 2, EPI_KV = 3, EPI_BLOCKINIT = 4, EPI_ARGMAX = 5 };
+
+constexpr int kMaxTaps = 8;
+constexpr int kMaxLayers = 16;
+
+struct WeightPtr {
+    const void* data = nullptr;
+    const uint16_t* scales = nullptr;
+    const uint16_t* biases = nullptr;
+};
+
+struct GemvParams {
+    // weights: per-layer pointers (grid.y selects the layer; entry 0 otherwise)
+    WeightPtr w[kMaxLayers];
+    int64_t w_row0;      // first weight row used (row offset into the matrix)
+    int N;               // weight rows processed (outputs; for EPI_GATED 2F)
+    int K;               // reduction length
+    int M;               // active activation rows (<= MAXM)
+    int rpw;             // weight rows per wavefront (1, 2 or 4; even for EPI_GATED)
+
+    // prologue
+    const float* x;      // PRO_PLAIN / PRO_NORM: fp32 rows
+    int64_t x_ld;
+    const void* gain[kMaxLayers];  // PRO_NORM: per-layer gain vectors [K]
+    int gain_f32;
+    float eps;
+    const void* taps[kMaxTaps];    // PRO_TAPS: tap j covers k in [j*H, (j+1)*H)
+    int64_t tap_ld;
+    int H;
+    int src_f32;         // PRO_TAPS / PRO_GATHER source element type (1 = fp32, 0 = bf16)
+    const int32_t* ids;  // PRO_GATHER: table rows
+    WeightPtr table;     // PRO_GATHER: embedding table [table_rows, K]
+    int table_rows;      // ids are clamped to [0, table_rows)
+    int table_type;      // WType of the table
+
+    // epilogue
+    float* out;
+    int64_t out_ld;
+    int round_out;       // EPI_STORE / EPI_GATED: round results to bf16
+    int F;               // EPI_GATED: gate rows [0, F), up rows [F, 2F)
+    int act;             // EPI_GATED: 0 gelu_tanh, 1 silu
+    // EPI_KV
+    void* kcache;        // [nl][B][hkv][cap][hd]
+    void* vcache;
+    const int32_t* len;
+    const int32_t* row_offsets;  // [B+1]
+    const int32_t* counts;       // [B] or null
+    int row_base;        // global index of activation row 0 of this launch
+    int B, hkv, hd, cap, kv_f32;
+    int64_t layer_stride;  // elements per layer in the cache
+    // EPI_BLOCKINIT
+    const void* block_pos;  // [gamma, d]
+    const void* mask_emb;   // [gamma-1, d]
+    int gamma;
+    int64_t seq_base;       // sequence index of activation row 0
+    // EPI_ARGMAX
+    float* part_val;     // [M][nblocks]
+    int32_t* part_idx;
+    int nblocks;
+};
+
+// Host-side launcher: picks MAXM, the weight type and the modes.
+hipError_t launch_gemv(int wtype, int pro, int epi, int maxm, const GemvParams& p, int layers, hipStream_t s);
+
+// LDS budget for staged activations per workgroup
+constexpr int kStageBytes = 64 * 1024;
+
+}  // namespace dfl

@@ -1,0 +1,175 @@
+// Small kernels of the drafter round:
+//   argmax_merge_kernel   per-workgroup (max, index) partials -> greedy ids
+//   verify_partial_kernel per (verify row, vocab slice) argmax of target logits
+//   verify_final_kernel   prefix compare: accepted, committed, ids, next anchor
+//   rownorm_kernel        in-place RMSNorm of fp32 rows with a gain (Eq 2)
+//   advance_len_kernel    len[b] += appended rows (retained context grows)
+//   f32_to_bf16_kernel    fp32 -> bf16 copy for optional outputs
+// Every reduction runs in a fixed order and resolves equal maxima to the
+// lowest index, so results are deterministic run to run.
+#include "common.hpp"
+#include "head.hpp"
+
+namespace dfl {
+
+__device__ __forceinline__ void block_argmax(float& v, int& i, float* sv, int* si) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    wave_argmax(v, i);
+    if (lane == 0) { sv[wave] = v; si[wave] = i; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int nw = (blockDim.x + 63) / 64;
+        for (int w = 1; w < nw; ++w) argmax_pick(v, i, sv[w], si[w]);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void argmax_merge_kernel(const float* part_val, const int32_t* part_idx,
+                                                              int nblocks, int32_t* ids, float* max_logit) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int m = blockIdx.x;
+    float v = -INFINITY;
+    int i = 0x7fffffff;
+    for (int j = threadIdx.x; j < nblocks; j += blockDim.x)
+        argmax_pick(v, i, part_val[(int64_t)m * nblocks + j], part_idx[(int64_t)m * nblocks + j]);
+    block_argmax(v, i, sv, si);
+    if (threadIdx.x == 0) {
+        ids[m] = i;
+        if (max_logit) max_logit[m] = v;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void verify_partial_kernel(const float* logits, int V, int nsplit,
+                                                                float* part_val, int32_t* part_idx) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int row = blockIdx.x / nsplit, s = blockIdx.x % nsplit;
+    const int chunk = (((V + nsplit - 1) / nsplit) + 3) & ~3;
+    const int v0 = s * chunk, v1 = min(V, v0 + chunk);
+    const float* src = logits + (int64_t)row * V;
+    float v = -INFINITY;
+    int i = 0x7fffffff;
+    if ((V & 3) == 0) {
+        for (int j = v0 + 4 * threadIdx.x; j < v1; j += 4 * blockDim.x) {
+            const float4 a = *reinterpret_cast<const float4*>(src + j);
+            argmax_pick(v, i, a.x, j);
+            argmax_pick(v, i, a.y, j + 1);
+            argmax_pick(v, i, a.z, j + 2);
+            argmax_pick(v, i, a.w, j + 3);
+        }
+    } else {
+        for (int j = v0 + threadIdx.x; j < v1; j += blockDim.x) argmax_pick(v, i, src[j], j);
+    }
+    block_argmax(v, i, sv, si);
+    if (threadIdx.x == 0) {
+        part_val[blockIdx.x] = v;
+        part_idx[blockIdx.x] = i;
+    }
+}
+
+// one 64-lane wavefront per sequence; lane j handles verify row j (gamma + 1 <= 64)
+__global__ __launch_bounds__(64) void verify_final_kernel(const float* part_val, const int32_t* part_idx, int nsplit,
+                                                          const int32_t* draft, int gamma, int32_t* accepted,
+                                                          int32_t* committed, int32_t* ids, int32_t* next_anchor) {
+    const int b = blockIdx.x, j = threadIdx.x;
+    const int W = gamma + 1;
+    int t = -1;
+    if (j < W) {
+        float v = -INFINITY;
+        int i = 0x7fffffff;
+        const int64_t base = ((int64_t)b * W + j) * nsplit;
+        for (int s = 0; s < nsplit; ++s) argmax_pick(v, i, part_val[base + s], part_idx[base + s]);
+        t = i;
+    }
+    const bool mismatch = (j < gamma) && (draft[(int64_t)b * gamma + j] != t);
+    const unsigned long long mask = __ballot(mismatch);
+    const int a = mask ? (__ffsll((long long)mask) - 1) : gamma;
+    if (j < W) ids[(int64_t)b * W + j] = (j <= a) ? t : -1;
+    if (j == a && next_anchor) next_anchor[b] = t;
+    if (j == 0) {
+        accepted[b] = a;
+        committed[b] = a + 1;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void rownorm_kernel(float* x, int d, const void* gain, int gain_f32, float eps) {
+    __shared__ float sv[4];
+    float* row = x + (int64_t)blockIdx.x * d;
+    float s = 0.f;
+    for (int k = threadIdx.x; k < d; k += blockDim.x) s += row[k] * row[k];
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) sv[threadIdx.x >> 6] = s;
+    __syncthreads();
+    const float tot = sv[0] + sv[1] + sv[2] + sv[3];
+    const float r = 1.0f / sqrtf(tot / (float)d + eps);
+    for (int k = threadIdx.x; k < d; k += blockDim.x) row[k] = row[k] * r * load_gain(gain, gain_f32, k);
+}
+
+__global__ void advance_len_kernel(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap) {
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+        const int rows = row_offsets[b + 1] - row_offsets[b];
+        const int add = counts ? min(counts[b], rows) : rows;
+        len[b] = min(cap, len[b] + max(add, 0));
+    }
+}
+
+__global__ void f32_to_bf16_kernel(const float* src, uint16_t* dst, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = (uint16_t)f32_to_bf16_bits(src[i]);
+}
+
+__global__ void copy_f32_kernel(const float* src, float* dst, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+
+hipError_t launch_argmax_merge(const float* pv, const int32_t* pi, int nblocks, int M, int32_t* ids, float* maxl,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(argmax_merge_kernel, dim3(M), dim3(kBlock), 0, s, pv, pi, nblocks, ids, maxl);
+    return hipGetLastError();
+}
+
+int verify_splits(int V) {
+    int ns = (V + 4095) / 4096;
+    return ns < 1 ? 1 : (ns > 64 ? 64 : ns);
+}
+
+hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int gamma, int V, int32_t* accepted,
+                         int32_t* committed, int32_t* ids, int32_t* next_anchor, float* pv, int32_t* pi,
+                         hipStream_t s) {
+    const int ns = verify_splits(V);
+    const int rows = B * (gamma + 1);
+    hipLaunchKernelGGL(verify_partial_kernel, dim3(rows * ns), dim3(kBlock), 0, s, logits, V, ns, pv, pi);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(verify_final_kernel, dim3(B), dim3(64), 0, s, pv, pi, ns, draft, gamma, accepted, committed,
+                       ids, next_anchor);
+    return hipGetLastError();
+}
+
+hipError_t launch_rownorm(float* x, int rows, int d, const void* gain, int gain_f32, float eps, hipStream_t s) {
+    hipLaunchKernelGGL(rownorm_kernel, dim3(rows), dim3(kBlock), 0, s, x, d, gain, gain_f32, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_advance_len(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap,
+                              hipStream_t s) {
+    hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, s, len, row_offsets, counts, B, cap);
+    return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+    return hipGetLastError();
+}
+
+}  // namespace dfl

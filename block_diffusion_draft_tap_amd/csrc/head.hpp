@@ -1,0 +1,22 @@
+// Argmax merge, greedy verification and small helper kernels (see head.hip).
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace dfl {
+
+hipError_t launch_argmax_merge(const float* pv, const int32_t* pi, int nblocks, int M, int32_t* ids, float* maxl,
+                               hipStream_t s);
+int verify_splits(int V);
+hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int gamma, int V, int32_t* accepted,
+                         int32_t* committed, int32_t* ids, int32_t* next_anchor, float* pv, int32_t* pi,
+                         hipStream_t s);
+hipError_t launch_rownorm(float* x, int rows, int d, const void* gain, int gain_f32, float eps, hipStream_t s);
+hipError_t launch_advance_len(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap,
+                              hipStream_t s);
+hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+
+}  // namespace dfl

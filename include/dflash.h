@@ -1,0 +1,237 @@
+/*
+ * dflash.h -- C ABI of libdflash.so, the MI355X (gfx950) hot path of the DFlash
+ * KV-injection block drafter: context projection, per-layer context K/V,
+ * drafter layers, LM-head argmax and greedy block verification.
+ *
+ * The method (page "@mlx-bun/inference 0.0.0-stage -> 1.0.0", dflash.ts, the
+ * header comment on Eq 2 and Eq 3):
+ *   Eq 2  H_ctx = RMSNorm(W_c [H^l1; ...; H^lm])  over every context row.
+ *   Eq 3  draft layer i: K_i = [W_K n_ctx ; W_K n_d], V_i = [W_V n_ctx ; W_V n_d],
+ *         Q_i = W_Q n_d, with n_ctx, n_d the layer's attn_norm of H_ctx and H_d;
+ *         the gamma block rows attend bidirectionally over [context ++ block].
+ *   Greedy verify (page "Inco Hacks Native: DFlash 2 Speculation", section 3):
+ *         accepted = longest draft prefix equal to the target argmax,
+ *         committed = accepted + 1.
+ *
+ * Conventions for every call below
+ *   - All tensor pointers are DEVICE pointers unless a comment says "host".
+ *   - Matrices are row-major [out, in]: the reduction axis is contiguous.
+ *     A product is y[m, n] = sum_k x[m, k] * W[n, k].
+ *   - Weight formats (dflash_weight.dtype):
+ *       DFLASH_F32      float  [rows, cols]
+ *       DFLASH_BF16     bfloat16 bits (uint16) [rows, cols]
+ *       DFLASH_INT4G64  codes: uint32 [rows, cols/8], 8 codes per word, low
+ *                       nibble = lowest column; scales, biases: bfloat16
+ *                       [rows, cols/64]; w[n, k] = scale[n, k/64] * q + bias[n, k/64].
+ *     Norm gains, mask_emb and block_pos are float for DFLASH_F32 models and
+ *     bfloat16 otherwise.
+ *   - Rounding contract (bf16 and int4 models; f32 models never round):
+ *     accumulation is fp32; the input of every weight product is rounded to
+ *     bf16 (nearest-even), as are the Q/K/V projections, the attention output,
+ *     the gated-FFN product, the out-projection result Y and the K/V cache.
+ *     The residual stream H_d and H_ctx stay fp32; logits stay fp32 and are
+ *     never materialised.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream), performs no host synchronisation and allocates nothing. The
+ *     caller owns every buffer (weights, KV cache, workspace, outputs) and
+ *     keeps it alive until the stream has passed the call. The library keeps
+ *     no pointer after return and holds no per-model state; calls are
+ *     thread-safe. Calls that share a workspace must be ordered on one stream.
+ *   - Return value: DFLASH_OK, or
+ *       DFLASH_DECLINED  a valid request this library will not serve (no
+ *                        gfx950 device, unsupported head dim / dtype / shape,
+ *                        or the kill switch DFLASH_DISABLE=1 in the
+ *                        environment). Nothing is enqueued or written; the
+ *                        caller falls back to plain decoding. (An acceleration
+ *                        path may decline a request but must never fail one:
+ *                        page "A Refusal Is Not A Failure", section "The rule
+ *                        it earned".)
+ *       DFLASH_EINVAL    null pointer, inconsistent dims or sizes.
+ *       DFLASH_ENOSPC    workspace or KV capacity too small.
+ *       DFLASH_EHIP      a kernel launch failed; the stream state is undefined.
+ *     Validation happens on the host before anything is enqueued.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_OK        0
+#define DFLASH_DECLINED  1
+#define DFLASH_EINVAL   (-1)
+#define DFLASH_ENOSPC   (-2)
+#define DFLASH_EHIP     (-3)
+
+enum { DFLASH_F32 = 0, DFLASH_BF16 = 1, DFLASH_INT4G64 = 2 };
+enum { DFLASH_ACT_GELU_TANH = 0, DFLASH_ACT_SILU = 1 };
+
+/* Drafter geometry. d must equal hq*hd and hq must be a multiple of hkv
+ * (query head h reads key/value head h / (hq/hkv)). hd is 64 or 128.
+ * gamma = block query rows = drafted tokens (the verify width is gamma+1). */
+typedef struct {
+    int32_t H;       /* target hidden size (tap width and LM-head width)   */
+    int32_t m;       /* number of tapped target layers                      */
+    int32_t d;       /* drafter width                                        */
+    int32_t nl;      /* drafter layers                                       */
+    int32_t hq;      /* query heads                                          */
+    int32_t hkv;     /* key/value heads                                      */
+    int32_t hd;      /* head dim                                             */
+    int32_t F;       /* FFN inner width                                      */
+    int32_t V;       /* vocabulary                                           */
+    int32_t gamma;   /* block rows                                           */
+    float   eps;     /* RMSNorm epsilon                                      */
+    int32_t act;     /* DFLASH_ACT_*: activation of the gate branch          */
+    int32_t wdtype;  /* DFLASH_F32 / DFLASH_BF16 / DFLASH_INT4G64            */
+} dflash_dims;
+
+typedef struct {
+    int32_t     dtype;   /* DFLASH_F32 / DFLASH_BF16 / DFLASH_INT4G64 */
+    int32_t     rows;    /* outputs N                                  */
+    int32_t     cols;    /* reduction K                                */
+    const void* data;    /* see the weight formats above               */
+    const void* scales;  /* int4 only, else NULL                       */
+    const void* biases;  /* int4 only, else NULL                       */
+} dflash_weight;
+
+/* One drafter layer (page 3, #layer). */
+typedef struct {
+    const void*   attn_norm;  /* [d]                                              */
+    dflash_weight w_qkv;      /* [(hq + 2 hkv) hd, d]: Q rows, then K rows, then V */
+    dflash_weight w_o;        /* [d, hq hd]                                       */
+    const void*   ffn_norm;   /* [d]                                              */
+    dflash_weight w_gate_up;  /* [2F, d]: gate rows (activated) then up rows      */
+    dflash_weight w_down;     /* [d, F]                                           */
+} dflash_layer;
+
+/* The drafter plus the two tables it borrows from the target (it has no
+ * embedding or head of its own: page "A Refusal Is Not A Failure"). */
+typedef struct {
+    dflash_dims          dims;
+    dflash_weight        w_c;        /* [d, m H]  Eq 2 projection                 */
+    const void*          ctx_norm;   /* [d]                                       */
+    dflash_weight        tok_proj;   /* [d, H]    anchor embedding -> width d     */
+    const void*          mask_emb;   /* [gamma-1, d]                              */
+    const void*          block_pos;  /* [gamma, d]                                */
+    const void*          out_norm;   /* [d]                                       */
+    dflash_weight        out_proj;   /* [H, d]                                    */
+    dflash_weight        embed_in;   /* [V, H]    target input embedding          */
+    dflash_weight        lm_head;    /* [V, H]    target LM head                  */
+    const dflash_layer*  layers;     /* HOST array of nl layers                   */
+} dflash_model;
+
+/* Retained per-layer context K/V of B sequences.
+ * k, v: [nl][B][hkv][cap][hd], element type `dtype` (DFLASH_F32 for f32 models,
+ * DFLASH_BF16 otherwise). len: device int32 [B], rows held per sequence. */
+typedef struct {
+    void*    k;
+    void*    v;
+    int32_t* len;
+    int32_t  B;
+    int32_t  cap;
+    int32_t  dtype;
+} dflash_kv;
+
+/* Workspace bytes needed by any call below for up to B sequences and a
+ * context capacity of cap rows (the per-call requirement never exceeds it).
+ * Returns 0 for invalid dims. */
+size_t dflash_workspace_bytes(const dflash_dims* dims, int32_t B, int32_t cap);
+
+/* DFLASH_OK if this library would serve models of these dims on the current
+ * device, DFLASH_DECLINED if not, DFLASH_EINVAL if the dims are inconsistent. */
+int dflash_query(const dflash_dims* dims);
+
+/* Static description of a status code. */
+const char* dflash_status_string(int status);
+
+/* Number of successful enqueues since load (all calls together): evidence
+ * that the accelerated path really ran. */
+uint64_t dflash_invocations(void);
+
+/* Eq 2 (page 3, #buildContext): h_ctx[r] = RMSNorm(sum_j T_j[r] W_c[:, jH:(j+1)H]^T; ctx_norm).
+ *   taps:   HOST array of m device pointers; tap j is [n, H] with row stride
+ *           tap_ld elements, float for f32 models, bfloat16 otherwise.
+ *   n:      rows (>= 0; 0 enqueues nothing).
+ *   h_ctx:  float [n, d] output.
+ * No workspace is used (ws may be NULL). */
+int dflash_context_project(const dflash_model* M, const void* const* taps, int64_t tap_ld, int32_t n,
+                           float* h_ctx, void* ws, size_t ws_bytes, void* stream);
+
+/* Eq 3, context half (page 3, projectContextRows): for every layer i and
+ * every appended row, K = bf16(bf16(RMSNorm(h_ctx; attn_norm_i)) W_K_i^T) and
+ * V likewise, written to kv at rows len[b], len[b]+1, ...; then
+ * len[b] += appended rows.
+ *   h_ctx:       float [n, d]; rows of sequence b are row_offsets[b] ..
+ *                row_offsets[b+1]-1 (device int32 [B+1], non-decreasing).
+ *   counts:      device int32 [B] or NULL. If given, only the first
+ *                min(counts[b], rows of b) rows of b are appended (the verified
+ *                rows of a round); NULL appends all rows.
+ *   Rows that would pass cap are not written and len[b] stops at cap (the
+ *   caller sizes cap; see dflash_workspace_bytes).
+ * No workspace is used (ws may be NULL). */
+int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, const int32_t* row_offsets,
+                         const int32_t* counts, const dflash_kv* kv, void* ws, size_t ws_bytes, void* stream);
+
+/* One drafter layer on the block (page 3, #layer, Eq 3), in place:
+ *   n = RMSNorm(H; attn_norm), Q/K_b/V_b = n W^T,
+ *   O = softmax(hd^-1/2 Q [K_ctx[0:len[b]] ; K_b]^T) [V_ctx ; V_b]  (no mask),
+ *   H += O W_o^T, n2 = RMSNorm(H; ffn_norm), H += (act(n2 W_gate^T) * n2 W_up^T) W_down^T.
+ *   h_block: float [B, gamma, d], read and written.
+ *   kv:      read only (never written by this call).
+ * Workspace: dflash_workspace_bytes(dims, B, kv->cap). */
+int dflash_draft_layer(const dflash_model* M, int32_t layer, float* h_block, const dflash_kv* kv, int32_t B,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Block init + every layer + out projection + LM-head argmax (page 3,
+ * forwardRows with a retained context, greedy; #buildBlock, #backbone,
+ * #baseLogits):
+ *   H_d[b, 0] = E_in[anchor[b]] tok_proj^T + block_pos[0],
+ *   H_d[b, k] = mask_emb[k-1] + block_pos[k]   (k >= 1),
+ *   ... layers ..., Y = bf16(bf16(RMSNorm(H_d; out_norm)) out_proj^T),
+ *   draft_ids[b, k] = argmax_v Y[b, k] . lm_head[v]  (lowest index on ties).
+ *   anchor_ids: device int32 [B], each in [0, V).
+ *   draft_ids:  device int32 [B, gamma] output.
+ *   y_out:      optional [B, gamma, H] output (float for f32 models, bfloat16
+ *               otherwise); NULL to skip.
+ *   max_logit:  optional float [B, gamma] output (the winning logit); NULL to skip.
+ * Workspace: dflash_workspace_bytes(dims, B, kv->cap). */
+int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const dflash_kv* kv, int32_t B,
+                         int32_t* draft_ids, void* y_out, float* max_logit, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Greedy ids under a borrowed LM head (page 3, #baseLogits and the argmax
+ * step of forwardRows): ids[r] = argmax_v y[r] . E_out[v], lowest index on
+ * ties; logits are fp32 accumulations and are never materialised.
+ *   E_out: HOST pointer to the weight descriptor, [V, H].
+ *   y:     [M, H], element type y_dtype (DFLASH_F32 or DFLASH_BF16); rounded
+ *          to bf16 before the product unless E_out is f32.
+ *   ids:   device int32 [M];  max_logit: optional float [M].
+ * Workspace: at least dflash_lm_head_workspace_bytes(E_out->rows, M). */
+int dflash_lm_head_argmax(const dflash_weight* E_out, const void* y, int32_t y_dtype, int32_t M, int32_t* ids,
+                          float* max_logit, void* ws, size_t ws_bytes, void* stream);
+size_t dflash_lm_head_workspace_bytes(int32_t V, int32_t M);
+
+/* Greedy block verification (page "Inco Hacks Native: DFlash 2
+ * Speculation", sections 1 and 3: block = 1 verify + gamma proposals;
+ * e.g. accepted=7 committed=8, accepted=5 committed=6 at block 8):
+ *   t[b, j] = argmax_v target_logits[b, j, v]  (j = 0..gamma, lowest index on ties)
+ *   accepted[b] = largest a <= gamma with draft_ids[b, k] == t[b, k] for all k < a
+ *   committed[b] = accepted[b] + 1
+ *   ids[b, j] = t[b, j] for j <= accepted[b], else -1
+ *   next_anchor[b] = t[b, accepted[b]]  (optional; NULL to skip)
+ *   target_logits: float [B, gamma+1, V]; draft_ids: int32 [B, gamma].
+ * Workspace: at least dflash_verify_workspace_bytes(B, gamma, V). */
+int dflash_verify_greedy(const float* target_logits, const int32_t* draft_ids, int32_t B, int32_t gamma, int32_t V,
+                         int32_t* accepted, int32_t* committed, int32_t* ids, int32_t* next_anchor, void* ws,
+                         size_t ws_bytes, void* stream);
+size_t dflash_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

@@ -1,0 +1,280 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded
+inputs, element by element, at sizes the oracle finishes in seconds.
+
+Workloads: the fp32 tiny drafter (context 32), a bf16 GQA drafter with three
+ragged sequences (contexts 200 / 77 / 131 keys: several 64-key tiles plus
+tails, a 1000-token vocabulary that is not a multiple of the head's row tile),
+and the default bf16 drafter at its full size (context 2048, vocab 32768).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_draft_tap_amd as dfa
+from block_diffusion_draft_tap_amd import binding as bd
+from gpu_common import (compare_ids, dev, faithful, log, oracle_prefill, rel_err, tol, TOL_F32)
+from oracle import dflash_oracle as O
+from synth import gen, TINY, DEFAULT, scaled
+
+pytestmark = pytest.mark.gpu
+
+GQA_BF16 = scaled(TINY, name="gqa_bf16", wdtype="bf16", H=256, d=256, hq=4, hkv=2, hd=64, F=512, gamma=5,
+                  V=1000, B=3, L=200)
+
+CASES = {
+    "tiny": (TINY, [TINY.L]),
+    "gqa_bf16": (GQA_BF16, [200, 77, 131]),
+    "default": (DEFAULT, [DEFAULT.L]),
+}
+
+_cache = {}
+
+
+class Setup:
+    def __init__(self, name):
+        dims, lengths = CASES[name]
+        log(f"[setup] {name}: dims={dims} lengths={lengths}")
+        self.name, self.dims, self.lengths = name, dims, list(lengths)
+        self.B = len(lengths)
+        self.fm = faithful(dims)
+        self.w = gen.Model(dims, gains="random").materialise()
+        self.dm = dfa.DeviceModel(dims, self.w)
+        self.ctx, self.Hs, self.taps = oracle_prefill(dims, self.w, self.lengths, self.fm)
+        self.cap = max(self.lengths) + 64
+        self.kv = dfa.KVCache(dims, self.B, self.cap)
+        taps_cat = [np.concatenate([self.taps[b][j] for b in range(self.B)]) for j in range(dims.m)]
+        self.taps_d = [dev(t) for t in taps_cat]
+        n = sum(self.lengths)
+        self.h_ctx = torch.empty(n, dims.d, dtype=torch.float32, device="cuda")
+        bd.check(dfa.dflash_context_project(self.dm, self.taps_d, self.h_ctx), "context_project")
+        offs = np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int32)
+        self.offs_d = torch.from_numpy(offs).cuda()
+        bd.check(dfa.dflash_ctx_kv_append(self.dm, self.h_ctx, self.offs_d, None, self.kv), "ctx_kv_append")
+        torch.cuda.synchronize()
+        self.ws = dfa.workspace(dims, self.B, self.cap)
+        log(f"[setup] {name}: done")
+
+
+def get(name):
+    if name not in _cache:
+        _cache[name] = Setup(name)
+    return _cache[name]
+
+
+NAMES = list(CASES)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_context_projection(name):
+    s = get(name)
+    ref = np.concatenate(s.Hs)
+    err = rel_err(s.h_ctx, ref)
+    log(f"[{name}] H_ctx rel err {err:.3e}")
+    assert err <= TOL_F32      # bf16 taps and weights are exact inputs; only fp32 accumulation differs
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_context_kv_cache(name):
+    s = get(name)
+    assert s.kv.len.cpu().tolist() == s.lengths
+    worst = 0.0
+    for i in range(s.dims.nl):
+        for b, L in enumerate(s.lengths):
+            for which, gpu, ref in (("k", s.kv.k, s.ctx.k), ("v", s.kv.v, s.ctx.v)):
+                g = gpu[i, b, :, :L, :].permute(1, 0, 2)
+                e = rel_err(g, ref[i][b])
+                worst = max(worst, e)
+                assert e <= tol(s.dims), (i, b, which, e)
+    log(f"[{name}] K/V cache worst rel err {worst:.3e}")
+
+
+def _block_input(s, round_idx=0):
+    anchors = gen.make_anchors(s.dims, round_idx)
+    H = O.block_init(anchors, s.w["E_in"], s.w["tok_proj"], s.w["mask_emb"], s.w["block_pos"], s.dims.gamma,
+                     s.fm)
+    return anchors, H
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_draft_layer(name):
+    s = get(name)
+    _, H = _block_input(s)
+    for layer in sorted({0, s.dims.nl - 1}):
+        h = torch.from_numpy(H.astype(np.float32)).cuda()
+        bd.check(dfa.dflash_draft_layer(s.dm, layer, h, s.kv, s.B, s.ws), "draft_layer")
+        ref = O.draft_layer(H, s.ctx, layer, s.w, s.dims, s.fm)
+        err = rel_err(h, ref)
+        log(f"[{name}] layer {layer} H_d rel err {err:.3e}")
+        assert err <= tol(s.dims)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_draft_layer_is_noncausal(name):
+    """Changing only the last block row's input changes row 0's output, on the
+    GPU as in the oracle (no causal mask inside the block)."""
+    s = get(name)
+    _, H = _block_input(s)
+    H2 = H.copy()
+    H2[:, -1, :] += 0.5
+    outs = []
+    for X in (H, H2):
+        h = torch.from_numpy(X.astype(np.float32)).cuda()
+        bd.check(dfa.dflash_draft_layer(s.dm, 0, h, s.kv, s.B, s.ws), "draft_layer")
+        outs.append(h.cpu().numpy())
+        assert rel_err(h, O.draft_layer(X, s.ctx, 0, s.w, s.dims, s.fm)) <= tol(s.dims)
+    assert np.max(np.abs(outs[1][:, 0] - outs[0][:, 0])) > 1e-4
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_draft_forward(name):
+    s = get(name)
+    d = s.dims
+    anchors, _ = _block_input(s)
+    ids = torch.empty(s.B, d.gamma, dtype=torch.int32, device="cuda")
+    y = torch.empty(s.B, d.gamma, d.H, dtype=s.dm.act_dtype, device="cuda")
+    maxl = torch.empty(s.B, d.gamma, dtype=torch.float32, device="cuda")
+    a_d = torch.from_numpy(anchors).cuda()
+    bd.check(dfa.dflash_draft_forward(s.dm, a_d, s.kv, s.B, ids, s.ws, y_out=y, max_logit=maxl), "forward")
+    ref_ids, ex = O.draft_forward(s.w, d, s.ctx, anchors, s.fm, return_all=True)
+    ey = rel_err(y, ex["Y"])
+    em = rel_err(maxl, ex["max_logit"])
+    decided = compare_ids(ids, ref_ids, ex["logits"])
+    log(f"[{name}] Y rel err {ey:.3e}, max-logit rel err {em:.3e}, ids decided {decided}/{ids.numel()}")
+    assert ey <= tol(d) and em <= tol(d)
+    assert decided >= ids.numel() // 2
+    # determinism: a second run is bitwise identical
+    ids2 = torch.empty_like(ids)
+    y2 = torch.empty_like(y)
+    maxl2 = torch.empty_like(maxl)
+    bd.check(dfa.dflash_draft_forward(s.dm, a_d, s.kv, s.B, ids2, s.ws, y_out=y2, max_logit=maxl2), "forward")
+    assert torch.equal(ids, ids2) and torch.equal(y, y2) and torch.equal(maxl, maxl2)
+
+
+@pytest.mark.parametrize("wd", ["f32", "bf16", "int4g64"])
+@pytest.mark.parametrize("M", [1, 5, 8, 13])
+def test_lm_head_argmax_planted_and_random(wd, M):
+    dims = scaled(TINY, wdtype=wd, H=256, V=1000)
+    E = gen.make_weight(dims, "E_out")
+    Ed = O.dense(E)
+    rng = np.random.default_rng(M)
+    Y = rng.standard_normal((M, dims.H)).astype(np.float32)
+    if wd != "f32":
+        Y = O.bf16(Y).astype(np.float32)
+    # planted rows: one-hot input selecting a column whose maximum is planted (with a tie)
+    if M >= 5:
+        c = 17
+        Y[0] = 0.0
+        Y[0, c] = 1.0
+        col = Ed[:, c]
+        top = np.argsort(col)[-2:]
+        lo, hi = int(min(top)), int(max(top))
+        if wd == "f32":
+            E = E.copy()
+            E[hi, c] = E[lo, c]            # exact tie between two rows: the lower index must win
+            Ed = O.dense(E)
+    W = dfa.Weight(E, torch.device("cuda"))
+    ids = torch.empty(M, dtype=torch.int32, device="cuda")
+    maxl = torch.empty(M, dtype=torch.float32, device="cuda")
+    ws = bd.lm_head_workspace(dims.V, M)
+    y_d = torch.from_numpy(Y).cuda()
+    bd.check(dfa.dflash_lm_head_argmax(W, y_d, ids, ws, max_logit=maxl), "lm_head")
+    ref_ids, best, logits = O.lm_head_argmax(Y.astype(np.float64), E, want_logits=True)
+    compare_ids(ids, ref_ids, logits)
+    assert rel_err(maxl, best) <= 1e-5
+    if M >= 5 and wd == "f32":
+        assert int(ids[0]) == lo
+
+
+@pytest.mark.parametrize("V", [5000, 5001, 32768])
+def test_verify_exhaustive_patterns(V):
+    """All 2^7 agreement patterns of a block-8 verify in one batch; bit-exact
+    against the oracle (and therefore against the definition)."""
+    G = 7
+    B = 2 ** G
+    rng = np.random.default_rng(V)
+    t = rng.integers(0, V, size=(B, G + 1))
+    draft = np.empty((B, G), dtype=np.int32)
+    for b in range(B):
+        for k in range(G):
+            draft[b, k] = t[b, k] if (b >> k) & 1 else (t[b, k] + 1 + rng.integers(0, V - 1)) % V
+    T = rng.standard_normal((B, G + 1, V)).astype(np.float32)
+    T[np.arange(B)[:, None], np.arange(G + 1)[None, :], t] = T.max(axis=2) + 1.0
+    T[0, 0, :] = 0.0                            # an all-tie row resolves to index 0
+    acc_o, com_o, ids_o, nxt_o = O.verify_greedy(T, draft)
+    T_d = torch.from_numpy(T).cuda()
+    dr_d = torch.from_numpy(draft).cuda()
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    com = torch.empty_like(acc)
+    nxt = torch.empty_like(acc)
+    ids = torch.empty(B, G + 1, dtype=torch.int32, device="cuda")
+    ws = bd.verify_workspace(B, G, V)
+    bd.check(dfa.dflash_verify_greedy(T_d, dr_d, acc, com, ids, ws, next_anchor=nxt), "verify")
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
+    assert np.array_equal(com.cpu().numpy(), com_o)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert np.array_equal(nxt.cpu().numpy(), nxt_o)
+    assert np.array_equal(com_o, acc_o + 1)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa_bf16"])
+def test_multi_round_loop(name):
+    """Rounds of append(committed rows) -> forward -> verify, both sides driven
+    by the oracle's schedule (planted logits realise accept lengths; the
+    oracle's committed counts and next anchors feed both sides)."""
+    base = get(name)
+    d = base.dims
+    B = base.B
+    ctx = O.Context(d.nl, B, d.hkv, d.hd)
+    for i in range(d.nl):
+        for b in range(B):
+            ctx.append(i, b, base.ctx.k[i][b].copy(), base.ctx.v[i][b].copy())
+    kv = dfa.KVCache(d, B, base.cap + 8 * (d.gamma + 1))
+    kv.k[:, :, :, :base.cap].copy_(base.kv.k)
+    kv.v[:, :, :, :base.cap].copy_(base.kv.v)
+    kv.len.copy_(base.kv.len)
+    ws = dfa.workspace(d, B, kv.cap)
+    vws = bd.verify_workspace(B, d.gamma, d.V)
+    anchors = gen.make_anchors(d, 0)
+    W = d.gamma + 1
+    offs = torch.arange(0, (B + 1) * W, W, dtype=torch.int32, device="cuda")
+    seen = set()
+    for r in range(6):
+        # forward
+        ids = torch.empty(B, d.gamma, dtype=torch.int32, device="cuda")
+        bd.check(dfa.dflash_draft_forward(base.dm, torch.from_numpy(anchors).cuda(), kv, B, ids, ws), "forward")
+        ref_ids, ex = O.draft_forward(base.w, d, ctx, anchors, base.fm, return_all=True)
+        compare_ids(ids, ref_ids, ex["logits"])
+        # verify on logits planted from the oracle's drafts
+        a = gen.accept_schedule(d, r) if d.name == "tiny" else np.array([(r + b) % W for b in range(B)], np.int32)
+        T = gen.plant_target_logits(d, ref_ids, a, r)
+        acc_o, com_o, ids_o, nxt_o = O.verify_greedy(T, ref_ids)
+        assert np.array_equal(acc_o, a)
+        acc = torch.empty(B, dtype=torch.int32, device="cuda")
+        com, nxt = torch.empty_like(acc), torch.empty_like(acc)
+        vid = torch.empty(B, W, dtype=torch.int32, device="cuda")
+        bd.check(dfa.dflash_verify_greedy(torch.from_numpy(T).cuda(), torch.from_numpy(ref_ids).cuda(), acc, com,
+                                          vid, vws, next_anchor=nxt), "verify")
+        assert np.array_equal(acc.cpu().numpy(), acc_o) and np.array_equal(vid.cpu().numpy(), ids_o)
+        assert np.array_equal(nxt.cpu().numpy(), nxt_o)
+        seen.update(int(x) for x in acc_o)
+        # append the committed rows of this round's verify
+        taps = [gen.make_taps(d, r * W, W, stream="round", seq=b) for b in range(B)]
+        taps_cat = [dev(np.concatenate([taps[b][j] for b in range(B)])) for j in range(d.m)]
+        h = torch.empty(B * W, d.d, dtype=torch.float32, device="cuda")
+        bd.check(dfa.dflash_context_project(base.dm, taps_cat, h), "project")
+        bd.check(dfa.dflash_ctx_kv_append(base.dm, h, offs, torch.from_numpy(com_o).cuda(), kv), "append")
+        for b in range(B):
+            Hc = O.context_project(taps[b], base.w["W_c"], base.w["ctx_norm"], d.eps)
+            O.append_context(ctx, base.w, d, Hc, [[]] * b + [list(range(W))] + [[]] * (B - b - 1),
+                             [0] * b + [int(com_o[b])] + [0] * (B - b - 1), base.fm)
+        anchors = nxt_o
+    torch.cuda.synchronize()
+    assert kv.len.cpu().tolist() == [ctx.length(b) for b in range(B)]
+    for i in range(d.nl):
+        for b in range(B):
+            L = ctx.length(b)
+            assert rel_err(kv.k[i, b, :, :L].permute(1, 0, 2), ctx.k[i][b]) <= tol(d)
+    log(f"[{name}] multi-round accepted lengths seen: {sorted(seen)}")
+    if name == "tiny":
+        assert seen == set(range(d.gamma + 1))
