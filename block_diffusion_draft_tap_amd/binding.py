@@ -15,7 +15,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdflash.so")
+# DFLASH_LIB_PATH selects another build of the library (tuning variants)
+LIB_PATH = os.environ.get("DFLASH_LIB_PATH") or os.path.join(_HERE, "libdflash.so")
 
 DFLASH_OK, DFLASH_DECLINED, DFLASH_EINVAL, DFLASH_ENOSPC, DFLASH_EHIP = 0, 1, -1, -2, -3
 DFLASH_F32, DFLASH_BF16, DFLASH_INT4G64 = 0, 1, 2
@@ -24,7 +25,7 @@ DFLASH_ACT_GELU_TANH, DFLASH_ACT_SILU = 0, 1
 EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "dflash_invocations",
            "dflash_context_project", "dflash_ctx_kv_append", "dflash_draft_layer", "dflash_draft_forward",
            "dflash_lm_head_argmax", "dflash_lm_head_workspace_bytes", "dflash_verify_greedy",
-           "dflash_verify_workspace_bytes"]
+           "dflash_verify_workspace_bytes", "dflash_trace_head_events"]
 
 
 class DflashError(RuntimeError):
@@ -90,6 +91,8 @@ def _load():
     lib.dflash_verify_greedy.restype = ctypes.c_int
     lib.dflash_verify_workspace_bytes.argtypes = [I32, I32, I32]
     lib.dflash_verify_workspace_bytes.restype = SZ
+    lib.dflash_trace_head_events.argtypes = [VP, VP]
+    lib.dflash_trace_head_events.restype = None
     return lib
 
 
@@ -266,11 +269,12 @@ def dflash_invocations():
     return int(lib.dflash_invocations())
 
 
-def dflash_context_project(model, taps, h_ctx, stream=None):
+def dflash_context_project(model, taps, h_ctx, ws=None, stream=None):
     n = taps[0].shape[0]
     arr = (ctypes.c_void_p * len(taps))(*[_ptr(t) for t in taps])
     ld = taps[0].stride(0)
-    return lib.dflash_context_project(ctypes.byref(model.c), arr, ld, n, _ptr(h_ctx), None, 0, _stream(stream))
+    return lib.dflash_context_project(ctypes.byref(model.c), arr, ld, n, _ptr(h_ctx), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(stream))
 
 
 def dflash_ctx_kv_append(model, h_ctx, row_offsets, counts, kv, stream=None):
@@ -310,3 +314,30 @@ def dflash_verify_greedy(target_logits, draft_ids, accepted, committed, ids, ws,
 
 def verify_workspace(B, gamma, V, device="cuda"):
     return torch.empty(lib.dflash_verify_workspace_bytes(B, gamma, V), dtype=torch.uint8, device=device)
+
+
+def dflash_trace_head_events(start=None, stop=None):
+    """Record torch.cuda.Event `start`/`stop` around every LM-head GEMV (None, None: off)."""
+    if start is None or stop is None:
+        lib.dflash_trace_head_events(None, None)
+    else:
+        if not start.cuda_event or not stop.cuda_event:
+            raise DflashError("trace events must be recorded once first (torch creates them lazily)")
+        lib.dflash_trace_head_events(start.cuda_event, stop.cuda_event)
+
+
+_hip = None
+
+
+def event_elapsed_ms(start, stop):
+    """hipEventElapsedTime on two torch.cuda.Event handles recorded by the
+    library (torch does not know about records it did not make itself).
+    Returns None if the runtime reports an error (e.g. not recorded)."""
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        _hip.hipEventElapsedTime.restype = ctypes.c_int
+    ms = ctypes.c_float(0.0)
+    rc = _hip.hipEventElapsedTime(ctypes.byref(ms), start.cuda_event, stop.cuda_event)
+    return float(ms.value) if rc == 0 else None

@@ -31,7 +31,8 @@ def hipcc():
 
 
 def common_flags():
-    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    extra = os.environ.get("DFLASH_DEFINES", "").split()  # -DNAME=VALUE tuning overrides
+    return extra + ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-Wno-unused-result"]
 
@@ -45,19 +46,23 @@ def _compile(src):
     return obj
 
 
-def build(verbose=True):
+def build(verbose=True, out=None, build_dir=None):
+    global BUILD
+    if build_dir:
+        BUILD = build_dir
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+    lib = out or LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

@@ -51,6 +51,61 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(const AttnParams p
     const int vcol = p.hq * HD + p.hkv * HD + g * HD;
     const int64_t cache_base = ((int64_t)b * p.hkv + g) * p.cap * HD;
 
+    // K/V rows of one 64-key tile, held in registers between the global loads
+    // and the LDS stores so that the next tile's loads overlap this tile's math
+    constexpr int UNITS = kTile * (HD / 8) / kBlock;
+    float kst[UNITS][8], vst[UNITS][8];
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            const int e = tid + u * kBlock;
+            const int key = e / (HD / 8), c8 = (e - key * (HD / 8)) * 8;
+            const int kk = t0 + key;
+            if (kk < lenb) {
+                const int64_t off = cache_base + (int64_t)kk * HD + c8;
+                if constexpr (KVF32) {
+                    const float* kp = static_cast<const float*>(p.kcache) + off;
+                    const float* vp = static_cast<const float*>(p.vcache) + off;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) { kst[u][j] = kp[j]; vst[u][j] = vp[j]; }
+                } else {
+                    const uint4 ka = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.kcache) + off);
+                    const uint4 va = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.vcache) + off);
+                    const uint32_t kw4[4] = {ka.x, ka.y, ka.z, ka.w}, vw4[4] = {va.x, va.y, va.z, va.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        kst[u][2 * j] = bf16_lo(kw4[j]); kst[u][2 * j + 1] = bf16_hi(kw4[j]);
+                        vst[u][2 * j] = bf16_lo(vw4[j]); vst[u][2 * j + 1] = bf16_hi(vw4[j]);
+                    }
+                }
+            } else if (kk < T) {
+                const float* rowp = qrow0 + (int64_t)(kk - lenb) * qkv_ld;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) { kst[u][j] = rowp[kcol + c8 + j]; vst[u][j] = rowp[vcol + c8 + j]; }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) { kst[u][j] = 0.f; vst[u][j] = 0.f; }
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            const int e = tid + u * kBlock;
+            const int key = e / (HD / 8), c8 = (e - key * (HD / 8)) * 8;
+            if constexpr (KVF32) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) ks[key * (HD + 4) + c8 + j] = __float_as_uint(kst[u][j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ks[key * KPAD + c8 / 2 + j] = pack_bf16x2(kst[u][2 * j], kst[u][2 * j + 1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vs[key * HD + c8 + j] = vst[u][j];
+        }
+    };
+    if (start < end) load_tile(start);
+
     // stage the group's query rows (already rounded to bf16 where the contract says so)
     for (int e = tid; e < R * HD; e += kBlock) {
         const int r = e / HD, dd = e - r * HD;
@@ -74,47 +129,9 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(const AttnParams p
 
     for (int t0 = start; t0 < end; t0 += kTile) {
         __syncthreads();
-        // ---- stage K and V rows t0 .. t0+63 (context rows, then block rows, then zeros)
-        for (int e = tid; e < kTile * (HD / 8); e += kBlock) {
-            const int key = e / (HD / 8), c8 = (e - key * (HD / 8)) * 8;
-            const int kk = t0 + key;
-            float kv8[8], vv8[8];
-            if (kk < lenb) {
-                const int64_t off = cache_base + (int64_t)kk * HD + c8;
-                if constexpr (KVF32) {
-                    const float* kp = static_cast<const float*>(p.kcache) + off;
-                    const float* vp = static_cast<const float*>(p.vcache) + off;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) { kv8[j] = kp[j]; vv8[j] = vp[j]; }
-                } else {
-                    const uint4 ka = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.kcache) + off);
-                    const uint4 va = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.vcache) + off);
-                    const uint32_t kw4[4] = {ka.x, ka.y, ka.z, ka.w}, vw4[4] = {va.x, va.y, va.z, va.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        kv8[2 * j] = bf16_lo(kw4[j]); kv8[2 * j + 1] = bf16_hi(kw4[j]);
-                        vv8[2 * j] = bf16_lo(vw4[j]); vv8[2 * j + 1] = bf16_hi(vw4[j]);
-                    }
-                }
-            } else if (kk < T) {
-                const float* rowp = qrow0 + (int64_t)(kk - lenb) * qkv_ld;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) { kv8[j] = rowp[kcol + c8 + j]; vv8[j] = rowp[vcol + c8 + j]; }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) { kv8[j] = 0.f; vv8[j] = 0.f; }
-            }
-            if constexpr (KVF32) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) ks[key * (HD + 4) + c8 + j] = __float_as_uint(kv8[j]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) ks[key * KPAD + c8 / 2 + j] = pack_bf16x2(kv8[2 * j], kv8[2 * j + 1]);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) vs[key * HD + c8 + j] = vv8[j];
-        }
+        store_tile();
         __syncthreads();
+        if (t0 + kTile < end) load_tile(t0 + kTile);
 
         // ---- scores and online softmax: lane = key, wavefront `wave` owns rows wave, wave+4, ...
         {
@@ -228,9 +245,15 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(const AttnParams p
     }
 }
 
-// One workgroup per (b, head, block row): combine the splits.
+// One workgroup per (b, head, block row): combine the splits. The split
+// weights exp(m_s - M) are formed once in LDS; each thread group then adds a
+// fixed subset of the splits and the groups are combined in a fixed order.
 template <int HD>
-__global__ __launch_bounds__(HD) void attn_merge_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) {
+    constexpr int G = kBlock / HD;
+    __shared__ float wts[64];
+    __shared__ float part[G][HD];
+    __shared__ float Lsh;
     const int row = blockIdx.x;  // (b*hq + h)*gamma + i
     const int i = row % p.gamma;
     const int bh = row / p.gamma;
@@ -238,34 +261,54 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(const AttnParams p) {
     const int W = HD + 2;
     const float* base = p.part + ((int64_t)bh * p.nsplit * p.gamma + i) * W;
     const int64_t sstride = (int64_t)p.gamma * W;
-    float M = -INFINITY;
-    for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, base[s * sstride + HD]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) {
-        const float ms = base[s * sstride + HD];
-        if (ms == -INFINITY) continue;
-        const float w = expf(ms - M);
-        L += w * base[s * sstride + HD + 1];
-        acc += w * base[s * sstride + threadIdx.x];
+    const int t = threadIdx.x;
+    if (t < 64) {
+        float ms = -INFINITY, ls = 0.f;
+        if (t < p.nsplit) {
+            ms = base[t * sstride + HD];
+            ls = base[t * sstride + HD + 1];
+        }
+        const float M = wave_max(ms);
+        const float w = (ms == -INFINITY) ? 0.f : expf(ms - M);
+        const float L = wave_sum(w * ls);
+        wts[t] = w;
+        if (t == 0) Lsh = L;
     }
-    float y = acc / L;
-    if (p.round_out) y = round_bf16(y);
-    p.out[((int64_t)b * p.gamma + i) * p.out_ld + h * HD + threadIdx.x] = y;
+    __syncthreads();
+    const int gi = t / HD, dcol = t % HD;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int sidx = gi; sidx < p.nsplit; sidx += G) acc += wts[sidx] * base[sidx * sstride + dcol];
+    part[gi][dcol] = acc;
+    __syncthreads();
+    if (gi == 0) {
+        float y = 0.f;
+#pragma unroll
+        for (int q = 0; q < G; ++q) y += part[q][dcol];
+        y /= Lsh;
+        const int64_t o = ((int64_t)b * p.gamma + i) * p.out_ld + h * HD + dcol;
+        if (p.round_out)
+            reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_to_bf16_bits(y);
+        else
+            p.out[o] = y;
+    }
 }
 
 template <int HD, bool KVF32>
 static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
     const int R = (p.hq / p.hkv) * p.gamma;
     dim3 grid((unsigned)((int64_t)p.B * p.hkv * p.nsplit));
-    if (R <= 8)
+    (void)hipGetLastError();  // report only this launch's status
+    if (R <= 8) {
         hipLaunchKernelGGL((attn_partial_kernel<HD, KVF32, 8>), grid, dim3(kBlock), 0, s, p);
-    else if (R <= 40)
+    } else if (R <= 40) {
         hipLaunchKernelGGL((attn_partial_kernel<HD, KVF32, 40>), grid, dim3(kBlock), 0, s, p);
-    else
+    } else {
         return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3((unsigned)(p.B * p.hq * p.gamma)), dim3(HD), 0, s, p);
+    hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3((unsigned)(p.B * p.hq * p.gamma)), dim3(kBlock), 0, s, p);
     return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ struct AttnParams {
     float* part;           // [B][hq][nsplit][gamma][hd+2]  (o, running max, running sum)
     float* out;            // O [B*gamma][out_ld], head h at columns h*hd
     int64_t out_ld;
-    int round_out;
+    int round_out;         // 1: O is rounded and stored as bf16 (out reinterpreted as uint16)
 };
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);

@@ -14,9 +14,16 @@
 
 using namespace dfl;
 
+// context keys per attention split (64-key tiles); the split count is capped at 64
+#ifndef DFL_ATTN_KEYS
+#define DFL_ATTN_KEYS 64
+#endif
+
 namespace {
 
 std::atomic<uint64_t> g_invocations{0};
+std::atomic<void*> g_trace_start{nullptr};
+std::atomic<void*> g_trace_stop{nullptr};
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -134,12 +141,24 @@ WeightPtr wptr(const dflash_weight& w) {
 
 int nsplit_for(int cap, int gamma) {
     const int T = cap + gamma;
-    int ns = (T + 63) / 64;
+    int ns = (T + DFL_ATTN_KEYS - 1) / DFL_ATTN_KEYS;
     return ns < 1 ? 1 : (ns > 64 ? 64 : ns);
 }
 
 int rpw_for(int N) { return N >= 16384 ? 4 : (N >= 2048 ? 2 : 1); }
-int lm_nblocks(int V) { return (V + 15) / 16; }  // LM head runs 4 rows per wavefront
+// workgroup cap of the per-layer projections (row tiles beyond it are looped over)
+#ifndef DFL_SMALL_WGS
+#define DFL_SMALL_WGS 512
+#endif
+// LM-head workgroups; each loops over row tiles of 16 vocabulary rows
+#ifndef DFL_LM_WGS
+#define DFL_LM_WGS 512
+#endif
+constexpr int kLmWgs = DFL_LM_WGS;
+// one argmax partial per LM-head workgroup; the head runs 4 rows per wavefront
+int lm_nblocks(int V) { return (V + 15) / 16 < kLmWgs ? (V + 15) / 16 : kLmWgs; }
+// split-K of the context projection for few rows: K ranges of at most 2048
+int ctx_splits(const dflash_dims& d) { return (d.m * d.H + 2047) / 2048; }
 
 struct Ws {
     float* hd;
@@ -150,6 +169,7 @@ struct Ws {
     float* y;
     float* lmv;
     int32_t* lmi;
+    float* ctxp;   // split-K partials of the context projection [splits][B*(gamma+1)][d]
     size_t total;
     int nsplit;
 };
@@ -174,6 +194,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     const size_t nb = lm_nblocks(d.V);
     const size_t o_lmv = take(rows * nb * 4);
     const size_t o_lmi = take(rows * nb * 4);
+    const size_t o_ctxp = take((size_t)ctx_splits(d) * B * (d.gamma + 1) * d.d * 4);
     w.total = off;
     char* c = static_cast<char*>(base);
     if (c) {
@@ -185,6 +206,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
         w.y = reinterpret_cast<float*>(c + o_y);
         w.lmv = reinterpret_cast<float*>(c + o_lmv);
         w.lmi = reinterpret_cast<int32_t*>(c + o_lmi);
+        w.ctxp = reinterpret_cast<float*>(c + o_ctxp);
     }
     return w;
 }
@@ -199,6 +221,8 @@ GemvParams base_params(const dflash_dims& d) {
     p.gain_f32 = d.wdtype == DFLASH_F32 ? 1 : 0;
     p.eps = d.eps;
     p.round_out = d.wdtype == DFLASH_F32 ? 0 : 1;
+    p.src_f32 = d.wdtype == DFLASH_F32 ? 1 : 0;  // rounded activations travel as bf16
+    p.max_wgs = DFL_SMALL_WGS;
     return p;
 }
 
@@ -208,14 +232,19 @@ hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStr
     for (int r0 = 0; r0 < rows; r0 += maxm) {
         GemvParams q = p;
         q.M = rows - r0 < maxm ? rows - r0 : maxm;
-        if (pro == PRO_PLAIN || pro == PRO_NORM) q.x = p.x + (int64_t)r0 * p.x_ld;
+        if (pro == PRO_NORM || (pro == PRO_PLAIN && p.src_f32)) q.x = p.x + (int64_t)r0 * p.x_ld;
+        if (pro == PRO_PLAIN && !p.src_f32)
+            q.x = reinterpret_cast<const float*>(reinterpret_cast<const uint16_t*>(p.x) + (int64_t)r0 * p.x_ld);
         if (pro == PRO_TAPS) {
             const size_t esz = p.src_f32 ? 4 : 2;
             for (int j = 0; j < kMaxTaps; ++j)
                 if (p.taps[j]) q.taps[j] = static_cast<const char*>(p.taps[j]) + (size_t)r0 * p.tap_ld * esz;
         }
         if (pro == PRO_GATHER) q.ids = p.ids + r0;
-        if (epi == EPI_STORE || epi == EPI_RESID || epi == EPI_GATED) q.out = p.out + (int64_t)r0 * p.out_ld;
+        if (epi == EPI_RESID || (epi == EPI_STORE && !p.out_bf16) || (epi == EPI_GATED && !p.round_out))
+            q.out = p.out + (int64_t)r0 * p.out_ld;
+        if ((epi == EPI_STORE && p.out_bf16) || (epi == EPI_GATED && p.round_out))
+            q.out = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(p.out) + (int64_t)r0 * p.out_ld);
         if (epi == EPI_KV) q.row_base = p.row_base + r0;
         if (epi == EPI_BLOCKINIT) q.seq_base = p.seq_base + r0;
         if (epi == EPI_ARGMAX) {
@@ -323,6 +352,7 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
     p.N = V;
     p.K = H;
     p.rpw = 4;
+    p.max_wgs = kLmWgs;
     p.taps[0] = y;
     p.tap_ld = H;
     p.H = H;
@@ -330,7 +360,17 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
     p.nblocks = lm_nblocks(V);
     p.part_val = pv;
     p.part_idx = pi;
+    void* ev0 = g_trace_start.load();
+    void* ev1 = g_trace_stop.load();
+    bool trace = ev0 && ev1;
+    if (trace) {
+        // a capturing stream cannot keep timing records: trace eager launches only
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) trace = false;
+    }
+    if (trace) DFL_HIP(hipEventRecord(static_cast<hipEvent_t>(ev0), s));
     DFL_HIP(gemv_rows(wtype_of(E.dtype), PRO_TAPS, EPI_ARGMAX, p, rows, s));
+    if (trace) DFL_HIP(hipEventRecord(static_cast<hipEvent_t>(ev1), s));
     DFL_HIP(launch_argmax_merge(pv, pi, p.nblocks, rows, ids, maxl, s));
     return DFLASH_OK;
 }
@@ -364,10 +404,18 @@ const char* dflash_status_string(int status) {
 
 uint64_t dflash_invocations(void) { return g_invocations.load(); }
 
+void dflash_trace_head_events(void* start, void* stop) {
+    if (start && stop) {
+        g_trace_start.store(start);
+        g_trace_stop.store(stop);
+    } else {
+        g_trace_start.store(nullptr);
+        g_trace_stop.store(nullptr);
+    }
+}
+
 int dflash_context_project(const dflash_model* M, const void* const* taps, int64_t tap_ld, int32_t n, float* h_ctx,
                            void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     DFL_TRY(check_model(M));
     const dflash_dims& d = M->dims;
     if (n < 0 || !taps || (n > 0 && !h_ctx) || tap_ld < d.H) return DFLASH_EINVAL;
@@ -390,8 +438,23 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
     p.out = h_ctx;
     p.out_ld = d.d;
     p.round_out = 0;  // P stays fp32; the norm follows
-    DFL_HIP(gemv_rows(wtype_of(d.wdtype), PRO_TAPS, EPI_STORE, p, n, s, 1, 32));
-    DFL_HIP(launch_rownorm(h_ctx, n, d.d, M->ctx_norm, d.wdtype == DFLASH_F32, d.eps, s));
+    const int splits = ctx_splits(d);
+    const size_t part_bytes = (size_t)splits * n * d.d * 4;
+    if (n <= 8 && splits > 1 && ws && ws_bytes >= part_bytes) {
+        // few rows: split the long reduction over more workgroups; partials in ws
+        p.rpw = 4;
+        p.ksplit = splits;
+        p.kslice = (p.K + splits - 1) / splits;
+        p.kslice = (p.kslice + 511) / 512 * 512;
+        p.out = static_cast<float*>(ws);
+        p.split_stride = (int64_t)n * d.d;
+        DFL_HIP(gemv_rows(wtype_of(d.wdtype), PRO_TAPS, EPI_STORE, p, n, s));
+        DFL_HIP(launch_rownorm(static_cast<float*>(ws), splits, (int64_t)n * d.d, h_ctx, n, d.d, M->ctx_norm,
+                               d.wdtype == DFLASH_F32, d.eps, s));
+    } else {
+        DFL_HIP(gemv_rows(wtype_of(d.wdtype), PRO_TAPS, EPI_STORE, p, n, s, 1, 32));
+        DFL_HIP(launch_rownorm(h_ctx, 1, 0, h_ctx, n, d.d, M->ctx_norm, d.wdtype == DFLASH_F32, d.eps, s));
+    }
     g_invocations++;
     return DFLASH_OK;
 }
@@ -413,6 +476,7 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
         p.gain[i] = M->layers[i].attn_norm;
     }
     p.w_row0 = (int64_t)d.hq * d.hd;  // the K and V rows of the fused QKV matrix
+    p.max_wgs = DFL_SMALL_WGS / d.nl > 0 ? DFL_SMALL_WGS / d.nl : 1;  // per layer (grid.y)
     p.N = 2 * d.hkv * d.hd;
     p.K = d.d;
     p.rpw = rpw_for(p.N);
@@ -481,7 +545,10 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
         DFL_HIP(gemv_rows(wt, PRO_GATHER, EPI_BLOCKINIT, p, B, s));
     }
     for (int i = 0; i < d.nl; ++i) DFL_TRY(run_layer(M, i, w.hd, kv, B, w, s));
-    {  // Y = bf16(bf16(RMSNorm(H; out_norm)) out_proj^T)
+    // Y = bf16(bf16(RMSNorm(H; out_norm)) out_proj^T), written straight into y_out
+    // when the caller wants it (bf16 for bf16/int4 models, fp32 for fp32 models)
+    float* y = y_out ? static_cast<float*>(y_out) : w.y;
+    {
         GemvParams p = base_params(d);
         p.w[0] = wptr(M->out_proj);
         p.N = d.H;
@@ -490,17 +557,13 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
         p.x = w.hd;
         p.x_ld = d.d;
         p.gain[0] = M->out_norm;
-        p.out = w.y;
+        p.out = y;
         p.out_ld = d.H;
+        p.out_bf16 = d.wdtype == DFLASH_F32 ? 0 : 1;
         DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_STORE, p, rows, s));
     }
-    DFL_TRY(lm_head(M->lm_head, w.y, 1, rows, d.H, d.V, draft_ids, max_logit, w.lmv, w.lmi, s));
-    if (y_out) {
-        if (d.wdtype == DFLASH_F32)
-            DFL_HIP(launch_copy_f32(w.y, static_cast<float*>(y_out), (int64_t)rows * d.H, s));
-        else
-            DFL_HIP(launch_to_bf16(w.y, static_cast<uint16_t*>(y_out), (int64_t)rows * d.H, s));
-    }
+    DFL_TRY(lm_head(M->lm_head, y, d.wdtype == DFLASH_F32, rows, d.H, d.V, draft_ids, max_logit, w.lmv, w.lmi,
+                    s));
     g_invocations++;
     return DFLASH_OK;
 }

@@ -1,12 +1,21 @@
 // Skinny GEMV family for the drafter projections (see gemv.hpp for the modes).
 //
-// Work split: a workgroup of 4 wavefronts owns 4*RPW consecutive weight rows
-// (for the gated FFN: 2*RPW gate/up row pairs) and reads each of them exactly
-// once over the full K range. Lane l of a wavefront reads the 16-byte chunk
-// at k = l*EPL + 64*EPL*i of each of its rows, so a wavefront instruction
-// covers one contiguous 1 KiB (bf16) or 512 B (int4) run of a row. The
-// activation rows are staged in LDS once per K chunk and read back as 16-byte
-// vectors that match the weight chunk lane by lane.
+// Work split: a workgroup of 4 wavefronts owns a tile of 4*RPW consecutive
+// weight rows (for the gated FFN: 2*RPW gate/up row pairs) and reads each of
+// them exactly once over its K range. Lane l of a wavefront reads the 16-byte
+// chunk at k = l*EPL + 64*EPL*i of each of its rows, so one wavefront
+// instruction covers a contiguous 1 KiB (bf16) or 512 B (int4) run of a row.
+// The activation rows are staged once per workgroup in LDS (in K chunks when
+// the range is long) and read back as 16-byte vectors matching the weight
+// chunk lane by lane. When the K range fits one chunk, a workgroup loops over
+// several row tiles (persistent tiles) and stages the activations only once.
+//
+// Latency: the first PF weight iterations of a tile are loaded into registers
+// before the activation prologue runs (and, across persistent tiles, before
+// the previous tile's reduction), so the HBM latency overlaps the staging.
+//
+// Split K (grid.z): each range writes its partial sums to its own slice of
+// the output; the consumer adds the slices in a fixed order.
 //
 // Products: bf16 weights use v_dot2 (two bf16 products per instruction into
 // an fp32 accumulator); int4 weights are turned into bf16 (128 + q) pairs with
@@ -19,10 +28,113 @@
 
 namespace dfl {
 
+constexpr int kRegNormMaxK = 2048;  // rows up to this length take the register RMSNorm prologue
+
+// weight iterations kept in flight per lane (register ring), for 1-2 and 4 rows per wavefront
+#ifndef DFL_PF
+#define DFL_PF 4
+#endif
+#ifndef DFL_PF_WIDE
+#define DFL_PF_WIDE 2
+#endif
+
 template <int WT> struct WTraits;
 template <> struct WTraits<W_F32> { typedef float X; static constexpr int EPL = 8; };
 template <> struct WTraits<W_BF16> { typedef uint16_t X; static constexpr int EPL = 8; };
 template <> struct WTraits<W_I4> { typedef uint16_t X; static constexpr int EPL = 32; };
+
+// one lane's weight chunk of one row
+template <int WT> struct WChunk;
+template <> struct WChunk<W_BF16> { uint4 v; };
+template <> struct WChunk<W_F32> { float4 a, b; };
+template <> struct WChunk<W_I4> { uint4 c; float s, b; };
+
+template <int WT>
+__device__ __forceinline__ void wload(WChunk<WT>& w, const WeightPtr& W, int64_t row, int K, int k) {
+    if constexpr (WT == W_BF16) {
+        w.v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W.data) + row * K + k);
+    } else if constexpr (WT == W_F32) {
+        const float* src = static_cast<const float*>(W.data) + row * K + k;
+        w.a = *reinterpret_cast<const float4*>(src);
+        w.b = *reinterpret_cast<const float4*>(src + 4);
+    } else {
+        w.c = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(W.data) + row * (K / 8) + k / 8);
+        const int64_t g = row * (K / 64) + k / 64;
+        w.s = bf16_bits_to_f32(W.scales[g]);
+        w.b = bf16_bits_to_f32(W.biases[g]);
+    }
+}
+
+// acc[r][m] += chunk(r) . x[m][kl .. kl+EPL)
+template <int WT, int MAXM, int RPW>
+__device__ __forceinline__ void wfma(const WChunk<WT> (&w)[RPW], const typename WTraits<WT>::X* xs, int KC, int kl,
+                                     const float* xsum, float (&acc)[RPW][MAXM]) {
+    if constexpr (WT == W_BF16) {
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)m * KC + kl);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                float a = acc[r][m];
+                a = dot2_bf16(w[r].v.x, xv.x, a);
+                a = dot2_bf16(w[r].v.y, xv.y, a);
+                a = dot2_bf16(w[r].v.z, xv.z, a);
+                a = dot2_bf16(w[r].v.w, xv.w, a);
+                acc[r][m] = a;
+            }
+        }
+    } else if constexpr (WT == W_F32) {
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const float* xr = xs + (size_t)m * KC + kl;
+            const float4 x0 = *reinterpret_cast<const float4*>(xr);
+            const float4 x1 = *reinterpret_cast<const float4*>(xr + 4);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                float a = acc[r][m];
+                a = fmaf(w[r].a.x, x0.x, a); a = fmaf(w[r].a.y, x0.y, a);
+                a = fmaf(w[r].a.z, x0.z, a); a = fmaf(w[r].a.w, x0.w, a);
+                a = fmaf(w[r].b.x, x1.x, a); a = fmaf(w[r].b.y, x1.y, a);
+                a = fmaf(w[r].b.z, x1.z, a); a = fmaf(w[r].b.w, x1.w, a);
+                acc[r][m] = a;
+            }
+        }
+    } else {
+        uint32_t pr[RPW][16];
+        float bi[RPW];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            bi[r] = w[r].b - 128.0f * w[r].s;
+            const uint32_t words[4] = {w[r].c.x, w[r].c.y, w[r].c.z, w[r].c.w};
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pr[r][4 * wd + j] = ((words[wd] >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+        }
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            float d[RPW];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) d[r] = 0.f;
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+                const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)m * KC + kl + 8 * wd);
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) {
+                    float a = d[r];
+                    a = dot2_bf16(pr[r][4 * wd + 0], xv.x, a);
+                    a = dot2_bf16(pr[r][4 * wd + 1], xv.y, a);
+                    a = dot2_bf16(pr[r][4 * wd + 2], xv.z, a);
+                    a = dot2_bf16(pr[r][4 * wd + 3], xv.w, a);
+                    d[r] = a;
+                }
+            }
+            const float xsm = xsum[m * (KC / 32) + kl / 32];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) acc[r][m] += w[r].s * d[r] + bi[r] * xsm;
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // activation loaders: 8 consecutive elements k..k+7 of activation row m
@@ -62,7 +174,10 @@ __device__ __forceinline__ void load_x8(const GemvParams& p, int layer, int m, i
         return;
     }
     if constexpr (PRO == PRO_PLAIN) {
-        load8_f32(p.x + (int64_t)m * p.x_ld + k, v);
+        if (p.src_f32)
+            load8_f32(p.x + (int64_t)m * p.x_ld + k, v);
+        else
+            load8_bf16(reinterpret_cast<const uint16_t*>(p.x) + (int64_t)m * p.x_ld + k, v);
     } else if constexpr (PRO == PRO_NORM) {
         load8_f32(p.x + (int64_t)m * p.x_ld + k, v);
         const float r = rinv[m];
@@ -81,277 +196,359 @@ __device__ __forceinline__ void load_x8(const GemvParams& p, int layer, int m, i
     }
 }
 
+// stage activation rows [0, MAXM) x [kc0, kc0 + kw) into LDS
+template <int WT, int PRO, int MAXM>
+__device__ __forceinline__ void stage(const GemvParams& p, int layer, int kc0, int kw, int KC,
+                                      typename WTraits<WT>::X* xs, float* xsum, const float* rinv) {
+    const int tid = threadIdx.x;
+    if constexpr (WT == W_I4) {
+        const int units = kw / 32;
+        for (int u = tid; u < MAXM * units; u += kBlock) {
+            const int m = u / units, c = u - m * units;
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[8];
+                load_x8<PRO>(p, layer, m, kc0 + 32 * c + 8 * q, rinv, v);
+                uint32_t b[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    b[j] = f32_to_bf16_bits(v[j]);
+                    s += bf16_bits_to_f32(b[j]);
+                }
+                // pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7): the nibble pairing of a code word
+                uint4 o;
+                o.x = b[0] | (b[4] << 16);
+                o.y = b[1] | (b[5] << 16);
+                o.z = b[2] | (b[6] << 16);
+                o.w = b[3] | (b[7] << 16);
+                *reinterpret_cast<uint4*>(xs + (size_t)m * KC + 32 * c + 8 * q) = o;
+            }
+            xsum[m * (KC / 32) + c] = s;
+        }
+    } else {
+        const int units = kw / 8;
+#pragma unroll 4
+        for (int u = tid; u < MAXM * units; u += kBlock) {
+            const int m = u / units, c = u - m * units;
+            float v[8];
+            load_x8<PRO>(p, layer, m, kc0 + 8 * c, rinv, v);
+            if constexpr (WT == W_BF16) {
+                uint4 o;
+                o.x = pack_bf16x2(v[0], v[1]);
+                o.y = pack_bf16x2(v[2], v[3]);
+                o.z = pack_bf16x2(v[4], v[5]);
+                o.w = pack_bf16x2(v[6], v[7]);
+                *reinterpret_cast<uint4*>(xs + (size_t)m * KC + 8 * c) = o;
+            } else {
+                float* d = xs + (size_t)m * KC + 8 * c;
+                *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            }
+        }
+    }
+}
+
+template <int EPI, int RPW>
+__device__ __forceinline__ void tile_rows(const GemvParams& p, int tile, int wave, int64_t (&rows)[RPW]) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        int64_t row;
+        bool ok;
+        if constexpr (EPI == EPI_GATED) {
+            const int j = tile * 2 * RPW + wave * (RPW / 2) + r / 2;
+            ok = j < p.F;
+            row = (r & 1) ? (int64_t)p.F + j : (int64_t)j;
+        } else {
+            const int n = tile * 4 * RPW + wave * RPW + r;
+            ok = n < p.N;
+            row = n;
+        }
+        rows[r] = p.w_row0 + (ok ? row : 0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 
 template <int WT, int PRO, int EPI, int MAXM, int RPW>
 __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const int KC) {
     typedef typename WTraits<WT>::X X;
     constexpr int EPL = WTraits<WT>::EPL;
-    constexpr bool kBf = (WT != W_F32);
+    constexpr int STEP = 64 * EPL;
+    constexpr int PF = RPW >= 4 ? DFL_PF_WIDE : DFL_PF;  // weight iterations kept in flight
     extern __shared__ __align__(16) unsigned char smem[];
-    X* xs = reinterpret_cast<X*>(smem);                                     // [MAXM][KC]
-    float* xsum = reinterpret_cast<float*>(smem + (size_t)MAXM * KC * sizeof(X));  // [MAXM][KC/32]
-    float* red = xsum + (WT == W_I4 ? MAXM * (KC / 32) : 0);                // [4*RPW][MAXM]
-    float* rinv = red + 4 * RPW * MAXM;                                     // [MAXM]
+    X* xs = reinterpret_cast<X*>(smem);                                                 // [MAXM][KC]
+    float* xsum = reinterpret_cast<float*>(smem + (size_t)MAXM * KC * sizeof(X));       // [MAXM][KC/32]
+    float* red = xsum + (WT == W_I4 ? MAXM * (KC / 32) : 0);                            // [4*RPW][MAXM]
+    float* rinv = red + 4 * RPW * MAXM;                                                 // [MAXM]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int layer = blockIdx.y;
     const WeightPtr W = p.w[layer];
     const int K = p.K;
+    const int kb = blockIdx.z * p.kslice;
+    const int ke = min(K, kb + p.kslice);
+    const int kw0 = min(KC, ke - kb);
+    const bool single = (ke - kb) <= KC;
+    const int ntiles = (EPI == EPI_GATED) ? (p.F + 2 * RPW - 1) / (2 * RPW) : (p.N + 4 * RPW - 1) / (4 * RPW);
 
-    // weight rows of this wavefront
+    int tile = blockIdx.x;
     int64_t rows[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-        int64_t row;
-        bool ok;
-        if constexpr (EPI == EPI_GATED) {
-            const int j = blockIdx.x * 2 * RPW + wave * (RPW / 2) + r / 2;
-            ok = j < p.F;
-            row = (r & 1) ? (int64_t)p.F + j : (int64_t)j;
-        } else {
-            const int n = blockIdx.x * 4 * RPW + wave * RPW + r;
-            ok = n < p.N;
-            row = n;
-        }
-        rows[r] = p.w_row0 + (ok ? row : 0);
-    }
+    tile_rows<EPI, RPW>(p, tile, wave, rows);
 
-    if constexpr (PRO == PRO_NORM) {
-        for (int m = wave; m < p.M; m += 4) {
-            const float* xr = p.x + (int64_t)m * p.x_ld;
-            float s = 0.f;
-            for (int k = lane * 4; k < K; k += 256) {
-                const float4 a = *reinterpret_cast<const float4*>(xr + k);
-                s += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
-            }
-            s = wave_sum(s);
-            if (lane == 0) rinv[m] = 1.0f / sqrtf(s / (float)K + p.eps);
-        }
-        __syncthreads();
-    }
+    // iterations of this lane in chunk 0
+    const int nit = (kw0 > lane * EPL) ? (kw0 - lane * EPL + STEP - 1) / STEP : 0;
 
-    float acc[RPW][MAXM];
+    // first PF weight iterations of this tile, in flight before the prologue
+    WChunk<WT> pre[PF][RPW];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
+    for (int i = 0; i < PF; ++i) {
+        if (i < nit) {
 #pragma unroll
-        for (int m = 0; m < MAXM; ++m) acc[r][m] = 0.f;
-
-    for (int kc0 = 0; kc0 < K; kc0 += KC) {
-        const int kw = min(KC, K - kc0);
-        __syncthreads();
-        // ---- stage activation rows [0, MAXM) x [kc0, kc0+kw) into LDS
-        if constexpr (WT == W_I4) {
-            const int units = kw / 32;
-            for (int u = tid; u < MAXM * units; u += kBlock) {
-                const int m = u / units, c = u - m * units;
-                float s = 0.f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float v[8];
-                    load_x8<PRO>(p, layer, m, kc0 + 32 * c + 8 * q, rinv, v);
-                    uint32_t b[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        b[j] = f32_to_bf16_bits(v[j]);
-                        s += bf16_bits_to_f32(b[j]);
-                    }
-                    // pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7): the nibble pairing of a code word
-                    uint4 o;
-                    o.x = b[0] | (b[4] << 16);
-                    o.y = b[1] | (b[5] << 16);
-                    o.z = b[2] | (b[6] << 16);
-                    o.w = b[3] | (b[7] << 16);
-                    *reinterpret_cast<uint4*>(xs + (size_t)m * KC + 32 * c + 8 * q) = o;
-                }
-                xsum[m * (KC / 32) + c] = s;
-            }
-        } else {
-            const int units = kw / 8;
-            for (int u = tid; u < MAXM * units; u += kBlock) {
-                const int m = u / units, c = u - m * units;
-                float v[8];
-                load_x8<PRO>(p, layer, m, kc0 + 8 * c, rinv, v);
-                if constexpr (kBf) {
-                    uint4 o;
-                    o.x = pack_bf16x2(v[0], v[1]);
-                    o.y = pack_bf16x2(v[2], v[3]);
-                    o.z = pack_bf16x2(v[4], v[5]);
-                    o.w = pack_bf16x2(v[6], v[7]);
-                    *reinterpret_cast<uint4*>(xs + (size_t)m * KC + 8 * c) = o;
-                } else {
-                    float* d = reinterpret_cast<float*>(xs) + (size_t)m * KC + 8 * c;
-                    *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
-                    *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- stream the weight rows over this chunk
-        for (int k = kc0 + lane * EPL; k < kc0 + kw; k += 64 * EPL) {
-            const int kl = k - kc0;
-            if constexpr (WT == W_BF16) {
-                uint4 wv[RPW];
-#pragma unroll
-                for (int r = 0; r < RPW; ++r)
-                    wv[r] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W.data) + rows[r] * K + k);
-#pragma unroll
-                for (int m = 0; m < MAXM; ++m) {
-                    const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)m * KC + kl);
-#pragma unroll
-                    for (int r = 0; r < RPW; ++r) {
-                        float a = acc[r][m];
-                        a = dot2_bf16(wv[r].x, xv.x, a);
-                        a = dot2_bf16(wv[r].y, xv.y, a);
-                        a = dot2_bf16(wv[r].z, xv.z, a);
-                        a = dot2_bf16(wv[r].w, xv.w, a);
-                        acc[r][m] = a;
-                    }
-                }
-            } else if constexpr (WT == W_F32) {
-                float4 w0[RPW], w1[RPW];
-#pragma unroll
-                for (int r = 0; r < RPW; ++r) {
-                    const float* src = static_cast<const float*>(W.data) + rows[r] * K + k;
-                    w0[r] = *reinterpret_cast<const float4*>(src);
-                    w1[r] = *reinterpret_cast<const float4*>(src + 4);
-                }
-#pragma unroll
-                for (int m = 0; m < MAXM; ++m) {
-                    const float* xr = reinterpret_cast<const float*>(xs) + (size_t)m * KC + kl;
-                    const float4 x0 = *reinterpret_cast<const float4*>(xr);
-                    const float4 x1 = *reinterpret_cast<const float4*>(xr + 4);
-#pragma unroll
-                    for (int r = 0; r < RPW; ++r) {
-                        float a = acc[r][m];
-                        a = fmaf(w0[r].x, x0.x, a); a = fmaf(w0[r].y, x0.y, a);
-                        a = fmaf(w0[r].z, x0.z, a); a = fmaf(w0[r].w, x0.w, a);
-                        a = fmaf(w1[r].x, x1.x, a); a = fmaf(w1[r].y, x1.y, a);
-                        a = fmaf(w1[r].z, x1.z, a); a = fmaf(w1[r].w, x1.w, a);
-                        acc[r][m] = a;
-                    }
-                }
-            } else {  // W_I4
-                uint32_t pr[RPW][16];
-                float sc[RPW], bi[RPW];
-#pragma unroll
-                for (int r = 0; r < RPW; ++r) {
-                    const uint4 cw = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(W.data) +
-                                                                     rows[r] * (K / 8) + k / 8);
-                    const int64_t g = rows[r] * (K / 64) + k / 64;
-                    sc[r] = bf16_bits_to_f32(W.scales[g]);
-                    bi[r] = bf16_bits_to_f32(W.biases[g]) - 128.0f * sc[r];
-                    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-                    for (int wd = 0; wd < 4; ++wd)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            pr[r][4 * wd + j] = ((words[wd] >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
-                }
-#pragma unroll
-                for (int m = 0; m < MAXM; ++m) {
-                    float d[RPW];
-#pragma unroll
-                    for (int r = 0; r < RPW; ++r) d[r] = 0.f;
-#pragma unroll
-                    for (int wd = 0; wd < 4; ++wd) {
-                        const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)m * KC + kl + 8 * wd);
-#pragma unroll
-                        for (int r = 0; r < RPW; ++r) {
-                            float a = d[r];
-                            a = dot2_bf16(pr[r][4 * wd + 0], xv.x, a);
-                            a = dot2_bf16(pr[r][4 * wd + 1], xv.y, a);
-                            a = dot2_bf16(pr[r][4 * wd + 2], xv.z, a);
-                            a = dot2_bf16(pr[r][4 * wd + 3], xv.w, a);
-                            d[r] = a;
-                        }
-                    }
-                    const float xsm = xsum[m * (KC / 32) + kl / 32];
-#pragma unroll
-                    for (int r = 0; r < RPW; ++r) acc[r][m] += sc[r] * d[r] + bi[r] * xsm;
-                }
-            }
+            for (int r = 0; r < RPW; ++r) wload<WT>(pre[i][r], W, rows[r], K, kb + lane * EPL + i * STEP);
         }
     }
 
-    // ---- reduce across the wavefront; sums land in red[wave*RPW + r][m]
-    {
-        constexpr int NV = RPW * MAXM;
-        float vals[NV];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-            for (int m = 0; m < MAXM; ++m) vals[r * MAXM + m] = acc[r][m];
-        const float tot = wave_sum_many<NV>(vals, lane);
-        const int vi = wave_sum_many_index<NV>(lane);
-        constexpr int SPAN = (NV >= 64) ? 1 : 64 / NV;
-        if ((lane % SPAN) == 0) red[(wave * RPW) * MAXM + vi] = tot;
-    }
-    __syncthreads();
-
-    // ---- epilogue
-    if constexpr (EPI == EPI_ARGMAX) {
-        if (tid < p.M) {
-            float best = -INFINITY;
-            int bi = 0x7fffffff;
-            for (int u = 0; u < 4 * RPW; ++u) {
-                const int n = blockIdx.x * 4 * RPW + u;
-                if (n < p.N) argmax_pick(best, bi, red[u * MAXM + tid], n);
-            }
-            p.part_val[(int64_t)tid * p.nblocks + blockIdx.x] = best;
-            p.part_idx[(int64_t)tid * p.nblocks + blockIdx.x] = bi;
-        }
-    } else if constexpr (EPI == EPI_GATED) {
-        for (int t = tid; t < 2 * RPW * MAXM; t += kBlock) {
-            const int q = t / MAXM, m = t - q * MAXM;
-            const int j = blockIdx.x * 2 * RPW + q;
-            if (m >= p.M || j >= p.F) continue;
-            const float g = red[(2 * q) * MAXM + m], u = red[(2 * q + 1) * MAXM + m];
-            float y = (p.act == 0 ? gelu_tanh(g) : silu(g)) * u;
-            if (p.round_out) y = round_bf16(y);
-            p.out[(int64_t)m * p.out_ld + j] = y;
-        }
-    } else {
-        for (int t = tid; t < 4 * RPW * MAXM; t += kBlock) {
-            const int u = t / MAXM, m = t - u * MAXM;
-            const int n = blockIdx.x * 4 * RPW + u;
-            if (m >= p.M || n >= p.N) continue;
-            const float y = red[t];
-            if constexpr (EPI == EPI_STORE) {
-                p.out[(int64_t)m * p.out_ld + n] = p.round_out ? round_bf16(y) : y;
-            } else if constexpr (EPI == EPI_RESID) {
-                p.out[(int64_t)m * p.out_ld + n] += y;
-            } else if constexpr (EPI == EPI_BLOCKINIT) {
-                const int64_t b = p.seq_base + m;
-                const int d = p.N;
-                float* hb = p.out + b * (int64_t)p.gamma * d;
-                hb[n] = y + load_gain(p.block_pos, p.gain_f32, n);
-                for (int kk = 1; kk < p.gamma; ++kk)
-                    hb[(int64_t)kk * d + n] = load_gain(p.mask_emb, p.gain_f32, (kk - 1) * d + n) +
-                                              load_gain(p.block_pos, p.gain_f32, kk * d + n);
-            } else if constexpr (EPI == EPI_KV) {
-                const int gm = p.row_base + m;
-                int b = 0;
+    // EPI_KV: sequence and cache position of each activation row, resolved once
+    int* meta_b = reinterpret_cast<int*>(rinv + MAXM);
+    int* meta_pos = meta_b + MAXM;
+    if constexpr (EPI == EPI_KV) {
+        if (tid < MAXM) {
+            int b = 0, pos = -1;
+            if (tid < p.M) {
+                const int gm = p.row_base + tid;
                 while (b + 1 < p.B && p.row_offsets[b + 1] <= gm) ++b;
                 const int rows_b = p.row_offsets[b + 1] - p.row_offsets[b];
                 const int i = gm - p.row_offsets[b];
                 const int cnt = p.counts ? min(p.counts[b], rows_b) : rows_b;
-                const int pos = p.len[b] + i;
-                if (i < cnt && pos < p.cap) {
-                    const int kvw = p.hkv * p.hd;
-                    const int which = n / kvw;
-                    const int head = (n - which * kvw) / p.hd;
-                    const int dim = n - which * kvw - head * p.hd;
-                    const int64_t off = (int64_t)layer * p.layer_stride +
-                                        (((int64_t)b * p.hkv + head) * p.cap + pos) * p.hd + dim;
-                    void* base = which ? p.vcache : p.kcache;
-                    if (p.kv_f32)
-                        static_cast<float*>(base)[off] = y;
-                    else
-                        static_cast<uint16_t*>(base)[off] = (uint16_t)f32_to_bf16_bits(y);
+                pos = p.len[b] + i;
+                if (!(i >= 0 && i < cnt && pos < p.cap)) pos = -1;
+            }
+            meta_b[tid] = b;
+            meta_pos[tid] = pos;
+        }
+    }
+
+    constexpr bool kRegNorm = (PRO == PRO_NORM) && (WT != W_I4) && (MAXM == 8);
+    if (kRegNorm && single && K <= kRegNormMaxK) {
+        // one round trip: each wavefront loads whole rows into registers (the
+        // gain goes to LDS meanwhile), reduces the sum of squares with
+        // shuffles and writes the normalised, rounded row to LDS
+        float* gl = reinterpret_cast<float*>(meta_b + 2 * MAXM);  // [K] gain
+        constexpr int RW = MAXM / 4, UM = kRegNormMaxK / 512;
+        float xr[RW][UM][8];
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            const int m = wave + 4 * j;
+#pragma unroll
+            for (int u = 0; u < UM; ++u) {
+                const int k = lane * 8 + u * 512;
+                if (m < p.M && k < K) {
+                    load8_f32(p.x + (int64_t)m * p.x_ld + k, xr[j][u]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xr[j][u][e] = 0.f;
                 }
             }
+        }
+        for (int k = tid; k < K; k += kBlock) gl[k] = load_gain(p.gain[layer], p.gain_f32, k);
+        float rr[RW];
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            float ss = 0.f;
+#pragma unroll
+            for (int u = 0; u < UM; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += xr[j][u][e] * xr[j][u][e];
+            ss = wave_sum(ss);
+            rr[j] = 1.0f / sqrtf(ss / (float)K + p.eps);
+        }
+        __syncthreads();  // gain in LDS
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            const int m = wave + 4 * j;
+#pragma unroll
+            for (int u = 0; u < UM; ++u) {
+                const int k = lane * 8 + u * 512;
+                if (k < K) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = (m < p.M) ? xr[j][u][e] * rr[j] * gl[k + e] : 0.f;
+                    if constexpr (WT == W_BF16) {
+                        uint4 o;
+                        o.x = pack_bf16x2(v[0], v[1]);
+                        o.y = pack_bf16x2(v[2], v[3]);
+                        o.z = pack_bf16x2(v[4], v[5]);
+                        o.w = pack_bf16x2(v[6], v[7]);
+                        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(xs) + (size_t)m * KC + k) = o;
+                    } else {
+                        float* d = reinterpret_cast<float*>(xs) + (size_t)m * KC + k;
+                        *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+                        *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    } else {
+        if constexpr (PRO == PRO_NORM) {
+            for (int m = wave; m < p.M; m += 4) {
+                const float* xr = p.x + (int64_t)m * p.x_ld;
+                float s = 0.f;
+                for (int k = lane * 4; k < K; k += 256) {
+                    const float4 a = *reinterpret_cast<const float4*>(xr + k);
+                    s += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+                }
+                s = wave_sum(s);
+                if (lane == 0) rinv[m] = 1.0f / sqrtf(s / (float)K + p.eps);
+            }
+            __syncthreads();
+        }
+        stage<WT, PRO, MAXM>(p, layer, kb, kw0, KC, xs, xsum, rinv);
+        __syncthreads();
+    }
+
+    // per-workgroup running argmax over all of its tiles
+    float amax = -INFINITY;
+    int aidx = 0x7fffffff;
+
+    while (true) {
+        float acc[RPW][MAXM];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) acc[r][m] = 0.f;
+
+        // chunk 0: a ring of PF register slots keeps PF weight iterations in
+        // flight; the slot just consumed is refilled with iteration it + PF
+        for (int base = 0; base < nit; base += PF) {
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                const int it = base + i;
+                if (it < nit) {
+                    wfma<WT, MAXM, RPW>(pre[i], xs, KC, lane * EPL + it * STEP, xsum, acc);
+                    const int nx = it + PF;
+                    if (nx < nit) {
+#pragma unroll
+                        for (int r = 0; r < RPW; ++r) wload<WT>(pre[i][r], W, rows[r], K, kb + lane * EPL + nx * STEP);
+                    }
+                }
+            }
+        }
+        // further chunks (long K ranges; such launches have one tile per workgroup)
+        for (int kc0 = kb + kw0; kc0 < ke; kc0 += KC) {
+            const int kw = min(KC, ke - kc0);
+            __syncthreads();
+            stage<WT, PRO, MAXM>(p, layer, kc0, kw, KC, xs, xsum, rinv);
+            __syncthreads();
+            for (int k = kc0 + lane * EPL; k < kc0 + kw; k += STEP) {
+                WChunk<WT> w[RPW];
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) wload<WT>(w[r], W, rows[r], K, k);
+                wfma<WT, MAXM, RPW>(w, xs, KC, k - kc0, xsum, acc);
+            }
+        }
+
+        // next tile's first iterations go out before this tile's reduction
+        const int next = tile + (int)gridDim.x;
+        const bool more = single && next < ntiles;
+        if (more) {
+            tile_rows<EPI, RPW>(p, next, wave, rows);
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                if (i < nit) {
+#pragma unroll
+                    for (int r = 0; r < RPW; ++r) wload<WT>(pre[i][r], W, rows[r], K, kb + lane * EPL + i * STEP);
+                }
+            }
+        }
+
+        // ---- reduce across the wavefront; sums land in red[wave*RPW + r][m]
+        {
+            constexpr int NV = RPW * MAXM;
+            float vals[NV];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+#pragma unroll
+                for (int m = 0; m < MAXM; ++m) vals[r * MAXM + m] = acc[r][m];
+            const float tot = wave_sum_many<NV>(vals, lane);
+            const int vi = wave_sum_many_index<NV>(lane);
+            constexpr int SPAN = (NV >= 64) ? 1 : 64 / NV;
+            if ((lane % SPAN) == 0) red[(wave * RPW) * MAXM + vi] = tot;
+        }
+        __syncthreads();
+
+        // ---- epilogue of this tile
+        if constexpr (EPI == EPI_ARGMAX) {
+            if (tid < p.M) {
+                for (int u = 0; u < 4 * RPW; ++u) {
+                    const int n = tile * 4 * RPW + u;
+                    if (n < p.N) argmax_pick(amax, aidx, red[u * MAXM + tid], n);
+                }
+            }
+        } else if constexpr (EPI == EPI_GATED) {
+            for (int t = tid; t < 2 * RPW * MAXM; t += kBlock) {
+                const int m = t / (2 * RPW), q = t - m * (2 * RPW);
+                const int j = tile * 2 * RPW + q;
+                if (m >= p.M || j >= p.F) continue;
+                const float g = red[(2 * q) * MAXM + m], u = red[(2 * q + 1) * MAXM + m];
+                const float y = (p.act == 0 ? gelu_tanh(g) : silu(g)) * u;
+                if (p.round_out)
+                    reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.out_ld + j] = (uint16_t)f32_to_bf16_bits(y);
+                else
+                    p.out[(int64_t)m * p.out_ld + j] = y;
+            }
+        } else {
+            for (int t = tid; t < 4 * RPW * MAXM; t += kBlock) {
+                const int m = t / (4 * RPW), u = t - m * (4 * RPW);
+                const int n = tile * 4 * RPW + u;
+                if (m >= p.M || n >= p.N) continue;
+                const float y = red[u * MAXM + m];
+                if constexpr (EPI == EPI_STORE) {
+                    if (p.out_bf16) {
+                        uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (int64_t)blockIdx.z * p.split_stride;
+                        o[(int64_t)m * p.out_ld + n] = (uint16_t)f32_to_bf16_bits(y);
+                    } else {
+                        float* o = p.out + (int64_t)blockIdx.z * p.split_stride;
+                        o[(int64_t)m * p.out_ld + n] = p.round_out ? round_bf16(y) : y;
+                    }
+                } else if constexpr (EPI == EPI_RESID) {
+                    p.out[(int64_t)m * p.out_ld + n] += y;
+                } else if constexpr (EPI == EPI_BLOCKINIT) {
+                    const int64_t b = p.seq_base + m;
+                    const int d = p.N;
+                    float* hb = p.out + b * (int64_t)p.gamma * d;
+                    hb[n] = y + load_gain(p.block_pos, p.gain_f32, n);
+                    for (int kk = 1; kk < p.gamma; ++kk)
+                        hb[(int64_t)kk * d + n] = load_gain(p.mask_emb, p.gain_f32, (kk - 1) * d + n) +
+                                                  load_gain(p.block_pos, p.gain_f32, kk * d + n);
+                } else if constexpr (EPI == EPI_KV) {
+                    const int b = meta_b[m], pos = meta_pos[m];
+                    if (pos >= 0) {
+                        const int kvw = p.hkv * p.hd;
+                        const int which = n / kvw;
+                        const int head = (n - which * kvw) / p.hd;
+                        const int dim = n - which * kvw - head * p.hd;
+                        const int64_t off = (int64_t)layer * p.layer_stride +
+                                            (((int64_t)b * p.hkv + head) * p.cap + pos) * p.hd + dim;
+                        void* base = which ? p.vcache : p.kcache;
+                        if (p.kv_f32)
+                            static_cast<float*>(base)[off] = y;
+                        else
+                            static_cast<uint16_t*>(base)[off] = (uint16_t)f32_to_bf16_bits(y);
+                    }
+                }
+            }
+        }
+        if (!more) break;
+        tile = next;
+        __syncthreads();  // red[] is rewritten by the next tile
+    }
+
+    if constexpr (EPI == EPI_ARGMAX) {
+        if (tid < p.M) {
+            p.part_val[(int64_t)tid * p.nblocks + blockIdx.x] = amax;
+            p.part_idx[(int64_t)tid * p.nblocks + blockIdx.x] = aidx;
         }
     }
 }
@@ -363,24 +560,29 @@ template <int WT, int PRO, int EPI, int MAXM, int RPW>
 static hipError_t launch_one(const GemvParams& p, int layers, hipStream_t s) {
     typedef typename WTraits<WT>::X X;
     const int unit = (WT == W_I4) ? 32 : 8;
+    GemvParams q = p;
+    if (q.ksplit < 1) q.ksplit = 1;
+    if (q.kslice <= 0 || q.ksplit == 1) q.kslice = q.K;
     int KC = kStageBytes / (MAXM * (int)sizeof(X));
     KC = (KC / 512) * 512;
-    if (KC >= p.K) KC = p.K;
-    KC = (KC / unit) * unit;
+    if (KC >= q.kslice) KC = q.kslice;
+    KC = (KC + unit - 1) / unit * unit;
     size_t smem = (size_t)MAXM * KC * sizeof(X) + (WT == W_I4 ? (size_t)MAXM * (KC / 32) * 4 : 0) +
-                  (size_t)4 * RPW * MAXM * 4 + (size_t)MAXM * 4;
-    int grid_x;
-    if (EPI == EPI_GATED)
-        grid_x = (p.F + 2 * RPW - 1) / (2 * RPW);
-    else
-        grid_x = (p.N + 4 * RPW - 1) / (4 * RPW);
-    dim3 grid(grid_x, layers);
+                  (size_t)4 * RPW * MAXM * 4 + (size_t)MAXM * 4 + (size_t)2 * MAXM * 4;
+    if (PRO == PRO_NORM && WT != W_I4 && MAXM == 8) smem += (size_t)kRegNormMaxK * 4;
+    const int ntiles = (EPI == EPI_GATED) ? (q.F + 2 * RPW - 1) / (2 * RPW) : (q.N + 4 * RPW - 1) / (4 * RPW);
+    int grid_x = ntiles;
+    // persistent tiles only when the K range is staged once
+    if (q.max_wgs > 0 && q.kslice <= KC && grid_x > q.max_wgs) grid_x = q.max_wgs;
+    if (EPI == EPI_ARGMAX && q.nblocks != grid_x) return hipErrorInvalidValue;  // partial buffer layout
+    dim3 grid(grid_x, layers, q.ksplit);
     // allow dynamic LDS beyond the 64 KiB default (gfx950 has 160 KiB per CU)
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&gemv_kernel<WT, PRO, EPI, MAXM, RPW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemv_kernel<WT, PRO, EPI, MAXM, RPW>), grid, dim3(kBlock), smem, s, p, KC);
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL((gemv_kernel<WT, PRO, EPI, MAXM, RPW>), grid, dim3(kBlock), smem, s, q, KC);
     return hipGetLastError();
 }
 

@@ -48,6 +48,10 @@ struct GemvParams {
     int K;               // reduction length
     int M;               // active activation rows (<= MAXM)
     int rpw;             // weight rows per wavefront (1, 2 or 4; even for EPI_GATED)
+    int ksplit;          // K ranges (grid.z); each writes its partial sums to out + z*split_stride
+    int kslice;          // K elements per range (multiple of 32)
+    int64_t split_stride;
+    int max_wgs;         // cap on workgroups; row tiles beyond it are looped over (0 = one per tile)
 
     // prologue
     const float* x;      // PRO_PLAIN / PRO_NORM: fp32 rows
@@ -58,7 +62,7 @@ struct GemvParams {
     const void* taps[kMaxTaps];    // PRO_TAPS: tap j covers k in [j*H, (j+1)*H)
     int64_t tap_ld;
     int H;
-    int src_f32;         // PRO_TAPS / PRO_GATHER source element type (1 = fp32, 0 = bf16)
+    int src_f32;         // PRO_PLAIN / PRO_TAPS source element type (1 = fp32, 0 = bf16)
     const int32_t* ids;  // PRO_GATHER: table rows
     WeightPtr table;     // PRO_GATHER: embedding table [table_rows, K]
     int table_rows;      // ids are clamped to [0, table_rows)
@@ -67,7 +71,8 @@ struct GemvParams {
     // epilogue
     float* out;
     int64_t out_ld;
-    int round_out;       // EPI_STORE / EPI_GATED: round results to bf16
+    int round_out;       // EPI_STORE / EPI_GATED: round results to bf16 (EPI_GATED then stores bf16)
+    int out_bf16;        // EPI_STORE: store bf16 values instead of fp32
     int F;               // EPI_GATED: gate rows [0, F), up rows [F, 2F)
     int act;             // EPI_GATED: 0 gelu_tanh, 1 silu
     // EPI_KV

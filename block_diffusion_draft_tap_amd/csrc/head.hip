@@ -92,17 +92,52 @@ __global__ __launch_bounds__(64) void verify_final_kernel(const float* part_val,
     }
 }
 
-__global__ __launch_bounds__(kBlock) void rownorm_kernel(float* x, int d, const void* gain, int gain_f32, float eps) {
+// dst[r] = RMSNorm(sum_z src[z][r]; gain): the split-K partials are added in
+// a fixed order (z = 0, 1, ...); dst may alias src when there is one split.
+__global__ __launch_bounds__(kBlock) void rownorm_kernel(const float* src, int nsplit, int64_t split_stride,
+                                                         float* dst, int d, const void* gain, int gain_f32,
+                                                         float eps) {
     __shared__ float sv[4];
-    float* row = x + (int64_t)blockIdx.x * d;
+    constexpr int kPer = 8;  // row elements held per thread (d <= 2048 fast path)
+    const int64_t roff = (int64_t)blockIdx.x * d;
+    float vals[kPer];
+    const bool held = d <= kPer * (int)blockDim.x;
     float s = 0.f;
-    for (int k = threadIdx.x; k < d; k += blockDim.x) s += row[k] * row[k];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int k = threadIdx.x + j * blockDim.x;
+        float v = 0.f;
+        if (held && k < d) {
+            for (int z = 0; z < nsplit; ++z) v += src[z * split_stride + roff + k];
+            s += v * v;
+        }
+        vals[j] = v;
+    }
+    if (!held) {
+        for (int k = threadIdx.x; k < d; k += blockDim.x) {
+            float v = 0.f;
+            for (int z = 0; z < nsplit; ++z) v += src[z * split_stride + roff + k];
+            s += v * v;
+        }
+    }
     s = wave_sum(s);
     if ((threadIdx.x & 63) == 0) sv[threadIdx.x >> 6] = s;
     __syncthreads();
     const float tot = sv[0] + sv[1] + sv[2] + sv[3];
     const float r = 1.0f / sqrtf(tot / (float)d + eps);
-    for (int k = threadIdx.x; k < d; k += blockDim.x) row[k] = row[k] * r * load_gain(gain, gain_f32, k);
+    if (held) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int k = threadIdx.x + j * blockDim.x;
+            if (k < d) dst[roff + k] = vals[j] * r * load_gain(gain, gain_f32, k);
+        }
+    } else {
+        for (int k = threadIdx.x; k < d; k += blockDim.x) {
+            float v = 0.f;
+            for (int z = 0; z < nsplit; ++z) v += src[z * split_stride + roff + k];
+            dst[roff + k] = v * r * load_gain(gain, gain_f32, k);
+        }
+    }
 }
 
 __global__ void advance_len_kernel(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap) {
@@ -127,6 +162,7 @@ __global__ void copy_f32_kernel(const float* src, float* dst, int64_t n) {
 
 hipError_t launch_argmax_merge(const float* pv, const int32_t* pi, int nblocks, int M, int32_t* ids, float* maxl,
                                hipStream_t s) {
+    (void)hipGetLastError();  // report only this launch's status
     hipLaunchKernelGGL(argmax_merge_kernel, dim3(M), dim3(kBlock), 0, s, pv, pi, nblocks, ids, maxl);
     return hipGetLastError();
 }
@@ -141,33 +177,41 @@ hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int g
                          hipStream_t s) {
     const int ns = verify_splits(V);
     const int rows = B * (gamma + 1);
+    (void)hipGetLastError();  // report only this launch's status
     hipLaunchKernelGGL(verify_partial_kernel, dim3(rows * ns), dim3(kBlock), 0, s, logits, V, ns, pv, pi);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    (void)hipGetLastError();  // report only this launch's status
     hipLaunchKernelGGL(verify_final_kernel, dim3(B), dim3(64), 0, s, pv, pi, ns, draft, gamma, accepted, committed,
                        ids, next_anchor);
     return hipGetLastError();
 }
 
-hipError_t launch_rownorm(float* x, int rows, int d, const void* gain, int gain_f32, float eps, hipStream_t s) {
-    hipLaunchKernelGGL(rownorm_kernel, dim3(rows), dim3(kBlock), 0, s, x, d, gain, gain_f32, eps);
+hipError_t launch_rownorm(const float* src, int nsplit, int64_t split_stride, float* dst, int rows, int d,
+                          const void* gain, int gain_f32, float eps, hipStream_t s) {
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL(rownorm_kernel, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
+                       gain_f32, eps);
     return hipGetLastError();
 }
 
 hipError_t launch_advance_len(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap,
                               hipStream_t s) {
+    (void)hipGetLastError();  // report only this launch's status
     hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, s, len, row_offsets, counts, B, cap);
     return hipGetLastError();
 }
 
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
     const int64_t blocks = (n + 255) / 256;
+    (void)hipGetLastError();  // report only this launch's status
     hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
     return hipGetLastError();
 }
 
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
     const int64_t blocks = (n + 255) / 256;
+    (void)hipGetLastError();  // report only this launch's status
     hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
     return hipGetLastError();
 }

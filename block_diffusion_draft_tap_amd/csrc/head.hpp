@@ -13,7 +13,8 @@ int verify_splits(int V);
 hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int gamma, int V, int32_t* accepted,
                          int32_t* committed, int32_t* ids, int32_t* next_anchor, float* pv, int32_t* pi,
                          hipStream_t s);
-hipError_t launch_rownorm(float* x, int rows, int d, const void* gain, int gain_f32, float eps, hipStream_t s);
+hipError_t launch_rownorm(const float* src, int nsplit, int64_t split_stride, float* dst, int rows, int d,
+                          const void* gain, int gain_f32, float eps, hipStream_t s);
 hipError_t launch_advance_len(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap,
                               hipStream_t s);
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);

@@ -152,12 +152,24 @@ const char* dflash_status_string(int status);
  * that the accelerated path really ran. */
 uint64_t dflash_invocations(void);
 
+/* Instrumentation. With both arguments non-NULL (hipEvent_t handles created
+ * by the caller), every later LM-head argmax -- inside dflash_draft_forward and
+ * dflash_lm_head_argmax -- records `start` on its stream immediately before
+ * its vocabulary GEMV kernel(s) and `stop` immediately after, so the caller can
+ * time exactly that kernel. Launches into a capturing stream (graph capture)
+ * are not traced. NULL, NULL switches it off. Process-wide setting; callers
+ * that trace must not run LM heads concurrently. */
+void dflash_trace_head_events(void* start, void* stop);
+
 /* Eq 2 (page 3, #buildContext): h_ctx[r] = RMSNorm(sum_j T_j[r] W_c[:, jH:(j+1)H]^T; ctx_norm).
  *   taps:   HOST array of m device pointers; tap j is [n, H] with row stride
  *           tap_ld elements, float for f32 models, bfloat16 otherwise.
  *   n:      rows (>= 0; 0 enqueues nothing).
  *   h_ctx:  float [n, d] output.
- * No workspace is used (ws may be NULL). */
+ * Workspace: optional. For n <= 8 rows and a workspace of
+ * dflash_workspace_bytes(dims, B, cap) bytes with B*(gamma+1) >= n, the long
+ * reduction is split across more workgroups (partial sums in ws, added in a
+ * fixed order); otherwise ws may be NULL. */
 int dflash_context_project(const dflash_model* M, const void* const* taps, int64_t tap_ld, int32_t n,
                            float* h_ctx, void* ws, size_t ws_bytes, void* stream);
 

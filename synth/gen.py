@@ -51,7 +51,7 @@ _MIX1 = np.uint64(0xBF58476D1CE4E5B9)
 _MIX2 = np.uint64(0x94D049BB133111EB)
 _S30, _S27, _S31, _S11 = np.uint64(30), np.uint64(27), np.uint64(31), np.uint64(11)
 
-_CHUNK = 1 << 16
+_CHUNK = 1 << 18
 _WORKERS = max(1, min(16, os.cpu_count() or 1))
 
 
@@ -123,6 +123,24 @@ def normals(seed: int, name: str, count: int, start: int = 0) -> np.ndarray:
     return _parallel(lambda s, n: _normals_serial(key, start + s, n), count, np.float64)
 
 
+def _stored_chunk(kind, seed, name, std, fp32, start, s, n):
+    key = stream_key(seed, name)
+    if kind == "codes":
+        return (raw64(key, start + s, n) >> np.uint64(60)).astype(np.uint8)
+    x = (_normals_serial(key, start + s, n) * std).astype(np.float32)
+    return x if fp32 else f32_to_bf16_bits(x)
+
+
+def _generate(kind, seed, name, std, fp32, start, count, dtype):
+    return _parallel(lambda s, n: _stored_chunk(kind, seed, name, std, fp32, start, s, n), count, dtype)
+
+
+def scaled_normals_stored(seed: int, name: str, count: int, std: float, fp32: bool, start: int = 0):
+    """std * N(0,1) in the storage type (float32, or bf16 bits), chunk by chunk
+    so that no full-size float64 temporary is ever allocated."""
+    return _generate("normal", seed, name, std, fp32, start, count, np.float32 if fp32 else np.uint16)
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); returns bit patterns."""
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
@@ -178,13 +196,9 @@ def _store_dense(x64: np.ndarray, fp32: bool) -> np.ndarray:
 def _int4_matrix(seed: int, name: str, shape):
     N, K = shape
     assert K % GROUP == 0, f"{name}: reduction width {K} is not a multiple of {GROUP}"
-    ckey = stream_key(seed, name + "#codes")
     count = N * K
-
-    def codes_chunk(s, n):
-        return (raw64(ckey, s, n) >> np.uint64(60)).astype(np.uint8)
-
-    q = _parallel(codes_chunk, count, np.uint8).reshape(N, K // 8, 8).astype(np.uint32)
+    q = _generate("codes", seed, name + "#codes", 0.0, False, 0, count, np.uint8)
+    q = q.reshape(N, K // 8, 8).astype(np.uint32)
     packed = np.zeros((N, K // 8), dtype=np.uint32)
     for j in range(8):
         packed |= q[:, :, j] << np.uint32(4 * j)
@@ -208,8 +222,7 @@ def make_weight(dims: Dims, name: str, seed: int = SEED_WEIGHTS, gains: str = "o
     if is_matrix(name) and dims.wdtype == WDTYPE_INT4G64:
         return _int4_matrix(seed, name, shape)
     count = int(np.prod(shape))
-    x = normals(seed, name, count) * 0.02
-    return _store_dense(x, fp32).reshape(shape)
+    return scaled_normals_stored(seed, name, count, 0.02, fp32).reshape(shape)
 
 
 class Model(dict):
@@ -239,8 +252,9 @@ def make_taps(dims: Dims, start_row: int, rows: int, stream: str = "ctx", seq: i
     """m tap buffers [rows, H] for rows start_row..start_row+rows-1 of a stream."""
     out = []
     for j in range(dims.m):
-        x = normals(seed, f"tap.{j}.{stream}.{seq}", rows * dims.H, start=start_row * dims.H)
-        out.append(_store_dense(x, dims.fp32).reshape(rows, dims.H))
+        x = scaled_normals_stored(seed, f"tap.{j}.{stream}.{seq}", rows * dims.H, 1.0, dims.fp32,
+                                  start=start_row * dims.H)
+        out.append(x.reshape(rows, dims.H))
     return out
 
 
