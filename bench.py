@@ -191,7 +191,7 @@ def main():
     len0 = kv.len.clone()
     assert kv.len.cpu().tolist() == lengths
 
-    ws = dfa.workspace(d, B, cap, dev)
+    ws = dfa.workspace(d, B, kv.cap, dev)
     vws = bd.verify_workspace(B, d.gamma, d.V, dev)
     offs = torch.arange(0, (B + 1) * W, W, dtype=torch.int32, device=dev)
     h_new = torch.empty(B * W, d.d, dtype=torch.float32, device=dev)

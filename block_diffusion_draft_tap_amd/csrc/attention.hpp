@@ -10,18 +10,22 @@ namespace dfl {
 struct AttnParams {
     const float* qkv;      // [B*gamma][qkv_ld]: Q cols [0, hq hd), K_b cols, then V_b cols
     int64_t qkv_ld;
-    const void* kcache;    // this layer's cache [B][hkv][cap][hd]
-    const void* vcache;
+    const void* kcache;    // this layer's keys   [B][hkv][cap][hd]
+    const void* vcache;    // this layer's values [B][hkv][hd][cap] (head-dim major)
     const int32_t* len;    // [B] context rows per sequence
     int B, hq, hkv, hd, gamma, cap, nsplit, kv_f32;
+    int nparts;            // partial results per (b, head): nsplit workgroups x parts each
     float scale;
-    float* part;           // [B][hq][nsplit][gamma][hd+2]  (o, running max, running sum)
+    float* part;           // [B][hq][nparts][gamma][hd+2]  (o, running max, running sum)
     float* out;            // O [B*gamma][out_ld], head h at columns h*hd
     int64_t out_ld;
     int round_out;         // 1: O is rounded and stored as bf16 (out reinterpreted as uint16)
 };
 
+// Workgroups per (sequence, kv head) and partial results per (sequence, head)
+// for a cache of `cap` rows; the workspace holds B*hq*nparts*gamma*(hd+2) floats.
+void attention_splits(int cap, int gamma, int kv_f32, int* nsplit, int* nparts);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
-int attention_max_rows();
+int attention_max_rows(int kv_f32);
 
 }  // namespace dfl

@@ -14,10 +14,6 @@
 
 using namespace dfl;
 
-// context keys per attention split (64-key tiles); the split count is capped at 64
-#ifndef DFL_ATTN_KEYS
-#define DFL_ATTN_KEYS 64
-#endif
 
 namespace {
 
@@ -68,7 +64,7 @@ int check_dims(const dflash_dims* d) {
     if (d->act != DFLASH_ACT_GELU_TANH && d->act != DFLASH_ACT_SILU) return DFLASH_DECLINED;
     if (d->nl > kMaxLayers || d->m > kMaxTaps) return DFLASH_DECLINED;
     if (d->gamma + 1 > 64) return DFLASH_DECLINED;
-    if ((d->hq / d->hkv) * d->gamma > attention_max_rows()) return DFLASH_DECLINED;
+    if ((d->hq / d->hkv) * d->gamma > attention_max_rows(d->wdtype == DFLASH_F32)) return DFLASH_DECLINED;
     const int q = d->wdtype == DFLASH_INT4G64 ? 64 : 8;
     if (d->H % q || d->d % q || d->F % q) return DFLASH_DECLINED;
     return DFLASH_OK;
@@ -128,6 +124,7 @@ int check_kv(const dflash_kv* kv, const dflash_dims& d, int B) {
     if (kv->B < B || B <= 0 || kv->cap <= 0) return DFLASH_EINVAL;
     const int want = d.wdtype == DFLASH_F32 ? DFLASH_F32 : DFLASH_BF16;
     if (kv->dtype != want) return DFLASH_EINVAL;
+    if (kv->dtype == DFLASH_BF16 && kv->cap % 32) return DFLASH_EINVAL;  // 32-key chunks of the value rows
     return DFLASH_OK;
 }
 
@@ -139,11 +136,6 @@ WeightPtr wptr(const dflash_weight& w) {
     return p;
 }
 
-int nsplit_for(int cap, int gamma) {
-    const int T = cap + gamma;
-    int ns = (T + DFL_ATTN_KEYS - 1) / DFL_ATTN_KEYS;
-    return ns < 1 ? 1 : (ns > 64 ? 64 : ns);
-}
 
 int rpw_for(int N) { return N >= 16384 ? 4 : (N >= 2048 ? 2 : 1); }
 // workgroup cap of the per-layer projections (row tiles beyond it are looped over)
@@ -171,14 +163,15 @@ struct Ws {
     int32_t* lmi;
     float* ctxp;   // split-K partials of the context projection [splits][B*(gamma+1)][d]
     size_t total;
-    int nsplit;
+    int nsplit;  // attention workgroups per (sequence, kv head)
+    int nparts;  // attention partials per (sequence, head)
 };
 
 Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     Ws w{};
     const size_t rows = (size_t)B * d.gamma;
     const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
-    w.nsplit = nsplit_for(cap, d.gamma);
+    attention_splits(cap, d.gamma, d.wdtype == DFLASH_F32, &w.nsplit, &w.nparts);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -187,7 +180,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     };
     const size_t o_hd = take(rows * d.d * 4);
     const size_t o_qkv = take(rows * qkv_rows * 4);
-    const size_t o_part = take((size_t)B * d.hq * w.nsplit * d.gamma * (d.hd + 2) * 4);
+    const size_t o_part = take((size_t)B * d.hq * w.nparts * d.gamma * (d.hd + 2) * 4);
     const size_t o_o = take(rows * d.hq * d.hd * 4);
     const size_t o_a = take(rows * d.F * 4);
     const size_t o_y = take(rows * d.H * 4);
@@ -294,6 +287,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         a.gamma = d.gamma;
         a.cap = kv->cap;
         a.nsplit = w.nsplit;
+        a.nparts = w.nparts;
         a.kv_f32 = kv->dtype == DFLASH_F32;
         a.scale = 1.0f / sqrtf((float)d.hd);
         a.part = w.part;

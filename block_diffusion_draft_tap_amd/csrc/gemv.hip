@@ -529,8 +529,10 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
                         const int which = n / kvw;
                         const int head = (n - which * kvw) / p.hd;
                         const int dim = n - which * kvw - head * p.hd;
-                        const int64_t off = (int64_t)layer * p.layer_stride +
-                                            (((int64_t)b * p.hkv + head) * p.cap + pos) * p.hd + dim;
+                        // keys [B][hkv][cap][hd]; values head-dim major [B][hkv][hd][cap]
+                        const int64_t hb = ((int64_t)b * p.hkv + head) * p.cap * p.hd;
+                        const int64_t off = (int64_t)layer * p.layer_stride + hb +
+                                            (which ? (int64_t)dim * p.cap + pos : (int64_t)pos * p.hd + dim);
                         void* base = which ? p.vcache : p.kcache;
                         if (p.kv_f32)
                             static_cast<float*>(base)[off] = y;

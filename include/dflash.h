@@ -124,9 +124,13 @@ typedef struct {
     const dflash_layer*  layers;     /* HOST array of nl layers                   */
 } dflash_model;
 
-/* Retained per-layer context K/V of B sequences.
- * k, v: [nl][B][hkv][cap][hd], element type `dtype` (DFLASH_F32 for f32 models,
- * DFLASH_BF16 otherwise). len: device int32 [B], rows held per sequence. */
+/* Retained per-layer context K/V of B sequences, element type `dtype`
+ * (DFLASH_F32 for f32 models, DFLASH_BF16 otherwise):
+ *   k: [nl][B][hkv][cap][hd]   (row-major keys)
+ *   v: [nl][B][hkv][hd][cap]   (head-dim major values: the attention's
+ *                               value operand is 8 consecutive keys of one dim)
+ * cap must be a multiple of 32 for DFLASH_BF16 caches.
+ * len: device int32 [B], rows held per sequence. */
 typedef struct {
     void*    k;
     void*    v;

@@ -49,14 +49,34 @@ def top2_gap(logits):
     return s[..., -1] - s[..., -2]
 
 
-def compare_ids(gpu_ids, ref_ids, ref_logits):
-    """Ids must agree wherever the oracle's winner leads by >= 1e-3."""
+# Near-tie band of the greedy ids. fp32 models: 1e-3 absolute. bf16 models:
+# the GPU and the bf16-faithful oracle round the same values, but fp32
+# accumulation flips about 1% of those roundings by one ulp, which moves
+# logits by ~0.1-0.3% relative; a fixed 1e-3 band is then tighter than the
+# stated 2e-2 relative logit tolerance allows. The band is 1e-2 of the row's
+# largest |logit| (half that tolerance), never below 1e-3.
+BAND_BF16_REL = 1e-2
+
+
+def compare_ids(gpu_ids, ref_ids, ref_logits, bf16=False):
+    """Ids must equal the oracle's wherever its winner leads by at least the
+    near-tie band; inside the band the GPU's token must itself be within the
+    band of the oracle's maximum (a valid greedy choice at that precision)."""
     g = gpu_ids.cpu().numpy().reshape(-1)
     r = np.asarray(ref_ids).reshape(-1)
-    gap = top2_gap(np.asarray(ref_logits).reshape(len(r), -1))
-    decided = gap >= NEAR_TIE
-    bad = np.nonzero(decided & (g != r))[0]
-    assert bad.size == 0, f"id mismatch at {bad[:10]}: gpu {g[bad[:10]]} oracle {r[bad[:10]]}"
+    L = np.asarray(ref_logits).reshape(len(r), -1)
+    gap = top2_gap(L)
+    band = np.full(len(r), NEAR_TIE)
+    if bf16:
+        band = np.maximum(band, BAND_BF16_REL * np.max(np.abs(L), axis=1))
+    decided = gap >= band
+    top = L.max(axis=1)
+    deficit = top - L[np.arange(len(g)), g]
+    bad = np.nonzero((decided & (g != r)) | (~decided & (deficit > band)))[0]
+    if bad.size:
+        info = [f"pos {i}: gpu {g[i]} (oracle logit {L[i, g[i]]:.6f}) oracle {r[i]} ({L[i, r[i]]:.6f}), "
+                f"gap {gap[i]:.2e}, band {band[i]:.2e}" for i in bad[:5]]
+        raise AssertionError("id mismatch: " + "; ".join(info))
     return int(decided.sum())
 
 

@@ -2,9 +2,11 @@
 inputs, element by element, at sizes the oracle finishes in seconds.
 
 Workloads: the fp32 tiny drafter (context 32), a bf16 GQA drafter with three
-ragged sequences (contexts 200 / 77 / 131 keys: several 64-key tiles plus
+ragged sequences (contexts 200 / 77 / 131 keys: several 32-key chunks plus
 tails, a 1000-token vocabulary that is not a multiple of the head's row tile),
-and the default bf16 drafter at its full size (context 2048, vocab 32768).
+a bf16 GQA drafter with 42 query rows per kv head (three MFMA row tiles) and
+two ragged sequences, and the default bf16 drafter at its full size (context
+2048, vocab 32768).
 """
 
 import numpy as np
@@ -22,9 +24,14 @@ pytestmark = pytest.mark.gpu
 GQA_BF16 = scaled(TINY, name="gqa_bf16", wdtype="bf16", H=256, d=256, hq=4, hkv=2, hd=64, F=512, gamma=5,
                   V=1000, B=3, L=200)
 
+# 6 query heads per kv head x gamma 7 = 42 query rows per kv head (three 16-row MFMA tiles)
+GQA_ROWS42 = scaled(TINY, name="gqa_rows42", wdtype="bf16", H=256, d=768, hq=12, hkv=2, hd=64, F=512, gamma=7,
+                    V=1000, B=2, L=150)
+
 CASES = {
     "tiny": (TINY, [TINY.L]),
     "gqa_bf16": (GQA_BF16, [200, 77, 131]),
+    "gqa_rows42": (GQA_ROWS42, [150, 96]),
     "default": (DEFAULT, [DEFAULT.L]),
 }
 
@@ -52,7 +59,7 @@ class Setup:
         self.offs_d = torch.from_numpy(offs).cuda()
         bd.check(dfa.dflash_ctx_kv_append(self.dm, self.h_ctx, self.offs_d, None, self.kv), "ctx_kv_append")
         torch.cuda.synchronize()
-        self.ws = dfa.workspace(dims, self.B, self.cap)
+        self.ws = dfa.workspace(dims, self.B, self.kv.cap)
         log(f"[setup] {name}: done")
 
 
@@ -82,7 +89,7 @@ def test_context_kv_cache(name):
     for i in range(s.dims.nl):
         for b, L in enumerate(s.lengths):
             for which, gpu, ref in (("k", s.kv.k, s.ctx.k), ("v", s.kv.v, s.ctx.v)):
-                g = gpu[i, b, :, :L, :].permute(1, 0, 2)
+                g = gpu[i, b, :, :L, :].permute(1, 0, 2) if which == "k" else gpu[i, b, :, :, :L].permute(2, 0, 1)
                 e = rel_err(g, ref[i][b])
                 worst = max(worst, e)
                 assert e <= tol(s.dims), (i, b, which, e)
@@ -139,7 +146,7 @@ def test_draft_forward(name):
     ref_ids, ex = O.draft_forward(s.w, d, s.ctx, anchors, s.fm, return_all=True)
     ey = rel_err(y, ex["Y"])
     em = rel_err(maxl, ex["max_logit"])
-    decided = compare_ids(ids, ref_ids, ex["logits"])
+    decided = compare_ids(ids, ref_ids, ex["logits"], bf16=s.fm)
     log(f"[{name}] Y rel err {ey:.3e}, max-logit rel err {em:.3e}, ids decided {decided}/{ids.numel()}")
     assert ey <= tol(d) and em <= tol(d)
     assert decided >= ids.numel() // 2
@@ -180,7 +187,7 @@ def test_lm_head_argmax_planted_and_random(wd, M):
     y_d = torch.from_numpy(Y).cuda()
     bd.check(dfa.dflash_lm_head_argmax(W, y_d, ids, ws, max_logit=maxl), "lm_head")
     ref_ids, best, logits = O.lm_head_argmax(Y.astype(np.float64), E, want_logits=True)
-    compare_ids(ids, ref_ids, logits)
+    compare_ids(ids, ref_ids, logits, bf16=(wd != "f32"))
     assert rel_err(maxl, best) <= 1e-5
     if M >= 5 and wd == "f32":
         assert int(ids[0]) == lo
@@ -217,7 +224,7 @@ def test_verify_exhaustive_patterns(V):
     assert np.array_equal(com_o, acc_o + 1)
 
 
-@pytest.mark.parametrize("name", ["tiny", "gqa_bf16"])
+@pytest.mark.parametrize("name", ["tiny", "gqa_bf16", "gqa_rows42"])
 def test_multi_round_loop(name):
     """Rounds of append(committed rows) -> forward -> verify, both sides driven
     by the oracle's schedule (planted logits realise accept lengths; the
@@ -230,8 +237,8 @@ def test_multi_round_loop(name):
         for b in range(B):
             ctx.append(i, b, base.ctx.k[i][b].copy(), base.ctx.v[i][b].copy())
     kv = dfa.KVCache(d, B, base.cap + 8 * (d.gamma + 1))
-    kv.k[:, :, :, :base.cap].copy_(base.kv.k)
-    kv.v[:, :, :, :base.cap].copy_(base.kv.v)
+    kv.k[:, :, :, :base.kv.cap].copy_(base.kv.k)
+    kv.v[..., :base.kv.cap].copy_(base.kv.v)
     kv.len.copy_(base.kv.len)
     ws = dfa.workspace(d, B, kv.cap)
     vws = bd.verify_workspace(B, d.gamma, d.V)
@@ -244,7 +251,7 @@ def test_multi_round_loop(name):
         ids = torch.empty(B, d.gamma, dtype=torch.int32, device="cuda")
         bd.check(dfa.dflash_draft_forward(base.dm, torch.from_numpy(anchors).cuda(), kv, B, ids, ws), "forward")
         ref_ids, ex = O.draft_forward(base.w, d, ctx, anchors, base.fm, return_all=True)
-        compare_ids(ids, ref_ids, ex["logits"])
+        compare_ids(ids, ref_ids, ex["logits"], bf16=base.fm)
         # verify on logits planted from the oracle's drafts
         a = gen.accept_schedule(d, r) if d.name == "tiny" else np.array([(r + b) % W for b in range(B)], np.int32)
         T = gen.plant_target_logits(d, ref_ids, a, r)
@@ -275,6 +282,7 @@ def test_multi_round_loop(name):
         for b in range(B):
             L = ctx.length(b)
             assert rel_err(kv.k[i, b, :, :L].permute(1, 0, 2), ctx.k[i][b]) <= tol(d)
+            assert rel_err(kv.v[i, b, :, :, :L].permute(2, 0, 1), ctx.v[i][b]) <= tol(d)
     log(f"[{name}] multi-round accepted lengths seen: {sorted(seen)}")
     if name == "tiny":
         assert seen == set(range(d.gamma + 1))
