@@ -27,15 +27,14 @@
 #include "attention.hpp"
 #include "common.hpp"
 
-#ifndef DFL_ATTN_CPW
-#define DFL_ATTN_CPW 1  // 32-key chunks per wavefront (bf16 caches)
-#endif
 
 namespace dfl {
 
 constexpr int kTile = 64;   // keys per tile, fp32 kernel
 constexpr int kChunk = 32;  // keys per chunk, MFMA kernel
 constexpr int kMaxParts = 256;
+constexpr int kMaxSplit = 64;  // workgroups per (sequence, kv head), MFMA kernel
+constexpr int kMaxRows = 48;   // query rows per kv head, MFMA kernel
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -73,14 +72,19 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel (bf16 caches)
+// MFMA kernel (bf16 caches; Q, K_b and V_b arrive as bf16)
 
 template <int HD, int NRT>
 __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     constexpr int KS = HD / 32;  // k-steps of S = Q K^T
     constexpr int DT = HD / 16;  // head-dim tiles of O
     constexpr int PLD = kChunk + 8;  // padded P row (bf16 elements)
-    __shared__ __align__(16) uint16_t plds[4][2][NRT][16][PLD];  // P as bf16 high and low parts
+    constexpr int PBYTES = 4 * 2 * NRT * 16 * PLD * 2;  // P tiles, high and low parts, per wavefront
+    constexpr int OBYTES = 3 * NRT * DT * 4 * 64 * 4;   // o of wavefronts 1..3 in register order
+    __shared__ __align__(16) unsigned char lds[PBYTES > OBYTES ? PBYTES : OBYTES];
+    __shared__ float wm[4][NRT * 16], wl[4][NRT * 16];
+    typedef uint16_t PTile[2][NRT][16][PLD];
+    PTile* plds = reinterpret_cast<PTile*>(lds);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -90,41 +94,66 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     const int qpg = p.hq / p.hkv;
     const int R = qpg * p.gamma;
     const int lenb = min(max(p.len[b], 0), p.cap);
-    const int part = s * 4 + wave;  // this wavefront's split
+    // work units: the context's 32-key chunks, then the block's gamma keys;
+    // wavefronts take equal runs of consecutive units
     const int nch = (lenb + kChunk - 1) / kChunk;
-    const int cpp = (nch + p.nparts - 1) / p.nparts;
-    const int c_begin = part * cpp;
-    const int c_end = min(nch, c_begin + cpp);
-    const bool do_block = (part == 0);  // the gamma block keys go to split 0
+    const int nunits = nch + 1;
+    const int upw = (nunits + 4 * p.nsplit - 1) / (4 * p.nsplit);
+    const int u_begin = min(nunits, (s * 4 + wave) * upw);
+    const int u_end = min(nunits, u_begin + upw);
 
     const int64_t qkv_ld = p.qkv_ld;
-    const float* qrow0 = p.qkv + (int64_t)b * p.gamma * qkv_ld;
+    const uint16_t* qrow0 = static_cast<const uint16_t*>(p.qkv) + (int64_t)b * p.gamma * qkv_ld;
     const int kcol = p.hq * HD + g * HD;
     const int vcol = p.hq * HD + p.hkv * HD + g * HD;
     const uint16_t* kc = static_cast<const uint16_t*>(p.kcache) + ((int64_t)b * p.hkv + g) * p.cap * HD;
     const uint16_t* vc = static_cast<const uint16_t*>(p.vcache) + ((int64_t)b * p.hkv + g) * HD * (int64_t)p.cap;
+    const float sl2 = p.scale * 1.4426950408889634f;  // scores in log2 units
 
-    // Q tiles as A operands: row = rt*16 + col, dims ks*32 + 8*grp + e
-    uint4 qa[NRT][KS];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-        const int r = rt * 16 + col;
-        const float* src = nullptr;
-        if (r < R) {
-            const int h = g * qpg + r / p.gamma, i = r % p.gamma;
-            src = qrow0 + (int64_t)i * qkv_ld + h * HD;
+    const uint16_t* vblk = p.vblk + ((int64_t)b * p.hkv + g) * HD * kChunk;
+
+    // K rows c0 + nt*16 + col (dims ks*32 + 8*grp ..) and V keys c0 + 8*grp .. +8 of dims
+    // dt*16 + col. Keys past nvalid come from in-bounds rows (cache rows below cap, clamped
+    // block rows): their scores are masked and their values zeroed before use.
+    uint4 kb[2][KS], vb[DT];
+    auto load_unit = [&](const int u) {
+        const uint16_t *k0, *k1, *vp;
+        int64_t vstride;
+        if (u != nch) {
+            k0 = kc + (int64_t)(u * kChunk + col) * HD + 8 * grp;
+            k1 = k0 + 16 * HD;
+            vp = vc + (int64_t)col * p.cap + u * kChunk + 8 * grp;
+            vstride = 16 * (int64_t)p.cap;
+        } else {
+            k0 = qrow0 + (int64_t)min(col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
+            k1 = qrow0 + (int64_t)min(16 + col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
+            vp = vblk + col * kChunk + 8 * grp;
+            vstride = 16 * kChunk;
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            float f[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = src ? src[ks * 32 + 8 * grp + e] : 0.f;
-            qa[rt][ks] = pack8(f);
+            kb[0][ks] = *reinterpret_cast<const uint4*>(k0 + ks * 32);
+            kb[1][ks] = *reinterpret_cast<const uint4*>(k1 + ks * 32);
         }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vb[dt] = *reinterpret_cast<const uint4*>(vp + dt * vstride);
+    };
+    // the first unit's loads go out together with Q's
+    if (u_begin < u_end) load_unit(u_begin);
+
+    // Q tiles as A operands: row = rt*16 + col, dims ks*32 + 8*grp ..; rows past R repeat
+    // row R-1 and are never stored
+    uint4 qa[NRT][KS];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        const int r = min(rt * 16 + col, R - 1);
+        const uint16_t* src = qrow0 + (int64_t)(r % p.gamma) * qkv_ld + (g * qpg + r / p.gamma) * HD + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[rt][ks] = *reinterpret_cast<const uint4*>(src + ks * 32);
     }
 
     f32x4 o[NRT][DT];
-    float m[NRT][4], l[NRT][4];
+    float m[NRT][4], l[NRT][4];  // running max (log2 units) and sum per row 4*grp + e
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
@@ -133,62 +162,45 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         for (int e = 0; e < 4; ++e) { m[rt][e] = -INFINITY; l[rt][e] = 0.f; }
     }
 
-    // one chunk of up to 32 keys: keys [c0, c0 + nvalid) of the context, or of the block
-    auto chunk = [&](const bool block, const int c0, const int nvalid) {
+    for (int u = u_begin; u < u_end; ++u) {
+        if (u != u_begin) load_unit(u);
+        const int nvalid = (u == nch) ? p.gamma : min(kChunk, lenb - u * kChunk);
+
         f32x4 sacc[NRT][2];
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) sacc[rt][0] = sacc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int j = nt * 16 + col;  // key within the chunk
-            uint4 kb[KS];
+            for (int nt = 0; nt < 2; ++nt) {
+                sacc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if (j < nvalid) {
-                    if (block) {
-                        const float* src = qrow0 + (int64_t)j * qkv_ld + kcol + ks * 32 + 8 * grp;
-                        float f[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) f[e] = src[e];
-                        kb[ks] = pack8(f);
-                    } else {
-                        kb[ks] = *reinterpret_cast<const uint4*>(kc + (int64_t)(c0 + j) * HD + ks * 32 + 8 * grp);
-                    }
-                } else {
-                    kb[ks] = make_uint4(0, 0, 0, 0);
-                }
+                for (int ks = 0; ks < KS; ++ks) sacc[rt][nt] = mfma16(qa[rt][ks], kb[nt][ks], sacc[rt][nt]);
             }
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) sacc[rt][nt] = mfma16(qa[rt][ks], kb[ks], sacc[rt][nt]);
-        }
         // online softmax; lane holds rows 4*grp+e, keys col and 16+col
         const bool v0ok = col < nvalid, v1ok = 16 + col < nvalid;
+        const bool rescale = (u != u_begin);  // o is still zero on a wavefront's first unit
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float s0 = v0ok ? sacc[rt][0][e] * p.scale : -INFINITY;
-                const float s1 = v1ok ? sacc[rt][1][e] * p.scale : -INFINITY;
-                const float mx = row16_max(fmaxf(s0, s1));
-                const float mn = fmaxf(m[rt][e], mx);
-                float p0 = 0.f, p1 = 0.f, al = 1.f;
-                if (mn != -INFINITY) {
-                    p0 = v0ok ? expf(s0 - mn) : 0.f;
-                    p1 = v1ok ? expf(s1 - mn) : 0.f;
-                    al = expf(m[rt][e] - mn);
-                }
+                const float s0 = v0ok ? sacc[rt][0][e] * sl2 : -INFINITY;
+                const float s1 = v1ok ? sacc[rt][1][e] * sl2 : -INFINITY;
+                const float mn = fmaxf(m[rt][e], row16_max(fmaxf(s0, s1)));  // finite: key 0 is valid
+                const float p0 = __builtin_amdgcn_exp2f(s0 - mn);
+                const float p1 = __builtin_amdgcn_exp2f(s1 - mn);
+                const float al = __builtin_amdgcn_exp2f(m[rt][e] - mn);
                 l[rt][e] = l[rt][e] * al + row16_sum(p0 + p1);
                 m[rt][e] = mn;
+                if (rescale) {
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) o[rt][dt][e] *= al;
+                    for (int dt = 0; dt < DT; ++dt) o[rt][dt][e] *= al;
+                }
                 // P = hi + lo with both parts bf16: the product keeps ~16 mantissa bits of P
-                const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
-                plds[wave][0][rt][4 * grp + e][col] = (uint16_t)h0;
-                plds[wave][0][rt][4 * grp + e][16 + col] = (uint16_t)h1;
-                plds[wave][1][rt][4 * grp + e][col] = (uint16_t)f32_to_bf16_bits(p0 - bf16_bits_to_f32(h0));
-                plds[wave][1][rt][4 * grp + e][16 + col] = (uint16_t)f32_to_bf16_bits(p1 - bf16_bits_to_f32(h1));
+                const uint32_t hp = pack_bf16x2(p0, p1);
+                const uint32_t lp = pack_bf16x2(p0 - bf16_lo(hp), p1 - bf16_hi(hp));
+                plds[wave][0][rt][4 * grp + e][col] = (uint16_t)hp;
+                plds[wave][0][rt][4 * grp + e][16 + col] = (uint16_t)(hp >> 16);
+                plds[wave][1][rt][4 * grp + e][col] = (uint16_t)lp;
+                plds[wave][1][rt][4 * grp + e][16 + col] = (uint16_t)(lp >> 16);
             }
         }
         // P as A operands (row col, keys 8*grp .. +8); LDS ops of one wavefront are ordered
@@ -198,58 +210,83 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
             pa[rt] = *reinterpret_cast<const uint4*>(&plds[wave][0][rt][col][8 * grp]);
             pl[rt] = *reinterpret_cast<const uint4*>(&plds[wave][1][rt][col][8 * grp]);
         }
-        // V as B operands: keys 8*grp + e, dim dt*16 + col
+        if (nvalid < kChunk) {
+            // keys past the context are zeroed in V (P is zero there; the cache may hold anything)
+            const int nk = nvalid - 8 * grp;  // valid keys among this lane's 8
+            uint32_t mk[4];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int dim = dt * 16 + col;
-            uint4 vb;
-            if (block) {
-                float f[8];
+            for (int q = 0; q < 4; ++q) mk[q] = (2 * q + 1 < nk) ? 0xFFFFFFFFu : ((2 * q < nk) ? 0x0000FFFFu : 0u);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = 8 * grp + e;
-                    f[e] = j < nvalid ? qrow0[(int64_t)j * qkv_ld + vcol + dim] : 0.f;
-                }
-                vb = pack8(f);
-            } else {
-                vb = *reinterpret_cast<const uint4*>(vc + (int64_t)dim * p.cap + c0 + 8 * grp);
-                // keys past the context are zeroed (P is zero there; the cache may hold anything)
-                const int nk = nvalid - 8 * grp;
-                if (nk < 8) {
-                    uint32_t w[4] = {vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        if (2 * q >= nk) w[q] = 0u;
-                        else if (2 * q + 1 >= nk) w[q] &= 0xFFFFu;
-                    }
-                    vb = make_uint4(w[0], w[1], w[2], w[3]);
-                }
+            for (int dt = 0; dt < DT; ++dt) {
+                vb[dt].x &= mk[0];
+                vb[dt].y &= mk[1];
+                vb[dt].z &= mk[2];
+                vb[dt].w &= mk[3];
             }
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) o[rt][dt] = mfma16(pl[rt], vb, mfma16(pa[rt], vb, o[rt][dt]));
         }
-    };
-
-    for (int c = c_begin; c < c_end; ++c) chunk(false, c * kChunk, min(kChunk, lenb - c * kChunk));
-    if (do_block) chunk(true, 0, p.gamma);
-
-    // partials of this split: [B][hq][nparts][gamma][HD + 2]
-    const int W = HD + 2;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) o[rt][dt] = mfma16(pl[rt], vb[dt], mfma16(pa[rt], vb[dt], o[rt][dt]));
+    }
+
+    // merge the four wavefronts in LDS; wavefront 0 writes the workgroup's partial
+    __syncthreads();  // the P tiles are dead; their LDS is reused below
+    if (col == 0) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                wm[wave][rt * 16 + 4 * grp + e] = m[rt][e];
+                wl[wave][rt * 16 + 4 * grp + e] = l[rt][e];
+            }
+    }
+    __syncthreads();
+    float* ob = reinterpret_cast<float*>(lds);  // [3][NRT][DT][4][64]
+    float Mrow[NRT][4], Lrow[NRT][4];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rt * 16 + 4 * grp + e;
-            if (r >= R) continue;
-            const int h = g * qpg + r / p.gamma, i = r % p.gamma;
-            float* dst = p.part + ((((int64_t)b * p.hq + h) * p.nparts + part) * p.gamma + i) * W;
+            const float M = fmaxf(fmaxf(wm[0][r], wm[1][r]), fmaxf(wm[2][r], wm[3][r]));
+            const float f = (m[rt][e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[rt][e] - M);
+            float L = 0.f;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) dst[dt * 16 + col] = o[rt][dt][e];
-            if (col == 0) {
-                dst[HD] = m[rt][e];
-                dst[HD + 1] = l[rt][e];
+            for (int w = 0; w < 4; ++w) L += (wm[w][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(wm[w][r] - M) * wl[w][r];
+            Mrow[rt][e] = M;
+            Lrow[rt][e] = L;
+            if (wave > 0) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) ob[((((wave - 1) * NRT + rt) * DT + dt) * 4 + e) * 64 + lane] = o[rt][dt][e] * f;
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[rt][dt][e] *= f;
             }
         }
+    __syncthreads();
+    if (wave == 0) {
+        const int W = HD + 2;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = rt * 16 + 4 * grp + e;
+                if (r >= R) continue;
+                const int h = g * qpg + r / p.gamma, i = r % p.gamma;
+                float* dst = p.part + ((((int64_t)b * p.hq + h) * p.nparts + s) * p.gamma + i) * W;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    float v = o[rt][dt][e];
+#pragma unroll
+                    for (int w = 0; w < 3; ++w) v += ob[(((w * NRT + rt) * DT + dt) * 4 + e) * 64 + lane];
+                    dst[dt * 16 + col] = v;
+                }
+                if (col == 0) {
+                    dst[HD] = Mrow[rt][e] * 0.6931471805599453f;  // natural-log units
+                    dst[HD + 1] = Lrow[rt][e];
+                }
+            }
     }
 }
 
@@ -281,7 +318,7 @@ __global__ __launch_bounds__(kBlock) void attn_valu_kernel(const AttnParams p) {
     const int end = min(T, start + C);
 
     const int64_t qkv_ld = p.qkv_ld;
-    const float* qrow0 = p.qkv + (int64_t)b * p.gamma * qkv_ld;
+    const float* qrow0 = static_cast<const float*>(p.qkv) + (int64_t)b * p.gamma * qkv_ld;
     const int kcol = p.hq * HD + g * HD;
     const int vcol = p.hq * HD + p.hkv * HD + g * HD;
     const float* kc = static_cast<const float*>(p.kcache) + ((int64_t)b * p.hkv + g) * p.cap * HD;
@@ -441,16 +478,16 @@ void attention_splits(int cap, int gamma, int kv_f32, int* nsplit, int* nparts) 
         *nsplit = ns;
         *nparts = ns;
     } else {
-        const int chunks = (cap + kChunk - 1) / kChunk;
-        const int parts = (chunks + DFL_ATTN_CPW - 1) / DFL_ATTN_CPW;
-        int ns = (parts + 3) / 4;
-        ns = ns < 1 ? 1 : (ns > kMaxParts / 4 ? kMaxParts / 4 : ns);
+        // one unit per wavefront while the split count allows: cap/32 chunks plus the block
+        const int units = (cap + kChunk - 1) / kChunk + 1;
+        int ns = (units + 3) / 4;
+        ns = ns < 1 ? 1 : (ns > kMaxSplit ? kMaxSplit : ns);
         *nsplit = ns;
-        *nparts = 4 * ns;
+        *nparts = ns;
     }
 }
 
-int attention_max_rows(int kv_f32) { return kv_f32 ? 40 : 48; }
+int attention_max_rows(int kv_f32) { return kv_f32 ? 40 : kMaxRows; }
 
 template <int HD>
 static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
@@ -469,7 +506,7 @@ static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
             hipLaunchKernelGGL((attn_mfma_kernel<HD, 1>), grid, dim3(kBlock), 0, s, p);
         else if (R <= 32)
             hipLaunchKernelGGL((attn_mfma_kernel<HD, 2>), grid, dim3(kBlock), 0, s, p);
-        else if (R <= 48)
+        else if (R <= kMaxRows)
             hipLaunchKernelGGL((attn_mfma_kernel<HD, 3>), grid, dim3(kBlock), 0, s, p);
         else
             return hipErrorInvalidValue;
@@ -482,6 +519,7 @@ static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
     if (p.nparts > kMaxParts || p.gamma > kChunk) return hipErrorInvalidValue;
+    if (!p.kv_f32 && p.nsplit > kMaxSplit) return hipErrorInvalidValue;
     if (!p.kv_f32 && (p.cap % kChunk)) return hipErrorInvalidValue;
     if (p.hd == 128) return launch_hd<128>(p, s);
     if (p.hd == 64) return launch_hd<64>(p, s);

@@ -8,7 +8,9 @@
 namespace dfl {
 
 struct AttnParams {
-    const float* qkv;      // [B*gamma][qkv_ld]: Q cols [0, hq hd), K_b cols, then V_b cols
+    const void* qkv;       // [B*gamma][qkv_ld]: Q cols [0, hq hd), K_b cols, then V_b cols
+                           // (fp32 with fp32 caches; bf16 with bf16 caches, V_b then in vblk)
+    const uint16_t* vblk;  // bf16 caches: block values head-dim major [B][hkv][hd][32], keys < gamma
     int64_t qkv_ld;
     const void* kcache;    // this layer's keys   [B][hkv][cap][hd]
     const void* vcache;    // this layer's values [B][hkv][hd][cap] (head-dim major)
@@ -23,7 +25,8 @@ struct AttnParams {
 };
 
 // Workgroups per (sequence, kv head) and partial results per (sequence, head)
-// for a cache of `cap` rows; the workspace holds B*hq*nparts*gamma*(hd+2) floats.
+// for a cache of `cap` rows (one partial per workgroup); the workspace holds
+// B*hq*nparts*gamma*(hd+2) floats.
 void attention_splits(int cap, int gamma, int kv_f32, int* nsplit, int* nparts);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 int attention_max_rows(int kv_f32);

@@ -16,15 +16,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// float -> bf16 bits, round to nearest even (inputs are finite)
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// float -> bf16 bits, round to nearest even: gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32, two values per instruction)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // c + a.lo*b.lo + a.hi*b.hi on packed bf16 pairs, fp32 accumulate

@@ -162,6 +162,7 @@ struct Ws {
     float* lmv;
     int32_t* lmi;
     float* ctxp;   // split-K partials of the context projection [splits][B*(gamma+1)][d]
+    uint16_t* vt;  // block values, head-dim major [B][hkv][hd][32] (bf16 models)
     size_t total;
     int nsplit;  // attention workgroups per (sequence, kv head)
     int nparts;  // attention partials per (sequence, head)
@@ -188,6 +189,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     const size_t o_lmv = take(rows * nb * 4);
     const size_t o_lmi = take(rows * nb * 4);
     const size_t o_ctxp = take((size_t)ctx_splits(d) * B * (d.gamma + 1) * d.d * 4);
+    const size_t o_vt = take((size_t)B * d.hkv * d.hd * 32 * 2);
     w.total = off;
     char* c = static_cast<char*>(base);
     if (c) {
@@ -200,6 +202,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
         w.lmv = reinterpret_cast<float*>(c + o_lmv);
         w.lmi = reinterpret_cast<int32_t*>(c + o_lmi);
         w.ctxp = reinterpret_cast<float*>(c + o_ctxp);
+        w.vt = reinterpret_cast<uint16_t*>(c + o_vt);
     }
     return w;
 }
@@ -238,7 +241,7 @@ hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStr
             q.out = p.out + (int64_t)r0 * p.out_ld;
         if ((epi == EPI_STORE && p.out_bf16) || (epi == EPI_GATED && p.round_out))
             q.out = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(p.out) + (int64_t)r0 * p.out_ld);
-        if (epi == EPI_KV) q.row_base = p.row_base + r0;
+        if (epi == EPI_KV || (epi == EPI_STORE && p.vt)) q.row_base = p.row_base + r0;
         if (epi == EPI_BLOCKINIT) q.seq_base = p.seq_base + r0;
         if (epi == EPI_ARGMAX) {
             q.part_val = p.part_val + (int64_t)r0 * p.nblocks;
@@ -268,6 +271,17 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.gain[0] = L.attn_norm;
         p.out = w.qkv;
         p.out_ld = qkv_rows;
+        if (d.wdtype != DFLASH_F32) {
+            // bf16 models (Q, K_b, V_b are bf16 by the rounding contract): Q and K_b row-major,
+            // V_b head-dim major like the value cache
+            p.out_bf16 = 1;
+            p.vt = w.vt;
+            p.vt_col = (d.hq + d.hkv) * d.hd;
+            p.row_base = 0;
+            p.gamma = d.gamma;
+            p.hkv = d.hkv;
+            p.hd = d.hd;
+        }
         DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_STORE, p, rows, s));
     }
     {  // O = softmax(Q [K_ctx; K_b]^T / sqrt(hd)) [V_ctx; V_b]
@@ -291,6 +305,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         a.kv_f32 = kv->dtype == DFLASH_F32;
         a.scale = 1.0f / sqrtf((float)d.hd);
         a.part = w.part;
+        a.vblk = w.vt;
         a.out = w.o;
         a.out_ld = d.hq * d.hd;
         a.round_out = d.wdtype == DFLASH_F32 ? 0 : 1;

@@ -506,8 +506,14 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
                 const float y = red[u * MAXM + m];
                 if constexpr (EPI == EPI_STORE) {
                     if (p.out_bf16) {
-                        uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (int64_t)blockIdx.z * p.split_stride;
-                        o[(int64_t)m * p.out_ld + n] = (uint16_t)f32_to_bf16_bits(y);
+                        if (p.vt && n >= p.vt_col) {
+                            const int row = p.row_base + m, bb = row / p.gamma, key = row - bb * p.gamma;
+                            const int c = n - p.vt_col, head = c / p.hd, dim = c - head * p.hd;
+                            p.vt[(((int64_t)bb * p.hkv + head) * p.hd + dim) * 32 + key] = (uint16_t)f32_to_bf16_bits(y);
+                        } else {
+                            uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (int64_t)blockIdx.z * p.split_stride;
+                            o[(int64_t)m * p.out_ld + n] = (uint16_t)f32_to_bf16_bits(y);
+                        }
                     } else {
                         float* o = p.out + (int64_t)blockIdx.z * p.split_stride;
                         o[(int64_t)m * p.out_ld + n] = p.round_out ? round_bf16(y) : y;

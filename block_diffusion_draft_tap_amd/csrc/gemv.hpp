@@ -73,6 +73,9 @@ struct GemvParams {
     int64_t out_ld;
     int round_out;       // EPI_STORE / EPI_GATED: round results to bf16 (EPI_GATED then stores bf16)
     int out_bf16;        // EPI_STORE: store bf16 values instead of fp32
+    uint16_t* vt;        // EPI_STORE with out_bf16: outputs n >= vt_col go head-dim major to
+    int vt_col;          //   vt[b][head][dim][32] (b = row / gamma, key = row % gamma; heads of hd)
+                         //   instead of out; row_base is the global index of row 0
     int F;               // EPI_GATED: gate rows [0, F), up rows [F, 2F)
     int act;             // EPI_GATED: 0 gelu_tanh, 1 silu
     // EPI_KV
