@@ -13,11 +13,11 @@ torch.cuda.CUDAGraph on the stream the library launches on) and the graphs
 are replayed in a cycle. The metric is draft blocks per second (B blocks per
 step); tokens proposed per second is gamma * B * blocks/s.
 
-The dominant kernel (the LM-head GEMV + argmax epilogue) is timed live with
-HIP events that the library records immediately around it, in eager rounds
-run right after the timed graph replays (a captured graph does not keep
-timing records); the preceding launches of each round keep the GPU behind
-the host, so the events bracket the kernel and not host gaps.
+The dominant kernel (the LM-head GEMV + argmax epilogue) is timed live inside
+the timed region: each of its workgroups writes the device wall clock at its
+start and end into a per-round buffer (a kernel argument, so graph replays
+write it too); its duration is the first start to the last end, averaged over
+the last timed run of every round.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config default]
 """
@@ -132,6 +132,33 @@ def cpu_baseline(d, rounds_inputs, seconds, gpu_ids):
 # ----------------------------------------------------------------------------
 
 
+COPY_BYTES = 256 << 20    # calibration copy: reads and writes this many bytes
+
+
+def profile_head(d, dev, launches=20):
+    """Workload for memory-counter passes: one elementwise copy of COPY_BYTES
+    (a kernel whose HBM reads and writes are known, to scale the counters),
+    then eager launches of the LM-head argmax alone at the workload's shape."""
+    import torch
+    from block_diffusion_draft_tap_amd import binding as bd
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    rows = d.B * d.gamma
+    E = bd.Weight(gen.make_weight(d, "E_out"), dev)
+    y16 = gen.f32_to_bf16_bits(np.random.default_rng(5).standard_normal((rows, d.H)).astype(np.float32))
+    y = torch.from_numpy(y16.view(np.int16)).to(dev).view(torch.bfloat16)
+    ids = torch.empty(rows, dtype=torch.int32, device=dev)
+    ws = bd.lm_head_workspace(d.V, rows, dev)
+    for _ in range(launches):
+        bd.check(bd.dflash_lm_head_argmax(E, y, ids, ws), "lm_head_argmax")
+    torch.cuda.synchronize()
+    log(f"[profile-head] copy {COPY_BYTES} B, {launches} LM-head launches ({d.V} x {d.H}, {rows} rows)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +169,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every call from the host (no graphs)")
+    ap.add_argument("--profile-head", action="store_true",
+                    help="counter workload: a 256 MiB device copy (calibration), then eager LM-head launches")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -160,6 +189,9 @@ def main():
     if bd.dflash_query(d) != bd.DFLASH_OK:
         print("libdflash declined this configuration on this device", file=sys.stderr)
         sys.exit(3)
+    if args.profile_head:
+        profile_head(d, dev)
+        return
 
     t_setup = time.perf_counter()
     log(f"[bench] generating weights for {d.name}")
@@ -198,6 +230,8 @@ def main():
 
     # per-round inputs, resident on the device
     accept = [gen.accept_schedule(d, r) for r in range(R)]
+    head_wgs = bd.dflash_lm_head_workgroups(d.V)
+    head_launches = (B * d.gamma + 7) // 8
     rounds = []
     for r in range(R):
         taps_r = [gen.make_taps(d, r * W, W, stream="round", seq=b) for b in range(B)]
@@ -212,15 +246,16 @@ def main():
             "com": torch.zeros(B, dtype=torch.int32, device=dev),
             "vids": torch.zeros(B, W, dtype=torch.int32, device=dev),
             "nxt": torch.zeros(B, dtype=torch.int32, device=dev),
-            "ev0": torch.cuda.Event(enable_timing=True),
-            "ev1": torch.cuda.Event(enable_timing=True),
+            # LM-head workgroup wall-clock stamps of this round's latest run
+            "stamps": torch.zeros(2 * head_wgs * head_launches, dtype=torch.int64, device=dev),
         }
         rr["counts"] = torch.from_numpy(rr["counts_h"]).to(dev)
-        for ev in (rr["ev0"], rr["ev1"]):
-            ev.record()            # torch creates the HIP event on first record; the library needs the handle
         rounds.append(rr)
 
     def run_round(rr, verify=True):
+        # the head kernel writes its workgroup stamps into this round's buffer (a kernel
+        # argument: captured graphs keep writing them on every replay)
+        bd.dflash_trace_head_stamps(rr["stamps"])
         bd.check(dfa.dflash_context_project(dm, rr["taps"], h_new, ws), "context_project")
         bd.check(dfa.dflash_ctx_kv_append(dm, h_new, offs, rr["counts"], kv), "append")
         bd.check(dfa.dflash_draft_forward(dm, rr["anchors"], kv, B, rr["ids"], ws), "forward")
@@ -228,6 +263,7 @@ def main():
             bd.check(dfa.dflash_verify_greedy(rr["T"], rr["ids"], rr["acc"], rr["com"], rr["vids"], vws,
                                               next_anchor=rr["nxt"]), "verify")
         kv.len.copy_(len0)
+        bd.dflash_trace_head_stamps(None)
 
     # untimed chain: drafts of each round plant that round's target logits
     log("[bench] building the round chain")
@@ -245,7 +281,7 @@ def main():
         anchor = rr["nxt"].cpu().numpy().copy()
     torch.cuda.synchronize()
 
-    # capture one graph per round; the library records the head events inside
+    # capture one graph per round
     graphs = []
     stream = torch.cuda.Stream(device=dev)
     use_graph = not args.eager
@@ -278,7 +314,6 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
-    bd.dflash_trace_head_events(None, None)
 
     # the replays must reproduce the chain exactly (deterministic kernels)
     for r, rr in enumerate(rounds):
@@ -286,19 +321,12 @@ def main():
         assert np.array_equal(rr["acc"].cpu().numpy(), accept[r]), f"round {r}: accepted changed on replay"
         assert np.array_equal(rr["com"].cpu().numpy(), accept[r] + 1)
 
-    # the dominant kernel, timed with events around it in eager rounds
-    head_source = ("HIP events recorded by the library around the kernel, in eager rounds "
-                   "right after the timed replays")
-    head_ms = []
-    for rep in range(3):
-        for rr in rounds:
-            bd.dflash_trace_head_events(rr["ev0"], rr["ev1"])
-            run_round(rr)
-            bd.dflash_trace_head_events(None, None)
-            torch.cuda.synchronize()
-            head_ms.append(bd.event_elapsed_ms(rr["ev0"], rr["ev1"]))
-    assert all(x is not None and x > 0 for x in head_ms), head_ms
-    head_us = [x * 1000.0 for x in head_ms]
+    # the dominant kernel's duration, from the wall-clock stamps its workgroups wrote
+    # during the timed region (the last run of each round)
+    head_source = (f"device wall-clock stamps written by the kernel's workgroups (first start to last end), "
+                   f"last timed run of each of the {R} rounds")
+    head_us = [t * 1e6 for rr in rounds for t in bd.stamps_duration_s(rr["stamps"], head_launches)]
+    assert all(0 < x < 1e5 for x in head_us), head_us
     head_us_avg = float(np.mean(head_us))
     ms_per_step = gpu_ms / args.steps
     blocks_per_s = B * args.steps / (gpu_ms / 1000.0)
@@ -310,15 +338,10 @@ def main():
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"lm_head_gemv_{d.name}_traffic.md")
     if os.path.exists(tfile):
-        # the file holds the counter-derived bytes per launch and the hash of the
-        # kernel source they were taken with; stale counters are not reported
-        import hashlib
-        src = open(os.path.join(ROOT, "block_diffusion_draft_tap_amd", "csrc", "gemv.hip"), "rb").read()
-        h = hashlib.sha256(src).hexdigest()[:16]
-        vals = dict(line.split(":", 1) for line in open(tfile).read().splitlines() if line.startswith("- ")
-                    and ":" in line)
-        vals = {k[2:].strip(): v.strip() for k, v in vals.items()}
-        if vals.get("gemv.hip sha256[:16]") == h and "bytes per launch" in vals:
+        # counter-derived bytes per launch, valid only for the kernel sources they were taken with
+        from block_diffusion_draft_tap_amd import prof_report
+        vals = prof_report.read_summary(tfile)
+        if vals.get("kernel sources sha256[:16]") == prof_report.kernel_sources_hash() and "bytes per launch" in vals:
             traffic = float(vals["bytes per launch"])
 
     res = {

@@ -25,7 +25,8 @@ DFLASH_ACT_GELU_TANH, DFLASH_ACT_SILU = 0, 1
 EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "dflash_invocations",
            "dflash_context_project", "dflash_ctx_kv_append", "dflash_draft_layer", "dflash_draft_forward",
            "dflash_lm_head_argmax", "dflash_lm_head_workspace_bytes", "dflash_verify_greedy",
-           "dflash_verify_workspace_bytes", "dflash_trace_head_events"]
+           "dflash_verify_workspace_bytes", "dflash_trace_head_stamps",
+           "dflash_lm_head_workgroups", "dflash_wall_clock_hz"]
 
 
 class DflashError(RuntimeError):
@@ -91,8 +92,12 @@ def _load():
     lib.dflash_verify_greedy.restype = ctypes.c_int
     lib.dflash_verify_workspace_bytes.argtypes = [I32, I32, I32]
     lib.dflash_verify_workspace_bytes.restype = SZ
-    lib.dflash_trace_head_events.argtypes = [VP, VP]
-    lib.dflash_trace_head_events.restype = None
+    lib.dflash_trace_head_stamps.argtypes = [VP, ctypes.c_int32]
+    lib.dflash_trace_head_stamps.restype = None
+    lib.dflash_lm_head_workgroups.argtypes = [ctypes.c_int32]
+    lib.dflash_lm_head_workgroups.restype = ctypes.c_int32
+    lib.dflash_wall_clock_hz.argtypes = []
+    lib.dflash_wall_clock_hz.restype = ctypes.c_double
     return lib
 
 
@@ -318,28 +323,30 @@ def verify_workspace(B, gamma, V, device="cuda"):
     return torch.empty(lib.dflash_verify_workspace_bytes(B, gamma, V), dtype=torch.uint8, device=device)
 
 
-def dflash_trace_head_events(start=None, stop=None):
-    """Record torch.cuda.Event `start`/`stop` around every LM-head GEMV (None, None: off)."""
-    if start is None or stop is None:
-        lib.dflash_trace_head_events(None, None)
+def dflash_trace_head_stamps(stamps=None):
+    """Route LM-head workgroup wall-clock stamps into `stamps` (a uint64-sized
+    int64 device tensor; None: off)."""
+    if stamps is None:
+        lib.dflash_trace_head_stamps(None, 0)
     else:
-        if not start.cuda_event or not stop.cuda_event:
-            raise DflashError("trace events must be recorded once first (torch creates them lazily)")
-        lib.dflash_trace_head_events(start.cuda_event, stop.cuda_event)
+        assert stamps.dtype == torch.int64 and stamps.is_cuda and stamps.is_contiguous()
+        lib.dflash_trace_head_stamps(_ptr(stamps), stamps.numel())
 
 
-_hip = None
+def dflash_lm_head_workgroups(V):
+    return lib.dflash_lm_head_workgroups(V)
 
 
-def event_elapsed_ms(start, stop):
-    """hipEventElapsedTime on two torch.cuda.Event handles recorded by the
-    library (torch does not know about records it did not make itself).
-    Returns None if the runtime reports an error (e.g. not recorded)."""
-    global _hip
-    if _hip is None:
-        _hip = ctypes.CDLL("libamdhip64.so")
-        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        _hip.hipEventElapsedTime.restype = ctypes.c_int
-    ms = ctypes.c_float(0.0)
-    rc = _hip.hipEventElapsedTime(ctypes.byref(ms), start.cuda_event, stop.cuda_event)
-    return float(ms.value) if rc == 0 else None
+def dflash_wall_clock_hz():
+    return lib.dflash_wall_clock_hz()
+
+
+def stamps_duration_s(stamps, launches=1):
+    """Kernel durations (seconds) from a stamp buffer: per launch, the last
+    workgroup end minus the first workgroup start."""
+    a = stamps.cpu().numpy().astype(np.int64).reshape(launches, -1, 2)
+    hz = lib.dflash_wall_clock_hz()
+    if hz <= 0:
+        raise DflashError("the runtime reports no wall-clock rate")
+    return [(int(x[:, 1].max()) - int(x[:, 0].min())) / hz for x in a]
+

@@ -18,8 +18,8 @@ using namespace dfl;
 namespace {
 
 std::atomic<uint64_t> g_invocations{0};
-std::atomic<void*> g_trace_start{nullptr};
-std::atomic<void*> g_trace_stop{nullptr};
+std::atomic<uint64_t*> g_stamps{nullptr};  // LM-head workgroup wall-clock stamps
+std::atomic<int32_t> g_stamps_cap{0};
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -142,9 +142,10 @@ int rpw_for(int N) { return N >= 16384 ? 4 : (N >= 2048 ? 2 : 1); }
 #ifndef DFL_SMALL_WGS
 #define DFL_SMALL_WGS 512
 #endif
-// LM-head workgroups; each loops over row tiles of 16 vocabulary rows
+// LM-head workgroups; each loops over row tiles of 16 vocabulary rows (768: three
+// workgroups per CU at the head kernel's register budget, all resident at once)
 #ifndef DFL_LM_WGS
-#define DFL_LM_WGS 512
+#define DFL_LM_WGS 768
 #endif
 constexpr int kLmWgs = DFL_LM_WGS;
 // one argmax partial per LM-head workgroup; the head runs 4 rows per wavefront
@@ -246,6 +247,7 @@ hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStr
         if (epi == EPI_ARGMAX) {
             q.part_val = p.part_val + (int64_t)r0 * p.nblocks;
             q.part_idx = p.part_idx + (int64_t)r0 * p.nblocks;
+            if (p.stamps) q.stamps = p.stamps + (int64_t)(r0 / maxm) * 2 * p.nblocks;
         }
         const hipError_t e = launch_gemv(wtype, pro, epi, maxm, q, layers, s);
         if (e != hipSuccess) return e;
@@ -369,17 +371,9 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
     p.nblocks = lm_nblocks(V);
     p.part_val = pv;
     p.part_idx = pi;
-    void* ev0 = g_trace_start.load();
-    void* ev1 = g_trace_stop.load();
-    bool trace = ev0 && ev1;
-    if (trace) {
-        // a capturing stream cannot keep timing records: trace eager launches only
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) trace = false;
-    }
-    if (trace) DFL_HIP(hipEventRecord(static_cast<hipEvent_t>(ev0), s));
+    uint64_t* st = g_stamps.load();
+    if (st && g_stamps_cap.load() >= 2 * p.nblocks * ((rows + 7) / 8)) p.stamps = st;
     DFL_HIP(gemv_rows(wtype_of(E.dtype), PRO_TAPS, EPI_ARGMAX, p, rows, s));
-    if (trace) DFL_HIP(hipEventRecord(static_cast<hipEvent_t>(ev1), s));
     DFL_HIP(launch_argmax_merge(pv, pi, p.nblocks, rows, ids, maxl, s));
     return DFLASH_OK;
 }
@@ -413,14 +407,18 @@ const char* dflash_status_string(int status) {
 
 uint64_t dflash_invocations(void) { return g_invocations.load(); }
 
-void dflash_trace_head_events(void* start, void* stop) {
-    if (start && stop) {
-        g_trace_start.store(start);
-        g_trace_stop.store(stop);
-    } else {
-        g_trace_start.store(nullptr);
-        g_trace_stop.store(nullptr);
-    }
+void dflash_trace_head_stamps(uint64_t* stamps, int32_t capacity) {
+    g_stamps_cap.store(stamps ? capacity : 0);
+    g_stamps.store(stamps);
+}
+
+int32_t dflash_lm_head_workgroups(int32_t V) { return V > 0 ? lm_nblocks(V) : 0; }
+
+double dflash_wall_clock_hz(void) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0.0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0.0;
+    return 1000.0 * khz;
 }
 
 int dflash_context_project(const dflash_model* M, const void* const* taps, int64_t tap_ld, int32_t n, float* h_ctx,

@@ -282,6 +282,10 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
     float* red = xsum + (WT == W_I4 ? MAXM * (KC / 32) : 0);                            // [4*RPW][MAXM]
     float* rinv = red + 4 * RPW * MAXM;                                                 // [MAXM]
 
+    uint64_t t_start = 0;
+    if constexpr (EPI == EPI_ARGMAX) {
+        if (p.stamps) t_start = wall_clock64();
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int layer = blockIdx.y;
     const WeightPtr W = p.w[layer];
@@ -557,6 +561,10 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
         if (tid < p.M) {
             p.part_val[(int64_t)tid * p.nblocks + blockIdx.x] = amax;
             p.part_idx[(int64_t)tid * p.nblocks + blockIdx.x] = aidx;
+        }
+        if (p.stamps && tid == 0) {
+            p.stamps[2 * blockIdx.x] = t_start;
+            p.stamps[2 * blockIdx.x + 1] = wall_clock64();
         }
     }
 }

@@ -96,6 +96,7 @@ struct GemvParams {
     float* part_val;     // [M][nblocks]
     int32_t* part_idx;
     int nblocks;
+    uint64_t* stamps;    // EPI_ARGMAX, optional: wall clock at start and end of each workgroup [nblocks][2]
 };
 
 // Host-side launcher: picks MAXM, the weight type and the modes.

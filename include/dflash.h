@@ -156,14 +156,25 @@ const char* dflash_status_string(int status);
  * that the accelerated path really ran. */
 uint64_t dflash_invocations(void);
 
-/* Instrumentation. With both arguments non-NULL (hipEvent_t handles created
- * by the caller), every later LM-head argmax -- inside dflash_draft_forward and
- * dflash_lm_head_argmax -- records `start` on its stream immediately before
- * its vocabulary GEMV kernel(s) and `stop` immediately after, so the caller can
- * time exactly that kernel. Launches into a capturing stream (graph capture)
- * are not traced. NULL, NULL switches it off. Process-wide setting; callers
- * that trace must not run LM heads concurrently. */
-void dflash_trace_head_events(void* start, void* stop);
+/* Instrumentation. With `stamps` non-NULL (device memory of `capacity`
+ * uint64 entries), every later LM-head argmax -- inside dflash_draft_forward
+ * and dflash_lm_head_argmax, captured graphs included (the pointer is a kernel
+ * argument, so each replay of a captured launch rewrites the same entries) --
+ * makes each vocabulary-GEMV workgroup w write the device wall clock at its
+ * start to stamps[2w] and at its end to stamps[2w + 1]; the kernel's duration
+ * is max(end) - min(start) in ticks of dflash_wall_clock_hz(). A head over M
+ * activation rows runs as ceil(M/8) launches of W = dflash_lm_head_workgroups(V)
+ * workgroups each; launch c writes entries [2cW, 2(c+1)W). When capacity is
+ * below 2W ceil(M/8) nothing is written. NULL switches it off. Process-wide
+ * setting: concurrent LM heads would share the buffer. */
+void dflash_trace_head_stamps(uint64_t* stamps, int32_t capacity);
+
+/* Workgroups of the LM-head GEMV for a vocabulary of V rows (0 if V <= 0). */
+int32_t dflash_lm_head_workgroups(int32_t V);
+
+/* Tick rate of the wall clock the stamps use, for the current device, in Hz
+ * (0 when the runtime cannot report it). */
+double dflash_wall_clock_hz(void);
 
 /* Eq 2 (page 3, #buildContext): h_ctx[r] = RMSNorm(sum_j T_j[r] W_c[:, jH:(j+1)H]^T; ctx_norm).
  *   taps:   HOST array of m device pointers; tap j is [n, H] with row stride

@@ -1,0 +1,49 @@
+"""Host logic of the rocprofv3 summary tool: counter scaling against the
+calibration copy, per-step call counts, and the summary-file parser."""
+
+import csv
+
+from block_diffusion_draft_tap_amd import prof_report
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, val) in enumerate(rows, start=1):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": val})
+
+
+def test_traffic_scaling(tmp_path):
+    copy = 1 << 20  # calibration kernel reads and writes 1 MiB
+    fetch = tmp_path / "f.csv"
+    write = tmp_path / "w.csv"
+    # the fill is not the calibration kernel: the last PyTorch dispatch before the target is
+    _counter_csv(fetch, "FETCH_SIZE", [("void at::native::fill", 0.0), ("void at::native::copy", 512.0),
+                                       ("void dfl::head", 100.0), ("void dfl::head", 102.0)])
+    _counter_csv(write, "WRITE_SIZE", [("void at::native::fill", 1024.0), ("void at::native::copy", 1024.0),
+                                       ("void dfl::head", 1.0), ("void dfl::head", 1.0)])
+    v = prof_report.traffic_summary(str(fetch), str(write), "dfl::head", copy, 200 * 1024)
+    # fetch counter reads half the true bytes -> scale 2; write exact -> scale 1
+    assert v["fetch scale"] == "2.00000" and v["write scale"] == "1.00000"
+    assert int(v["bytes per launch"]) == (101.0 * 2 + 1.0) * 1024
+    assert v["kernel sources sha256[:16]"] == prof_report.kernel_sources_hash()
+
+
+def test_summary_parser_keeps_colons_in_keys(tmp_path):
+    p = tmp_path / "s.md"
+    p.write_text("# t\n\n- kernel sources sha256[:16]: abc\n- bytes per launch: 12\nnot a field: x\n")
+    assert prof_report.read_summary(str(p)) == {"kernel sources sha256[:16]": "abc", "bytes per launch": "12"}
+
+
+def test_stats_per_step(tmp_path):
+    p = tmp_path / "k.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow(["head", 4, 400, 100, 0, 90, 110, 0])
+        w.writerow(["layer", 20, 600, 30, 0, 20, 40, 0])
+    t = prof_report.stats_table(str(p), per_kernel="head")
+    assert "| `layer` | 20 | 5.00 |" in t and "| `head` | 4 | 1.00 |" in t and "60.0%" in t
