@@ -77,22 +77,33 @@ def decode_bf16(bits):
 
 
 def dequant_int4(w, rows=None):
-    """4-bit groups -> float64 [N, K] (optionally only the given rows)."""
+    """4-bit groups -> float64 [N, K] (optionally only the given rows):
+    element k of a row is scale[k // 64] * q_k + bias[k // 64], where q_k is
+    nibble k % 8 (lowest first) of code word k // 8."""
     codes, scales, biases = w["codes"], w["scales"], w["biases"]
     if rows is not None:
         codes, scales, biases = codes[rows], scales[rows], biases[rows]
     N, K8 = codes.shape
-    q = np.empty((N, K8, 8), dtype=np.float64)
-    for j in range(8):
-        q[:, :, j] = (codes >> np.uint32(4 * j)) & np.uint32(15)
-    q = q.reshape(N, K8 * 8)
-    s = np.repeat(decode_bf16(scales), GROUP, axis=1)
-    b = np.repeat(decode_bf16(biases), GROUP, axis=1)
-    return s * q + b
+    # little-endian bytes of a code word: byte j holds nibbles 2j (low) and 2j + 1 (high)
+    by = np.ascontiguousarray(codes, dtype="<u4").view(np.uint8).reshape(N, K8 * 4)
+    q = np.empty((N, K8 * 4, 2), dtype=np.uint8)
+    q[:, :, 0] = by & 15
+    q[:, :, 1] = by >> 4
+    q = q.reshape(N, K8 * 8 // GROUP, GROUP).astype(np.float64)
+    s = decode_bf16(scales)[:, :, None]
+    b = decode_bf16(biases)[:, :, None]
+    return (s * q + b).reshape(N, K8 * 8)
 
 
-def dense(w, rows=None):
-    """Any stored weight -> float64 array."""
+# Whole-matrix decodes are kept (read-only) for the stored arrays they came
+# from, so repeated forwards over one model decode each weight once. Stored
+# weights are treated as immutable: a changed weight is a new array.
+_DENSE_LIMIT = 8 << 30
+_dense_memo = {}
+_dense_bytes = [0]
+
+
+def _decode(w, rows):
     if isinstance(w, dict):
         return dequant_int4(w, rows)
     w = np.asarray(w)
@@ -101,6 +112,24 @@ def dense(w, rows=None):
     if w.dtype == np.uint16:
         return decode_bf16(w)
     return w.astype(np.float64)
+
+
+def dense(w, rows=None):
+    """Any stored weight -> float64 array (whole matrices: a read-only view
+    shared between calls)."""
+    if rows is not None:
+        return _decode(w, rows)
+    hit = _dense_memo.get(id(w))
+    if hit is not None and hit[0] is w:
+        return hit[1]
+    a = _decode(w, None)
+    a.setflags(write=False)
+    if _dense_bytes[0] + a.nbytes > _DENSE_LIMIT:
+        _dense_memo.clear()
+        _dense_bytes[0] = 0
+    _dense_memo[id(w)] = (w, a)
+    _dense_bytes[0] += a.nbytes
+    return a
 
 
 def n_rows(w):

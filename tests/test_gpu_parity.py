@@ -5,8 +5,11 @@ Workloads: the fp32 tiny drafter (context 32), a bf16 GQA drafter with three
 ragged sequences (contexts 200 / 77 / 131 keys: several 32-key chunks plus
 tails, a 1000-token vocabulary that is not a multiple of the head's row tile),
 a bf16 GQA drafter with 42 query rows per kv head (three MFMA row tiles) and
-two ragged sequences, and the default bf16 drafter at its full size (context
-2048, vocab 32768).
+two ragged sequences, the default bf16 drafter at its full size (context
+2048, vocab 32768), and reduced-width versions of the three wide workloads
+that keep their kernel paths: the wide drafter's heads (40 query / 8 kv heads
+of dim 128, 35 query rows per kv head, SiLU FFN, 7-row block), the same heads
+with int4-g64 weights everywhere (4-row block), and 16 ragged sequences.
 """
 
 import numpy as np
@@ -17,7 +20,7 @@ import block_diffusion_draft_tap_amd as dfa
 from block_diffusion_draft_tap_amd import binding as bd
 from gpu_common import (compare_ids, dev, faithful, log, oracle_prefill, rel_err, tol, TOL_F32)
 from oracle import dflash_oracle as O
-from synth import gen, TINY, DEFAULT, scaled
+from synth import gen, TINY, DEFAULT, WIDE, WIDE4, BATCHED, scaled
 
 pytestmark = pytest.mark.gpu
 
@@ -28,11 +31,22 @@ GQA_BF16 = scaled(TINY, name="gqa_bf16", wdtype="bf16", H=256, d=256, hq=4, hkv=
 GQA_ROWS42 = scaled(TINY, name="gqa_rows42", wdtype="bf16", H=256, d=768, hq=12, hkv=2, hd=64, F=512, gamma=7,
                     V=1000, B=2, L=150)
 
+# the wide drafter's attention geometry (d = 40 x 128) with fewer layers and narrower taps / FFN
+WIDE_HEADS = scaled(WIDE, name="wide_heads", H=512, m=2, nl=1, F=1024, V=2048, L=300, B=2)
+# the same heads with int4-g64 weights on every matrix, LM head included
+WIDE4_SMALL = scaled(WIDE4, name="wide4_small", H=512, m=2, nl=2, F=1024, V=2048, L=300, B=2)
+# 16 ragged sequences (batched workload), narrow layers
+BATCHED_SMALL = scaled(BATCHED, name="batched_small", H=256, m=2, d=256, hq=4, hkv=2, hd=64, nl=2, F=512,
+                       V=1000, L=40, L_max=200, B=16)
+
 CASES = {
     "tiny": (TINY, [TINY.L]),
     "gqa_bf16": (GQA_BF16, [200, 77, 131]),
     "gqa_rows42": (GQA_ROWS42, [150, 96]),
     "default": (DEFAULT, [DEFAULT.L]),
+    "wide_heads": (WIDE_HEADS, [300, 157]),
+    "wide4_small": (WIDE4_SMALL, [300, 211]),
+    "batched_small": (BATCHED_SMALL, [int(x) for x in gen.context_lengths(BATCHED_SMALL)]),
 }
 
 _cache = {}
@@ -224,7 +238,7 @@ def test_verify_exhaustive_patterns(V):
     assert np.array_equal(com_o, acc_o + 1)
 
 
-@pytest.mark.parametrize("name", ["tiny", "gqa_bf16", "gqa_rows42"])
+@pytest.mark.parametrize("name", ["tiny", "gqa_bf16", "gqa_rows42", "wide4_small", "batched_small"])
 def test_multi_round_loop(name):
     """Rounds of append(committed rows) -> forward -> verify, both sides driven
     by the oracle's schedule (planted logits realise accept lengths; the
