@@ -112,4 +112,17 @@ __device__ __forceinline__ float load_gain(const void* g, bool f32, int i) {
     return f32 ? static_cast<const float*>(g)[i] : bf16_bits_to_f32(static_cast<const uint16_t*>(g)[i]);
 }
 
+// gains i .. i+7 (i a multiple of 8) as one or two 16-byte loads
+__device__ __forceinline__ void load_gain8(const void* g, bool f32, int i, float (&v)[8]) {
+    if (f32) {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(g) + i);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(g) + i + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(g) + i);
+        v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+        v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+    }
+}
+
 }  // namespace dfl

@@ -72,8 +72,11 @@ int check_dims(const dflash_dims* d) {
 
 int wtype_of(int dtype) { return dtype == DFLASH_F32 ? W_F32 : (dtype == DFLASH_BF16 ? W_BF16 : W_I4); }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 int check_weight(const dflash_weight& w, int rows, int cols, int want_dtype /* -1: any */) {
     if (!w.data) return DFLASH_EINVAL;
+    if (!aligned16(w.data)) return DFLASH_DECLINED;  // rows are read as 16-byte vectors
     if (w.dtype != DFLASH_F32 && w.dtype != DFLASH_BF16 && w.dtype != DFLASH_INT4G64) return DFLASH_EINVAL;
     if (want_dtype >= 0 && w.dtype != want_dtype) return DFLASH_EINVAL;
     if (w.rows != rows || w.cols != cols) return DFLASH_EINVAL;
@@ -103,6 +106,7 @@ int check_model(const dflash_model* M) {
     const int wd = d.wdtype;
     if (!M->ctx_norm || !M->block_pos || !M->out_norm || (d.gamma > 1 && !M->mask_emb)) return DFLASH_EINVAL;
     if (d.nl > 0 && !M->layers) return DFLASH_EINVAL;
+    if (!aligned16(M->ctx_norm) || !aligned16(M->out_norm)) return DFLASH_DECLINED;  // gains: 16-byte vectors
     DFL_TRY(check_weight(M->w_c, d.d, d.m * d.H, wd));
     DFL_TRY(check_weight(M->tok_proj, d.d, d.H, wd));
     DFL_TRY(check_weight(M->out_proj, d.H, d.d, wd));
@@ -111,6 +115,7 @@ int check_model(const dflash_model* M) {
     for (int i = 0; i < d.nl; ++i) {
         const dflash_layer& L = M->layers[i];
         if (!L.attn_norm || !L.ffn_norm) return DFLASH_EINVAL;
+        if (!aligned16(L.attn_norm) || !aligned16(L.ffn_norm)) return DFLASH_DECLINED;
         DFL_TRY(check_weight(L.w_qkv, (d.hq + 2 * d.hkv) * d.hd, d.d, wd));
         DFL_TRY(check_weight(L.w_o, d.d, d.hq * d.hd, wd));
         DFL_TRY(check_weight(L.w_gate_up, 2 * d.F, d.d, wd));

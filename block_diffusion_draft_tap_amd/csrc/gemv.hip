@@ -313,6 +313,18 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
         }
     }
 
+    // EPI_RESID: this thread's first residual value (first tile, first epilogue slot) is
+    // read now, alongside the weights, instead of after the reduction. Each output is
+    // owned by one workgroup and the residual stream is not this launch's input.
+    const int first_tile = tile;
+    float rpre = 0.f;
+    if constexpr (EPI == EPI_RESID) {
+        if (tid < 4 * RPW * MAXM) {
+            const int m = tid / (4 * RPW), n = tile * 4 * RPW + (tid - m * 4 * RPW);
+            if (m < p.M && n < p.N) rpre = p.out[(int64_t)m * p.out_ld + n];
+        }
+    }
+
     // EPI_KV: sequence and cache position of each activation row, resolved once
     int* meta_b = reinterpret_cast<int*>(rinv + MAXM);
     int* meta_pos = meta_b + MAXM;
@@ -335,12 +347,22 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
 
     constexpr bool kRegNorm = (PRO == PRO_NORM) && (WT != W_I4) && (MAXM == 8);
     if (kRegNorm && single && K <= kRegNormMaxK) {
-        // one round trip: each wavefront loads whole rows into registers (the
-        // gain goes to LDS meanwhile), reduces the sum of squares with
-        // shuffles and writes the normalised, rounded row to LDS
-        float* gl = reinterpret_cast<float*>(meta_b + 2 * MAXM);  // [K] gain
+        // one round trip: each wavefront loads whole rows and the matching gains
+        // into registers, reduces the sum of squares with shuffles and writes the
+        // normalised, rounded row to LDS
         constexpr int RW = MAXM / 4, UM = kRegNormMaxK / 512;
         float xr[RW][UM][8];
+        float gr[UM][8];
+#pragma unroll
+        for (int u = 0; u < UM; ++u) {
+            const int k = lane * 8 + u * 512;
+            if (k < K) {
+                load_gain8(p.gain[layer], p.gain_f32, k, gr[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) gr[u][e] = 0.f;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < RW; ++j) {
             const int m = wave + 4 * j;
@@ -355,7 +377,6 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
                 }
             }
         }
-        for (int k = tid; k < K; k += kBlock) gl[k] = load_gain(p.gain[layer], p.gain_f32, k);
         float rr[RW];
 #pragma unroll
         for (int j = 0; j < RW; ++j) {
@@ -367,7 +388,6 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
             ss = wave_sum(ss);
             rr[j] = 1.0f / sqrtf(ss / (float)K + p.eps);
         }
-        __syncthreads();  // gain in LDS
 #pragma unroll
         for (int j = 0; j < RW; ++j) {
             const int m = wave + 4 * j;
@@ -377,7 +397,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
                 if (k < K) {
                     float v[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = (m < p.M) ? xr[j][u][e] * rr[j] * gl[k + e] : 0.f;
+                    for (int e = 0; e < 8; ++e) v[e] = (m < p.M) ? xr[j][u][e] * rr[j] * gr[u][e] : 0.f;
                     if constexpr (WT == W_BF16) {
                         uint4 o;
                         o.x = pack_bf16x2(v[0], v[1]);
@@ -523,7 +543,8 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
                         o[(int64_t)m * p.out_ld + n] = p.round_out ? round_bf16(y) : y;
                     }
                 } else if constexpr (EPI == EPI_RESID) {
-                    p.out[(int64_t)m * p.out_ld + n] += y;
+                    float* o = p.out + (int64_t)m * p.out_ld + n;
+                    *o = ((t == tid && tile == first_tile) ? rpre : *o) + y;
                 } else if constexpr (EPI == EPI_BLOCKINIT) {
                     const int64_t b = p.seq_base + m;
                     const int d = p.N;
@@ -585,7 +606,6 @@ static hipError_t launch_one(const GemvParams& p, int layers, hipStream_t s) {
     KC = (KC + unit - 1) / unit * unit;
     size_t smem = (size_t)MAXM * KC * sizeof(X) + (WT == W_I4 ? (size_t)MAXM * (KC / 32) * 4 : 0) +
                   (size_t)4 * RPW * MAXM * 4 + (size_t)MAXM * 4 + (size_t)2 * MAXM * 4;
-    if (PRO == PRO_NORM && WT != W_I4 && MAXM == 8) smem += (size_t)kRegNormMaxK * 4;
     const int ntiles = (EPI == EPI_GATED) ? (q.F + 2 * RPW - 1) / (2 * RPW) : (q.N + 4 * RPW - 1) / (4 * RPW);
     int grid_x = ntiles;
     // persistent tiles only when the K range is staged once

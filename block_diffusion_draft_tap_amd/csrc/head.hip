@@ -30,6 +30,8 @@ __global__ __launch_bounds__(kBlock) void argmax_merge_kernel(const float* part_
     const int m = blockIdx.x;
     float v = -INFINITY;
     int i = 0x7fffffff;
+    // (max, lowest index) is order-independent: the loop is unrolled so a thread's loads go out together
+#pragma unroll 4
     for (int j = threadIdx.x; j < nblocks; j += blockDim.x)
         argmax_pick(v, i, part_val[(int64_t)m * nblocks + j], part_idx[(int64_t)m * nblocks + j]);
     block_argmax(v, i, sv, si);
@@ -50,6 +52,7 @@ __global__ __launch_bounds__(kBlock) void verify_partial_kernel(const float* log
     float v = -INFINITY;
     int i = 0x7fffffff;
     if ((V & 3) == 0) {
+#pragma unroll 4
         for (int j = v0 + 4 * threadIdx.x; j < v1; j += 4 * blockDim.x) {
             const float4 a = *reinterpret_cast<const float4*>(src + j);
             argmax_pick(v, i, a.x, j);
@@ -94,45 +97,58 @@ __global__ __launch_bounds__(64) void verify_final_kernel(const float* part_val,
 
 // dst[r] = RMSNorm(sum_z src[z][r]; gain): the split-K partials are added in
 // a fixed order (z = 0, 1, ...); dst may alias src when there is one split.
+// Rows of up to KP*256 elements with up to kMaxZ splits take the fast path:
+// every load of a thread is issued before the first add (indexes past the row
+// or the split count are clamped to valid addresses and their values unused).
+constexpr int kMaxZ = 8;
+
+template <int KP>
 __global__ __launch_bounds__(kBlock) void rownorm_kernel(const float* src, int nsplit, int64_t split_stride,
                                                          float* dst, int d, const void* gain, int gain_f32,
                                                          float eps) {
     __shared__ float sv[4];
-    constexpr int kPer = 8;  // row elements held per thread (d <= 2048 fast path)
     const int64_t roff = (int64_t)blockIdx.x * d;
-    float vals[kPer];
-    const bool held = d <= kPer * (int)blockDim.x;
+    const int tid = threadIdx.x;
+    float vals[KP];
     float s = 0.f;
+    const bool fast = d <= KP * kBlock && nsplit <= kMaxZ;
+    if (fast) {
+        float t[kMaxZ][KP];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int k = threadIdx.x + j * blockDim.x;
-        float v = 0.f;
-        if (held && k < d) {
-            for (int z = 0; z < nsplit; ++z) v += src[z * split_stride + roff + k];
-            s += v * v;
+        for (int z = 0; z < kMaxZ; ++z) {
+            const int64_t zo = (int64_t)min(z, nsplit - 1) * split_stride + roff;
+#pragma unroll
+            for (int j = 0; j < KP; ++j) t[z][j] = src[zo + min(tid + j * kBlock, d - 1)];
         }
-        vals[j] = v;
-    }
-    if (!held) {
-        for (int k = threadIdx.x; k < d; k += blockDim.x) {
+#pragma unroll
+        for (int j = 0; j < KP; ++j) {
+            float v = 0.f;
+#pragma unroll
+            for (int z = 0; z < kMaxZ; ++z)
+                if (z < nsplit) v += t[z][j];
+            vals[j] = (tid + j * kBlock < d) ? v : 0.f;
+            s += vals[j] * vals[j];
+        }
+    } else {
+        for (int k = tid; k < d; k += kBlock) {
             float v = 0.f;
             for (int z = 0; z < nsplit; ++z) v += src[z * split_stride + roff + k];
             s += v * v;
         }
     }
     s = wave_sum(s);
-    if ((threadIdx.x & 63) == 0) sv[threadIdx.x >> 6] = s;
+    if ((tid & 63) == 0) sv[tid >> 6] = s;
     __syncthreads();
     const float tot = sv[0] + sv[1] + sv[2] + sv[3];
     const float r = 1.0f / sqrtf(tot / (float)d + eps);
-    if (held) {
+    if (fast) {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int k = threadIdx.x + j * blockDim.x;
+        for (int j = 0; j < KP; ++j) {
+            const int k = tid + j * kBlock;
             if (k < d) dst[roff + k] = vals[j] * r * load_gain(gain, gain_f32, k);
         }
     } else {
-        for (int k = threadIdx.x; k < d; k += blockDim.x) {
+        for (int k = tid; k < d; k += kBlock) {
             float v = 0.f;
             for (int z = 0; z < nsplit; ++z) v += src[z * split_stride + roff + k];
             dst[roff + k] = v * r * load_gain(gain, gain_f32, k);
@@ -190,8 +206,12 @@ hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int g
 hipError_t launch_rownorm(const float* src, int nsplit, int64_t split_stride, float* dst, int rows, int d,
                           const void* gain, int gain_f32, float eps, hipStream_t s) {
     (void)hipGetLastError();  // report only this launch's status
-    hipLaunchKernelGGL(rownorm_kernel, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
-                       gain_f32, eps);
+    if (d <= 4 * kBlock)
+        hipLaunchKernelGGL(rownorm_kernel<4>, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
+                           gain_f32, eps);
+    else
+        hipLaunchKernelGGL(rownorm_kernel<8>, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
+                           gain_f32, eps);
     return hipGetLastError();
 }
 

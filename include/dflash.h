@@ -24,7 +24,8 @@
  *                       nibble = lowest column; scales, biases: bfloat16
  *                       [rows, cols/64]; w[n, k] = scale[n, k/64] * q + bias[n, k/64].
  *     Norm gains, mask_emb and block_pos are float for DFLASH_F32 models and
- *     bfloat16 otherwise.
+ *     bfloat16 otherwise. Weight data and norm gains are read as 16-byte
+ *     vectors: they must be 16-byte aligned, else the call is DECLINED.
  *   - Rounding contract (bf16 and int4 models; f32 models never round):
  *     accumulation is fp32; the input of every weight product is rounded to
  *     bf16 (nearest-even), as are the Q/K/V projections, the attention output,

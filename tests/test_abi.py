@@ -116,6 +116,15 @@ def test_forward_argument_validation():
     assert lib.dflash_draft_forward(ctypes.byref(fm.c), P, ctypes.byref(fm.kv), 1, P, None, None, P, 1 << 30,
                                     None) == bd.DFLASH_EINVAL
     fm.kv.dtype = bd.DFLASH_BF16
+    # weight data and norm gains are read as 16-byte vectors: other alignments are declined
+    fm.c.out_norm = P + 8
+    assert lib.dflash_draft_forward(ctypes.byref(fm.c), P, ctypes.byref(fm.kv), 1, P, None, None, P, 1 << 30,
+                                    None) == bd.DFLASH_DECLINED
+    fm.c.out_norm = P
+    fm.c.w_c.data = P + 4
+    assert lib.dflash_draft_forward(ctypes.byref(fm.c), P, ctypes.byref(fm.kv), 1, P, None, None, P, 1 << 30,
+                                    None) == bd.DFLASH_DECLINED
+    fm.c.w_c.data = P
     # a valid request reaches the device gate: served on gfx950, declined without one
     rc = lib.dflash_draft_layer(ctypes.byref(fm.c), 9, P, ctypes.byref(fm.kv), 1, P, 1 << 30, None)
     assert rc == bd.DFLASH_EINVAL  # layer index out of range
