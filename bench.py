@@ -159,6 +159,77 @@ def profile_head(d, dev, launches=20):
     log(f"[profile-head] copy {COPY_BYTES} B, {launches} LM-head launches ({d.V} x {d.H}, {rows} rows)")
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+
+
+def bench_prefill(d, dev, args):
+    """Context prefill of every sequence of the workload in one pass: the
+    context projection (Eq 2) of all sum(L) rows, then every layer's context
+    K/V. bf16 models run both as matrix-core GEMMs. Weights and taps are drawn
+    on the device (N(0, 0.02) and N(0, 1) in bf16): the values do not change
+    the work, and drawing ~10 GB of taps on the host would dominate the run."""
+    import torch
+    import block_diffusion_draft_tap_amd as dfa
+    from block_diffusion_draft_tap_amd import binding as bd
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+
+    def rnd(shape, std):
+        return (torch.randn(*shape, generator=g, device=dev) * std).to(torch.bfloat16)
+
+    log(f"[prefill] drawing {d.name} weights on the device")
+    w = {}
+    for name in gen.weight_names(d):
+        shape = gen.weight_shape(d, name)
+        w[name] = torch.ones(shape, dtype=torch.bfloat16, device=dev) if gen.is_gain(name) else rnd(shape, 0.02)
+    dm = dfa.DeviceModel(d, w, dev)
+    del w
+    lengths = [int(x) for x in gen.context_lengths(d)]
+    n = sum(lengths)
+    kv = dfa.KVCache(d, d.B, max(lengths) + 64, dev)
+    ws = dfa.workspace(d, d.B, kv.cap, dev)
+    taps = [rnd((n, d.H), 1.0) for _ in range(d.m)]
+    h = torch.empty(n, d.d, dtype=torch.float32, device=dev)
+    offs = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32, device=dev)
+    flops_proj = 2.0 * n * d.m * d.H * d.d
+    flops_kv = 2.0 * n * d.d * 2 * d.hkv * d.hd * d.nl
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    reps = max(1, args.steps)
+    proj_ms, kv_ms = [], []
+    for r in range(reps + 1):
+        kv.len.zero_()
+        torch.cuda.synchronize()
+        ev[0].record()
+        bd.check(dfa.dflash_context_project(dm, taps, h, ws), "context_project")
+        ev[1].record()
+        bd.check(dfa.dflash_ctx_kv_append(dm, h, offs, None, kv, ws), "append")
+        ev[2].record()
+        torch.cuda.synchronize()
+        if r > 0:  # the first pass is the warm-up
+            proj_ms.append(ev[0].elapsed_time(ev[1]))
+            kv_ms.append(ev[1].elapsed_time(ev[2]))
+    assert kv.len.cpu().tolist() == lengths
+    pm, km = float(np.median(proj_ms)), float(np.median(kv_ms))
+    tot_tf = (flops_proj + flops_kv) / ((pm + km) / 1e3) / 1e12
+    res = {
+        "metric": "context prefill (projection + per-layer K/V) TFLOP/s at 1 MI355X; % MFMA bf16 roofline",
+        "value": round(tot_tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "higher_is_better": True,
+        "dtype": "bf16" if d.wdtype == "bf16" else d.wdtype,
+        "data": "synthetic (weights and taps drawn on the device)",
+        "config": {"workload": describe(d, lengths), "rows": n},
+        "projection": {"ms": round(pm, 3), "tflops": round(flops_proj / (pm / 1e3) / 1e12, 2),
+                       "flops": flops_proj},
+        "kv": {"ms": round(km, 3), "tflops": round(flops_kv / (km / 1e3) / 1e12, 2), "flops": flops_kv},
+        "roofline": {"bound": "mfma", "achieved": round(tot_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tot_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +242,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch every call from the host (no graphs)")
     ap.add_argument("--profile-head", action="store_true",
                     help="counter workload: a 256 MiB device copy (calibration), then eager LM-head launches")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the context prefill (projection + K/V of every context row) instead of the round")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -192,6 +265,9 @@ def main():
     if args.profile_head:
         profile_head(d, dev)
         return
+    if args.prefill:
+        bench_prefill(d, dev, args)
+        return
 
     t_setup = time.perf_counter()
     log(f"[bench] generating weights for {d.name}")
@@ -208,22 +284,23 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
+    ws = dfa.workspace(d, B, kv.cap, dev)
+
     # prefill the retained context (untimed)
     log("[bench] prefilling the context")
     for b in range(B):
         L = lengths[b]
         taps = [up(t) for t in gen.make_taps(d, 0, L, stream="ctx", seq=b)]
         h = torch.empty(L, d.d, dtype=torch.float32, device=dev)
-        bd.check(dfa.dflash_context_project(dm, taps, h), "context_project")
+        bd.check(dfa.dflash_context_project(dm, taps, h, ws), "context_project")
         offs = torch.zeros(B + 1, dtype=torch.int32, device=dev)
         offs[b + 1:] = L
-        bd.check(dfa.dflash_ctx_kv_append(dm, h, offs, None, kv), "append")
+        bd.check(dfa.dflash_ctx_kv_append(dm, h, offs, None, kv, ws), "append")
         del taps, h
     torch.cuda.synchronize()
     len0 = kv.len.clone()
     assert kv.len.cpu().tolist() == lengths
 
-    ws = dfa.workspace(d, B, kv.cap, dev)
     vws = bd.verify_workspace(B, d.gamma, d.V, dev)
     offs = torch.arange(0, (B + 1) * W, W, dtype=torch.int32, device=dev)
     h_new = torch.empty(B * W, d.d, dtype=torch.float32, device=dev)

@@ -146,6 +146,8 @@ def make_dims(d):
 
 
 def _to_dev(a, device):
+    if isinstance(a, torch.Tensor):
+        return a.to(device).contiguous()
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
@@ -165,6 +167,13 @@ class Weight:
             self.data = _to_dev(stored["codes"], device)
             self.scales = _to_dev(stored["scales"], device)
             self.biases = _to_dev(stored["biases"], device)
+        elif isinstance(stored, torch.Tensor):
+            if stored.dtype not in (torch.bfloat16, torch.float32) or stored.dim() != 2:
+                raise DflashError("device weights are 2-D bfloat16 or float32 tensors")
+            self.dtype = DFLASH_BF16 if stored.dtype == torch.bfloat16 else DFLASH_F32
+            self.rows, self.cols = stored.shape
+            self.data = _to_dev(stored, device)
+            self.scales = self.biases = None
         else:
             a = np.asarray(stored)
             self.dtype = DFLASH_BF16 if a.dtype == np.uint16 else DFLASH_F32
@@ -183,6 +192,8 @@ def cat_rows(parts):
     """Concatenate stored matrices along the output axis (fused layouts)."""
     if isinstance(parts[0], dict):
         return {k: np.concatenate([p[k] for p in parts], axis=0) for k in ("codes", "scales", "biases")}
+    if isinstance(parts[0], torch.Tensor):
+        return torch.cat(parts, dim=0)
     return np.concatenate([np.asarray(p) for p in parts], axis=0)
 
 
@@ -200,7 +211,8 @@ class DeviceModel:
         self._keep = []
 
         def vec(name):
-            t = _to_dev(np.asarray(weights[name]), dev)
+            w = weights[name]
+            t = _to_dev(w if isinstance(w, torch.Tensor) else np.asarray(w), dev)
             self._keep.append(t)
             return t
 
@@ -284,10 +296,11 @@ def dflash_context_project(model, taps, h_ctx, ws=None, stream=None):
                                       0 if ws is None else ws.numel(), _stream(stream))
 
 
-def dflash_ctx_kv_append(model, h_ctx, row_offsets, counts, kv, stream=None):
+def dflash_ctx_kv_append(model, h_ctx, row_offsets, counts, kv, ws=None, stream=None):
     n = h_ctx.shape[0]
     return lib.dflash_ctx_kv_append(ctypes.byref(model.c), _ptr(h_ctx), n, _ptr(row_offsets), _ptr(counts),
-                                    ctypes.byref(kv.c), None, 0, _stream(stream))
+                                    ctypes.byref(kv.c), _ptr(ws), 0 if ws is None else ws.numel(),
+                                    _stream(stream))
 
 
 def dflash_draft_layer(model, layer, h_block, kv, B, ws, stream=None):

@@ -417,9 +417,13 @@ __global__ __launch_bounds__(kBlock) void attn_valu_kernel(const AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per (b, head, block row): combine the partials. The weights
-// exp(m_s - M) are formed once in LDS; each thread group adds a fixed subset
-// of the partials and the groups are combined in a fixed order.
+// One workgroup per (b, head, block row): combine the partials. Thread group
+// gi (HD threads, one head-dim column each) sums the partials gi, gi + G, ...;
+// up to kMergeRegs of them are loaded into registers together with the (m, l)
+// pairs, so the whole merge costs one round trip. The weights exp(m_s - M)
+// are formed once in LDS and the groups are combined in a fixed order.
+constexpr int kMergeRegs = 32;
+
 template <int HD>
 __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) {
     constexpr int G = kBlock / HD;
@@ -434,6 +438,16 @@ __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) 
     const float* base = p.part + ((int64_t)bh * p.nparts * p.gamma + i) * W;
     const int64_t sstride = (int64_t)p.gamma * W;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int gi = t / HD, dcol = t % HD;
+    const bool in_regs = p.nparts <= kMergeRegs * G;
+    float ov[kMergeRegs];
+    if (in_regs) {
+#pragma unroll
+        for (int q = 0; q < kMergeRegs; ++q) {
+            const int sidx = min(gi + q * G, p.nparts - 1);  // clamped: in bounds, unused past nparts
+            ov[q] = base[sidx * sstride + dcol];
+        }
+    }
     float ms = -INFINITY, ls = 0.f;
     if (t < p.nparts) {
         ms = base[t * sstride + HD];
@@ -450,10 +464,15 @@ __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) 
     if (lane == 0) red[wave] = L;
     __syncthreads();
     L = red[0] + red[1] + red[2] + red[3];
-    const int gi = t / HD, dcol = t % HD;
     float acc = 0.f;
+    if (in_regs) {
+#pragma unroll
+        for (int q = 0; q < kMergeRegs; ++q)
+            if (gi + q * G < p.nparts) acc += wts[gi + q * G] * ov[q];
+    } else {
 #pragma unroll 8
-    for (int sidx = gi; sidx < p.nparts; sidx += G) acc += wts[sidx] * base[sidx * sstride + dcol];
+        for (int sidx = gi; sidx < p.nparts; sidx += G) acc += wts[sidx] * base[sidx * sstride + dcol];
+    }
     part[gi][dcol] = acc;
     __syncthreads();
     if (gi == 0) {

@@ -9,6 +9,7 @@
 
 #include "../../include/dflash.h"
 #include "attention.hpp"
+#include "gemm.hpp"
 #include "gemv.hpp"
 #include "head.hpp"
 
@@ -147,6 +148,11 @@ int rpw_for(int N) { return N >= 16384 ? 4 : (N >= 2048 ? 2 : 1); }
 #ifndef DFL_SMALL_WGS
 #define DFL_SMALL_WGS 512
 #endif
+// row counts from which the context projection and the K/V append run as
+// matrix-core GEMMs (prefill) instead of GEMVs
+#ifndef DFL_GEMM_MIN_ROWS
+#define DFL_GEMM_MIN_ROWS 64
+#endif
 // LM-head workgroups; each loops over row tiles of 16 vocabulary rows (768: three
 // workgroups per CU at the head kernel's register budget, all resident at once)
 #ifndef DFL_LM_WGS
@@ -197,6 +203,8 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     const size_t o_ctxp = take((size_t)ctx_splits(d) * B * (d.gamma + 1) * d.d * 4);
     const size_t o_vt = take((size_t)B * d.hkv * d.hd * 32 * 2);
     w.total = off;
+    // the context append of up to B*cap rows keeps one float per row at the base
+    if (w.total < (size_t)B * cap * 4) w.total = align_up((size_t)B * cap * 4);
     char* c = static_cast<char*>(base);
     if (c) {
         w.hd = reinterpret_cast<float*>(c + o_hd);
@@ -452,7 +460,22 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
     p.round_out = 0;  // P stays fp32; the norm follows
     const int splits = ctx_splits(d);
     const size_t part_bytes = (size_t)splits * n * d.d * 4;
-    if (n <= 8 && splits > 1 && ws && ws_bytes >= part_bytes) {
+    if (n >= DFL_GEMM_MIN_ROWS && d.wdtype == DFLASH_BF16 && d.H % 64 == 0 && d.m <= kMaxTaps) {
+        // prefill: P = [T_1 .. T_m] W_c^T on matrix cores, then the norm in place
+        GemmParams g;
+        std::memset(&g, 0, sizeof(g));
+        g.M = n;
+        g.N = d.d;
+        g.K = d.m * d.H;
+        for (int j = 0; j < d.m; ++j) g.a[j] = static_cast<const uint16_t*>(taps[j]);
+        g.a_ld = tap_ld;
+        g.seg_k = d.H;
+        g.b[0] = static_cast<const uint16_t*>(M->w_c.data);
+        g.c = h_ctx;
+        g.c_ld = d.d;
+        DFL_HIP(launch_gemm(GEMM_A_TAPS, GEMM_EPI_F32, g, 1, s));
+        DFL_HIP(launch_rownorm(h_ctx, 1, 0, h_ctx, n, d.d, M->ctx_norm, 0, d.eps, s));
+    } else if (n <= 8 && splits > 1 && ws && ws_bytes >= part_bytes) {
         // few rows: split the long reduction over more workgroups; partials in ws
         p.rpw = 4;
         p.ksplit = splits;
@@ -473,8 +496,6 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
 
 int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, const int32_t* row_offsets,
                          const int32_t* counts, const dflash_kv* kv, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     DFL_TRY(check_model(M));
     const dflash_dims& d = M->dims;
     if (n < 0 || (n > 0 && !h_ctx) || !row_offsets || !kv) return DFLASH_EINVAL;
@@ -482,6 +503,41 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
     DFL_TRY(gate());
     if (n == 0 || d.nl == 0) return DFLASH_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n >= DFL_GEMM_MIN_ROWS && d.wdtype == DFLASH_BF16 && d.d % 64 == 0 && ws && aligned16(ws) &&
+        ws_bytes >= (size_t)n * 4) {
+        // prefill: per-row RMS factors into ws, then every layer's [K | V] = bf16(N) [W_K | W_V]^T
+        // on matrix cores (grid.z = layer), scattered into the cache
+        float* rinv = static_cast<float*>(ws);
+        DFL_HIP(launch_row_rinv(h_ctx, d.d, n, d.d, d.eps, rinv, s));
+        GemmParams g;
+        std::memset(&g, 0, sizeof(g));
+        g.M = n;
+        g.N = 2 * d.hkv * d.hd;
+        g.K = d.d;
+        g.x = h_ctx;
+        g.a_ld = d.d;
+        g.rinv = rinv;
+        g.gain_f32 = 0;
+        for (int i = 0; i < d.nl; ++i) {
+            g.b[i] = static_cast<const uint16_t*>(M->layers[i].w_qkv.data);
+            g.gain[i] = M->layers[i].attn_norm;
+        }
+        g.b_row0 = (int64_t)d.hq * d.hd;  // the K and V rows of the fused QKV matrix
+        g.kcache = kv->k;
+        g.vcache = kv->v;
+        g.len = kv->len;
+        g.row_offsets = row_offsets;
+        g.counts = counts;
+        g.B = kv->B;
+        g.hkv = d.hkv;
+        g.hd = d.hd;
+        g.cap = kv->cap;
+        g.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
+        DFL_HIP(launch_gemm(GEMM_A_NORM, GEMM_EPI_KV, g, d.nl, s));
+        DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
+        g_invocations++;
+        return DFLASH_OK;
+    }
     GemvParams p = base_params(d);
     for (int i = 0; i < d.nl; ++i) {
         p.w[i] = wptr(M->layers[i].w_qkv);

@@ -185,7 +185,8 @@ double dflash_wall_clock_hz(void);
  * Workspace: optional. For n <= 8 rows and a workspace of
  * dflash_workspace_bytes(dims, B, cap) bytes with B*(gamma+1) >= n, the long
  * reduction is split across more workgroups (partial sums in ws, added in a
- * fixed order); otherwise ws may be NULL. */
+ * fixed order); otherwise ws may be NULL. From 64 rows on, bf16 models run the
+ * projection as a matrix-core GEMM (prefill; no workspace needed). */
 int dflash_context_project(const dflash_model* M, const void* const* taps, int64_t tap_ld, int32_t n,
                            float* h_ctx, void* ws, size_t ws_bytes, void* stream);
 
@@ -200,7 +201,10 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
  *                rows of a round); NULL appends all rows.
  *   Rows that would pass cap are not written and len[b] stops at cap (the
  *   caller sizes cap; see dflash_workspace_bytes).
- * No workspace is used (ws may be NULL). */
+ * Workspace: optional. For bf16 models, n >= 64 rows and a 16-byte aligned
+ * workspace of at least 4n bytes (dflash_workspace_bytes(dims, B, cap) always
+ * holds B*cap rows), the projection runs as one matrix-core GEMM over all
+ * layers (per-row RMS factors kept in ws); otherwise as GEMVs. ws may be NULL. */
 int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, const int32_t* row_offsets,
                          const int32_t* counts, const dflash_kv* kv, void* ws, size_t ws_bytes, void* stream);
 

@@ -71,9 +71,11 @@ class Setup:
         bd.check(dfa.dflash_context_project(self.dm, self.taps_d, self.h_ctx), "context_project")
         offs = np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int32)
         self.offs_d = torch.from_numpy(offs).cuda()
-        bd.check(dfa.dflash_ctx_kv_append(self.dm, self.h_ctx, self.offs_d, None, self.kv), "ctx_kv_append")
-        torch.cuda.synchronize()
         self.ws = dfa.workspace(dims, self.B, self.kv.cap)
+        # with a workspace, a prefill of bf16 rows runs as matrix-core GEMMs
+        bd.check(dfa.dflash_ctx_kv_append(self.dm, self.h_ctx, self.offs_d, None, self.kv, self.ws),
+                 "ctx_kv_append")
+        torch.cuda.synchronize()
         log(f"[setup] {name}: done")
 
 
@@ -115,6 +117,36 @@ def _block_input(s, round_idx=0):
     H = O.block_init(anchors, s.w["E_in"], s.w["tok_proj"], s.w["mask_emb"], s.w["block_pos"], s.dims.gamma,
                      s.fm)
     return anchors, H
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16", "wide4_small", "default"])
+def test_projection_paths_agree(name):
+    """The GEMV paths of the same calls: the K/V append without a workspace
+    (per-row GEMVs, 32 rows a launch), the context projection of 40 rows (GEMVs,
+    32 rows a launch) and of 8 rows with a workspace (split reduction): each
+    against the oracle."""
+    s = get(name)
+    d = s.dims
+    kv2 = dfa.KVCache(d, s.B, s.cap)
+    bd.check(dfa.dflash_ctx_kv_append(s.dm, s.h_ctx, s.offs_d, None, kv2), "append without ws")
+    torch.cuda.synchronize()
+    t = tol(d)
+    for i in range(d.nl):
+        for b in range(s.B):
+            L = s.lengths[b]
+            ek = rel_err(kv2.k[i, b, :, :L].permute(1, 0, 2), s.ctx.k[i][b])
+            ev = rel_err(kv2.v[i, b, :, :, :L].permute(2, 0, 1), s.ctx.v[i][b])
+            assert ek <= t and ev <= t, (i, b, ek, ev)
+    assert torch.equal(kv2.len, s.kv.len)
+    ref = np.concatenate(s.Hs)
+    for n, use_ws in ((40, False), (8, True)):
+        taps = [t_[:n] for t_ in s.taps_d]
+        h = torch.empty(n, d.d, dtype=torch.float32, device="cuda")
+        bd.check(dfa.dflash_context_project(s.dm, taps, h, s.ws if use_ws else None), "project")
+        torch.cuda.synchronize()
+        err = rel_err(h, ref[:n])
+        log(f"[{name}] {n} rows, ws {use_ws}: H_ctx rel err {err:.3e}")
+        assert err <= t
 
 
 @pytest.mark.parametrize("name", NAMES)
