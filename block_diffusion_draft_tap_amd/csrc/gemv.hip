@@ -498,18 +498,20 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
             const float tot = wave_sum_many<NV>(vals, lane);
             const int vi = wave_sum_many_index<NV>(lane);
             constexpr int SPAN = (NV >= 64) ? 1 : 64 / NV;
-            if ((lane % SPAN) == 0) red[(wave * RPW) * MAXM + vi] = tot;
-        }
-        __syncthreads();
-
-        // ---- epilogue of this tile
-        if constexpr (EPI == EPI_ARGMAX) {
-            if (tid < p.M) {
-                for (int u = 0; u < 4 * RPW; ++u) {
-                    const int n = tile * 4 * RPW + u;
-                    if (n < p.N) argmax_pick(amax, aidx, red[u * MAXM + tid], n);
-                }
+            if constexpr (EPI == EPI_ARGMAX) {
+                // each lane keeps a running (max, lowest index) for its (row slot r, activation
+                // row m) across the workgroup's tiles; the wavefronts are combined once at the end
+                const int r = vi / MAXM, m = vi - r * MAXM;
+                const int n = tile * 4 * RPW + wave * RPW + r;
+                if ((lane % SPAN) == 0 && m < p.M && n < p.N) argmax_pick(amax, aidx, tot, n);
+            } else {
+                if ((lane % SPAN) == 0) red[(wave * RPW) * MAXM + vi] = tot;
             }
+        }
+        if constexpr (EPI != EPI_ARGMAX) __syncthreads();
+
+        // ---- epilogue of this tile (the argmax epilogue runs after the last tile)
+        if constexpr (EPI == EPI_ARGMAX) {
         } else if constexpr (EPI == EPI_GATED) {
             for (int t = tid; t < 2 * RPW * MAXM; t += kBlock) {
                 const int m = t / (2 * RPW), q = t - m * (2 * RPW);
@@ -575,13 +577,31 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
         }
         if (!more) break;
         tile = next;
-        __syncthreads();  // red[] is rewritten by the next tile
+        if constexpr (EPI != EPI_ARGMAX) __syncthreads();  // red[] is rewritten by the next tile
     }
 
     if constexpr (EPI == EPI_ARGMAX) {
+        // combine the running (max, index) of every wavefront lane slot per activation row
+        constexpr int NV = RPW * MAXM;
+        constexpr int SPAN = (NV >= 64) ? 1 : 64 / NV;
+        // the activation staging area (at least MAXM * 32 elements, >= 8 * NV bytes) is free once
+        // every wavefront has finished its last tile
+        __syncthreads();
+        float* rv = reinterpret_cast<float*>(smem);               // [4][NV]
+        int* ri = reinterpret_cast<int*>(smem) + 4 * NV;          // [4][NV]
+        if ((lane % SPAN) == 0) {
+            const int vi = wave_sum_many_index<NV>(lane);
+            rv[wave * NV + vi] = amax;
+            ri[wave * NV + vi] = aidx;
+        }
+        __syncthreads();
         if (tid < p.M) {
-            p.part_val[(int64_t)tid * p.nblocks + blockIdx.x] = amax;
-            p.part_idx[(int64_t)tid * p.nblocks + blockIdx.x] = aidx;
+            float v = -INFINITY;
+            int i = 0x7fffffff;
+            for (int w = 0; w < 4; ++w)
+                for (int r = 0; r < RPW; ++r) argmax_pick(v, i, rv[w * NV + r * MAXM + tid], ri[w * NV + r * MAXM + tid]);
+            p.part_val[(int64_t)tid * p.nblocks + blockIdx.x] = v;
+            p.part_idx[(int64_t)tid * p.nblocks + blockIdx.x] = i;
         }
         if (p.stamps && tid == 0) {
             p.stamps[2 * blockIdx.x] = t_start;
@@ -606,6 +626,8 @@ static hipError_t launch_one(const GemvParams& p, int layers, hipStream_t s) {
     KC = (KC + unit - 1) / unit * unit;
     size_t smem = (size_t)MAXM * KC * sizeof(X) + (WT == W_I4 ? (size_t)MAXM * (KC / 32) * 4 : 0) +
                   (size_t)4 * RPW * MAXM * 4 + (size_t)MAXM * 4 + (size_t)2 * MAXM * 4;
+    // the argmax epilogue combines its wavefronts' (value, index) slots at the start of LDS
+    if (EPI == EPI_ARGMAX && smem < (size_t)8 * 4 * RPW * MAXM) smem = (size_t)8 * 4 * RPW * MAXM;
     const int ntiles = (EPI == EPI_GATED) ? (q.F + 2 * RPW - 1) / (2 * RPW) : (q.N + 4 * RPW - 1) / (4 * RPW);
     int grid_x = ntiles;
     // persistent tiles only when the K range is staged once
