@@ -242,6 +242,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch every call from the host (no graphs)")
     ap.add_argument("--profile-head", action="store_true",
                     help="counter workload: a 256 MiB device copy (calibration), then eager LM-head launches")
+    ap.add_argument("--device-taps", action="store_true",
+                    help="draw the prefilled context's taps on the device (large batched contexts)")
     ap.add_argument("--prefill", action="store_true",
                     help="time the context prefill (projection + K/V of every context row) instead of the round")
     args = ap.parse_args()
@@ -268,6 +270,9 @@ def main():
     if args.prefill:
         bench_prefill(d, dev, args)
         return
+    if args.device_taps and not args.skip_cpu:
+        print("--device-taps changes the prefilled context: use it with --skip-cpu", file=sys.stderr)
+        sys.exit(2)
 
     t_setup = time.perf_counter()
     log(f"[bench] generating weights for {d.name}")
@@ -290,7 +295,13 @@ def main():
     log("[bench] prefilling the context")
     for b in range(B):
         L = lengths[b]
-        taps = [up(t) for t in gen.make_taps(d, 0, L, stream="ctx", seq=b)]
+        if args.device_taps:
+            gt = torch.Generator(device=dev)
+            gt.manual_seed(1000 + b)
+            taps = [torch.randn(L, d.H, generator=gt, device=dev).to(torch.bfloat16 if d.wdtype != "f32" else
+                                                                      torch.float32) for _ in range(d.m)]
+        else:
+            taps = [up(t) for t in gen.make_taps(d, 0, L, stream="ctx", seq=b)]
         h = torch.empty(L, d.d, dtype=torch.float32, device=dev)
         bd.check(dfa.dflash_context_project(dm, taps, h, ws), "context_project")
         offs = torch.zeros(B + 1, dtype=torch.int32, device=dev)
@@ -307,7 +318,7 @@ def main():
 
     # per-round inputs, resident on the device
     accept = [gen.accept_schedule(d, r) for r in range(R)]
-    head_wgs = bd.dflash_lm_head_workgroups(d.V)
+    head_wgs = bd.dflash_lm_head_workgroups(d.V, d.H, d.wdtype)
     head_launches = (B * d.gamma + 7) // 8
     rounds = []
     for r in range(R):

@@ -94,7 +94,7 @@ def _load():
     lib.dflash_verify_workspace_bytes.restype = SZ
     lib.dflash_trace_head_stamps.argtypes = [VP, ctypes.c_int32]
     lib.dflash_trace_head_stamps.restype = None
-    lib.dflash_lm_head_workgroups.argtypes = [ctypes.c_int32]
+    lib.dflash_lm_head_workgroups.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.dflash_lm_head_workgroups.restype = ctypes.c_int32
     lib.dflash_wall_clock_hz.argtypes = []
     lib.dflash_wall_clock_hz.restype = ctypes.c_double
@@ -346,8 +346,11 @@ def dflash_trace_head_stamps(stamps=None):
         lib.dflash_trace_head_stamps(_ptr(stamps), stamps.numel())
 
 
-def dflash_lm_head_workgroups(V):
-    return lib.dflash_lm_head_workgroups(V)
+def dflash_lm_head_workgroups(V, H, dtype):
+    """dtype: a DFLASH_* weight format or a workload weight name ("f32", "bf16", "int4g64")."""
+    if isinstance(dtype, str):
+        dtype = _WD[dtype]
+    return lib.dflash_lm_head_workgroups(V, H, dtype)
 
 
 def dflash_wall_clock_hz():

@@ -160,7 +160,11 @@ int rpw_for(int N) { return N >= 16384 ? 4 : (N >= 2048 ? 2 : 1); }
 #endif
 constexpr int kLmWgs = DFL_LM_WGS;
 // one argmax partial per LM-head workgroup; the head runs 4 rows per wavefront
-int lm_nblocks(int V) { return (V + 15) / 16 < kLmWgs ? (V + 15) / 16 : kLmWgs; }
+// Row tiles of 16 vocabulary rows; a head whose rows (H) stage in one pass runs
+// persistent workgroups (kLmWgs, or one per CU for long rows), a longer one a
+// workgroup per tile.
+int lm_tiles(int V) { return (V + 15) / 16; }
+int lm_nblocks(int V, int H, int wtype) { return gemv_head_grid(wtype, H, lm_tiles(V), kLmWgs); }
 // split-K of the context projection for few rows: K ranges of at most 2048
 int ctx_splits(const dflash_dims& d) { return (d.m * d.H + 2047) / 2048; }
 
@@ -197,7 +201,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     const size_t o_o = take(rows * d.hq * d.hd * 4);
     const size_t o_a = take(rows * d.F * 4);
     const size_t o_y = take(rows * d.H * 4);
-    const size_t nb = lm_nblocks(d.V);
+    const size_t nb = lm_tiles(d.V);  // enough for any head layout
     const size_t o_lmv = take(rows * nb * 4);
     const size_t o_lmi = take(rows * nb * 4);
     const size_t o_ctxp = take((size_t)ctx_splits(d) * B * (d.gamma + 1) * d.d * 4);
@@ -381,7 +385,7 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
     p.tap_ld = H;
     p.H = H;
     p.src_f32 = y_f32;
-    p.nblocks = lm_nblocks(V);
+    p.nblocks = lm_nblocks(V, H, wtype_of(E.dtype));
     p.part_val = pv;
     p.part_idx = pi;
     uint64_t* st = g_stamps.load();
@@ -425,7 +429,10 @@ void dflash_trace_head_stamps(uint64_t* stamps, int32_t capacity) {
     g_stamps.store(stamps);
 }
 
-int32_t dflash_lm_head_workgroups(int32_t V) { return V > 0 ? lm_nblocks(V) : 0; }
+int32_t dflash_lm_head_workgroups(int32_t V, int32_t H, int32_t dtype) {
+    if (V <= 0 || H <= 0 || (dtype != DFLASH_F32 && dtype != DFLASH_BF16 && dtype != DFLASH_INT4G64)) return 0;
+    return lm_nblocks(V, H, wtype_of(dtype));
+}
 
 double dflash_wall_clock_hz(void) {
     int dev = 0, khz = 0;
@@ -638,7 +645,7 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
 
 size_t dflash_lm_head_workspace_bytes(int32_t V, int32_t M) {
     if (V <= 0 || M <= 0) return 0;
-    return 2 * align_up((size_t)M * lm_nblocks(V) * 4);
+    return 2 * align_up((size_t)M * lm_tiles(V) * 4);
 }
 
 int dflash_lm_head_argmax(const dflash_weight* E_out, const void* y, int32_t y_dtype, int32_t M, int32_t* ids,

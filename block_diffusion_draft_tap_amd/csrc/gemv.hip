@@ -613,6 +613,58 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
 // ---------------------------------------------------------------------------
 // host dispatch
 
+// LDS staging of the activation rows. Reductions up to the normal budget stage
+// once and run the requested persistent grid; longer ones up to the wide budget
+// (one workgroup per CU) stage once and run one persistent workgroup per CU;
+// longer still, one workgroup per row tile stages chunk by chunk.
+constexpr int kStageBytesWide = 136 * 1024;
+
+static int num_cus() {
+    static int n = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            return 256;
+        return v;
+    }();
+    return n;
+}
+
+template <int WT, int MAXM>
+static int stage_cols(int budget) {
+    typedef typename WTraits<WT>::X X;
+    return (budget / (MAXM * (int)sizeof(X))) / 512 * 512;
+}
+
+struct StagePlan {
+    int KC;       // staged K elements per pass
+    int max_wgs;  // persistent workgroup cap (0: one per tile)
+};
+
+template <int WT, int MAXM>
+static StagePlan stage_plan(int kslice, int max_wgs) {
+    const int kc = stage_cols<WT, MAXM>(kStageBytes);
+    if (kslice <= kc) return {kc, max_wgs};
+    const int kw = stage_cols<WT, MAXM>(kStageBytesWide);
+    if (max_wgs > 0 && kslice <= kw) return {kw, max_wgs < num_cus() ? max_wgs : num_cus()};
+    return {kc, max_wgs};
+}
+
+template <int WT>
+static int head_grid_t(int K, int ntiles, int max_wgs) {
+    const StagePlan sp = stage_plan<WT, 8>(K, max_wgs);
+    return (sp.max_wgs > 0 && K <= sp.KC && ntiles > sp.max_wgs) ? sp.max_wgs : ntiles;
+}
+
+int gemv_head_grid(int wtype, int K, int ntiles, int max_wgs) {
+    switch (wtype) {
+        case W_F32: return head_grid_t<W_F32>(K, ntiles, max_wgs);
+        case W_BF16: return head_grid_t<W_BF16>(K, ntiles, max_wgs);
+        case W_I4: return head_grid_t<W_I4>(K, ntiles, max_wgs);
+    }
+    return 0;
+}
+
 template <int WT, int PRO, int EPI, int MAXM, int RPW>
 static hipError_t launch_one(const GemvParams& p, int layers, hipStream_t s) {
     typedef typename WTraits<WT>::X X;
@@ -620,8 +672,9 @@ static hipError_t launch_one(const GemvParams& p, int layers, hipStream_t s) {
     GemvParams q = p;
     if (q.ksplit < 1) q.ksplit = 1;
     if (q.kslice <= 0 || q.ksplit == 1) q.kslice = q.K;
-    int KC = kStageBytes / (MAXM * (int)sizeof(X));
-    KC = (KC / 512) * 512;
+    const StagePlan sp = stage_plan<WT, MAXM>(q.kslice, q.max_wgs);
+    q.max_wgs = sp.max_wgs;
+    int KC = sp.KC;
     if (KC >= q.kslice) KC = q.kslice;
     KC = (KC + unit - 1) / unit * unit;
     size_t smem = (size_t)MAXM * KC * sizeof(X) + (WT == W_I4 ? (size_t)MAXM * (KC / 32) * 4 : 0) +

@@ -102,6 +102,11 @@ struct GemvParams {
 // Host-side launcher: picks MAXM, the weight type and the modes.
 hipError_t launch_gemv(int wtype, int pro, int epi, int maxm, const GemvParams& p, int layers, hipStream_t s);
 
+// Grid of a launch with up to 8 activation rows, reduction length K and ntiles
+// row tiles under a persistent-workgroup cap (what the argmax partials are
+// sized by): reductions that stage in one pass run persistent workgroups.
+int gemv_head_grid(int wtype, int K, int ntiles, int max_wgs);
+
 // LDS budget for staged activations per workgroup
 constexpr int kStageBytes = 64 * 1024;
 

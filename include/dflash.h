@@ -164,14 +164,15 @@ uint64_t dflash_invocations(void);
  * makes each vocabulary-GEMV workgroup w write the device wall clock at its
  * start to stamps[2w] and at its end to stamps[2w + 1]; the kernel's duration
  * is max(end) - min(start) in ticks of dflash_wall_clock_hz(). A head over M
- * activation rows runs as ceil(M/8) launches of W = dflash_lm_head_workgroups(V)
+ * activation rows runs as ceil(M/8) launches of W = dflash_lm_head_workgroups(V, H, dtype)
  * workgroups each; launch c writes entries [2cW, 2(c+1)W). When capacity is
  * below 2W ceil(M/8) nothing is written. NULL switches it off. Process-wide
  * setting: concurrent LM heads would share the buffer. */
 void dflash_trace_head_stamps(uint64_t* stamps, int32_t capacity);
 
-/* Workgroups of the LM-head GEMV for a vocabulary of V rows (0 if V <= 0). */
-int32_t dflash_lm_head_workgroups(int32_t V);
+/* Workgroups of the LM-head GEMV for a V x H head of weight format dtype
+ * (DFLASH_F32 / DFLASH_BF16 / DFLASH_INT4G64); 0 for invalid arguments. */
+int32_t dflash_lm_head_workgroups(int32_t V, int32_t H, int32_t dtype);
 
 /* Tick rate of the wall clock the stamps use, for the current device, in Hz
  * (0 when the runtime cannot report it). */

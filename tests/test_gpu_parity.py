@@ -205,9 +205,11 @@ def test_draft_forward(name):
 
 
 @pytest.mark.parametrize("wd", ["f32", "bf16", "int4g64"])
-@pytest.mark.parametrize("M", [1, 5, 8, 13])
-def test_lm_head_argmax_planted_and_random(wd, M):
-    dims = scaled(TINY, wdtype=wd, H=256, V=1000)
+@pytest.mark.parametrize("M,H", [(1, 256), (5, 256), (8, 256), (13, 256), (7, 5120)])
+def test_lm_head_argmax_planted_and_random(wd, M, H):
+    """H = 5120 (the wide workloads' rows) is longer than one staging chunk: the
+    head then runs one workgroup per 16-row tile instead of persistent tiles."""
+    dims = scaled(TINY, wdtype=wd, H=H, V=1000 if H <= 256 else 3001)
     E = gen.make_weight(dims, "E_out")
     Ed = O.dense(E)
     rng = np.random.default_rng(M)
