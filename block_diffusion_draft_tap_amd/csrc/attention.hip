@@ -80,9 +80,10 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     constexpr int DT = HD / 16;  // head-dim tiles of O
     constexpr int PLD = kChunk + 8;  // padded P row (bf16 elements)
     constexpr int PBYTES = 4 * 2 * NRT * 16 * PLD * 2;  // P tiles, high and low parts, per wavefront
-    constexpr int OBYTES = 3 * NRT * DT * 4 * 64 * 4;   // o of wavefronts 1..3 in register order
+    constexpr int OBYTES = 4 * NRT * DT * 4 * 64 * 4;   // o of the four wavefronts in register order
     __shared__ __align__(16) unsigned char lds[PBYTES > OBYTES ? PBYTES : OBYTES];
-    __shared__ float wm[4][NRT * 16], wl[4][NRT * 16];
+    __shared__ float wm[4][NRT * 16], wl[4][NRT * 16], wf[4][NRT * 16];
+    __shared__ float rowm[NRT * 16], rowl[NRT * 16];
     typedef uint16_t PTile[2][NRT][16][PLD];
     PTile* plds = reinterpret_cast<PTile*>(lds);
 
@@ -230,7 +231,9 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
             for (int rt = 0; rt < NRT; ++rt) o[rt][dt] = mfma16(pl[rt], vb[dt], mfma16(pa[rt], vb[dt], o[rt][dt]));
     }
 
-    // merge the four wavefronts in LDS; wavefront 0 writes the workgroup's partial
+    // merge the four wavefronts in LDS: each writes its o; the per-row weights
+    // exp2(m_w - M) and sums L are formed once; then all threads add the four
+    // contributions (wavefront order 0..3) of (row, dim) elements and store them
     __syncthreads();  // the P tiles are dead; their LDS is reused below
     if (col == 0) {
 #pragma unroll
@@ -241,52 +244,40 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
                 wl[wave][rt * 16 + 4 * grp + e] = l[rt][e];
             }
     }
-    __syncthreads();
-    float* ob = reinterpret_cast<float*>(lds);  // [3][NRT][DT][4][64]
-    float Mrow[NRT][4], Lrow[NRT][4];
+    float* ob = reinterpret_cast<float*>(lds);  // [4][NRT][DT][4][64]
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = rt * 16 + 4 * grp + e;
-            const float M = fmaxf(fmaxf(wm[0][r], wm[1][r]), fmaxf(wm[2][r], wm[3][r]));
-            const float f = (m[rt][e] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[rt][e] - M);
-            float L = 0.f;
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) L += (wm[w][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(wm[w][r] - M) * wl[w][r];
-            Mrow[rt][e] = M;
-            Lrow[rt][e] = L;
-            if (wave > 0) {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) ob[((((wave - 1) * NRT + rt) * DT + dt) * 4 + e) * 64 + lane] = o[rt][dt][e] * f;
-            } else {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) o[rt][dt][e] *= f;
-            }
-        }
+            for (int e = 0; e < 4; ++e) ob[(((wave * NRT + rt) * DT + dt) * 4 + e) * 64 + lane] = o[rt][dt][e];
     __syncthreads();
-    if (wave == 0) {
-        const int W = HD + 2;
+    for (int r = threadIdx.x; r < NRT * 16; r += kBlock) {
+        const float M = fmaxf(fmaxf(wm[0][r], wm[1][r]), fmaxf(wm[2][r], wm[3][r]));
+        float L = 0.f;
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
+        for (int w = 0; w < 4; ++w) {
+            const float f = (wm[w][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(wm[w][r] - M);
+            wf[w][r] = f;
+            L += f * wl[w][r];
+        }
+        rowm[r] = M;
+        rowl[r] = L;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < R * HD; idx += kBlock) {
+        const int r = idx / HD, dim = idx - r * HD;
+        const int rt = r >> 4, rr = r & 15, e = rr & 3, ln = (rr >> 2) * 16 + (dim & 15), dt = dim >> 4;
+        float v = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = rt * 16 + 4 * grp + e;
-                if (r >= R) continue;
-                const int h = g * qpg + r / p.gamma, i = r % p.gamma;
-                float* dst = p.part + ((((int64_t)b * p.hq + h) * p.nparts + s) * p.gamma + i) * W;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    float v = o[rt][dt][e];
-#pragma unroll
-                    for (int w = 0; w < 3; ++w) v += ob[(((w * NRT + rt) * DT + dt) * 4 + e) * 64 + lane];
-                    dst[dt * 16 + col] = v;
-                }
-                if (col == 0) {
-                    dst[HD] = Mrow[rt][e] * 0.6931471805599453f;  // natural-log units
-                    dst[HD + 1] = Lrow[rt][e];
-                }
-            }
+        for (int w = 0; w < 4; ++w) v += wf[w][r] * ob[(((w * NRT + rt) * DT + dt) * 4 + e) * 64 + ln];
+        const int h = g * qpg + r / p.gamma, i = r % p.gamma;
+        float* dst = p.part + ((((int64_t)b * p.hq + h) * p.nparts + s) * p.gamma + i) * (HD + 2);
+        dst[dim] = v;
+        if (dim == 0) {
+            dst[HD] = rowm[r] * 0.6931471805599453f;  // natural-log units
+            dst[HD + 1] = rowl[r];
+        }
     }
 }
 

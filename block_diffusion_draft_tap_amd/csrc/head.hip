@@ -97,10 +97,12 @@ __global__ __launch_bounds__(64) void verify_final_kernel(const float* part_val,
 
 // dst[r] = RMSNorm(sum_z src[z][r]; gain): the split-K partials are added in
 // a fixed order (z = 0, 1, ...); dst may alias src when there is one split.
-// Rows of up to KP*256 elements with up to kMaxZ splits take the fast path:
-// every load of a thread is issued before the first add (indexes past the row
-// or the split count are clamped to valid addresses and their values unused).
-constexpr int kMaxZ = 8;
+// A thread holds KP elements of its row (rows of up to KP*256 elements) and
+// takes the splits in batches of kZB: every load of a batch is issued before
+// the first add (indexes past the row or the split count are clamped to valid
+// addresses and their values unused), so a row costs ceil(nsplit / kZB) round
+// trips.
+constexpr int kZB = 4;
 
 template <int KP>
 __global__ __launch_bounds__(kBlock) void rownorm_kernel(const float* src, int nsplit, int64_t split_stride,
@@ -110,49 +112,38 @@ __global__ __launch_bounds__(kBlock) void rownorm_kernel(const float* src, int n
     const int64_t roff = (int64_t)blockIdx.x * d;
     const int tid = threadIdx.x;
     float vals[KP];
+#pragma unroll
+    for (int j = 0; j < KP; ++j) vals[j] = 0.f;
+    for (int z0 = 0; z0 < nsplit; z0 += kZB) {
+        float t[kZB][KP];
+#pragma unroll
+        for (int zb = 0; zb < kZB; ++zb) {
+            const int64_t zo = (int64_t)min(z0 + zb, nsplit - 1) * split_stride + roff;
+#pragma unroll
+            for (int j = 0; j < KP; ++j) t[zb][j] = src[zo + min(tid + j * kBlock, d - 1)];
+        }
+#pragma unroll
+        for (int zb = 0; zb < kZB; ++zb)
+            if (z0 + zb < nsplit) {
+#pragma unroll
+                for (int j = 0; j < KP; ++j) vals[j] += t[zb][j];
+            }
+    }
     float s = 0.f;
-    const bool fast = d <= KP * kBlock && nsplit <= kMaxZ;
-    if (fast) {
-        float t[kMaxZ][KP];
 #pragma unroll
-        for (int z = 0; z < kMaxZ; ++z) {
-            const int64_t zo = (int64_t)min(z, nsplit - 1) * split_stride + roff;
-#pragma unroll
-            for (int j = 0; j < KP; ++j) t[z][j] = src[zo + min(tid + j * kBlock, d - 1)];
-        }
-#pragma unroll
-        for (int j = 0; j < KP; ++j) {
-            float v = 0.f;
-#pragma unroll
-            for (int z = 0; z < kMaxZ; ++z)
-                if (z < nsplit) v += t[z][j];
-            vals[j] = (tid + j * kBlock < d) ? v : 0.f;
-            s += vals[j] * vals[j];
-        }
-    } else {
-        for (int k = tid; k < d; k += kBlock) {
-            float v = 0.f;
-            for (int z = 0; z < nsplit; ++z) v += src[z * split_stride + roff + k];
-            s += v * v;
-        }
+    for (int j = 0; j < KP; ++j) {
+        if (tid + j * kBlock >= d) vals[j] = 0.f;
+        s += vals[j] * vals[j];
     }
     s = wave_sum(s);
     if ((tid & 63) == 0) sv[tid >> 6] = s;
     __syncthreads();
     const float tot = sv[0] + sv[1] + sv[2] + sv[3];
     const float r = 1.0f / sqrtf(tot / (float)d + eps);
-    if (fast) {
 #pragma unroll
-        for (int j = 0; j < KP; ++j) {
-            const int k = tid + j * kBlock;
-            if (k < d) dst[roff + k] = vals[j] * r * load_gain(gain, gain_f32, k);
-        }
-    } else {
-        for (int k = tid; k < d; k += kBlock) {
-            float v = 0.f;
-            for (int z = 0; z < nsplit; ++z) v += src[z * split_stride + roff + k];
-            dst[roff + k] = v * r * load_gain(gain, gain_f32, k);
-        }
+    for (int j = 0; j < KP; ++j) {
+        const int k = tid + j * kBlock;
+        if (k < d) dst[roff + k] = vals[j] * r * load_gain(gain, gain_f32, k);
     }
 }
 
@@ -209,9 +200,14 @@ hipError_t launch_rownorm(const float* src, int nsplit, int64_t split_stride, fl
     if (d <= 4 * kBlock)
         hipLaunchKernelGGL(rownorm_kernel<4>, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
                            gain_f32, eps);
-    else
+    else if (d <= 8 * kBlock)
         hipLaunchKernelGGL(rownorm_kernel<8>, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
                            gain_f32, eps);
+    else if (d <= 32 * kBlock)
+        hipLaunchKernelGGL(rownorm_kernel<32>, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
+                           gain_f32, eps);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

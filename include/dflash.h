@@ -72,7 +72,8 @@ enum { DFLASH_F32 = 0, DFLASH_BF16 = 1, DFLASH_INT4G64 = 2 };
 enum { DFLASH_ACT_GELU_TANH = 0, DFLASH_ACT_SILU = 1 };
 
 /* Drafter geometry. d must equal hq*hd and hq must be a multiple of hkv
- * (query head h reads key/value head h / (hq/hkv)). hd is 64 or 128.
+ * (query head h reads key/value head h / (hq/hkv)). hd is 64 or 128; d is at
+ * most 8192 (wider drafters are DECLINED).
  * gamma = block query rows = drafted tokens (the verify width is gamma+1). */
 typedef struct {
     int32_t H;       /* target hidden size (tap width and LM-head width)   */
