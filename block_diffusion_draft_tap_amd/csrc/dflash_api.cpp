@@ -167,7 +167,13 @@ constexpr int kLmWgs = DFL_LM_WGS;
 int lm_tiles(int V) { return (V + 15) / 16; }
 int lm_nblocks(int V, int H, int wtype) { return gemv_head_grid(wtype, H, lm_tiles(V), kLmWgs); }
 // split-K of the context projection for few rows: K ranges of at most 2048
-int ctx_splits(const dflash_dims& d) { return (d.m * d.H + 2047) / 2048; }
+#ifndef DFL_CTX_SPLIT_K
+#define DFL_CTX_SPLIT_K 2048
+#endif
+#ifndef DFL_KV_WGS
+#define DFL_KV_WGS DFL_SMALL_WGS  // workgroup cap of the context K/V append, all layers together
+#endif
+int ctx_splits(const dflash_dims& d) { return (d.m * d.H + DFL_CTX_SPLIT_K - 1) / DFL_CTX_SPLIT_K; }
 
 struct Ws {
     float* hd;
@@ -552,7 +558,7 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
         p.gain[i] = M->layers[i].attn_norm;
     }
     p.w_row0 = (int64_t)d.hq * d.hd;  // the K and V rows of the fused QKV matrix
-    p.max_wgs = DFL_SMALL_WGS / d.nl > 0 ? DFL_SMALL_WGS / d.nl : 1;  // per layer (grid.y)
+    p.max_wgs = DFL_KV_WGS / d.nl > 0 ? DFL_KV_WGS / d.nl : 1;  // per layer (grid.y)
     p.N = 2 * d.hkv * d.hd;
     p.K = d.d;
     p.rpw = rpw_for(p.N);
