@@ -318,8 +318,7 @@ def main():
 
     # per-round inputs, resident on the device
     accept = [gen.accept_schedule(d, r) for r in range(R)]
-    head_wgs = bd.dflash_lm_head_workgroups(d.V, d.H, d.wdtype)
-    head_launches = (B * d.gamma + 7) // 8
+    head_wgs, head_launches = bd.dflash_lm_head_workgroups(d.V, d.H, d.wdtype, B * d.gamma)
     rounds = []
     for r in range(R):
         taps_r = [gen.make_taps(d, r * W, W, stream="round", seq=b) for b in range(B)]
@@ -345,7 +344,7 @@ def main():
         # argument: captured graphs keep writing them on every replay)
         bd.dflash_trace_head_stamps(rr["stamps"])
         bd.check(dfa.dflash_context_project(dm, rr["taps"], h_new, ws), "context_project")
-        bd.check(dfa.dflash_ctx_kv_append(dm, h_new, offs, rr["counts"], kv), "append")
+        bd.check(dfa.dflash_ctx_kv_append(dm, h_new, offs, rr["counts"], kv, ws), "append")
         bd.check(dfa.dflash_draft_forward(dm, rr["anchors"], kv, B, rr["ids"], ws), "forward")
         if verify:
             bd.check(dfa.dflash_verify_greedy(rr["T"], rr["ids"], rr["acc"], rr["com"], rr["vids"], vws,
@@ -456,7 +455,8 @@ def main():
         "round_hbm_frac": round(round_gbs / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_kernel (LM head, argmax epilogue)",
+            "kernel": "LM head with argmax epilogue",
+            "launches_x_workgroups": f"{head_launches} x {head_wgs}",
             "achieved": round(head_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -94,7 +94,8 @@ def _load():
     lib.dflash_verify_workspace_bytes.restype = SZ
     lib.dflash_trace_head_stamps.argtypes = [VP, ctypes.c_int32]
     lib.dflash_trace_head_stamps.restype = None
-    lib.dflash_lm_head_workgroups.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.dflash_lm_head_workgroups.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.dflash_lm_head_workgroups.restype = ctypes.c_int32
     lib.dflash_wall_clock_hz.argtypes = []
     lib.dflash_wall_clock_hz.restype = ctypes.c_double
@@ -346,11 +347,17 @@ def dflash_trace_head_stamps(stamps=None):
         lib.dflash_trace_head_stamps(_ptr(stamps), stamps.numel())
 
 
-def dflash_lm_head_workgroups(V, H, dtype):
-    """dtype: a DFLASH_* weight format or a workload weight name ("f32", "bf16", "int4g64")."""
+def dflash_lm_head_workgroups(V, H, dtype, M, y_dtype=None):
+    """(workgroups per launch, launches) of the LM head over M rows. dtype: a
+    DFLASH_* weight format or a workload weight name ("f32", "bf16", "int4g64");
+    y_dtype: the rows' format (default: fp32 rows for an f32 head, bf16 otherwise)."""
     if isinstance(dtype, str):
         dtype = _WD[dtype]
-    return lib.dflash_lm_head_workgroups(V, H, dtype)
+    if y_dtype is None:
+        y_dtype = DFLASH_F32 if dtype == DFLASH_F32 else DFLASH_BF16
+    n = ctypes.c_int32(0)
+    w = lib.dflash_lm_head_workgroups(V, H, dtype, M, y_dtype, ctypes.byref(n))
+    return w, n.value
 
 
 def dflash_wall_clock_hz():

@@ -12,6 +12,7 @@
 #include "gemm.hpp"
 #include "gemv.hpp"
 #include "head.hpp"
+#include "skinny.hpp"
 
 using namespace dfl;
 
@@ -174,6 +175,55 @@ int lm_nblocks(int V, int H, int wtype) { return gemv_head_grid(wtype, H, lm_til
 #define DFL_KV_WGS DFL_SMALL_WGS  // workgroup cap of the context K/V append, all layers together
 #endif
 int ctx_splits(const dflash_dims& d) { return (d.m * d.H + DFL_CTX_SPLIT_K - 1) / DFL_CTX_SPLIT_K; }
+// block row counts from which the projections of a bf16 drafter run on matrix
+// cores (one pass over each weight matrix) instead of 8-row GEMV passes
+#ifndef DFL_SKINNY_MIN_ROWS
+#define DFL_SKINNY_MIN_ROWS 16
+#endif
+bool lm_head_skinny(int wdtype, int y_f32, int rows, int H) {
+    return wdtype == DFLASH_BF16 && !y_f32 && rows >= DFL_SKINNY_MIN_ROWS && H % kSkinnyK == 0;
+}
+bool skinny_ok(const dflash_dims& d, int rows) {
+    return d.wdtype == DFLASH_BF16 && rows >= DFL_SKINNY_MIN_ROWS && d.d % kSkinnyK == 0 && d.F % kSkinnyK == 0 &&
+           d.H % kSkinnyK == 0;
+}
+// fp32 split-K partials of the skinny launches of a forward (rows in launches of kSkinnyRows)
+size_t skinny_part_bytes(const dflash_dims& d, int rows) {
+    const int r = rows < kSkinnyRows ? rows : kSkinnyRows;
+    const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
+    const int shapes[4][3] = {{SK_STORE, qkv_rows, d.d}, {SK_RESID, d.d, d.hq * d.hd}, {SK_RESID, d.d, d.F},
+                              {SK_STORE, d.H, d.d}};
+    size_t most = 0;
+    for (const auto& sh : shapes) {
+        int ns = 1, ks = 0;
+        skinny_split(sh[0], sh[1], sh[2], 1, &ns, &ks);
+        const size_t b = ns > 1 ? (size_t)ns * r * sh[1] * 4 : 0;
+        if (b > most) most = b;
+    }
+    return most;
+}
+
+// Workspace of the matrix-core paths for n context rows (a round's appended
+// block rows); 0 when those paths do not apply. Context projection: split-K
+// partial sums [nsplit][n][d]. K/V append: each layer's normalised rows, bf16
+// [nl][n][d], then the split-K partials [nl][nsplit][n][2 hkv hd].
+bool ctx_skinny_rows(const dflash_dims& d, int n) {
+    return d.wdtype == DFLASH_BF16 && n >= DFL_SKINNY_MIN_ROWS && n <= kSkinnyRows;
+}
+size_t ctx_project_skinny_bytes(const dflash_dims& d, int n) {
+    if (!ctx_skinny_rows(d, n) || d.H % kSkinnyK || d.m > kMaxTaps) return 0;
+    int ns = 1, ks = 0;
+    skinny_split(SK_PARTIAL, d.d, d.m * d.H, 1, &ns, &ks);
+    return (size_t)ns * n * d.d * 4;
+}
+size_t kv_append_norm_bytes(const dflash_dims& d, int n) { return align_up((size_t)d.nl * n * d.d * 2); }
+size_t kv_append_skinny_bytes(const dflash_dims& d, int n) {
+    if (!ctx_skinny_rows(d, n) || d.d % kSkinnyK || d.nl < 1) return 0;
+    const int N = 2 * d.hkv * d.hd;
+    int ns = 1, ks = 0;
+    skinny_split(SK_KV, N, d.d, d.nl, &ns, &ks);
+    return kv_append_norm_bytes(d, n) + (ns > 1 ? (size_t)d.nl * ns * n * N * 4 : 0);
+}
 
 struct Ws {
     float* hd;
@@ -186,6 +236,9 @@ struct Ws {
     int32_t* lmi;
     float* ctxp;   // split-K partials of the context projection [splits][B*(gamma+1)][d]
     uint16_t* vt;  // block values, head-dim major [B][hkv][hd][32] (bf16 models)
+    uint16_t* an;  // matrix-core path: normalised block rows, bf16 [B*gamma][d]
+    float* skp;    // matrix-core path: split-K partial sums
+    bool skinny;   // the block projections run on matrix cores
     size_t total;
     int nsplit;  // attention workgroups per (sequence, kv head)
     int nparts;  // attention partials per (sequence, head)
@@ -213,9 +266,17 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     const size_t o_lmi = take(rows * nb * 4);
     const size_t o_ctxp = take((size_t)ctx_splits(d) * B * (d.gamma + 1) * d.d * 4);
     const size_t o_vt = take((size_t)B * d.hkv * d.hd * 32 * 2);
+    w.skinny = skinny_ok(d, (int)rows);
+    const size_t o_an = take(w.skinny ? rows * d.d * 2 : 0);
+    const size_t o_skp = take(w.skinny ? skinny_part_bytes(d, (int)rows) : 0);
     w.total = off;
-    // the context append of up to B*cap rows keeps one float per row at the base
+    // the context append of up to B*cap rows keeps one float per row at the base; the
+    // matrix-core context paths of a round's B*(gamma+1) rows use the base as well
     if (w.total < (size_t)B * cap * 4) w.total = align_up((size_t)B * cap * 4);
+    const int nr = B * (d.gamma + 1);
+    const size_t ctx_need = align_up(ctx_project_skinny_bytes(d, nr)), kv_need = align_up(kv_append_skinny_bytes(d, nr));
+    if (w.total < ctx_need) w.total = ctx_need;
+    if (w.total < kv_need) w.total = kv_need;
     char* c = static_cast<char*>(base);
     if (c) {
         w.hd = reinterpret_cast<float*>(c + o_hd);
@@ -228,6 +289,8 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
         w.lmi = reinterpret_cast<int32_t*>(c + o_lmi);
         w.ctxp = reinterpret_cast<float*>(c + o_ctxp);
         w.vt = reinterpret_cast<uint16_t*>(c + o_vt);
+        w.an = reinterpret_cast<uint16_t*>(c + o_an);
+        w.skp = reinterpret_cast<float*>(c + o_skp);
     }
     return w;
 }
@@ -279,6 +342,107 @@ hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStr
     return hipSuccess;
 }
 
+// matrix-core projections of `rows` block rows, in launches of up to kSkinnyRows
+hipError_t skinny_rows(int epi, SkinnyParams p, int rows, hipStream_t s) {
+    skinny_split(epi, p.N, p.K, p.layers, &p.nsplit, &p.kslice);
+    p.nblocks = skinny_tiles(epi, p.N);
+    const size_t out_esz = (epi == SK_GATED || (epi == SK_STORE && p.out_bf16)) ? 2 : 4;
+    for (int r0 = 0; r0 < rows; r0 += kSkinnyRows) {
+        SkinnyParams q = p;
+        q.M = rows - r0 < kSkinnyRows ? rows - r0 : kSkinnyRows;
+        q.a = p.a + (int64_t)r0 * p.a_ld;
+        q.row_base = p.row_base + r0;
+        if (p.out) q.out = static_cast<char*>(p.out) + (size_t)r0 * p.out_ld * out_esz;
+        if (epi == SK_ARGMAX) {
+            q.part_val = p.part_val + (int64_t)r0 * p.nblocks;
+            q.part_idx = p.part_idx + (int64_t)r0 * p.nblocks;
+            if (p.stamps) q.stamps = p.stamps + (int64_t)(r0 / kSkinnyRows) * 2 * p.nblocks;
+        }
+        const hipError_t e = launch_skinny(epi, q, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+SkinnyParams skinny_params(const dflash_weight& W, const uint16_t* a, int64_t a_ld, int N, int K, float* part) {
+    SkinnyParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.a = a;
+    p.a_ld = a_ld;
+    p.w[0] = static_cast<const uint16_t*>(W.data);
+    p.layers = 1;
+    p.N = N;
+    p.K = K;
+    p.part = part;
+    return p;
+}
+
+hipError_t norm_rows(const float* x, int rows, int K, const void* gain, float eps, uint16_t* dst, hipStream_t s) {
+    NormRowsParams q;
+    std::memset(&q, 0, sizeof(q));
+    q.x = x;
+    q.x_ld = K;
+    q.rows = rows;
+    q.K = K;
+    q.layers = 1;
+    q.eps = eps;
+    q.gain[0] = gain;
+    q.dst = dst;
+    q.dst_ld = K;
+    return launch_norm_rows(q, s);
+}
+
+// a draft layer's projections on matrix cores (bf16 drafter, 16 or more block
+// rows), with the rounding points of the GEMV path: bf16 normalised rows, Q/K/V,
+// O and A. skinny_qkv: before the attention; skinny_out_ffn: after it
+int skinny_qkv(const dflash_model* M, int i, float* h, int rows, const Ws& w, hipStream_t s) {
+    const dflash_dims& d = M->dims;
+    const dflash_layer& L = M->layers[i];
+    const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
+    {  // [Q | K_b | V_b] = bf16(RMSNorm(H; attn_norm)) W_qkv^T, V_b head-dim major
+        DFL_HIP(norm_rows(h, rows, d.d, L.attn_norm, d.eps, w.an, s));
+        SkinnyParams p = skinny_params(L.w_qkv, w.an, d.d, qkv_rows, d.d, w.skp);
+        p.out = w.qkv;
+        p.out_ld = qkv_rows;
+        p.out_bf16 = 1;
+        p.vt = w.vt;
+        p.vt_col = (d.hq + d.hkv) * d.hd;
+        p.gamma = d.gamma;
+        p.hkv = d.hkv;
+        p.hd = d.hd;
+        DFL_HIP(skinny_rows(SK_STORE, p, rows, s));
+    }
+    return DFLASH_OK;
+}
+
+int skinny_out_ffn(const dflash_model* M, int i, float* h, int rows, const Ws& w, hipStream_t s) {
+    const dflash_dims& d = M->dims;
+    const dflash_layer& L = M->layers[i];
+    {  // H += O W_o^T
+        SkinnyParams p = skinny_params(L.w_o, reinterpret_cast<const uint16_t*>(w.o), d.hq * d.hd, d.d,
+                                       d.hq * d.hd, w.skp);
+        p.out = h;
+        p.out_ld = d.d;
+        DFL_HIP(skinny_rows(SK_RESID, p, rows, s));
+    }
+    {  // A = bf16(act(n2 W_gate^T) * (n2 W_up^T)), n2 = bf16(RMSNorm(H; ffn_norm))
+        DFL_HIP(norm_rows(h, rows, d.d, L.ffn_norm, d.eps, w.an, s));
+        SkinnyParams p = skinny_params(L.w_gate_up, w.an, d.d, 2 * d.F, d.d, w.skp);
+        p.F = d.F;
+        p.act = d.act;
+        p.out = w.a;
+        p.out_ld = d.F;
+        DFL_HIP(skinny_rows(SK_GATED, p, rows, s));
+    }
+    {  // H += A W_down^T
+        SkinnyParams p = skinny_params(L.w_down, reinterpret_cast<const uint16_t*>(w.a), d.F, d.d, d.F, w.skp);
+        p.out = h;
+        p.out_ld = d.d;
+        DFL_HIP(skinny_rows(SK_RESID, p, rows, s));
+    }
+    return DFLASH_OK;
+}
+
 int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B, const Ws& w, hipStream_t s) {
     const dflash_dims& d = M->dims;
     const dflash_layer& L = M->layers[i];
@@ -286,7 +450,9 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
     const int rows = B * d.gamma;
     const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
 
-    {  // n = RMSNorm(H; attn_norm); [Q | K_b | V_b] = n W_qkv^T
+    if (w.skinny) {
+        DFL_TRY(skinny_qkv(M, i, h, rows, w, s));
+    } else {  // n = RMSNorm(H; attn_norm); [Q | K_b | V_b] = n W_qkv^T
         GemvParams p = base_params(d);
         p.w[0] = wptr(L.w_qkv);
         p.N = qkv_rows;
@@ -337,6 +503,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         a.round_out = d.wdtype == DFLASH_F32 ? 0 : 1;
         DFL_HIP(launch_attention(a, s));
     }
+    if (w.skinny) return skinny_out_ffn(M, i, h, rows, w, s);
     {  // H += O W_o^T
         GemvParams p = base_params(d);
         p.w[0] = wptr(L.w_o);
@@ -381,6 +548,18 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
 
 int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, int V, int32_t* ids, float* maxl,
             float* pv, int32_t* pi, hipStream_t s) {
+    if (lm_head_skinny(E.dtype, y_f32, rows, H)) {
+        // matrix cores: one pass over the head for all rows, a (max, index) partial per row and tile
+        SkinnyParams p = skinny_params(E, static_cast<const uint16_t*>(y), H, V, H, nullptr);
+        p.part_val = pv;
+        p.part_idx = pi;
+        uint64_t* st = g_stamps.load();
+        const int nt = skinny_tiles(SK_ARGMAX, V), launches = (rows + kSkinnyRows - 1) / kSkinnyRows;
+        if (st && g_stamps_cap.load() >= 2 * nt * launches) p.stamps = st;
+        DFL_HIP(skinny_rows(SK_ARGMAX, p, rows, s));
+        DFL_HIP(launch_argmax_merge(pv, pi, skinny_tiles(SK_ARGMAX, V), rows, ids, maxl, s));
+        return DFLASH_OK;
+    }
     GemvParams p;
     std::memset(&p, 0, sizeof(p));
     p.w[0] = wptr(E);
@@ -436,8 +615,15 @@ void dflash_trace_head_stamps(uint64_t* stamps, int32_t capacity) {
     g_stamps.store(stamps);
 }
 
-int32_t dflash_lm_head_workgroups(int32_t V, int32_t H, int32_t dtype) {
-    if (V <= 0 || H <= 0 || (dtype != DFLASH_F32 && dtype != DFLASH_BF16 && dtype != DFLASH_INT4G64)) return 0;
+int32_t dflash_lm_head_workgroups(int32_t V, int32_t H, int32_t dtype, int32_t M, int32_t y_dtype, int32_t* launches) {
+    if (V <= 0 || H <= 0 || M <= 0 || (dtype != DFLASH_F32 && dtype != DFLASH_BF16 && dtype != DFLASH_INT4G64) ||
+        (y_dtype != DFLASH_F32 && y_dtype != DFLASH_BF16))
+        return 0;
+    if (lm_head_skinny(dtype, y_dtype == DFLASH_F32, M, H)) {
+        if (launches) *launches = (M + kSkinnyRows - 1) / kSkinnyRows;
+        return skinny_tiles(SK_ARGMAX, V);
+    }
+    if (launches) *launches = (M + 7) / 8;
     return lm_nblocks(V, H, wtype_of(dtype));
 }
 
@@ -474,7 +660,26 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
     p.round_out = 0;  // P stays fp32; the norm follows
     const int splits = ctx_splits(d);
     const size_t part_bytes = (size_t)splits * n * d.d * 4;
-    if (n >= DFL_GEMM_MIN_ROWS && d.wdtype == DFLASH_BF16 && d.H % 64 == 0 && d.m <= kMaxTaps) {
+    const size_t sk_bytes = ctx_project_skinny_bytes(d, n);
+    if (sk_bytes > 0 && ws && aligned16(ws) && ws_bytes >= sk_bytes) {
+        // a round's rows: P = [T_1 .. T_m] W_c^T on matrix cores, split-K partials in ws,
+        // added in split order by the norm
+        SkinnyParams q;
+        std::memset(&q, 0, sizeof(q));
+        q.M = n;
+        q.N = d.d;
+        q.K = d.m * d.H;
+        for (int j = 0; j < d.m; ++j) q.a_seg[j] = static_cast<const uint16_t*>(taps[j]);
+        q.a = q.a_seg[0];
+        q.a_ld = tap_ld;
+        q.seg_k = d.H;
+        q.w[0] = static_cast<const uint16_t*>(M->w_c.data);
+        q.layers = 1;
+        q.part = static_cast<float*>(ws);
+        skinny_split(SK_PARTIAL, q.N, q.K, 1, &q.nsplit, &q.kslice);
+        DFL_HIP(launch_skinny(SK_PARTIAL, q, s));
+        DFL_HIP(launch_rownorm(q.part, q.nsplit, (int64_t)n * d.d, h_ctx, n, d.d, M->ctx_norm, 0, d.eps, s));
+    } else if (n >= DFL_GEMM_MIN_ROWS && d.wdtype == DFLASH_BF16 && d.H % 64 == 0 && d.m <= kMaxTaps) {
         // prefill: P = [T_1 .. T_m] W_c^T on matrix cores, then the norm in place
         GemmParams g;
         std::memset(&g, 0, sizeof(g));
@@ -517,6 +722,53 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
     DFL_TRY(gate());
     if (n == 0 || d.nl == 0) return DFLASH_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t sk_bytes = kv_append_skinny_bytes(d, n);
+    if (sk_bytes > 0 && ws && aligned16(ws) && ws_bytes >= sk_bytes) {
+        // a round's rows: every layer's bf16(RMSNorm(h_ctx; attn_norm_i)) into ws, then
+        // [K | V] = those rows [W_K | W_V]^T for all layers in one matrix-core launch
+        // (grid.z = layer), scattered into the cache
+        uint16_t* an = static_cast<uint16_t*>(ws);
+        NormRowsParams q;
+        std::memset(&q, 0, sizeof(q));
+        q.x = h_ctx;
+        q.x_ld = d.d;
+        q.rows = n;
+        q.K = d.d;
+        q.layers = d.nl;
+        q.eps = d.eps;
+        for (int i = 0; i < d.nl; ++i) q.gain[i] = M->layers[i].attn_norm;
+        q.dst = an;
+        q.dst_ld = d.d;
+        q.dst_layer_stride = (int64_t)n * d.d;
+        DFL_HIP(launch_norm_rows(q, s));
+        SkinnyParams p;
+        std::memset(&p, 0, sizeof(p));
+        p.M = n;
+        p.N = 2 * d.hkv * d.hd;
+        p.K = d.d;
+        p.a = an;
+        p.a_ld = d.d;
+        p.a_layer_stride = (int64_t)n * d.d;
+        for (int i = 0; i < d.nl; ++i) p.w[i] = static_cast<const uint16_t*>(M->layers[i].w_qkv.data);
+        p.w_row0 = (int64_t)d.hq * d.hd;  // the K and V rows of the fused QKV matrix
+        p.layers = d.nl;
+        p.part = reinterpret_cast<float*>(static_cast<char*>(ws) + kv_append_norm_bytes(d, n));
+        p.kcache = static_cast<uint16_t*>(kv->k);
+        p.vcache = static_cast<uint16_t*>(kv->v);
+        p.len = kv->len;
+        p.row_offsets = row_offsets;
+        p.counts = counts;
+        p.B = kv->B;
+        p.hkv = d.hkv;
+        p.hd = d.hd;
+        p.cap = kv->cap;
+        p.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
+        skinny_split(SK_KV, p.N, p.K, p.layers, &p.nsplit, &p.kslice);
+        DFL_HIP(launch_skinny(SK_KV, p, s));
+        DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
+        g_invocations++;
+        return DFLASH_OK;
+    }
     if (n >= DFL_GEMM_MIN_ROWS && d.wdtype == DFLASH_BF16 && d.d % 64 == 0 && ws && aligned16(ws) &&
         ws_bytes >= (size_t)n * 4) {
         // prefill: per-row RMS factors into ws, then every layer's [K | V] = bf16(N) [W_K | W_V]^T
@@ -630,7 +882,14 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
     // Y = bf16(bf16(RMSNorm(H; out_norm)) out_proj^T), written straight into y_out
     // when the caller wants it (bf16 for bf16/int4 models, fp32 for fp32 models)
     float* y = y_out ? static_cast<float*>(y_out) : w.y;
-    {
+    if (w.skinny) {
+        DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, w.an, s));
+        SkinnyParams p = skinny_params(M->out_proj, w.an, d.d, d.H, d.d, w.skp);
+        p.out = y;
+        p.out_ld = d.H;
+        p.out_bf16 = 1;
+        DFL_HIP(skinny_rows(SK_STORE, p, rows, s));
+    } else {
         GemvParams p = base_params(d);
         p.w[0] = wptr(M->out_proj);
         p.N = d.H;

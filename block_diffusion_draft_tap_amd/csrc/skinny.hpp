@@ -1,0 +1,91 @@
+// Matrix-core projections of 16 to 128 activation rows (see skinny.hip):
+//   y[m, n] = sum_k A[m, k] W[w_row0 + n, k]
+// with bf16 A and W and fp32 accumulation, each weight row streamed once per
+// launch; grid.z runs several layers' products in one launch.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "gemv.hpp"
+
+namespace dfl {
+
+enum { SK_STORE = 0, SK_RESID = 1, SK_GATED = 2, SK_ARGMAX = 3, SK_KV = 4, SK_PARTIAL = 5 };
+
+constexpr int kSkinnyRows = 128;  // activation rows per launch
+constexpr int kSkinnyK = 128;     // K (and each split's K range) is a multiple of this
+
+struct SkinnyParams {
+    int M, N, K;          // SK_GATED: N = 2F weight rows (gate rows [0, F), up rows [F, 2F))
+    // A: bf16 rows [M, K] at a + z * a_layer_stride (row stride a_ld); with seg_k > 0 the
+    // columns come in segments of seg_k (a multiple of kSkinnyK): column k of row m is
+    // a_seg[k / seg_k][m * a_ld + k % seg_k]
+    const uint16_t* a;
+    int64_t a_ld;
+    int64_t a_layer_stride;
+    const uint16_t* a_seg[kMaxTaps];
+    int seg_k;
+    // bf16 weights [*, K] of layer z; rows w_row0 .. w_row0 + N - 1 are used
+    const uint16_t* w[kMaxLayers];
+    int64_t w_row0;
+    int layers;           // grid.z
+    int F;                // SK_GATED
+    int act;              // SK_GATED: 0 gelu_tanh, 1 silu
+    // split-K: K ranges of kslice (grid.y). fp32 partial sums go to part
+    // [layers][nsplit][M][N]; for SK_STORE / SK_RESID / SK_KV a second kernel adds them in
+    // split order and applies the epilogue, for SK_PARTIAL the caller consumes them
+    int nsplit, kslice;
+    float* part;
+    // SK_STORE: out[m, n] = y, fp32 or (out_bf16) bf16; with vt, bf16 columns n >= vt_col go
+    //   head-dim major to vt[b][head][dim][32], b = (row_base + m) / gamma, key = its remainder
+    // SK_RESID: out[m, n] += y (fp32)
+    // SK_GATED: out[m, j] = bf16(act(y[m, j]) * y[m, F + j]) (bf16)
+    void* out;
+    int64_t out_ld;
+    int out_bf16;
+    uint16_t* vt;
+    int vt_col, row_base, gamma, hkv, hd;
+    // SK_ARGMAX: per row and workgroup tile, the (max, lowest index) of the row's outputs
+    float* part_val;      // [M][nblocks]
+    int32_t* part_idx;
+    int nblocks;          // skinny_tiles(SK_ARGMAX, N)
+    uint64_t* stamps;     // SK_ARGMAX, optional: wall clock at start and end of each workgroup [nblocks][2]
+    // SK_KV: columns [0, hkv*hd) are keys, [hkv*hd, 2*hkv*hd) values (bf16 caches). Row
+    // r = row_base + m belongs to the sequence b with row_offsets[b] <= r < row_offsets[b+1]
+    // and goes to cache position len[b] + (r - row_offsets[b]) when that index is below
+    // counts[b] (all rows when counts is null) and the position below cap
+    uint16_t* kcache;     // [layers][B][hkv][cap][hd]
+    uint16_t* vcache;     // [layers][B][hkv][hd][cap]
+    const int32_t* len;
+    const int32_t* row_offsets;
+    const int32_t* counts;
+    int B, cap;
+    int64_t layer_stride; // cache elements per layer
+};
+
+// workgroup tiles of a launch over N weight rows (the argmax partials per row)
+int skinny_tiles(int epi, int N);
+// split-K of a launch over `layers` products: the number of K ranges and their length
+void skinny_split(int epi, int N, int K, int layers, int* nsplit, int* kslice);
+
+// M in [1, kSkinnyRows], K a multiple of kSkinnyK; nsplit / kslice / nblocks as given by
+// the functions above (part holds layers * nsplit * M * N floats when nsplit > 1 or
+// for SK_PARTIAL)
+hipError_t launch_skinny(int epi, const SkinnyParams& p, hipStream_t s);
+
+// dst + z * dst_layer_stride: rows r of bf16(x[r, k] * (mean_k x[r, k]^2 + eps)^-1/2 * gain[z][k])
+// for rows of K fp32 values (K a multiple of 8, at most 8192), z < layers (grid.y)
+struct NormRowsParams {
+    const float* x;
+    int64_t x_ld;
+    int rows, K, layers, gain_f32;
+    float eps;
+    const void* gain[kMaxLayers];
+    uint16_t* dst;
+    int64_t dst_ld, dst_layer_stride;
+};
+hipError_t launch_norm_rows(const NormRowsParams& p, hipStream_t s);
+
+}  // namespace dfl

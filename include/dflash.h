@@ -162,18 +162,24 @@ uint64_t dflash_invocations(void);
  * uint64 entries), every later LM-head argmax -- inside dflash_draft_forward
  * and dflash_lm_head_argmax, captured graphs included (the pointer is a kernel
  * argument, so each replay of a captured launch rewrites the same entries) --
- * makes each vocabulary-GEMV workgroup w write the device wall clock at its
- * start to stamps[2w] and at its end to stamps[2w + 1]; the kernel's duration
- * is max(end) - min(start) in ticks of dflash_wall_clock_hz(). A head over M
- * activation rows runs as ceil(M/8) launches of W = dflash_lm_head_workgroups(V, H, dtype)
- * workgroups each; launch c writes entries [2cW, 2(c+1)W). When capacity is
- * below 2W ceil(M/8) nothing is written. NULL switches it off. Process-wide
- * setting: concurrent LM heads would share the buffer. */
+ * makes each head workgroup w write the device wall clock at its start to
+ * stamps[2w] and at its end to stamps[2w + 1]; the kernel's duration is
+ * max(end) - min(start) in ticks of dflash_wall_clock_hz(). A head over M
+ * activation rows runs as C launches of W workgroups each, with
+ * W = dflash_lm_head_workgroups(V, H, dtype, M, y_dtype, &C); launch c writes
+ * entries [2cW, 2(c+1)W). When capacity is below 2WC nothing is written. NULL
+ * switches it off. Process-wide setting: concurrent LM heads would share the
+ * buffer. */
 void dflash_trace_head_stamps(uint64_t* stamps, int32_t capacity);
 
-/* Workgroups of the LM-head GEMV for a V x H head of weight format dtype
- * (DFLASH_F32 / DFLASH_BF16 / DFLASH_INT4G64); 0 for invalid arguments. */
-int32_t dflash_lm_head_workgroups(int32_t V, int32_t H, int32_t dtype);
+/* Launch shape of the LM-head argmax over M rows of activations in y_dtype
+ * (DFLASH_F32 / DFLASH_BF16) against a V x H head of weight format dtype
+ * (DFLASH_F32 / DFLASH_BF16 / DFLASH_INT4G64): returns the workgroups per
+ * launch and stores the number of launches in *launches (GEMV launches of up to
+ * 8 rows, or, for a bf16 head with bf16 rows, 16 or more of them and H a
+ * multiple of 128, matrix-core launches of up to 128 rows). 0 for invalid
+ * arguments (launches may be NULL). */
+int32_t dflash_lm_head_workgroups(int32_t V, int32_t H, int32_t dtype, int32_t M, int32_t y_dtype, int32_t* launches);
 
 /* Tick rate of the wall clock the stamps use, for the current device, in Hz
  * (0 when the runtime cannot report it). */
@@ -184,11 +190,14 @@ double dflash_wall_clock_hz(void);
  *           tap_ld elements, float for f32 models, bfloat16 otherwise.
  *   n:      rows (>= 0; 0 enqueues nothing).
  *   h_ctx:  float [n, d] output.
- * Workspace: optional. For n <= 8 rows and a workspace of
- * dflash_workspace_bytes(dims, B, cap) bytes with B*(gamma+1) >= n, the long
- * reduction is split across more workgroups (partial sums in ws, added in a
- * fixed order); otherwise ws may be NULL. From 64 rows on, bf16 models run the
- * projection as a matrix-core GEMM (prefill; no workspace needed). */
+ * Workspace: optional; a workspace of dflash_workspace_bytes(dims, B, cap)
+ * bytes with B*(gamma+1) >= n serves every use below, and ws may be NULL.
+ * For n <= 8 rows with a workspace the long reduction is split across more
+ * workgroups (partial sums in ws, added in a fixed order). For bf16 models
+ * with 16 <= n <= 128 rows (a round's rows), H a multiple of 128 and a
+ * 16-byte aligned workspace, the projection runs on matrix cores with
+ * split-K partial sums in ws. Otherwise, from 64 rows on, bf16 models run it
+ * as a matrix-core GEMM (prefill; no workspace needed), and as GEMVs below. */
 int dflash_context_project(const dflash_model* M, const void* const* taps, int64_t tap_ld, int32_t n,
                            float* h_ctx, void* ws, size_t ws_bytes, void* stream);
 
@@ -203,10 +212,13 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
  *                rows of a round); NULL appends all rows.
  *   Rows that would pass cap are not written and len[b] stops at cap (the
  *   caller sizes cap; see dflash_workspace_bytes).
- * Workspace: optional. For bf16 models, n >= 64 rows and a 16-byte aligned
- * workspace of at least 4n bytes (dflash_workspace_bytes(dims, B, cap) always
- * holds B*cap rows), the projection runs as one matrix-core GEMM over all
- * layers (per-row RMS factors kept in ws); otherwise as GEMVs. ws may be NULL. */
+ * Workspace: optional (ws may be NULL; dflash_workspace_bytes(dims, B, cap)
+ * serves every use below). For bf16 models, d a multiple of 128 and a
+ * 16-byte aligned workspace: 16 <= n <= 128 rows (a round's rows) run on
+ * matrix cores, all layers in one launch (each layer's normalised rows and
+ * split-K partial sums in ws, B*(gamma+1) >= n); n >= 64 rows otherwise run
+ * as one matrix-core GEMM over all layers (per-row RMS factors in ws, at
+ * least 4n bytes; B*cap rows always fit). Everything else runs as GEMVs. */
 int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, const int32_t* row_offsets,
                          const int32_t* counts, const dflash_kv* kv, void* ws, size_t ws_bytes, void* stream);
 

@@ -39,6 +39,11 @@ WIDE4_SMALL = scaled(WIDE4, name="wide4_small", H=512, m=2, nl=2, F=1024, V=2048
 BATCHED_SMALL = scaled(BATCHED, name="batched_small", H=256, m=2, d=256, hq=4, hkv=2, hd=64, nl=2, F=512,
                        V=1000, L=40, L_max=200, B=16)
 
+# block rows of a bf16 batch on the matrix-core projections: 3 x 7 = 21 rows (two 16-row
+# fragments, ragged) and 20 x 7 = 140 rows (a launch of 128 rows and one of 12)
+BATCHED_R21 = scaled(BATCHED_SMALL, name="batched_r21", B=3, L=150, L_max=150)
+BATCHED_R140 = scaled(BATCHED_SMALL, name="batched_r140", B=20, V=3001, L=40, L_max=120)
+
 CASES = {
     "tiny": (TINY, [TINY.L]),
     "gqa_bf16": (GQA_BF16, [200, 77, 131]),
@@ -47,6 +52,8 @@ CASES = {
     "wide_heads": (WIDE_HEADS, [300, 157]),
     "wide4_small": (WIDE4_SMALL, [300, 211]),
     "batched_small": (BATCHED_SMALL, [int(x) for x in gen.context_lengths(BATCHED_SMALL)]),
+    "batched_r21": (BATCHED_R21, [150, 33, 97]),
+    "batched_r140": (BATCHED_R140, [int(x) for x in gen.context_lengths(BATCHED_R140)]),
 }
 
 _cache = {}
@@ -241,6 +248,30 @@ def test_lm_head_argmax_planted_and_random(wd, M, H):
         assert int(ids[0]) == lo
 
 
+@pytest.mark.parametrize("M,H,V", [(16, 256, 1000), (37, 256, 1000), (112, 5120, 3001), (128, 256, 1000),
+                                   (130, 384, 1000)])
+def test_lm_head_argmax_matrix_cores(M, H, V):
+    """bf16 head and bf16 rows, 16 or more of them: the head runs on matrix
+    cores (one pass over the head; row counts that are not a multiple of 16,
+    a vocabulary that is not a multiple of the 128-row tile, and more rows than
+    one launch takes)."""
+    dims = scaled(TINY, wdtype="bf16", H=H, V=V)
+    E = gen.make_weight(dims, "E_out")
+    rng = np.random.default_rng(M + H)
+    Y = O.bf16(rng.standard_normal((M, H))).astype(np.float32)
+    W = dfa.Weight(E, torch.device("cuda"))
+    ids = torch.empty(M, dtype=torch.int32, device="cuda")
+    maxl = torch.empty(M, dtype=torch.float32, device="cuda")
+    ws = bd.lm_head_workspace(V, M)
+    y_d = torch.from_numpy(Y).cuda().to(torch.bfloat16)
+    bd.check(dfa.dflash_lm_head_argmax(W, y_d, ids, ws, max_logit=maxl), "lm_head")
+    ref_ids, best, logits = O.lm_head_argmax(Y.astype(np.float64), E, want_logits=True)
+    decided = compare_ids(ids, ref_ids, logits, bf16=True)
+    log(f"[lm_head mfma M={M} H={H} V={V}] ids decided {decided}/{M}")
+    assert decided >= M // 2
+    assert rel_err(maxl, best) <= 1e-5
+
+
 @pytest.mark.parametrize("V", [5000, 5001, 32768])
 def test_verify_exhaustive_patterns(V):
     """All 2^7 agreement patterns of a block-8 verify in one batch; bit-exact
@@ -272,7 +303,7 @@ def test_verify_exhaustive_patterns(V):
     assert np.array_equal(com_o, acc_o + 1)
 
 
-@pytest.mark.parametrize("name", ["tiny", "gqa_bf16", "gqa_rows42", "wide4_small", "batched_small"])
+@pytest.mark.parametrize("name", ["tiny", "gqa_bf16", "gqa_rows42", "wide4_small", "batched_small", "batched_r140"])
 def test_multi_round_loop(name):
     """Rounds of append(committed rows) -> forward -> verify, both sides driven
     by the oracle's schedule (planted logits realise accept lengths; the
@@ -317,8 +348,11 @@ def test_multi_round_loop(name):
         taps = [gen.make_taps(d, r * W, W, stream="round", seq=b) for b in range(B)]
         taps_cat = [dev(np.concatenate([taps[b][j] for b in range(B)])) for j in range(d.m)]
         h = torch.empty(B * W, d.d, dtype=torch.float32, device="cuda")
-        bd.check(dfa.dflash_context_project(base.dm, taps_cat, h), "project")
-        bd.check(dfa.dflash_ctx_kv_append(base.dm, h, offs, torch.from_numpy(com_o).cuda(), kv), "append")
+        # even rounds pass the workspace (matrix-core context paths for 16..128 bf16 rows),
+        # odd rounds do not (GEMV paths)
+        rws = ws if r % 2 == 0 else None
+        bd.check(dfa.dflash_context_project(base.dm, taps_cat, h, rws), "project")
+        bd.check(dfa.dflash_ctx_kv_append(base.dm, h, offs, torch.from_numpy(com_o).cuda(), kv, rws), "append")
         for b in range(B):
             Hc = O.context_project(taps[b], base.w["W_c"], base.w["ctx_norm"], d.eps)
             O.append_context(ctx, base.w, d, Hc, [[]] * b + [list(range(W))] + [[]] * (B - b - 1),
