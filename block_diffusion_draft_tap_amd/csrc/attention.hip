@@ -38,8 +38,11 @@ constexpr int kMaxRows = 48;   // query rows per kv head, MFMA kernel
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// (native vectors: arrays of them stay in registers where arrays of the HIP
+// vector structs may be kept in scratch memory)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f32x4& c) {
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                    0, 0);
 }
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     // K rows c0 + nt*16 + col (dims ks*32 + 8*grp ..) and V keys c0 + 8*grp .. +8 of dims
     // dt*16 + col. Keys past nvalid come from in-bounds rows (cache rows below cap, clamped
     // block rows): their scores are masked and their values zeroed before use.
-    uint4 kb[2][KS], vb[DT];
+    u32x4 kb[2][KS], vb[DT];
     auto load_unit = [&](const int u) {
         const uint16_t *k0, *k1, *vp;
         int64_t vstride;
@@ -133,24 +136,24 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            kb[0][ks] = *reinterpret_cast<const uint4*>(k0 + ks * 32);
-            kb[1][ks] = *reinterpret_cast<const uint4*>(k1 + ks * 32);
+            kb[0][ks] = *reinterpret_cast<const u32x4*>(k0 + ks * 32);
+            kb[1][ks] = *reinterpret_cast<const u32x4*>(k1 + ks * 32);
         }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vb[dt] = *reinterpret_cast<const uint4*>(vp + dt * vstride);
+        for (int dt = 0; dt < DT; ++dt) vb[dt] = *reinterpret_cast<const u32x4*>(vp + dt * vstride);
     };
     // the first unit's loads go out together with Q's
     if (u_begin < u_end) load_unit(u_begin);
 
     // Q tiles as A operands: row = rt*16 + col, dims ks*32 + 8*grp ..; rows past R repeat
     // row R-1 and are never stored
-    uint4 qa[NRT][KS];
+    u32x4 qa[NRT][KS];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
         const int r = min(rt * 16 + col, R - 1);
         const uint16_t* src = qrow0 + (int64_t)(r % p.gamma) * qkv_ld + (g * qpg + r / p.gamma) * HD + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qa[rt][ks] = *reinterpret_cast<const uint4*>(src + ks * 32);
+        for (int ks = 0; ks < KS; ++ks) qa[rt][ks] = *reinterpret_cast<const u32x4*>(src + ks * 32);
     }
 
     f32x4 o[NRT][DT];
@@ -205,25 +208,20 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
             }
         }
         // P as A operands (row col, keys 8*grp .. +8); LDS ops of one wavefront are ordered
-        uint4 pa[NRT], pl[NRT];
+        u32x4 pa[NRT], pl[NRT];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            pa[rt] = *reinterpret_cast<const uint4*>(&plds[wave][0][rt][col][8 * grp]);
-            pl[rt] = *reinterpret_cast<const uint4*>(&plds[wave][1][rt][col][8 * grp]);
+            pa[rt] = *reinterpret_cast<const u32x4*>(&plds[wave][0][rt][col][8 * grp]);
+            pl[rt] = *reinterpret_cast<const u32x4*>(&plds[wave][1][rt][col][8 * grp]);
         }
         if (nvalid < kChunk) {
             // keys past the context are zeroed in V (P is zero there; the cache may hold anything)
             const int nk = nvalid - 8 * grp;  // valid keys among this lane's 8
-            uint32_t mk[4];
+            u32x4 mk;
 #pragma unroll
             for (int q = 0; q < 4; ++q) mk[q] = (2 * q + 1 < nk) ? 0xFFFFFFFFu : ((2 * q < nk) ? 0x0000FFFFu : 0u);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                vb[dt].x &= mk[0];
-                vb[dt].y &= mk[1];
-                vb[dt].z &= mk[2];
-                vb[dt].w &= mk[3];
-            }
+            for (int dt = 0; dt < DT; ++dt) vb[dt] &= mk;
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -481,16 +479,25 @@ __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) 
 
 // ---------------------------------------------------------------------------
 
-void attention_splits(int cap, int gamma, int kv_f32, int* nsplit, int* nparts) {
+// attention workgroups a launch aims for over all (sequence, kv head) pairs
+#ifndef DFL_ATTN_WGS
+#define DFL_ATTN_WGS 1024
+#endif
+
+void attention_splits(int cap, int gamma, int kv_f32, int pairs, int* nsplit, int* nparts) {
     if (kv_f32) {
         int ns = (cap + gamma + kTile - 1) / kTile;
         ns = ns < 1 ? 1 : (ns > 64 ? 64 : ns);
         *nsplit = ns;
         *nparts = ns;
     } else {
-        // one unit per wavefront while the split count allows: cap/32 chunks plus the block
+        // one unit per wavefront (cap/32 chunks plus the block) while the launch stays
+        // below DFL_ATTN_WGS workgroups; with many (sequence, kv head) pairs, fewer splits
+        // of more units each (fewer partial results, and the GPU is full either way)
         const int units = (cap + kChunk - 1) / kChunk + 1;
         int ns = (units + 3) / 4;
+        const int want = (DFL_ATTN_WGS + (pairs > 0 ? pairs : 1) - 1) / (pairs > 0 ? pairs : 1);
+        if (ns > want) ns = want;
         ns = ns < 1 ? 1 : (ns > kMaxSplit ? kMaxSplit : ns);
         *nsplit = ns;
         *nparts = ns;
