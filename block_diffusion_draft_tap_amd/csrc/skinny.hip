@@ -12,7 +12,10 @@
 // one load instruction reads 16 rows x 64 contiguous bytes). The activation
 // chunk (all M rows x 128) is shared by the wavefronts through LDS, double
 // buffered with one barrier per chunk; every workgroup of a launch reads the
-// same activation rows, so they come from L2. Lane l holds
+// same activation rows, so they mostly come from L2. Activations are loaded
+// two chunks ahead too, each chunk's before its weights: loads complete in
+// issue order, so the wait for chunk c + 1's activations (before their LDS
+// store) leaves the weights of c + 1 and c + 2 in flight. Lane l holds
 //   A[l % 16][8 (l / 16) + e],  B[8 (l / 16) + e][l % 16]   (e < 8)
 //   D[4 (l / 16) + e][l % 16]                               (e < 4)
 // of each 16 x 16 product, and a wavefront keeps the M x 16 kSNB accumulators
@@ -45,6 +48,12 @@ namespace dfl {
 #endif
 #ifndef DFL_SK_WGS
 #define DFL_SK_WGS 256
+#endif
+// chunks of activations loaded ahead of the one multiplied (1 or 2; with 2, the wait
+// for chunk c + 1's activations before their LDS store leaves the weights of c + 1 and
+// c + 2 in flight, loads completing in issue order)
+#ifndef DFL_SK_ADEPTH
+#define DFL_SK_ADEPTH 2
 #endif
 
 namespace {
@@ -165,24 +174,25 @@ __global__ __launch_bounds__(kST) void skinny_kernel(const SkinnyParams p) {
 #pragma unroll
         for (int f = 0; f < kSNB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // three register sets of weights: chunk c lives in set c % 3
+    // three register sets of weights: chunk c lives in set c % 3. Loads past the last
+    // chunk re-read it (never multiplied): unconditional loads let the compiler count the
+    // loads in flight, so waiting for an older load never drains the younger ones
     u32x4 w0[kSNB][kSSteps], w1[kSNB][kSSteps], w2[kSNB][kSSteps];
     auto load_w = [&](u32x4 (&wr)[kSNB][kSSteps], int c) {
-        if (c < nc) {
+        const int cc = min(c, nc - 1);
 #pragma unroll
-            for (int s = 0; s < kSSteps; ++s)
+        for (int s = 0; s < kSSteps; ++s)
 #pragma unroll
-                for (int f = 0; f < kSNB; ++f)
-                    wr[f][s] = *reinterpret_cast<const u32x4*>(wp[f] + c * kSKC + s * 32);
-        }
+            for (int f = 0; f < kSNB; ++f)
+                wr[f][s] = *reinterpret_cast<const u32x4*>(wp[f] + cc * kSKC + s * 32);
     };
     // the activation chunk: MT*16 rows x 16 pieces of 16 bytes, spread over the threads
     constexpr int PIECES = MT * 16 * (kSKC / 8);
     constexpr int APT = (PIECES + kST - 1) / kST;
-    u32x4 ast[APT];
+    u32x4 ast[APT], ast2[APT];
     // (past the last chunk it reloads the last one, which is never stored: unconditional
     // loads keep the staging registers out of scratch memory)
-    auto load_a = [&](int c) {
+    auto load_a_into = [&](u32x4 (&dst)[APT], int c) {
         const int k0 = kbeg + min(c, nc - 1) * kSKC;
         const uint16_t* src;
         if (p.seg_k > 0) {  // tap segments: a chunk never straddles two
@@ -199,53 +209,98 @@ __global__ __launch_bounds__(kST) void skinny_kernel(const SkinnyParams p) {
         for (int i = 0; i < APT; ++i) {
             const int q = min((int)threadIdx.x + kST * i, PIECES - 1);
             const int row = min(q >> 4, p.M - 1);  // rows past M: any valid row, never stored
-            ast[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)row * p.a_ld + 8 * (q & 15));
+            dst[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)row * p.a_ld + 8 * (q & 15));
         }
     };
-    auto store_a = [&](int buf) {
+    auto store_a_from = [&](const u32x4 (&srcr)[APT], int buf) {
 #pragma unroll
         for (int i = 0; i < APT; ++i) {
             const int q = threadIdx.x + kST * i;
-            if (PIECES % kST == 0 || q < PIECES) *reinterpret_cast<u32x4*>(&As[buf][q >> 4][8 * (q & 15)]) = ast[i];
+            if (PIECES % kST == 0 || q < PIECES) *reinterpret_cast<u32x4*>(&As[buf][q >> 4][8 * (q & 15)]) = srcr[i];
         }
     };
+    auto load_a = [&](int c) { load_a_into(ast, c); };
+    auto store_a = [&](int buf) { store_a_from(ast, buf); };
     auto mma = [&](int buf, const u32x4 (&wr)[kSNB][kSSteps]) {
 #pragma unroll
-        for (int s = 0; s < kSSteps; ++s)
+        for (int s = 0; s < kSSteps; ++s) {
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 const u32x4 af = *reinterpret_cast<const u32x4*>(&As[buf][i * 16 + col][s * 32 + 8 * grp]);
 #pragma unroll
                 for (int f = 0; f < kSNB; ++f) acc[i][f] = mfma_bf16(af, wr[f][s], acc[i][f]);
             }
+        }
     };
 
     // chunk c multiplies LDS buffer c % 2; the activations of c + 1 are loaded before the
-    // weights of c + 2, so the wait for them before their LDS store leaves the weights in flight
+    // weights of c + 2, so the wait for them before their LDS store leaves the weights in
+    // flight. Whole triples of chunks run without branches (a store into the idle buffer
+    // past the last chunk is never read); the last one or two chunks follow.
+#if DFL_SK_ADEPTH == 2
+    // activations two chunks ahead as well: A(k) sits in staging set k % 2 from its load
+    // (during chunk k - 2) until its LDS store (end of chunk k - 1); six chunks per trip
+    auto stage = [&](int cc, u32x4 (&wc)[kSNB][kSSteps], u32x4 (&wn)[kSNB][kSSteps], u32x4 (&al)[APT],
+                     const u32x4 (&as)[APT]) {
+        load_a_into(al, cc + 2);
+        load_w(wn, cc + 2);
+        mma(cc & 1, wc);
+        store_a_from(as, (cc + 1) & 1);
+        __syncthreads();
+    };
+    load_w(w0, 0);
+    load_w(w1, 1);
+    load_a_into(ast, 0);
+    load_a_into(ast2, 1);
+    store_a_from(ast, 0);
+    __syncthreads();
+    int c = 0;
+    for (; c + 6 <= nc; c += 6) {
+        stage(c, w0, w2, ast, ast2);
+        stage(c + 1, w1, w0, ast2, ast);
+        stage(c + 2, w2, w1, ast, ast2);
+        stage(c + 3, w0, w2, ast2, ast);
+        stage(c + 4, w1, w0, ast, ast2);
+        stage(c + 5, w2, w1, ast2, ast);
+    }
+    if (c < nc) stage(c, w0, w2, ast, ast2);
+    if (c + 1 < nc) stage(c + 1, w1, w0, ast2, ast);
+    if (c + 2 < nc) stage(c + 2, w2, w1, ast, ast2);
+    if (c + 3 < nc) stage(c + 3, w0, w2, ast2, ast);
+    if (c + 4 < nc) stage(c + 4, w1, w0, ast, ast2);
+#else
     load_w(w0, 0);
     load_w(w1, 1);
     load_a(0);
     store_a(0);
     __syncthreads();
-    for (int c = 0; c < nc; c += 3) {
+    int c = 0;
+    for (; c + 3 <= nc; c += 3) {
         load_a(c + 1);
         load_w(w2, c + 2);
         mma(c & 1, w0);
-        if (c + 1 < nc) store_a((c + 1) & 1);
+        store_a((c + 1) & 1);
         __syncthreads();
-        if (c + 1 >= nc) break;
         load_a(c + 2);
         load_w(w0, c + 3);
         mma((c + 1) & 1, w1);
-        if (c + 2 < nc) store_a(c & 1);
+        store_a(c & 1);
         __syncthreads();
-        if (c + 2 >= nc) break;
         load_a(c + 3);
         load_w(w1, c + 4);
         mma(c & 1, w2);
-        if (c + 3 < nc) store_a((c + 1) & 1);
+        store_a((c + 1) & 1);
         __syncthreads();
     }
+    if (c < nc) {
+        load_a(c + 1);
+        mma(c & 1, w0);
+        store_a((c + 1) & 1);
+        __syncthreads();
+        if (c + 1 < nc) mma((c + 1) & 1, w1);
+    }
+#endif
+
 
     // ---- epilogue: lane holds rows i*16 + 4*grp + e, columns of fragment f at col
     if constexpr (EPI == SK_GATED) {
