@@ -180,6 +180,26 @@ int ctx_splits(const dflash_dims& d) { return (d.m * d.H + DFL_CTX_SPLIT_K - 1) 
 #ifndef DFL_SKINNY_MIN_ROWS
 #define DFL_SKINNY_MIN_ROWS 16
 #endif
+// long rows of a bf16 / int4 drafter: RMSNorm once per row into bf16 rows (norm_rows)
+// instead of two passes over the fp32 row in every GEMV workgroup's prologue
+bool prenorm(const dflash_dims& d) { return d.wdtype != DFLASH_F32 && d.d > kRegNormMaxK; }
+// split-K of the plain-prologue GEMVs (residual and store epilogues): K ranges of at most
+// this many elements (staged once within the normal LDS budget, several workgroups per
+// CU); a reduce kernel adds the partial sums in split order and applies the epilogue
+#ifndef DFL_GEMV_SPLIT_K
+#define DFL_GEMV_SPLIT_K 4096
+#endif
+void gemv_split(const dflash_dims& d, int K, int* nsplit, int* kslice) {
+    int ns = d.wdtype == DFLASH_F32 ? 1 : (K + DFL_GEMV_SPLIT_K - 1) / DFL_GEMV_SPLIT_K;
+    int ks = K;
+    if (ns > 1) {
+        ks = ((K + ns - 1) / ns + 511) / 512 * 512;
+        ns = (K + ks - 1) / ks;
+    }
+    *nsplit = ns;
+    *kslice = ks;
+}
+
 bool lm_head_skinny(int wdtype, int y_f32, int rows, int H) {
     return wdtype == DFLASH_BF16 && !y_f32 && rows >= DFL_SKINNY_MIN_ROWS && H % kSkinnyK == 0;
 }
@@ -236,8 +256,9 @@ struct Ws {
     int32_t* lmi;
     float* ctxp;   // split-K partials of the context projection [splits][B*(gamma+1)][d]
     uint16_t* vt;  // block values, head-dim major [B][hkv][hd][32] (bf16 models)
-    uint16_t* an;  // matrix-core path: normalised block rows, bf16 [B*gamma][d]
+    uint16_t* an;  // normalised block rows, bf16 [B*gamma][d] (matrix-core path, long rows)
     float* skp;    // matrix-core path: split-K partial sums
+    float* rsp;    // GEMV path: split-K partial sums of the residual projections
     bool skinny;   // the block projections run on matrix cores
     size_t total;
     int nsplit;  // attention workgroups per (sequence, kv head)
@@ -267,8 +288,22 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     const size_t o_ctxp = take((size_t)ctx_splits(d) * B * (d.gamma + 1) * d.d * 4);
     const size_t o_vt = take((size_t)B * d.hkv * d.hd * 32 * 2);
     w.skinny = skinny_ok(d, (int)rows);
-    const size_t o_an = take(w.skinny ? rows * d.d * 2 : 0);
+    const size_t o_an = take((w.skinny || prenorm(d)) ? rows * d.d * 2 : 0);
     const size_t o_skp = take(w.skinny ? skinny_part_bytes(d, (int)rows) : 0);
+    size_t rsp_bytes = 0;
+    if (!w.skinny) {
+        // O and down (N = d), QKV (K = d) and out (N = H, K = d), when their rows are
+        // pre-normalised (plain prologue)
+        const int shapes[4][2] = {{d.hq * d.hd, d.d}, {d.F, d.d}, {d.d, qkv_rows}, {d.d, d.H}};
+        for (int q = 0; q < 4; ++q) {
+            if (q >= 2 && !prenorm(d)) break;
+            int ns = 1, ks = 0;
+            gemv_split(d, shapes[q][0], &ns, &ks);
+            const size_t b = (size_t)ns * rows * shapes[q][1] * 4;
+            if (ns > 1 && b > rsp_bytes) rsp_bytes = b;
+        }
+    }
+    const size_t o_rsp = take(rsp_bytes);
     w.total = off;
     // the context append of up to B*cap rows keeps one float per row at the base; the
     // matrix-core context paths of a round's B*(gamma+1) rows use the base as well
@@ -277,6 +312,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     const size_t ctx_need = align_up(ctx_project_skinny_bytes(d, nr)), kv_need = align_up(kv_append_skinny_bytes(d, nr));
     if (w.total < ctx_need) w.total = ctx_need;
     if (w.total < kv_need) w.total = kv_need;
+    if (prenorm(d) && w.total < kv_append_norm_bytes(d, nr)) w.total = kv_append_norm_bytes(d, nr);
     char* c = static_cast<char*>(base);
     if (c) {
         w.hd = reinterpret_cast<float*>(c + o_hd);
@@ -291,6 +327,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
         w.vt = reinterpret_cast<uint16_t*>(c + o_vt);
         w.an = reinterpret_cast<uint16_t*>(c + o_an);
         w.skp = reinterpret_cast<float*>(c + o_skp);
+        w.rsp = reinterpret_cast<float*>(c + o_rsp);
     }
     return w;
 }
@@ -340,6 +377,42 @@ hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStr
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// A plain-prologue GEMV with a residual (out += x W^T, fp32) or store epilogue (p's
+// out fields): one launch, or split-K partials into part and the ordered reduce that
+// applies the epilogue (long K ranges)
+hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int rows, float* part, hipStream_t s) {
+    int ns = 1, ks = p.K;
+    gemv_split(d, p.K, &ns, &ks);
+    if (ns <= 1) return gemv_rows(wt, PRO_PLAIN, epi, p, rows, s);
+    SkinnyParams r;
+    std::memset(&r, 0, sizeof(r));
+    r.M = rows;
+    r.N = p.N;
+    r.nsplit = ns;
+    r.part = part;
+    r.out = p.out;
+    r.out_ld = p.out_ld;
+    r.out_bf16 = epi == EPI_STORE ? p.out_bf16 : 0;
+    r.vt = epi == EPI_STORE ? p.vt : nullptr;
+    r.vt_col = p.vt_col;
+    r.row_base = p.row_base;
+    r.gamma = p.gamma;
+    r.hkv = p.hkv;
+    r.hd = p.hd;
+    p.ksplit = ns;
+    p.kslice = ks;
+    p.max_wgs = DFL_SMALL_WGS / ns > 0 ? DFL_SMALL_WGS / ns : 1;
+    p.out = part;
+    p.out_ld = p.N;
+    p.split_stride = (int64_t)rows * p.N;
+    p.round_out = 0;
+    p.out_bf16 = 0;
+    p.vt = nullptr;
+    const hipError_t e = gemv_rows(wt, PRO_PLAIN, EPI_STORE, p, rows, s);
+    if (e != hipSuccess) return e;
+    return launch_split_reduce(epi == EPI_RESID ? SK_RESID : SK_STORE, r, s);
 }
 
 // matrix-core projections of `rows` block rows, in launches of up to kSkinnyRows
@@ -461,6 +534,12 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.x = h;
         p.x_ld = d.d;
         p.gain[0] = L.attn_norm;
+        int pro = PRO_NORM;
+        if (prenorm(d)) {
+            DFL_HIP(norm_rows(h, rows, d.d, L.attn_norm, d.eps, w.an, s));
+            p.x = reinterpret_cast<const float*>(w.an);  // bf16 rows (src_f32 = 0)
+            pro = PRO_PLAIN;
+        }
         p.out = w.qkv;
         p.out_ld = qkv_rows;
         if (d.wdtype != DFLASH_F32) {
@@ -474,7 +553,10 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
             p.hkv = d.hkv;
             p.hd = d.hd;
         }
-        DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_STORE, p, rows, s));
+        if (pro == PRO_PLAIN)
+            DFL_HIP(gemv_plain(d, wt, EPI_STORE, p, rows, w.rsp, s));
+        else
+            DFL_HIP(gemv_rows(wt, pro, EPI_STORE, p, rows, s));
     }
     {  // O = softmax(Q [K_ctx; K_b]^T / sqrt(hd)) [V_ctx; V_b]
         AttnParams a;
@@ -514,7 +596,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.x_ld = d.hq * d.hd;
         p.out = h;
         p.out_ld = d.d;
-        DFL_HIP(gemv_rows(wt, PRO_PLAIN, EPI_RESID, p, rows, s));
+        DFL_HIP(gemv_plain(d, wt, EPI_RESID, p, rows, w.rsp, s));
     }
     {  // A = act(n2 W_gate^T) * (n2 W_up^T), n2 = RMSNorm(H; ffn_norm)
         GemvParams p = base_params(d);
@@ -529,7 +611,13 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.gain[0] = L.ffn_norm;
         p.out = w.a;
         p.out_ld = d.F;
-        DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_GATED, p, rows, s));
+        int pro = PRO_NORM;
+        if (prenorm(d)) {
+            DFL_HIP(norm_rows(h, rows, d.d, L.ffn_norm, d.eps, w.an, s));
+            p.x = reinterpret_cast<const float*>(w.an);
+            pro = PRO_PLAIN;
+        }
+        DFL_HIP(gemv_rows(wt, pro, EPI_GATED, p, rows, s));
     }
     {  // H += A W_down^T
         GemvParams p = base_params(d);
@@ -541,7 +629,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.x_ld = d.F;
         p.out = h;
         p.out_ld = d.d;
-        DFL_HIP(gemv_rows(wt, PRO_PLAIN, EPI_RESID, p, rows, s));
+        DFL_HIP(gemv_plain(d, wt, EPI_RESID, p, rows, w.rsp, s));
     }
     return DFLASH_OK;
 }
@@ -809,13 +897,33 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
         p.w[i] = wptr(M->layers[i].w_qkv);
         p.gain[i] = M->layers[i].attn_norm;
     }
+    int pro = PRO_NORM;
+    if (prenorm(d) && ws && aligned16(ws) && ws_bytes >= kv_append_norm_bytes(d, n)) {
+        // long rows: every layer's bf16(RMSNorm(h_ctx; attn_norm_i)) once into ws (one
+        // launch, grid.y = layer); the GEMV then stages layer y's plain rows
+        NormRowsParams q;
+        std::memset(&q, 0, sizeof(q));
+        q.x = h_ctx;
+        q.x_ld = d.d;
+        q.rows = n;
+        q.K = d.d;
+        q.layers = d.nl;
+        q.eps = d.eps;
+        for (int i = 0; i < d.nl; ++i) q.gain[i] = M->layers[i].attn_norm;
+        q.dst = static_cast<uint16_t*>(ws);
+        q.dst_ld = d.d;
+        q.dst_layer_stride = (int64_t)n * d.d;
+        DFL_HIP(launch_norm_rows(q, s));
+        pro = PRO_PLAIN;
+    }
     p.w_row0 = (int64_t)d.hq * d.hd;  // the K and V rows of the fused QKV matrix
     p.max_wgs = DFL_KV_WGS / d.nl > 0 ? DFL_KV_WGS / d.nl : 1;  // per layer (grid.y)
     p.N = 2 * d.hkv * d.hd;
     p.K = d.d;
     p.rpw = rpw_for(p.N);
-    p.x = h_ctx;
+    p.x = pro == PRO_PLAIN ? static_cast<const float*>(ws) : h_ctx;  // bf16 rows for PRO_PLAIN
     p.x_ld = d.d;
+    p.x_layer_stride = pro == PRO_PLAIN ? (int64_t)n * d.d : 0;
     p.kcache = kv->k;
     p.vcache = kv->v;
     p.len = kv->len;
@@ -828,7 +936,7 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
     p.cap = kv->cap;
     p.kv_f32 = kv->dtype == DFLASH_F32;
     p.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
-    DFL_HIP(gemv_rows(wtype_of(d.wdtype), PRO_NORM, EPI_KV, p, n, s, d.nl, 32));
+    DFL_HIP(gemv_rows(wtype_of(d.wdtype), pro, EPI_KV, p, n, s, d.nl, 32));
     DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
     g_invocations++;
     return DFLASH_OK;
@@ -901,7 +1009,13 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
         p.out = y;
         p.out_ld = d.H;
         p.out_bf16 = d.wdtype == DFLASH_F32 ? 0 : 1;
-        DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_STORE, p, rows, s));
+        if (prenorm(d)) {
+            DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, w.an, s));
+            p.x = reinterpret_cast<const float*>(w.an);
+            DFL_HIP(gemv_plain(d, wt, EPI_STORE, p, rows, w.rsp, s));
+        } else {
+            DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_STORE, p, rows, s));
+        }
     }
     DFL_TRY(lm_head(M->lm_head, y, d.wdtype == DFLASH_F32, rows, d.H, d.V, draft_ids, max_logit, w.lmv, w.lmi,
                     s));

@@ -28,7 +28,6 @@
 
 namespace dfl {
 
-constexpr int kRegNormMaxK = 2048;  // rows up to this length take the register RMSNorm prologue
 
 // weight iterations kept in flight per lane (register ring), for 1-2 and 4 rows per wavefront
 #ifndef DFL_PF
@@ -174,10 +173,11 @@ __device__ __forceinline__ void load_x8(const GemvParams& p, int layer, int m, i
         return;
     }
     if constexpr (PRO == PRO_PLAIN) {
+        const int64_t off = (int64_t)layer * p.x_layer_stride + (int64_t)m * p.x_ld + k;
         if (p.src_f32)
-            load8_f32(p.x + (int64_t)m * p.x_ld + k, v);
+            load8_f32(p.x + off, v);
         else
-            load8_bf16(reinterpret_cast<const uint16_t*>(p.x) + (int64_t)m * p.x_ld + k, v);
+            load8_bf16(reinterpret_cast<const uint16_t*>(p.x) + off, v);
     } else if constexpr (PRO == PRO_NORM) {
         load8_f32(p.x + (int64_t)m * p.x_ld + k, v);
         const float r = rinv[m];
@@ -728,9 +728,12 @@ hipError_t launch_gemv(int wtype, int pro, int epi, int maxm, const GemvParams& 
     }
     DFL_CASE(PRO_TAPS, EPI_STORE)
     DFL_CASE(PRO_NORM, EPI_KV)
+    DFL_CASE(PRO_PLAIN, EPI_KV)
     if (pro == PRO_GATHER && epi == EPI_BLOCKINIT) return launch_wt<PRO_GATHER, EPI_BLOCKINIT, 8>(wtype, p, layers, s);
     if (pro == PRO_NORM && epi == EPI_STORE) return launch_wt<PRO_NORM, EPI_STORE, 8>(wtype, p, layers, s);
     if (pro == PRO_PLAIN && epi == EPI_RESID) return launch_wt<PRO_PLAIN, EPI_RESID, 8>(wtype, p, layers, s);
+    if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_wt<PRO_PLAIN, EPI_STORE, 8>(wtype, p, layers, s);
+    if (pro == PRO_PLAIN && epi == EPI_GATED) return launch_wt<PRO_PLAIN, EPI_GATED, 8>(wtype, p, layers, s);
     if (pro == PRO_NORM && epi == EPI_GATED) return launch_wt<PRO_NORM, EPI_GATED, 8>(wtype, p, layers, s);
     if (pro == PRO_TAPS && epi == EPI_ARGMAX) return launch_wt<PRO_TAPS, EPI_ARGMAX, 8>(wtype, p, layers, s);
 #undef DFL_CASE

@@ -54,8 +54,9 @@ struct GemvParams {
     int max_wgs;         // cap on workgroups; row tiles beyond it are looped over (0 = one per tile)
 
     // prologue
-    const float* x;      // PRO_PLAIN / PRO_NORM: fp32 rows
+    const float* x;      // PRO_PLAIN / PRO_NORM: fp32 rows (PRO_PLAIN: bf16 rows when src_f32 = 0)
     int64_t x_ld;
+    int64_t x_layer_stride;  // PRO_PLAIN: layer y's rows start at x + y * x_layer_stride elements
     const void* gain[kMaxLayers];  // PRO_NORM: per-layer gain vectors [K]
     int gain_f32;
     float eps;
@@ -109,5 +110,8 @@ int gemv_head_grid(int wtype, int K, int ntiles, int max_wgs);
 
 // LDS budget for staged activations per workgroup
 constexpr int kStageBytes = 64 * 1024;
+// PRO_NORM rows up to this length are normalised in registers in one round trip;
+// longer rows take two passes over the fp32 row in every workgroup's prologue
+constexpr int kRegNormMaxK = 2048;
 
 }  // namespace dfl

@@ -549,6 +549,19 @@ hipError_t launch_skinny(int epi, const SkinnyParams& p, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_split_reduce(int epi, const SkinnyParams& p, hipStream_t s) {
+    if (p.M < 1 || p.N <= 0 || (p.N % 4) || p.nsplit < 1 || !p.part || !p.out) return hipErrorInvalidValue;
+    const int64_t blocks = ((int64_t)p.M * p.N / 4 + kBlock - 1) / kBlock;
+    (void)hipGetLastError();  // report only this launch's status
+    if (epi == SK_RESID)
+        hipLaunchKernelGGL((skinny_reduce_kernel<SK_RESID>), dim3((unsigned)blocks, 1), dim3(kBlock), 0, s, p);
+    else if (epi == SK_STORE)
+        hipLaunchKernelGGL((skinny_reduce_kernel<SK_STORE>), dim3((unsigned)blocks, 1), dim3(kBlock), 0, s, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_norm_rows(const NormRowsParams& p, hipStream_t s) {
     if (p.rows <= 0) return hipSuccess;
     if (p.K <= 0 || (p.K % 8) || p.K > kNormMaxK || (p.x_ld % 4) || (p.dst_ld % 8) || (p.dst_layer_stride % 8) ||

@@ -75,6 +75,11 @@ void skinny_split(int epi, int N, int K, int layers, int* nsplit, int* kslice);
 // for SK_PARTIAL)
 hipError_t launch_skinny(int epi, const SkinnyParams& p, hipStream_t s);
 
+// The split-K sum and epilogue alone (SK_STORE / SK_RESID, one layer): adds the
+// nsplit fp32 partials part [nsplit][M][N] in split order and applies the
+// epilogue; used for partials written by other kernels (N a multiple of 4)
+hipError_t launch_split_reduce(int epi, const SkinnyParams& p, hipStream_t s);
+
 // dst + z * dst_layer_stride: rows r of bf16(x[r, k] * (mean_k x[r, k]^2 + eps)^-1/2 * gain[z][k])
 // for rows of K fp32 values (K a multiple of 8, at most 8192), z < layers (grid.y)
 struct NormRowsParams {

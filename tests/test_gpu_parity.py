@@ -8,8 +8,11 @@ a bf16 GQA drafter with 42 query rows per kv head (three MFMA row tiles) and
 two ragged sequences, the default bf16 drafter at its full size (context
 2048, vocab 32768), and reduced-width versions of the three wide workloads
 that keep their kernel paths: the wide drafter's heads (40 query / 8 kv heads
-of dim 128, 35 query rows per kv head, SiLU FFN, 7-row block), the same heads
-with int4-g64 weights everywhere (4-row block), and 16 ragged sequences.
+of dim 128, 35 query rows per kv head, SiLU FFN, 7-row block; rows of 5120
+normalised once per row, the O projection in two split-K ranges), its layer
+with a 9216-wide FFN (the down projection in three split-K ranges), the same
+heads with int4-g64 weights everywhere (4-row block), and 16 ragged sequences
+(plus 3 and 20 sequences: 21 and 140 block rows on the matrix-core path).
 """
 
 import numpy as np
@@ -33,6 +36,8 @@ GQA_ROWS42 = scaled(TINY, name="gqa_rows42", wdtype="bf16", H=256, d=768, hq=12,
 
 # the wide drafter's attention geometry (d = 40 x 128) with fewer layers and narrower taps / FFN
 WIDE_HEADS = scaled(WIDE, name="wide_heads", H=512, m=2, nl=1, F=1024, V=2048, L=300, B=2)
+# the wide drafter's layer with a long FFN (down projection K = 9216: three split-K ranges)
+WIDE_FFN = scaled(WIDE, name="wide_ffn", H=512, m=2, nl=1, F=9216, V=2048, L=100, B=1)
 # the same heads with int4-g64 weights on every matrix, LM head included
 WIDE4_SMALL = scaled(WIDE4, name="wide4_small", H=512, m=2, nl=2, F=1024, V=2048, L=300, B=2)
 # 16 ragged sequences (batched workload), narrow layers
@@ -50,6 +55,7 @@ CASES = {
     "gqa_rows42": (GQA_ROWS42, [150, 96]),
     "default": (DEFAULT, [DEFAULT.L]),
     "wide_heads": (WIDE_HEADS, [300, 157]),
+    "wide_ffn": (WIDE_FFN, [100]),
     "wide4_small": (WIDE4_SMALL, [300, 211]),
     "batched_small": (BATCHED_SMALL, [int(x) for x in gen.context_lengths(BATCHED_SMALL)]),
     "batched_r21": (BATCHED_R21, [150, 33, 97]),
