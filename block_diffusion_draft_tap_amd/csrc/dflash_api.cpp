@@ -161,12 +161,29 @@ int rpw_for(int N) { return N >= 16384 ? 4 : (N >= 2048 ? 2 : 1); }
 #define DFL_LM_WGS 768
 #endif
 constexpr int kLmWgs = DFL_LM_WGS;
+// weight rows per wavefront and workgroups of an int4 LM head (its products are
+// ALU-bound: two rows per wavefront keep two wavefronts per SIMD)
+#ifndef DFL_LM_RPW_I4
+#define DFL_LM_RPW_I4 2
+#endif
+#ifndef DFL_LM_WGS_I4
+#define DFL_LM_WGS_I4 512
+#endif
 // one argmax partial per LM-head workgroup; the head runs 4 rows per wavefront
 // Row tiles of 16 vocabulary rows; a head whose rows (H) stage in one pass runs
 // persistent workgroups (kLmWgs, or one per CU for long rows), a longer one a
 // workgroup per tile.
-int lm_tiles(int V) { return (V + 15) / 16; }
-int lm_nblocks(int V, int H, int wtype) { return gemv_head_grid(wtype, H, lm_tiles(V), kLmWgs); }
+int lm_rpw(int wtype) { return wtype == W_I4 ? DFL_LM_RPW_I4 : 4; }
+int lm_tiles(int V, int wtype) { return (V + 4 * lm_rpw(wtype) - 1) / (4 * lm_rpw(wtype)); }
+// argmax partials per row, enough for any head layout
+int lm_tiles_max(int V) {
+    const int r = DFL_LM_RPW_I4 < 4 ? DFL_LM_RPW_I4 : 4;
+    return (V + 4 * r - 1) / (4 * r);
+}
+int lm_wgs(int wtype) { return wtype == W_I4 ? DFL_LM_WGS_I4 : kLmWgs; }
+int lm_nblocks(int V, int H, int wtype, int rows) {
+    return gemv_head_grid(wtype, H, lm_tiles(V, wtype), lm_wgs(wtype), rows);
+}
 // split-K of the context projection for few rows: K ranges of at most 2048
 #ifndef DFL_CTX_SPLIT_K
 #define DFL_CTX_SPLIT_K 2048
@@ -282,7 +299,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     const size_t o_o = take(rows * d.hq * d.hd * 4);
     const size_t o_a = take(rows * d.F * 4);
     const size_t o_y = take(rows * d.H * 4);
-    const size_t nb = lm_tiles(d.V);  // enough for any head layout
+    const size_t nb = lm_tiles_max(d.V);  // enough for any head layout
     const size_t o_lmv = take(rows * nb * 4);
     const size_t o_lmi = take(rows * nb * 4);
     const size_t o_ctxp = take((size_t)ctx_splits(d) * B * (d.gamma + 1) * d.d * 4);
@@ -349,7 +366,7 @@ GemvParams base_params(const dflash_dims& d) {
 
 hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStream_t s, int layers = 1,
                      int maxm_long = 8) {
-    const int maxm = rows > 8 ? maxm_long : 8;
+    const int maxm = rows > 8 ? maxm_long : gemv_maxm(wtype, rows);
     for (int r0 = 0; r0 < rows; r0 += maxm) {
         GemvParams q = p;
         q.M = rows - r0 < maxm ? rows - r0 : maxm;
@@ -653,13 +670,13 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
     p.w[0] = wptr(E);
     p.N = V;
     p.K = H;
-    p.rpw = 4;
-    p.max_wgs = kLmWgs;
+    p.rpw = lm_rpw(wtype_of(E.dtype));
+    p.max_wgs = lm_wgs(wtype_of(E.dtype));
     p.taps[0] = y;
     p.tap_ld = H;
     p.H = H;
     p.src_f32 = y_f32;
-    p.nblocks = lm_nblocks(V, H, wtype_of(E.dtype));
+    p.nblocks = lm_nblocks(V, H, wtype_of(E.dtype), rows < 8 ? rows : 8);
     p.part_val = pv;
     p.part_idx = pi;
     uint64_t* st = g_stamps.load();
@@ -712,7 +729,7 @@ int32_t dflash_lm_head_workgroups(int32_t V, int32_t H, int32_t dtype, int32_t M
         return skinny_tiles(SK_ARGMAX, V);
     }
     if (launches) *launches = (M + 7) / 8;
-    return lm_nblocks(V, H, wtype_of(dtype));
+    return lm_nblocks(V, H, wtype_of(dtype), M < 8 ? M : 8);
 }
 
 double dflash_wall_clock_hz(void) {
@@ -1025,7 +1042,7 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
 
 size_t dflash_lm_head_workspace_bytes(int32_t V, int32_t M) {
     if (V <= 0 || M <= 0) return 0;
-    return 2 * align_up((size_t)M * lm_tiles(V) * 4);
+    return 2 * align_up((size_t)M * lm_tiles_max(V) * 4);
 }
 
 int dflash_lm_head_argmax(const dflash_weight* E_out, const void* y, int32_t y_dtype, int32_t M, int32_t* ids,

@@ -650,17 +650,19 @@ static StagePlan stage_plan(int kslice, int max_wgs) {
     return {kc, max_wgs};
 }
 
-template <int WT>
+template <int WT, int MAXM>
 static int head_grid_t(int K, int ntiles, int max_wgs) {
-    const StagePlan sp = stage_plan<WT, 8>(K, max_wgs);
+    const StagePlan sp = stage_plan<WT, MAXM>(K, max_wgs);
     return (sp.max_wgs > 0 && K <= sp.KC && ntiles > sp.max_wgs) ? sp.max_wgs : ntiles;
 }
 
-int gemv_head_grid(int wtype, int K, int ntiles, int max_wgs) {
+int gemv_head_grid(int wtype, int K, int ntiles, int max_wgs, int rows) {
     switch (wtype) {
-        case W_F32: return head_grid_t<W_F32>(K, ntiles, max_wgs);
-        case W_BF16: return head_grid_t<W_BF16>(K, ntiles, max_wgs);
-        case W_I4: return head_grid_t<W_I4>(K, ntiles, max_wgs);
+        case W_F32: return head_grid_t<W_F32, 8>(K, ntiles, max_wgs);
+        case W_BF16: return head_grid_t<W_BF16, 8>(K, ntiles, max_wgs);
+        case W_I4:
+            return gemv_maxm(W_I4, rows) == 4 ? head_grid_t<W_I4, 4>(K, ntiles, max_wgs)
+                                              : head_grid_t<W_I4, 8>(K, ntiles, max_wgs);
     }
     return 0;
 }
@@ -699,7 +701,7 @@ static hipError_t launch_one(const GemvParams& p, int layers, hipStream_t s) {
 
 template <int WT, int PRO, int EPI, int MAXM>
 static hipError_t launch_rpw(const GemvParams& p, int layers, hipStream_t s) {
-    if constexpr (MAXM == 8) {
+    if constexpr (MAXM <= 8) {
         if (p.rpw >= 4) return launch_one<WT, PRO, EPI, MAXM, 4>(p, layers, s);
         if (p.rpw == 2 || EPI == EPI_GATED) return launch_one<WT, PRO, EPI, MAXM, 2>(p, layers, s);
         if constexpr (EPI != EPI_GATED) return launch_one<WT, PRO, EPI, MAXM, 1>(p, layers, s);
@@ -711,7 +713,10 @@ static hipError_t launch_rpw(const GemvParams& p, int layers, hipStream_t s) {
 }
 
 template <int PRO, int EPI, int MAXM>
-static hipError_t launch_wt(int wtype, const GemvParams& p, int layers, hipStream_t s) {
+static hipError_t launch_wt(int wtype, const GemvParams& p, int layers, hipStream_t s, int maxm) {
+    if constexpr (MAXM == 8) {
+        if (maxm == 4 && wtype == W_I4) return launch_rpw<W_I4, PRO, EPI, 4>(p, layers, s);
+    }
     switch (wtype) {
         case W_F32: return launch_rpw<W_F32, PRO, EPI, MAXM>(p, layers, s);
         case W_BF16: return launch_rpw<W_BF16, PRO, EPI, MAXM>(p, layers, s);
@@ -721,21 +726,22 @@ static hipError_t launch_wt(int wtype, const GemvParams& p, int layers, hipStrea
 }
 
 hipError_t launch_gemv(int wtype, int pro, int epi, int maxm, const GemvParams& p, int layers, hipStream_t s) {
+    if (maxm == 4 && (wtype != W_I4 || p.M > 4)) return hipErrorInvalidValue;
 #define DFL_CASE(PRO, EPI)                                                                      \
     if (pro == PRO && epi == EPI) {                                                             \
-        return maxm <= 8 ? launch_wt<PRO, EPI, 8>(wtype, p, layers, s)                          \
-                         : launch_wt<PRO, EPI, 32>(wtype, p, layers, s);                        \
+        return maxm <= 8 ? launch_wt<PRO, EPI, 8>(wtype, p, layers, s, maxm)                          \
+                         : launch_wt<PRO, EPI, 32>(wtype, p, layers, s, maxm);                        \
     }
     DFL_CASE(PRO_TAPS, EPI_STORE)
     DFL_CASE(PRO_NORM, EPI_KV)
     DFL_CASE(PRO_PLAIN, EPI_KV)
-    if (pro == PRO_GATHER && epi == EPI_BLOCKINIT) return launch_wt<PRO_GATHER, EPI_BLOCKINIT, 8>(wtype, p, layers, s);
-    if (pro == PRO_NORM && epi == EPI_STORE) return launch_wt<PRO_NORM, EPI_STORE, 8>(wtype, p, layers, s);
-    if (pro == PRO_PLAIN && epi == EPI_RESID) return launch_wt<PRO_PLAIN, EPI_RESID, 8>(wtype, p, layers, s);
-    if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_wt<PRO_PLAIN, EPI_STORE, 8>(wtype, p, layers, s);
-    if (pro == PRO_PLAIN && epi == EPI_GATED) return launch_wt<PRO_PLAIN, EPI_GATED, 8>(wtype, p, layers, s);
-    if (pro == PRO_NORM && epi == EPI_GATED) return launch_wt<PRO_NORM, EPI_GATED, 8>(wtype, p, layers, s);
-    if (pro == PRO_TAPS && epi == EPI_ARGMAX) return launch_wt<PRO_TAPS, EPI_ARGMAX, 8>(wtype, p, layers, s);
+    if (pro == PRO_GATHER && epi == EPI_BLOCKINIT) return launch_wt<PRO_GATHER, EPI_BLOCKINIT, 8>(wtype, p, layers, s, maxm);
+    if (pro == PRO_NORM && epi == EPI_STORE) return launch_wt<PRO_NORM, EPI_STORE, 8>(wtype, p, layers, s, maxm);
+    if (pro == PRO_PLAIN && epi == EPI_RESID) return launch_wt<PRO_PLAIN, EPI_RESID, 8>(wtype, p, layers, s, maxm);
+    if (pro == PRO_PLAIN && epi == EPI_STORE) return launch_wt<PRO_PLAIN, EPI_STORE, 8>(wtype, p, layers, s, maxm);
+    if (pro == PRO_PLAIN && epi == EPI_GATED) return launch_wt<PRO_PLAIN, EPI_GATED, 8>(wtype, p, layers, s, maxm);
+    if (pro == PRO_NORM && epi == EPI_GATED) return launch_wt<PRO_NORM, EPI_GATED, 8>(wtype, p, layers, s, maxm);
+    if (pro == PRO_TAPS && epi == EPI_ARGMAX) return launch_wt<PRO_TAPS, EPI_ARGMAX, 8>(wtype, p, layers, s, maxm);
 #undef DFL_CASE
     return hipErrorInvalidValue;
 }

@@ -100,13 +100,19 @@ struct GemvParams {
     uint64_t* stamps;    // EPI_ARGMAX, optional: wall clock at start and end of each workgroup [nblocks][2]
 };
 
-// Host-side launcher: picks MAXM, the weight type and the modes.
+// Host-side launcher: picks the kernel for the weight type and the modes; maxm is
+// the row capacity (4: int4 weights and M <= 4 only; 8; or 32 for the long-row
+// paths).
 hipError_t launch_gemv(int wtype, int pro, int epi, int maxm, const GemvParams& p, int layers, hipStream_t s);
 
-// Grid of a launch with up to 8 activation rows, reduction length K and ntiles
-// row tiles under a persistent-workgroup cap (what the argmax partials are
-// sized by): reductions that stage in one pass run persistent workgroups.
-int gemv_head_grid(int wtype, int K, int ntiles, int max_wgs);
+// Grid of a launch with `rows` (<= 8) activation rows, reduction length K and
+// ntiles row tiles under a persistent-workgroup cap (what the argmax partials
+// are sized by): reductions that stage in one pass run persistent workgroups.
+int gemv_head_grid(int wtype, int K, int ntiles, int max_wgs, int rows);
+
+// Activation rows a launch of `rows` rows is compiled for: int4 weights, whose
+// products are ALU-bound, take a 4-row kernel for up to 4 rows; everything else 8
+inline int gemv_maxm(int wtype, int rows) { return (wtype == W_I4 && rows <= 4) ? 4 : 8; }
 
 // LDS budget for staged activations per workgroup
 constexpr int kStageBytes = 64 * 1024;

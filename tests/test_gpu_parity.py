@@ -40,6 +40,8 @@ WIDE_HEADS = scaled(WIDE, name="wide_heads", H=512, m=2, nl=1, F=1024, V=2048, L
 WIDE_FFN = scaled(WIDE, name="wide_ffn", H=512, m=2, nl=1, F=9216, V=2048, L=100, B=1)
 # the same heads with int4-g64 weights on every matrix, LM head included
 WIDE4_SMALL = scaled(WIDE4, name="wide4_small", H=512, m=2, nl=2, F=1024, V=2048, L=300, B=2)
+# one sequence: 4 block rows, the 4-row int4 kernels (the wide4 workload's shape)
+WIDE4_B1 = scaled(WIDE4_SMALL, name="wide4_b1", B=1)
 # 16 ragged sequences (batched workload), narrow layers
 BATCHED_SMALL = scaled(BATCHED, name="batched_small", H=256, m=2, d=256, hq=4, hkv=2, hd=64, nl=2, F=512,
                        V=1000, L=40, L_max=200, B=16)
@@ -57,6 +59,7 @@ CASES = {
     "wide_heads": (WIDE_HEADS, [300, 157]),
     "wide_ffn": (WIDE_FFN, [100]),
     "wide4_small": (WIDE4_SMALL, [300, 211]),
+    "wide4_b1": (WIDE4_B1, [257]),
     "batched_small": (BATCHED_SMALL, [int(x) for x in gen.context_lengths(BATCHED_SMALL)]),
     "batched_r21": (BATCHED_R21, [150, 33, 97]),
     "batched_r140": (BATCHED_R140, [int(x) for x in gen.context_lengths(BATCHED_R140)]),
@@ -218,10 +221,13 @@ def test_draft_forward(name):
 
 
 @pytest.mark.parametrize("wd", ["f32", "bf16", "int4g64"])
-@pytest.mark.parametrize("M,H", [(1, 256), (5, 256), (8, 256), (13, 256), (7, 5120)])
+@pytest.mark.parametrize("M,H", [(1, 256), (4, 256), (5, 256), (8, 256), (12, 256), (13, 256), (3, 5120),
+                                 (7, 5120)])
 def test_lm_head_argmax_planted_and_random(wd, M, H):
     """H = 5120 (the wide workloads' rows) is longer than one staging chunk: the
-    head then runs one workgroup per 16-row tile instead of persistent tiles."""
+    head then runs one workgroup per 16-row tile instead of persistent tiles.
+    int4 heads over at most 4 rows take the 4-row kernel (its own persistent
+    grid); 12 rows are a launch of 8 and one of 4 rows on the 8-row kernel."""
     dims = scaled(TINY, wdtype=wd, H=H, V=1000 if H <= 256 else 3001)
     E = gen.make_weight(dims, "E_out")
     Ed = O.dense(E)
@@ -309,7 +315,8 @@ def test_verify_exhaustive_patterns(V):
     assert np.array_equal(com_o, acc_o + 1)
 
 
-@pytest.mark.parametrize("name", ["tiny", "gqa_bf16", "gqa_rows42", "wide4_small", "batched_small", "batched_r140"])
+@pytest.mark.parametrize("name", ["tiny", "gqa_bf16", "gqa_rows42", "wide4_small", "wide4_b1", "batched_small",
+                                  "batched_r140"])
 def test_multi_round_loop(name):
     """Rounds of append(committed rows) -> forward -> verify, both sides driven
     by the oracle's schedule (planted logits realise accept lengths; the
