@@ -191,7 +191,14 @@ int lm_nblocks(int V, int H, int wtype, int rows) {
 #ifndef DFL_KV_WGS
 #define DFL_KV_WGS DFL_SMALL_WGS  // workgroup cap of the context K/V append, all layers together
 #endif
-int ctx_splits(const dflash_dims& d) { return (d.m * d.H + DFL_CTX_SPLIT_K - 1) / DFL_CTX_SPLIT_K; }
+// (int4 weights: staging the activations costs ALU work as well, so wider K ranges)
+#ifndef DFL_CTX_SPLIT_K_I4
+#define DFL_CTX_SPLIT_K_I4 8192
+#endif
+int ctx_splits(const dflash_dims& d) {
+    const int w = d.wdtype == DFLASH_INT4G64 ? DFL_CTX_SPLIT_K_I4 : DFL_CTX_SPLIT_K;
+    return (d.m * d.H + w - 1) / w;
+}
 // block row counts from which the projections of a bf16 drafter run on matrix
 // cores (one pass over each weight matrix) instead of 8-row GEMV passes
 #ifndef DFL_SKINNY_MIN_ROWS
@@ -398,10 +405,14 @@ hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStr
 
 // A plain-prologue GEMV with a residual (out += x W^T, fp32) or store epilogue (p's
 // out fields): one launch, or split-K partials into part and the ordered reduce that
-// applies the epilogue (long K ranges)
-hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int rows, float* part, hipStream_t s) {
+// applies the epilogue (long K ranges). With norm_gain, a split residual reduce also
+// writes bf16(RMSNorm(out; norm_gain)) to norm_dst (the next projection's rows) and
+// sets *normed; otherwise *normed is cleared.
+hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int rows, float* part, hipStream_t s,
+                      const void* norm_gain = nullptr, uint16_t* norm_dst = nullptr, bool* normed = nullptr) {
     int ns = 1, ks = p.K;
     gemv_split(d, p.K, &ns, &ks);
+    if (normed) *normed = false;
     if (ns <= 1) return gemv_rows(wt, PRO_PLAIN, epi, p, rows, s);
     SkinnyParams r;
     std::memset(&r, 0, sizeof(r));
@@ -429,6 +440,11 @@ hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int r
     p.vt = nullptr;
     const hipError_t e = gemv_rows(wt, PRO_PLAIN, EPI_STORE, p, rows, s);
     if (e != hipSuccess) return e;
+    if (epi == EPI_RESID && norm_gain && norm_dst && normed) {
+        *normed = true;
+        return launch_resid_norm(part, ns, rows, p.N, static_cast<float*>(r.out), r.out_ld, norm_gain,
+                                 d.wdtype == DFLASH_F32, d.eps, norm_dst, d.d, s);
+    }
     return launch_split_reduce(epi == EPI_RESID ? SK_RESID : SK_STORE, r, s);
 }
 
@@ -533,7 +549,12 @@ int skinny_out_ffn(const dflash_model* M, int i, float* h, int rows, const Ws& w
     return DFLASH_OK;
 }
 
-int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B, const Ws& w, hipStream_t s) {
+// next_gain: the RMSNorm gain of the projection that follows the layer (the next
+// layer's attn_norm or out_norm; null when none follows in this call); *an_ready says
+// on entry whether w.an already holds this layer's normalised input rows (bf16) and on
+// return whether it holds the next projection's
+int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B, const Ws& w, hipStream_t s,
+              const void* next_gain, bool* an_ready) {
     const dflash_dims& d = M->dims;
     const dflash_layer& L = M->layers[i];
     const int wt = wtype_of(d.wdtype);
@@ -553,7 +574,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.gain[0] = L.attn_norm;
         int pro = PRO_NORM;
         if (prenorm(d)) {
-            DFL_HIP(norm_rows(h, rows, d.d, L.attn_norm, d.eps, w.an, s));
+            if (!*an_ready) DFL_HIP(norm_rows(h, rows, d.d, L.attn_norm, d.eps, w.an, s));
             p.x = reinterpret_cast<const float*>(w.an);  // bf16 rows (src_f32 = 0)
             pro = PRO_PLAIN;
         }
@@ -602,7 +623,10 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         a.round_out = d.wdtype == DFLASH_F32 ? 0 : 1;
         DFL_HIP(launch_attention(a, s));
     }
+    *an_ready = false;
     if (w.skinny) return skinny_out_ffn(M, i, h, rows, w, s);
+    const bool pn = prenorm(d);
+    bool ffn_ready = false;
     {  // H += O W_o^T
         GemvParams p = base_params(d);
         p.w[0] = wptr(L.w_o);
@@ -613,7 +637,8 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.x_ld = d.hq * d.hd;
         p.out = h;
         p.out_ld = d.d;
-        DFL_HIP(gemv_plain(d, wt, EPI_RESID, p, rows, w.rsp, s));
+        // a split reduce also writes the FFN's normalised rows
+        DFL_HIP(gemv_plain(d, wt, EPI_RESID, p, rows, w.rsp, s, pn ? L.ffn_norm : nullptr, w.an, &ffn_ready));
     }
     {  // A = act(n2 W_gate^T) * (n2 W_up^T), n2 = RMSNorm(H; ffn_norm)
         GemvParams p = base_params(d);
@@ -629,8 +654,8 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.out = w.a;
         p.out_ld = d.F;
         int pro = PRO_NORM;
-        if (prenorm(d)) {
-            DFL_HIP(norm_rows(h, rows, d.d, L.ffn_norm, d.eps, w.an, s));
+        if (pn) {
+            if (!ffn_ready) DFL_HIP(norm_rows(h, rows, d.d, L.ffn_norm, d.eps, w.an, s));
             p.x = reinterpret_cast<const float*>(w.an);
             pro = PRO_PLAIN;
         }
@@ -646,7 +671,8 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.x_ld = d.F;
         p.out = h;
         p.out_ld = d.d;
-        DFL_HIP(gemv_plain(d, wt, EPI_RESID, p, rows, w.rsp, s));
+        // a split reduce also writes the next projection's normalised rows
+        DFL_HIP(gemv_plain(d, wt, EPI_RESID, p, rows, w.rsp, s, pn ? next_gain : nullptr, w.an, an_ready));
     }
     return DFLASH_OK;
 }
@@ -802,13 +828,13 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
     } else if (n <= 8 && splits > 1 && ws && ws_bytes >= part_bytes) {
         // few rows: split the long reduction over more workgroups; partials in ws
         p.rpw = 4;
-        p.ksplit = splits;
         p.kslice = (p.K + splits - 1) / splits;
         p.kslice = (p.kslice + 511) / 512 * 512;
+        p.ksplit = (p.K + p.kslice - 1) / p.kslice;  // every range non-empty
         p.out = static_cast<float*>(ws);
         p.split_stride = (int64_t)n * d.d;
         DFL_HIP(gemv_rows(wtype_of(d.wdtype), PRO_TAPS, EPI_STORE, p, n, s));
-        DFL_HIP(launch_rownorm(static_cast<float*>(ws), splits, (int64_t)n * d.d, h_ctx, n, d.d, M->ctx_norm,
+        DFL_HIP(launch_rownorm(static_cast<float*>(ws), p.ksplit, (int64_t)n * d.d, h_ctx, n, d.d, M->ctx_norm,
                                d.wdtype == DFLASH_F32, d.eps, s));
     } else {
         DFL_HIP(gemv_rows(wtype_of(d.wdtype), PRO_TAPS, EPI_STORE, p, n, s, 1, 32));
@@ -968,7 +994,8 @@ int dflash_draft_layer(const dflash_model* M, int32_t layer, float* h_block, con
     const Ws w = ws_layout(d, B, kv->cap, ws);
     if (!ws || ws_bytes < w.total) return DFLASH_ENOSPC;
     DFL_TRY(gate());
-    DFL_TRY(run_layer(M, layer, h_block, kv, B, w, static_cast<hipStream_t>(stream)));
+    bool an_ready = false;
+    DFL_TRY(run_layer(M, layer, h_block, kv, B, w, static_cast<hipStream_t>(stream), nullptr, &an_ready));
     g_invocations++;
     return DFLASH_OK;
 }
@@ -1003,7 +1030,10 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
         p.seq_base = 0;
         DFL_HIP(gemv_rows(wt, PRO_GATHER, EPI_BLOCKINIT, p, B, s));
     }
-    for (int i = 0; i < d.nl; ++i) DFL_TRY(run_layer(M, i, w.hd, kv, B, w, s));
+    bool an_ready = false;  // w.an holds the next projection's normalised rows
+    for (int i = 0; i < d.nl; ++i)
+        DFL_TRY(run_layer(M, i, w.hd, kv, B, w, s, i + 1 < d.nl ? M->layers[i + 1].attn_norm : M->out_norm,
+                          &an_ready));
     // Y = bf16(bf16(RMSNorm(H; out_norm)) out_proj^T), written straight into y_out
     // when the caller wants it (bf16 for bf16/int4 models, fp32 for fp32 models)
     float* y = y_out ? static_cast<float*>(y_out) : w.y;
@@ -1027,7 +1057,7 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
         p.out_ld = d.H;
         p.out_bf16 = d.wdtype == DFLASH_F32 ? 0 : 1;
         if (prenorm(d)) {
-            DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, w.an, s));
+            if (!an_ready) DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, w.an, s));
             p.x = reinterpret_cast<const float*>(w.an);
             DFL_HIP(gemv_plain(d, wt, EPI_STORE, p, rows, w.rsp, s));
         } else {

@@ -64,6 +64,7 @@ constexpr int kSKC = kSkinnyK;           // K per chunk
 constexpr int kSLd = kSKC + 8;           // padded LDS row (bf16): 8 lanes of a 16-byte read on distinct banks
 constexpr int kSSteps = kSKC / 32;       // MFMA k-steps per chunk
 static_assert(kSNB % 2 == 0, "the gated epilogue pairs gate and up fragments");
+constexpr int kNormMaxK = 8192;  // longest row of the row-norm kernels
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -420,8 +421,6 @@ __global__ __launch_bounds__(kBlock) void skinny_reduce_kernel(const SkinnyParam
     }
 }
 
-constexpr int kNormMaxK = 8192;
-
 // one wavefront per row: the row and its sum of squares in registers, then the
 // scaled row rounded to bf16; grid.y = layer (gain)
 __global__ __launch_bounds__(kBlock) void norm_rows_kernel(const NormRowsParams p) {
@@ -465,6 +464,68 @@ __global__ __launch_bounds__(kBlock) void norm_rows_kernel(const NormRowsParams 
             q.z = pack_bf16x2(v[u][4] * r * g[4], v[u][5] * r * g[5]);
             q.w = pack_bf16x2(v[u][6] * r * g[6], v[u][7] * r * g[7]);
             *reinterpret_cast<uint4*>(o + k) = q;
+        }
+    }
+}
+
+// one workgroup per row: the split partials summed in order into the residual row,
+// its sum of squares reduced over the workgroup, then the normalised row as bf16
+constexpr int kRnThreads = 1024;  // a row of up to 8192 values: two float4 per thread, all loads in flight at once
+__global__ __launch_bounds__(kRnThreads) void resid_norm_kernel(const float* part, int nsplit, int M, int N, float* h,
+                                                                int64_t h_ld, const void* gain, int gain_f32, float eps,
+                                                                uint16_t* dst, int64_t dst_ld) {
+    constexpr int kBlock = kRnThreads;
+    constexpr int U = kNormMaxK / (4 * kBlock);
+    __shared__ float red[kBlock / kWave];
+    const int m = blockIdx.x, tid = threadIdx.x;
+    const int64_t mn = (int64_t)M * N;
+    float* hr = h + (int64_t)m * h_ld;
+    float4 v[U];
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k = (tid + u * kBlock) * 4;
+        if (k < N) {
+            const float* src = part + (int64_t)m * N + k;
+            float4 a = *reinterpret_cast<const float4*>(src);
+#pragma unroll 8
+            for (int sp = 1; sp < nsplit; ++sp) {
+                const float4 t = *reinterpret_cast<const float4*>(src + sp * mn);
+                a.x += t.x;
+                a.y += t.y;
+                a.z += t.z;
+                a.w += t.w;
+            }
+            const float4 o = *reinterpret_cast<const float4*>(hr + k);
+            v[u] = make_float4(o.x + a.x, o.y + a.y, o.z + a.z, o.w + a.w);
+            *reinterpret_cast<float4*>(hr + k) = v[u];
+            ss += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
+        }
+    }
+    ss = wave_sum(ss);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kBlock / kWave; ++w) tot += red[w];
+    const float r = 1.0f / sqrtf(tot / (float)N + eps);
+    uint16_t* o = dst + (int64_t)m * dst_ld;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k = (tid + u * kBlock) * 4;
+        if (k < N) {
+            float g[4];
+            if (gain_f32) {
+                const float4 gv = *reinterpret_cast<const float4*>(static_cast<const float*>(gain) + k);
+                g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
+            } else {
+                const uint2 gv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(gain) + k);
+                g[0] = bf16_lo(gv.x); g[1] = bf16_hi(gv.x); g[2] = bf16_lo(gv.y); g[3] = bf16_hi(gv.y);
+            }
+            uint2 q;
+            q.x = pack_bf16x2(v[u].x * r * g[0], v[u].y * r * g[1]);
+            q.y = pack_bf16x2(v[u].z * r * g[2], v[u].w * r * g[3]);
+            *reinterpret_cast<uint2*>(o + k) = q;
         }
     }
 }
@@ -559,6 +620,16 @@ hipError_t launch_split_reduce(int epi, const SkinnyParams& p, hipStream_t s) {
         hipLaunchKernelGGL((skinny_reduce_kernel<SK_STORE>), dim3((unsigned)blocks, 1), dim3(kBlock), 0, s, p);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_resid_norm(const float* part, int nsplit, int M, int N, float* h, int64_t h_ld, const void* gain,
+                             int gain_f32, float eps, uint16_t* dst, int64_t dst_ld, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    if (N <= 0 || (N % 4) || N > kNormMaxK || nsplit < 1 || (h_ld % 4) || (dst_ld % 4)) return hipErrorInvalidValue;
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL(resid_norm_kernel, dim3((unsigned)M), dim3(kRnThreads), 0, s, part, nsplit, M, N, h, h_ld, gain,
+                       gain_f32, eps, dst, dst_ld);
     return hipGetLastError();
 }
 

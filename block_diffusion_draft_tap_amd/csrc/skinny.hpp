@@ -80,6 +80,12 @@ hipError_t launch_skinny(int epi, const SkinnyParams& p, hipStream_t s);
 // epilogue; used for partials written by other kernels (N a multiple of 4)
 hipError_t launch_split_reduce(int epi, const SkinnyParams& p, hipStream_t s);
 
+// The residual split-K sum fused with the next RMSNorm: for each of the M rows,
+// h[m] += sum_s part[s][m] (split order), then dst[m] = bf16(h[m] * (mean h[m]^2 +
+// eps)^-1/2 * gain); one workgroup per row, N a multiple of 4 and at most 8192
+hipError_t launch_resid_norm(const float* part, int nsplit, int M, int N, float* h, int64_t h_ld, const void* gain,
+                             int gain_f32, float eps, uint16_t* dst, int64_t dst_ld, hipStream_t s);
+
 // dst + z * dst_layer_stride: rows r of bf16(x[r, k] * (mean_k x[r, k]^2 + eps)^-1/2 * gain[z][k])
 // for rows of K fp32 values (K a multiple of 8, at most 8192), z < layers (grid.y)
 struct NormRowsParams {

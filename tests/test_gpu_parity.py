@@ -36,8 +36,9 @@ GQA_ROWS42 = scaled(TINY, name="gqa_rows42", wdtype="bf16", H=256, d=768, hq=12,
 
 # the wide drafter's attention geometry (d = 40 x 128) with fewer layers and narrower taps / FFN
 WIDE_HEADS = scaled(WIDE, name="wide_heads", H=512, m=2, nl=1, F=1024, V=2048, L=300, B=2)
-# the wide drafter's layer with a long FFN (down projection K = 9216: three split-K ranges)
-WIDE_FFN = scaled(WIDE, name="wide_ffn", H=512, m=2, nl=1, F=9216, V=2048, L=100, B=1)
+# the wide drafter's layers with a long FFN (down projection K = 9216: three split-K ranges,
+# whose reduce also normalises the next layer's or the out projection's rows)
+WIDE_FFN = scaled(WIDE, name="wide_ffn", H=512, m=2, nl=2, F=9216, V=2048, L=100, B=1)
 # the same heads with int4-g64 weights on every matrix, LM head included
 WIDE4_SMALL = scaled(WIDE4, name="wide4_small", H=512, m=2, nl=2, F=1024, V=2048, L=300, B=2)
 # one sequence: 4 block rows, the 4-row int4 kernels (the wide4 workload's shape)
