@@ -207,14 +207,17 @@ int ctx_splits(const dflash_dims& d) {
 // long rows of a bf16 / int4 drafter: RMSNorm once per row into bf16 rows (norm_rows)
 // instead of two passes over the fp32 row in every GEMV workgroup's prologue
 bool prenorm(const dflash_dims& d) { return d.wdtype != DFLASH_F32 && d.d > kRegNormMaxK; }
-// split-K of the plain-prologue GEMVs (residual and store epilogues): K ranges of at most
-// this many elements (staged once within the normal LDS budget, several workgroups per
-// CU); a reduce kernel adds the partial sums in split order and applies the epilogue
+// split-K of the plain-prologue GEMVs (residual, store and gated epilogues): K ranges
+// of at most this many elements for the 8-row kernels (twice as many for the 4-row
+// int4 kernel), which stage once within the normal LDS budget with several
+// workgroups per CU; a reduce kernel adds the partial sums in split order and applies
+// the epilogue
 #ifndef DFL_GEMV_SPLIT_K
 #define DFL_GEMV_SPLIT_K 4096
 #endif
-void gemv_split(const dflash_dims& d, int K, int* nsplit, int* kslice) {
-    int ns = d.wdtype == DFLASH_F32 ? 1 : (K + DFL_GEMV_SPLIT_K - 1) / DFL_GEMV_SPLIT_K;
+void gemv_split(const dflash_dims& d, int K, int rows, int* nsplit, int* kslice) {
+    const int lim = DFL_GEMV_SPLIT_K * (8 / gemv_maxm(wtype_of(d.wdtype), rows < 8 ? rows : 8));
+    int ns = d.wdtype == DFLASH_F32 ? 1 : (K + lim - 1) / lim;
     int ks = K;
     if (ns > 1) {
         ks = ((K + ns - 1) / ns + 511) / 512 * 512;
@@ -316,13 +319,13 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     const size_t o_skp = take(w.skinny ? skinny_part_bytes(d, (int)rows) : 0);
     size_t rsp_bytes = 0;
     if (!w.skinny) {
-        // O and down (N = d), QKV (K = d) and out (N = H, K = d), when their rows are
-        // pre-normalised (plain prologue)
-        const int shapes[4][2] = {{d.hq * d.hd, d.d}, {d.F, d.d}, {d.d, qkv_rows}, {d.d, d.H}};
-        for (int q = 0; q < 4; ++q) {
+        // O and down (N = d), QKV (K = d), out (N = H, K = d) and gate/up (2F rows, K = d),
+        // when their rows are pre-normalised (plain prologue)
+        const int shapes[5][2] = {{d.hq * d.hd, d.d}, {d.F, d.d}, {d.d, qkv_rows}, {d.d, d.H}, {d.d, 2 * d.F}};
+        for (int q = 0; q < 5; ++q) {
             if (q >= 2 && !prenorm(d)) break;
             int ns = 1, ks = 0;
-            gemv_split(d, shapes[q][0], &ns, &ks);
+            gemv_split(d, shapes[q][0], (int)rows, &ns, &ks);
             const size_t b = (size_t)ns * rows * shapes[q][1] * 4;
             if (ns > 1 && b > rsp_bytes) rsp_bytes = b;
         }
@@ -411,13 +414,14 @@ hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStr
 hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int rows, float* part, hipStream_t s,
                       const void* norm_gain = nullptr, uint16_t* norm_dst = nullptr, bool* normed = nullptr) {
     int ns = 1, ks = p.K;
-    gemv_split(d, p.K, &ns, &ks);
+    gemv_split(d, p.K, rows, &ns, &ks);
     if (normed) *normed = false;
     if (ns <= 1) return gemv_rows(wt, PRO_PLAIN, epi, p, rows, s);
     SkinnyParams r;
     std::memset(&r, 0, sizeof(r));
     r.M = rows;
-    r.N = p.N;
+    r.N = epi == EPI_GATED ? p.F : p.N;  // gated: F outputs from the 2F gate and up rows
+    r.act = p.act;
     r.nsplit = ns;
     r.part = part;
     r.out = p.out;
@@ -432,6 +436,7 @@ hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int r
     p.ksplit = ns;
     p.kslice = ks;
     p.max_wgs = DFL_SMALL_WGS / ns > 0 ? DFL_SMALL_WGS / ns : 1;
+    p.rpw = rpw_for(p.N);
     p.out = part;
     p.out_ld = p.N;
     p.split_stride = (int64_t)rows * p.N;
@@ -445,7 +450,7 @@ hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int r
         return launch_resid_norm(part, ns, rows, p.N, static_cast<float*>(r.out), r.out_ld, norm_gain,
                                  d.wdtype == DFLASH_F32, d.eps, norm_dst, d.d, s);
     }
-    return launch_split_reduce(epi == EPI_RESID ? SK_RESID : SK_STORE, r, s);
+    return launch_split_reduce(epi == EPI_RESID ? SK_RESID : (epi == EPI_GATED ? SK_GATED : SK_STORE), r, s);
 }
 
 // matrix-core projections of `rows` block rows, in launches of up to kSkinnyRows
@@ -659,7 +664,10 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
             p.x = reinterpret_cast<const float*>(w.an);
             pro = PRO_PLAIN;
         }
-        DFL_HIP(gemv_rows(wt, pro, EPI_GATED, p, rows, s));
+        if (pro == PRO_PLAIN)
+            DFL_HIP(gemv_plain(d, wt, EPI_GATED, p, rows, w.rsp, s));
+        else
+            DFL_HIP(gemv_rows(wt, pro, EPI_GATED, p, rows, s));
     }
     {  // H += A W_down^T
         GemvParams p = base_params(d);

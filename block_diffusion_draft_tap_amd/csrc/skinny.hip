@@ -388,13 +388,33 @@ __global__ __launch_bounds__(kST) void skinny_kernel(const SkinnyParams p) {
 }
 
 // the sum of the split-K partials in split order, then the epilogue; 4 outputs a
-// thread, grid.y = layer
+// thread, grid.y = layer. SK_GATED (N = F): the partials hold 2F rows per activation
+// row, gate rows [0, F) then up rows [F, 2F)
 template <int EPI>
 __global__ __launch_bounds__(kBlock) void skinny_reduce_kernel(const SkinnyParams p) {
     const int64_t mn = (int64_t)p.M * p.N;
     const int64_t e = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4;
     if (e >= mn) return;
     const int z = blockIdx.y;
+    const int m = (int)(e / p.N), n = (int)(e - (int64_t)m * p.N);
+    if constexpr (EPI == SK_GATED) {
+        // partials hold the 2F gate and up rows; this thread's 4 outputs j = n .. n+3 (N = F)
+        const int64_t mn2 = 2 * mn;
+        const float* gp = p.part + (int64_t)m * 2 * p.N + n;
+        float4 g = *reinterpret_cast<const float4*>(gp), u = *reinterpret_cast<const float4*>(gp + p.N);
+        for (int sp = 1; sp < p.nsplit; ++sp) {
+            const float4 tg = *reinterpret_cast<const float4*>(gp + sp * mn2);
+            const float4 tu = *reinterpret_cast<const float4*>(gp + sp * mn2 + p.N);
+            g.x += tg.x; g.y += tg.y; g.z += tg.z; g.w += tg.w;
+            u.x += tu.x; u.y += tu.y; u.z += tu.z; u.w += tu.w;
+        }
+        const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+        uint16_t* o = static_cast<uint16_t*>(p.out) + (int64_t)m * p.out_ld + n;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            o[q] = (uint16_t)f32_to_bf16_bits((p.act == 0 ? gelu_tanh(gv[q]) : silu(gv[q])) * uv[q]);
+        return;
+    }
     const float* src = p.part + (int64_t)z * p.nsplit * mn + e;
     float4 s = *reinterpret_cast<const float4*>(src);
     for (int sp = 1; sp < p.nsplit; ++sp) {
@@ -404,7 +424,6 @@ __global__ __launch_bounds__(kBlock) void skinny_reduce_kernel(const SkinnyParam
         s.z += t.z;
         s.w += t.w;
     }
-    const int m = (int)(e / p.N), n = (int)(e - (int64_t)m * p.N);
     if constexpr (EPI == SK_KV) {
         int b, pos;
         kv_slot(p, p.row_base + m, b, pos);
@@ -616,6 +635,8 @@ hipError_t launch_split_reduce(int epi, const SkinnyParams& p, hipStream_t s) {
     (void)hipGetLastError();  // report only this launch's status
     if (epi == SK_RESID)
         hipLaunchKernelGGL((skinny_reduce_kernel<SK_RESID>), dim3((unsigned)blocks, 1), dim3(kBlock), 0, s, p);
+    else if (epi == SK_GATED)
+        hipLaunchKernelGGL((skinny_reduce_kernel<SK_GATED>), dim3((unsigned)blocks, 1), dim3(kBlock), 0, s, p);
     else if (epi == SK_STORE)
         hipLaunchKernelGGL((skinny_reduce_kernel<SK_STORE>), dim3((unsigned)blocks, 1), dim3(kBlock), 0, s, p);
     else
