@@ -280,6 +280,162 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Row-split MFMA kernel (bf16 caches, 33..48 query rows per kv head): one
+// wavefront per 16-row tile, every wavefront walking all of the workgroup's
+// units. Each wavefront holds one tile's Q, O and softmax state (about half
+// the registers of one wavefront holding all tiles), so two wavefronts fit on
+// a SIMD and the next unit's K and V go into a second register set while the
+// current unit is multiplied. The wavefronts read the same K and V (served by
+// L2 and L1 after the first) and write their own rows' partial results: no
+// in-workgroup merge.
+
+template <int HD, int NRT>
+__global__ __launch_bounds__(64 * NRT, 2) void attn_rows_kernel(const AttnParams p) {
+    constexpr int KS = HD / 32, DT = HD / 16;
+    constexpr int PLD = kChunk + 8;
+    __shared__ __align__(16) uint16_t plds[NRT][2][16][PLD];  // P tiles (high, low) per wavefront
+
+    const int lane = threadIdx.x & 63, rt = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int s = blockIdx.x % p.nsplit;
+    const int bg = blockIdx.x / p.nsplit;
+    const int g = bg % p.hkv, b = bg / p.hkv;
+    const int qpg = p.hq / p.hkv;
+    const int R = qpg * p.gamma;
+    const int lenb = min(max(p.len[b], 0), p.cap);
+    // units: the context's 32-key chunks, then the block's gamma keys; the workgroup
+    // takes an equal run of consecutive units
+    const int nch = (lenb + kChunk - 1) / kChunk;
+    const int nunits = nch + 1;
+    const int upw = (nunits + p.nsplit - 1) / p.nsplit;
+    const int u_begin = min(nunits, s * upw);
+    const int u_end = min(nunits, u_begin + upw);
+
+    const int64_t qkv_ld = p.qkv_ld;
+    const uint16_t* qrow0 = static_cast<const uint16_t*>(p.qkv) + (int64_t)b * p.gamma * qkv_ld;
+    const int kcol = p.hq * HD + g * HD;
+    const uint16_t* kc = static_cast<const uint16_t*>(p.kcache) + ((int64_t)b * p.hkv + g) * p.cap * HD;
+    const uint16_t* vc = static_cast<const uint16_t*>(p.vcache) + ((int64_t)b * p.hkv + g) * HD * (int64_t)p.cap;
+    const uint16_t* vblk = p.vblk + ((int64_t)b * p.hkv + g) * HD * kChunk;
+    const float sl2 = p.scale * 1.4426950408889634f;  // scores in log2 units
+
+    // K rows c0 + nt*16 + col (dims ks*32 + 8*grp ..) and V keys c0 + 8*grp .. +8 of dims
+    // dt*16 + col (rows past the valid keys: in-bounds rows, masked / zeroed before use)
+    u32x4 kA[2][KS], vA[DT], kB[2][KS], vB[DT];
+    auto load_unit = [&](const int u, u32x4 (&kb)[2][KS], u32x4 (&vb)[DT]) {
+        const uint16_t *k0, *k1, *vp;
+        int64_t vstride;
+        if (u != nch) {
+            k0 = kc + (int64_t)(u * kChunk + col) * HD + 8 * grp;
+            k1 = k0 + 16 * HD;
+            vp = vc + (int64_t)col * p.cap + u * kChunk + 8 * grp;
+            vstride = 16 * (int64_t)p.cap;
+        } else {
+            k0 = qrow0 + (int64_t)min(col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
+            k1 = qrow0 + (int64_t)min(16 + col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
+            vp = vblk + col * kChunk + 8 * grp;
+            vstride = 16 * kChunk;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            kb[0][ks] = *reinterpret_cast<const u32x4*>(k0 + ks * 32);
+            kb[1][ks] = *reinterpret_cast<const u32x4*>(k1 + ks * 32);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vb[dt] = *reinterpret_cast<const u32x4*>(vp + dt * vstride);
+    };
+    const bool any = u_begin < u_end;
+    if (any) load_unit(u_begin, kA, vA);
+
+    // this wavefront's Q tile: rows rt*16 + col (rows past R repeat row R-1, never stored)
+    u32x4 qa[KS];
+    {
+        const int r = min(rt * 16 + col, R - 1);
+        const uint16_t* src = qrow0 + (int64_t)(r % p.gamma) * qkv_ld + (g * qpg + r / p.gamma) * HD + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = *reinterpret_cast<const u32x4*>(src + ks * 32);
+    }
+
+    f32x4 o[DT];
+    float m[4], l[4];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { m[e] = -INFINITY; l[e] = 0.f; }
+
+    auto unit = [&](const int u, u32x4 (&kb)[2][KS], u32x4 (&vb)[DT]) {
+        const int nvalid = (u == nch) ? p.gamma : min(kChunk, lenb - u * kChunk);
+        f32x4 sacc[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sacc[nt] = mfma16(qa[ks], kb[nt][ks], sacc[nt]);
+        }
+        const bool v0ok = col < nvalid, v1ok = 16 + col < nvalid;
+        const bool rescale = (u != u_begin);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float s0 = v0ok ? sacc[0][e] * sl2 : -INFINITY;
+            const float s1 = v1ok ? sacc[1][e] * sl2 : -INFINITY;
+            const float mn = fmaxf(m[e], row16_max(fmaxf(s0, s1)));  // finite: key 0 is valid
+            const float p0 = __builtin_amdgcn_exp2f(s0 - mn);
+            const float p1 = __builtin_amdgcn_exp2f(s1 - mn);
+            const float al = __builtin_amdgcn_exp2f(m[e] - mn);
+            l[e] = l[e] * al + row16_sum(p0 + p1);
+            m[e] = mn;
+            if (rescale) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[dt][e] *= al;
+            }
+            const uint32_t hp = pack_bf16x2(p0, p1);
+            const uint32_t lp = pack_bf16x2(p0 - bf16_lo(hp), p1 - bf16_hi(hp));
+            plds[rt][0][4 * grp + e][col] = (uint16_t)hp;
+            plds[rt][0][4 * grp + e][16 + col] = (uint16_t)(hp >> 16);
+            plds[rt][1][4 * grp + e][col] = (uint16_t)lp;
+            plds[rt][1][4 * grp + e][16 + col] = (uint16_t)(lp >> 16);
+        }
+        const u32x4 pa = *reinterpret_cast<const u32x4*>(&plds[rt][0][col][8 * grp]);
+        const u32x4 pl = *reinterpret_cast<const u32x4*>(&plds[rt][1][col][8 * grp]);
+        if (nvalid < kChunk) {
+            const int nk = nvalid - 8 * grp;
+            u32x4 mk;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) mk[q] = (2 * q + 1 < nk) ? 0xFFFFFFFFu : ((2 * q < nk) ? 0x0000FFFFu : 0u);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) vb[dt] &= mk;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = mfma16(pl, vb[dt], mfma16(pa, vb[dt], o[dt]));
+    };
+
+    // two units per trip (set A: even offsets from u_begin, set B: odd); the loads of the
+    // last trip re-read the last unit, never multiplied
+    for (int u = u_begin; u < u_end; u += 2) {
+        load_unit(min(u + 1, u_end - 1), kB, vB);
+        unit(u, kA, vA);
+        if (u + 1 >= u_end) break;
+        load_unit(min(u + 2, u_end - 1), kA, vA);
+        unit(u + 1, kB, vB);
+    }
+
+    // this wavefront's rows: o (lane holds dims dt*16 + col of rows 4*grp + e), m, l
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = rt * 16 + 4 * grp + e;
+        if (r >= R) continue;
+        const int h = g * qpg + r / p.gamma, i = r % p.gamma;
+        float* dst = p.part + ((((int64_t)b * p.hq + h) * p.nparts + s) * p.gamma + i) * (HD + 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) dst[dt * 16 + col] = o[dt][e];
+        if (col == 0) {
+            dst[HD] = m[e] * 0.6931471805599453f;  // natural-log units (-inf without units)
+            dst[HD + 1] = l[e];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // VALU kernel (fp32 caches)
 
 template <int HD, int RMAX>
@@ -484,7 +640,35 @@ __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) 
 #define DFL_ATTN_WGS 1024
 #endif
 
-void attention_splits(int cap, int gamma, int kv_f32, int pairs, int* nsplit, int* nparts) {
+// workgroups the row-split kernel aims for (three wavefronts each)
+#ifndef DFL_ATTN_ROWS_WGS
+#define DFL_ATTN_ROWS_WGS 2048
+#endif
+// the row-split kernel serves launches of up to this many 32-key units in all (pairs x
+// units): there attention is latency-bound. Beyond it (many long sequences) the K/V
+// stream is the bound, and the kernel's three reads of each unit cost more than its
+// registers save.
+#ifndef DFL_ATTN_ROWS_MAX_UNITS
+#define DFL_ATTN_ROWS_MAX_UNITS 8192
+#endif
+
+static bool use_rows_kernel(int rows, int kv_f32, int pairs, int cap) {
+    const int64_t units = (int64_t)(cap + kChunk - 1) / kChunk + 1;
+    return !kv_f32 && rows > 32 && rows <= kMaxRows && (int64_t)pairs * units <= DFL_ATTN_ROWS_MAX_UNITS;
+}
+
+void attention_splits(int cap, int gamma, int kv_f32, int pairs, int rows, int* nsplit, int* nparts) {
+    if (use_rows_kernel(rows, kv_f32, pairs, cap)) {
+        // a workgroup walks its units with three wavefronts; enough workgroups to fill the GPU
+        const int units = (cap + kChunk - 1) / kChunk + 1;
+        const int np = pairs > 0 ? pairs : 1;
+        int ns = (DFL_ATTN_ROWS_WGS + np - 1) / np;
+        ns = ns > units ? units : ns;
+        ns = ns < 1 ? 1 : (ns > kMaxSplit ? kMaxSplit : ns);
+        *nsplit = ns;
+        *nparts = ns;
+        return;
+    }
     if (kv_f32) {
         int ns = (cap + gamma + kTile - 1) / kTile;
         ns = ns < 1 ? 1 : (ns > 64 ? 64 : ns);
@@ -523,6 +707,8 @@ static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
             hipLaunchKernelGGL((attn_mfma_kernel<HD, 1>), grid, dim3(kBlock), 0, s, p);
         else if (R <= 32)
             hipLaunchKernelGGL((attn_mfma_kernel<HD, 2>), grid, dim3(kBlock), 0, s, p);
+        else if (use_rows_kernel(R, 0, p.B * p.hkv, p.cap))
+            hipLaunchKernelGGL((attn_rows_kernel<HD, 3>), grid, dim3(64 * 3), 0, s, p);
         else if (R <= kMaxRows)
             hipLaunchKernelGGL((attn_mfma_kernel<HD, 3>), grid, dim3(kBlock), 0, s, p);
         else

@@ -25,9 +25,10 @@ struct AttnParams {
 };
 
 // Workgroups per (sequence, kv head) and partial results per (sequence, head)
-// for a cache of `cap` rows and `pairs` (sequence, kv head) pairs (one partial
-// per workgroup); the workspace holds B*hq*nparts*gamma*(hd+2) floats.
-void attention_splits(int cap, int gamma, int kv_f32, int pairs, int* nsplit, int* nparts);
+// for a cache of `cap` rows, `pairs` (sequence, kv head) pairs and `rows` query
+// rows per kv head (one partial per workgroup); the workspace holds
+// B*hq*nparts*gamma*(hd+2) floats.
+void attention_splits(int cap, int gamma, int kv_f32, int pairs, int rows, int* nsplit, int* nparts);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 int attention_max_rows(int kv_f32);
 

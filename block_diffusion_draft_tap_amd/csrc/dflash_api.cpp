@@ -296,7 +296,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     Ws w{};
     const size_t rows = (size_t)B * d.gamma;
     const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
-    attention_splits(cap, d.gamma, d.wdtype == DFLASH_F32, B * d.hkv, &w.nsplit, &w.nparts);
+    attention_splits(cap, d.gamma, d.wdtype == DFLASH_F32, B * d.hkv, (d.hq / d.hkv) * d.gamma, &w.nsplit, &w.nparts);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;

@@ -52,6 +52,13 @@ BATCHED_SMALL = scaled(BATCHED, name="batched_small", H=256, m=2, d=256, hq=4, h
 BATCHED_R21 = scaled(BATCHED_SMALL, name="batched_r21", B=3, L=150, L_max=150)
 BATCHED_R140 = scaled(BATCHED_SMALL, name="batched_r140", B=20, V=3001, L=40, L_max=120)
 
+# 35 query rows per kv head over many long sequences (64 x 2 kv heads, ~2100 keys: more
+# key units in all than the row-split attention kernel takes, so the kernel whose
+# wavefronts each hold all three row tiles runs) and 448 block rows (four matrix-core
+# launches of 128 rows and one of 64)
+ROWS35_MANY = scaled(BATCHED, name="rows35_many", H=128, m=2, d=640, hq=10, hkv=2, hd=64, nl=1, F=256, V=500,
+                     B=64, L=2050, L_max=2100)
+
 CASES = {
     "tiny": (TINY, [TINY.L]),
     "gqa_bf16": (GQA_BF16, [200, 77, 131]),
@@ -64,6 +71,7 @@ CASES = {
     "batched_small": (BATCHED_SMALL, [int(x) for x in gen.context_lengths(BATCHED_SMALL)]),
     "batched_r21": (BATCHED_R21, [150, 33, 97]),
     "batched_r140": (BATCHED_R140, [int(x) for x in gen.context_lengths(BATCHED_R140)]),
+    "rows35_many": (ROWS35_MANY, [int(x) for x in gen.context_lengths(ROWS35_MANY)]),
 }
 
 _cache = {}
