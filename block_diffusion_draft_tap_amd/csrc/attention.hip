@@ -37,10 +37,6 @@ constexpr int kMaxSplit = 64;  // workgroups per (sequence, kv head), MFMA kerne
 constexpr int kMaxRows = 48;   // query rows per kv head, MFMA kernel
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-// (native vectors: arrays of them stay in registers where arrays of the HIP
-// vector structs may be kept in scratch memory)
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,

@@ -7,6 +7,11 @@
 
 namespace dfl {
 
+// native vectors: arrays of them stay in registers where arrays of the HIP vector
+// structs may be kept in scratch memory
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWave = 64;
 constexpr int kBlock = 256;  // 4 wavefronts per workgroup
 

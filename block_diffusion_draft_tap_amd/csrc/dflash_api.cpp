@@ -169,15 +169,18 @@ constexpr int kLmWgs = DFL_LM_WGS;
 #ifndef DFL_LM_WGS_I4
 #define DFL_LM_WGS_I4 512
 #endif
-// one argmax partial per LM-head workgroup; the head runs 4 rows per wavefront
-// Row tiles of 16 vocabulary rows; a head whose rows (H) stage in one pass runs
-// persistent workgroups (kLmWgs, or one per CU for long rows), a longer one a
-// workgroup per tile.
-int lm_rpw(int wtype) { return wtype == W_I4 ? DFL_LM_RPW_I4 : 4; }
+// weight rows per wavefront of a bf16 / fp32 LM head
+#ifndef DFL_LM_RPW
+#define DFL_LM_RPW 4
+#endif
+// One argmax partial per LM-head workgroup. Row tiles of 4 * rpw vocabulary rows; a
+// head whose rows (H) stage in one pass runs persistent workgroups (kLmWgs, or one
+// per CU for long rows), a longer one a workgroup per tile.
+int lm_rpw(int wtype) { return wtype == W_I4 ? DFL_LM_RPW_I4 : DFL_LM_RPW; }
 int lm_tiles(int V, int wtype) { return (V + 4 * lm_rpw(wtype) - 1) / (4 * lm_rpw(wtype)); }
 // argmax partials per row, enough for any head layout
 int lm_tiles_max(int V) {
-    const int r = DFL_LM_RPW_I4 < 4 ? DFL_LM_RPW_I4 : 4;
+    const int r = DFL_LM_RPW_I4 < DFL_LM_RPW ? DFL_LM_RPW_I4 : DFL_LM_RPW;
     return (V + 4 * r - 1) / (4 * r);
 }
 int lm_wgs(int wtype) { return wtype == W_I4 ? DFL_LM_WGS_I4 : kLmWgs; }

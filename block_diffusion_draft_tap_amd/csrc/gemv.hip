@@ -36,6 +36,10 @@ namespace dfl {
 #ifndef DFL_PF_WIDE
 #define DFL_PF_WIDE 2
 #endif
+// weight iterations in flight in the bf16 / fp32 LM head (argmax epilogue)
+#ifndef DFL_PF_HEAD
+#define DFL_PF_HEAD 2
+#endif
 
 template <int WT> struct WTraits;
 template <> struct WTraits<W_F32> { typedef float X; static constexpr int EPL = 8; };
@@ -275,7 +279,8 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
     typedef typename WTraits<WT>::X X;
     constexpr int EPL = WTraits<WT>::EPL;
     constexpr int STEP = 64 * EPL;
-    constexpr int PF = RPW >= 4 ? DFL_PF_WIDE : DFL_PF;  // weight iterations kept in flight
+    // weight iterations kept in flight
+    constexpr int PF = (EPI == EPI_ARGMAX && WT != W_I4) ? DFL_PF_HEAD : (RPW >= 4 ? DFL_PF_WIDE : DFL_PF);
     extern __shared__ __align__(16) unsigned char smem[];
     X* xs = reinterpret_cast<X*>(smem);                                                 // [MAXM][KC]
     float* xsum = reinterpret_cast<float*>(smem + (size_t)MAXM * KC * sizeof(X));       // [MAXM][KC/32]
@@ -303,11 +308,39 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
     // iterations of this lane in chunk 0
     const int nit = (kw0 > lane * EPL) ? (kw0 - lane * EPL + STEP - 1) / STEP : 0;
 
-    // first PF weight iterations of this tile, in flight before the prologue
+    // LM head over bf16 rows: the activation rows go out before the weights. Loads return
+    // in issue order, so staged after the weight prefetch they would wait behind it and
+    // hold back the first products; issued first, they land while the weights stream.
+    // Up to kYB 16-byte chunks per thread; a longer head stages as below.
+    constexpr bool kHeadY = EPI == EPI_ARGMAX && WT == W_BF16 && PRO == PRO_TAPS;
+    constexpr int kYB = 8;
+    u32x4 yreg[kHeadY ? kYB : 1];
+    const int yunits = kw0 / 8;
+    const bool yfast = kHeadY && !p.src_f32 && p.M > 0 && (kw0 % 8) == 0 && p.M * yunits <= kYB * kBlock;
+    if constexpr (kHeadY) {
+        if (yfast) {
+            const uint16_t* y = static_cast<const uint16_t*>(p.taps[0]);
+#pragma unroll
+            for (int i = 0; i < kYB; ++i) {
+                const int u = min(tid + i * kBlock, p.M * yunits - 1);
+                const int m = u / yunits, c = u - m * yunits;
+                yreg[i] = *reinterpret_cast<const u32x4*>(y + (int64_t)m * p.tap_ld + kb + 8 * c);
+            }
+        }
+    }
+
+    // first PF weight iterations of this tile, in flight before the prologue (after the
+    // activation loads above, all PF go out, lanes past the K range re-reading its last
+    // chunk: a fixed count lets the wait for the activations leave them in flight; a
+    // head staged the usual way keeps the per-lane guard, measured faster there)
     WChunk<WT> pre[PF][RPW];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-        if (i < nit) {
+        if (kHeadY && yfast) {
+            const int kk = min(kb + lane * EPL + i * STEP, ke - EPL);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) wload<WT>(pre[i][r], W, rows[r], K, kk);
+        } else if (i < nit) {
 #pragma unroll
             for (int r = 0; r < RPW; ++r) wload<WT>(pre[i][r], W, rows[r], K, kb + lane * EPL + i * STEP);
         }
@@ -346,7 +379,20 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
     }
 
     constexpr bool kRegNorm = (PRO == PRO_NORM) && (WT != W_I4) && (MAXM == 8);
-    if (kRegNorm && single && K <= kRegNormMaxK) {
+    if (kHeadY && yfast) {
+        // rows at or past M stay unwritten: their products land in accumulator slots that
+        // never reach a result
+        uint16_t* xb = reinterpret_cast<uint16_t*>(xs);
+#pragma unroll
+        for (int i = 0; i < (kHeadY ? kYB : 1); ++i) {
+            const int u = tid + i * kBlock;
+            if (u < p.M * yunits) {
+                const int m = u / yunits, c = u - m * yunits;
+                *reinterpret_cast<u32x4*>(xb + (size_t)m * KC + 8 * c) = yreg[i];
+            }
+        }
+        __syncthreads();
+    } else if (kRegNorm && single && K <= kRegNormMaxK) {
         // one round trip: each wavefront loads whole rows and the matching gains
         // into registers, reduces the sum of squares with shuffles and writes the
         // normalised, rounded row to LDS

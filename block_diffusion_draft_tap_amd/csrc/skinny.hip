@@ -67,10 +67,6 @@ static_assert(kSNB % 2 == 0, "the gated epilogue pairs gate and up fragments");
 constexpr int kNormMaxK = 8192;  // longest row of the row-norm kernels
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-// (native vectors: arrays of them stay in registers where arrays of the HIP
-// vector structs may be kept in scratch memory)
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
