@@ -4,10 +4,11 @@
 //
 // Tiles: a workgroup of GWM x GWN wavefronts owns a BM x BN output tile and
 // walks K in steps of 64. Each step's A and B tiles (rows x 64 bf16) go through
-// registers into one of two LDS buffers (rows padded to 72 elements, which
-// keeps groups of eight lanes on distinct banks for 16-byte reads) while the
-// other buffer feeds the matrix cores, so global loads of step k+1 overlap the
-// products of step k; one barrier per step. Wavefront (wm, wn) computes its
+// registers into one of two LDS buffers (rows padded to 80 elements: no bank
+// conflicts for the 16-byte fragment reads and tile writes, where a pad of 8
+// measured conflicts on 37% of the LDS cycles) while the other buffer feeds the
+// matrix cores; one barrier per step. The global loads run one step ahead
+// (normalised A) or two (tap A, two register sets). Wavefront (wm, wn) computes its
 // (BM/GWM) x (BN/GWN) block of the tile as 16 x 16 products of
 // v_mfma_f32_16x16x32_bf16, lane l holding
 //   A[l % 16][8 (l / 16) + e],  B[8 (l / 16) + e][l % 16]   (e < 8)
@@ -38,9 +39,18 @@ namespace dfl {
 #ifndef DFL_GEMM_WN
 #define DFL_GEMM_WN 2
 #endif
-// K steps whose global loads are in flight ahead of the step being multiplied (1 or 2)
-#ifndef DFL_GEMM_DEPTH
-#define DFL_GEMM_DEPTH 1
+// K steps whose global loads are in flight ahead of the step being multiplied (1 or 2),
+// for tap A operands and for normalised fp32 A operands (whose staging takes twice the
+// registers: two sets spill)
+#ifndef DFL_GEMM_DEPTH_TAPS
+#define DFL_GEMM_DEPTH_TAPS 2
+#endif
+#ifndef DFL_GEMM_DEPTH_NORM
+#define DFL_GEMM_DEPTH_NORM 1
+#endif
+// LDS row padding (bf16 elements)
+#ifndef DFL_GEMM_PAD
+#define DFL_GEMM_PAD 16
 #endif
 // consecutive output tiles of one XCD walk GROUP_M row tiles for each column tile
 #ifndef DFL_GEMM_GROUP_M
@@ -50,14 +60,13 @@ namespace dfl {
 constexpr int kBM = DFL_GEMM_BM, kBN = DFL_GEMM_BN, kBK = 64;
 constexpr int kGWM = DFL_GEMM_WM, kGWN = DFL_GEMM_WN, kThreads = 64 * kGWM * kGWN;
 constexpr int kMT = kBM / kGWM / 16, kNT = kBN / kGWN / 16;  // 16 x 16 products per wavefront
-constexpr int kLd = kBK + 8;  // padded LDS row (bf16 elements)
+constexpr int kLd = kBK + DFL_GEMM_PAD;  // padded LDS row (bf16 elements)
 constexpr int kAC = kBM * 8 / kThreads, kBC = kBN * 8 / kThreads;  // 16-byte chunks per thread
 static_assert(kAC * kThreads == kBM * 8 && kBC * kThreads == kBN * 8, "tile must split evenly");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f32x4& c) {
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                    0, 0);
 }
@@ -66,7 +75,7 @@ __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f3
 template <int AMODE>
 struct AStage;
 template <>
-struct AStage<GEMM_A_TAPS> { uint4 v[kAC]; };
+struct AStage<GEMM_A_TAPS> { u32x4 v[kAC]; };
 template <>
 struct AStage<GEMM_A_NORM> { float4 lo[kAC], hi[kAC]; float r[kAC]; };
 
@@ -91,7 +100,7 @@ __device__ __forceinline__ void load_a(const GemmParams& p, int m0, int k0, ASta
         const int c = t + kThreads * i;
         const int row = min(m0 + (c >> 3), p.M - 1);  // rows past M: any valid row, never stored
         if constexpr (AMODE == GEMM_A_TAPS) {
-            st.v[i] = *reinterpret_cast<const uint4*>(abase + (int64_t)row * p.a_ld + 8 * (c & 7));
+            st.v[i] = *reinterpret_cast<const u32x4*>(abase + (int64_t)row * p.a_ld + 8 * (c & 7));
         } else {
             const float* src = p.x + (int64_t)row * p.a_ld + k0 + 8 * (c & 7);
             st.lo[i] = *reinterpret_cast<const float4*>(src);
@@ -109,7 +118,7 @@ __device__ __forceinline__ void store_a(const GemmParams& p, int k0, const void*
     for (int i = 0; i < kAC; ++i) {
         const int c = t + kThreads * i;
         const int r = c >> 3, kc = 8 * (c & 7);
-        uint4 v;
+        u32x4 v;
         if constexpr (AMODE == GEMM_A_TAPS) {
             v = st.v[i];
         } else {
@@ -125,26 +134,26 @@ __device__ __forceinline__ void store_a(const GemmParams& p, int k0, const void*
             v.z = pack_bf16x2(y[4], y[5]);
             v.w = pack_bf16x2(y[6], y[7]);
         }
-        *reinterpret_cast<uint4*>(&As[r][kc]) = v;
+        *reinterpret_cast<u32x4*>(&As[r][kc]) = v;
     }
 }
 
-__device__ __forceinline__ void load_b(const GemmParams& p, const uint16_t* B, int n0, int k0, uint4 (&st)[kBC]) {
+__device__ __forceinline__ void load_b(const GemmParams& p, const uint16_t* B, int n0, int k0, u32x4 (&st)[kBC]) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < kBC; ++i) {
         const int c = t + kThreads * i;
         const int64_t row = p.b_row0 + min(n0 + (c >> 3), p.N - 1);
-        st[i] = *reinterpret_cast<const uint4*>(B + row * p.K + k0 + 8 * (c & 7));
+        st[i] = *reinterpret_cast<const u32x4*>(B + row * p.K + k0 + 8 * (c & 7));
     }
 }
 
-__device__ __forceinline__ void store_b(const uint4 (&st)[kBC], uint16_t (*Bs)[kLd]) {
+__device__ __forceinline__ void store_b(const u32x4 (&st)[kBC], uint16_t (*Bs)[kLd]) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < kBC; ++i) {
         const int c = t + kThreads * i;
-        *reinterpret_cast<uint4*>(&Bs[c >> 3][8 * (c & 7)]) = st[i];
+        *reinterpret_cast<u32x4*>(&Bs[c >> 3][8 * (c & 7)]) = st[i];
     }
 }
 
@@ -198,13 +207,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
     auto mma_step = [&](const int cur) {
 #pragma unroll
         for (int ks = 0; ks < kBK / 32; ++ks) {
-            uint4 af[kMT], bfr[kNT];
+            u32x4 af[kMT], bfr[kNT];
 #pragma unroll
             for (int i = 0; i < kMT; ++i)
-                af[i] = *reinterpret_cast<const uint4*>(&As[cur][wm * (kBM / kGWM) + i * 16 + col][ks * 32 + 8 * grp]);
+                af[i] = *reinterpret_cast<const u32x4*>(&As[cur][wm * (kBM / kGWM) + i * 16 + col][ks * 32 + 8 * grp]);
 #pragma unroll
             for (int j = 0; j < kNT; ++j)
-                bfr[j] = *reinterpret_cast<const uint4*>(&Bs[cur][wn * (kBN / kGWN) + j * 16 + col][ks * 32 + 8 * grp]);
+                bfr[j] = *reinterpret_cast<const u32x4*>(&Bs[cur][wn * (kBN / kGWN) + j * 16 + col][ks * 32 + 8 * grp]);
 #pragma unroll
             for (int i = 0; i < kMT; ++i)
 #pragma unroll
@@ -212,9 +221,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
         }
     };
 
-    if constexpr (DFL_GEMM_DEPTH == 1) {
+    constexpr int kDepth = AMODE == GEMM_A_TAPS ? DFL_GEMM_DEPTH_TAPS : DFL_GEMM_DEPTH_NORM;
+    if constexpr (kDepth == 1) {
         AStage<AMODE> sa;
-        uint4 sb[kBC];
+        u32x4 sb[kBC];
         load_a<AMODE>(p, m0, 0, sa);
         load_b(p, Bw, n0, 0, sb);
         store_a<AMODE>(p, 0, gain, sa, As[0]);
@@ -226,6 +236,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
             const int kn = min(kt + 1, KT - 1) * kBK;
             load_a<AMODE>(p, m0, kn, sa);
             load_b(p, Bw, n0, kn, sb);
+            // keep the loads ahead of the products (left alone, the scheduler sinks them
+            // below most of the step's products and the step then waits for them)
+            __builtin_amdgcn_sched_barrier(0);
             mma_step(cur);
             store_a<AMODE>(p, kn, gain, sa, As[cur ^ 1]);
             store_b(sb, Bs[cur ^ 1]);
@@ -235,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
         // two register sets: step t's tiles live in set t % 2 from their load (two
         // steps ahead) until they are written to LDS buffer t % 2 one step ahead
         AStage<AMODE> sa0, sa1;
-        uint4 sb0[kBC], sb1[kBC];
+        u32x4 sb0[kBC], sb1[kBC];
         const int k1 = min(1, KT - 1) * kBK;
         load_a<AMODE>(p, m0, 0, sa0);
         load_b(p, Bw, n0, 0, sb0);
