@@ -2,7 +2,8 @@
 //   argmax_merge_kernel   per-workgroup (max, index) partials -> greedy ids
 //   verify_partial_kernel per (verify row, vocab slice) argmax of target logits
 //   verify_final_kernel   prefix compare: accepted, committed, ids, next anchor
-//   rownorm_kernel        in-place RMSNorm of fp32 rows with a gain (Eq 2)
+//   rownorm_kernel        RMSNorm of fp32 rows (sum of split partials) with a gain (Eq 2)
+//   rownorm1_kernel       the same for rows from a single source, read once
 //   advance_len_kernel    len[b] += appended rows (retained context grows)
 //   f32_to_bf16_kernel    fp32 -> bf16 copy for optional outputs
 // Every reduction runs in a fixed order and resolves equal maxima to the
@@ -147,6 +148,43 @@ __global__ __launch_bounds__(kBlock) void rownorm_kernel(const float* src, int n
     }
 }
 
+// single-source rows (no split partials): each 16-byte chunk of the row is read once into
+// registers, the sum of squares reduced across the workgroup, then scaled and written
+// (in place when src == dst: every thread writes only the chunks it read)
+template <int KP4>
+__global__ __launch_bounds__(kBlock) void rownorm1_kernel(const float* src, float* dst, int d, const void* gain,
+                                                          int gain_f32, float eps) {
+    __shared__ float sv[4];
+    const int64_t roff = (int64_t)blockIdx.x * d;
+    const int tid = threadIdx.x, n4 = d / 4;
+    f32x4 v[KP4];
+#pragma unroll
+    for (int j = 0; j < KP4; ++j)
+        v[j] = *reinterpret_cast<const f32x4*>(src + roff + 4 * min(tid + j * kBlock, n4 - 1));
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < KP4; ++j)
+        if (tid + j * kBlock < n4) s += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    s = wave_sum(s);
+    if ((tid & 63) == 0) sv[tid >> 6] = s;
+    __syncthreads();
+    const float tot = sv[0] + sv[1] + sv[2] + sv[3];
+    const float r = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+    for (int j = 0; j < KP4; ++j) {
+        const int q = tid + j * kBlock;
+        if (q < n4) {
+            const int k = 4 * q;
+            f32x4 o;
+            o.x = v[j].x * r * load_gain(gain, gain_f32, k);
+            o.y = v[j].y * r * load_gain(gain, gain_f32, k + 1);
+            o.z = v[j].z * r * load_gain(gain, gain_f32, k + 2);
+            o.w = v[j].w * r * load_gain(gain, gain_f32, k + 3);
+            *reinterpret_cast<f32x4*>(dst + roff + k) = o;
+        }
+    }
+}
+
 __global__ void advance_len_kernel(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap) {
     for (int b = threadIdx.x; b < B; b += blockDim.x) {
         const int rows = row_offsets[b + 1] - row_offsets[b];
@@ -197,6 +235,19 @@ hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int g
 hipError_t launch_rownorm(const float* src, int nsplit, int64_t split_stride, float* dst, int rows, int d,
                           const void* gain, int gain_f32, float eps, hipStream_t s) {
     (void)hipGetLastError();  // report only this launch's status
+    const bool vec = nsplit == 1 && d % 4 == 0 && ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+    if (vec && d <= 4 * kBlock) {
+        hipLaunchKernelGGL(rownorm1_kernel<1>, dim3(rows), dim3(kBlock), 0, s, src, dst, d, gain, gain_f32, eps);
+        return hipGetLastError();
+    }
+    if (vec && d <= 8 * kBlock) {
+        hipLaunchKernelGGL(rownorm1_kernel<2>, dim3(rows), dim3(kBlock), 0, s, src, dst, d, gain, gain_f32, eps);
+        return hipGetLastError();
+    }
+    if (vec && d <= 32 * kBlock) {
+        hipLaunchKernelGGL(rownorm1_kernel<8>, dim3(rows), dim3(kBlock), 0, s, src, dst, d, gain, gain_f32, eps);
+        return hipGetLastError();
+    }
     if (d <= 4 * kBlock)
         hipLaunchKernelGGL(rownorm_kernel<4>, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
                            gain_f32, eps);

@@ -15,6 +15,12 @@
       reads and writes N bytes: the last PyTorch kernel dispatched before the
       first launch of the measured kernel.
 
+  python -m block_diffusion_draft_tap_amd.prof_report counters <counter_collection.csv>...
+      --kernel <name substring> [--command CMD ...]
+      Per-dispatch averages of the counters of one kernel over one or more
+      `--pmc` passes, with the share of LDS-active cycles lost to bank
+      conflicts when both SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE are there.
+
 The traffic summary records a hash of the kernel sources it was measured with
 (kernel_sources_hash); a reader of the summary compares it with the current
 sources and ignores the figure once they differ.
@@ -117,6 +123,25 @@ def traffic_summary(fetch_csv, write_csv, kernel, copy_bytes, algorithmic_bytes)
     }
 
 
+def counter_summary(paths, kernel):
+    vals, name, n = {}, None, 0
+    for path in paths:
+        disp = _dispatches(path)
+        ids = [i for i in sorted(disp) if kernel in disp[i]["name"]]
+        if not ids:
+            raise SystemExit(f"{path}: no dispatch of a kernel containing {kernel!r}")
+        name = disp[ids[0]]["name"]
+        n = max(n, len(ids))
+        for c in disp[ids[0]]["vals"]:
+            vals[c] = sum(disp[i]["vals"][c] for i in ids) / len(ids)
+    out = {"kernel": name[:120], "dispatches per pass": str(n)}
+    out.update({f"{c} per dispatch": f"{v:.6g}" for c, v in sorted(vals.items())})
+    if vals.get("SQ_LDS_IDX_ACTIVE"):
+        if "SQ_LDS_BANK_CONFLICT" in vals:
+            out["bank-conflict cycles / LDS-active cycles"] = f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_LDS_IDX_ACTIVE']:.4f}"
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -134,12 +159,19 @@ def main(argv=None):
     t.add_argument("--algorithmic-bytes", type=int, required=True)
     t.add_argument("--title", default="Memory traffic per launch")
     t.add_argument("--command", action="append", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--title", default="Hardware counters per dispatch")
+    c.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
     out = [f"# {a.title}", ""]
     if a.command:
         out += ["Made with:", "", "```"] + a.command + ["```", ""]
     if a.cmd == "stats":
         out.append(stats_table(a.csv, a.per, per_kernel=a.per_kernel))
+    elif a.cmd == "counters":
+        out += [f"- {k}: {v}" for k, v in counter_summary(a.csv, a.kernel).items()]
     else:
         vals = traffic_summary(a.fetch, a.write, a.kernel, a.copy_bytes, a.algorithmic_bytes)
         out += [f"- {k}: {v}" for k, v in vals.items()]

@@ -47,3 +47,21 @@ def test_stats_per_step(tmp_path):
         w.writerow(["layer", 20, 600, 30, 0, 20, 40, 0])
     t = prof_report.stats_table(str(p), per_kernel="head")
     assert "| `layer` | 20 | 5.00 |" in t and "| `head` | 4 | 1.00 |" in t and "60.0%" in t
+
+
+def test_counter_summary_averages_and_conflict_share(tmp_path):
+    p1 = tmp_path / "a.csv"
+    p2 = tmp_path / "b.csv"
+    with open(p1, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, c, v) in enumerate([("void other", "SQ_LDS_IDX_ACTIVE", 5.0),
+                                          ("void dfl::gemm_kernel<0, 0>", "SQ_LDS_IDX_ACTIVE", 100.0),
+                                          ("void dfl::gemm_kernel<0, 0>", "SQ_LDS_BANK_CONFLICT", 30.0)], start=1):
+            w.writerow({"Dispatch_Id": 7 if i > 1 else 1, "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
+    _counter_csv(p2, "SQ_VALU_MFMA_BUSY_CYCLES", [("void dfl::gemm_kernel<0, 0>", 40.0), ("void dfl::gemm_kernel<0, 0>", 60.0)])
+    v = prof_report.counter_summary([str(p1), str(p2)], "gemm_kernel<0, 0>")
+    assert v["SQ_LDS_IDX_ACTIVE per dispatch"] == "100"
+    assert v["SQ_VALU_MFMA_BUSY_CYCLES per dispatch"] == "50"
+    assert v["bank-conflict cycles / LDS-active cycles"] == "0.3000"
+    assert v["dispatches per pass"] == "2"
