@@ -51,9 +51,16 @@ namespace dfl {
 #endif
 // chunks of activations loaded ahead of the one multiplied (1 or 2; with 2, the wait
 // for chunk c + 1's activations before their LDS store leaves the weights of c + 1 and
-// c + 2 in flight, loads completing in issue order)
+// c + 2 in flight, loads completing in issue order), and the wavefronts per SIMD the
+// kernel is compiled for. Two wavefronts per SIMD (two workgroups per CU, one's LDS and
+// barrier work overlapping the other's weight stream) fit the register budget only with
+// one chunk of activations ahead: with two the kernel spills, and so does the 8-fragment
+// (113 to 128 rows) kernel, which keeps one wavefront per SIMD.
 #ifndef DFL_SK_ADEPTH
-#define DFL_SK_ADEPTH 2
+#define DFL_SK_ADEPTH 1
+#endif
+#ifndef DFL_SK_OCC
+#define DFL_SK_OCC 2
 #endif
 
 namespace {
@@ -117,7 +124,7 @@ __device__ __forceinline__ void store_one(const SkinnyParams& p, int m, int n, f
 }
 
 template <int MT, int EPI>
-__global__ __launch_bounds__(kST) void skinny_kernel(const SkinnyParams p) {
+__global__ __launch_bounds__(kST, MT >= 8 ? 1 : DFL_SK_OCC) void skinny_kernel(const SkinnyParams p) {
     constexpr int RED = EPI == SK_ARGMAX ? MT * 16 : 1;
     constexpr int META = EPI == SK_KV ? MT * 16 : 1;
     __shared__ __align__(16) uint16_t As[2][MT * 16][kSLd];
