@@ -379,7 +379,12 @@ GemvParams base_params(const dflash_dims& d) {
 
 hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStream_t s, int layers = 1,
                      int maxm_long = 8) {
-    const int maxm = rows > 8 ? maxm_long : gemv_maxm(wtype, rows);
+    // the bf16 block init of at most 4 sequences over rows longer than the 8-row kernel
+    // stages in its normal LDS budget (H 5120) stages 4 rows: half the LDS keeps it in
+    // that budget, at three persistent workgroups per CU instead of one
+    const bool init4 = wtype == W_BF16 && pro == PRO_GATHER && epi == EPI_BLOCKINIT && rows <= 4 &&
+                       p.K > kStageBytes / (8 * 2);
+    const int maxm = rows > 8 ? maxm_long : init4 ? 4 : gemv_maxm(wtype, rows);
     for (int r0 = 0; r0 < rows; r0 += maxm) {
         GemvParams q = p;
         q.M = rows - r0 < maxm ? rows - r0 : maxm;

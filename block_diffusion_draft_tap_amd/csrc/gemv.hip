@@ -762,6 +762,8 @@ template <int PRO, int EPI, int MAXM>
 static hipError_t launch_wt(int wtype, const GemvParams& p, int layers, hipStream_t s, int maxm) {
     if constexpr (MAXM == 8) {
         if (maxm == 4 && wtype == W_I4) return launch_rpw<W_I4, PRO, EPI, 4>(p, layers, s);
+        if constexpr (PRO == PRO_GATHER && EPI == EPI_BLOCKINIT)
+            if (maxm == 4 && wtype == W_BF16) return launch_rpw<W_BF16, PRO, EPI, 4>(p, layers, s);
     }
     switch (wtype) {
         case W_F32: return launch_rpw<W_F32, PRO, EPI, MAXM>(p, layers, s);
@@ -772,7 +774,9 @@ static hipError_t launch_wt(int wtype, const GemvParams& p, int layers, hipStrea
 }
 
 hipError_t launch_gemv(int wtype, int pro, int epi, int maxm, const GemvParams& p, int layers, hipStream_t s) {
-    if (maxm == 4 && (wtype != W_I4 || p.M > 4)) return hipErrorInvalidValue;
+    // 4-row kernels: int4 weights, and the bf16 block init (one anchor row per sequence)
+    if (maxm == 4 && (p.M > 4 || !(wtype == W_I4 || (wtype == W_BF16 && pro == PRO_GATHER && epi == EPI_BLOCKINIT))))
+        return hipErrorInvalidValue;
 #define DFL_CASE(PRO, EPI)                                                                      \
     if (pro == PRO && epi == EPI) {                                                             \
         return maxm <= 8 ? launch_wt<PRO, EPI, 8>(wtype, p, layers, s, maxm)                          \

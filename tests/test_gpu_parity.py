@@ -11,7 +11,8 @@ that keep their kernel paths: the wide drafter's heads (40 query / 8 kv heads
 of dim 128, 35 query rows per kv head, SiLU FFN, 7-row block; rows of 5120
 normalised once per row, the O projection in two split-K ranges), its layer
 with a 9216-wide FFN (the down projection in three split-K ranges), the same
-heads with int4-g64 weights everywhere (4-row block), and 16 ragged sequences
+heads with int4-g64 weights everywhere (4-row block), target rows of 5120 on a
+narrow drafter (long-row block init, context projection and LM head), and 16 ragged sequences
 (plus 3 and 20 sequences: 21 and 140 block rows on the matrix-core path).
 """
 
@@ -43,6 +44,11 @@ WIDE_FFN = scaled(WIDE, name="wide_ffn", H=512, m=2, nl=2, F=9216, V=2048, L=100
 WIDE4_SMALL = scaled(WIDE4, name="wide4_small", H=512, m=2, nl=2, F=1024, V=2048, L=300, B=2)
 # one sequence: 4 block rows, the 4-row int4 kernels (the wide4 workload's shape)
 WIDE4_B1 = scaled(WIDE4_SMALL, name="wide4_b1", B=1)
+# target hidden rows of 5120 (the wide workloads' taps, embedding and LM-head rows) on a
+# narrow drafter: the 4-row bf16 block init over rows longer than the 8-row kernel's normal
+# LDS budget, split-K context projection over 2 x 5120 columns, long-row LM head
+WIDE_LONGROW = scaled(WIDE, name="wide_longrow", H=5120, m=2, d=256, hq=4, hkv=2, hd=64, nl=1, F=512, V=1000,
+                      L=64, B=2)
 # 16 ragged sequences (batched workload), narrow layers
 BATCHED_SMALL = scaled(BATCHED, name="batched_small", H=256, m=2, d=256, hq=4, hkv=2, hd=64, nl=2, F=512,
                        V=1000, L=40, L_max=200, B=16)
@@ -66,6 +72,7 @@ CASES = {
     "default": (DEFAULT, [DEFAULT.L]),
     "wide_heads": (WIDE_HEADS, [300, 157]),
     "wide_ffn": (WIDE_FFN, [100]),
+    "wide_longrow": (WIDE_LONGROW, [64, 41]),
     "wide4_small": (WIDE4_SMALL, [300, 211]),
     "wide4_b1": (WIDE4_B1, [257]),
     "batched_small": (BATCHED_SMALL, [int(x) for x in gen.context_lengths(BATCHED_SMALL)]),
