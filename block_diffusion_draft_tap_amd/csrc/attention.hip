@@ -115,31 +115,43 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     // K rows c0 + nt*16 + col (dims ks*32 + 8*grp ..) and V keys c0 + 8*grp .. +8 of dims
     // dt*16 + col. Keys past nvalid come from in-bounds rows (cache rows below cap, clamped
     // block rows): their scores are masked and their values zeroed before use.
+    // The next unit's K goes out as soon as this unit's scores are issued and its V once
+    // the P.V products are, so they land during the softmax and products instead of
+    // after them, with no second register set.
     u32x4 kb[2][KS], vb[DT];
-    auto load_unit = [&](const int u) {
-        const uint16_t *k0, *k1, *vp;
-        int64_t vstride;
+    auto load_k = [&](const int u) {
+        const uint16_t *k0, *k1;
         if (u != nch) {
             k0 = kc + (int64_t)(u * kChunk + col) * HD + 8 * grp;
             k1 = k0 + 16 * HD;
-            vp = vc + (int64_t)col * p.cap + u * kChunk + 8 * grp;
-            vstride = 16 * (int64_t)p.cap;
         } else {
             k0 = qrow0 + (int64_t)min(col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
             k1 = qrow0 + (int64_t)min(16 + col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
-            vp = vblk + col * kChunk + 8 * grp;
-            vstride = 16 * kChunk;
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             kb[0][ks] = *reinterpret_cast<const u32x4*>(k0 + ks * 32);
             kb[1][ks] = *reinterpret_cast<const u32x4*>(k1 + ks * 32);
         }
+    };
+    auto load_v = [&](const int u) {
+        const uint16_t* vp;
+        int64_t vstride;
+        if (u != nch) {
+            vp = vc + (int64_t)col * p.cap + u * kChunk + 8 * grp;
+            vstride = 16 * (int64_t)p.cap;
+        } else {
+            vp = vblk + col * kChunk + 8 * grp;
+            vstride = 16 * kChunk;
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) vb[dt] = *reinterpret_cast<const u32x4*>(vp + dt * vstride);
     };
     // the first unit's loads go out together with Q's
-    if (u_begin < u_end) load_unit(u_begin);
+    if (u_begin < u_end) {
+        load_k(u_begin);
+        load_v(u_begin);
+    }
 
     // Q tiles as A operands: row = rt*16 + col, dims ks*32 + 8*grp ..; rows past R repeat
     // row R-1 and are never stored
@@ -163,7 +175,6 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     }
 
     for (int u = u_begin; u < u_end; ++u) {
-        if (u != u_begin) load_unit(u);
         const int nvalid = (u == nch) ? p.gamma : min(kChunk, lenb - u * kChunk);
 
         f32x4 sacc[NRT][2];
@@ -175,6 +186,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) sacc[rt][nt] = mfma16(qa[rt][ks], kb[nt][ks], sacc[rt][nt]);
             }
+        if (u + 1 < u_end) load_k(u + 1);
         // online softmax; lane holds rows 4*grp+e, keys col and 16+col
         const bool v0ok = col < nvalid, v1ok = 16 + col < nvalid;
         const bool rescale = (u != u_begin);  // o is still zero on a wavefront's first unit
@@ -223,6 +235,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) o[rt][dt] = mfma16(pl[rt], vb[dt], mfma16(pa[rt], vb[dt], o[rt][dt]));
+        if (u + 1 < u_end) load_v(u + 1);
     }
 
     // merge the four wavefronts in LDS: each writes its o; the per-row weights
