@@ -646,7 +646,7 @@ __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) 
 
 // attention workgroups a launch aims for over all (sequence, kv head) pairs
 #ifndef DFL_ATTN_WGS
-#define DFL_ATTN_WGS 1024
+#define DFL_ATTN_WGS 768
 #endif
 
 // workgroups the row-split kernel aims for (three wavefronts each)
