@@ -238,6 +238,22 @@ bool skinny_ok(const dflash_dims& d, int rows) {
            d.H % kSkinnyK == 0;
 }
 // fp32 split-K partials of the skinny launches of a forward (rows in launches of kSkinnyRows)
+// Split-K of the gated (gate/up) matrix-core projection: gate/up tiles alone give about
+// one workgroup per CU at the wide width (2F = 34816 rows: 272 tiles), where the kernel
+// holds two per CU; split, the K ranges write partial sums over the 2F gate and up rows
+// and an ordered reduce applies the activation.
+#ifndef DFL_SK_GATED_WGS
+#define DFL_SK_GATED_WGS 512
+#endif
+void skinny_gated_split(int n2, int K, int* nsplit, int* kslice) {
+    const int tiles = skinny_tiles(SK_PARTIAL, n2), chunks = K / kSkinnyK;
+    int sp = tiles >= DFL_SK_GATED_WGS ? 1 : (DFL_SK_GATED_WGS + tiles - 1) / tiles;
+    sp = sp < 1 ? 1 : (sp > chunks ? chunks : sp);
+    const int per = chunks > 0 ? (chunks + sp - 1) / sp : 1;
+    *kslice = per * kSkinnyK;
+    *nsplit = chunks > 0 ? (chunks + per - 1) / per : 1;
+}
+
 size_t skinny_part_bytes(const dflash_dims& d, int rows) {
     const int r = rows < kSkinnyRows ? rows : kSkinnyRows;
     const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
@@ -250,7 +266,10 @@ size_t skinny_part_bytes(const dflash_dims& d, int rows) {
         const size_t b = ns > 1 ? (size_t)ns * r * sh[1] * 4 : 0;
         if (b > most) most = b;
     }
-    return most;
+    int ns = 1, ks = 0;
+    skinny_gated_split(2 * d.F, d.d, &ns, &ks);
+    const size_t g = ns > 1 ? (size_t)ns * r * 2 * d.F * 4 : 0;
+    return g > most ? g : most;
 }
 
 // Workspace of the matrix-core paths for n context rows (a round's appended
@@ -483,6 +502,31 @@ hipError_t skinny_rows(int epi, SkinnyParams p, int rows, hipStream_t s) {
     return hipSuccess;
 }
 
+// the gated projection: one launch with the activation epilogue, or (split K) partial
+// sums over the 2F gate and up rows and the gated reduce, per launch of kSkinnyRows rows
+hipError_t skinny_gated(SkinnyParams p, int rows, hipStream_t s) {
+    int ns = 1, ks = p.K;
+    skinny_gated_split(p.N, p.K, &ns, &ks);
+    if (ns <= 1) return skinny_rows(SK_GATED, p, rows, s);
+    for (int r0 = 0; r0 < rows; r0 += kSkinnyRows) {
+        SkinnyParams q = p;
+        q.M = rows - r0 < kSkinnyRows ? rows - r0 : kSkinnyRows;
+        q.a = p.a + (int64_t)r0 * p.a_ld;
+        q.nsplit = ns;
+        q.kslice = ks;
+        q.nblocks = skinny_tiles(SK_PARTIAL, p.N);
+        q.out = nullptr;
+        hipError_t e = launch_skinny(SK_PARTIAL, q, s);
+        if (e != hipSuccess) return e;
+        SkinnyParams r = q;
+        r.N = p.F;
+        r.out = static_cast<uint16_t*>(p.out) + (size_t)r0 * p.out_ld;
+        e = launch_split_reduce(SK_GATED, r, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 SkinnyParams skinny_params(const dflash_weight& W, const uint16_t* a, int64_t a_ld, int N, int K, float* part) {
     SkinnyParams p;
     std::memset(&p, 0, sizeof(p));
@@ -551,7 +595,7 @@ int skinny_out_ffn(const dflash_model* M, int i, float* h, int rows, const Ws& w
         p.act = d.act;
         p.out = w.a;
         p.out_ld = d.F;
-        DFL_HIP(skinny_rows(SK_GATED, p, rows, s));
+        DFL_HIP(skinny_gated(p, rows, s));
     }
     {  // H += A W_down^T
         SkinnyParams p = skinny_params(L.w_down, reinterpret_cast<const uint16_t*>(w.a), d.F, d.d, d.F, w.skp);
