@@ -555,15 +555,45 @@ hipError_t norm_rows(const float* x, int rows, int K, const void* gain, float ep
     return launch_norm_rows(q, s);
 }
 
+// H += a W^T on matrix cores (p's out = H). Split K with norm_gain: the partial sums,
+// then one kernel per row that adds them in split order and also writes
+// bf16(RMSNorm(H; norm_gain)) to norm_dst (the next projection's rows), *normed set;
+// otherwise the residual epilogue alone, *normed cleared
+hipError_t skinny_resid(const dflash_dims& d, SkinnyParams p, int rows, hipStream_t s, const void* norm_gain,
+                        uint16_t* norm_dst, bool* normed) {
+    int ns = 1, ks = p.K;
+    skinny_split(SK_RESID, p.N, p.K, 1, &ns, &ks);
+    *normed = false;
+    if (ns <= 1 || !norm_gain || !norm_dst || (p.N % 4) || p.N > kNormMaxK) return skinny_rows(SK_RESID, p, rows, s);
+    float* h = static_cast<float*>(p.out);
+    for (int r0 = 0; r0 < rows; r0 += kSkinnyRows) {
+        SkinnyParams q = p;
+        q.M = rows - r0 < kSkinnyRows ? rows - r0 : kSkinnyRows;
+        q.a = p.a + (int64_t)r0 * p.a_ld;
+        q.nsplit = ns;
+        q.kslice = ks;
+        q.nblocks = skinny_tiles(SK_PARTIAL, p.N);
+        q.out = nullptr;
+        hipError_t e = launch_skinny(SK_PARTIAL, q, s);
+        if (e != hipSuccess) return e;
+        e = launch_resid_norm(p.part, ns, q.M, p.N, h + (int64_t)r0 * p.out_ld, p.out_ld, norm_gain,
+                              d.wdtype == DFLASH_F32, d.eps, norm_dst + (int64_t)r0 * d.d, d.d, s);
+        if (e != hipSuccess) return e;
+    }
+    *normed = true;
+    return hipSuccess;
+}
+
 // a draft layer's projections on matrix cores (bf16 drafter, 16 or more block
 // rows), with the rounding points of the GEMV path: bf16 normalised rows, Q/K/V,
-// O and A. skinny_qkv: before the attention; skinny_out_ffn: after it
-int skinny_qkv(const dflash_model* M, int i, float* h, int rows, const Ws& w, hipStream_t s) {
+// O and A. skinny_qkv: before the attention (an_ready: w.an already holds the
+// normalised rows); skinny_out_ffn: after it
+int skinny_qkv(const dflash_model* M, int i, float* h, int rows, const Ws& w, hipStream_t s, bool an_ready) {
     const dflash_dims& d = M->dims;
     const dflash_layer& L = M->layers[i];
     const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
     {  // [Q | K_b | V_b] = bf16(RMSNorm(H; attn_norm)) W_qkv^T, V_b head-dim major
-        DFL_HIP(norm_rows(h, rows, d.d, L.attn_norm, d.eps, w.an, s));
+        if (!an_ready) DFL_HIP(norm_rows(h, rows, d.d, L.attn_norm, d.eps, w.an, s));
         SkinnyParams p = skinny_params(L.w_qkv, w.an, d.d, qkv_rows, d.d, w.skp);
         p.out = w.qkv;
         p.out_ld = qkv_rows;
@@ -578,18 +608,21 @@ int skinny_qkv(const dflash_model* M, int i, float* h, int rows, const Ws& w, hi
     return DFLASH_OK;
 }
 
-int skinny_out_ffn(const dflash_model* M, int i, float* h, int rows, const Ws& w, hipStream_t s) {
+// next_gain / an_ready: as for run_layer
+int skinny_out_ffn(const dflash_model* M, int i, float* h, int rows, const Ws& w, hipStream_t s,
+                   const void* next_gain, bool* an_ready) {
     const dflash_dims& d = M->dims;
     const dflash_layer& L = M->layers[i];
-    {  // H += O W_o^T
+    bool ffn_ready = false;
+    {  // H += O W_o^T (a split reduce also writes the FFN's normalised rows)
         SkinnyParams p = skinny_params(L.w_o, reinterpret_cast<const uint16_t*>(w.o), d.hq * d.hd, d.d,
                                        d.hq * d.hd, w.skp);
         p.out = h;
         p.out_ld = d.d;
-        DFL_HIP(skinny_rows(SK_RESID, p, rows, s));
+        DFL_HIP(skinny_resid(d, p, rows, s, L.ffn_norm, w.an, &ffn_ready));
     }
     {  // A = bf16(act(n2 W_gate^T) * (n2 W_up^T)), n2 = bf16(RMSNorm(H; ffn_norm))
-        DFL_HIP(norm_rows(h, rows, d.d, L.ffn_norm, d.eps, w.an, s));
+        if (!ffn_ready) DFL_HIP(norm_rows(h, rows, d.d, L.ffn_norm, d.eps, w.an, s));
         SkinnyParams p = skinny_params(L.w_gate_up, w.an, d.d, 2 * d.F, d.d, w.skp);
         p.F = d.F;
         p.act = d.act;
@@ -597,11 +630,11 @@ int skinny_out_ffn(const dflash_model* M, int i, float* h, int rows, const Ws& w
         p.out_ld = d.F;
         DFL_HIP(skinny_gated(p, rows, s));
     }
-    {  // H += A W_down^T
+    {  // H += A W_down^T (a split reduce also writes the next projection's normalised rows)
         SkinnyParams p = skinny_params(L.w_down, reinterpret_cast<const uint16_t*>(w.a), d.F, d.d, d.F, w.skp);
         p.out = h;
         p.out_ld = d.d;
-        DFL_HIP(skinny_rows(SK_RESID, p, rows, s));
+        DFL_HIP(skinny_resid(d, p, rows, s, next_gain, w.an, an_ready));
     }
     return DFLASH_OK;
 }
@@ -619,7 +652,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
     const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
 
     if (w.skinny) {
-        DFL_TRY(skinny_qkv(M, i, h, rows, w, s));
+        DFL_TRY(skinny_qkv(M, i, h, rows, w, s, *an_ready));
     } else {  // n = RMSNorm(H; attn_norm); [Q | K_b | V_b] = n W_qkv^T
         GemvParams p = base_params(d);
         p.w[0] = wptr(L.w_qkv);
@@ -681,7 +714,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         DFL_HIP(launch_attention(a, s));
     }
     *an_ready = false;
-    if (w.skinny) return skinny_out_ffn(M, i, h, rows, w, s);
+    if (w.skinny) return skinny_out_ffn(M, i, h, rows, w, s, next_gain, an_ready);
     const bool pn = prenorm(d);
     bool ffn_ready = false;
     {  // H += O W_o^T
@@ -1098,7 +1131,7 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
     // when the caller wants it (bf16 for bf16/int4 models, fp32 for fp32 models)
     float* y = y_out ? static_cast<float*>(y_out) : w.y;
     if (w.skinny) {
-        DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, w.an, s));
+        if (!an_ready) DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, w.an, s));
         SkinnyParams p = skinny_params(M->out_proj, w.an, d.d, d.H, d.d, w.skp);
         p.out = y;
         p.out_ld = d.H;

@@ -71,7 +71,6 @@ constexpr int kSKC = kSkinnyK;           // K per chunk
 constexpr int kSLd = kSKC + 8;           // padded LDS row (bf16): 8 lanes of a 16-byte read on distinct banks
 constexpr int kSSteps = kSKC / 32;       // MFMA k-steps per chunk
 static_assert(kSNB % 2 == 0, "the gated epilogue pairs gate and up fragments");
-constexpr int kNormMaxK = 8192;  // longest row of the row-norm kernels
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 

@@ -16,6 +16,7 @@ enum { SK_STORE = 0, SK_RESID = 1, SK_GATED = 2, SK_ARGMAX = 3, SK_KV = 4, SK_PA
 
 constexpr int kSkinnyRows = 128;  // activation rows per launch
 constexpr int kSkinnyK = 128;     // K (and each split's K range) is a multiple of this
+constexpr int kNormMaxK = 8192;   // longest row of the row-norm kernels
 
 struct SkinnyParams {
     int M, N, K;          // SK_GATED: N = 2F weight rows (gate rows [0, F), up rows [F, 2F))
