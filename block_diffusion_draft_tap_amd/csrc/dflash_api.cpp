@@ -257,8 +257,8 @@ void skinny_gated_split(int n2, int K, int* nsplit, int* kslice) {
 size_t skinny_part_bytes(const dflash_dims& d, int rows) {
     const int r = rows < kSkinnyRows ? rows : kSkinnyRows;
     const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
-    const int shapes[4][3] = {{SK_STORE, qkv_rows, d.d}, {SK_RESID, d.d, d.hq * d.hd}, {SK_RESID, d.d, d.F},
-                              {SK_STORE, d.H, d.d}};
+    const int shapes[5][3] = {{SK_STORE, qkv_rows, d.d}, {SK_RESID, d.d, d.hq * d.hd}, {SK_RESID, d.d, d.F},
+                              {SK_STORE, d.H, d.d}, {SK_STORE, d.d, d.H}};
     size_t most = 0;
     for (const auto& sh : shapes) {
         int ns = 1, ks = 0;
@@ -1106,7 +1106,21 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int wt = wtype_of(d.wdtype);
     const int rows = B * d.gamma;
-    {  // block rows: E_in[anchor] tok_proj^T + block_pos[0]; mask_emb[k-1] + block_pos[k]
+    const bool init_sk = w.skinny && d.wdtype == DFLASH_BF16 && M->embed_in.dtype == DFLASH_BF16 &&
+                         M->tok_proj.dtype == DFLASH_BF16 && B >= DFL_SKINNY_MIN_ROWS && d.H % kSkinnyK == 0 &&
+                         (int64_t)d.gamma * d.d >= d.H;
+    if (init_sk) {
+        // 16 or more sequences on matrix cores: the anchors' embeddings gathered into w.an
+        // (B rows of H; it holds B * gamma rows of d), their tok_proj product stored as row 0
+        // of each block, then the block positions added and the mask rows written
+        DFL_HIP(launch_gather_rows(static_cast<const uint16_t*>(M->embed_in.data), M->embed_in.rows, anchor_ids, B,
+                                   d.H, w.an, s));
+        SkinnyParams p = skinny_params(M->tok_proj, w.an, d.H, d.d, d.H, w.skp);
+        p.out = w.hd;
+        p.out_ld = (int64_t)d.gamma * d.d;
+        DFL_HIP(skinny_rows(SK_STORE, p, B, s));
+        DFL_HIP(launch_block_fill(w.hd, B, d.gamma, d.d, M->block_pos, M->mask_emb, 0, s));
+    } else {  // block rows: E_in[anchor] tok_proj^T + block_pos[0]; mask_emb[k-1] + block_pos[k]
         GemvParams p = base_params(d);
         p.w[0] = wptr(M->tok_proj);
         p.N = d.d;

@@ -4,6 +4,8 @@
 //   verify_final_kernel   prefix compare: accepted, committed, ids, next anchor
 //   rownorm_kernel        RMSNorm of fp32 rows (sum of split partials) with a gain (Eq 2)
 //   rownorm1_kernel       the same for rows from a single source, read once
+//   gather_rows_kernel    bf16 table rows by id (the anchors' embeddings)
+//   block_fill_kernel     block rows around a stored anchor product (Eq 3 block init)
 //   advance_len_kernel    len[b] += appended rows (retained context grows)
 //   f32_to_bf16_kernel    fp32 -> bf16 copy for optional outputs
 // Every reduction runs in a fixed order and resolves equal maxima to the
@@ -185,6 +187,31 @@ __global__ __launch_bounds__(kBlock) void rownorm1_kernel(const float* src, floa
     }
 }
 
+// dst[r] = table[clamp(ids[r])] for rows of K bf16 values (K a multiple of 8); one
+// workgroup per row, 16-byte copies
+__global__ __launch_bounds__(kBlock) void gather_rows_kernel(const uint16_t* table, int table_rows, const int32_t* ids,
+                                                            int K, uint16_t* dst) {
+    const int r = blockIdx.x;
+    const int id = min(max(ids[r], 0), table_rows - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(table + (int64_t)id * K);
+    u32x4* out = reinterpret_cast<u32x4*>(dst + (int64_t)r * K);
+    for (int i = threadIdx.x; i < K / 8; i += kBlock) out[i] = src[i];
+}
+
+// the block rows of sequence b around its stored anchor product h[b][0][:] = E_in[anchor] W_tok^T:
+// h[b][0][n] += block_pos[0][n]; h[b][k][n] = mask_emb[k-1][n] + block_pos[k][n] for 0 < k < gamma
+__global__ __launch_bounds__(kBlock) void block_fill_kernel(float* h, int gamma, int d, const void* block_pos,
+                                                           const void* mask_emb, int gain_f32) {
+    const int b = blockIdx.y, k = blockIdx.z;
+    const int n = blockIdx.x * kBlock + threadIdx.x;
+    if (n >= d) return;
+    float* row = h + ((int64_t)b * gamma + k) * d;
+    if (k == 0)
+        row[n] += load_gain(block_pos, gain_f32, n);
+    else
+        row[n] = load_gain(mask_emb, gain_f32, (k - 1) * d + n) + load_gain(block_pos, gain_f32, k * d + n);
+}
+
 __global__ void advance_len_kernel(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap) {
     for (int b = threadIdx.x; b < B; b += blockDim.x) {
         const int rows = row_offsets[b + 1] - row_offsets[b];
@@ -259,6 +286,24 @@ hipError_t launch_rownorm(const float* src, int nsplit, int64_t split_stride, fl
                            gain_f32, eps);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const uint16_t* table, int table_rows, const int32_t* ids, int rows, int K,
+                              uint16_t* dst, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if ((K % 8) || table_rows <= 0) return hipErrorInvalidValue;
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)rows), dim3(kBlock), 0, s, table, table_rows, ids, K, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_fill(float* h, int B, int gamma, int d, const void* block_pos, const void* mask_emb,
+                             int gain_f32, hipStream_t s) {
+    if (B <= 0) return hipSuccess;
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL(block_fill_kernel, dim3((unsigned)((d + kBlock - 1) / kBlock), (unsigned)B, (unsigned)gamma),
+                       dim3(kBlock), 0, s, h, gamma, d, block_pos, mask_emb, gain_f32);
     return hipGetLastError();
 }
 

@@ -15,6 +15,12 @@ hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int g
                          hipStream_t s);
 hipError_t launch_rownorm(const float* src, int nsplit, int64_t split_stride, float* dst, int rows, int d,
                           const void* gain, int gain_f32, float eps, hipStream_t s);
+// dst[r][:] = table[clamp(ids[r])][:] (bf16 rows of K, K a multiple of 8)
+hipError_t launch_gather_rows(const uint16_t* table, int table_rows, const int32_t* ids, int rows, int K,
+                              uint16_t* dst, hipStream_t s);
+// block rows around stored anchor products: h[b][0] += block_pos[0]; h[b][k] = mask_emb[k-1] + block_pos[k]
+hipError_t launch_block_fill(float* h, int B, int gamma, int d, const void* block_pos, const void* mask_emb,
+                             int gain_f32, hipStream_t s);
 hipError_t launch_advance_len(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap,
                               hipStream_t s);
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
