@@ -571,70 +571,77 @@ __global__ __launch_bounds__(kBlock) void attn_valu_kernel(const AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per (b, head, block row): combine the partials. Thread group
-// gi (HD threads, one head-dim column each) sums the partials gi, gi + G, ...;
-// up to kMergeRegs of them are loaded into registers together with the (m, l)
-// pairs, so the whole merge costs one round trip. The weights exp(m_s - M)
-// are formed once in LDS and the groups are combined in a fixed order.
+// One wavefront per (b, head, block row), four rows per workgroup, no barriers:
+// combine the nparts partials (o, m, l) of the row. The (m, l) of the first 64
+// partials (one per lane) and the values of the first kMergeRegs go out in one
+// batch, so up to kMergeRegs partials cost one round trip. M = max m_s, weights
+// w_s = exp(m_s - M) (lane s, read back uniformly), L = sum w_s l_s, and each lane
+// sums its HD/64 head-dim columns over the partials in order s = 0, 1, ...
 constexpr int kMergeRegs = 32;
 
 template <int HD>
 __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) {
-    constexpr int G = kBlock / HD;
-    __shared__ float wts[kMaxParts];
-    __shared__ float red[4];
-    __shared__ float part[G][HD];
-    const int row = blockIdx.x;  // (b*hq + h)*gamma + i
+    constexpr int DPL = HD / 64;  // head-dim columns per lane
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*hq + h)*gamma + i
+    if (row >= p.B * p.hq * p.gamma) return;
     const int i = row % p.gamma;
     const int bh = row / p.gamma;
     const int h = bh % p.hq, b = bh / p.hq;
     const int W = HD + 2;
-    const float* base = p.part + ((int64_t)bh * p.nparts * p.gamma + i) * W;
+    const int np = p.nparts;
+    const float* base = p.part + ((int64_t)bh * np * p.gamma + i) * W;
     const int64_t sstride = (int64_t)p.gamma * W;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int gi = t / HD, dcol = t % HD;
-    const bool in_regs = p.nparts <= kMergeRegs * G;
-    float ov[kMergeRegs];
-    if (in_regs) {
+    float ms = -INFINITY, ls = 0.f;
+    if (lane < np) {
+        ms = base[lane * sstride + HD];
+        ls = base[lane * sstride + HD + 1];
+    }
+    float v[kMergeRegs][DPL];  // partials past np: clamped, in bounds, unused
 #pragma unroll
-        for (int q = 0; q < kMergeRegs; ++q) {
-            const int sidx = min(gi + q * G, p.nparts - 1);  // clamped: in bounds, unused past nparts
-            ov[q] = base[sidx * sstride + dcol];
+    for (int j = 0; j < kMergeRegs; ++j)
+#pragma unroll
+        for (int q = 0; q < DPL; ++q) v[j][q] = base[(int64_t)min(j, np - 1) * sstride + lane + 64 * q];
+    float mx = ms;
+    for (int sidx = 64 + lane; sidx < np; sidx += 64) mx = fmaxf(mx, base[sidx * sstride + HD]);
+    const float M = wave_max(mx);
+    float w = (lane < np && ms != -INFINITY) ? expf(ms - M) : 0.f;
+    float lsum = w * ls;
+    float acc[DPL];
+#pragma unroll
+    for (int q = 0; q < DPL; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMergeRegs; ++j) {
+        if (j < np) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+#pragma unroll
+            for (int q = 0; q < DPL; ++q) acc[q] += wj * v[j][q];
         }
     }
-    float ms = -INFINITY, ls = 0.f;
-    if (t < p.nparts) {
-        ms = base[t * sstride + HD];
-        ls = base[t * sstride + HD + 1];
-    }
-    float M = wave_max(ms);
-    if (lane == 0) red[wave] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float w = (ms == -INFINITY) ? 0.f : expf(ms - M);
-    wts[t] = w;
-    float L = wave_sum(w * ls);
-    __syncthreads();
-    if (lane == 0) red[wave] = L;
-    __syncthreads();
-    L = red[0] + red[1] + red[2] + red[3];
-    float acc = 0.f;
-    if (in_regs) {
-#pragma unroll
-        for (int q = 0; q < kMergeRegs; ++q)
-            if (gi + q * G < p.nparts) acc += wts[gi + q * G] * ov[q];
-    } else {
+    for (int c0 = 0; c0 < np; c0 += 64) {
+        if (c0 > 0) {  // the weights of partials c0 .. c0 + 63
+            const int sidx = c0 + lane;
+            w = 0.f;
+            if (sidx < np) {
+                const float m2 = base[sidx * sstride + HD];
+                w = (m2 == -INFINITY) ? 0.f : expf(m2 - M);
+                lsum += w * base[sidx * sstride + HD + 1];
+            }
+        }
+        const int j0 = c0 == 0 ? kMergeRegs : 0, cnt = min(64, np - c0);
 #pragma unroll 8
-        for (int sidx = gi; sidx < p.nparts; sidx += G) acc += wts[sidx] * base[sidx * sstride + dcol];
-    }
-    part[gi][dcol] = acc;
-    __syncthreads();
-    if (gi == 0) {
-        float y = 0.f;
+        for (int j = j0; j < cnt; ++j) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+            const float* src = base + (int64_t)(c0 + j) * sstride;
 #pragma unroll
-        for (int q = 0; q < G; ++q) y += part[q][dcol];
-        y /= L;
-        const int64_t o = ((int64_t)b * p.gamma + i) * p.out_ld + h * HD + dcol;
+            for (int q = 0; q < DPL; ++q) acc[q] += wj * src[lane + 64 * q];
+        }
+    }
+    const float L = wave_sum(lsum);
+#pragma unroll
+    for (int q = 0; q < DPL; ++q) {
+        const float y = acc[q] / L;
+        const int64_t o = ((int64_t)b * p.gamma + i) * p.out_ld + h * HD + lane + 64 * q;
         if (p.round_out)
             reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_to_bf16_bits(y);
         else
@@ -725,7 +732,7 @@ static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3((unsigned)(p.B * p.hq * p.gamma)), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3((unsigned)((p.B * p.hq * p.gamma + 3) / 4)), dim3(kBlock), 0, s, p);
     return hipGetLastError();
 }
 
