@@ -145,7 +145,19 @@ WeightPtr wptr(const dflash_weight& w) {
 }
 
 
-int rpw_for(int N) { return N >= 16384 ? 4 : (N >= 2048 ? 2 : 1); }
+// output rows from which a projection's GEMV takes 4 weight rows per wavefront: bf16 and
+// fp32 weights from 4096 (wide drafter 628 -> 660 blocks/s), int4 weights (ALU-bound
+// products) from 16384 (4096 cost the int4 wide drafter 8%)
+#ifndef DFL_RPW4_N
+#define DFL_RPW4_N 4096
+#endif
+#ifndef DFL_RPW4_N_I4
+#define DFL_RPW4_N_I4 16384
+#endif
+int rpw_for(int N, int wdtype) {
+    const int n4 = wdtype == DFLASH_INT4G64 ? DFL_RPW4_N_I4 : DFL_RPW4_N;
+    return N >= n4 ? 4 : (N >= 2048 ? 2 : 1);
+}
 // workgroup cap of the per-layer projections (row tiles beyond it are looped over)
 #ifndef DFL_SMALL_WGS
 #define DFL_SMALL_WGS 512
@@ -463,7 +475,7 @@ hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int r
     p.ksplit = ns;
     p.kslice = ks;
     p.max_wgs = DFL_SMALL_WGS / ns > 0 ? DFL_SMALL_WGS / ns : 1;
-    p.rpw = rpw_for(p.N);
+    p.rpw = rpw_for(p.N, d.wdtype);
     p.out = part;
     p.out_ld = p.N;
     p.split_stride = (int64_t)rows * p.N;
@@ -658,7 +670,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.w[0] = wptr(L.w_qkv);
         p.N = qkv_rows;
         p.K = d.d;
-        p.rpw = rpw_for(p.N);
+        p.rpw = rpw_for(p.N, d.wdtype);
         p.x = h;
         p.x_ld = d.d;
         p.gain[0] = L.attn_norm;
@@ -722,7 +734,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.w[0] = wptr(L.w_o);
         p.N = d.d;
         p.K = d.hq * d.hd;
-        p.rpw = rpw_for(p.N);
+        p.rpw = rpw_for(p.N, d.wdtype);
         p.x = w.o;
         p.x_ld = d.hq * d.hd;
         p.out = h;
@@ -759,7 +771,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.w[0] = wptr(L.w_down);
         p.N = d.d;
         p.K = d.F;
-        p.rpw = rpw_for(p.N);
+        p.rpw = rpw_for(p.N, d.wdtype);
         p.x = w.a;
         p.x_ld = d.F;
         p.out = h;
@@ -874,7 +886,7 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
     p.w[0] = wptr(M->w_c);
     p.N = d.d;
     p.K = d.m * d.H;
-    p.rpw = rpw_for(p.N);
+    p.rpw = rpw_for(p.N, d.wdtype);
     for (int j = 0; j < d.m; ++j) p.taps[j] = taps[j];
     p.tap_ld = tap_ld;
     p.H = d.H;
@@ -1056,7 +1068,7 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
     p.max_wgs = DFL_KV_WGS / d.nl > 0 ? DFL_KV_WGS / d.nl : 1;  // per layer (grid.y)
     p.N = 2 * d.hkv * d.hd;
     p.K = d.d;
-    p.rpw = rpw_for(p.N);
+    p.rpw = rpw_for(p.N, d.wdtype);
     p.x = pro == PRO_PLAIN ? static_cast<const float*>(ws) : h_ctx;  // bf16 rows for PRO_PLAIN
     p.x_ld = d.d;
     p.x_layer_stride = pro == PRO_PLAIN ? (int64_t)n * d.d : 0;
@@ -1125,7 +1137,7 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
         p.w[0] = wptr(M->tok_proj);
         p.N = d.d;
         p.K = d.H;
-        p.rpw = rpw_for(p.N);
+        p.rpw = rpw_for(p.N, d.wdtype);
         p.ids = anchor_ids;
         p.table = wptr(M->embed_in);
         p.table_type = wtype_of(M->embed_in.dtype);
@@ -1156,7 +1168,7 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
         p.w[0] = wptr(M->out_proj);
         p.N = d.H;
         p.K = d.d;
-        p.rpw = rpw_for(p.N);
+        p.rpw = rpw_for(p.N, d.wdtype);
         p.x = w.hd;
         p.x_ld = d.d;
         p.gain[0] = M->out_norm;
