@@ -573,13 +573,12 @@ __global__ __launch_bounds__(kBlock) void attn_valu_kernel(const AttnParams p) {
 // ---------------------------------------------------------------------------
 // One wavefront per (b, head, block row), four rows per workgroup, no barriers:
 // combine the nparts partials (o, m, l) of the row. The (m, l) of the first 64
-// partials (one per lane) and the values of the first kMergeRegs go out in one
-// batch, so up to kMergeRegs partials cost one round trip. M = max m_s, weights
+// partials (one per lane) and the values of the first MR go out in one batch, so
+// up to MR partials cost one round trip (MR = 32 up to 32 partials, else 64: the
+// wider batch measured slower where fewer partials suffice). M = max m_s, weights
 // w_s = exp(m_s - M) (lane s, read back uniformly), L = sum w_s l_s, and each lane
 // sums its HD/64 head-dim columns over the partials in order s = 0, 1, ...
-constexpr int kMergeRegs = 32;
-
-template <int HD>
+template <int HD, int MR>
 __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) {
     constexpr int DPL = HD / 64;  // head-dim columns per lane
     const int lane = threadIdx.x & 63;
@@ -597,9 +596,9 @@ __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) 
         ms = base[lane * sstride + HD];
         ls = base[lane * sstride + HD + 1];
     }
-    float v[kMergeRegs][DPL];  // partials past np: clamped, in bounds, unused
+    float v[MR][DPL];  // partials past np: clamped, in bounds, unused
 #pragma unroll
-    for (int j = 0; j < kMergeRegs; ++j)
+    for (int j = 0; j < MR; ++j)
 #pragma unroll
         for (int q = 0; q < DPL; ++q) v[j][q] = base[(int64_t)min(j, np - 1) * sstride + lane + 64 * q];
     float mx = ms;
@@ -611,7 +610,7 @@ __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) 
 #pragma unroll
     for (int q = 0; q < DPL; ++q) acc[q] = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMergeRegs; ++j) {
+    for (int j = 0; j < MR; ++j) {
         if (j < np) {
             const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
 #pragma unroll
@@ -628,7 +627,7 @@ __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) 
                 lsum += w * base[sidx * sstride + HD + 1];
             }
         }
-        const int j0 = c0 == 0 ? kMergeRegs : 0, cnt = min(64, np - c0);
+        const int j0 = c0 == 0 ? MR : 0, cnt = min(64, np - c0);
 #pragma unroll 8
         for (int j = j0; j < cnt; ++j) {
             const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
@@ -732,7 +731,11 @@ static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3((unsigned)((p.B * p.hq * p.gamma + 3) / 4)), dim3(kBlock), 0, s, p);
+    const dim3 mgrid((unsigned)((p.B * p.hq * p.gamma + 3) / 4));
+    if (p.nparts <= 32)
+        hipLaunchKernelGGL((attn_merge_kernel<HD, 32>), mgrid, dim3(kBlock), 0, s, p);
+    else
+        hipLaunchKernelGGL((attn_merge_kernel<HD, 64>), mgrid, dim3(kBlock), 0, s, p);
     return hipGetLastError();
 }
 

@@ -12,7 +12,8 @@ of dim 128, 35 query rows per kv head, SiLU FFN, 7-row block; rows of 5120
 normalised once per row, the O projection in two split-K ranges), its layer
 with a 9216-wide FFN (the down projection in three split-K ranges), the same
 heads with int4-g64 weights everywhere (4-row block), target rows of 5120 on a
-narrow drafter (long-row block init, context projection and LM head), and 16 ragged sequences
+narrow drafter (long-row block init, context projection and LM head), one 2100-key
+sequence whose attention merges 64 partials per row, and 16 ragged sequences
 (plus 3 and 20 sequences: 21 and 140 block rows on the matrix-core path).
 """
 
@@ -49,6 +50,10 @@ WIDE4_B1 = scaled(WIDE4_SMALL, name="wide4_b1", B=1)
 # LDS budget, split-K context projection over 2 x 5120 columns, long-row LM head
 WIDE_LONGROW = scaled(WIDE, name="wide_longrow", H=5120, m=2, d=256, hq=4, hkv=2, hd=64, nl=1, F=512, V=1000,
                       L=64, B=2)
+# one long sequence on one kv head with 35 query rows (the row-split attention): 2100 keys
+# in 64 key-range partials per row, the merge's wide single-batch path
+ROWS_SPLIT64 = scaled(WIDE, name="rows_split64", H=256, m=2, d=640, hq=5, hkv=1, hd=128, nl=1, F=512, V=1000,
+                      L=2100, B=1)
 # 16 ragged sequences (batched workload), narrow layers
 BATCHED_SMALL = scaled(BATCHED, name="batched_small", H=256, m=2, d=256, hq=4, hkv=2, hd=64, nl=2, F=512,
                        V=1000, L=40, L_max=200, B=16)
@@ -73,6 +78,7 @@ CASES = {
     "wide_heads": (WIDE_HEADS, [300, 157]),
     "wide_ffn": (WIDE_FFN, [100]),
     "wide_longrow": (WIDE_LONGROW, [64, 41]),
+    "rows_split64": (ROWS_SPLIT64, [2100]),
     "wide4_small": (WIDE4_SMALL, [300, 211]),
     "wide4_b1": (WIDE4_B1, [257]),
     "batched_small": (BATCHED_SMALL, [int(x) for x in gen.context_lengths(BATCHED_SMALL)]),
