@@ -298,6 +298,22 @@ size_t ctx_project_skinny_bytes(const dflash_dims& d, int n) {
     return (size_t)ns * n * d.d * 4;
 }
 size_t kv_append_norm_bytes(const dflash_dims& d, int n) { return align_up((size_t)d.nl * n * d.d * 2); }
+// the GEMV append of up to 8 pre-normalised rows over K ranges beyond one pass of the
+// 8-row kernel's normal LDS budget splits K (two ranges at width 5120: half the staging,
+// twice the resident workgroups); its fp32 partials [nl][nsplit][n][2 hkv hd] follow the
+// normalised rows in the workspace
+int kv_append_gemv_split(const dflash_dims& d, int n, int* kslice) {
+    int ns = 1, ks = d.d;
+    if (d.wdtype == DFLASH_BF16 && prenorm(d) && n >= 1 && n <= 8 && d.d > kStageBytes / (8 * 2))
+        gemv_split(d, d.d, n, &ns, &ks);
+    *kslice = ks;
+    return ns;
+}
+size_t kv_append_split_bytes(const dflash_dims& d, int n) {
+    int ks = 0;
+    const int ns = kv_append_gemv_split(d, n, &ks);
+    return kv_append_norm_bytes(d, n) + (ns > 1 ? align_up((size_t)d.nl * ns * n * 2 * d.hkv * d.hd * 4) : 0);
+}
 size_t kv_append_skinny_bytes(const dflash_dims& d, int n) {
     if (!ctx_skinny_rows(d, n) || d.d % kSkinnyK || d.nl < 1) return 0;
     const int N = 2 * d.hkv * d.hd;
@@ -374,6 +390,8 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     if (w.total < ctx_need) w.total = ctx_need;
     if (w.total < kv_need) w.total = kv_need;
     if (prenorm(d) && w.total < kv_append_norm_bytes(d, nr)) w.total = kv_append_norm_bytes(d, nr);
+    if (prenorm(d) && w.total < kv_append_split_bytes(d, nr < 8 ? nr : 8))
+        w.total = kv_append_split_bytes(d, nr < 8 ? nr : 8);
     char* c = static_cast<char*>(base);
     if (c) {
         w.hd = reinterpret_cast<float*>(c + o_hd);
@@ -1084,7 +1102,45 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
     p.cap = kv->cap;
     p.kv_f32 = kv->dtype == DFLASH_F32;
     p.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
-    DFL_HIP(gemv_rows(wtype_of(d.wdtype), pro, EPI_KV, p, n, s, d.nl, 32));
+    int split_ks = 0;
+    const int split_ns = pro == PRO_PLAIN ? kv_append_gemv_split(d, n, &split_ks) : 1;
+    if (split_ns > 1 && !p.kv_f32 && ws_bytes >= kv_append_split_bytes(d, n)) {
+        // K ranges write fp32 partials (one set per layer), then one reduce over all layers
+        // adds them in split order and scatters the rows into the caches
+        float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + kv_append_norm_bytes(d, n));
+        GemvParams q = p;
+        q.ksplit = split_ns;
+        q.kslice = split_ks;
+        q.max_wgs = p.max_wgs / split_ns > 0 ? p.max_wgs / split_ns : 1;
+        q.out = part;
+        q.out_ld = p.N;
+        q.split_stride = (int64_t)n * p.N;  // layer y, range z at (y * split_ns + z) * split_stride
+        q.round_out = 0;
+        q.out_bf16 = 0;
+        q.vt = nullptr;
+        DFL_HIP(gemv_rows(wtype_of(d.wdtype), PRO_PLAIN, EPI_STORE, q, n, s, d.nl));
+        SkinnyParams r;
+        std::memset(&r, 0, sizeof(r));
+        r.M = n;
+        r.N = p.N;
+        r.layers = d.nl;
+        r.nsplit = split_ns;
+        r.part = part;
+        r.kcache = static_cast<uint16_t*>(kv->k);
+        r.vcache = static_cast<uint16_t*>(kv->v);
+        r.len = kv->len;
+        r.row_offsets = row_offsets;
+        r.counts = counts;
+        r.row_base = 0;
+        r.B = kv->B;
+        r.cap = kv->cap;
+        r.hkv = d.hkv;
+        r.hd = d.hd;
+        r.layer_stride = p.layer_stride;
+        DFL_HIP(launch_split_reduce(SK_KV, r, s));
+    } else {
+        DFL_HIP(gemv_rows(wtype_of(d.wdtype), pro, EPI_KV, p, n, s, d.nl, 32));
+    }
     DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
     g_invocations++;
     return DFLASH_OK;

@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
                             o[(int64_t)m * p.out_ld + n] = (uint16_t)f32_to_bf16_bits(y);
                         }
                     } else {
-                        float* o = p.out + (int64_t)blockIdx.z * p.split_stride;
+                        float* o = p.out + ((int64_t)layer * gridDim.z + blockIdx.z) * p.split_stride;
                         o[(int64_t)m * p.out_ld + n] = p.round_out ? round_bf16(y) : y;
                     }
                 } else if constexpr (EPI == EPI_RESID) {

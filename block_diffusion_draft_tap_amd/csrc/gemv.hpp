@@ -49,6 +49,7 @@ struct GemvParams {
     int M;               // active activation rows (<= MAXM)
     int rpw;             // weight rows per wavefront (1, 2 or 4; even for EPI_GATED)
     int ksplit;          // K ranges (grid.z); each writes its partial sums to out + z*split_stride
+                         // (EPI_STORE fp32 over several layers: out + (y*ksplit + z)*split_stride)
     int kslice;          // K elements per range (multiple of 32)
     int64_t split_stride;
     int max_wgs;         // cap on workgroups; row tiles beyond it are looped over (0 = one per tile)

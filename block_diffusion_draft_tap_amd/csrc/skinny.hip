@@ -632,7 +632,9 @@ hipError_t launch_skinny(int epi, const SkinnyParams& p, hipStream_t s) {
 }
 
 hipError_t launch_split_reduce(int epi, const SkinnyParams& p, hipStream_t s) {
-    if (p.M < 1 || p.N <= 0 || (p.N % 4) || p.nsplit < 1 || !p.part || !p.out) return hipErrorInvalidValue;
+    if (p.M < 1 || p.N <= 0 || (p.N % 4) || p.nsplit < 1 || !p.part) return hipErrorInvalidValue;
+    if (epi == SK_KV ? (!p.kcache || !p.vcache || p.layers < 1 || p.layers > kMaxLayers) : !p.out)
+        return hipErrorInvalidValue;
     const int64_t blocks = ((int64_t)p.M * p.N / 4 + kBlock - 1) / kBlock;
     (void)hipGetLastError();  // report only this launch's status
     if (epi == SK_RESID)
@@ -641,6 +643,9 @@ hipError_t launch_split_reduce(int epi, const SkinnyParams& p, hipStream_t s) {
         hipLaunchKernelGGL((skinny_reduce_kernel<SK_GATED>), dim3((unsigned)blocks, 1), dim3(kBlock), 0, s, p);
     else if (epi == SK_STORE)
         hipLaunchKernelGGL((skinny_reduce_kernel<SK_STORE>), dim3((unsigned)blocks, 1), dim3(kBlock), 0, s, p);
+    else if (epi == SK_KV)
+        hipLaunchKernelGGL((skinny_reduce_kernel<SK_KV>), dim3((unsigned)blocks, (unsigned)p.layers), dim3(kBlock), 0,
+                           s, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

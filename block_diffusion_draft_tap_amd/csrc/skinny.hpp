@@ -76,10 +76,11 @@ void skinny_split(int epi, int N, int K, int layers, int* nsplit, int* kslice);
 // for SK_PARTIAL)
 hipError_t launch_skinny(int epi, const SkinnyParams& p, hipStream_t s);
 
-// The split-K sum and epilogue alone (SK_STORE / SK_RESID / SK_GATED, one layer):
-// adds the nsplit fp32 partials part [nsplit][M][N] in split order and applies the
-// epilogue (SK_GATED: N = F outputs from partials [nsplit][M][2F] of the gate and up
-// rows); used for partials written by other kernels (N a multiple of 4)
+// The split-K sum and epilogue alone (SK_STORE / SK_RESID / SK_GATED, one layer; SK_KV,
+// p.layers layers of partials [layers][nsplit][M][N] into bf16 caches): adds the nsplit
+// fp32 partials part [nsplit][M][N] in split order and applies the epilogue (SK_GATED:
+// N = F outputs from partials [nsplit][M][2F] of the gate and up rows); used for
+// partials written by other kernels (N a multiple of 4)
 hipError_t launch_split_reduce(int epi, const SkinnyParams& p, hipStream_t s);
 
 // The residual split-K sum fused with the next RMSNorm: for each of the M rows,
