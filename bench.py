@@ -191,6 +191,8 @@ def bench_prefill(d, dev, args):
     taps = [rnd((n, d.H), 1.0) for _ in range(d.m)]
     h = torch.empty(n, d.d, dtype=torch.float32, device=dev)
     offs = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32, device=dev)
+    # room for every layer's bf16 normalised rows: the K/V GEMM reads plain bf16 tiles
+    kws = dfa.kv_prefill_workspace(d, n) if d.wdtype == "bf16" else ws
     flops_proj = 2.0 * n * d.m * d.H * d.d
     flops_kv = 2.0 * n * d.d * 2 * d.hkv * d.hd * d.nl
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -202,7 +204,7 @@ def bench_prefill(d, dev, args):
         ev[0].record()
         bd.check(dfa.dflash_context_project(dm, taps, h, ws), "context_project")
         ev[1].record()
-        bd.check(dfa.dflash_ctx_kv_append(dm, h, offs, None, kv, ws), "append")
+        bd.check(dfa.dflash_ctx_kv_append(dm, h, offs, None, kv, kws), "append")
         ev[2].record()
         torch.cuda.synchronize()
         if r > 0:  # the first pass is the warm-up
@@ -220,7 +222,8 @@ def bench_prefill(d, dev, args):
         "higher_is_better": True,
         "dtype": "bf16" if d.wdtype == "bf16" else d.wdtype,
         "data": "synthetic (weights and taps drawn on the device)",
-        "config": {"workload": describe(d, lengths), "rows": n},
+        "config": {"workload": describe(d, lengths), "rows": n,
+                   "kv_workspace_bytes": int(kws.numel())},
         "projection": {"ms": round(pm, 3), "tflops": round(flops_proj / (pm / 1e3) / 1e12, 2),
                        "flops": flops_proj},
         "kv": {"ms": round(km, 3), "tflops": round(flops_kv / (km / 1e3) / 1e12, 2), "flops": flops_kv},

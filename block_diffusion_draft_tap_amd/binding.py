@@ -25,7 +25,7 @@ DFLASH_ACT_GELU_TANH, DFLASH_ACT_SILU = 0, 1
 EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "dflash_invocations",
            "dflash_context_project", "dflash_ctx_kv_append", "dflash_draft_layer", "dflash_draft_forward",
            "dflash_lm_head_argmax", "dflash_lm_head_workspace_bytes", "dflash_verify_greedy",
-           "dflash_verify_workspace_bytes", "dflash_trace_head_stamps",
+           "dflash_verify_workspace_bytes", "dflash_kv_prefill_workspace_bytes", "dflash_trace_head_stamps",
            "dflash_lm_head_workgroups", "dflash_wall_clock_hz"]
 
 
@@ -70,6 +70,8 @@ def _load():
     P, I32, SZ, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
     lib.dflash_workspace_bytes.argtypes = [P(dflash_dims), I32, I32]
     lib.dflash_workspace_bytes.restype = SZ
+    lib.dflash_kv_prefill_workspace_bytes.argtypes = [P(dflash_dims), I32]
+    lib.dflash_kv_prefill_workspace_bytes.restype = SZ
     lib.dflash_query.argtypes = [P(dflash_dims)]
     lib.dflash_query.restype = ctypes.c_int
     lib.dflash_status_string.argtypes = [ctypes.c_int]
@@ -320,6 +322,15 @@ def dflash_lm_head_argmax(weight, y, ids, ws, max_logit=None, stream=None):
     ydt = DFLASH_F32 if y.dtype == torch.float32 else DFLASH_BF16
     return lib.dflash_lm_head_argmax(ctypes.byref(cw), _ptr(y), ydt, y.shape[0], _ptr(ids), _ptr(max_logit),
                                      _ptr(ws), ws.numel(), _stream(stream))
+
+
+def kv_prefill_workspace(dims, n, device="cuda"):
+    """Workspace with which a K/V append of n >= 64 rows stages every layer's
+    normalised rows as bf16 before its matrix-core GEMM."""
+    nb = lib.dflash_kv_prefill_workspace_bytes(ctypes.byref(make_dims(dims)), n)
+    if nb == 0:
+        raise DflashError("invalid dims or row count for a prefill workspace")
+    return torch.empty(nb, dtype=torch.uint8, device=device)
 
 
 def lm_head_workspace(V, M, device="cuda"):

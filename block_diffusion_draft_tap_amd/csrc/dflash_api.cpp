@@ -1023,6 +1023,51 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
         g_invocations++;
         return DFLASH_OK;
     }
+    if (n >= DFL_GEMM_MIN_ROWS && d.wdtype == DFLASH_BF16 && d.d % 64 == 0 && d.d <= kNormMaxK && ws &&
+        aligned16(ws) && aligned16(h_ctx) && ws_bytes >= kv_append_norm_bytes(d, n)) {
+        // prefill with room for every layer's normalised rows: bf16(RMSNorm(h_ctx; attn_norm_i))
+        // into ws once (grid.y = layer), then every layer's [K | V] = those rows [W_K | W_V]^T as
+        // one matrix-core GEMM over all layers (grid.z = layer) on plain bf16 A tiles
+        uint16_t* an = static_cast<uint16_t*>(ws);
+        NormRowsParams q;
+        std::memset(&q, 0, sizeof(q));
+        q.x = h_ctx;
+        q.x_ld = d.d;
+        q.rows = n;
+        q.K = d.d;
+        q.layers = d.nl;
+        q.eps = d.eps;
+        for (int i = 0; i < d.nl; ++i) q.gain[i] = M->layers[i].attn_norm;
+        q.dst = an;
+        q.dst_ld = d.d;
+        q.dst_layer_stride = (int64_t)n * d.d;
+        DFL_HIP(launch_norm_rows(q, s));
+        GemmParams g;
+        std::memset(&g, 0, sizeof(g));
+        g.M = n;
+        g.N = 2 * d.hkv * d.hd;
+        g.K = d.d;
+        g.a[0] = an;
+        g.a_ld = d.d;
+        g.a_layer_stride = (int64_t)n * d.d;
+        g.seg_k = d.d;
+        for (int i = 0; i < d.nl; ++i) g.b[i] = static_cast<const uint16_t*>(M->layers[i].w_qkv.data);
+        g.b_row0 = (int64_t)d.hq * d.hd;  // the K and V rows of the fused QKV matrix
+        g.kcache = kv->k;
+        g.vcache = kv->v;
+        g.len = kv->len;
+        g.row_offsets = row_offsets;
+        g.counts = counts;
+        g.B = kv->B;
+        g.hkv = d.hkv;
+        g.hd = d.hd;
+        g.cap = kv->cap;
+        g.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
+        DFL_HIP(launch_gemm(GEMM_A_TAPS, GEMM_EPI_KV, g, d.nl, s));
+        DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
+        g_invocations++;
+        return DFLASH_OK;
+    }
     if (n >= DFL_GEMM_MIN_ROWS && d.wdtype == DFLASH_BF16 && d.d % 64 == 0 && ws && aligned16(ws) &&
         ws_bytes >= (size_t)n * 4) {
         // prefill: per-row RMS factors into ws, then every layer's [K | V] = bf16(N) [W_K | W_V]^T
@@ -1267,6 +1312,11 @@ int dflash_lm_head_argmax(const dflash_weight* E_out, const void* y, int32_t y_d
                     static_cast<hipStream_t>(stream)));
     g_invocations++;
     return DFLASH_OK;
+}
+
+size_t dflash_kv_prefill_workspace_bytes(const dflash_dims* dims, int32_t n) {
+    if (check_dims(dims) == DFLASH_EINVAL || n <= 0) return 0;
+    return kv_append_norm_bytes(*dims, n);
 }
 
 size_t dflash_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V) {

@@ -15,10 +15,11 @@
 //   D[4 (l / 16) + e][l % 16]                               (e < 4),
 // where B[k][n] is weight row n, so both operands are read as 16-byte rows.
 //
-// A operands: tap segments (the concatenation of the tapped hidden states,
-// one pointer per tap) or fp32 rows scaled by a per-row RMS factor and a
-// per-column gain and rounded to bf16 while they are staged. Epilogues: fp32
-// store, or the K/V cache scatter of the context append.
+// A operands: bf16 segments (the concatenation of the tapped hidden states,
+// one pointer per tap; or each layer's pre-normalised context rows, one set per
+// grid.z) or fp32 rows scaled by a per-row RMS factor and a per-column gain and
+// rounded to bf16 while they are staged. Epilogues: fp32 store, or the K/V
+// cache scatter of the context append.
 #include "common.hpp"
 #include "gemm.hpp"
 
@@ -80,14 +81,15 @@ template <>
 struct AStage<GEMM_A_NORM> { float4 lo[kAC], hi[kAC]; float r[kAC]; };
 
 // tap segment holding columns [k0, k0 + 64): a uniform choice (segments are
-// multiples of 64), made with compares so the pointer array stays in registers
+// multiples of 64), made with compares so the pointer array stays in registers;
+// a launch over layers (grid.z) reads each layer's own rows, a_layer_stride apart
 __device__ __forceinline__ const uint16_t* tap_base(const GemmParams& p, int k0) {
     const int j = k0 / p.seg_k;
     const uint16_t* a = p.a[0];
 #pragma unroll
     for (int q = 1; q < kMaxTaps; ++q)
         if (j == q) a = p.a[q];
-    return a + (k0 - j * p.seg_k);
+    return a + (int64_t)blockIdx.z * p.a_layer_stride + (k0 - j * p.seg_k);
 }
 
 template <int AMODE>
@@ -351,6 +353,7 @@ hipError_t launch_gemm(int amode, int epi, const GemmParams& p, int layers, hipS
     if (amode == GEMM_A_TAPS && (p.seg_k <= 0 || (p.seg_k % kBK) || p.K > kMaxTaps * p.seg_k))
         return hipErrorInvalidValue;
     if (amode == GEMM_A_TAPS && epi == GEMM_EPI_F32) return launch_t<GEMM_A_TAPS, GEMM_EPI_F32>(p, layers, s);
+    if (amode == GEMM_A_TAPS && epi == GEMM_EPI_KV) return launch_t<GEMM_A_TAPS, GEMM_EPI_KV>(p, layers, s);
     if (amode == GEMM_A_NORM && epi == GEMM_EPI_KV) return launch_t<GEMM_A_NORM, GEMM_EPI_KV>(p, layers, s);
     return hipErrorInvalidValue;
 }

@@ -17,9 +17,11 @@ enum { GEMM_EPI_F32 = 0, GEMM_EPI_KV = 1 };
 struct GemmParams {
     int M, N, K;  // K a multiple of 64
     // GEMM_A_TAPS: bf16 rows split along K into segments of seg_k columns
-    // (a multiple of 64); segment j starts at a[j], row stride a_ld elements
+    // (a multiple of 64); segment j starts at a[j] + layer * a_layer_stride
+    // (layer = grid.z), row stride a_ld elements
     const uint16_t* a[kMaxTaps];
     int64_t a_ld;
+    int64_t a_layer_stride;
     int seg_k;
     // GEMM_A_NORM: A[m, k] = bf16((x[m, k] * rinv[m]) * gain[k]) from fp32 rows
     // x (row stride a_ld); gain per layer (grid.z)

@@ -218,9 +218,18 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
  * matrix cores, all layers in one launch (each layer's normalised rows and
  * split-K partial sums in ws, B*(gamma+1) >= n); n >= 64 rows otherwise run
  * as one matrix-core GEMM over all layers (per-row RMS factors in ws, at
- * least 4n bytes; B*cap rows always fit). Everything else runs as GEMVs. */
+ * least 4n bytes; B*cap rows always fit). With a workspace of at least
+ * dflash_kv_prefill_workspace_bytes(dims, n) bytes and h_ctx 16-byte aligned,
+ * that GEMM first writes every layer's bf16 normalised rows into ws and then
+ * reads them as plain bf16 tiles (the same values, fewer bytes per tile).
+ * Everything else runs as GEMVs. */
 int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, const int32_t* row_offsets,
                          const int32_t* counts, const dflash_kv* kv, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes with which dflash_ctx_kv_append of n >= 64 rows stages
+ * every layer's normalised rows as bf16 before its matrix-core GEMM
+ * (layers * n * d * 2, rounded up to 256); 0 for invalid dims or n <= 0. */
+size_t dflash_kv_prefill_workspace_bytes(const dflash_dims* dims, int32_t n);
 
 /* One drafter layer on the block (page 3, #layer, Eq 3), in place:
  *   n = RMSNorm(H; attn_norm), Q/K_b/V_b = n W^T,

@@ -187,6 +187,44 @@ def test_projection_paths_agree(name):
         assert err <= t
 
 
+@pytest.mark.parametrize("name", ["gqa_bf16", "default", "wide_heads", "batched_small", "rows35_many"])
+def test_kv_prefill_staged(name):
+    """The matrix-core K/V prefill both ways: with a workspace of only the
+    per-row RMS factors (A normalised while it is staged) and with room for
+    every layer's bf16 normalised rows (A staged as plain bf16 tiles). Each
+    against the oracle's K/V, lengths advanced by every row."""
+    s = get(name)
+    d = s.dims
+    n = sum(s.lengths)
+    assert n >= 64 and d.wdtype == "bf16"
+    big = dfa.kv_prefill_workspace(d, n)
+    assert big.numel() >= d.nl * n * d.d * 2
+    small = torch.empty(((4 * n + 255) // 256) * 256, dtype=torch.uint8, device="cuda")
+    assert small.numel() < big.numel()
+    t = tol(d)
+    kvs = {}
+    for label, ws in (("rinv", small), ("staged", big)):
+        kv2 = dfa.KVCache(d, s.B, s.cap)
+        bd.check(dfa.dflash_ctx_kv_append(s.dm, s.h_ctx, s.offs_d, None, kv2, ws), f"append {label}")
+        torch.cuda.synchronize()
+        assert kv2.len.cpu().tolist() == s.lengths
+        worst = 0.0
+        for i in range(d.nl):
+            for b, L in enumerate(s.lengths):
+                ek = rel_err(kv2.k[i, b, :, :L].permute(1, 0, 2), s.ctx.k[i][b])
+                ev = rel_err(kv2.v[i, b, :, :, :L].permute(2, 0, 1), s.ctx.v[i][b])
+                worst = max(worst, ek, ev)
+                assert ek <= t and ev <= t, (label, i, b, ek, ev)
+        log(f"[{name}] K/V prefill ({label}, ws {ws.numel()} B): worst rel err {worst:.3e}")
+        kvs[label] = kv2
+    # the two stagings round the same products of the same normalised values
+    for i in range(d.nl):
+        for b, L in enumerate(s.lengths):
+            a = kvs["rinv"].k[i, b, :, :L].float()
+            c = kvs["staged"].k[i, b, :, :L].float()
+            assert float((a - c).abs().max()) <= t * float(a.abs().max()), (i, b)
+
+
 @pytest.mark.parametrize("name", NAMES)
 def test_draft_layer(name):
     s = get(name)
