@@ -1026,8 +1026,9 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
     if (n >= DFL_GEMM_MIN_ROWS && d.wdtype == DFLASH_BF16 && d.d % 64 == 0 && d.d <= kNormMaxK && ws &&
         aligned16(ws) && aligned16(h_ctx) && ws_bytes >= kv_append_norm_bytes(d, n)) {
         // prefill with room for every layer's normalised rows: bf16(RMSNorm(h_ctx; attn_norm_i))
-        // into ws once (grid.y = layer), then every layer's [K | V] = those rows [W_K | W_V]^T as
-        // one matrix-core GEMM over all layers (grid.z = layer) on plain bf16 A tiles
+        // into ws (each fp32 row read once for all layers), then every layer's [K | V] = those
+        // rows [W_K | W_V]^T as one matrix-core GEMM over all layers (grid.z = layer) on plain
+        // bf16 A tiles
         uint16_t* an = static_cast<uint16_t*>(ws);
         NormRowsParams q;
         std::memset(&q, 0, sizeof(q));
@@ -1041,6 +1042,7 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
         q.dst = an;
         q.dst_ld = d.d;
         q.dst_layer_stride = (int64_t)n * d.d;
+        q.all_layers = 1;
         DFL_HIP(launch_norm_rows(q, s));
         GemmParams g;
         std::memset(&g, 0, sizeof(g));

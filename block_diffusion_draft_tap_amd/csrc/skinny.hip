@@ -443,14 +443,11 @@ __global__ __launch_bounds__(kBlock) void skinny_reduce_kernel(const SkinnyParam
 }
 
 // one wavefront per row: the row and its sum of squares in registers, then the
-// scaled row rounded to bf16; grid.y = layer (gain)
+// scaled row rounded to bf16; grid.y = layer (gain), or every layer in turn from
+// the same registers when all_layers is set
 __global__ __launch_bounds__(kBlock) void norm_rows_kernel(const NormRowsParams p) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63, z = blockIdx.y;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (row >= p.rows) return;
-    const void* gain = p.gain[0];
-#pragma unroll
-    for (int q = 1; q < kMaxLayers; ++q)
-        if (z == q) gain = p.gain[q];
     constexpr int UM = kNormMaxK / 512;
     const float* src = p.x + (int64_t)row * p.x_ld;
     float v[UM][8];
@@ -472,19 +469,26 @@ __global__ __launch_bounds__(kBlock) void norm_rows_kernel(const NormRowsParams 
     }
     ss = wave_sum(ss);
     const float r = 1.0f / sqrtf(ss / (float)p.K + p.eps);
-    uint16_t* o = p.dst + (int64_t)z * p.dst_layer_stride + (int64_t)row * p.dst_ld;
+    const int z0 = p.all_layers ? 0 : (int)blockIdx.y, z1 = p.all_layers ? p.layers : z0 + 1;
+    for (int z = z0; z < z1; ++z) {
+        const void* gain = p.gain[0];
 #pragma unroll
-    for (int u = 0; u < UM; ++u) {
-        const int k = lane * 8 + u * 512;
-        if (k < p.K) {
-            float g[8];
-            load_gain8(gain, p.gain_f32, k, g);
-            uint4 q;
-            q.x = pack_bf16x2(v[u][0] * r * g[0], v[u][1] * r * g[1]);
-            q.y = pack_bf16x2(v[u][2] * r * g[2], v[u][3] * r * g[3]);
-            q.z = pack_bf16x2(v[u][4] * r * g[4], v[u][5] * r * g[5]);
-            q.w = pack_bf16x2(v[u][6] * r * g[6], v[u][7] * r * g[7]);
-            *reinterpret_cast<uint4*>(o + k) = q;
+        for (int q = 1; q < kMaxLayers; ++q)
+            if (z == q) gain = p.gain[q];
+        uint16_t* o = p.dst + (int64_t)z * p.dst_layer_stride + (int64_t)row * p.dst_ld;
+#pragma unroll
+        for (int u = 0; u < UM; ++u) {
+            const int k = lane * 8 + u * 512;
+            if (k < p.K) {
+                float g[8];
+                load_gain8(gain, p.gain_f32, k, g);
+                uint4 q;
+                q.x = pack_bf16x2(v[u][0] * r * g[0], v[u][1] * r * g[1]);
+                q.y = pack_bf16x2(v[u][2] * r * g[2], v[u][3] * r * g[3]);
+                q.z = pack_bf16x2(v[u][4] * r * g[4], v[u][5] * r * g[5]);
+                q.w = pack_bf16x2(v[u][6] * r * g[6], v[u][7] * r * g[7]);
+                *reinterpret_cast<uint4*>(o + k) = q;
+            }
         }
     }
 }
@@ -667,7 +671,8 @@ hipError_t launch_norm_rows(const NormRowsParams& p, hipStream_t s) {
         p.layers < 1 || p.layers > kMaxLayers)
         return hipErrorInvalidValue;
     (void)hipGetLastError();  // report only this launch's status
-    hipLaunchKernelGGL(norm_rows_kernel, dim3((unsigned)((p.rows + 3) / 4), p.layers), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL(norm_rows_kernel, dim3((unsigned)((p.rows + 3) / 4), p.all_layers ? 1 : p.layers),
+                       dim3(kBlock), 0, s, p);
     return hipGetLastError();
 }
 

@@ -99,6 +99,9 @@ struct NormRowsParams {
     const void* gain[kMaxLayers];
     uint16_t* dst;
     int64_t dst_ld, dst_layer_stride;
+    // 0: one layer per grid.y (more workgroups for a few rows); 1: each row read
+    // once and written for every layer (long prefills)
+    int all_layers;
 };
 hipError_t launch_norm_rows(const NormRowsParams& p, hipStream_t s);
 
