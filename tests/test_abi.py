@@ -65,6 +65,21 @@ def test_query_rejects_inconsistent_and_unsupported_dims():
     assert bd.lib.dflash_query(None) == bd.DFLASH_EINVAL
 
 
+def test_kv_prefill_workspace_size():
+    # every layer's normalised rows as bf16, rounded up to 256 bytes; 0 when invalid
+    f = bd.lib.dflash_kv_prefill_workspace_bytes
+    for cfg, n in ((DEFAULT, 2048), (BATCHED, 192011), (scaled(DEFAULT, nl=1, hq=4, hkv=4, d=512), 65)):
+        exact = cfg.nl * n * cfg.d * 2
+        got = f(ctypes.byref(bd.make_dims(cfg)), n)
+        assert got >= exact and got - exact < 256 and got % 256 == 0, (cfg.name, n, got)
+    assert f(ctypes.byref(bd.make_dims(DEFAULT)), 0) == 0
+    assert f(ctypes.byref(bd.make_dims(DEFAULT)), -5) == 0
+    assert f(None, 100) == 0
+    bad = bd.make_dims(DEFAULT)
+    bad.d = 1000                   # d != hq * hd
+    assert f(ctypes.byref(bad), 100) == 0
+
+
 def test_kill_switch_declines(monkeypatch):
     monkeypatch.setenv("DFLASH_DISABLE", "1")
     assert bd.dflash_query(DEFAULT) == bd.DFLASH_DECLINED
