@@ -283,6 +283,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 
     // ---- epilogue: lane holds rows 4*grp + e of each 16 x 16 product, column col
     const int kvw = p.hkv * p.hd;
+    // sequence b of the lane's current row, its rows [seq_lo, seq_hi), appended-row count
+    // and cache length: rows grow along (i, e), so b only advances and these reload only
+    // when a row passes seq_hi
+    int b = 0, seq_lo = 0, seq_hi = -1, cnt = 0, len_b = 0;  // rows are >= 0: the first row loads
 #pragma unroll
     for (int i = 0; i < kMT; ++i) {
 #pragma unroll
@@ -297,12 +301,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
                     if (n < p.N) dst[n] = acc[i][j][e];
                 }
             } else {
-                int b = 0;
-                while (b + 1 < p.B && p.row_offsets[b + 1] <= row) ++b;
-                const int rows_b = p.row_offsets[b + 1] - p.row_offsets[b];
-                const int ri = row - p.row_offsets[b];
-                const int cnt = p.counts ? min(p.counts[b], rows_b) : rows_b;
-                const int pos = p.len[b] + ri;
+                if (row >= seq_hi) {
+                    while (b + 1 < p.B && p.row_offsets[b + 1] <= row) ++b;
+                    seq_lo = p.row_offsets[b];
+                    seq_hi = p.row_offsets[b + 1];
+                    const int rows_b = seq_hi - seq_lo;
+                    cnt = p.counts ? min(p.counts[b], rows_b) : rows_b;
+                    len_b = p.len[b];
+                }
+                const int ri = row - seq_lo;
+                const int pos = len_b + ri;
                 if (ri < 0 || ri >= cnt || pos >= p.cap) continue;
 #pragma unroll
                 for (int j = 0; j < kNT; ++j) {
