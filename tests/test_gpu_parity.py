@@ -225,6 +225,47 @@ def test_kv_prefill_staged(name):
             assert float((a - c).abs().max()) <= t * float(a.abs().max()), (i, b)
 
 
+@pytest.mark.parametrize("name", ["gqa_bf16", "batched_small"])
+def test_kv_prefill_two_stages(name):
+    """The matrix-core K/V append at non-zero cache lengths and with counts:
+    first a counted prefix of each sequence (some none, some all of it, the
+    rest a seeded share), then the remaining rows, each call over all
+    sequences' rows. Both stagings; the final cache must hold the oracle's
+    K/V of every row, and the lengths must be the full lengths."""
+    s = get(name)
+    d = s.dims
+    rng = np.random.default_rng(7)
+    L = np.array(s.lengths)
+    c1 = rng.integers(0, L + 1)
+    c1[0], c1[-1] = 0, L[-1]                       # one sequence empty first, one complete first
+    offs = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    rest = [s.h_ctx[offs[b] + c1[b]:offs[b + 1]] for b in range(s.B)]
+    h2 = torch.cat(rest).contiguous()
+    offs2 = torch.from_numpy(np.concatenate([[0], np.cumsum(L - c1)]).astype(np.int32)).cuda()
+    n1, n2 = int(L.sum()), int((L - c1).sum())
+    assert n1 >= 64 and n2 >= 64, (n1, n2)       # both calls take the matrix-core GEMM
+    t = tol(d)
+    for label in ("rinv", "staged"):
+        def ws_for(n):
+            if label == "staged":
+                return dfa.kv_prefill_workspace(d, n)
+            return torch.empty(((4 * n + 255) // 256) * 256, dtype=torch.uint8, device="cuda")
+        kv2 = dfa.KVCache(d, s.B, s.cap)
+        counts = torch.from_numpy(c1.astype(np.int32)).cuda()
+        bd.check(dfa.dflash_ctx_kv_append(s.dm, s.h_ctx, s.offs_d, counts, kv2, ws_for(n1)), f"append 1 {label}")
+        torch.cuda.synchronize()
+        assert kv2.len.cpu().numpy().tolist() == c1.tolist()
+        bd.check(dfa.dflash_ctx_kv_append(s.dm, h2, offs2, None, kv2, ws_for(n2)), f"append 2 {label}")
+        torch.cuda.synchronize()
+        assert kv2.len.cpu().tolist() == s.lengths
+        for i in range(d.nl):
+            for b, Lb in enumerate(s.lengths):
+                ek = rel_err(kv2.k[i, b, :, :Lb].permute(1, 0, 2), s.ctx.k[i][b])
+                ev = rel_err(kv2.v[i, b, :, :, :Lb].permute(2, 0, 1), s.ctx.v[i][b])
+                assert ek <= t and ev <= t, (label, i, b, int(c1[b]), ek, ev)
+        log(f"[{name}] two-stage K/V append ({label}): first counts {c1.tolist()}")
+
+
 @pytest.mark.parametrize("name", NAMES)
 def test_draft_layer(name):
     s = get(name)
