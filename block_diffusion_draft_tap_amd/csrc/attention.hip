@@ -32,6 +32,7 @@ namespace dfl {
 
 constexpr int kTile = 64;   // keys per tile, fp32 kernel
 constexpr int kChunk = 32;  // keys per chunk, MFMA kernel
+static_assert(kChunk == kAttnMaxGamma, "the block's keys form one chunk");
 constexpr int kMaxParts = 256;
 constexpr int kMaxSplit = 64;  // workgroups per (sequence, kv head), MFMA kernel
 constexpr int kMaxRows = 48;   // query rows per kv head, MFMA kernel

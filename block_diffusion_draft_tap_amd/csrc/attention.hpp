@@ -7,6 +7,10 @@
 
 namespace dfl {
 
+// The block's keys (gamma of them) form one 32-key unit of the attention kernels,
+// and the block values travel in one [hd][32] tile per (sequence, kv head).
+constexpr int kAttnMaxGamma = 32;
+
 struct AttnParams {
     const void* qkv;       // [B*gamma][qkv_ld]: Q cols [0, hq hd), K_b cols, then V_b cols
                            // (fp32 with fp32 caches; bf16 with bf16 caches, V_b then in vblk)

@@ -65,7 +65,7 @@ int check_dims(const dflash_dims* d) {
     if (d->wdtype != DFLASH_F32 && d->wdtype != DFLASH_BF16 && d->wdtype != DFLASH_INT4G64) return DFLASH_DECLINED;
     if (d->act != DFLASH_ACT_GELU_TANH && d->act != DFLASH_ACT_SILU) return DFLASH_DECLINED;
     if (d->nl > kMaxLayers || d->m > kMaxTaps) return DFLASH_DECLINED;
-    if (d->gamma + 1 > 64) return DFLASH_DECLINED;
+    if (d->gamma > kAttnMaxGamma) return DFLASH_DECLINED;  // the block's keys form one 32-key unit
     if (d->d > 8192) return DFLASH_DECLINED;  // the row norms hold a row in one workgroup's registers
     if ((d->hq / d->hkv) * d->gamma > attention_max_rows(d->wdtype == DFLASH_F32)) return DFLASH_DECLINED;
     const int q = d->wdtype == DFLASH_INT4G64 ? 64 : 8;

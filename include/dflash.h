@@ -74,7 +74,10 @@ enum { DFLASH_ACT_GELU_TANH = 0, DFLASH_ACT_SILU = 1 };
 /* Drafter geometry. d must equal hq*hd and hq must be a multiple of hkv
  * (query head h reads key/value head h / (hq/hkv)). hd is 64 or 128; d is at
  * most 8192 (wider drafters are DECLINED).
- * gamma = block query rows = drafted tokens (the verify width is gamma+1). */
+ * gamma = block query rows = drafted tokens (the verify width is gamma+1); at
+ * most 32 (the block's keys form one 32-key attention unit), and
+ * (hq/hkv)*gamma query rows per kv head at most 48 (40 for f32 models): larger
+ * blocks are DECLINED. */
 typedef struct {
     int32_t H;       /* target hidden size (tap width and LM-head width)   */
     int32_t m;       /* number of tapped target layers                      */

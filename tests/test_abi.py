@@ -58,6 +58,15 @@ def test_query_rejects_inconsistent_and_unsupported_dims():
     assert bd.lib.dflash_query(ctypes.byref(d)) == bd.DFLASH_DECLINED
     d = bd.make_dims(scaled(DEFAULT, gamma=70))
     assert bd.lib.dflash_query(ctypes.byref(d)) == bd.DFLASH_DECLINED      # verify width > 64
+    # the block's keys form one 32-key attention unit: gamma 32 is served (where a gfx950
+    # device is), 33 is declined for every weight format, MHA or grouped heads alike
+    for wd in ("f32", "bf16", "int4g64"):
+        for hq, hkv in ((8, 8), (8, 1)):
+            ok = bd.make_dims(scaled(DEFAULT, gamma=32, hq=hq, hkv=hkv, wdtype=wd))
+            if hq // hkv * 32 <= 48:
+                assert bd.lib.dflash_query(ctypes.byref(ok)) in (bd.DFLASH_OK, bd.DFLASH_DECLINED)
+            big = bd.make_dims(scaled(DEFAULT, gamma=33, hq=hq, hkv=hkv, wdtype=wd))
+            assert bd.lib.dflash_query(ctypes.byref(big)) == bd.DFLASH_DECLINED, (wd, hq, hkv)
     d = bd.make_dims(DEFAULT)
     d.eps = -1.0
     assert bd.lib.dflash_query(ctypes.byref(d)) == bd.DFLASH_EINVAL

@@ -325,6 +325,118 @@ def test_draft_layer_matches_torch_layer():
     assert rel(got[0], x.numpy()) < 1e-12
 
 
+def _torch_nonretained_layer(dims, w, taps, Hd, layer, faithful=False):
+    """One drafter layer for one sequence by the non-retained branch of page 3
+    (#layer with the context passed in, no cache): Eq 2 from the raw taps, then
+    the layer's own attn_norm applied to BOTH the context and the block, one
+    K/V projection over [context ++ block] rows, SDPA with no mask (grouped
+    query heads), O projection and the gated FFN. Every step is a torch float64
+    library call; nothing here reuses the oracle. With faithful, values are cast
+    to bfloat16 and back at the rounding points the GPU contract names."""
+    t = lambda a: torch.from_numpy(np.array(a, dtype=np.float64))
+    r = (lambda x: x.to(torch.bfloat16).to(torch.float64)) if faithful else (lambda x: x)
+    F = torch.nn.functional
+    W = {n: t(O.dense(w[f"bb.{layer}.{n}"])) for n in
+         ("q", "k", "v", "o", "gate", "up", "down", "attn_norm", "ff_norm")}
+    # Eq 2: concatenate the taps on the feature axis, project, normalise with ctx_norm
+    X = torch.cat([t(O.dense(a)) for a in taps], dim=1)
+    Hc = F.rms_norm(X @ t(O.dense(w["W_c"])).T, (dims.d,), t(O.dense(w["ctx_norm"])), eps=dims.eps)
+    x = t(Hd)
+    G, Lc = x.shape[0], Hc.shape[0]
+    # the same norm and the same K/V weights for the context rows and the block rows
+    rows = torch.cat([Hc, x], dim=0)
+    n_all = r(F.rms_norm(rows, (dims.d,), W["attn_norm"], eps=dims.eps))
+    k = r(n_all @ W["k"].T).reshape(Lc + G, dims.hkv, dims.hd).transpose(0, 1)
+    v = r(n_all @ W["v"].T).reshape(Lc + G, dims.hkv, dims.hd).transpose(0, 1)
+    q = r(n_all[Lc:] @ W["q"].T).reshape(G, dims.hq, dims.hd).transpose(0, 1)
+    a = F.scaled_dot_product_attention(q, k, v, is_causal=False, enable_gqa=True)
+    x = x + r(a.transpose(0, 1).reshape(G, -1)) @ W["o"].T
+    n2 = r(F.rms_norm(x, (dims.d,), W["ff_norm"], eps=dims.eps))
+    act = F.silu(n2 @ W["gate"].T) if dims.act == "silu" else F.gelu(n2 @ W["gate"].T, approximate="tanh")
+    return (x + r(act * (n2 @ W["up"].T)) @ W["down"].T).numpy()
+
+
+# a grouped-query SiLU layer whose K/V width (hkv * hd = 64) differs from the drafter
+# width (d = 256), and a square multi-head GELU layer (hkv * hd = d) on which a
+# transposed K/V weight still has the right shape
+EQ3_GQA = dict(H=96, m=3, d=256, hq=4, hkv=1, hd=64, F=192, act="silu", gamma=3, V=64)
+EQ3_MHA = dict(H=96, m=2, d=128, hq=2, hkv=2, hd=64, F=160, gamma=4, V=64)
+
+
+def _eq3_case(geom, L=11, seed=21):
+    dims = scaled(TINY, **geom)
+    w = gen.Model(dims, gains="random").materialise()
+    taps = gen.make_taps(dims, 0, L, stream="ctx")
+    Hd = np.random.default_rng(seed).standard_normal((dims.gamma, dims.d))
+    return dims, w, taps, Hd
+
+
+def _oracle_retained_layer(dims, w, taps, Hd, layer, faithful=False):
+    Hc = O.context_project(taps, w["W_c"], w["ctx_norm"], dims.eps)
+    ctx = O.Context(dims.nl, 1, dims.hkv, dims.hd)
+    O.append_context(ctx, w, dims, Hc, [list(range(Hc.shape[0]))], [Hc.shape[0]], faithful)
+    return O.draft_layer(Hd[None], ctx, layer, w, dims, faithful)[0]
+
+
+@pytest.mark.parametrize("geom", [EQ3_GQA, EQ3_MHA], ids=["gqa_silu_nonsquare", "mha_gelu_square"])
+@pytest.mark.parametrize("layer", [0, 1])
+def test_eq3_context_half_against_nonretained_torch_layer(geom, layer):
+    """Eq 3 with the context K/V computed from H_ctx: the oracle's retained
+    path (context_kv into a Context, then draft_layer) equals a torch float64
+    layer that re-projects the context itself from the taps."""
+    dims, w, taps, Hd = _eq3_case(geom)
+    got = _oracle_retained_layer(dims, w, taps, Hd, layer)
+    ref = _torch_nonretained_layer(dims, w, taps, Hd, layer)
+    assert rel(got, ref) < 1e-12
+    # the faithful (bf16-rounding) mode against the same layer with the casts in torch.
+    # The roundings move the output by 4e-5..1.2e-4 from the fp64 layer; the two
+    # faithful computations agree far inside that (a summation order that flips one
+    # rare rounding moves a single element by one bf16 ulp, well under 1e-5 here)
+    got_f = _oracle_retained_layer(dims, w, taps, Hd, layer, faithful=True)
+    ref_f = _torch_nonretained_layer(dims, w, taps, Hd, layer, faithful=True)
+    assert rel(got_f, ref_f) < 1e-5 and rel(got_f, ref) > 3e-5
+
+
+def test_eq3_context_half_catches_planted_slips(monkeypatch):
+    """Plausible slips in the context half of Eq 3, planted in copies of
+    context_kv, each fail the non-retained torch pin above."""
+    real = O.context_kv
+
+    def transposed_wk(H_ctx, g_attn, W_k, W_v, hkv, hd, eps, faithful):
+        n = O.rmsnorm(H_ctx, O.dense(g_attn), eps)
+        K = n @ O.dense(W_k)                         # W_K not transposed
+        V = n @ O.dense(W_v).T
+        return K.reshape(len(H_ctx), hkv, hd), V.reshape(len(H_ctx), hkv, hd)
+
+    def swapped_kv(H_ctx, g_attn, W_k, W_v, hkv, hd, eps, faithful):
+        K, V = real(H_ctx, g_attn, W_k, W_v, hkv, hd, eps, faithful)
+        return V, K
+
+    def head_major_reshape(H_ctx, g_attn, W_k, W_v, hkv, hd, eps, faithful):
+        K, V = real(H_ctx, g_attn, W_k, W_v, hkv, hd, eps, faithful)
+        n = len(H_ctx)
+        return (K.reshape(n, hkv * hd).reshape(n, hd, hkv).transpose(0, 2, 1),
+                V.reshape(n, hkv * hd).reshape(n, hd, hkv).transpose(0, 2, 1))
+
+    def block_weights_for_context(H_ctx, g_attn, W_k, W_v, hkv, hd, eps, faithful):
+        # the context projected with the NEXT layer's W_K / W_V (layers 0 and 1 of the case)
+        return real(H_ctx, g_attn, w["bb.1.k"], w["bb.1.v"], hkv, hd, eps, faithful)
+
+    # the square case: every slip keeps valid shapes and must change the values
+    dims, w, taps, Hd = _eq3_case(EQ3_MHA)
+    ref = _torch_nonretained_layer(dims, w, taps, Hd, 0)
+    for slip in (transposed_wk, swapped_kv, head_major_reshape, block_weights_for_context):
+        monkeypatch.setattr(O, "context_kv", slip)
+        bad = _oracle_retained_layer(dims, w, taps, Hd, 0)
+        monkeypatch.setattr(O, "context_kv", real)
+        assert rel(bad, ref) > 1e-4, slip.__name__
+    # the non-square case: the transposed weight cannot even be applied
+    dims, w, taps, Hd = _eq3_case(EQ3_GQA)
+    monkeypatch.setattr(O, "context_kv", transposed_wk)
+    with pytest.raises(ValueError):
+        _oracle_retained_layer(dims, w, taps, Hd, 0)
+
+
 def test_single_key_layer_closed_form():
     """Empty context and a one-row block: attention over the single block key
     returns V_b exactly, so the layer has a closed form."""
