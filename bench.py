@@ -3,7 +3,8 @@
 
 A step is one steady-state speculative round of the whole hot path on one
 batch of synthetic input, inputs resident in HBM:
-  1. context projection of the gamma+1 tapped rows the last verify produced,
+  1. context projection of the gamma+1 tapped rows per sequence the last
+     verify produced,
   2. per-layer context K/V append of the committed rows (counts on device),
   3. drafter forward: block init, every layer, out projection, LM-head argmax,
   4. greedy verify of the drafts against planted target logits,
@@ -13,18 +14,31 @@ torch.cuda.CUDAGraph on the stream the library launches on) and the graphs
 are replayed in a cycle. The metric is draft blocks per second (B blocks per
 step); tokens proposed per second is gamma * B * blocks/s.
 
-The dominant kernel (the LM-head GEMV + argmax epilogue) is timed live inside
-the timed region: each of its workgroups writes the device wall clock at its
-start and end into a per-round buffer (a kernel argument, so graph replays
-write it too); its duration is the first start to the last end, averaged over
-the last timed run of every round.
+The default workload is the largest single-GPU one: 16 sequences of the wide
+bf16 drafter with contexts of 9050-16059 rows (the batched workload).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config default]
+Before the rounds, the whole context of every sequence is prefilled in one
+call per step (projection, then every layer's K/V) and timed: the matrix-core
+figure of the prefill. Taps of the prefilled context are drawn on the device
+(the values do not change the work), except for the one sequence the CPU
+oracle replays, whose taps are the seeded ones; every round input is seeded.
+
+Kernel durations come from the kernels themselves: while the rounds are
+captured, the library's launch tracing is on, so during every replay each
+traced workgroup writes the device wall clock at its start and end into the
+round's stamp buffer. A kernel's duration is its first start to last end; the
+line reports the last timed replay of every round.
+
+The CPU baseline is the oracle (numpy float64) replaying the round of one
+sequence, interleaved with further timed GPU segments in the same minute.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config batched]
 """
 
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,10 +47,14 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from synth import CONFIGS, gen  # noqa: E402
+from synth import CONFIGS, gen, scaled  # noqa: E402
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s (published)
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, GB/s (published)
+MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak (published)
 METRIC = "draft blocks/sec (drafter fwd+verify) at 1 MI355X; % HBM/MFMA roofline"
+NEAR_TIE = 1e-3                   # draft ids are compared where the oracle's top-2 gap is at least this
+FLUSH_BYTES = 1 << 30             # MALL flush between rounds: a 1 GiB write (the MALL holds 256 MB)
+STAMP_ENTRIES = 1 << 20           # per round: room for every traced workgroup's (start, end)
 
 
 def log(msg):
@@ -71,166 +89,226 @@ def describe(d, lengths):
             f"(block {d.gamma + 1}), {ctx}, vocab {d.V}, batch {d.B}")
 
 
+def host_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model,
+            "load_average": [round(x, 2) for x in os.getloadavg()]}
+
+
+def tag(kernel):
+    return re.sub(r"[^a-z0-9]+", "_", kernel.lower()).strip("_")
+
+
 # ----------------------------------------------------------------------------
-# CPU baseline: the oracle, untuned, on a bounded sample of the same rounds
+# CPU baseline: the oracle, untuned, on one sequence of the same rounds
 
 
-def cpu_baseline(d, rounds_inputs, seconds, gpu_ids):
-    from threadpoolctl import threadpool_info
-    from oracle import dflash_oracle as O
+class CpuLeg:
+    """The oracle replaying the round of sequence `b` (seeded taps, the same
+    round inputs and accept schedule as the GPU chain). Setup (the oracle's own
+    prefill of that sequence's context) is untimed; each timed oracle round is
+    context projection + K/V append of the committed rows, the forward, the LM
+    head and verify, then the rollback."""
 
-    faithful = d.wdtype != "f32"
-    w = gen.Model(d).materialise()
-    lengths = gen.context_lengths(d)
-    ctx = O.Context(d.nl, d.B, d.hkv, d.hd)
-    for b in range(d.B):
-        taps = gen.make_taps(d, 0, int(lengths[b]), stream="ctx", seq=b)
+    def __init__(self, d, w, b, L, rounds):
+        from oracle import dflash_oracle as O
+        self.O, self.d, self.w, self.b, self.L, self.rounds = O, d, w, b, L, rounds
+        self.fm = d.wdtype != "f32"
+        self.d1 = scaled(d, B=1)
+        taps = gen.make_taps(d, 0, L, stream="ctx", seq=b)
         Hc = O.context_project(taps, w["W_c"], w["ctx_norm"], d.eps)
-        O.append_context(ctx, w, d, Hc, [[]] * b + [list(range(int(lengths[b])))] + [[]] * (d.B - b - 1),
-                         [0] * b + [int(lengths[b])] + [0] * (d.B - b - 1), faithful)
-    W = d.gamma + 1
-    n_done, agree, compared = 0, 0, 0
-    anchor = gen.make_anchors(d, 0)
-    t0 = time.perf_counter()
-    while True:
-        r = n_done % len(rounds_inputs)
-        counts = rounds_inputs[r]["counts"]
-        for b in range(d.B):
+        self.ctx = O.Context(d.nl, 1, d.hkv, d.hd)
+        O.append_context(self.ctx, w, d, Hc, [list(range(L))], [L], self.fm)
+        self.done = 0
+        self.seconds = 0.0
+        self.checked = []
+        self.anchor = None
+
+    def run(self, seconds):
+        O, d, w, b = self.O, self.d, self.w, self.b
+        W = d.gamma + 1
+        t0 = time.perf_counter()
+        while True:
+            r = self.done % len(self.rounds)
+            rr = self.rounds[r]
             taps = gen.make_taps(d, r * W, W, stream="round", seq=b)
             Hc = O.context_project(taps, w["W_c"], w["ctx_norm"], d.eps)
-            O.append_context(ctx, w, d, Hc, [[]] * b + [list(range(W))] + [[]] * (d.B - b - 1),
-                             [0] * b + [int(counts[b])] + [0] * (d.B - b - 1), faithful)
-        ids, ex = O.draft_forward(w, d, ctx, anchor, faithful, return_all=True)
-        T = gen.plant_target_logits(d, ids, rounds_inputs[r]["accept"], r)
-        _, _, _, nxt = O.verify_greedy(T, ids)
-        for b in range(d.B):
-            ctx.truncate(b, int(lengths[b]))
-        if n_done < len(rounds_inputs):
-            # parity spot check of the GPU chain (same seeded inputs, same schedule)
-            s = np.sort(ex["logits"].reshape(d.B * d.gamma, -1), axis=1)
-            decided = (s[:, -1] - s[:, -2]) >= 1e-3
-            g = gpu_ids[r].reshape(-1)
+            O.append_context(self.ctx, w, d, Hc, [list(range(W))], [int(rr["counts_h"][b])], self.fm)
+            if r == 0:  # the chain starts from the seeded anchors, like the GPU's
+                self.anchor = gen.make_anchors(d, 0)[b:b + 1]
+            anchor = self.anchor
+            ids, ex = O.draft_forward(w, self.d1, self.ctx, anchor, self.fm, return_all=True)
+            full = np.zeros((d.B, d.gamma), np.int32)
+            full[b] = ids[0]
+            T = gen.plant_target_logits(d, full, rr["accept"], r)
+            _, _, _, nxt = O.verify_greedy(T[b:b + 1], ids)
+            self.anchor = nxt
+            self.ctx.truncate(0, self.L)
+            if self.done < len(self.rounds):
+                self.checked.append((r, int(anchor[0]), ids[0].copy(), ex["logits"]))
+            self.done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        self.seconds += time.perf_counter() - t0
+
+    def parity(self, gpu_anchors, gpu_ids, gpu_y):
+        """The GPU chain's drafts of this sequence against the oracle's at the
+        stated 1e-3 band, in the rounds where both chains drafted from the same
+        anchor. A miss counts as explained when the oracle's head, evaluated on
+        the GPU's own Y, picks the GPU's token."""
+        O, b = self.O, self.b
+        agree = compared = 0
+        misses = []
+        for r, anchor, ids, logits in self.checked:
+            if anchor != int(gpu_anchors[r][b]):
+                misses.append({"round": r, "anchor_differs": True})
+                continue
+            s = np.sort(logits, axis=1)
+            decided = (s[:, -1] - s[:, -2]) >= NEAR_TIE
+            g = gpu_ids[r][b]
             compared += int(decided.sum())
-            agree += int((decided & (g == ids.reshape(-1))).sum())
-        anchor = nxt
-        n_done += 1
-        if time.perf_counter() - t0 >= seconds and n_done >= 2:
-            break
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {
-        "value": round(n_done * d.B / dt, 4),
-        "unit": "blocks/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"{n_done} full rounds (append + forward + verify) of the same workload, numpy float64 "
-                  f"bf16-faithful oracle, {dt:.1f} s wall on the host; context prefill untimed",
-        "parity_ids_agree": f"{agree}/{compared}",
-    }
+            agree += int((decided & (g == ids)).sum())
+            for k in np.nonzero(decided & (g != ids))[0]:
+                y = gpu_y[r][b, k:k + 1].astype(np.float64)
+                own, best, lg = O.lm_head_argmax(y, self.w["E_out"], want_logits=True)
+                explained = int(own[0]) == int(g[k]) or best[0] - lg[0, g[k]] <= NEAR_TIE
+                misses.append({"round": r, "pos": int(k), "gpu": int(g[k]), "oracle": int(ids[k]),
+                               "oracle_top2_gap": round(float(s[k, -1] - s[k, -2]), 6),
+                               "explained_by_gpu_Y": bool(explained)})
+        return agree, compared, misses
 
 
 # ----------------------------------------------------------------------------
+# counter workload
 
 
 COPY_BYTES = 256 << 20    # calibration copy: reads and writes this many bytes
 
 
-def profile_head(d, dev, launches=20):
-    """Workload for memory-counter passes: one elementwise copy of COPY_BYTES
-    (a kernel whose HBM reads and writes are known, to scale the counters),
-    then eager launches of the LM-head argmax alone at the workload's shape."""
+def calibration_copy(dev):
+    """One elementwise copy whose HBM reads and writes are known (COPY_BYTES
+    each), to scale the memory counters of the kernels that follow."""
     import torch
-    from block_diffusion_draft_tap_amd import binding as bd
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     del src, dst
-    rows = d.B * d.gamma
-    E = bd.Weight(gen.make_weight(d, "E_out"), dev)
-    y16 = gen.f32_to_bf16_bits(np.random.default_rng(5).standard_normal((rows, d.H)).astype(np.float32))
-    y = torch.from_numpy(y16.view(np.int16)).to(dev).view(torch.bfloat16)
-    ids = torch.empty(rows, dtype=torch.int32, device=dev)
-    ws = bd.lm_head_workspace(d.V, rows, dev)
-    for _ in range(launches):
-        bd.check(bd.dflash_lm_head_argmax(E, y, ids, ws), "lm_head_argmax")
-    torch.cuda.synchronize()
-    log(f"[profile-head] copy {COPY_BYTES} B, {launches} LM-head launches ({d.V} x {d.H}, {rows} rows)")
 
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+# ----------------------------------------------------------------------------
 
 
-def bench_prefill(d, dev, args):
-    """Context prefill of every sequence of the workload in one pass: the
-    context projection (Eq 2) of all sum(L) rows, then every layer's context
-    K/V. bf16 models run both as matrix-core GEMMs. Weights and taps are drawn
-    on the device (N(0, 0.02) and N(0, 1) in bf16): the values do not change
-    the work, and drawing ~10 GB of taps on the host would dominate the run."""
+def prefill(d, dm, kv, ws, lengths, cpu_seq, dev, reps, up):
+    """The whole context of every sequence in one projection call and one K/V
+    call, `reps` + 1 times (the first untimed); returns the timing summary."""
     import torch
     import block_diffusion_draft_tap_amd as dfa
     from block_diffusion_draft_tap_amd import binding as bd
-    g = torch.Generator(device=dev)
-    g.manual_seed(0)
-
-    def rnd(shape, std):
-        return (torch.randn(*shape, generator=g, device=dev) * std).to(torch.bfloat16)
-
-    log(f"[prefill] drawing {d.name} weights on the device")
-    w = {}
-    for name in gen.weight_names(d):
-        shape = gen.weight_shape(d, name)
-        w[name] = torch.ones(shape, dtype=torch.bfloat16, device=dev) if gen.is_gain(name) else rnd(shape, 0.02)
-    dm = dfa.DeviceModel(d, w, dev)
-    del w
-    lengths = [int(x) for x in gen.context_lengths(d)]
     n = sum(lengths)
-    kv = dfa.KVCache(d, d.B, max(lengths) + 64, dev)
-    ws = dfa.workspace(d, d.B, kv.cap, dev)
-    taps = [rnd((n, d.H), 1.0) for _ in range(d.m)]
+    offs_h = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    act = torch.float32 if d.wdtype == "f32" else torch.bfloat16
+    taps = [torch.empty(n, d.H, dtype=act, device=dev) for _ in range(d.m)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000)
+    for b in range(d.B):
+        s0, s1 = int(offs_h[b]), int(offs_h[b + 1])
+        if b == cpu_seq or n * d.m * d.H <= (64 << 20):
+            for j, t in enumerate(gen.make_taps(d, 0, lengths[b], stream="ctx", seq=b)):
+                taps[j][s0:s1] = up(t)
+        else:
+            for j in range(d.m):
+                taps[j][s0:s1] = torch.randn(s1 - s0, d.H, generator=g, device=dev).to(act)
     h = torch.empty(n, d.d, dtype=torch.float32, device=dev)
-    offs = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32, device=dev)
-    # room for every layer's bf16 normalised rows: the K/V GEMM reads plain bf16 tiles
-    kws = dfa.kv_prefill_workspace(d, n) if d.wdtype == "bf16" else ws
-    flops_proj = 2.0 * n * d.m * d.H * d.d
-    flops_kv = 2.0 * n * d.d * 2 * d.hkv * d.hd * d.nl
+    offs = torch.from_numpy(offs_h.astype(np.int32)).to(dev)
+    kws = dfa.kv_prefill_workspace(d, n, dev) if (d.wdtype == "bf16" and n >= 64) else ws
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    reps = max(1, args.steps)
     proj_ms, kv_ms = [], []
     for r in range(reps + 1):
         kv.len.zero_()
         torch.cuda.synchronize()
         ev[0].record()
-        bd.check(dfa.dflash_context_project(dm, taps, h, ws), "context_project")
+        bd.check(dfa.dflash_context_project(dm, taps, h, ws), "context_project (prefill)")
         ev[1].record()
-        bd.check(dfa.dflash_ctx_kv_append(dm, h, offs, None, kv, kws), "append")
+        bd.check(dfa.dflash_ctx_kv_append(dm, h, offs, None, kv, kws), "append (prefill)")
         ev[2].record()
         torch.cuda.synchronize()
-        if r > 0:  # the first pass is the warm-up
+        if r > 0:
             proj_ms.append(ev[0].elapsed_time(ev[1]))
             kv_ms.append(ev[1].elapsed_time(ev[2]))
     assert kv.len.cpu().tolist() == lengths
+    del taps, h, kws
+    torch.cuda.empty_cache()
+    if reps == 0:
+        return None
     pm, km = float(np.median(proj_ms)), float(np.median(kv_ms))
-    tot_tf = (flops_proj + flops_kv) / ((pm + km) / 1e3) / 1e12
-    res = {
-        "metric": "context prefill (projection + per-layer K/V) TFLOP/s at 1 MI355X; % MFMA bf16 roofline",
-        "value": round(tot_tf, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": reps,
-        "higher_is_better": True,
-        "dtype": "bf16" if d.wdtype == "bf16" else d.wdtype,
-        "data": "synthetic (weights and taps drawn on the device)",
-        "config": {"workload": describe(d, lengths), "rows": n,
-                   "kv_workspace_bytes": int(kws.numel())},
-        "projection": {"ms": round(pm, 3), "tflops": round(flops_proj / (pm / 1e3) / 1e12, 2),
-                       "flops": flops_proj},
-        "kv": {"ms": round(km, 3), "tflops": round(flops_kv / (km / 1e3) / 1e12, 2), "flops": flops_kv},
-        "roofline": {"bound": "mfma", "achieved": round(tot_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tot_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+    flops_proj = 2.0 * n * d.m * d.H * d.d
+    flops_kv = 2.0 * n * d.d * 2 * d.hkv * d.hd * d.nl
+    tot = (flops_proj + flops_kv) / ((pm + km) / 1e3) / 1e12
+    return {"rows": n, "reps": reps,
+            "projection": {"ms": round(pm, 3), "tflops": round(flops_proj / (pm / 1e3) / 1e12, 2)},
+            "kv": {"ms": round(km, 3), "tflops": round(flops_kv / (km / 1e3) / 1e12, 2)},
+            "tflops": round(tot, 2), "mfma_frac": round(tot / MFMA_BF16_PEAK_TFLOPS, 4),
+            "peak_tflops": MFMA_BF16_PEAK_TFLOPS}
+
+
+def kernel_table(rounds, lengths_after):
+    """Per kernel: launches and time per round, algorithmic bytes, achieved
+    GB/s, from the stamps of every round's last replay."""
+    from block_diffusion_draft_tap_amd import binding as bd
+    acc = {}
+    for r, rr in enumerate(rounds):
+        durs = bd.traced_durations_s(rr["stamps"], rr["records"])
+        for rec, t in zip(rr["records"], durs):
+            a = acc.setdefault(rec["kernel"], {"kind": rec["kind"], "launches": 0, "s": 0.0, "bytes": 0.0})
+            a["launches"] += 1
+            a["s"] += t
+            a["bytes"] += rec["bytes"] + rec["ctx_row_bytes"] * lengths_after[r]
+    R = len(rounds)
+    table = []
+    for k, a in acc.items():
+        assert a["s"] > 0, k
+        table.append({"kernel": k, "kind": {1: "lm_head", 2: "attention", 4: "projection"}[a["kind"]],
+                      "launches_per_round": a["launches"] / R, "us_per_round": a["s"] / R * 1e6,
+                      "avg_launch_us": a["s"] / a["launches"] * 1e6,
+                      "algorithmic_bytes_per_launch": a["bytes"] / a["launches"],
+                      "achieved_gbs": a["bytes"] / a["s"] / 1e9})
+    table.sort(key=lambda x: -x["us_per_round"])
+    return table
+
+
+def roofline_entry(k, d, timing):
+    entry = {
+        "bound": "hbm",
+        "kernel": k["kernel"],
+        "launches_per_round": round(k["launches_per_round"], 2),
+        "achieved": round(k["achieved_gbs"], 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(k["achieved_gbs"] / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "algorithmic_bytes_per_launch": int(k["algorithmic_bytes_per_launch"]),
+        "avg_launch_us": round(k["avg_launch_us"], 3),
+        "us_per_round": round(k["us_per_round"], 2),
+        "timing": timing,
     }
-    print(json.dumps(res), flush=True)
+    tfile = os.path.join(ROOT, "profiles", f"{tag(k['kernel'])}_{d.name}_traffic.md")
+    if os.path.exists(tfile):
+        # counter-derived bytes per launch, valid only for the kernel sources they were taken with
+        from block_diffusion_draft_tap_amd import prof_report
+        vals = prof_report.read_summary(tfile)
+        if vals.get("kernel sources sha256[:16]") == prof_report.kernel_sources_hash() and "bytes per launch" in vals:
+            entry["traffic"] = float(vals["bytes per launch"])
+    return entry
 
 
 def main():
@@ -238,17 +316,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", default="default", choices=sorted(CONFIGS))
+    ap.add_argument("--config", default="batched", choices=sorted(CONFIGS))
     ap.add_argument("--rounds", type=int, default=8, help="distinct round inputs, replayed in a cycle")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=24.0, help="oracle time, split over the CPU segments")
+    ap.add_argument("--cpu-segments", type=int, default=2, help="CPU segments interleaved with GPU segments")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--prefill-reps", type=int, default=2, help="timed whole-context prefills")
+    ap.add_argument("--flush-steps", type=int, default=40, help="rounds timed one by one after a MALL flush")
     ap.add_argument("--eager", action="store_true", help="launch every call from the host (no graphs)")
-    ap.add_argument("--profile-head", action="store_true",
-                    help="counter workload: a 256 MiB device copy (calibration), then eager LM-head launches")
-    ap.add_argument("--device-taps", action="store_true",
-                    help="draw the prefilled context's taps on the device (large batched contexts)")
-    ap.add_argument("--prefill", action="store_true",
-                    help="time the context prefill (projection + K/V of every context row) instead of the round")
+    ap.add_argument("--no-trace", action="store_true", help="rounds without the in-kernel stamps")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="counter workload: a 256 MiB device copy (calibration), then eager rounds")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -267,24 +345,6 @@ def main():
     if bd.dflash_query(d) != bd.DFLASH_OK:
         print("libdflash declined this configuration on this device", file=sys.stderr)
         sys.exit(3)
-    if args.profile_head:
-        profile_head(d, dev)
-        return
-    if args.prefill:
-        bench_prefill(d, dev, args)
-        return
-    if args.device_taps and not args.skip_cpu:
-        print("--device-taps changes the prefilled context: use it with --skip-cpu", file=sys.stderr)
-        sys.exit(2)
-
-    t_setup = time.perf_counter()
-    log(f"[bench] generating weights for {d.name}")
-    w = gen.Model(d).materialise()
-    dm = dfa.DeviceModel(d, w, dev)
-    del w
-    lengths = [int(x) for x in gen.context_lengths(d)]
-    cap = max(lengths) + W + 64
-    kv = dfa.KVCache(d, B, cap, dev)
 
     def up(a):
         a = np.ascontiguousarray(a)
@@ -292,36 +352,27 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
+    t_setup = time.perf_counter()
+    log(f"[bench] generating weights for {d.name}")
+    w = gen.Model(d).materialise()
+    dm = dfa.DeviceModel(d, w, dev)
+    lengths = [int(x) for x in gen.context_lengths(d)]
+    cpu_seq = int(np.argmin(lengths))
+    cap = max(lengths) + W + 64
+    kv = dfa.KVCache(d, B, cap, dev)
     ws = dfa.workspace(d, B, kv.cap, dev)
 
-    # prefill the retained context (untimed)
-    log("[bench] prefilling the context")
-    for b in range(B):
-        L = lengths[b]
-        if args.device_taps:
-            gt = torch.Generator(device=dev)
-            gt.manual_seed(1000 + b)
-            taps = [torch.randn(L, d.H, generator=gt, device=dev).to(torch.bfloat16 if d.wdtype != "f32" else
-                                                                      torch.float32) for _ in range(d.m)]
-        else:
-            taps = [up(t) for t in gen.make_taps(d, 0, L, stream="ctx", seq=b)]
-        h = torch.empty(L, d.d, dtype=torch.float32, device=dev)
-        bd.check(dfa.dflash_context_project(dm, taps, h, ws), "context_project")
-        offs = torch.zeros(B + 1, dtype=torch.int32, device=dev)
-        offs[b + 1:] = L
-        bd.check(dfa.dflash_ctx_kv_append(dm, h, offs, None, kv, ws), "append")
-        del taps, h
-    torch.cuda.synchronize()
+    log(f"[bench] prefilling {sum(lengths)} context rows ({B} sequences)")
+    pre = prefill(d, dm, kv, ws, lengths, cpu_seq, dev, 0 if args.profile_kernels else args.prefill_reps, up)
     len0 = kv.len.clone()
-    assert kv.len.cpu().tolist() == lengths
 
     vws = bd.verify_workspace(B, d.gamma, d.V, dev)
     offs = torch.arange(0, (B + 1) * W, W, dtype=torch.int32, device=dev)
     h_new = torch.empty(B * W, d.d, dtype=torch.float32, device=dev)
+    y_chain = torch.empty(B, d.gamma, d.H, dtype=dm.act_dtype, device=dev)
 
     # per-round inputs, resident on the device
     accept = [gen.accept_schedule(d, r) for r in range(R)]
-    head_wgs, head_launches = bd.dflash_lm_head_workgroups(d.V, d.H, d.wdtype, B * d.gamma)
     rounds = []
     for r in range(R):
         taps_r = [gen.make_taps(d, r * W, W, stream="round", seq=b) for b in range(B)]
@@ -336,42 +387,55 @@ def main():
             "com": torch.zeros(B, dtype=torch.int32, device=dev),
             "vids": torch.zeros(B, W, dtype=torch.int32, device=dev),
             "nxt": torch.zeros(B, dtype=torch.int32, device=dev),
-            # LM-head workgroup wall-clock stamps of this round's latest run
-            "stamps": torch.zeros(2 * head_wgs * head_launches, dtype=torch.int64, device=dev),
+            "stamps": torch.zeros(STAMP_ENTRIES, dtype=torch.int64, device=dev),
+            "records": [],
         }
         rr["counts"] = torch.from_numpy(rr["counts_h"]).to(dev)
         rounds.append(rr)
 
-    def run_round(rr, verify=True):
-        # the head kernel writes its workgroup stamps into this round's buffer (a kernel
-        # argument: captured graphs keep writing them on every replay)
-        bd.dflash_trace_head_stamps(rr["stamps"])
+    def run_round(rr, verify=True, trace=False, y=None):
+        if trace:
+            bd.dflash_trace_begin(bd.DFLASH_TRACE_LM_HEAD | bd.DFLASH_TRACE_ATTENTION | bd.DFLASH_TRACE_PROJECTIONS,
+                                  rr["stamps"])
         bd.check(dfa.dflash_context_project(dm, rr["taps"], h_new, ws), "context_project")
         bd.check(dfa.dflash_ctx_kv_append(dm, h_new, offs, rr["counts"], kv, ws), "append")
-        bd.check(dfa.dflash_draft_forward(dm, rr["anchors"], kv, B, rr["ids"], ws), "forward")
+        bd.check(dfa.dflash_draft_forward(dm, rr["anchors"], kv, B, rr["ids"], ws, y_out=y), "forward")
         if verify:
             bd.check(dfa.dflash_verify_greedy(rr["T"], rr["ids"], rr["acc"], rr["com"], rr["vids"], vws,
                                               next_anchor=rr["nxt"]), "verify")
         kv.len.copy_(len0)
-        bd.dflash_trace_head_stamps(None)
+        if trace:
+            rr["records"] = bd.dflash_trace_end()
 
     # untimed chain: drafts of each round plant that round's target logits
     log("[bench] building the round chain")
     anchor = gen.make_anchors(d, 0)
-    chain_ids = []
+    chain_ids, chain_y = [], []
     for r, rr in enumerate(rounds):
         rr["anchors"].copy_(torch.from_numpy(anchor))
-        run_round(rr, verify=False)
+        rr["anchors_h"] = anchor.copy()
+        run_round(rr, verify=False, y=y_chain)
         ids = rr["ids"].cpu().numpy().copy()
         chain_ids.append(ids)
+        chain_y.append(y_chain.float().cpu().numpy())
         rr["T"].copy_(torch.from_numpy(gen.plant_target_logits(d, ids, accept[r], r)))
         bd.check(dfa.dflash_verify_greedy(rr["T"], rr["ids"], rr["acc"], rr["com"], rr["vids"], vws,
                                           next_anchor=rr["nxt"]), "verify")
         assert np.array_equal(rr["acc"].cpu().numpy(), accept[r])
         anchor = rr["nxt"].cpu().numpy().copy()
     torch.cuda.synchronize()
+    del y_chain
 
-    # capture one graph per round
+    if args.profile_kernels:
+        calibration_copy(dev)
+        for rr in rounds:
+            run_round(rr)
+        torch.cuda.synchronize()
+        log(f"[profile-kernels] copy {COPY_BYTES} B, then {R} eager rounds of {d.name}")
+        return
+
+    # capture one graph per round (the trace records each launch's stamp slice)
+    trace = not args.no_trace
     graphs = []
     stream = torch.cuda.Stream(device=dev)
     use_graph = not args.eager
@@ -381,7 +445,7 @@ def main():
         for rr in rounds:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
-                run_round(rr)
+                run_round(rr, trace=trace)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -389,21 +453,40 @@ def main():
         if use_graph:
             graphs[i % R].replay()
         else:
-            run_round(rounds[i % R])
+            run_round(rounds[i % R], trace=trace)
+
+    def timed(nsteps, first):
+        """nsteps consecutive rounds between synchronisations, one event pair
+        around all of them: total ms."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(nsteps):
+            step(first + i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def timed_per_step(nsteps, first):
+        """nsteps consecutive rounds with an event between rounds: ms of each."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(nsteps):
+            step(first + i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(nsteps)]
 
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s; warmup {args.warmup}, timed {args.steps}")
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record()
-    torch.cuda.synchronize()
+    gpu_ms = timed(args.steps, args.warmup)
     wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
+    nxt = args.warmup + args.steps
+    per_step = timed_per_step(args.steps, nxt)
+    nxt += args.steps
 
     # the replays must reproduce the chain exactly (deterministic kernels)
     for r, rr in enumerate(rounds):
@@ -411,28 +494,11 @@ def main():
         assert np.array_equal(rr["acc"].cpu().numpy(), accept[r]), f"round {r}: accepted changed on replay"
         assert np.array_equal(rr["com"].cpu().numpy(), accept[r] + 1)
 
-    # the dominant kernel's duration, from the wall-clock stamps its workgroups wrote
-    # during the timed region (the last run of each round)
-    head_source = (f"device wall-clock stamps written by the kernel's workgroups (first start to last end), "
-                   f"last timed run of each of the {R} rounds")
-    head_us = [t * 1e6 for rr in rounds for t in bd.stamps_duration_s(rr["stamps"], head_launches)]
-    assert all(0 < x < 1e5 for x in head_us), head_us
-    head_us_avg = float(np.mean(head_us))
     ms_per_step = gpu_ms / args.steps
     blocks_per_s = B * args.steps / (gpu_ms / 1000.0)
     mean_new = float(np.mean([rr["counts_h"].sum() for rr in rounds]))
     ab = algorithmic_bytes(d, B, sum(lengths), mean_new / B)
     round_gbs = ab["total"] / (ms_per_step / 1000.0) / 1e9
-    head_gbs = ab["lm_head"] / (head_us_avg / 1e6) / 1e9
-
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"lm_head_gemv_{d.name}_traffic.md")
-    if os.path.exists(tfile):
-        # counter-derived bytes per launch, valid only for the kernel sources they were taken with
-        from block_diffusion_draft_tap_amd import prof_report
-        vals = prof_report.read_summary(tfile)
-        if vals.get("kernel sources sha256[:16]") == prof_report.kernel_sources_hash() and "bytes per launch" in vals:
-            traffic = float(vals["bytes per launch"])
 
     res = {
         "metric": METRIC,
@@ -446,7 +512,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": d.wdtype,
-        "data": "synthetic",
+        "data": "synthetic (seeded round inputs; prefilled context taps drawn on the device except the "
+                "CPU-replayed sequence's)",
         "config": {
             "workload": describe(d, lengths),
             "rounds_cycled": R,
@@ -454,27 +521,80 @@ def main():
             "launch": "hip graph per round" if use_graph else "eager",
         },
         "tokens_proposed_per_s": round(blocks_per_s * d.gamma, 1),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 5) for q in (10, 50, 90)],
+        "step_ms_note": "per-round distribution from a second run of the same steps with an event between rounds",
         "round_algorithmic_bytes": int(ab["total"]),
         "round_hbm_frac": round(round_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "LM head with argmax epilogue",
-            "launches_x_workgroups": f"{head_launches} x {head_wgs}",
-            "achieved": round(head_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(head_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": int(ab["lm_head"]),
-            "avg_launch_us": round(head_us_avg, 3),
-            "timing": head_source,
-        },
-        "wall_s_timed": round(wall, 4),
     }
+
+    lengths_after = [sum(lengths) + int(rr["counts_h"].sum()) for rr in rounds]
+    if trace:
+        table = kernel_table(rounds, lengths_after)
+        timing = (f"device wall-clock stamps written by the kernel's workgroups (first start to last end per "
+                  f"launch), last timed replay of each of the {R} rounds")
+        res["roofline"] = roofline_entry(table[0], d, timing)
+        head = [k for k in table if k["kind"] == "lm_head"]
+        if head and head[0] is not table[0]:
+            res["roofline_lm_head"] = roofline_entry(head[0], d, timing)
+        res["kernels_per_round"] = [{k2: (round(v, 2) if isinstance(v, float) else v) for k2, v in k.items()}
+                                    for k in table[:8]]
+        traced = sum(k["us_per_round"] for k in table)
+        res["traced_share_of_round"] = round(traced / (ms_per_step * 1e3), 4)
+    res["prefill"] = pre
+    res["wall_s_timed"] = round(wall, 4)
+
+    # rounds one by one, each after a write that evicts the MALL (a decode loop runs the
+    # target model between drafter rounds)
+    if args.flush_steps > 0:
+        junk = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fl = []
+        for i in range(args.flush_steps):
+            junk.fill_(float(i))
+            e0.record()
+            step(nxt + i)
+            e1.record()
+            torch.cuda.synchronize()
+            fl.append(e0.elapsed_time(e1))
+        nxt += args.flush_steps
+        del junk
+        med = float(np.median(fl))
+        res["mall_flushed"] = {"rounds": args.flush_steps, "flush_bytes": FLUSH_BYTES,
+                               "ms_p10_p50_p90": [round(float(np.percentile(fl, q)), 5) for q in (10, 50, 90)],
+                               "blocks_per_s_at_median": round(B / (med / 1e3), 2)}
+
     if not args.skip_cpu:
-        log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f}s of oracle rounds)")
-        rounds_inputs = [{"counts": rr["counts_h"], "accept": rr["accept"]} for rr in rounds]
-        res["cpu_baseline"] = cpu_baseline(d, rounds_inputs, args.cpu_seconds, chain_ids)
+        log(f"[bench] cpu baseline: oracle setup for sequence {cpu_seq} ({lengths[cpu_seq]} context rows)")
+        cpu = CpuLeg(d, w, cpu_seq, lengths[cpu_seq], rounds)
+        seg_gpu = []
+        nseg = max(1, args.cpu_segments)
+        for sgi in range(nseg):
+            log(f"[bench] cpu segment {sgi + 1}/{nseg}")
+            cpu.run(args.cpu_seconds / nseg)
+            ms = timed(args.steps, nxt)
+            nxt += args.steps
+            seg_gpu.append(round(B * args.steps / (ms / 1e3), 2))
+        agree, compared, misses = cpu.parity([rr["anchors_h"] for rr in rounds], chain_ids, chain_y)
+        threads = 1
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except ImportError:
+            pass
+        res["cpu_baseline"] = {
+            "value": round(cpu.done / cpu.seconds, 5),
+            "unit": "blocks/s",
+            "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{cpu.done} rounds of one sequence (seq {cpu_seq}, context {lengths[cpu_seq]}) of the same "
+                      f"workload: context projection + K/V append of the committed rows, forward, LM head, "
+                      f"verify; numpy float64 bf16-faithful oracle, {cpu.seconds:.1f} s on the host in {nseg} "
+                      f"segments interleaved with timed GPU segments; its context prefill untimed",
+            "host": host_info(),
+            "gpu_blocks_per_s_interleaved_segments": seg_gpu,
+            "parity_ids_agree_1e-3": f"{agree}/{compared}",
+            "parity_misses": misses,
+        }
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

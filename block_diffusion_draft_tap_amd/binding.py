@@ -25,8 +25,9 @@ DFLASH_ACT_GELU_TANH, DFLASH_ACT_SILU = 0, 1
 EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "dflash_invocations",
            "dflash_context_project", "dflash_ctx_kv_append", "dflash_draft_layer", "dflash_draft_forward",
            "dflash_lm_head_argmax", "dflash_lm_head_workspace_bytes", "dflash_verify_greedy",
-           "dflash_verify_workspace_bytes", "dflash_kv_prefill_workspace_bytes", "dflash_trace_head_stamps",
-           "dflash_lm_head_workgroups", "dflash_wall_clock_hz"]
+           "dflash_verify_workspace_bytes", "dflash_kv_prefill_workspace_bytes", "dflash_trace_begin",
+           "dflash_trace_end", "dflash_lm_head_workgroups", "dflash_wall_clock_hz"]
+DFLASH_TRACE_LM_HEAD, DFLASH_TRACE_ATTENTION, DFLASH_TRACE_PROJECTIONS = 1, 2, 4
 
 
 class DflashError(RuntimeError):
@@ -62,6 +63,11 @@ class dflash_kv(ctypes.Structure):
                 ("B", ctypes.c_int32), ("cap", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class dflash_trace_record(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char * 64), ("kind", ctypes.c_int32), ("workgroups", ctypes.c_int32),
+                ("offset", ctypes.c_int64), ("bytes", ctypes.c_double), ("ctx_row_bytes", ctypes.c_double)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_diffusion_draft_tap_amd.build` "
@@ -94,8 +100,10 @@ def _load():
     lib.dflash_verify_greedy.restype = ctypes.c_int
     lib.dflash_verify_workspace_bytes.argtypes = [I32, I32, I32]
     lib.dflash_verify_workspace_bytes.restype = SZ
-    lib.dflash_trace_head_stamps.argtypes = [VP, ctypes.c_int32]
-    lib.dflash_trace_head_stamps.restype = None
+    lib.dflash_trace_begin.argtypes = [I32, VP, ctypes.c_int64]
+    lib.dflash_trace_begin.restype = None
+    lib.dflash_trace_end.argtypes = [P(dflash_trace_record), I32]
+    lib.dflash_trace_end.restype = I32
     lib.dflash_lm_head_workgroups.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.dflash_lm_head_workgroups.restype = ctypes.c_int32
@@ -348,14 +356,20 @@ def verify_workspace(B, gamma, V, device="cuda"):
     return torch.empty(lib.dflash_verify_workspace_bytes(B, gamma, V), dtype=torch.uint8, device=device)
 
 
-def dflash_trace_head_stamps(stamps=None):
-    """Route LM-head workgroup wall-clock stamps into `stamps` (a uint64-sized
-    int64 device tensor; None: off)."""
-    if stamps is None:
-        lib.dflash_trace_head_stamps(None, 0)
-    else:
-        assert stamps.dtype == torch.int64 and stamps.is_cuda and stamps.is_contiguous()
-        lib.dflash_trace_head_stamps(_ptr(stamps), stamps.numel())
+def dflash_trace_begin(kinds, stamps):
+    """Trace the launches of `kinds` (DFLASH_TRACE_* bits): their workgroups
+    write wall-clock (start, end) pairs into `stamps`, an int64 device tensor."""
+    assert stamps.dtype == torch.int64 and stamps.is_cuda and stamps.is_contiguous()
+    lib.dflash_trace_begin(int(kinds), _ptr(stamps), stamps.numel())
+
+
+def dflash_trace_end(capacity=4096):
+    """Stop tracing; the records of the traced launches as dicts (kernel,
+    kind, workgroups, offset, bytes, ctx_row_bytes), in enqueue order."""
+    recs = (dflash_trace_record * capacity)()
+    n = lib.dflash_trace_end(recs, capacity)
+    return [{"kernel": r.kernel.decode(), "kind": r.kind, "workgroups": r.workgroups, "offset": r.offset,
+             "bytes": r.bytes, "ctx_row_bytes": r.ctx_row_bytes} for r in recs[:min(n, capacity)]]
 
 
 def dflash_lm_head_workgroups(V, H, dtype, M, y_dtype=None):
@@ -375,12 +389,15 @@ def dflash_wall_clock_hz():
     return lib.dflash_wall_clock_hz()
 
 
-def stamps_duration_s(stamps, launches=1):
-    """Kernel durations (seconds) from a stamp buffer: per launch, the last
-    workgroup end minus the first workgroup start."""
-    a = stamps.cpu().numpy().astype(np.int64).reshape(launches, -1, 2)
+def traced_durations_s(stamps, records):
+    """Duration (seconds) of every traced launch: its last workgroup end minus
+    its first workgroup start, read from the stamp buffer."""
+    a = stamps.cpu().numpy().astype(np.int64)
     hz = lib.dflash_wall_clock_hz()
     if hz <= 0:
         raise DflashError("the runtime reports no wall-clock rate")
-    return [(int(x[:, 1].max()) - int(x[:, 0].min())) / hz for x in a]
-
+    out = []
+    for r in records:
+        x = a[r["offset"]:r["offset"] + 2 * r["workgroups"]].reshape(-1, 2)
+        out.append((int(x[:, 1].max()) - int(x[:, 0].min())) / hz)
+    return out

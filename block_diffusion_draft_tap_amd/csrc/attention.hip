@@ -24,8 +24,11 @@
 //
 // fp32 caches (the fp32 workload): attn_valu_kernel, LDS-staged 64-key tiles,
 // one key per lane for the scores, one head-dim column per thread for P V.
+#include <cstdio>
+
 #include "attention.hpp"
 #include "common.hpp"
+#include "trace.hpp"
 
 
 namespace dfl {
@@ -76,6 +79,7 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
 
 template <int HD, int NRT>
 __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
+    const uint64_t t_start = trace_start(p.stamps);
     constexpr int KS = HD / 32;  // k-steps of S = Q K^T
     constexpr int DT = HD / 16;  // head-dim tiles of O
     constexpr int PLD = kChunk + 8;  // padded P row (bf16 elements)
@@ -287,6 +291,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
             dst[HD + 1] = rowl[r];
         }
     }
+    trace_end(p.stamps, t_start);
 }
 
 // ---------------------------------------------------------------------------
@@ -301,6 +306,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
 
 template <int HD, int NRT>
 __global__ __launch_bounds__(64 * NRT, 2) void attn_rows_kernel(const AttnParams p) {
+    const uint64_t t_start = trace_start(p.stamps);
     constexpr int KS = HD / 32, DT = HD / 16;
     constexpr int PLD = kChunk + 8;
     __shared__ __align__(16) uint16_t plds[NRT][2][16][PLD];  // P tiles (high, low) per wavefront
@@ -443,6 +449,7 @@ __global__ __launch_bounds__(64 * NRT, 2) void attn_rows_kernel(const AttnParams
             dst[HD + 1] = l[e];
         }
     }
+    trace_end(p.stamps, t_start);
 }
 
 // ---------------------------------------------------------------------------
@@ -450,6 +457,7 @@ __global__ __launch_bounds__(64 * NRT, 2) void attn_rows_kernel(const AttnParams
 
 template <int HD, int RMAX>
 __global__ __launch_bounds__(kBlock) void attn_valu_kernel(const AttnParams p) {
+    const uint64_t t_start = trace_start(p.stamps);
     constexpr int NPH = kBlock / HD;    // P.V phases (threads per head-dim column)
     constexpr int RPT = (RMAX + NPH - 1) / NPH;
     constexpr int RPWV = (RMAX + 3) / 4;  // softmax rows per wavefront
@@ -569,6 +577,7 @@ __global__ __launch_bounds__(kBlock) void attn_valu_kernel(const AttnParams p) {
             }
         }
     }
+    trace_end(p.stamps, t_start);
 }
 
 // ---------------------------------------------------------------------------
@@ -710,25 +719,41 @@ template <int HD>
 static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
     const int R = (p.hq / p.hkv) * p.gamma;
     dim3 grid((unsigned)((int64_t)p.B * p.hkv * p.nsplit));
+    // instrumentation: the launch reads Q, the block's keys and values and every held
+    // context row's keys and values (counted by the caller from the lengths), and writes O
+    const double esz = p.kv_f32 ? 4.0 : 2.0;
+    const double rows = (double)p.B * p.gamma;
+    const double bytes = rows * p.hq * HD * esz * 2.0 + rows * p.hkv * HD * 2.0 * esz;
+    const double ctx_row_bytes = (double)p.hkv * HD * 2.0 * esz;
+    char name[40];
+    AttnParams q = p;
     (void)hipGetLastError();  // report only this launch's status
     if (p.kv_f32) {
-        if (R <= 8)
-            hipLaunchKernelGGL((attn_valu_kernel<HD, 8>), grid, dim3(kBlock), 0, s, p);
-        else if (R <= 40)
-            hipLaunchKernelGGL((attn_valu_kernel<HD, 40>), grid, dim3(kBlock), 0, s, p);
-        else
+        if (R <= 8) {
+            snprintf(name, sizeof name, "attn_valu_kernel<%d, 8>", HD);
+            q.stamps = trace_launch(TRACE_ATTENTION, name, grid.x, bytes, ctx_row_bytes);
+            hipLaunchKernelGGL((attn_valu_kernel<HD, 8>), grid, dim3(kBlock), 0, s, q);
+        } else if (R <= 40) {
+            snprintf(name, sizeof name, "attn_valu_kernel<%d, 40>", HD);
+            q.stamps = trace_launch(TRACE_ATTENTION, name, grid.x, bytes, ctx_row_bytes);
+            hipLaunchKernelGGL((attn_valu_kernel<HD, 40>), grid, dim3(kBlock), 0, s, q);
+        } else {
             return hipErrorInvalidValue;
+        }
     } else {
-        if (R <= 16)
-            hipLaunchKernelGGL((attn_mfma_kernel<HD, 1>), grid, dim3(kBlock), 0, s, p);
-        else if (R <= 32)
-            hipLaunchKernelGGL((attn_mfma_kernel<HD, 2>), grid, dim3(kBlock), 0, s, p);
-        else if (use_rows_kernel(R, 0, p.B * p.hkv, p.cap))
-            hipLaunchKernelGGL((attn_rows_kernel<HD, 3>), grid, dim3(64 * 3), 0, s, p);
-        else if (R <= kMaxRows)
-            hipLaunchKernelGGL((attn_mfma_kernel<HD, 3>), grid, dim3(kBlock), 0, s, p);
+        const int nrt = R <= 16 ? 1 : (R <= 32 ? 2 : 3);
+        const bool rows_kernel = R > 32 && use_rows_kernel(R, 0, p.B * p.hkv, p.cap);
+        if (R > kMaxRows) return hipErrorInvalidValue;
+        snprintf(name, sizeof name, rows_kernel ? "attn_rows_kernel<%d, %d>" : "attn_mfma_kernel<%d, %d>", HD, nrt);
+        q.stamps = trace_launch(TRACE_ATTENTION, name, grid.x, bytes, ctx_row_bytes);
+        if (nrt == 1)
+            hipLaunchKernelGGL((attn_mfma_kernel<HD, 1>), grid, dim3(kBlock), 0, s, q);
+        else if (nrt == 2)
+            hipLaunchKernelGGL((attn_mfma_kernel<HD, 2>), grid, dim3(kBlock), 0, s, q);
+        else if (rows_kernel)
+            hipLaunchKernelGGL((attn_rows_kernel<HD, 3>), grid, dim3(64 * 3), 0, s, q);
         else
-            return hipErrorInvalidValue;
+            hipLaunchKernelGGL((attn_mfma_kernel<HD, 3>), grid, dim3(kBlock), 0, s, q);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -26,6 +26,7 @@ struct AttnParams {
     float* out;            // O [B*gamma][out_ld], head h at columns h*hd
     int64_t out_ld;
     int round_out;         // 1: O is rounded and stored as bf16 (out reinterpreted as uint16)
+    uint64_t* stamps;      // set by the launcher when the launch is traced: (start, end) wall clock per workgroup
 };
 
 // Workgroups per (sequence, kv head) and partial results per (sequence, head)

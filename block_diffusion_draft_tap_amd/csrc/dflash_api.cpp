@@ -4,6 +4,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include <hip/hip_runtime.h>
 
@@ -13,6 +14,7 @@
 #include "gemv.hpp"
 #include "head.hpp"
 #include "skinny.hpp"
+#include "trace.hpp"
 
 using namespace dfl;
 
@@ -20,8 +22,16 @@ using namespace dfl;
 namespace {
 
 std::atomic<uint64_t> g_invocations{0};
-std::atomic<uint64_t*> g_stamps{nullptr};  // LM-head workgroup wall-clock stamps
-std::atomic<int32_t> g_stamps_cap{0};
+
+// launch tracing (dflash_trace_begin / dflash_trace_end)
+struct TraceState {
+    std::mutex mu;
+    std::atomic<int> kinds{0};
+    uint64_t* stamps = nullptr;
+    int64_t capacity = 0, cursor = 0;
+    std::vector<dflash_trace_record> records;
+};
+TraceState g_trace;
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -455,7 +465,6 @@ hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStr
         if (epi == EPI_ARGMAX) {
             q.part_val = p.part_val + (int64_t)r0 * p.nblocks;
             q.part_idx = p.part_idx + (int64_t)r0 * p.nblocks;
-            if (p.stamps) q.stamps = p.stamps + (int64_t)(r0 / maxm) * 2 * p.nblocks;
         }
         const hipError_t e = launch_gemv(wtype, pro, epi, maxm, q, layers, s);
         if (e != hipSuccess) return e;
@@ -524,7 +533,6 @@ hipError_t skinny_rows(int epi, SkinnyParams p, int rows, hipStream_t s) {
         if (epi == SK_ARGMAX) {
             q.part_val = p.part_val + (int64_t)r0 * p.nblocks;
             q.part_idx = p.part_idx + (int64_t)r0 * p.nblocks;
-            if (p.stamps) q.stamps = p.stamps + (int64_t)(r0 / kSkinnyRows) * 2 * p.nblocks;
         }
         const hipError_t e = launch_skinny(epi, q, s);
         if (e != hipSuccess) return e;
@@ -807,9 +815,6 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
         SkinnyParams p = skinny_params(E, static_cast<const uint16_t*>(y), H, V, H, nullptr);
         p.part_val = pv;
         p.part_idx = pi;
-        uint64_t* st = g_stamps.load();
-        const int nt = skinny_tiles(SK_ARGMAX, V), launches = (rows + kSkinnyRows - 1) / kSkinnyRows;
-        if (st && g_stamps_cap.load() >= 2 * nt * launches) p.stamps = st;
         DFL_HIP(skinny_rows(SK_ARGMAX, p, rows, s));
         DFL_HIP(launch_argmax_merge(pv, pi, skinny_tiles(SK_ARGMAX, V), rows, ids, maxl, s));
         return DFLASH_OK;
@@ -828,14 +833,34 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
     p.nblocks = lm_nblocks(V, H, wtype_of(E.dtype), rows < 8 ? rows : 8);
     p.part_val = pv;
     p.part_idx = pi;
-    uint64_t* st = g_stamps.load();
-    if (st && g_stamps_cap.load() >= 2 * p.nblocks * ((rows + 7) / 8)) p.stamps = st;
     DFL_HIP(gemv_rows(wtype_of(E.dtype), PRO_TAPS, EPI_ARGMAX, p, rows, s));
     DFL_HIP(launch_argmax_merge(pv, pi, p.nblocks, rows, ids, maxl, s));
     return DFLASH_OK;
 }
 
 }  // namespace
+
+uint64_t* dfl::trace_launch(int kind, const char* name, int64_t workgroups, double bytes, double ctx_row_bytes) {
+    static_assert(TRACE_LM_HEAD == DFLASH_TRACE_LM_HEAD && TRACE_ATTENTION == DFLASH_TRACE_ATTENTION &&
+                      TRACE_PROJECTIONS == DFLASH_TRACE_PROJECTIONS,
+                  "trace kinds");
+    if (!(g_trace.kinds.load(std::memory_order_relaxed) & kind)) return nullptr;
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    if (!(g_trace.kinds.load() & kind) || !g_trace.stamps || g_trace.cursor + 2 * workgroups > g_trace.capacity)
+        return nullptr;
+    dflash_trace_record r;
+    std::memset(&r, 0, sizeof(r));
+    std::strncpy(r.kernel, name, sizeof(r.kernel) - 1);
+    r.kind = kind;
+    r.workgroups = (int32_t)workgroups;
+    r.offset = g_trace.cursor;
+    r.bytes = bytes;
+    r.ctx_row_bytes = ctx_row_bytes;
+    g_trace.records.push_back(r);
+    uint64_t* slice = g_trace.stamps + g_trace.cursor;
+    g_trace.cursor += 2 * workgroups;
+    return slice;
+}
 
 // ===========================================================================
 
@@ -864,9 +889,25 @@ const char* dflash_status_string(int status) {
 
 uint64_t dflash_invocations(void) { return g_invocations.load(); }
 
-void dflash_trace_head_stamps(uint64_t* stamps, int32_t capacity) {
-    g_stamps_cap.store(stamps ? capacity : 0);
-    g_stamps.store(stamps);
+void dflash_trace_begin(int32_t kinds, uint64_t* stamps, int64_t capacity) {
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    const bool on = stamps && capacity > 0 && kinds > 0;
+    g_trace.stamps = on ? stamps : nullptr;
+    g_trace.capacity = on ? capacity : 0;
+    g_trace.cursor = 0;
+    g_trace.records.clear();
+    g_trace.kinds.store(on ? (kinds & (DFLASH_TRACE_LM_HEAD | DFLASH_TRACE_ATTENTION | DFLASH_TRACE_PROJECTIONS)) : 0);
+}
+
+int32_t dflash_trace_end(dflash_trace_record* records, int32_t capacity) {
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    const int32_t n = (int32_t)g_trace.records.size();
+    for (int32_t i = 0; i < n && i < capacity && records; ++i) records[i] = g_trace.records[i];
+    g_trace.kinds.store(0);
+    g_trace.stamps = nullptr;
+    g_trace.capacity = g_trace.cursor = 0;
+    g_trace.records.clear();
+    return n;
 }
 
 int32_t dflash_lm_head_workgroups(int32_t V, int32_t H, int32_t dtype, int32_t M, int32_t y_dtype, int32_t* launches) {
@@ -974,8 +1015,13 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
     if (n < 0 || (n > 0 && !h_ctx) || !row_offsets || !kv) return DFLASH_EINVAL;
     DFL_TRY(check_kv(kv, d, kv->B));
     DFL_TRY(gate());
-    if (n == 0 || d.nl == 0) return DFLASH_OK;
+    if (n == 0) return DFLASH_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (d.nl == 0) {  // no layer caches: only the held-row counts advance
+        DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
+        g_invocations++;
+        return DFLASH_OK;
+    }
     const size_t sk_bytes = kv_append_skinny_bytes(d, n);
     if (sk_bytes > 0 && ws && aligned16(ws) && ws_bytes >= sk_bytes) {
         // a round's rows: every layer's bf16(RMSNorm(h_ctx; attn_norm_i)) into ws, then

@@ -23,8 +23,11 @@
 //   sum_k x_k (s q_k + b) = s sum_k x_k (128 + q_k) + (b - 128 s) sum_k x_k
 // evaluated per 32-element lane chunk (the activation sums are staged with
 // the activations); fp32 weights use plain fp32 FMAs.
+#include <cstdio>
+
 #include "common.hpp"
 #include "gemv.hpp"
+#include "trace.hpp"
 
 namespace dfl {
 
@@ -287,10 +290,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
     float* red = xsum + (WT == W_I4 ? MAXM * (KC / 32) : 0);                            // [4*RPW][MAXM]
     float* rinv = red + 4 * RPW * MAXM;                                                 // [MAXM]
 
-    uint64_t t_start = 0;
-    if constexpr (EPI == EPI_ARGMAX) {
-        if (p.stamps) t_start = wall_clock64();
-    }
+    const uint64_t t_start = trace_start(p.stamps);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int layer = blockIdx.y;
     const WeightPtr W = p.w[layer];
@@ -649,11 +649,8 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
             p.part_val[(int64_t)tid * p.nblocks + blockIdx.x] = v;
             p.part_idx[(int64_t)tid * p.nblocks + blockIdx.x] = i;
         }
-        if (p.stamps && tid == 0) {
-            p.stamps[2 * blockIdx.x] = t_start;
-            p.stamps[2 * blockIdx.x + 1] = wall_clock64();
-        }
     }
+    trace_end(p.stamps, t_start);
 }
 
 // ---------------------------------------------------------------------------
@@ -735,6 +732,16 @@ static hipError_t launch_one(const GemvParams& p, int layers, hipStream_t s) {
     if (q.max_wgs > 0 && q.kslice <= KC && grid_x > q.max_wgs) grid_x = q.max_wgs;
     if (EPI == EPI_ARGMAX && q.nblocks != grid_x) return hipErrorInvalidValue;  // partial buffer layout
     dim3 grid(grid_x, layers, q.ksplit);
+    {  // instrumentation: algorithmic bytes = weights + activation rows + outputs
+        const double wb = WT == W_F32 ? 4.0 : (WT == W_BF16 ? 2.0 : 0.5 + 4.0 / 64);
+        const double xb = q.src_f32 ? 4.0 : 2.0;
+        const double nout = EPI == EPI_GATED ? q.F : (EPI == EPI_ARGMAX ? 0 : q.N);
+        const double bytes = layers * ((double)q.N * q.K * wb + (double)q.M * q.K * xb + (double)q.M * nout * 4.0);
+        char name[64];
+        snprintf(name, sizeof name, "gemv_kernel<%d, %d, %d, %d, %d>", WT, PRO, EPI, MAXM, RPW);
+        q.stamps = trace_launch(EPI == EPI_ARGMAX ? TRACE_LM_HEAD : TRACE_PROJECTIONS, name,
+                                (int64_t)grid_x * layers * q.ksplit, bytes, 0.0);
+    }
     // allow dynamic LDS beyond the 64 KiB default (gfx950 has 160 KiB per CU)
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&gemv_kernel<WT, PRO, EPI, MAXM, RPW>),

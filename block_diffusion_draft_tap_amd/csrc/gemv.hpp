@@ -98,7 +98,7 @@ struct GemvParams {
     float* part_val;     // [M][nblocks]
     int32_t* part_idx;
     int nblocks;
-    uint64_t* stamps;    // EPI_ARGMAX, optional: wall clock at start and end of each workgroup [nblocks][2]
+    uint64_t* stamps;    // set by the launcher when the launch is traced: (start, end) wall clock per workgroup
 };
 
 // Host-side launcher: picks the kernel for the weight type and the modes; maxm is

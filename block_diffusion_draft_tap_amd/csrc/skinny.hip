@@ -33,8 +33,11 @@
 // too few column tiles to fill the GPU split K: fp32 partial sums go to a
 // buffer, and a second kernel adds them in split order and applies the
 // epilogue (or the caller consumes them).
+#include <cstdio>
+
 #include "common.hpp"
 #include "skinny.hpp"
+#include "trace.hpp"
 
 namespace dfl {
 
@@ -130,9 +133,7 @@ __global__ __launch_bounds__(kST, MT >= 8 ? 1 : DFL_SK_OCC) void skinny_kernel(c
     __shared__ float red_v[kSW][RED];
     __shared__ int red_i[kSW][RED];
     __shared__ int meta_b[META], meta_pos[META];
-    uint64_t t_start = 0;
-    if constexpr (EPI == SK_ARGMAX)
-        if (p.stamps) t_start = wall_clock64();
+    const uint64_t t_start = trace_start(p.stamps);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int tile = blockIdx.x, split = blockIdx.y, z = blockIdx.z;
@@ -356,10 +357,6 @@ __global__ __launch_bounds__(kST, MT >= 8 ? 1 : DFL_SK_OCC) void skinny_kernel(c
             p.part_val[(int64_t)m * p.nblocks + tile] = v;
             p.part_idx[(int64_t)m * p.nblocks + tile] = idx;
         }
-        if (p.stamps && threadIdx.x == 0) {
-            p.stamps[2 * tile] = t_start;
-            p.stamps[2 * tile + 1] = wall_clock64();
-        }
     } else {
         float* part = (EPI == SK_PARTIAL) ? p.part + ((int64_t)z * p.nsplit + split) * p.M * p.N : nullptr;
 #pragma unroll
@@ -387,6 +384,7 @@ __global__ __launch_bounds__(kST, MT >= 8 ? 1 : DFL_SK_OCC) void skinny_kernel(c
                 }
             }
     }
+    trace_end(p.stamps, t_start);
 }
 
 // the sum of the split-K partials in split order, then the epilogue; 4 outputs a
@@ -555,13 +553,27 @@ __global__ __launch_bounds__(kRnThreads) void resid_norm_kernel(const float* par
     }
 }
 
+// instrumentation: the stamp slice of one matrix-core launch (algorithmic bytes =
+// weights + activation rows + outputs, per layer)
+template <int MT, int EPI>
+uint64_t* skinny_trace(const SkinnyParams& p, int tiles) {
+    const double nout = EPI == SK_GATED ? p.N / 2 : (EPI == SK_ARGMAX ? 0 : p.N);
+    const double bytes = p.layers * ((double)p.N * p.K * 2.0 + (double)p.M * p.K * 2.0 + (double)p.M * nout * 4.0);
+    char name[48];
+    snprintf(name, sizeof name, "skinny_kernel<%d, %d>", MT, EPI);
+    return trace_launch(EPI == SK_ARGMAX ? TRACE_LM_HEAD : TRACE_PROJECTIONS, name,
+                        (int64_t)tiles * p.nsplit * p.layers, bytes, 0.0);
+}
+
 template <int MT, int EPI>
 hipError_t launch_mt(const SkinnyParams& p, hipStream_t s) {
     const int tiles = skinny_tiles(EPI, p.N);
     (void)hipGetLastError();  // report only these launches' status
     if constexpr (EPI == SK_STORE || EPI == SK_RESID || EPI == SK_KV) {
         if (p.nsplit > 1) {
-            hipLaunchKernelGGL((skinny_kernel<MT, SK_PARTIAL>), dim3(tiles, p.nsplit, p.layers), dim3(kST), 0, s, p);
+            SkinnyParams q = p;
+            q.stamps = skinny_trace<MT, SK_PARTIAL>(p, tiles);
+            hipLaunchKernelGGL((skinny_kernel<MT, SK_PARTIAL>), dim3(tiles, p.nsplit, p.layers), dim3(kST), 0, s, q);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             const int64_t blocks = ((int64_t)p.M * p.N / 4 + kBlock - 1) / kBlock;
@@ -569,7 +581,9 @@ hipError_t launch_mt(const SkinnyParams& p, hipStream_t s) {
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((skinny_kernel<MT, EPI>), dim3(tiles, p.nsplit, p.layers), dim3(kST), 0, s, p);
+    SkinnyParams q = p;
+    q.stamps = skinny_trace<MT, EPI>(p, tiles);
+    hipLaunchKernelGGL((skinny_kernel<MT, EPI>), dim3(tiles, p.nsplit, p.layers), dim3(kST), 0, s, q);
     return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ struct SkinnyParams {
     float* part_val;      // [M][nblocks]
     int32_t* part_idx;
     int nblocks;          // skinny_tiles(SK_ARGMAX, N)
-    uint64_t* stamps;     // SK_ARGMAX, optional: wall clock at start and end of each workgroup [nblocks][2]
+    uint64_t* stamps;     // set by the launcher when the launch is traced: (start, end) wall clock per workgroup
     // SK_KV: columns [0, hkv*hd) are keys, [hkv*hd, 2*hkv*hd) values (bf16 caches). Row
     // r = row_base + m belongs to the sequence b with row_offsets[b] <= r < row_offsets[b+1]
     // and goes to cache position len[b] + (r - row_offsets[b]) when that index is below

@@ -33,15 +33,17 @@ import os
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# sources that decide the GEMV kernels' code and launch shapes
-KERNEL_SOURCES = ("csrc/gemv.hip", "csrc/gemv.hpp", "csrc/common.hpp", "csrc/dflash_api.cpp")
+def kernel_sources():
+    """Every source that decides the kernels' code and launch shapes."""
+    d = os.path.join(HERE, "csrc")
+    return sorted(os.path.join("csrc", f) for f in os.listdir(d) if f.endswith((".hip", ".hpp", ".cpp")))
 
 
 def kernel_sources_hash():
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in kernel_sources():
         with open(os.path.join(HERE, rel), "rb") as f:
-            h.update(f.read())
+            h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

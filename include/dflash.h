@@ -161,19 +161,42 @@ const char* dflash_status_string(int status);
  * that the accelerated path really ran. */
 uint64_t dflash_invocations(void);
 
-/* Instrumentation. With `stamps` non-NULL (device memory of `capacity`
- * uint64 entries), every later LM-head argmax -- inside dflash_draft_forward
- * and dflash_lm_head_argmax, captured graphs included (the pointer is a kernel
- * argument, so each replay of a captured launch rewrites the same entries) --
- * makes each head workgroup w write the device wall clock at its start to
- * stamps[2w] and at its end to stamps[2w + 1]; the kernel's duration is
- * max(end) - min(start) in ticks of dflash_wall_clock_hz(). A head over M
- * activation rows runs as C launches of W workgroups each, with
- * W = dflash_lm_head_workgroups(V, H, dtype, M, y_dtype, &C); launch c writes
- * entries [2cW, 2(c+1)W). When capacity is below 2WC nothing is written. NULL
- * switches it off. Process-wide setting: concurrent LM heads would share the
- * buffer. */
-void dflash_trace_head_stamps(uint64_t* stamps, int32_t capacity);
+/* Instrumentation: launch tracing. Between dflash_trace_begin and
+ * dflash_trace_end, every launch of the chosen kinds (a bit mask) makes each of
+ * its workgroups write the device wall clock at its start and end into the
+ * stamp buffer: launch j takes entries [offset_j, offset_j + 2 W_j) of
+ * `stamps` (device memory of `capacity` uint64 entries), workgroup w writing
+ * its start to entry offset_j + 2w and its end to offset_j + 2w + 1, in ticks
+ * of dflash_wall_clock_hz(); the launch's duration is max(end) - min(start).
+ * The stamp pointer is a kernel argument, so launches captured into a graph
+ * while tracing is on rewrite their entries on every replay. Launches beyond
+ * the capacity are not traced. Process-wide setting: concurrent calls share
+ * the buffer. Tracing changes no result. */
+enum { DFLASH_TRACE_LM_HEAD = 1,      /* LM-head argmax projections                 */
+       DFLASH_TRACE_ATTENTION = 2,    /* block attention (not the partial merge)    */
+       DFLASH_TRACE_PROJECTIONS = 4   /* every other projection launch: context
+                                         projection, K/V append, block init, layer
+                                         and out projections                        */ };
+typedef struct {
+    char    kernel[64];      /* kernel name with its template arguments, e.g.
+                                "skinny_kernel<7, 5>"                              */
+    int32_t kind;            /* one DFLASH_TRACE_* bit                              */
+    int32_t workgroups;      /* W: stamp pairs the launch writes                    */
+    int64_t offset;          /* first stamp entry of the launch                     */
+    double  bytes;           /* algorithmic HBM bytes known on the host: weights,
+                                activation rows and outputs (attention: Q, the
+                                block's keys and values, and O)                    */
+    double  ctx_row_bytes;   /* attention: bytes per held context row (keys and
+                                values), which the caller multiplies by the held
+                                row count (it lives on the device); else 0          */
+} dflash_trace_record;
+
+/* Start tracing the launches of `kinds` into `stamps`; NULL or capacity 0 switches tracing off. */
+void dflash_trace_begin(int32_t kinds, uint64_t* stamps, int64_t capacity);
+/* Stop tracing; copy the records of the traced launches (in enqueue order, at
+ * most `capacity` of them) to `records` (host memory) and return how many
+ * launches were traced. */
+int32_t dflash_trace_end(dflash_trace_record* records, int32_t capacity);
 
 /* Launch shape of the LM-head argmax over M rows of activations in y_dtype
  * (DFLASH_F32 / DFLASH_BF16) against a V x H head of weight format dtype
