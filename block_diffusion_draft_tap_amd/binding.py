@@ -26,7 +26,8 @@ EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "df
            "dflash_context_project", "dflash_ctx_kv_append", "dflash_draft_layer", "dflash_draft_forward",
            "dflash_lm_head_argmax", "dflash_lm_head_workspace_bytes", "dflash_verify_greedy",
            "dflash_verify_workspace_bytes", "dflash_kv_prefill_workspace_bytes", "dflash_trace_begin",
-           "dflash_trace_end", "dflash_lm_head_workgroups", "dflash_wall_clock_hz"]
+           "dflash_trace_end", "dflash_lm_head_workgroups", "dflash_wall_clock_hz", "dflash_verify_greedy_noalloc",
+           "dflash_verify_noalloc_max_bytes"]
 DFLASH_TRACE_LM_HEAD, DFLASH_TRACE_ATTENTION, DFLASH_TRACE_PROJECTIONS = 1, 2, 4
 
 
@@ -100,6 +101,10 @@ def _load():
     lib.dflash_verify_greedy.restype = ctypes.c_int
     lib.dflash_verify_workspace_bytes.argtypes = [I32, I32, I32]
     lib.dflash_verify_workspace_bytes.restype = SZ
+    lib.dflash_verify_greedy_noalloc.argtypes = [VP, VP, I32, I32, I32, VP, VP, VP, VP, VP]
+    lib.dflash_verify_greedy_noalloc.restype = ctypes.c_int
+    lib.dflash_verify_noalloc_max_bytes.argtypes = []
+    lib.dflash_verify_noalloc_max_bytes.restype = SZ
     lib.dflash_trace_begin.argtypes = [I32, VP, ctypes.c_int64]
     lib.dflash_trace_begin.restype = None
     lib.dflash_trace_end.argtypes = [P(dflash_trace_record), I32]
@@ -350,6 +355,13 @@ def dflash_verify_greedy(target_logits, draft_ids, accepted, committed, ids, ws,
     return lib.dflash_verify_greedy(_ptr(target_logits), _ptr(draft_ids), B, W - 1, V, _ptr(accepted),
                                     _ptr(committed), _ptr(ids), _ptr(next_anchor), _ptr(ws), ws.numel(),
                                     _stream(stream))
+
+
+def dflash_verify_greedy_noalloc(target_logits, draft_ids, accepted, committed, ids, next_anchor=None,
+                                 stream=None):
+    B, W, V = target_logits.shape
+    return lib.dflash_verify_greedy_noalloc(_ptr(target_logits), _ptr(draft_ids), B, W - 1, V, _ptr(accepted),
+                                            _ptr(committed), _ptr(ids), _ptr(next_anchor), _stream(stream))
 
 
 def verify_workspace(B, gamma, V, device="cuda"):

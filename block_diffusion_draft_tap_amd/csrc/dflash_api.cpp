@@ -18,6 +18,11 @@
 
 using namespace dfl;
 
+namespace dfl {
+int api_gate();
+void api_count_invocation();
+}  // namespace dfl
+
 
 namespace {
 
@@ -839,6 +844,9 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
 }
 
 }  // namespace
+
+int dfl::api_gate() { return gate(); }
+void dfl::api_count_invocation() { g_invocations++; }
 
 uint64_t* dfl::trace_launch(int kind, const char* name, int64_t workgroups, double bytes, double ctx_row_bytes) {
     static_assert(TRACE_LM_HEAD == DFLASH_TRACE_LM_HEAD && TRACE_ATTENTION == DFLASH_TRACE_ATTENTION &&

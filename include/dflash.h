@@ -311,6 +311,20 @@ int dflash_verify_greedy(const float* target_logits, const int32_t* draft_ids, i
                          size_t ws_bytes, void* stream);
 size_t dflash_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V);
 
+/* For callers that cannot allocate (code under HIP graph capture, serving
+ * loops or harnesses that forbid hipMalloc): dflash_verify_greedy without a
+ * workspace argument. Same arguments, outputs and checks otherwise. Its
+ * partial results live in a device array the library holds, one per device,
+ * of dflash_verify_noalloc_max_bytes() bytes (1 MiB) from the library's load to
+ * the end of the process; a request whose dflash_verify_workspace_bytes(B,
+ * gamma, V) exceeds it returns DFLASH_ENOSPC before anything is enqueued. The
+ * call allocates nothing. Calls that overlap on one device share that array and
+ * race; order them on one stream. */
+int dflash_verify_greedy_noalloc(const float* target_logits, const int32_t* draft_ids, int32_t B, int32_t gamma,
+                                 int32_t V, int32_t* accepted, int32_t* committed, int32_t* ids,
+                                 int32_t* next_anchor, void* stream);
+size_t dflash_verify_noalloc_max_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -162,6 +162,16 @@ def test_verify_and_head_validation():
     assert lib.dflash_verify_greedy(P, P, 1, 7, 100, P, P, P, None, P, 4, None) == bd.DFLASH_ENOSPC
     assert lib.dflash_verify_greedy(P + 4, P, 1, 7, 100, P, P, P, None, P, 1 << 20, None) == bd.DFLASH_DECLINED
     assert lib.dflash_verify_workspace_bytes(1, 7, 151936) > 0
+    # the variant without a workspace: the same checks, and requests beyond its fixed
+    # scratch are refused before any enqueue
+    mx = lib.dflash_verify_noalloc_max_bytes()
+    assert mx == 1 << 20
+    assert lib.dflash_verify_greedy_noalloc(None, P, 1, 7, 100, P, P, P, None, None) == bd.DFLASH_EINVAL
+    assert lib.dflash_verify_greedy_noalloc(P, P, 1, 70, 100, P, P, P, None, None) == bd.DFLASH_DECLINED
+    assert lib.dflash_verify_greedy_noalloc(P + 4, P, 1, 7, 100, P, P, P, None, None) == bd.DFLASH_DECLINED
+    big_b = 4000                                           # 4000 x 8 rows x 38 splits x 8 B > 1 MiB
+    assert lib.dflash_verify_workspace_bytes(big_b, 7, 151936) > mx
+    assert lib.dflash_verify_greedy_noalloc(P, P, big_b, 7, 151936, P, P, P, None, None) == bd.DFLASH_ENOSPC
     w = bd.dflash_weight(dtype=bd.DFLASH_BF16, rows=1000, cols=256, data=P, scales=None, biases=None)
     assert lib.dflash_lm_head_argmax(ctypes.byref(w), P, bd.DFLASH_BF16, 5, P, None, P, 8, None) == bd.DFLASH_ENOSPC
     assert lib.dflash_lm_head_argmax(ctypes.byref(w), P, 9, 5, P, None, P, 1 << 20, None) == bd.DFLASH_EINVAL
