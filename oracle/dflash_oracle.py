@@ -26,6 +26,11 @@ Plain numpy in float64, written from the pages' definition of the method:
     embedding dtype, scored by the borrowed target LM head; forwardRows takes
     the greedy argmax of each row (row k proposes the (k+1)-th token after
     the anchor).
+  * #markov, #confidence and the greedy loop of forwardRows (page 3): the
+    DSpark sequential head adds w1[previous token] w2 to each block row's base
+    logits before the argmax, one row after the other; the confidence head is
+    sigmoid([block row; w1[previous]] conf.w + conf.b), and Alg 1 cuts a row's
+    draft where it falls below the step's threshold.
   * Greedy verification (page "Inco Hacks Native: DFlash 2 Speculation",
     section 3, log lines "accepted=7 committed=8" and "accepted=5
     committed=6" for block 8): accepted = longest prefix of drafts equal to
@@ -330,7 +335,7 @@ def argmax_lowest(x):
 # greedy verification
 
 
-def verify_greedy(target_logits, draft_ids):
+def verify_greedy(target_logits, draft_ids, lengths=None):
     """target_logits [B, gamma+1, V], draft_ids [B, gamma] ->
     accepted [B], committed [B], ids [B, gamma+1] (-1 padded), next anchor [B].
 
@@ -338,13 +343,15 @@ def verify_greedy(target_logits, draft_ids):
     against row k; accepted is the longest agreeing prefix; the committed
     tokens are t[b, 0..accepted] (the verified drafts plus the target's own
     next token), so committed = accepted + 1, and t[b, accepted] is the next
-    anchor."""
+    anchor. With lengths [B] (a confidence-pruned block, page 3's Alg 1: only
+    the first lengths[b] drafts are proposed) the prefix stops there too."""
     t = argmax_lowest(target_logits)
     B, G = draft_ids.shape
     accepted = np.zeros(B, dtype=np.int32)
     for b in range(B):
+        limit = G if lengths is None else int(lengths[b])
         a = 0
-        while a < G and int(draft_ids[b, a]) == int(t[b, a]):
+        while a < limit and int(draft_ids[b, a]) == int(t[b, a]):
             a += 1
         accepted[b] = a
     committed = accepted + 1
@@ -353,6 +360,89 @@ def verify_greedy(target_logits, draft_ids):
         ids[b, : committed[b]] = t[b, : committed[b]]
     nxt = t[np.arange(B), accepted].astype(np.int32)
     return accepted, committed.astype(np.int32), ids, nxt
+
+
+# ----------------------------------------------------------------------------
+# DSpark sequential head, confidence head and confidence-scheduled pruning
+
+
+def block_rows(H_d, g_out, eps, faithful):
+    """The backbone's output rows, RMSNorm(H_d; out_norm) (page 3, #backbone:
+    `block`); rounded to bf16 in faithful mode, where they are the out
+    projection's input."""
+    return _r(rmsnorm(H_d, dense(g_out), eps), faithful)
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def dspark_greedy(base, anchors, w1, w2, conf_w, conf_b, block, thresholds=None, min_conf=None):
+    """Greedy drafting with the Markov sequential head and the confidence head
+    (page 3, #markov, #confidence and the greedy loop of forwardRows).
+
+    base [B, gamma, V]: the base logits of the block rows (#baseLogits);
+    anchors [B]; w1 = markov.w1 [V, r]; w2 = markov.w2 [r, V];
+    conf_w = conf.w [d + r, 1]; conf_b = conf.b [1]; block [B, gamma, d].
+
+    Step k = 0 .. gamma-1, starting from previous = the anchors:
+      e1 = w1[previous]                                  [B, r]
+      scores = base[:, k] + e1 w2                        [B, V]
+      token_k = argmax(scores), lowest index on ties; previous = token_k
+      conf_k = sigmoid([block[:, k]; e1] conf_w + conf_b)
+    Pruning (Alg 1, pages' single-user form): for k >= 1, with threshold
+    thresholds[k] (else min_conf), a row whose conf_k falls below it is cut to
+    length k; the first cut of a row stands, and position 0 is always kept.
+    The page stops the loop once every row is cut; the tokens of the kept
+    positions do not depend on that, and here every step runs.
+
+    Returns tokens [B, gamma], conf [B, gamma], lengths [B] and the scores
+    [B, gamma, V] of every step."""
+    base = np.asarray(base, dtype=np.float64)
+    B, G, V = base.shape
+    W1, W2 = dense(w1), dense(w2)
+    cw = dense(conf_w).reshape(-1)
+    cb = float(dense(conf_b).reshape(-1)[0])
+    pruning = thresholds is not None or min_conf is not None
+    previous = np.asarray(anchors, dtype=np.int64)
+    tokens = np.zeros((B, G), dtype=np.int32)
+    conf = np.zeros((B, G))
+    scores = np.zeros((B, G, V))
+    lengths = np.full(B, G, dtype=np.int32)
+    cut = np.zeros(B, dtype=bool)
+    for k in range(G):
+        e1 = W1[previous]
+        scores[:, k] = base[:, k] + e1 @ W2
+        tok = argmax_lowest(scores[:, k])
+        tokens[:, k] = tok
+        joined = np.concatenate([np.asarray(block[:, k], dtype=np.float64), e1], axis=1)
+        conf[:, k] = sigmoid(joined @ cw + cb)
+        if pruning and k > 0:
+            threshold = thresholds[k] if thresholds is not None else min_conf
+            newly = (~cut) & (conf[:, k] < threshold)
+            lengths[newly] = k
+            cut |= newly
+        previous = tok.astype(np.int64)
+    return tokens, conf, lengths, scores
+
+
+def dspark_forward(weights, dims, ctx, anchor_ids, faithful, thresholds=None, min_conf=None):
+    """forwardRows with the DSpark heads over the retained context: the
+    backbone (block init, every layer, out_norm), the base logits through the
+    borrowed head, then dspark_greedy. Returns (tokens, conf, lengths, extra)
+    with extra = {"block", "Y", "base", "scores"}."""
+    H = block_init(anchor_ids, weights["E_in"], weights["tok_proj"], weights["mask_emb"],
+                   weights["block_pos"], dims.gamma, faithful)
+    for i in range(dims.nl):
+        H = draft_layer(H, ctx, i, weights, dims, faithful)
+    blk = block_rows(H, weights["out_norm"], dims.eps, faithful)
+    Y = _r(blk @ dense(weights["out_proj"]).T, faithful)
+    B, G = H.shape[0], dims.gamma
+    _, _, logits = lm_head_argmax(Y.reshape(B * G, -1), weights["E_out"], want_logits=True)
+    base = logits.reshape(B, G, -1)
+    tokens, conf, lengths, scores = dspark_greedy(base, anchor_ids, weights["markov.w1"], weights["markov.w2"],
+                                                  weights["conf.w"], weights["conf.b"], blk, thresholds, min_conf)
+    return tokens, conf, lengths, {"block": blk, "Y": Y, "base": base, "scores": scores}
 
 
 # ----------------------------------------------------------------------------

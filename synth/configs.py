@@ -50,6 +50,7 @@ class Dims:
     wdtype: str     # weight format
     eps: float = 1e-6
     L_max: Optional[int] = None   # ragged batches: lengths drawn from [L, L_max]
+    r: int = 0                    # rank of the DSpark sequential (Markov) head; 0 = no head
 
     @property
     def qkv_rows(self) -> int:

@@ -161,11 +161,22 @@ def weight_names(dims: Dims):
     for i in range(dims.nl):
         names += [f"bb.{i}.{w}" for w in ("attn_norm", "q", "k", "v", "o", "ff_norm", "gate", "up", "down")]
     names += ["W_c", "ctx_norm", "tok_proj", "mask_emb", "block_pos", "out_norm", "out_proj", "E_in", "E_out"]
+    if dims.r > 0:
+        names += HEAD_NAMES
     return names
+
+
+# the DSpark sequential head and confidence head (page 3 names and shapes: markov.w1 [V, r],
+# markov.w2 [r, V], conf.w [d + r, 1], conf.b [1]); stored bf16 (f32 for f32 models), never 4-bit
+HEAD_NAMES = ["markov.w1", "markov.w2", "conf.w", "conf.b"]
 
 
 def weight_shape(dims: Dims, name: str):
     d, H, F = dims.d, dims.H, dims.F
+    head = {"markov.w1": (dims.V, dims.r), "markov.w2": (dims.r, dims.V), "conf.w": (d + dims.r, 1),
+            "conf.b": (1,)}
+    if name in head:
+        return head[name]
     qw, kw = dims.hq * dims.hd, dims.kv_width
     leaf = name.split(".")[-1]
     table = {
@@ -210,7 +221,7 @@ def _int4_matrix(seed: int, name: str, shape):
             "biases": bias_bits.reshape(N, K // GROUP)}
 
 
-def make_weight(dims: Dims, name: str, seed: int = SEED_WEIGHTS, gains: str = "ones"):
+def make_weight(dims: Dims, name: str, seed: int = SEED_WEIGHTS, gains: str = "ones", std: float = 0.02):
     shape = weight_shape(dims, name)
     fp32 = dims.wdtype == WDTYPE_F32
     if is_gain(name):
@@ -222,18 +233,21 @@ def make_weight(dims: Dims, name: str, seed: int = SEED_WEIGHTS, gains: str = "o
     if is_matrix(name) and dims.wdtype == WDTYPE_INT4G64:
         return _int4_matrix(seed, name, shape)
     count = int(np.prod(shape))
-    return scaled_normals_stored(seed, name, count, 0.02, fp32).reshape(shape)
+    return scaled_normals_stored(seed, name, count, std, fp32).reshape(shape)
 
 
 class Model(dict):
-    """Lazily generated weight set: model[name] generates on first access."""
+    """Lazily generated weight set: model[name] generates on first access.
+    stds overrides the N(0, 0.02) scale of chosen weights (e.g. a DSpark head
+    whose Markov bias competes with the base logits)."""
 
-    def __init__(self, dims: Dims, seed: int = SEED_WEIGHTS, gains: str = "ones"):
+    def __init__(self, dims: Dims, seed: int = SEED_WEIGHTS, gains: str = "ones", stds=None):
         super().__init__()
         self.dims, self.seed, self.gains = dims, seed, gains
+        self.stds = dict(stds or {})
 
     def __missing__(self, name):
-        w = make_weight(self.dims, name, self.seed, self.gains)
+        w = make_weight(self.dims, name, self.seed, self.gains, self.stds.get(name, 0.02))
         self[name] = w
         return w
 

@@ -619,3 +619,147 @@ def test_faithful_mode_is_close_to_pure():
     assert 1e-5 < r < 3e-2          # rounding is applied, and it is small
     # faithful K/V caches hold bf16 values exactly
     assert np.array_equal(O.bf16(ctx_f.k[0][0]), ctx_f.k[0][0])
+
+
+# ----------------------------------------------------------------------------
+# DSpark sequential head, confidence head and pruning (page 3: #markov, #confidence,
+# the greedy loop of forwardRows, Alg 1)
+
+
+def _dspark_model(r=16, w2_std=0.02, **kw):
+    dims = scaled(TINY, r=r, **kw)
+    return dims, gen.Model(dims, gains="random", stds={"markov.w2": w2_std}).materialise()
+
+
+def test_dspark_w2_zero_reduces_to_the_parallel_drafter():
+    """markov.w2 starts at zero (page 3's initialisation: the drafter then is
+    plain parallel DFlash): every step's scores are the base logits, so the
+    tokens are the plain forward's greedy ids, whatever w1 and the anchors."""
+    dims, w = _dspark_model()
+    w["markov.w2"] = np.zeros_like(w["markov.w2"])
+    ctx, _, _ = tiny_context(dims, w, 12)
+    anchors = np.array([5], np.int32)
+    ids, ex = O.draft_forward(w, dims, ctx, anchors, False, return_all=True)
+    tok, conf, lengths, extra = O.dspark_forward(w, dims, ctx, anchors, False)
+    assert np.array_equal(tok, ids)
+    assert rel(extra["base"].reshape(-1, dims.V), ex["logits"]) < 1e-14
+    assert np.array_equal(lengths, [dims.gamma]) and np.all((conf > 0) & (conf < 1))
+
+
+def _planted_chain(B=3, G=6, V=40, r=8, big=50.0, seed=0):
+    """Base logits of small noise, w1 one-hot (row v = e_{v mod r}), w2 row j
+    one-hot at succ[j] scaled by `big`: from token p the Markov bias favours
+    succ[p mod r] by `big`, so the greedy chain is p -> succ[p mod r]."""
+    rng = np.random.default_rng(seed)
+    base = rng.standard_normal((B, G, V)) * 0.1
+    w1 = np.zeros((V, r))
+    w1[np.arange(V), np.arange(V) % r] = 1.0
+    succ = rng.permutation(V)[:r]
+    w2 = np.zeros((r, V))
+    w2[np.arange(r), succ] = big
+    return base, w1, w2, succ
+
+
+def test_dspark_follows_a_planted_markov_chain():
+    B, G, V, r, d = 3, 6, 40, 8, 5
+    base, w1, w2, succ = _planted_chain(B, G, V, r)
+    anchors = np.array([3, 17, 38])
+    cw, cb = np.zeros((d + r, 1)), np.zeros(1)
+    block = np.zeros((B, G, d))
+    tok, conf, lengths, scores = O.dspark_greedy(base, anchors, w1, w2, cw, cb, block)
+    for b in range(B):
+        p = anchors[b]
+        for k in range(G):
+            p = succ[p % r]
+            assert tok[b, k] == p, (b, k)
+    assert np.allclose(conf, 0.5) and np.array_equal(lengths, [G] * B)
+
+    # planted mistake: a parallel head that conditions every step on the anchor
+    # (no sequential dependence) proposes succ[anchor mod r] at every position
+    def parallel(base, anchors, w1, w2):
+        bias = w1[anchors] @ w2
+        return np.argmax(base + bias[:, None, :], axis=-1)
+    assert not np.array_equal(parallel(base, anchors, w1, w2), tok)
+
+
+def test_dspark_argmax_ties_go_to_the_lowest_index():
+    B, G, V, r, d = 1, 2, 12, 4, 3
+    base = np.zeros((B, G, V))
+    base[0, 0, [7, 2, 9]] = 1.0                 # a three-way tie at step 0 -> token 2
+    w1 = np.zeros((V, r))
+    w2 = np.zeros((r, V))
+    tok, _, _, _ = O.dspark_greedy(base, np.array([0]), w1, w2, np.zeros((d + r, 1)), np.zeros(1),
+                                   np.zeros((B, G, d)))
+    assert tok[0, 0] == 2 and tok[0, 1] == 0     # step 1: all scores equal -> 0
+
+
+def test_confidence_closed_forms():
+    """conf_k = sigmoid([block_k; w1[previous]] conf.w + conf.b): with conf.w
+    zero it is sigmoid(conf.b); with weight only on e1 coordinate j and
+    one-hot e1 it is sigmoid(w_j + b) for previous tokens in class j; with
+    weight only on block coordinate c it is sigmoid(block_k[c] w_c + b)."""
+    B, G, V, r, d = 2, 5, 40, 8, 6
+    base, w1, w2, succ = _planted_chain(B, G, V, r)
+    anchors = np.array([3, 12])
+    rng = np.random.default_rng(4)
+    block = rng.standard_normal((B, G, d))
+    b0 = 0.3
+    _, conf, _, _ = O.dspark_greedy(base, anchors, w1, w2, np.zeros((d + r, 1)), np.array([b0]), block)
+    assert np.allclose(conf, 1.0 / (1.0 + math.exp(-b0)), rtol=0, atol=1e-15)
+    cw = np.zeros((d + r, 1))
+    cw[d + 5, 0] = 2.0
+    tok, conf, _, _ = O.dspark_greedy(base, anchors, w1, w2, cw, np.array([b0]), block)
+    prev = np.concatenate([anchors[:, None], tok[:, :-1]], axis=1)     # the token each step conditions on
+    want = np.where(prev % r == 5, 1.0 / (1.0 + math.exp(-(2.0 + b0))), 1.0 / (1.0 + math.exp(-b0)))
+    assert np.allclose(conf, want, rtol=0, atol=1e-15)
+    cw = np.zeros((d + r, 1))
+    cw[2, 0] = -1.5
+    _, conf, _, _ = O.dspark_greedy(base, anchors, w1, w2, cw, np.array([b0]), block)
+    assert np.allclose(conf, 1.0 / (1.0 + np.exp(-(block[:, :, 2] * -1.5 + b0))), rtol=0, atol=1e-15)
+
+
+def test_alg1_pruning_cuts_at_the_first_low_confidence_step():
+    """Alg 1: position 0 is always kept; the first step k >= 1 whose confidence
+    is below thresholds[k] (or min_conf) cuts the row to length k, and a later
+    confident step does not undo the cut; without thresholds nothing is cut."""
+    B, G, V, r, d = 4, 6, 40, 8, 6
+    base, w1, w2, succ = _planted_chain(B, G, V, r)
+    anchors = np.array([1, 2, 3, 4])
+    block = np.zeros((B, G, d))
+    # confidence by step through the block rows: conf_k = sigmoid(block[b, k, 0])
+    cw = np.zeros((d + r, 1))
+    cw[0, 0] = 1.0
+    logit = np.array([[5, 5, 5, 5, 5, 5],
+                      [5, -5, 5, 5, 5, 5],       # cut at 1
+                      [-5, 5, 5, -5, 5, -5],     # position 0 is kept whatever its confidence; cut at 3
+                      [5, 5, 5, 5, 5, -5]], float)   # cut at the last step
+    block[:, :, 0] = logit
+    run = lambda **kw: O.dspark_greedy(base, anchors, w1, w2, cw, np.zeros(1), block, **kw)
+    _, conf, lengths, _ = run(min_conf=0.5)
+    assert list(lengths) == [6, 1, 3, 5]
+    _, _, lengths, _ = run()
+    assert list(lengths) == [6, 6, 6, 6]
+    _, _, lengths, _ = run(thresholds=[2.0] * G)       # every step below: cut at 1, never at 0
+    assert list(lengths) == [1, 1, 1, 1]
+    thr = [0.0, 0.0, 0.0, 0.999, 0.0, 0.0]            # per-step thresholds: only step 3 can cut
+    _, _, lengths, _ = run(thresholds=thr)
+    assert list(lengths) == [3, 3, 3, 3]
+    tok_all, _, _, _ = run()
+    tok_cut, _, _, _ = run(min_conf=0.5)
+    assert np.array_equal(tok_all, tok_cut)           # pruning changes the lengths, never the tokens
+
+
+@pytest.mark.parametrize("G", [1, 4, 7])
+def test_verify_with_lengths_exhaustive(G):
+    """A pruned block of length l proposes only its first l drafts: accepted
+    is the agreeing prefix capped at l, committed = accepted + 1."""
+    rng = np.random.default_rng(13)
+    V = 50
+    for bits in range(2 ** G):
+        pattern = [(bits >> k) & 1 == 1 for k in range(G)]
+        prefix = next((k for k in range(G) if not pattern[k]), G)
+        T, draft, t = _planted_verify_inputs(G, V, pattern, rng)
+        for l in range(1, G + 1):
+            acc, com, ids, nxt = O.verify_greedy(T, draft, lengths=np.array([l]))
+            assert acc[0] == min(prefix, l) and com[0] == acc[0] + 1
+            assert nxt[0] == t[acc[0]] and list(ids[0, :acc[0] + 1]) == list(t[:acc[0] + 1])
