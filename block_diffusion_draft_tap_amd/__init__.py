@@ -10,7 +10,8 @@ _BINDING_NAMES = (
     "DeviceModel", "KVCache", "Weight", "workspace", "lm_head_workspace", "verify_workspace", "kv_prefill_workspace",
     "dflash_query", "dflash_context_project", "dflash_ctx_kv_append", "dflash_draft_layer",
     "dflash_draft_forward", "dflash_lm_head_argmax", "dflash_verify_greedy", "dflash_invocations",
-    "dflash_trace_begin", "dflash_trace_end", "check", "DflashError",
+    "dflash_trace_begin", "dflash_trace_end", "DsparkHead", "dspark_workspace",
+    "dflash_draft_forward_dspark", "dflash_verify_greedy_lengths", "check", "DflashError",
 )
 
 

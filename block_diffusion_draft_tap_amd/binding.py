@@ -27,7 +27,8 @@ EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "df
            "dflash_lm_head_argmax", "dflash_lm_head_workspace_bytes", "dflash_verify_greedy",
            "dflash_verify_workspace_bytes", "dflash_kv_prefill_workspace_bytes", "dflash_trace_begin",
            "dflash_trace_end", "dflash_lm_head_workgroups", "dflash_wall_clock_hz", "dflash_verify_greedy_noalloc",
-           "dflash_verify_noalloc_max_bytes"]
+           "dflash_verify_noalloc_max_bytes", "dflash_dspark_workspace_bytes", "dflash_draft_forward_dspark",
+           "dflash_verify_greedy_lengths"]
 DFLASH_TRACE_LM_HEAD, DFLASH_TRACE_ATTENTION, DFLASH_TRACE_PROJECTIONS = 1, 2, 4
 
 
@@ -62,6 +63,11 @@ class dflash_model(ctypes.Structure):
 class dflash_kv(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("len", ctypes.c_void_p),
                 ("B", ctypes.c_int32), ("cap", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class dflash_dspark_head(ctypes.Structure):
+    _fields_ = [("r", ctypes.c_int32), ("w1", ctypes.c_void_p), ("w2t", ctypes.c_void_p),
+                ("conf_w", ctypes.c_void_p), ("conf_b", ctypes.c_void_p)]
 
 
 class dflash_trace_record(ctypes.Structure):
@@ -103,6 +109,13 @@ def _load():
     lib.dflash_verify_workspace_bytes.restype = SZ
     lib.dflash_verify_greedy_noalloc.argtypes = [VP, VP, I32, I32, I32, VP, VP, VP, VP, VP]
     lib.dflash_verify_greedy_noalloc.restype = ctypes.c_int
+    lib.dflash_dspark_workspace_bytes.argtypes = [P(dflash_dims), I32, I32, I32]
+    lib.dflash_dspark_workspace_bytes.restype = SZ
+    lib.dflash_draft_forward_dspark.argtypes = [P(dflash_model), P(dflash_dspark_head), VP, P(dflash_kv), I32, VP,
+                                                ctypes.c_float, VP, VP, VP, VP, VP, SZ, VP]
+    lib.dflash_draft_forward_dspark.restype = ctypes.c_int
+    lib.dflash_verify_greedy_lengths.argtypes = [VP, VP, VP, I32, I32, I32, VP, VP, VP, VP, VP, SZ, VP]
+    lib.dflash_verify_greedy_lengths.restype = ctypes.c_int
     lib.dflash_verify_noalloc_max_bytes.argtypes = []
     lib.dflash_verify_noalloc_max_bytes.restype = SZ
     lib.dflash_trace_begin.argtypes = [I32, VP, ctypes.c_int64]
@@ -335,6 +348,48 @@ def dflash_lm_head_argmax(weight, y, ids, ws, max_logit=None, stream=None):
     ydt = DFLASH_F32 if y.dtype == torch.float32 else DFLASH_BF16
     return lib.dflash_lm_head_argmax(ctypes.byref(cw), _ptr(y), ydt, y.shape[0], _ptr(ids), _ptr(max_logit),
                                      _ptr(ws), ws.numel(), _stream(stream))
+
+
+class DsparkHead:
+    """The DSpark heads on the device: markov.w1 [V, r], markov.w2 [r, V]
+    (uploaded transposed, [V, r]), conf.w [d + r, 1], conf.b [1]; stored
+    arrays of the weights' storage format (bf16 bits, or float32 for f32
+    models)."""
+
+    def __init__(self, weights, device="cuda"):
+        w1 = weights["markov.w1"]
+        w2 = weights["markov.w2"]
+        self.r = int(np.asarray(w1).shape[1]) if not isinstance(w1, torch.Tensor) else int(w1.shape[1])
+        self.w1 = _to_dev(w1, device)
+        w2t = w2.t().contiguous() if isinstance(w2, torch.Tensor) else np.ascontiguousarray(np.asarray(w2).T)
+        self.w2t = _to_dev(w2t, device)
+        self.conf_w = _to_dev(weights["conf.w"], device).reshape(-1).contiguous()
+        self.conf_b = _to_dev(weights["conf.b"], device).reshape(-1).contiguous()
+        self.c = dflash_dspark_head(r=self.r, w1=_ptr(self.w1), w2t=_ptr(self.w2t), conf_w=_ptr(self.conf_w),
+                                    conf_b=_ptr(self.conf_b))
+
+
+def dspark_workspace(dims, r, B, cap, device="cuda"):
+    n = lib.dflash_dspark_workspace_bytes(ctypes.byref(make_dims(dims)), r, B, cap)
+    if n == 0:
+        raise DflashError("invalid dims for a DSpark workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def dflash_draft_forward_dspark(model, head, anchor_ids, kv, B, draft_ids, ws, thresholds=None, min_conf=0.0,
+                                conf=None, lengths=None, y_out=None, stream=None):
+    return lib.dflash_draft_forward_dspark(ctypes.byref(model.c), ctypes.byref(head.c), _ptr(anchor_ids),
+                                           ctypes.byref(kv.c), B, _ptr(thresholds), float(min_conf),
+                                           _ptr(draft_ids), _ptr(conf), _ptr(lengths), _ptr(y_out), _ptr(ws),
+                                           ws.numel(), _stream(stream))
+
+
+def dflash_verify_greedy_lengths(target_logits, draft_ids, lengths, accepted, committed, ids, ws, next_anchor=None,
+                                 stream=None):
+    B, W, V = target_logits.shape
+    return lib.dflash_verify_greedy_lengths(_ptr(target_logits), _ptr(draft_ids), _ptr(lengths), B, W - 1, V,
+                                            _ptr(accepted), _ptr(committed), _ptr(ids), _ptr(next_anchor),
+                                            _ptr(ws), ws.numel(), _stream(stream))
 
 
 def kv_prefill_workspace(dims, n, device="cuda"):

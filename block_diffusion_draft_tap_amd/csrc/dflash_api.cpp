@@ -2,6 +2,7 @@
 // the host, workspace layout, and the kernel sequence of each call.
 #include <atomic>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -470,6 +471,7 @@ hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStr
         if (epi == EPI_ARGMAX) {
             q.part_val = p.part_val + (int64_t)r0 * p.nblocks;
             q.part_idx = p.part_idx + (int64_t)r0 * p.nblocks;
+            if (p.base) q.base = p.base + (int64_t)r0 * p.base_ld;
         }
         const hipError_t e = launch_gemv(wtype, pro, epi, maxm, q, layers, s);
         if (e != hipSuccess) return e;
@@ -538,6 +540,7 @@ hipError_t skinny_rows(int epi, SkinnyParams p, int rows, hipStream_t s) {
         if (epi == SK_ARGMAX) {
             q.part_val = p.part_val + (int64_t)r0 * p.nblocks;
             q.part_idx = p.part_idx + (int64_t)r0 * p.nblocks;
+            if (p.base) q.base = p.base + (int64_t)r0 * p.base_ld;
         }
         const hipError_t e = launch_skinny(epi, q, s);
         if (e != hipSuccess) return e;
@@ -841,6 +844,199 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
     DFL_HIP(gemv_rows(wtype_of(E.dtype), PRO_TAPS, EPI_ARGMAX, p, rows, s));
     DFL_HIP(launch_argmax_merge(pv, pi, p.nblocks, rows, ids, maxl, s));
     return DFLASH_OK;
+}
+
+// block init and every layer: H_d in w.hd; *an_ready says whether w.an holds the out
+// projection's normalised rows
+int forward_backbone(const dflash_model* M, const int32_t* anchor_ids, const dflash_kv* kv, int B, const Ws& w,
+                     hipStream_t s, bool* an_ready) {
+    const dflash_dims& d = M->dims;
+    const int wt = wtype_of(d.wdtype);
+    const bool init_sk = w.skinny && d.wdtype == DFLASH_BF16 && M->embed_in.dtype == DFLASH_BF16 &&
+                         M->tok_proj.dtype == DFLASH_BF16 && B >= DFL_SKINNY_MIN_ROWS && d.H % kSkinnyK == 0 &&
+                         (int64_t)d.gamma * d.d >= d.H;
+    if (init_sk) {
+        // 16 or more sequences on matrix cores: the anchors' embeddings gathered into w.an
+        // (B rows of H; it holds B * gamma rows of d), their tok_proj product stored as row 0
+        // of each block, then the block positions added and the mask rows written
+        DFL_HIP(launch_gather_rows(static_cast<const uint16_t*>(M->embed_in.data), M->embed_in.rows, anchor_ids, B,
+                                   d.H, w.an, s));
+        SkinnyParams p = skinny_params(M->tok_proj, w.an, d.H, d.d, d.H, w.skp);
+        p.out = w.hd;
+        p.out_ld = (int64_t)d.gamma * d.d;
+        DFL_HIP(skinny_rows(SK_STORE, p, B, s));
+        DFL_HIP(launch_block_fill(w.hd, B, d.gamma, d.d, M->block_pos, M->mask_emb, 0, s));
+    } else {  // block rows: E_in[anchor] tok_proj^T + block_pos[0]; mask_emb[k-1] + block_pos[k]
+        GemvParams p = base_params(d);
+        p.w[0] = wptr(M->tok_proj);
+        p.N = d.d;
+        p.K = d.H;
+        p.rpw = rpw_for(p.N, d.wdtype);
+        p.ids = anchor_ids;
+        p.table = wptr(M->embed_in);
+        p.table_type = wtype_of(M->embed_in.dtype);
+        p.table_rows = M->embed_in.rows;
+        p.out = w.hd;
+        p.block_pos = M->block_pos;
+        p.mask_emb = M->mask_emb;
+        p.gamma = d.gamma;
+        p.seq_base = 0;
+        DFL_HIP(gemv_rows(wt, PRO_GATHER, EPI_BLOCKINIT, p, B, s));
+    }
+    *an_ready = false;  // w.an holds the next projection's normalised rows
+    for (int i = 0; i < d.nl; ++i)
+        DFL_TRY(run_layer(M, i, w.hd, kv, B, w, s, i + 1 < d.nl ? M->layers[i + 1].attn_norm : M->out_norm,
+                          an_ready));
+    return DFLASH_OK;
+}
+
+// Y = bf16(bf16(RMSNorm(H_d; out_norm)) out_proj^T) into y (fp32 throughout for fp32 models).
+// rows_in: the normalised rows already computed (bf16, fp32 for fp32 models), or null
+int forward_out(const dflash_model* M, int B, const Ws& w, hipStream_t s, bool an_ready, const void* rows_in,
+                float* y) {
+    const dflash_dims& d = M->dims;
+    const int wt = wtype_of(d.wdtype);
+    const int rows = B * d.gamma;
+    if (w.skinny) {
+        const uint16_t* a = static_cast<const uint16_t*>(rows_in);
+        if (!a) {
+            if (!an_ready) DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, w.an, s));
+            a = w.an;
+        }
+        SkinnyParams p = skinny_params(M->out_proj, a, d.d, d.H, d.d, w.skp);
+        p.out = y;
+        p.out_ld = d.H;
+        p.out_bf16 = 1;
+        DFL_HIP(skinny_rows(SK_STORE, p, rows, s));
+        return DFLASH_OK;
+    }
+    GemvParams p = base_params(d);
+    p.w[0] = wptr(M->out_proj);
+    p.N = d.H;
+    p.K = d.d;
+    p.rpw = rpw_for(p.N, d.wdtype);
+    p.x = w.hd;
+    p.x_ld = d.d;
+    p.gain[0] = M->out_norm;
+    p.out = y;
+    p.out_ld = d.H;
+    p.out_bf16 = d.wdtype == DFLASH_F32 ? 0 : 1;
+    if (rows_in) {
+        p.x = static_cast<const float*>(rows_in);  // bf16 rows unless fp32 model (src_f32)
+        DFL_HIP(gemv_plain(d, wt, EPI_STORE, p, rows, w.rsp, s));
+    } else if (prenorm(d)) {
+        if (!an_ready) DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, w.an, s));
+        p.x = reinterpret_cast<const float*>(w.an);
+        DFL_HIP(gemv_plain(d, wt, EPI_STORE, p, rows, w.rsp, s));
+    } else {
+        DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_STORE, p, rows, s));
+    }
+    return DFLASH_OK;
+}
+
+// the borrowed head's logits of `rows` rows, fp32 [rows, V] (matrix cores for 16 or more bf16
+// rows; part holds their split-K partial sums for a short vocabulary)
+int lm_head_store(const dflash_weight& E, const void* y, int y_f32, int rows, int H, int V, float* out, float* part,
+                  hipStream_t s) {
+    if (lm_head_skinny(E.dtype, y_f32, rows, H)) {
+        SkinnyParams p = skinny_params(E, static_cast<const uint16_t*>(y), H, V, H, part);
+        p.out = out;
+        p.out_ld = V;
+        p.out_bf16 = 0;
+        DFL_HIP(skinny_rows(SK_STORE, p, rows, s));
+        return DFLASH_OK;
+    }
+    GemvParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.w[0] = wptr(E);
+    p.N = V;
+    p.K = H;
+    p.rpw = rpw_for(V, E.dtype);
+    p.max_wgs = DFL_SMALL_WGS;
+    p.taps[0] = y;
+    p.tap_ld = H;
+    p.H = H;
+    p.src_f32 = y_f32;
+    p.out = out;
+    p.out_ld = V;
+    DFL_HIP(gemv_rows(wtype_of(E.dtype), PRO_TAPS, EPI_STORE, p, rows, s));
+    return DFLASH_OK;
+}
+
+// one Markov step: per row m < B, the (max, lowest index) over v of
+// base[m * base_ld + v] + e1[m] . w2t[v], as partials [B][*nblocks]
+int markov_argmax(const dflash_weight& w2t, const void* e1, int f32, int B, int r, int V, const float* base,
+                  int64_t base_ld, float* pv, int32_t* pi, int* nblocks, hipStream_t s) {
+    if (lm_head_skinny(w2t.dtype, f32, B, r)) {
+        SkinnyParams p = skinny_params(w2t, static_cast<const uint16_t*>(e1), r, V, r, nullptr);
+        p.part_val = pv;
+        p.part_idx = pi;
+        p.base = base;
+        p.base_ld = base_ld;
+        *nblocks = skinny_tiles(SK_ARGMAX, V);
+        DFL_HIP(skinny_rows(SK_ARGMAX, p, B, s));
+        return DFLASH_OK;
+    }
+    GemvParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.w[0] = wptr(w2t);
+    p.N = V;
+    p.K = r;
+    p.rpw = lm_rpw(wtype_of(w2t.dtype));
+    p.max_wgs = lm_wgs(wtype_of(w2t.dtype));
+    p.taps[0] = e1;
+    p.tap_ld = r;
+    p.H = r;
+    p.src_f32 = f32;
+    p.nblocks = lm_nblocks(V, r, wtype_of(w2t.dtype), B < 8 ? B : 8);
+    p.part_val = pv;
+    p.part_idx = pi;
+    p.base = base;
+    p.base_ld = base_ld;
+    *nblocks = p.nblocks;
+    DFL_HIP(gemv_rows(wtype_of(w2t.dtype), PRO_TAPS, EPI_ARGMAX, p, B, s));
+    return DFLASH_OK;
+}
+
+// workspace of the DSpark forward: the forward's own, then the base logits [B gamma][V] fp32,
+// the block rows [B gamma][d] (4 bytes each), the Markov operand rows [B][r] (4 bytes each),
+// the step partials [B][tiles] (value, index), pruning lengths [B] when the caller passes
+// none, and the split-K partials of a matrix-core head store over a short vocabulary
+struct Dspark {
+    Ws fw;
+    float* base;
+    void* hout;
+    void* e1;
+    float* pv;
+    int32_t* pi;
+    int32_t* lens;
+    float* skp;
+    size_t total;
+};
+Dspark dspark_layout(const dflash_dims& d, int r, int B, int cap, void* wsp) {
+    Dspark ds{};
+    char* c = static_cast<char*>(wsp);
+    ds.fw = ws_layout(d, B, cap, wsp);
+    size_t off = align_up(ds.fw.total);
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes);
+        return c ? c + o : nullptr;
+    };
+    const size_t rows = (size_t)B * d.gamma;
+    ds.base = reinterpret_cast<float*>(take(rows * d.V * 4));
+    ds.hout = take(rows * d.d * 4);
+    ds.e1 = take((size_t)B * r * 4);
+    const size_t nb = lm_tiles_max(d.V);
+    ds.pv = reinterpret_cast<float*>(take((size_t)B * nb * 4));
+    ds.pi = reinterpret_cast<int32_t*>(take((size_t)B * nb * 4));
+    ds.lens = reinterpret_cast<int32_t*>(take((size_t)B * 4));
+    int ns = 1, ks = 0;
+    skinny_split(SK_STORE, d.V, d.H, 1, &ns, &ks);
+    const size_t r0 = rows < (size_t)kSkinnyRows ? rows : (size_t)kSkinnyRows;
+    ds.skp = reinterpret_cast<float*>(take(ns > 1 ? (size_t)ns * r0 * d.V * 4 : 0));
+    ds.total = off;
+    return ds;
 }
 
 }  // namespace
@@ -1273,75 +1469,89 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
     if (!ws || ws_bytes < w.total) return DFLASH_ENOSPC;
     DFL_TRY(gate());
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int wt = wtype_of(d.wdtype);
-    const int rows = B * d.gamma;
-    const bool init_sk = w.skinny && d.wdtype == DFLASH_BF16 && M->embed_in.dtype == DFLASH_BF16 &&
-                         M->tok_proj.dtype == DFLASH_BF16 && B >= DFL_SKINNY_MIN_ROWS && d.H % kSkinnyK == 0 &&
-                         (int64_t)d.gamma * d.d >= d.H;
-    if (init_sk) {
-        // 16 or more sequences on matrix cores: the anchors' embeddings gathered into w.an
-        // (B rows of H; it holds B * gamma rows of d), their tok_proj product stored as row 0
-        // of each block, then the block positions added and the mask rows written
-        DFL_HIP(launch_gather_rows(static_cast<const uint16_t*>(M->embed_in.data), M->embed_in.rows, anchor_ids, B,
-                                   d.H, w.an, s));
-        SkinnyParams p = skinny_params(M->tok_proj, w.an, d.H, d.d, d.H, w.skp);
-        p.out = w.hd;
-        p.out_ld = (int64_t)d.gamma * d.d;
-        DFL_HIP(skinny_rows(SK_STORE, p, B, s));
-        DFL_HIP(launch_block_fill(w.hd, B, d.gamma, d.d, M->block_pos, M->mask_emb, 0, s));
-    } else {  // block rows: E_in[anchor] tok_proj^T + block_pos[0]; mask_emb[k-1] + block_pos[k]
-        GemvParams p = base_params(d);
-        p.w[0] = wptr(M->tok_proj);
-        p.N = d.d;
-        p.K = d.H;
-        p.rpw = rpw_for(p.N, d.wdtype);
-        p.ids = anchor_ids;
-        p.table = wptr(M->embed_in);
-        p.table_type = wtype_of(M->embed_in.dtype);
-        p.table_rows = M->embed_in.rows;
-        p.out = w.hd;
-        p.block_pos = M->block_pos;
-        p.mask_emb = M->mask_emb;
-        p.gamma = d.gamma;
-        p.seq_base = 0;
-        DFL_HIP(gemv_rows(wt, PRO_GATHER, EPI_BLOCKINIT, p, B, s));
-    }
-    bool an_ready = false;  // w.an holds the next projection's normalised rows
-    for (int i = 0; i < d.nl; ++i)
-        DFL_TRY(run_layer(M, i, w.hd, kv, B, w, s, i + 1 < d.nl ? M->layers[i + 1].attn_norm : M->out_norm,
-                          &an_ready));
-    // Y = bf16(bf16(RMSNorm(H; out_norm)) out_proj^T), written straight into y_out
-    // when the caller wants it (bf16 for bf16/int4 models, fp32 for fp32 models)
+    bool an_ready = false;
+    DFL_TRY(forward_backbone(M, anchor_ids, kv, B, w, s, &an_ready));
+    // Y written straight into y_out when the caller wants it (bf16 for bf16/int4 models,
+    // fp32 for fp32 models)
     float* y = y_out ? static_cast<float*>(y_out) : w.y;
-    if (w.skinny) {
-        if (!an_ready) DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, w.an, s));
-        SkinnyParams p = skinny_params(M->out_proj, w.an, d.d, d.H, d.d, w.skp);
-        p.out = y;
-        p.out_ld = d.H;
-        p.out_bf16 = 1;
-        DFL_HIP(skinny_rows(SK_STORE, p, rows, s));
-    } else {
-        GemvParams p = base_params(d);
-        p.w[0] = wptr(M->out_proj);
-        p.N = d.H;
-        p.K = d.d;
-        p.rpw = rpw_for(p.N, d.wdtype);
-        p.x = w.hd;
-        p.x_ld = d.d;
-        p.gain[0] = M->out_norm;
-        p.out = y;
-        p.out_ld = d.H;
-        p.out_bf16 = d.wdtype == DFLASH_F32 ? 0 : 1;
-        if (prenorm(d)) {
-            if (!an_ready) DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, w.an, s));
-            p.x = reinterpret_cast<const float*>(w.an);
-            DFL_HIP(gemv_plain(d, wt, EPI_STORE, p, rows, w.rsp, s));
-        } else {
-            DFL_HIP(gemv_rows(wt, PRO_NORM, EPI_STORE, p, rows, s));
-        }
-    }
-    DFL_TRY(lm_head(M->lm_head, y, d.wdtype == DFLASH_F32, rows, d.H, d.V, draft_ids, max_logit, w.lmv, w.lmi,
+    DFL_TRY(forward_out(M, B, w, s, an_ready, nullptr, y));
+    DFL_TRY(lm_head(M->lm_head, y, d.wdtype == DFLASH_F32, B * d.gamma, d.H, d.V, draft_ids, max_logit, w.lmv, w.lmi,
                     s));
+    g_invocations++;
+    return DFLASH_OK;
+}
+
+size_t dflash_dspark_workspace_bytes(const dflash_dims* dims, int32_t r, int32_t B, int32_t cap) {
+    if (check_dims(dims) == DFLASH_EINVAL || r <= 0 || B <= 0 || cap < 0) return 0;
+    return dspark_layout(*dims, r, B, cap, nullptr).total;
+}
+
+int dflash_draft_forward_dspark(const dflash_model* M, const dflash_dspark_head* head, const int32_t* anchor_ids,
+                                const dflash_kv* kv, int32_t B, const float* thresholds, float min_conf,
+                                int32_t* draft_ids, float* conf, int32_t* lengths, void* y_out, void* ws,
+                                size_t ws_bytes, void* stream) {
+    DFL_TRY(check_model(M));
+    const dflash_dims& d = M->dims;
+    if (!head || !anchor_ids || !draft_ids || B <= 0) return DFLASH_EINVAL;
+    if (head->r <= 0 || !head->w1 || !head->w2t || !head->conf_w || !head->conf_b) return DFLASH_EINVAL;
+    if (head->r % 8 || !aligned16(head->w1) || !aligned16(head->w2t)) return DFLASH_DECLINED;
+    if (std::isnan(min_conf)) return DFLASH_EINVAL;
+    DFL_TRY(check_kv(kv, d, B));
+    const Dspark ds = dspark_layout(d, head->r, B, kv->cap, ws);
+    if (!ws || ws_bytes < ds.total) return DFLASH_ENOSPC;
+    DFL_TRY(gate());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Ws& w = ds.fw;
+    const bool f32 = d.wdtype == DFLASH_F32;
+    const int rows = B * d.gamma;
+    bool an_ready = false;
+    DFL_TRY(forward_backbone(M, anchor_ids, kv, B, w, s, &an_ready));
+    // the block rows RMSNorm(H_d; out_norm) (page 3, #backbone), kept for the confidence head:
+    // bf16 for bf16/int4 models (the out projection's input), fp32 for fp32 models
+    if (f32)
+        DFL_HIP(launch_rownorm(w.hd, 1, 0, static_cast<float*>(ds.hout), rows, d.d, M->out_norm, 1, d.eps, s));
+    else
+        DFL_HIP(norm_rows(w.hd, rows, d.d, M->out_norm, d.eps, static_cast<uint16_t*>(ds.hout), s));
+    float* y = y_out ? static_cast<float*>(y_out) : w.y;
+    DFL_TRY(forward_out(M, B, w, s, false, ds.hout, y));
+    // base logits of every block row, fp32 (page 3, #baseLogits)
+    DFL_TRY(lm_head_store(M->lm_head, y, f32, rows, d.H, d.V, ds.base, ds.skp, s));
+    // the sequential loop: step k merges step k-1's argmax, gathers w1[previous] and scores
+    // base[:, k] + w1[previous] w2 over the vocabulary
+    dflash_weight w2t;
+    w2t.dtype = f32 ? DFLASH_F32 : DFLASH_BF16;
+    w2t.rows = d.V;
+    w2t.cols = head->r;
+    w2t.data = head->w2t;
+    w2t.scales = w2t.biases = nullptr;
+    DsparkStepParams sp;
+    std::memset(&sp, 0, sizeof(sp));
+    sp.gamma = d.gamma;
+    sp.B = B;
+    sp.V = d.V;
+    sp.r = head->r;
+    sp.d = d.d;
+    sp.f32 = f32;
+    sp.anchors = anchor_ids;
+    sp.part_val = ds.pv;
+    sp.part_idx = ds.pi;
+    sp.w1 = head->w1;
+    sp.hout = ds.hout;
+    sp.conf_w = head->conf_w;
+    sp.conf_b = head->conf_b;
+    sp.thresholds = thresholds;
+    sp.min_conf = min_conf;
+    sp.e1 = ds.e1;
+    sp.ids = draft_ids;
+    sp.conf = conf;
+    sp.lengths = lengths ? lengths : ds.lens;
+    for (int k = 0; k <= d.gamma; ++k) {
+        sp.step = k;
+        DFL_HIP(launch_dspark_step(sp, s));
+        if (k == d.gamma) break;
+        DFL_TRY(markov_argmax(w2t, ds.e1, f32, B, head->r, d.V, ds.base + (int64_t)k * d.V, (int64_t)d.gamma * d.V,
+                              ds.pv, ds.pi, &sp.nblocks, s));
+    }
     g_invocations++;
     return DFLASH_OK;
 }
@@ -1373,6 +1583,26 @@ int dflash_lm_head_argmax(const dflash_weight* E_out, const void* y, int32_t y_d
 size_t dflash_kv_prefill_workspace_bytes(const dflash_dims* dims, int32_t n) {
     if (check_dims(dims) == DFLASH_EINVAL || n <= 0) return 0;
     return kv_append_norm_bytes(*dims, n);
+}
+
+int dflash_verify_greedy_lengths(const float* target_logits, const int32_t* draft_ids, const int32_t* lengths,
+                                 int32_t B, int32_t gamma, int32_t V, int32_t* accepted, int32_t* committed,
+                                 int32_t* ids, int32_t* next_anchor, void* ws, size_t ws_bytes, void* stream) {
+    if (!lengths) return DFLASH_EINVAL;
+    if (!target_logits || !draft_ids || !accepted || !committed || !ids) return DFLASH_EINVAL;
+    if (B <= 0 || gamma <= 0 || V <= 0) return DFLASH_EINVAL;
+    if (gamma + 1 > 64) return DFLASH_DECLINED;
+    if (reinterpret_cast<uintptr_t>(target_logits) & 15) return DFLASH_DECLINED;
+    const size_t need = dflash_verify_workspace_bytes(B, gamma, V);
+    if (!ws || ws_bytes < need) return DFLASH_ENOSPC;
+    DFL_TRY(gate());
+    char* c = static_cast<char*>(ws);
+    float* pv = reinterpret_cast<float*>(c);
+    int32_t* pi = reinterpret_cast<int32_t*>(c + need / 2);
+    DFL_HIP(launch_verify(target_logits, draft_ids, B, gamma, V, accepted, committed, ids, next_anchor, pv, pi,
+                          static_cast<hipStream_t>(stream), lengths));
+    g_invocations++;
+    return DFLASH_OK;
 }
 
 size_t dflash_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V) {

@@ -549,7 +549,8 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
                 // row m) across the workgroup's tiles; the wavefronts are combined once at the end
                 const int r = vi / MAXM, m = vi - r * MAXM;
                 const int n = tile * 4 * RPW + wave * RPW + r;
-                if ((lane % SPAN) == 0 && m < p.M && n < p.N) argmax_pick(amax, aidx, tot, n);
+                if ((lane % SPAN) == 0 && m < p.M && n < p.N)
+                    argmax_pick(amax, aidx, p.base ? tot + p.base[(int64_t)m * p.base_ld + n] : tot, n);
             } else {
                 if ((lane % SPAN) == 0) red[(wave * RPW) * MAXM + vi] = tot;
             }

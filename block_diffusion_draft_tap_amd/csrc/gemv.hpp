@@ -98,6 +98,8 @@ struct GemvParams {
     float* part_val;     // [M][nblocks]
     int32_t* part_idx;
     int nblocks;
+    const float* base;   // optional: the argmax runs over base[m * base_ld + n] + (row m . W[n])
+    int64_t base_ld;
     uint64_t* stamps;    // set by the launcher when the launch is traced: (start, end) wall clock per workgroup
 };
 

@@ -2,6 +2,8 @@
 //   argmax_merge_kernel   per-workgroup (max, index) partials -> greedy ids
 //   verify_partial_kernel per (verify row, vocab slice) argmax of target logits
 //   verify_final_kernel   prefix compare: accepted, committed, ids, next anchor
+//   dspark_step_kernel    one step of the DSpark greedy loop (previous token, Markov operand,
+//                         confidence, pruning length)
 //   rownorm_kernel        RMSNorm of fp32 rows (sum of split partials) with a gain (Eq 2)
 //   rownorm1_kernel       the same for rows from a single source, read once
 //   gather_rows_kernel    bf16 table rows by id (the anchors' embeddings)
@@ -73,10 +75,12 @@ __global__ __launch_bounds__(kBlock) void verify_partial_kernel(const float* log
     }
 }
 
-// one 64-lane wavefront per sequence; lane j handles verify row j (gamma + 1 <= 64)
+// one 64-lane wavefront per sequence; lane j handles verify row j (gamma + 1 <= 64). With
+// lengths (a pruned block proposes its first lengths[b] drafts) the prefix stops there too.
 __global__ __launch_bounds__(64) void verify_final_kernel(const float* part_val, const int32_t* part_idx, int nsplit,
-                                                          const int32_t* draft, int gamma, int32_t* accepted,
-                                                          int32_t* committed, int32_t* ids, int32_t* next_anchor) {
+                                                          const int32_t* draft, int gamma, const int32_t* lengths,
+                                                          int32_t* accepted, int32_t* committed, int32_t* ids,
+                                                          int32_t* next_anchor) {
     const int b = blockIdx.x, j = threadIdx.x;
     const int W = gamma + 1;
     int t = -1;
@@ -87,7 +91,8 @@ __global__ __launch_bounds__(64) void verify_final_kernel(const float* part_val,
         for (int s = 0; s < nsplit; ++s) argmax_pick(v, i, part_val[base + s], part_idx[base + s]);
         t = i;
     }
-    const bool mismatch = (j < gamma) && (draft[(int64_t)b * gamma + j] != t);
+    const int lim = lengths ? min(max(lengths[b], 0), gamma) : gamma;
+    const bool mismatch = (j < gamma) && (j >= lim || draft[(int64_t)b * gamma + j] != t);
     const unsigned long long mask = __ballot(mismatch);
     const int a = mask ? (__ffsll((long long)mask) - 1) : gamma;
     if (j < W) ids[(int64_t)b * W + j] = (j <= a) ? t : -1;
@@ -96,6 +101,77 @@ __global__ __launch_bounds__(64) void verify_final_kernel(const float* part_val,
         accepted[b] = a;
         committed[b] = a + 1;
     }
+}
+
+// One step of the DSpark greedy loop for sequence b = blockIdx.x (page 3, forwardRows with
+// #markov and #confidence): the previous token (the anchor at step 0, else the argmax of the
+// previous step's (max, index) partials, lowest index on ties) becomes draft step - 1; the
+// Markov operand row e1 = w1[previous] is written for this step's projection; this step's
+// confidence sigmoid([block row; e1] . conf_w + conf_b) and the Alg 1 length update (a row
+// still at full length is cut to `step` when the confidence falls below the step's
+// threshold; step 0 always stays). step == gamma only merges the last step's partials.
+__global__ __launch_bounds__(kBlock) void dspark_step_kernel(const DsparkStepParams p) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    __shared__ int prev_s;
+    __shared__ float red[4];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    if (p.step == 0) {
+        if (tid == 0) prev_s = p.anchors[b];
+    } else {
+        float v = -INFINITY;
+        int i = 0x7fffffff;
+        const int64_t base = (int64_t)b * p.nblocks;
+        for (int j = tid; j < p.nblocks; j += blockDim.x) argmax_pick(v, i, p.part_val[base + j], p.part_idx[base + j]);
+        block_argmax(v, i, sv, si);
+        if (tid == 0) {
+            prev_s = i;
+            p.ids[(int64_t)b * p.gamma + p.step - 1] = i;
+        }
+    }
+    __syncthreads();
+    if (p.step == p.gamma) return;
+    const int prev = min(max(prev_s, 0), p.V - 1);
+    const int64_t row = (int64_t)b * p.gamma + p.step;
+    float acc = 0.f;
+    for (int c = tid; c < p.r; c += blockDim.x) {
+        float e;
+        if (p.f32) {
+            e = static_cast<const float*>(p.w1)[(int64_t)prev * p.r + c];
+            static_cast<float*>(p.e1)[(int64_t)b * p.r + c] = e;
+        } else {
+            const uint16_t bits = static_cast<const uint16_t*>(p.w1)[(int64_t)prev * p.r + c];
+            e = bf16_bits_to_f32(bits);
+            static_cast<uint16_t*>(p.e1)[(int64_t)b * p.r + c] = bits;
+        }
+        acc += e * load_gain(p.conf_w, p.f32, p.d + c);
+    }
+    for (int c = tid; c < p.d; c += blockDim.x) {
+        const float h = p.f32 ? static_cast<const float*>(p.hout)[row * p.d + c]
+                              : bf16_bits_to_f32(static_cast<const uint16_t*>(p.hout)[row * p.d + c]);
+        acc += h * load_gain(p.conf_w, p.f32, c);
+    }
+    acc = wave_sum(acc);
+    if ((tid & 63) == 0) red[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        float z = load_gain(p.conf_b, p.f32, 0);
+        for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) z += red[w];
+        const float c = 1.0f / (1.0f + expf(-z));
+        if (p.conf) p.conf[row] = c;
+        if (p.step == 0) {
+            p.lengths[b] = p.gamma;
+        } else {
+            const float thr = p.thresholds ? p.thresholds[p.step] : p.min_conf;
+            if (p.lengths[b] == p.gamma && c < thr) p.lengths[b] = p.step;
+        }
+    }
+}
+
+hipError_t launch_dspark_step(const DsparkStepParams& p, hipStream_t s) {
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL(dspark_step_kernel, dim3(p.B), dim3(kBlock), 0, s, p);
+    return hipGetLastError();
 }
 
 // dst[r] = RMSNorm(sum_z src[z][r]; gain): the split-K partials are added in
@@ -246,7 +322,7 @@ int verify_splits(int V) {
 
 hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int gamma, int V, int32_t* accepted,
                          int32_t* committed, int32_t* ids, int32_t* next_anchor, float* pv, int32_t* pi,
-                         hipStream_t s) {
+                         hipStream_t s, const int32_t* lengths) {
     const int ns = verify_splits(V);
     const int rows = B * (gamma + 1);
     (void)hipGetLastError();  // report only this launch's status
@@ -254,8 +330,8 @@ hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int g
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     (void)hipGetLastError();  // report only this launch's status
-    hipLaunchKernelGGL(verify_final_kernel, dim3(B), dim3(64), 0, s, pv, pi, ns, draft, gamma, accepted, committed,
-                       ids, next_anchor);
+    hipLaunchKernelGGL(verify_final_kernel, dim3(B), dim3(64), 0, s, pv, pi, ns, draft, gamma, lengths, accepted,
+                       committed, ids, next_anchor);
     return hipGetLastError();
 }
 

@@ -12,7 +12,26 @@ hipError_t launch_argmax_merge(const float* pv, const int32_t* pi, int nblocks, 
 int verify_splits(int V);
 hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int gamma, int V, int32_t* accepted,
                          int32_t* committed, int32_t* ids, int32_t* next_anchor, float* pv, int32_t* pi,
-                         hipStream_t s);
+                         hipStream_t s, const int32_t* lengths = nullptr);
+
+// One step of the DSpark greedy loop per sequence (see head.hip)
+struct DsparkStepParams {
+    int step, gamma, B, V, r, d, nblocks, f32;  // f32: head weights and block rows in fp32
+    const int32_t* anchors;                     // [B]
+    const float* part_val;                      // previous step's argmax partials [B][nblocks]
+    const int32_t* part_idx;
+    const void* w1;                             // [V, r]
+    const void* hout;                           // block rows [B * gamma, d]
+    const void* conf_w;                         // [d + r]
+    const void* conf_b;                         // [1]
+    const float* thresholds;                    // [gamma] or null (then min_conf)
+    float min_conf;
+    void* e1;                                   // out: Markov operand rows [B, r]
+    int32_t* ids;                               // out: drafts [B, gamma]
+    float* conf;                                // out: [B, gamma] or null
+    int32_t* lengths;                           // out: [B]
+};
+hipError_t launch_dspark_step(const DsparkStepParams& p, hipStream_t s);
 hipError_t launch_rownorm(const float* src, int nsplit, int64_t split_stride, float* dst, int rows, int d,
                           const void* gain, int gain_f32, float eps, hipStream_t s);
 // dst[r][:] = table[clamp(ids[r])][:] (bf16 rows of K, K a multiple of 8)

@@ -330,10 +330,14 @@ __global__ __launch_bounds__(kST, MT >= 8 ? 1 : DFL_SK_OCC) void skinny_kernel(c
             for (int e = 0; e < 4; ++e) {
                 float v = -INFINITY;
                 int idx = 0x7fffffff;
+                const int mrow = i * 16 + 4 * grp + e;
 #pragma unroll
                 for (int f = 0; f < kSNB; ++f) {
                     const int n = tile * kSCols + wave * 16 * kSNB + f * 16 + col;
-                    if (n < p.N) argmax_pick(v, idx, acc[i][f][e], n);
+                    if (n < p.N) {
+                        const float y = acc[i][f][e];
+                        argmax_pick(v, idx, (p.base && mrow < p.M) ? y + p.base[(int64_t)mrow * p.base_ld + n] : y, n);
+                    }
                 }
                 // the 16 lanes of a group hold the same row
 #pragma unroll

@@ -52,6 +52,8 @@ struct SkinnyParams {
     float* part_val;      // [M][nblocks]
     int32_t* part_idx;
     int nblocks;          // skinny_tiles(SK_ARGMAX, N)
+    const float* base;    // SK_ARGMAX, optional: the argmax runs over base[m * base_ld + n] + y[m, n]
+    int64_t base_ld;
     uint64_t* stamps;     // set by the launcher when the launch is traced: (start, end) wall clock per workgroup
     // SK_KV: columns [0, hkv*hd) are keys, [hkv*hd, 2*hkv*hd) values (bf16 caches). Row
     // r = row_base + m belongs to the sequence b with row_offsets[b] <= r < row_offsets[b+1]

@@ -284,6 +284,50 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
                          int32_t* draft_ids, void* y_out, float* max_logit, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* The DSpark heads (page 3, #markov and #confidence; initialised there with
+ * markov.w2 = 0 and conf.w = 0): bf16 for bf16 and int4 models, float for f32
+ * models.
+ *   w1:     [V, r]  markov.w1, the sequential head's token table
+ *   w2t:    [V, r]  markov.w2 (the page's [r, V] matrix) transposed: row v holds
+ *           column v, so the Markov bias of token v is e1 . w2t[v]
+ *   conf_w: [d + r] conf.w over [block row; e1];  conf_b: [1] conf.b
+ * r must be a multiple of 8 and w1, w2t 16-byte aligned, else DECLINED. */
+typedef struct {
+    int32_t     r;
+    const void* w1;
+    const void* w2t;
+    const void* conf_w;
+    const void* conf_b;
+} dflash_dspark_head;
+
+/* Workspace bytes of dflash_draft_forward_dspark for up to B sequences and a
+ * context capacity of cap rows (0 for invalid arguments). */
+size_t dflash_dspark_workspace_bytes(const dflash_dims* dims, int32_t r, int32_t B, int32_t cap);
+
+/* Greedy drafting with the DSpark sequential (Markov) head and confidence
+ * head, and confidence-scheduled draft-length pruning (page 3: forwardRows with
+ * #markov and #confidence; DflashDraftOpts.thresholds / minConf, Alg 1):
+ *   block = RMSNorm(H_d; out_norm) after every layer (#backbone), Y as in
+ *   dflash_draft_forward, base = Y . lm_head^T (fp32, #baseLogits); then for
+ *   k = 0 .. gamma-1, previous = the anchor (k = 0) or draft k-1:
+ *     e1 = w1[previous]
+ *     draft_ids[b, k] = argmax_v base[b, k, v] + e1 . w2t[v]  (lowest index on ties)
+ *     conf[b, k] = sigmoid([block[b, k]; e1] . conf_w + conf_b)
+ *   lengths[b] = the first k >= 1 with conf[b, k] < thresholds[k] (min_conf
+ *   when thresholds is NULL), else gamma: the row's draft is cut there and
+ *   position 0 is always kept. Every step runs for every row (no host
+ *   synchronisation); positions at or past lengths[b] are not proposed.
+ *   min_conf <= 0 with thresholds NULL never cuts (a confidence is positive).
+ *   thresholds: device float [gamma] or NULL.  conf: device float [B, gamma]
+ *   or NULL.  lengths: device int32 [B] or NULL.  y_out: as in
+ *   dflash_draft_forward.  Other arguments as in dflash_draft_forward; EINVAL
+ *   for a NULL head pointer or min_conf NaN.
+ * Workspace: dflash_dspark_workspace_bytes(dims, r, B, kv->cap). */
+int dflash_draft_forward_dspark(const dflash_model* M, const dflash_dspark_head* head, const int32_t* anchor_ids,
+                                const dflash_kv* kv, int32_t B, const float* thresholds, float min_conf,
+                                int32_t* draft_ids, float* conf, int32_t* lengths, void* y_out, void* ws,
+                                size_t ws_bytes, void* stream);
+
 /* Greedy ids under a borrowed LM head (page 3, #baseLogits and the argmax
  * step of forwardRows): ids[r] = argmax_v y[r] . E_out[v], lowest index on
  * ties; logits are fp32 accumulations and are never materialised.
@@ -310,6 +354,16 @@ int dflash_verify_greedy(const float* target_logits, const int32_t* draft_ids, i
                          int32_t* accepted, int32_t* committed, int32_t* ids, int32_t* next_anchor, void* ws,
                          size_t ws_bytes, void* stream);
 size_t dflash_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V);
+
+/* dflash_verify_greedy for a pruned block (page 3, Alg 1: sequence b proposes
+ * only its first lengths[b] drafts): accepted[b] = largest a <= lengths[b]
+ * with draft_ids[b, k] == t[b, k] for all k < a; committed, ids and
+ * next_anchor follow from it as in dflash_verify_greedy.
+ *   lengths: device int32 [B], each clamped to [0, gamma] (not NULL: EINVAL).
+ * Workspace: at least dflash_verify_workspace_bytes(B, gamma, V). */
+int dflash_verify_greedy_lengths(const float* target_logits, const int32_t* draft_ids, const int32_t* lengths,
+                                 int32_t B, int32_t gamma, int32_t V, int32_t* accepted, int32_t* committed,
+                                 int32_t* ids, int32_t* next_anchor, void* ws, size_t ws_bytes, void* stream);
 
 /* For callers that cannot allocate (code under HIP graph capture, serving
  * loops or harnesses that forbid hipMalloc): dflash_verify_greedy without a

@@ -180,6 +180,31 @@ def test_verify_and_head_validation():
                                      None) == bd.DFLASH_EINVAL
 
 
+def test_dspark_and_length_verify_validation():
+    fm = _FakeModel(DEFAULT)
+    lib = bd.lib
+    P = 1 << 20
+    head = bd.dflash_dspark_head(r=256, w1=P, w2t=P, conf_w=P, conf_b=P)
+    args = lambda h, mc=0.0, ws=1 << 30: (ctypes.byref(fm.c), h, P, ctypes.byref(fm.kv), 1, None, mc, P, None, None,
+                                          None, P, ws, None)
+    assert lib.dflash_draft_forward_dspark(*args(None)) == bd.DFLASH_EINVAL
+    assert lib.dflash_draft_forward_dspark(*args(ctypes.byref(head), float("nan"))) == bd.DFLASH_EINVAL
+    assert lib.dflash_draft_forward_dspark(*args(ctypes.byref(head), 0.0, 16)) == bd.DFLASH_ENOSPC
+    bad = bd.dflash_dspark_head(r=12, w1=P, w2t=P, conf_w=P, conf_b=P)      # rows of 12 bf16: not 16-byte
+    assert lib.dflash_draft_forward_dspark(*args(ctypes.byref(bad))) == bd.DFLASH_DECLINED
+    bad = bd.dflash_dspark_head(r=256, w1=P, w2t=None, conf_w=P, conf_b=P)
+    assert lib.dflash_draft_forward_dspark(*args(ctypes.byref(bad))) == bd.DFLASH_EINVAL
+    dims = ctypes.byref(bd.make_dims(DEFAULT))
+    n = lib.dflash_dspark_workspace_bytes(dims, 256, 1, 2112)
+    # the forward's own workspace plus the base logits of the block rows at least
+    assert n >= lib.dflash_workspace_bytes(dims, 1, 2112) + DEFAULT.gamma * DEFAULT.V * 4
+    assert lib.dflash_dspark_workspace_bytes(dims, 0, 1, 2112) == 0
+    # the length-capped verify: lengths are required; otherwise the plain verify's checks
+    assert lib.dflash_verify_greedy_lengths(P, P, None, 1, 7, 100, P, P, P, None, P, 1 << 20, None) == bd.DFLASH_EINVAL
+    assert lib.dflash_verify_greedy_lengths(P, P, P, 1, 70, 100, P, P, P, None, P, 1 << 20, None) == bd.DFLASH_DECLINED
+    assert lib.dflash_verify_greedy_lengths(P, P, P, 1, 7, 100, P, P, P, None, P, 4, None) == bd.DFLASH_ENOSPC
+
+
 def test_append_and_project_validation():
     fm = _FakeModel(TINY)
     lib = bd.lib
