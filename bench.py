@@ -65,6 +65,14 @@ def weight_bytes_per_elem(wdtype):
     return {"f32": 4.0, "bf16": 2.0, "int4g64": 0.5 + 4.0 / 64}[wdtype]
 
 
+def dspark_bytes(d, B, r):
+    """Extra minimum bytes of a round with the DSpark heads: the base logits of
+    every block row written once and read once, markov.w2 streamed once per
+    step, one w1 row and the confidence weights per step and sequence."""
+    wb = 4.0 if d.wdtype == "f32" else 2.0
+    return 2 * B * d.gamma * d.V * 4 + d.gamma * d.V * r * wb + d.gamma * B * r * wb + (d.d + r) * wb
+
+
 def algorithmic_bytes(d, B, ctx_rows, n_new):
     """Minimum bytes of one round: every weight once (the K/V rows shared by
     the append and the block counted once), the borrowed LM head once, one
@@ -118,9 +126,10 @@ class CpuLeg:
     context projection + K/V append of the committed rows, the forward, the LM
     head and verify, then the rollback."""
 
-    def __init__(self, d, w, b, L, rounds):
+    def __init__(self, d, w, b, L, rounds, thresholds=None):
         from oracle import dflash_oracle as O
         self.O, self.d, self.w, self.b, self.L, self.rounds = O, d, w, b, L, rounds
+        self.thresholds = thresholds     # the DSpark round (Markov and confidence heads, Alg 1)
         self.fm = d.wdtype != "f32"
         self.d1 = scaled(d, B=1)
         taps = gen.make_taps(d, 0, L, stream="ctx", seq=b)
@@ -145,11 +154,17 @@ class CpuLeg:
             if r == 0:  # the chain starts from the seeded anchors, like the GPU's
                 self.anchor = gen.make_anchors(d, 0)[b:b + 1]
             anchor = self.anchor
-            ids, ex = O.draft_forward(w, self.d1, self.ctx, anchor, self.fm, return_all=True)
+            if self.thresholds is None:
+                ids, ex = O.draft_forward(w, self.d1, self.ctx, anchor, self.fm, return_all=True)
+                lengths = None
+            else:
+                ids, _, lengths, extra = O.dspark_forward(w, self.d1, self.ctx, anchor, self.fm,
+                                                          thresholds=self.thresholds)
+                ex = {"logits": extra["scores"].reshape(d.gamma, -1)}
             full = np.zeros((d.B, d.gamma), np.int32)
             full[b] = ids[0]
             T = gen.plant_target_logits(d, full, rr["accept"], r)
-            _, _, _, nxt = O.verify_greedy(T[b:b + 1], ids)
+            _, _, _, nxt = O.verify_greedy(T[b:b + 1], ids, lengths=lengths)
             self.anchor = nxt
             self.ctx.truncate(0, self.L)
             if self.done < len(self.rounds):
@@ -174,9 +189,19 @@ class CpuLeg:
             s = np.sort(logits, axis=1)
             decided = (s[:, -1] - s[:, -2]) >= NEAR_TIE
             g = gpu_ids[r][b]
+            if self.thresholds is not None:
+                # the Markov head conditions each step on the previous token: compare up to and
+                # including the first step where the two chains differ
+                diff = np.nonzero(g != ids)[0]
+                if diff.size:
+                    decided = decided & (np.arange(len(g)) <= diff[0])
             compared += int(decided.sum())
             agree += int((decided & (g == ids)).sum())
             for k in np.nonzero(decided & (g != ids))[0]:
+                if self.thresholds is not None:
+                    misses.append({"round": r, "pos": int(k), "gpu": int(g[k]), "oracle": int(ids[k]),
+                                   "oracle_top2_gap": round(float(s[k, -1] - s[k, -2]), 6)})
+                    continue
                 y = gpu_y[r][b, k:k + 1].astype(np.float64)
                 own, best, lg = O.lm_head_argmax(y, self.w["E_out"], want_logits=True)
                 explained = int(own[0]) == int(g[k]) or best[0] - lg[0, g[k]] <= NEAR_TIE
@@ -327,8 +352,17 @@ def main():
     ap.add_argument("--no-trace", action="store_true", help="rounds without the in-kernel stamps")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="counter workload: a 256 MiB device copy (calibration), then eager rounds")
+    ap.add_argument("--dspark", action="store_true",
+                    help="the round with the DSpark heads (Markov sequential head of rank --rank, confidence "
+                         "head, Alg 1 pruning at --threshold) and the length-capped verify")
+    ap.add_argument("--rank", type=int, default=256, help="DSpark Markov rank (page 3's default config: 256)")
+    ap.add_argument("--threshold", type=float, default=0.5, help="DSpark per-step pruning threshold (synthetic)")
+    ap.add_argument("--one-call", action="store_true",
+                    help="the round's projection, append and forward as one dflash_draft_round call")
     args = ap.parse_args()
 
+    if args.one_call and args.dspark:
+        sys.exit("bench.py: --one-call runs the plain drafter's round; it does not combine with --dspark")
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -354,8 +388,12 @@ def main():
 
     t_setup = time.perf_counter()
     log(f"[bench] generating weights for {d.name}")
+    if args.dspark:
+        d = scaled(d, r=args.rank)
     w = gen.Model(d).materialise()
     dm = dfa.DeviceModel(d, w, dev)
+    head = dfa.DsparkHead(w, dev) if args.dspark else None
+    thresholds = np.full(d.gamma, args.threshold, np.float32) if args.dspark else None
     lengths = [int(x) for x in gen.context_lengths(d)]
     cpu_seq = int(np.argmin(lengths))
     cap = max(lengths) + W + 64
@@ -367,6 +405,10 @@ def main():
     len0 = kv.len.clone()
 
     vws = bd.verify_workspace(B, d.gamma, d.V, dev)
+    rws = dfa.round_workspace(d, B, kv.cap, dev) if args.one_call else None
+    if args.dspark:
+        dws = dfa.dspark_workspace(d, d.r, B, kv.cap, dev)
+        thr_d = torch.from_numpy(thresholds).to(dev)
     offs = torch.arange(0, (B + 1) * W, W, dtype=torch.int32, device=dev)
     h_new = torch.empty(B * W, d.d, dtype=torch.float32, device=dev)
     y_chain = torch.empty(B, d.gamma, d.H, dtype=dm.act_dtype, device=dev)
@@ -389,20 +431,37 @@ def main():
             "nxt": torch.zeros(B, dtype=torch.int32, device=dev),
             "stamps": torch.zeros(STAMP_ENTRIES, dtype=torch.int64, device=dev),
             "records": [],
+            "lengths": torch.full((B,), d.gamma, dtype=torch.int32, device=dev),
         }
         rr["counts"] = torch.from_numpy(rr["counts_h"]).to(dev)
         rounds.append(rr)
+
+    def verify_round(rr):
+        if args.dspark:
+            bd.check(dfa.dflash_verify_greedy_lengths(rr["T"], rr["ids"], rr["lengths"], rr["acc"], rr["com"],
+                                                      rr["vids"], vws, next_anchor=rr["nxt"]), "verify lengths")
+        else:
+            bd.check(dfa.dflash_verify_greedy(rr["T"], rr["ids"], rr["acc"], rr["com"], rr["vids"], vws,
+                                              next_anchor=rr["nxt"]), "verify")
 
     def run_round(rr, verify=True, trace=False, y=None):
         if trace:
             bd.dflash_trace_begin(bd.DFLASH_TRACE_LM_HEAD | bd.DFLASH_TRACE_ATTENTION | bd.DFLASH_TRACE_PROJECTIONS,
                                   rr["stamps"])
-        bd.check(dfa.dflash_context_project(dm, rr["taps"], h_new, ws), "context_project")
-        bd.check(dfa.dflash_ctx_kv_append(dm, h_new, offs, rr["counts"], kv, ws), "append")
-        bd.check(dfa.dflash_draft_forward(dm, rr["anchors"], kv, B, rr["ids"], ws, y_out=y), "forward")
+        if args.one_call:
+            bd.check(dfa.dflash_draft_round(dm, rr["taps"], offs, rr["counts"], kv, B, rr["anchors"], rr["ids"], rws,
+                                            y_out=y), "round")
+        else:
+            bd.check(dfa.dflash_context_project(dm, rr["taps"], h_new, ws), "context_project")
+            bd.check(dfa.dflash_ctx_kv_append(dm, h_new, offs, rr["counts"], kv, ws), "append")
+            if args.dspark:
+                bd.check(dfa.dflash_draft_forward_dspark(dm, head, rr["anchors"], kv, B, rr["ids"], dws,
+                                                         thresholds=thr_d, lengths=rr["lengths"], y_out=y),
+                         "forward_dspark")
+            else:
+                bd.check(dfa.dflash_draft_forward(dm, rr["anchors"], kv, B, rr["ids"], ws, y_out=y), "forward")
         if verify:
-            bd.check(dfa.dflash_verify_greedy(rr["T"], rr["ids"], rr["acc"], rr["com"], rr["vids"], vws,
-                                              next_anchor=rr["nxt"]), "verify")
+            verify_round(rr)
         kv.len.copy_(len0)
         if trace:
             rr["records"] = bd.dflash_trace_end()
@@ -419,9 +478,10 @@ def main():
         chain_ids.append(ids)
         chain_y.append(y_chain.float().cpu().numpy())
         rr["T"].copy_(torch.from_numpy(gen.plant_target_logits(d, ids, accept[r], r)))
-        bd.check(dfa.dflash_verify_greedy(rr["T"], rr["ids"], rr["acc"], rr["com"], rr["vids"], vws,
-                                          next_anchor=rr["nxt"]), "verify")
-        assert np.array_equal(rr["acc"].cpu().numpy(), accept[r])
+        verify_round(rr)
+        rr["lengths_h"] = rr["lengths"].cpu().numpy().copy()
+        rr["accepted_h"] = np.minimum(accept[r], rr["lengths_h"])     # a pruned block proposes fewer
+        assert np.array_equal(rr["acc"].cpu().numpy(), rr["accepted_h"])
         anchor = rr["nxt"].cpu().numpy().copy()
     torch.cuda.synchronize()
     del y_chain
@@ -434,9 +494,11 @@ def main():
         log(f"[profile-kernels] copy {COPY_BYTES} B, then {R} eager rounds of {d.name}")
         return
 
-    # capture one graph per round (the trace records each launch's stamp slice)
+    # capture one graph per round, and a second set with launch tracing on (each traced launch
+    # records its stamp slice): the headline replays the untraced graphs, the per-kernel
+    # durations come from a timed pass over the traced ones
     trace = not args.no_trace
-    graphs = []
+    graphs, tgraphs = [], []
     stream = torch.cuda.Stream(device=dev)
     use_graph = not args.eager
     if use_graph:
@@ -445,24 +507,29 @@ def main():
         for rr in rounds:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
-                run_round(rr, trace=trace)
+                run_round(rr)
             graphs.append(g)
+            if trace:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    run_round(rr, trace=True)
+                tgraphs.append(g)
         torch.cuda.synchronize()
 
-    def step(i):
+    def step(i, traced=False):
         if use_graph:
-            graphs[i % R].replay()
+            (tgraphs if traced else graphs)[i % R].replay()
         else:
-            run_round(rounds[i % R], trace=trace)
+            run_round(rounds[i % R], trace=traced)
 
-    def timed(nsteps, first):
+    def timed(nsteps, first, traced=False):
         """nsteps consecutive rounds between synchronisations, one event pair
         around all of them: total ms."""
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
         for i in range(nsteps):
-            step(first + i)
+            step(first + i, traced)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
@@ -487,17 +554,24 @@ def main():
     nxt = args.warmup + args.steps
     per_step = timed_per_step(args.steps, nxt)
     nxt += args.steps
+    if trace:
+        traced_ms = timed(args.steps, nxt, traced=True)
+        nxt += args.steps
 
     # the replays must reproduce the chain exactly (deterministic kernels)
     for r, rr in enumerate(rounds):
         assert np.array_equal(rr["ids"].cpu().numpy(), chain_ids[r]), f"round {r}: drafts changed on replay"
-        assert np.array_equal(rr["acc"].cpu().numpy(), accept[r]), f"round {r}: accepted changed on replay"
-        assert np.array_equal(rr["com"].cpu().numpy(), accept[r] + 1)
+        assert np.array_equal(rr["acc"].cpu().numpy(), rr["accepted_h"]), f"round {r}: accepted changed on replay"
+        assert np.array_equal(rr["com"].cpu().numpy(), rr["accepted_h"] + 1)
+        assert np.array_equal(rr["lengths"].cpu().numpy(), rr["lengths_h"])
 
     ms_per_step = gpu_ms / args.steps
     blocks_per_s = B * args.steps / (gpu_ms / 1000.0)
     mean_new = float(np.mean([rr["counts_h"].sum() for rr in rounds]))
     ab = algorithmic_bytes(d, B, sum(lengths), mean_new / B)
+    if args.dspark:
+        ab["dspark"] = dspark_bytes(d, B, d.r)
+        ab["total"] += ab["dspark"]
     round_gbs = ab["total"] / (ms_per_step / 1000.0) / 1e9
 
     res = {
@@ -519,8 +593,15 @@ def main():
             "rounds_cycled": R,
             "mean_committed_rows_appended": round(mean_new / B, 3),
             "launch": "hip graph per round" if use_graph else "eager",
+            "round_calls": ("dflash_draft_round" if args.one_call else
+                            "dflash_context_project + dflash_ctx_kv_append + dflash_draft_forward"
+                            + ("_dspark" if args.dspark else "")) + " + verify",
         },
-        "tokens_proposed_per_s": round(blocks_per_s * d.gamma, 1),
+        "dspark": ({"rank": d.r, "thresholds": "synthetic: %.3f at every step k >= 1" % args.threshold,
+                    "mean_proposed_per_block": round(float(np.mean([rr["lengths_h"].mean() for rr in rounds])), 3),
+                    "round_algorithmic_bytes_heads": int(ab["dspark"])} if args.dspark else None),
+        "tokens_proposed_per_s": round(blocks_per_s * (np.mean([rr["lengths_h"].mean() for rr in rounds])
+                                                       if args.dspark else d.gamma), 1),
         "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 5) for q in (10, 50, 90)],
         "step_ms_note": "per-round distribution from a second run of the same steps with an event between rounds",
         "round_algorithmic_bytes": int(ab["total"]),
@@ -531,7 +612,8 @@ def main():
     if trace:
         table = kernel_table(rounds, lengths_after)
         timing = (f"device wall-clock stamps written by the kernel's workgroups (first start to last end per "
-                  f"launch), last timed replay of each of the {R} rounds")
+                  f"launch), last replay of each of the {R} rounds in a timed pass of {args.steps} traced rounds "
+                  f"({traced_ms / args.steps:.5f} ms per round; the headline replays untraced graphs)")
         res["roofline"] = roofline_entry(table[0], d, timing)
         head = [k for k in table if k["kind"] == "lm_head"]
         if head and head[0] is not table[0]:
@@ -539,7 +621,8 @@ def main():
         res["kernels_per_round"] = [{k2: (round(v, 2) if isinstance(v, float) else v) for k2, v in k.items()}
                                     for k in table[:8]]
         traced = sum(k["us_per_round"] for k in table)
-        res["traced_share_of_round"] = round(traced / (ms_per_step * 1e3), 4)
+        res["traced_ms_per_step"] = round(traced_ms / args.steps, 5)
+        res["traced_share_of_round"] = round(traced / (traced_ms / args.steps * 1e3), 4)
     res["prefill"] = pre
     res["wall_s_timed"] = round(wall, 4)
 
@@ -565,7 +648,7 @@ def main():
 
     if not args.skip_cpu:
         log(f"[bench] cpu baseline: oracle setup for sequence {cpu_seq} ({lengths[cpu_seq]} context rows)")
-        cpu = CpuLeg(d, w, cpu_seq, lengths[cpu_seq], rounds)
+        cpu = CpuLeg(d, w, cpu_seq, lengths[cpu_seq], rounds, thresholds)
         seg_gpu = []
         nseg = max(1, args.cpu_segments)
         for sgi in range(nseg):

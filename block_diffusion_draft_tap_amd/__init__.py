@@ -11,7 +11,8 @@ _BINDING_NAMES = (
     "dflash_query", "dflash_context_project", "dflash_ctx_kv_append", "dflash_draft_layer",
     "dflash_draft_forward", "dflash_lm_head_argmax", "dflash_verify_greedy", "dflash_invocations",
     "dflash_trace_begin", "dflash_trace_end", "DsparkHead", "dspark_workspace",
-    "dflash_draft_forward_dspark", "dflash_verify_greedy_lengths", "check", "DflashError",
+    "dflash_draft_forward_dspark", "dflash_verify_greedy_lengths", "dflash_draft_round", "round_workspace",
+    "check", "DflashError",
 )
 
 

@@ -28,7 +28,7 @@ EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "df
            "dflash_verify_workspace_bytes", "dflash_kv_prefill_workspace_bytes", "dflash_trace_begin",
            "dflash_trace_end", "dflash_lm_head_workgroups", "dflash_wall_clock_hz", "dflash_verify_greedy_noalloc",
            "dflash_verify_noalloc_max_bytes", "dflash_dspark_workspace_bytes", "dflash_draft_forward_dspark",
-           "dflash_verify_greedy_lengths"]
+           "dflash_verify_greedy_lengths", "dflash_draft_round", "dflash_round_workspace_bytes"]
 DFLASH_TRACE_LM_HEAD, DFLASH_TRACE_ATTENTION, DFLASH_TRACE_PROJECTIONS = 1, 2, 4
 
 
@@ -116,6 +116,11 @@ def _load():
     lib.dflash_draft_forward_dspark.restype = ctypes.c_int
     lib.dflash_verify_greedy_lengths.argtypes = [VP, VP, VP, I32, I32, I32, VP, VP, VP, VP, VP, SZ, VP]
     lib.dflash_verify_greedy_lengths.restype = ctypes.c_int
+    lib.dflash_draft_round.argtypes = [P(dflash_model), P(VP), ctypes.c_int64, I32, VP, VP, P(dflash_kv), I32, VP, VP,
+                                       VP, VP, VP, SZ, VP]
+    lib.dflash_draft_round.restype = ctypes.c_int
+    lib.dflash_round_workspace_bytes.argtypes = [P(dflash_dims), I32, I32]
+    lib.dflash_round_workspace_bytes.restype = SZ
     lib.dflash_verify_noalloc_max_bytes.argtypes = []
     lib.dflash_verify_noalloc_max_bytes.restype = SZ
     lib.dflash_trace_begin.argtypes = [I32, VP, ctypes.c_int64]
@@ -390,6 +395,22 @@ def dflash_verify_greedy_lengths(target_logits, draft_ids, lengths, accepted, co
     return lib.dflash_verify_greedy_lengths(_ptr(target_logits), _ptr(draft_ids), _ptr(lengths), B, W - 1, V,
                                             _ptr(accepted), _ptr(committed), _ptr(ids), _ptr(next_anchor),
                                             _ptr(ws), ws.numel(), _stream(stream))
+
+
+def round_workspace(dims, B, cap, device="cuda"):
+    n = lib.dflash_round_workspace_bytes(ctypes.byref(make_dims(dims)), B, cap)
+    if n == 0:
+        raise DflashError("invalid dims for a round workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def dflash_draft_round(model, taps, row_offsets, counts, kv, B, anchor_ids, draft_ids, ws, y_out=None, max_logit=None,
+                       stream=None):
+    n = taps[0].shape[0]
+    arr = (ctypes.c_void_p * len(taps))(*[_ptr(t) for t in taps])
+    return lib.dflash_draft_round(ctypes.byref(model.c), arr, taps[0].stride(0), n, _ptr(row_offsets), _ptr(counts),
+                                  ctypes.byref(kv.c), B, _ptr(anchor_ids), _ptr(draft_ids), _ptr(y_out),
+                                  _ptr(max_logit), _ptr(ws), ws.numel(), _stream(stream))
 
 
 def kv_prefill_workspace(dims, n, device="cuda"):

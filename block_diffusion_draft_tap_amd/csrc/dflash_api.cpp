@@ -689,8 +689,26 @@ int skinny_out_ffn(const dflash_model* M, int i, float* h, int rows, const Ws& w
 // layer's attn_norm or out_norm; null when none follows in this call); *an_ready says
 // on entry whether w.an already holds this layer's normalised input rows (bf16) and on
 // return whether it holds the next projection's
+// The round's new context rows for the one-pass layers: their K/V are produced by each
+// layer's own Q|K|V pass (rows of h_ctx, sequence b's rows row_offsets[b] ..; the first
+// counts[b] of them stored at len_old[b] + i, the lengths before the round)
+struct CtxRows {
+    const float* h_ctx;
+    int n;
+    const int32_t* row_offsets;
+    const int32_t* counts;
+    const int32_t* len_old;
+};
+
+// the fused pass applies: GEMV path with the in-register RMSNorm prologue, and the block rows
+// plus the context rows within one 16-row launch
+bool fused_qkv_ok(const dflash_dims& d, const Ws& w, int rows, int n) {
+    return !w.skinny && !prenorm(d) && d.wdtype != DFLASH_INT4G64 && d.d <= kRegNormMaxK && n > 0 &&
+           rows + n <= 16;
+}
+
 int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B, const Ws& w, hipStream_t s,
-              const void* next_gain, bool* an_ready) {
+              const void* next_gain, bool* an_ready, const CtxRows* ctx = nullptr) {
     const dflash_dims& d = M->dims;
     const dflash_layer& L = M->layers[i];
     const int wt = wtype_of(d.wdtype);
@@ -727,10 +745,38 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
             p.hkv = d.hkv;
             p.hd = d.hd;
         }
-        if (pro == PRO_PLAIN)
+        if (ctx && fused_qkv_ok(d, w, rows, ctx->n)) {
+            // one pass over the layer's Q|K|V rows: the block rows' Q, K_b, V_b as above, and
+            // the round's context rows' K, V into this layer's cache
+            p.x2 = ctx->h_ctx;
+            p.M1 = rows;
+            p.M = rows + ctx->n;
+            p.kv_col0 = d.hq * d.hd;
+            p.out_bf16 = d.wdtype != DFLASH_F32;
+            p.vt_col = (d.hq + d.hkv) * d.hd;
+            p.row_base = 0;
+            p.kcache = kv->k;
+            p.vcache = kv->v;
+            p.len = ctx->len_old;
+            p.row_offsets = ctx->row_offsets;
+            p.counts = ctx->counts;
+            p.B = kv->B;
+            p.cap = kv->cap;
+            p.kv_f32 = kv->dtype == DFLASH_F32;
+            p.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
+            const size_t esz = kv->dtype == DFLASH_F32 ? 4 : 2;
+            // this layer's caches: the launch's grid.y is 1, so layer 0 of the pointers
+            p.kcache = static_cast<char*>(kv->k) + (size_t)i * p.layer_stride * esz;
+            p.vcache = static_cast<char*>(kv->v) + (size_t)i * p.layer_stride * esz;
+            p.hkv = d.hkv;
+            p.hd = d.hd;
+            p.gamma = d.gamma;
+            DFL_HIP(launch_gemv(wt, PRO_NORM, EPI_QKVKV, 16, p, 1, s));
+        } else if (pro == PRO_PLAIN) {
             DFL_HIP(gemv_plain(d, wt, EPI_STORE, p, rows, w.rsp, s));
-        else
+        } else {
             DFL_HIP(gemv_rows(wt, pro, EPI_STORE, p, rows, s));
+        }
     }
     {  // O = softmax(Q [K_ctx; K_b]^T / sqrt(hd)) [V_ctx; V_b]
         AttnParams a;
@@ -849,7 +895,7 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
 // block init and every layer: H_d in w.hd; *an_ready says whether w.an holds the out
 // projection's normalised rows
 int forward_backbone(const dflash_model* M, const int32_t* anchor_ids, const dflash_kv* kv, int B, const Ws& w,
-                     hipStream_t s, bool* an_ready) {
+                     hipStream_t s, bool* an_ready, const CtxRows* ctx = nullptr) {
     const dflash_dims& d = M->dims;
     const int wt = wtype_of(d.wdtype);
     const bool init_sk = w.skinny && d.wdtype == DFLASH_BF16 && M->embed_in.dtype == DFLASH_BF16 &&
@@ -886,7 +932,7 @@ int forward_backbone(const dflash_model* M, const int32_t* anchor_ids, const dfl
     *an_ready = false;  // w.an holds the next projection's normalised rows
     for (int i = 0; i < d.nl; ++i)
         DFL_TRY(run_layer(M, i, w.hd, kv, B, w, s, i + 1 < d.nl ? M->layers[i + 1].attn_norm : M->out_norm,
-                          an_ready));
+                          an_ready, ctx));
     return DFLASH_OK;
 }
 
@@ -996,6 +1042,28 @@ int markov_argmax(const dflash_weight& w2t, const void* e1, int f32, int B, int 
     *nblocks = p.nblocks;
     DFL_HIP(gemv_rows(wtype_of(w2t.dtype), PRO_TAPS, EPI_ARGMAX, p, B, s));
     return DFLASH_OK;
+}
+
+// workspace of the round: the forward's own (which the context projection and a separate
+// append also use), then the new rows' H_ctx [B (gamma + 1)][d] fp32 and the lengths before
+// the round [B]
+struct Round {
+    Ws fw;
+    float* h_ctx;
+    int32_t* len_old;
+    size_t total;
+};
+Round round_layout(const dflash_dims& d, int B, int cap, void* wsp) {
+    Round rd{};
+    char* c = static_cast<char*>(wsp);
+    rd.fw = ws_layout(d, B, cap, wsp);
+    size_t off = align_up(rd.fw.total);
+    rd.h_ctx = c ? reinterpret_cast<float*>(c + off) : nullptr;
+    off += align_up((size_t)B * (d.gamma + 1) * d.d * 4);
+    rd.len_old = c ? reinterpret_cast<int32_t*>(c + off) : nullptr;
+    off += align_up((size_t)B * 4);
+    rd.total = off;
+    return rd;
 }
 
 // workspace of the DSpark forward: the forward's own, then the base logits [B gamma][V] fp32,
@@ -1473,6 +1541,53 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
     DFL_TRY(forward_backbone(M, anchor_ids, kv, B, w, s, &an_ready));
     // Y written straight into y_out when the caller wants it (bf16 for bf16/int4 models,
     // fp32 for fp32 models)
+    float* y = y_out ? static_cast<float*>(y_out) : w.y;
+    DFL_TRY(forward_out(M, B, w, s, an_ready, nullptr, y));
+    DFL_TRY(lm_head(M->lm_head, y, d.wdtype == DFLASH_F32, B * d.gamma, d.H, d.V, draft_ids, max_logit, w.lmv, w.lmi,
+                    s));
+    g_invocations++;
+    return DFLASH_OK;
+}
+
+size_t dflash_round_workspace_bytes(const dflash_dims* dims, int32_t B, int32_t cap) {
+    if (check_dims(dims) == DFLASH_EINVAL || B <= 0 || cap < 0) return 0;
+    return round_layout(*dims, B, cap, nullptr).total;
+}
+
+int dflash_draft_round(const dflash_model* M, const void* const* taps, int64_t tap_ld, int32_t n,
+                       const int32_t* row_offsets, const int32_t* counts, const dflash_kv* kv, int32_t B,
+                       const int32_t* anchor_ids, int32_t* draft_ids, void* y_out, float* max_logit, void* ws,
+                       size_t ws_bytes, void* stream) {
+    DFL_TRY(check_model(M));
+    const dflash_dims& d = M->dims;
+    if (n < 0 || !taps || !row_offsets || !anchor_ids || !draft_ids || B <= 0) return DFLASH_EINVAL;
+    DFL_TRY(check_kv(kv, d, B));
+    const Round rd = round_layout(d, B, kv->cap, ws);
+    if (!ws || ws_bytes < rd.total || n > B * (d.gamma + 1)) return DFLASH_ENOSPC;
+    DFL_TRY(gate());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Ws& w = rd.fw;
+    bool an_ready = false;
+    if (n > 0) {
+        // Eq 2 for the round's new rows (split partials, if any, in the forward's region)
+        const int rc = dflash_context_project(M, taps, tap_ld, n, rd.h_ctx, ws, w.total, stream);
+        if (rc != DFLASH_OK) return rc;
+        g_invocations--;  // counted once, below
+    }
+    CtxRows ctx{rd.h_ctx, n, row_offsets, counts, rd.len_old};
+    if (n > 0 && d.nl > 0 && fused_qkv_ok(d, w, B * d.gamma, n)) {
+        // lengths advance first (the attention reads them); the layers store the new rows'
+        // K/V at the saved lengths
+        DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s, rd.len_old));
+        DFL_TRY(forward_backbone(M, anchor_ids, kv, B, w, s, &an_ready, &ctx));
+    } else {
+        if (n > 0) {
+            const int rc = dflash_ctx_kv_append(M, rd.h_ctx, n, row_offsets, counts, kv, ws, w.total, stream);
+            if (rc != DFLASH_OK) return rc;
+            g_invocations--;
+        }
+        DFL_TRY(forward_backbone(M, anchor_ids, kv, B, w, s, &an_ready));
+    }
     float* y = y_out ? static_cast<float*>(y_out) : w.y;
     DFL_TRY(forward_out(M, B, w, s, an_ready, nullptr, y));
     DFL_TRY(lm_head(M->lm_head, y, d.wdtype == DFLASH_F32, B * d.gamma, d.H, d.V, draft_ids, max_logit, w.lmv, w.lmi,

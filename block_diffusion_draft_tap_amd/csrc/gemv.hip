@@ -171,6 +171,11 @@ __device__ __forceinline__ void load8_weight_row(const WeightPtr& t, int type, i
     }
 }
 
+// PRO_NORM source row m: below M1 from x, the rest from x2 (the fused QKV and context K/V pass)
+__device__ __forceinline__ const float* norm_row(const GemvParams& p, int m) {
+    return (p.x2 && m >= p.M1) ? p.x2 + (int64_t)(m - p.M1) * p.x_ld : p.x + (int64_t)m * p.x_ld;
+}
+
 template <int PRO>
 __device__ __forceinline__ void load_x8(const GemvParams& p, int layer, int m, int k, const float* rinv,
                                         float (&v)[8]) {
@@ -186,7 +191,7 @@ __device__ __forceinline__ void load_x8(const GemvParams& p, int layer, int m, i
         else
             load8_bf16(reinterpret_cast<const uint16_t*>(p.x) + off, v);
     } else if constexpr (PRO == PRO_NORM) {
-        load8_f32(p.x + (int64_t)m * p.x_ld + k, v);
+        load8_f32(norm_row(p, m) + k, v);
         const float r = rinv[m];
         const void* g = p.gain[layer];
 #pragma unroll
@@ -361,11 +366,12 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
     // EPI_KV: sequence and cache position of each activation row, resolved once
     int* meta_b = reinterpret_cast<int*>(rinv + MAXM);
     int* meta_pos = meta_b + MAXM;
-    if constexpr (EPI == EPI_KV) {
+    if constexpr (EPI == EPI_KV || EPI == EPI_QKVKV) {
         if (tid < MAXM) {
             int b = 0, pos = -1;
-            if (tid < p.M) {
-                const int gm = p.row_base + tid;
+            const int m0 = EPI == EPI_QKVKV ? p.M1 : 0;  // the first context row
+            if (tid < p.M && tid >= m0) {
+                const int gm = p.row_base + tid - m0;
                 while (b + 1 < p.B && p.row_offsets[b + 1] <= gm) ++b;
                 const int rows_b = p.row_offsets[b + 1] - p.row_offsets[b];
                 const int i = gm - p.row_offsets[b];
@@ -378,7 +384,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
         }
     }
 
-    constexpr bool kRegNorm = (PRO == PRO_NORM) && (WT != W_I4) && (MAXM == 8);
+    constexpr bool kRegNorm = (PRO == PRO_NORM) && (WT != W_I4) && (MAXM == 8 || MAXM == 16);
     if (kHeadY && yfast) {
         // rows at or past M stay unwritten: their products land in accumulator slots that
         // never reach a result
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
             for (int u = 0; u < UM; ++u) {
                 const int k = lane * 8 + u * 512;
                 if (m < p.M && k < K) {
-                    load8_f32(p.x + (int64_t)m * p.x_ld + k, xr[j][u]);
+                    load8_f32(norm_row(p, m) + k, xr[j][u]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) xr[j][u][e] = 0.f;
@@ -463,7 +469,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
     } else {
         if constexpr (PRO == PRO_NORM) {
             for (int m = wave; m < p.M; m += 4) {
-                const float* xr = p.x + (int64_t)m * p.x_ld;
+                const float* xr = norm_row(p, m);
                 float s = 0.f;
                 for (int k = lane * 4; k < K; k += 256) {
                     const float4 a = *reinterpret_cast<const float4*>(xr + k);
@@ -590,6 +596,38 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
                     } else {
                         float* o = p.out + ((int64_t)layer * gridDim.z + blockIdx.z) * p.split_stride;
                         o[(int64_t)m * p.out_ld + n] = p.round_out ? round_bf16(y) : y;
+                    }
+                } else if constexpr (EPI == EPI_QKVKV) {
+                    if (m < p.M1) {  // block row: Q | K_b | V_b
+                        if (p.out_bf16) {
+                            if (n >= p.vt_col) {
+                                const int row = p.row_base + m, bb = row / p.gamma, key = row - bb * p.gamma;
+                                const int c = n - p.vt_col, head = c / p.hd, dim = c - head * p.hd;
+                                p.vt[(((int64_t)bb * p.hkv + head) * p.hd + dim) * 32 + key] =
+                                    (uint16_t)f32_to_bf16_bits(y);
+                            } else {
+                                reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.out_ld + n] =
+                                    (uint16_t)f32_to_bf16_bits(y);
+                            }
+                        } else {
+                            p.out[(int64_t)m * p.out_ld + n] = y;
+                        }
+                    } else if (n >= p.kv_col0) {  // context row: its key or value into the cache
+                        const int b = meta_b[m], pos = meta_pos[m];
+                        if (pos >= 0) {
+                            const int kvw = p.hkv * p.hd, c = n - p.kv_col0;
+                            const int which = c / kvw;
+                            const int head = (c - which * kvw) / p.hd;
+                            const int dim = c - which * kvw - head * p.hd;
+                            const int64_t hb = ((int64_t)b * p.hkv + head) * p.cap * p.hd;
+                            const int64_t off = (int64_t)layer * p.layer_stride + hb +
+                                                (which ? (int64_t)dim * p.cap + pos : (int64_t)pos * p.hd + dim);
+                            void* base = which ? p.vcache : p.kcache;
+                            if (p.kv_f32)
+                                static_cast<float*>(base)[off] = y;
+                            else
+                                static_cast<uint16_t*>(base)[off] = (uint16_t)f32_to_bf16_bits(y);
+                        }
                     }
                 } else if constexpr (EPI == EPI_RESID) {
                     float* o = p.out + (int64_t)m * p.out_ld + n;
@@ -800,6 +838,8 @@ hipError_t launch_gemv(int wtype, int pro, int epi, int maxm, const GemvParams& 
     if (pro == PRO_PLAIN && epi == EPI_GATED) return launch_wt<PRO_PLAIN, EPI_GATED, 8>(wtype, p, layers, s, maxm);
     if (pro == PRO_NORM && epi == EPI_GATED) return launch_wt<PRO_NORM, EPI_GATED, 8>(wtype, p, layers, s, maxm);
     if (pro == PRO_TAPS && epi == EPI_ARGMAX) return launch_wt<PRO_TAPS, EPI_ARGMAX, 8>(wtype, p, layers, s, maxm);
+    if (pro == PRO_NORM && epi == EPI_QKVKV && maxm == 16 && wtype != W_I4)
+        return launch_wt<PRO_NORM, EPI_QKVKV, 16>(wtype, p, layers, s, maxm);
 #undef DFL_CASE
     return hipErrorInvalidValue;
 }

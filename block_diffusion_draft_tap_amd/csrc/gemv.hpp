@@ -29,7 +29,7 @@ namespace dfl {
 
 enum WType { W_F32 = 0, W_BF16 = 1, W_I4 = 2 };
 enum { PRO_PLAIN = 0, PRO_NORM = 1, PRO_TAPS = 2, PRO_GATHER = 3 };
-enum { EPI_STORE = 0, EPI_RESID = 1, EPI_GATED = 2, EPI_KV = 3, EPI_BLOCKINIT = 4, EPI_ARGMAX = 5 };
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_GATED = 2, EPI_KV = 3, EPI_BLOCKINIT = 4, EPI_ARGMAX = 5, EPI_QKVKV = 6 };
 
 constexpr int kMaxTaps = 8;
 constexpr int kMaxLayers = 16;
@@ -57,6 +57,8 @@ struct GemvParams {
     // prologue
     const float* x;      // PRO_PLAIN / PRO_NORM: fp32 rows (PRO_PLAIN: bf16 rows when src_f32 = 0)
     int64_t x_ld;
+    const float* x2;     // PRO_NORM with x2: rows m >= M1 come from x2 + (m - M1) * x_ld
+    int M1;
     int64_t x_layer_stride;  // PRO_PLAIN: layer y's rows start at x + y * x_layer_stride elements
     const void* gain[kMaxLayers];  // PRO_NORM: per-layer gain vectors [K]
     int gain_f32;
@@ -89,6 +91,11 @@ struct GemvParams {
     int row_base;        // global index of activation row 0 of this launch
     int B, hkv, hd, cap, kv_f32;
     int64_t layer_stride;  // elements per layer in the cache
+    // EPI_QKVKV (one pass over a layer's fused Q|K|V rows): activation rows m < M1 are block
+    // rows stored as EPI_STORE does (bf16 rows, values head-dim major through vt); rows
+    // m >= M1 are context rows row_base + m - M1 whose key / value columns (n >= kv_col0)
+    // go to the cache as EPI_KV does, at len[b] + i (len: the lengths before this round)
+    int kv_col0;
     // EPI_BLOCKINIT
     const void* block_pos;  // [gamma, d]
     const void* mask_emb;   // [gamma-1, d]

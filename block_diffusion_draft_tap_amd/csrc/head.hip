@@ -288,11 +288,14 @@ __global__ __launch_bounds__(kBlock) void block_fill_kernel(float* h, int gamma,
         row[n] = load_gain(mask_emb, gain_f32, (k - 1) * d + n) + load_gain(block_pos, gain_f32, k * d + n);
 }
 
-__global__ void advance_len_kernel(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap) {
+__global__ void advance_len_kernel(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap,
+                                   int32_t* save) {
     for (int b = threadIdx.x; b < B; b += blockDim.x) {
         const int rows = row_offsets[b + 1] - row_offsets[b];
         const int add = counts ? min(counts[b], rows) : rows;
-        len[b] = min(cap, len[b] + max(add, 0));
+        const int old = len[b];
+        if (save) save[b] = old;
+        len[b] = min(cap, old + max(add, 0));
     }
 }
 
@@ -384,9 +387,9 @@ hipError_t launch_block_fill(float* h, int B, int gamma, int d, const void* bloc
 }
 
 hipError_t launch_advance_len(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap,
-                              hipStream_t s) {
+                              hipStream_t s, int32_t* save) {
     (void)hipGetLastError();  // report only this launch's status
-    hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, s, len, row_offsets, counts, B, cap);
+    hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, s, len, row_offsets, counts, B, cap, save);
     return hipGetLastError();
 }
 

@@ -328,6 +328,28 @@ int dflash_draft_forward_dspark(const dflash_model* M, const dflash_dspark_head*
                                 int32_t* draft_ids, float* conf, int32_t* lengths, void* y_out, void* ws,
                                 size_t ws_bytes, void* stream);
 
+/* One drafting round in one call (page 3, forwardRows with a retained
+ * context: the new rows projected by Eq 2, their per-layer K/V appended, then
+ * the block drafted; projectContextRows notes that the context half is
+ * independent of the block and can be retained): the same results as
+ *   dflash_context_project(taps, n) -> h_ctx;
+ *   dflash_ctx_kv_append(h_ctx, row_offsets, counts);
+ *   dflash_draft_forward(anchor_ids)
+ * with these arguments. Where a layer's block rows and the new context rows fit
+ * one projection pass (the GEMV path: bf16 or f32 weights, d <= 2048 and
+ * B*gamma + n <= 16 rows), the context rows' K/V come out of that layer's own
+ * Q|K|V pass, so each layer's K/V weights are read once per round; otherwise
+ * the calls run one after the other.
+ *   taps, tap_ld, n:        as in dflash_context_project (n <= B*(gamma+1)).
+ *   row_offsets, counts:    as in dflash_ctx_kv_append.
+ *   the rest:               as in dflash_draft_forward.
+ * Workspace: dflash_round_workspace_bytes(dims, B, kv->cap). */
+int dflash_draft_round(const dflash_model* M, const void* const* taps, int64_t tap_ld, int32_t n,
+                       const int32_t* row_offsets, const int32_t* counts, const dflash_kv* kv, int32_t B,
+                       const int32_t* anchor_ids, int32_t* draft_ids, void* y_out, float* max_logit, void* ws,
+                       size_t ws_bytes, void* stream);
+size_t dflash_round_workspace_bytes(const dflash_dims* dims, int32_t B, int32_t cap);
+
 /* Greedy ids under a borrowed LM head (page 3, #baseLogits and the argmax
  * step of forwardRows): ids[r] = argmax_v y[r] . E_out[v], lowest index on
  * ties; logits are fp32 accumulations and are never materialised.

@@ -536,3 +536,89 @@ def test_trace_stamps_leave_results_unchanged(name):
     durs = bd.traced_durations_s(stamps, recs)
     assert all(0 < t < 0.1 for t in durs)
     log(f"[{name}] traced launches: " + ", ".join(f"{r['kernel']} {t * 1e6:.1f}us" for r, t in zip(recs, durs)))
+
+
+# cases whose round fits one 16-row Q|K|V pass per layer (block rows plus new context rows,
+# fp32 or bf16 GEMV path): their context rows' K/V come out of that pass, in a different
+# summation order from the separate append's kernels
+ROUND_FUSED = {"tiny", "default", "gamma1"}
+
+
+@pytest.mark.parametrize("name", ["tiny", "default", "gamma1", "gqa_bf16", "wide4_b1", "batched_small", "nl0",
+                                  "empty_ctx"])
+def test_round_matches_separate_calls(name):
+    """One round in one call (the new rows projected, their K/V appended, the
+    block drafted) against the three separate calls and the oracle. Where the
+    layers take the new rows' K/V in their own Q|K|V pass the caches agree to
+    the parity tolerance; otherwise the round runs the separate calls' kernels
+    and everything is bitwise equal."""
+    s = get(name)
+    d = s.dims
+    B, W = s.B, d.gamma + 1
+    fused = name in ROUND_FUSED
+
+    def clone_kv():
+        kv = dfa.KVCache(d, B, s.cap)
+        kv.k.copy_(s.kv.k)
+        kv.v.copy_(s.kv.v)
+        kv.len.copy_(s.kv.len)
+        return kv
+
+    kv1, kv2 = clone_kv(), clone_kv()
+    taps = [gen.make_taps(d, 0, W, stream="round", seq=b) for b in range(B)]
+    taps_d = [dev(np.concatenate([taps[b][j] for b in range(B)])) for j in range(d.m)]
+    offs = torch.arange(0, (B + 1) * W, W, dtype=torch.int32, device="cuda")
+    counts_h = ((np.arange(B) + 2) % W + 1).astype(np.int32)
+    counts = torch.from_numpy(counts_h).cuda()
+    anchors = gen.make_anchors(d, 5)
+    a_d = torch.from_numpy(anchors).cuda()
+    mk = lambda: (torch.empty(B, d.gamma, dtype=torch.int32, device="cuda"),
+                  torch.empty(B, d.gamma, d.H, dtype=s.dm.act_dtype, device="cuda"))
+    ids1, y1 = mk()
+    ws = dfa.workspace(d, B, kv1.cap)
+    h = torch.empty(B * W, d.d, dtype=torch.float32, device="cuda")
+    bd.check(dfa.dflash_context_project(s.dm, taps_d, h, ws), "project")
+    bd.check(dfa.dflash_ctx_kv_append(s.dm, h, offs, counts, kv1, None if fused else ws), "append")
+    bd.check(dfa.dflash_draft_forward(s.dm, a_d, kv1, B, ids1, ws, y_out=y1), "forward")
+    ids2, y2 = mk()
+    rws = dfa.round_workspace(d, B, kv2.cap)
+    n0 = bd.dflash_invocations()
+    bd.check(dfa.dflash_draft_round(s.dm, taps_d, offs, counts, kv2, B, a_d, ids2, rws, y_out=y2), "round")
+    torch.cuda.synchronize()
+    assert bd.dflash_invocations() == n0 + 1
+    assert torch.equal(kv1.len, kv2.len)
+    assert kv2.len.cpu().tolist() == [s.lengths[b] + int(counts_h[b]) for b in range(B)]
+    if fused:
+        # untouched cache slots stay bitwise; the new rows agree to the tolerance
+        for b in range(B):
+            L0, L1 = s.lengths[b], s.lengths[b] + int(counts_h[b])
+            assert torch.equal(kv1.k[:, b, :, :L0], kv2.k[:, b, :, :L0])
+            assert torch.equal(kv1.k[:, b, :, L1:], kv2.k[:, b, :, L1:])
+            assert torch.equal(kv1.v[:, b, ..., :L0], kv2.v[:, b, ..., :L0])
+            assert torch.equal(kv1.v[:, b, ..., L1:], kv2.v[:, b, ..., L1:])
+            assert rel_err(kv2.k[:, b, :, L0:L1], kv1.k[:, b, :, L0:L1].double().cpu().numpy()) <= tol(d)
+            assert rel_err(kv2.v[:, b, ..., L0:L1], kv1.v[:, b, ..., L0:L1].double().cpu().numpy()) <= tol(d)
+        assert rel_err(y2, y1.double().cpu().numpy()) <= tol(d)
+    else:
+        assert torch.equal(kv1.k, kv2.k) and torch.equal(kv1.v, kv2.v)
+        assert torch.equal(ids1, ids2) and torch.equal(y1, y2)
+    # the oracle: the retained context plus the committed rows, then the forward
+    ctx = O.Context(d.nl, B, d.hkv, d.hd)
+    for i in range(d.nl):
+        for b in range(B):
+            ctx.append(i, b, s.ctx.k[i][b].copy(), s.ctx.v[i][b].copy())
+    for b in range(B):
+        Hc = O.context_project(taps[b], s.w["W_c"], s.w["ctx_norm"], d.eps)
+        O.append_context(ctx, s.w, d, Hc, [[]] * b + [list(range(W))] + [[]] * (B - b - 1),
+                         [0] * b + [int(counts_h[b])] + [0] * (B - b - 1), s.fm)
+    ref_ids, ex = O.draft_forward(s.w, d, ctx, anchors, s.fm, return_all=True)
+    assert rel_err(y2, ex["Y"]) <= tol(d)
+    c = compare_ids(ids2, ref_ids, ex["logits"], gpu_y=y2, head=s.w["E_out"], what=f"round {name}")
+    for i in range(d.nl):
+        for b in range(B):
+            L = ctx.length(b)
+            assert rel_err(kv2.k[i, b, :, :L].permute(1, 0, 2), ctx.k[i][b]) <= tol(d)
+            assert rel_err(kv2.v[i, b, :, :, :L].permute(2, 0, 1), ctx.v[i][b]) <= tol(d)
+    same = torch.equal(kv1.k, kv2.k) and torch.equal(kv1.v, kv2.v) and torch.equal(y1, y2)
+    log(f"[{name}] round in one call ({'one Q|K|V pass' if fused else 'separate kernels'}): bitwise equal to "
+        f"the separate calls: {same}; ids decided {c['decided']}/{c['total']}")
