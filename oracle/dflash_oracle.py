@@ -36,12 +36,28 @@ Plain numpy in float64, written from the pages' definition of the method:
     committed=6" for block 8): accepted = longest prefix of drafts equal to
     the target's argmax, committed = accepted + 1.
 
+  * The DFlash2 variant (page "Inco Hacks Native: DFlash 2 Speculation",
+    section 1: a sliding-window drafter; section 3: the target verifies the
+    block): rotary positions on Q and K, attention over only the last
+    `window` context keys, and verification that scores the target's own
+    hidden states with the borrowed LM head instead of given logits.
+
 Readings where the pages are silent (each listed in the design notes):
   RMSNorm is x * (mean(x^2) + eps)^-1/2 * g with eps = 1e-6; attention scale
-  is hd^-1/2 with no positional rotation; query head h reads kv head
+  is hd^-1/2, with no positional rotation unless the variant's rope_theta is
+  set; query head h reads kv head
   h // (hq / hkv); argmax ties resolve to the lowest index; the FFN
   activation is the tanh-form GELU or SiLU per the workload; the rows
   appended to the context each round are the `committed` verified rows.
+  DFlash2 variant (the pages give neither the window nor the rotation): the
+  rotation pairs dims i and i + hd/2 of a head (the rotate-half layout of
+  the Qwen family the drafter pairs with) at the angle position *
+  rope_theta^(-2i/hd); context row t sits at position t and block row k at
+  position len + k (the block continues the context: row 0 holds the
+  anchor, the token after the last retained row); the window keeps the last
+  `window` context keys for every block row (0 = the whole context); the
+  verify hidden states are the target's final hidden rows, already normed,
+  that the borrowed LM head scores.
 
 Modes:
   pure      float64 throughout (the fp32 workloads are compared to this).
@@ -49,7 +65,8 @@ Modes:
             the GPU contract rounds: every input of a weight product (the
             normalised block, context and FFN inputs, the attention output,
             the FFN product, the out-norm output), the Q/K/V projections, the
-            context K/V cache and the out-projection result Y.
+            context K/V cache and the out-projection result Y; with rotary
+            positions, Q and K are rounded once more after their rotation.
 
 Weights are in the synthetic generator's storage formats: float32 arrays,
 uint16 bfloat16 bit patterns, or 4-bit groups dict(codes, scales, biases)
@@ -190,14 +207,36 @@ def context_project(taps, W_c, g_ctx, eps):
 # Eq 3, context half: per-layer K/V of the context
 
 
-def context_kv(H_ctx, g_attn, W_k, W_v, hkv, hd, eps, faithful):
+def rope_inv_freq(hd, theta):
+    """Angular frequency of each rotated pair: theta^(-2i/hd), i < hd/2."""
+    return float(theta) ** (-2.0 * np.arange(hd // 2) / hd)
+
+
+def rope(x, positions, theta):
+    """Rotary positions (DFlash2 variant; the pairing is this library's
+    reading): x [n, heads, hd] at positions [n]; dims i and i + hd/2 of each
+    head turn by the angle position * theta^(-2i/hd). theta 0: no rotation."""
+    if not theta:
+        return x
+    hd = x.shape[-1]
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * rope_inv_freq(hd, theta)[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = x[..., : hd // 2], x[..., hd // 2:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def context_kv(H_ctx, g_attn, W_k, W_v, hkv, hd, eps, faithful, positions=None, theta=0.0):
     """One layer's context keys/values [n, hkv, hd] (page 3,
-    projectContextRows: the layer's own attn_norm, then its own W_K, W_V)."""
+    projectContextRows: the layer's own attn_norm, then its own W_K, W_V);
+    with rotary positions, each key turned at its row's position."""
     n = _r(rmsnorm(H_ctx, dense(g_attn), eps), faithful)
     K = _r(n @ dense(W_k).T, faithful)
     V = _r(n @ dense(W_v).T, faithful)
     rows = H_ctx.shape[0]
-    return K.reshape(rows, hkv, hd), V.reshape(rows, hkv, hd)
+    K = K.reshape(rows, hkv, hd)
+    if theta:
+        K = _r(rope(K, positions, theta), faithful)
+    return K, V.reshape(rows, hkv, hd)
 
 
 class Context:
@@ -230,8 +269,10 @@ def append_context(ctx, weights, dims, H_ctx, seq_rows, counts, faithful):
             take = list(rows)[: int(counts[b])]
             if not take:
                 continue
+            theta = getattr(dims, "rope_theta", 0.0)
+            rot = {"positions": ctx.k[i][b].shape[0] + np.arange(len(take)), "theta": theta} if theta else {}
             K, V = context_kv(H_ctx[take], weights[f"bb.{i}.attn_norm"], weights[f"bb.{i}.k"],
-                              weights[f"bb.{i}.v"], dims.hkv, dims.hd, dims.eps, faithful)
+                              weights[f"bb.{i}.v"], dims.hkv, dims.hd, dims.eps, faithful, **rot)
             ctx.append(i, b, K, V)
 
 
@@ -265,9 +306,12 @@ def attention(Q, K, V, scale):
     return O
 
 
-def draft_layer(H_d, ctx, layer, weights, dims, faithful, attn=attention):
+def draft_layer(H_d, ctx, layer, weights, dims, faithful, attn=attention, start=None):
     """One KV-injection layer over all sequences (page 3, #layer, Eq 3).
-    H_d [B, gamma, d] -> new H_d. ctx.k[layer][b] is read, never written."""
+    H_d [B, gamma, d] -> new H_d. ctx.k[layer][b] is read, never written.
+    DFlash2 variant: block row k of sequence b sits at position start[b] + k
+    (start defaults to the retained context's length) and only the last
+    dims.window context keys are attended (0: all)."""
     B, G, d = H_d.shape
     hq, hkv, hd = dims.hq, dims.hkv, dims.hd
     w = lambda n: weights[f"bb.{layer}.{n}"]
@@ -275,6 +319,7 @@ def draft_layer(H_d, ctx, layer, weights, dims, faithful, attn=attention):
     Wg, Wu, Wd = dense(w("gate")), dense(w("up")), dense(w("down"))
     g_attn, g_ffn = dense(w("attn_norm")), dense(w("ff_norm"))
     act = ACTS[dims.act]
+    theta, window = getattr(dims, "rope_theta", 0.0), getattr(dims, "window", 0)
     out = np.empty_like(H_d)
     for b in range(B):
         x = H_d[b]
@@ -282,8 +327,14 @@ def draft_layer(H_d, ctx, layer, weights, dims, faithful, attn=attention):
         Q = _r(n @ Wq.T, faithful).reshape(G, hq, hd)
         Kb = _r(n @ Wk.T, faithful).reshape(G, hkv, hd)
         Vb = _r(n @ Wv.T, faithful).reshape(G, hkv, hd)
-        K = np.concatenate([ctx.k[layer][b], Kb], axis=0)
-        V = np.concatenate([ctx.v[layer][b], Vb], axis=0)
+        Kc, Vc = ctx.k[layer][b], ctx.v[layer][b]
+        if theta:
+            pos = (Kc.shape[0] if start is None else int(start[b])) + np.arange(G)
+            Q, Kb = _r(rope(Q, pos, theta), faithful), _r(rope(Kb, pos, theta), faithful)
+        if window > 0:
+            Kc, Vc = Kc[max(0, Kc.shape[0] - window):], Vc[max(0, Vc.shape[0] - window):]
+        K = np.concatenate([Kc, Kb], axis=0)
+        V = np.concatenate([Vc, Vb], axis=0)
         O = _r(attn(Q, K, V, hd ** -0.5).reshape(G, hq * hd), faithful)
         x = x + O @ Wo.T
         n2 = _r(rmsnorm(x, g_ffn, dims.eps), faithful)
@@ -360,6 +411,17 @@ def verify_greedy(target_logits, draft_ids, lengths=None):
         ids[b, : committed[b]] = t[b, : committed[b]]
     nxt = t[np.arange(B), accepted].astype(np.int32)
     return accepted, committed.astype(np.int32), ids, nxt
+
+
+def verify_from_hidden(target_hidden, E_out, draft_ids, lengths=None):
+    """Greedy verification from the target's own hidden states (DFlash2
+    variant: the target verifies the block, page "Inco Hacks Native: DFlash 2
+    Speculation", section 3): target_hidden [B, gamma+1, H] are the target's
+    final hidden rows at the verify positions; the borrowed LM head scores
+    them (logits = hidden E_out^T) and the greedy rule above decides."""
+    B, W, H = target_hidden.shape
+    logits = dense(target_hidden.reshape(B * W, H)) @ dense(E_out).T
+    return verify_greedy(logits.reshape(B, W, -1), draft_ids, lengths)
 
 
 # ----------------------------------------------------------------------------
@@ -449,15 +511,16 @@ def dspark_forward(weights, dims, ctx, anchor_ids, faithful, thresholds=None, mi
 # composition
 
 
-def draft_forward(weights, dims, ctx, anchor_ids, faithful, return_all=False):
+def draft_forward(weights, dims, ctx, anchor_ids, faithful, return_all=False, start=None):
     """Block init, every layer, out projection, LM head argmax (page 3,
     forwardRows with the retained context). Returns draft ids [B, gamma]
-    (and the intermediates when return_all)."""
+    (and the intermediates when return_all). start: the block's first
+    position per sequence under rotary positions (default: context length)."""
     H = block_init(anchor_ids, weights["E_in"], weights["tok_proj"], weights["mask_emb"],
                    weights["block_pos"], dims.gamma, faithful)
     layers = [H]
     for i in range(dims.nl):
-        H = draft_layer(H, ctx, i, weights, dims, faithful)
+        H = draft_layer(H, ctx, i, weights, dims, faithful, start=start)
         layers.append(H)
     Y = out_project(H, weights["out_norm"], weights["out_proj"], dims.eps, faithful)
     B, G = H.shape[0], dims.gamma

@@ -51,6 +51,9 @@ class Dims:
     eps: float = 1e-6
     L_max: Optional[int] = None   # ragged batches: lengths drawn from [L, L_max]
     r: int = 0                    # rank of the DSpark sequential (Markov) head; 0 = no head
+    window: int = 0               # DFlash2: context keys attended, from the end; 0 = all
+    rope_theta: float = 0.0       # DFlash2: rotary base; 0 = no rotary positions
+    verify: str = "logits"        # what the target hands the verify: "logits" or "hidden" states
 
     @property
     def qkv_rows(self) -> int:
@@ -81,7 +84,16 @@ BATCHED = Dims("batched", H=5120, m=5, d=5120, nl=5, hq=40, hkv=8, hd=128, F=174
                act=ACT_SILU, gamma=7, L=8192, V=151936, B=16, wdtype=WDTYPE_BF16,
                L_max=16384)
 
-CONFIGS = {c.name: c for c in (TINY, DEFAULT, WIDE, WIDE4, BATCHED)}
+# The DFlash2 drafter (page "Inco Hacks Native: DFlash 2 Speculation", section 1): the wide
+# geometry in 4-bit weights, block 8 (gamma 7), a sliding window over the context, rotary
+# positions, and a verify that scores the target's hidden states with the borrowed head. The
+# page gives neither the window nor the rotary base: 2048 keys and base 1e6 (the Qwen3
+# family's) are this library's choices.
+DFLASH2 = Dims("dflash2", H=5120, m=5, d=5120, nl=5, hq=40, hkv=8, hd=128, F=17408,
+               act=ACT_SILU, gamma=7, L=8192, V=151936, B=1, wdtype=WDTYPE_INT4G64,
+               window=2048, rope_theta=1e6, verify="hidden")
+
+CONFIGS = {c.name: c for c in (TINY, DEFAULT, WIDE, WIDE4, BATCHED, DFLASH2)}
 
 
 def scaled(base: Dims, **kw) -> Dims:
