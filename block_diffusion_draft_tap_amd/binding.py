@@ -28,7 +28,8 @@ EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "df
            "dflash_verify_workspace_bytes", "dflash_kv_prefill_workspace_bytes", "dflash_trace_begin",
            "dflash_trace_end", "dflash_lm_head_workgroups", "dflash_wall_clock_hz", "dflash_verify_greedy_noalloc",
            "dflash_verify_noalloc_max_bytes", "dflash_dspark_workspace_bytes", "dflash_draft_forward_dspark",
-           "dflash_verify_greedy_lengths", "dflash_draft_round", "dflash_round_workspace_bytes"]
+           "dflash_verify_greedy_lengths", "dflash_draft_round", "dflash_round_workspace_bytes",
+           "dflash_verify_from_hidden", "dflash_verify_hidden_workspace_bytes"]
 DFLASH_TRACE_LM_HEAD, DFLASH_TRACE_ATTENTION, DFLASH_TRACE_PROJECTIONS = 1, 2, 4
 
 
@@ -40,7 +41,8 @@ class dflash_dims(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("m", ctypes.c_int32), ("d", ctypes.c_int32), ("nl", ctypes.c_int32),
                 ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("hd", ctypes.c_int32), ("F", ctypes.c_int32),
                 ("V", ctypes.c_int32), ("gamma", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("act", ctypes.c_int32), ("wdtype", ctypes.c_int32)]
+                ("act", ctypes.c_int32), ("wdtype", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float)]
 
 
 class dflash_weight(ctypes.Structure):
@@ -121,6 +123,10 @@ def _load():
     lib.dflash_draft_round.restype = ctypes.c_int
     lib.dflash_round_workspace_bytes.argtypes = [P(dflash_dims), I32, I32]
     lib.dflash_round_workspace_bytes.restype = SZ
+    lib.dflash_verify_from_hidden.argtypes = [P(dflash_model), VP, I32, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+    lib.dflash_verify_from_hidden.restype = ctypes.c_int
+    lib.dflash_verify_hidden_workspace_bytes.argtypes = [P(dflash_dims), I32]
+    lib.dflash_verify_hidden_workspace_bytes.restype = SZ
     lib.dflash_verify_noalloc_max_bytes.argtypes = []
     lib.dflash_verify_noalloc_max_bytes.restype = SZ
     lib.dflash_trace_begin.argtypes = [I32, VP, ctypes.c_int64]
@@ -176,7 +182,8 @@ _ACT = {"gelu_tanh": DFLASH_ACT_GELU_TANH, "silu": DFLASH_ACT_SILU}
 def make_dims(d):
     """dflash_dims from any object with the drafter geometry attributes."""
     return dflash_dims(H=d.H, m=d.m, d=d.d, nl=d.nl, hq=d.hq, hkv=d.hkv, hd=d.hd, F=d.F, V=d.V, gamma=d.gamma,
-                       eps=float(d.eps), act=_ACT[d.act], wdtype=_WD[d.wdtype])
+                       eps=float(d.eps), act=_ACT[d.act], wdtype=_WD[d.wdtype], window=int(getattr(d, "window", 0)),
+                       rope_theta=float(getattr(d, "rope_theta", 0.0)))
 
 
 def _to_dev(a, device):
@@ -395,6 +402,21 @@ def dflash_verify_greedy_lengths(target_logits, draft_ids, lengths, accepted, co
     return lib.dflash_verify_greedy_lengths(_ptr(target_logits), _ptr(draft_ids), _ptr(lengths), B, W - 1, V,
                                             _ptr(accepted), _ptr(committed), _ptr(ids), _ptr(next_anchor),
                                             _ptr(ws), ws.numel(), _stream(stream))
+
+
+def verify_hidden_workspace(dims, B, device="cuda"):
+    n = lib.dflash_verify_hidden_workspace_bytes(ctypes.byref(make_dims(dims)), B)
+    if n == 0:
+        raise DflashError("invalid dims for a verify-from-hidden workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def dflash_verify_from_hidden(model, target_hidden, draft_ids, accepted, committed, ids, ws, lengths=None,
+                              next_anchor=None, stream=None):
+    B = target_hidden.shape[0]
+    return lib.dflash_verify_from_hidden(ctypes.byref(model.c), _ptr(target_hidden), B, _ptr(draft_ids),
+                                         _ptr(lengths), _ptr(accepted), _ptr(committed), _ptr(ids),
+                                         _ptr(next_anchor), _ptr(ws), ws.numel(), _stream(stream))
 
 
 def round_workspace(dims, B, cap, device="cuda"):

@@ -99,9 +99,12 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     const int qpg = p.hq / p.hkv;
     const int R = qpg * p.gamma;
     const int lenb = min(max(p.len[b], 0), p.cap);
-    // work units: the context's 32-key chunks, then the block's gamma keys;
-    // wavefronts take equal runs of consecutive units
-    const int nch = (lenb + kChunk - 1) / kChunk;
+    // work units: the 32-key chunks from the one holding the first attended key (key 0,
+    // or the window's first), then the block's gamma keys; wavefronts take equal runs of
+    // consecutive units
+    const int kbeg = p.window > 0 ? max(0, lenb - p.window) : 0;
+    const int cb = kbeg & ~(kChunk - 1);
+    const int nch = (lenb - cb + kChunk - 1) / kChunk;
     const int nunits = nch + 1;
     const int upw = (nunits + 4 * p.nsplit - 1) / (4 * p.nsplit);
     const int u_begin = min(nunits, (s * 4 + wave) * upw);
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     auto load_k = [&](const int u) {
         const uint16_t *k0, *k1;
         if (u != nch) {
-            k0 = kc + (int64_t)(u * kChunk + col) * HD + 8 * grp;
+            k0 = kc + (int64_t)(cb + u * kChunk + col) * HD + 8 * grp;
             k1 = k0 + 16 * HD;
         } else {
             k0 = qrow0 + (int64_t)min(col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         const uint16_t* vp;
         int64_t vstride;
         if (u != nch) {
-            vp = vc + (int64_t)col * p.cap + u * kChunk + 8 * grp;
+            vp = vc + (int64_t)col * p.cap + cb + u * kChunk + 8 * grp;
             vstride = 16 * (int64_t)p.cap;
         } else {
             vp = vblk + col * kChunk + 8 * grp;
@@ -180,7 +183,10 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     }
 
     for (int u = u_begin; u < u_end; ++u) {
-        const int nvalid = (u == nch) ? p.gamma : min(kChunk, lenb - u * kChunk);
+        const int nvalid = (u == nch) ? p.gamma : min(kChunk, lenb - cb - u * kChunk);
+        // keys of the first chunk before the window's first key take no weight (they are
+        // held context rows: their values are finite and meet zero probabilities)
+        const int lo = (u == 0 && u != nch) ? kbeg - cb : 0;
 
         f32x4 sacc[NRT][2];
 #pragma unroll
@@ -193,7 +199,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
             }
         if (u + 1 < u_end) load_k(u + 1);
         // online softmax; lane holds rows 4*grp+e, keys col and 16+col
-        const bool v0ok = col < nvalid, v1ok = 16 + col < nvalid;
+        const bool v0ok = col >= lo && col < nvalid, v1ok = 16 + col >= lo && 16 + col < nvalid;
         const bool rescale = (u != u_begin);  // o is still zero on a wavefront's first unit
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
             for (int e = 0; e < 4; ++e) {
                 const float s0 = v0ok ? sacc[rt][0][e] * sl2 : -INFINITY;
                 const float s1 = v1ok ? sacc[rt][1][e] * sl2 : -INFINITY;
-                const float mn = fmaxf(m[rt][e], row16_max(fmaxf(s0, s1)));  // finite: key 0 is valid
+                const float mn = fmaxf(m[rt][e], row16_max(fmaxf(s0, s1)));  // finite: a unit holds a valid key
                 const float p0 = __builtin_amdgcn_exp2f(s0 - mn);
                 const float p1 = __builtin_amdgcn_exp2f(s1 - mn);
                 const float al = __builtin_amdgcn_exp2f(m[rt][e] - mn);
@@ -319,9 +325,11 @@ __global__ __launch_bounds__(64 * NRT, 2) void attn_rows_kernel(const AttnParams
     const int qpg = p.hq / p.hkv;
     const int R = qpg * p.gamma;
     const int lenb = min(max(p.len[b], 0), p.cap);
-    // units: the context's 32-key chunks, then the block's gamma keys; the workgroup
-    // takes an equal run of consecutive units
-    const int nch = (lenb + kChunk - 1) / kChunk;
+    // units: the 32-key chunks from the one holding the first attended key, then the
+    // block's gamma keys; the workgroup takes an equal run of consecutive units
+    const int kbeg = p.window > 0 ? max(0, lenb - p.window) : 0;
+    const int cb = kbeg & ~(kChunk - 1);
+    const int nch = (lenb - cb + kChunk - 1) / kChunk;
     const int nunits = nch + 1;
     const int upw = (nunits + p.nsplit - 1) / p.nsplit;
     const int u_begin = min(nunits, s * upw);
@@ -342,9 +350,9 @@ __global__ __launch_bounds__(64 * NRT, 2) void attn_rows_kernel(const AttnParams
         const uint16_t *k0, *k1, *vp;
         int64_t vstride;
         if (u != nch) {
-            k0 = kc + (int64_t)(u * kChunk + col) * HD + 8 * grp;
+            k0 = kc + (int64_t)(cb + u * kChunk + col) * HD + 8 * grp;
             k1 = k0 + 16 * HD;
-            vp = vc + (int64_t)col * p.cap + u * kChunk + 8 * grp;
+            vp = vc + (int64_t)col * p.cap + cb + u * kChunk + 8 * grp;
             vstride = 16 * (int64_t)p.cap;
         } else {
             k0 = qrow0 + (int64_t)min(col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
@@ -380,7 +388,8 @@ __global__ __launch_bounds__(64 * NRT, 2) void attn_rows_kernel(const AttnParams
     for (int e = 0; e < 4; ++e) { m[e] = -INFINITY; l[e] = 0.f; }
 
     auto unit = [&](const int u, u32x4 (&kb)[2][KS], u32x4 (&vb)[DT]) {
-        const int nvalid = (u == nch) ? p.gamma : min(kChunk, lenb - u * kChunk);
+        const int nvalid = (u == nch) ? p.gamma : min(kChunk, lenb - cb - u * kChunk);
+        const int lo = (u == 0 && u != nch) ? kbeg - cb : 0;  // keys before the window's first
         f32x4 sacc[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -388,13 +397,13 @@ __global__ __launch_bounds__(64 * NRT, 2) void attn_rows_kernel(const AttnParams
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) sacc[nt] = mfma16(qa[ks], kb[nt][ks], sacc[nt]);
         }
-        const bool v0ok = col < nvalid, v1ok = 16 + col < nvalid;
+        const bool v0ok = col >= lo && col < nvalid, v1ok = 16 + col >= lo && 16 + col < nvalid;
         const bool rescale = (u != u_begin);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float s0 = v0ok ? sacc[0][e] * sl2 : -INFINITY;
             const float s1 = v1ok ? sacc[1][e] * sl2 : -INFINITY;
-            const float mn = fmaxf(m[e], row16_max(fmaxf(s0, s1)));  // finite: key 0 is valid
+            const float mn = fmaxf(m[e], row16_max(fmaxf(s0, s1)));  // finite: a unit holds a valid key
             const float p0 = __builtin_amdgcn_exp2f(s0 - mn);
             const float p1 = __builtin_amdgcn_exp2f(s1 - mn);
             const float al = __builtin_amdgcn_exp2f(m[e] - mn);
@@ -474,7 +483,10 @@ __global__ __launch_bounds__(kBlock) void attn_valu_kernel(const AttnParams p) {
     const int qpg = p.hq / p.hkv;
     const int R = qpg * p.gamma;
     const int lenb = min(max(p.len[b], 0), p.cap);
-    const int T = lenb + p.gamma;
+    // keys: the attended context rows kbeg .. lenb-1 (all, or the window's), then the block's
+    const int kbeg = p.window > 0 ? max(0, lenb - p.window) : 0;
+    const int nctx = lenb - kbeg;
+    const int T = nctx + p.gamma;
     int C = (T + p.nsplit - 1) / p.nsplit;
     C = ((C + kTile - 1) / kTile) * kTile;
     const int start = s * C;
@@ -507,11 +519,11 @@ __global__ __launch_bounds__(kBlock) void attn_valu_kernel(const AttnParams p) {
             const int key = e / HD, dd = e - key * HD;
             const int kk = t0 + key;
             float kv = 0.f, vv = 0.f;
-            if (kk < lenb) {
-                kv = kc[(int64_t)kk * HD + dd];
-                vv = vc[(int64_t)dd * p.cap + kk];
+            if (kk < nctx) {
+                kv = kc[(int64_t)(kbeg + kk) * HD + dd];
+                vv = vc[(int64_t)dd * p.cap + kbeg + kk];
             } else if (kk < T) {
-                const float* rowp = qrow0 + (int64_t)(kk - lenb) * qkv_ld;
+                const float* rowp = qrow0 + (int64_t)(kk - nctx) * qkv_ld;
                 kv = rowp[kcol + dd];
                 vv = rowp[vcol + dd];
             }
@@ -742,7 +754,7 @@ static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
         }
     } else {
         const int nrt = R <= 16 ? 1 : (R <= 32 ? 2 : 3);
-        const bool rows_kernel = R > 32 && use_rows_kernel(R, 0, p.B * p.hkv, p.cap);
+        const bool rows_kernel = R > 32 && use_rows_kernel(R, 0, p.B * p.hkv, attn_span(p.cap, p.window));
         if (R > kMaxRows) return hipErrorInvalidValue;
         snprintf(name, sizeof name, rows_kernel ? "attn_rows_kernel<%d, %d>" : "attn_mfma_kernel<%d, %d>", HD, nrt);
         q.stamps = trace_launch(TRACE_ATTENTION, name, grid.x, bytes, ctx_row_bytes);
@@ -765,8 +777,10 @@ static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+int attn_span(int cap, int window) { return window > 0 && window + kChunk < cap ? window + kChunk : cap; }
+
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
-    if (p.nparts > kMaxParts || p.gamma > kChunk) return hipErrorInvalidValue;
+    if (p.nparts > kMaxParts || p.gamma > kChunk || p.window < 0) return hipErrorInvalidValue;
     if (!p.kv_f32 && p.nsplit > kMaxSplit) return hipErrorInvalidValue;
     if (!p.kv_f32 && (p.cap % kChunk)) return hipErrorInvalidValue;
     if (p.hd == 128) return launch_hd<128>(p, s);

@@ -20,6 +20,7 @@ struct AttnParams {
     const void* vcache;    // this layer's values [B][hkv][hd][cap] (head-dim major)
     const int32_t* len;    // [B] context rows per sequence
     int B, hq, hkv, hd, gamma, cap, nsplit, kv_f32;
+    int window;            // attend to the last `window` context keys of each sequence; 0 = all
     int nparts;            // partial results per (b, head): nsplit workgroups x parts each
     float scale;
     float* part;           // [B][hq][nparts][gamma][hd+2]  (o, running max, running sum)
@@ -34,6 +35,9 @@ struct AttnParams {
 // rows per kv head (one partial per workgroup); the workspace holds
 // B*hq*nparts*gamma*(hd+2) floats.
 void attention_splits(int cap, int gamma, int kv_f32, int pairs, int rows, int* nsplit, int* nparts);
+// context keys a sequence can attend in a cache of `cap` rows under a window (0: cap): the
+// window plus the part of its first 32-key chunk before it; pass it as attention_splits' cap
+int attn_span(int cap, int window);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 int attention_max_rows(int kv_f32);
 

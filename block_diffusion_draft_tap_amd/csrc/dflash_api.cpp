@@ -14,6 +14,7 @@
 #include "gemm.hpp"
 #include "gemv.hpp"
 #include "head.hpp"
+#include "rope.hpp"
 #include "skinny.hpp"
 #include "trace.hpp"
 
@@ -77,6 +78,7 @@ int check_dims(const dflash_dims* d) {
         return DFLASH_EINVAL;
     if (d->d != d->hq * d->hd || d->hq % d->hkv != 0) return DFLASH_EINVAL;
     if (!(d->eps >= 0.0f) || d->eps > 1.0f) return DFLASH_EINVAL;
+    if (d->window < 0 || !(d->rope_theta >= 0.0f) || d->rope_theta > 1e30f) return DFLASH_EINVAL;
     if (d->hd != 64 && d->hd != 128) return DFLASH_DECLINED;
     if (d->wdtype != DFLASH_F32 && d->wdtype != DFLASH_BF16 && d->wdtype != DFLASH_INT4G64) return DFLASH_DECLINED;
     if (d->act != DFLASH_ACT_GELU_TANH && d->act != DFLASH_ACT_SILU) return DFLASH_DECLINED;
@@ -90,6 +92,19 @@ int check_dims(const dflash_dims* d) {
 }
 
 int wtype_of(int dtype) { return dtype == DFLASH_F32 ? W_F32 : (dtype == DFLASH_BF16 ? W_BF16 : W_I4); }
+
+// the rotary frequencies of (hd, theta), formed once per thread for the last pair asked for
+const RopeFreq& rope_freqs(int hd, float theta) {
+    thread_local RopeFreq f{};
+    thread_local int f_hd = -1;
+    thread_local float f_theta = -1.0f;
+    if (hd != f_hd || theta != f_theta) {
+        f = rope_freq(hd, theta);
+        f_hd = hd;
+        f_theta = theta;
+    }
+    return f;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -362,7 +377,8 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     Ws w{};
     const size_t rows = (size_t)B * d.gamma;
     const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
-    attention_splits(cap, d.gamma, d.wdtype == DFLASH_F32, B * d.hkv, (d.hq / d.hkv) * d.gamma, &w.nsplit, &w.nparts);
+    attention_splits(attn_span(cap, d.window), d.gamma, d.wdtype == DFLASH_F32, B * d.hkv, (d.hq / d.hkv) * d.gamma,
+                     &w.nsplit, &w.nparts);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -703,8 +719,23 @@ struct CtxRows {
 // the fused pass applies: GEMV path with the in-register RMSNorm prologue, and the block rows
 // plus the context rows within one 16-row launch
 bool fused_qkv_ok(const dflash_dims& d, const Ws& w, int rows, int n) {
+    // rotary keys turn after their rows are written, at the pre-round lengths: kept to the
+    // separate append
     return !w.skinny && !prenorm(d) && d.wdtype != DFLASH_INT4G64 && d.d <= kRegNormMaxK && n > 0 &&
-           rows + n <= 16;
+           rows + n <= 16 && d.rope_theta == 0.0f;
+}
+
+// the end of a K/V append: with rotary positions the new keys turn at the positions they
+// were written to (the lengths before the append), then the lengths advance
+int append_done(const dflash_model* M, const dflash_kv* kv, const int32_t* row_offsets, const int32_t* counts, int n,
+                hipStream_t s) {
+    const dflash_dims& d = M->dims;
+    if (d.rope_theta > 0.0f && d.nl > 0)
+        DFL_HIP(launch_rope_cache(kv->k, kv->dtype == DFLASH_F32, d.nl, (int64_t)kv->B * d.hkv * kv->cap * d.hd, kv->B,
+                                  d.hkv, kv->cap, d.hd, row_offsets, counts, kv->len, n, rope_freqs(d.hd, d.rope_theta),
+                                  s));
+    DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
+    return DFLASH_OK;
 }
 
 int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B, const Ws& w, hipStream_t s,
@@ -778,6 +809,9 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
             DFL_HIP(gemv_rows(wt, pro, EPI_STORE, p, rows, s));
         }
     }
+    if (d.rope_theta > 0.0f)  // block row k of sequence b at position len[b] + k
+        DFL_HIP(launch_rope_block(w.qkv, d.wdtype == DFLASH_F32, qkv_rows, kv->len, B, d.gamma, d.hq, d.hkv, d.hd,
+                                  rope_freqs(d.hd, d.rope_theta), s));
     {  // O = softmax(Q [K_ctx; K_b]^T / sqrt(hd)) [V_ctx; V_b]
         AttnParams a;
         std::memset(&a, 0, sizeof(a));
@@ -794,6 +828,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         a.hd = d.hd;
         a.gamma = d.gamma;
         a.cap = kv->cap;
+        a.window = d.window;
         a.nsplit = w.nsplit;
         a.nparts = w.nparts;
         a.kv_f32 = kv->dtype == DFLASH_F32;
@@ -1337,7 +1372,7 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
         p.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
         skinny_split(SK_KV, p.N, p.K, p.layers, &p.nsplit, &p.kslice);
         DFL_HIP(launch_skinny(SK_KV, p, s));
-        DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
+        DFL_TRY(append_done(M, kv, row_offsets, counts, n, s));
         g_invocations++;
         return DFLASH_OK;
     }
@@ -1384,7 +1419,7 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
         g.cap = kv->cap;
         g.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
         DFL_HIP(launch_gemm(GEMM_A_TAPS, GEMM_EPI_KV, g, d.nl, s));
-        DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
+        DFL_TRY(append_done(M, kv, row_offsets, counts, n, s));
         g_invocations++;
         return DFLASH_OK;
     }
@@ -1419,7 +1454,7 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
         g.cap = kv->cap;
         g.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
         DFL_HIP(launch_gemm(GEMM_A_NORM, GEMM_EPI_KV, g, d.nl, s));
-        DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
+        DFL_TRY(append_done(M, kv, row_offsets, counts, n, s));
         g_invocations++;
         return DFLASH_OK;
     }
@@ -1506,7 +1541,7 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
     } else {
         DFL_HIP(gemv_rows(wtype_of(d.wdtype), pro, EPI_KV, p, n, s, d.nl, 32));
     }
-    DFL_HIP(launch_advance_len(kv->len, row_offsets, counts, kv->B, kv->cap, s));
+    DFL_TRY(append_done(M, kv, row_offsets, counts, n, s));
     g_invocations++;
     return DFLASH_OK;
 }
@@ -1716,6 +1751,36 @@ int dflash_verify_greedy_lengths(const float* target_logits, const int32_t* draf
     int32_t* pi = reinterpret_cast<int32_t*>(c + need / 2);
     DFL_HIP(launch_verify(target_logits, draft_ids, B, gamma, V, accepted, committed, ids, next_anchor, pv, pi,
                           static_cast<hipStream_t>(stream), lengths));
+    g_invocations++;
+    return DFLASH_OK;
+}
+
+size_t dflash_verify_hidden_workspace_bytes(const dflash_dims* dims, int32_t B) {
+    if (check_dims(dims) == DFLASH_EINVAL || B <= 0) return 0;
+    const size_t rows = (size_t)B * (dims->gamma + 1);
+    return align_up(rows * 4) + 2 * align_up(rows * lm_tiles_max(dims->V) * 4);
+}
+
+int dflash_verify_from_hidden(const dflash_model* M, const void* target_hidden, int32_t B, const int32_t* draft_ids,
+                              const int32_t* lengths, int32_t* accepted, int32_t* committed, int32_t* ids,
+                              int32_t* next_anchor, void* ws, size_t ws_bytes, void* stream) {
+    DFL_TRY(check_model(M));
+    const dflash_dims& d = M->dims;
+    if (!target_hidden || !draft_ids || !accepted || !committed || !ids || B <= 0) return DFLASH_EINVAL;
+    if (!aligned16(target_hidden)) return DFLASH_DECLINED;
+    const size_t need = dflash_verify_hidden_workspace_bytes(&d, B);
+    if (!ws || !aligned16(ws) || ws_bytes < need) return DFLASH_ENOSPC;
+    DFL_TRY(gate());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int rows = B * (d.gamma + 1);
+    const size_t part = align_up((size_t)rows * lm_tiles_max(d.V) * 4);
+    char* c = static_cast<char*>(ws);
+    int32_t* tids = reinterpret_cast<int32_t*>(c);
+    float* pv = reinterpret_cast<float*>(c + align_up((size_t)rows * 4));
+    int32_t* pi = reinterpret_cast<int32_t*>(c + align_up((size_t)rows * 4) + part);
+    // the target's greedy token of every verify row: its hidden row scored by the borrowed head
+    DFL_TRY(lm_head(M->lm_head, target_hidden, d.wdtype == DFLASH_F32, rows, d.H, d.V, tids, nullptr, pv, pi, s));
+    DFL_HIP(launch_verify_ids(tids, draft_ids, B, d.gamma, accepted, committed, ids, next_anchor, lengths, s));
     g_invocations++;
     return DFLASH_OK;
 }

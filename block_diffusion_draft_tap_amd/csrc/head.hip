@@ -1,7 +1,8 @@
 // Small kernels of the drafter round:
 //   argmax_merge_kernel   per-workgroup (max, index) partials -> greedy ids
 //   verify_partial_kernel per (verify row, vocab slice) argmax of target logits
-//   verify_final_kernel   prefix compare: accepted, committed, ids, next anchor
+//   verify_final_kernel   prefix compare: accepted, committed, ids, next anchor (from the
+//                         split partials of given logits, or from the target's greedy ids)
 //   dspark_step_kernel    one step of the DSpark greedy loop (previous token, Markov operand,
 //                         confidence, pruning length)
 //   rownorm_kernel        RMSNorm of fp32 rows (sum of split partials) with a gain (Eq 2)
@@ -77,14 +78,18 @@ __global__ __launch_bounds__(kBlock) void verify_partial_kernel(const float* log
 
 // one 64-lane wavefront per sequence; lane j handles verify row j (gamma + 1 <= 64). With
 // lengths (a pruned block proposes its first lengths[b] drafts) the prefix stops there too.
+// tids: the target's greedy tokens [B][gamma+1] when they are already known (the verify
+// from the target's hidden states), else merged here from the split partials
 __global__ __launch_bounds__(64) void verify_final_kernel(const float* part_val, const int32_t* part_idx, int nsplit,
                                                           const int32_t* draft, int gamma, const int32_t* lengths,
                                                           int32_t* accepted, int32_t* committed, int32_t* ids,
-                                                          int32_t* next_anchor) {
+                                                          int32_t* next_anchor, const int32_t* tids) {
     const int b = blockIdx.x, j = threadIdx.x;
     const int W = gamma + 1;
     int t = -1;
-    if (j < W) {
+    if (j < W && tids) {
+        t = tids[(int64_t)b * W + j];
+    } else if (j < W) {
         float v = -INFINITY;
         int i = 0x7fffffff;
         const int64_t base = ((int64_t)b * W + j) * nsplit;
@@ -334,7 +339,17 @@ hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int g
     if (e != hipSuccess) return e;
     (void)hipGetLastError();  // report only this launch's status
     hipLaunchKernelGGL(verify_final_kernel, dim3(B), dim3(64), 0, s, pv, pi, ns, draft, gamma, lengths, accepted,
-                       committed, ids, next_anchor);
+                       committed, ids, next_anchor, (const int32_t*)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_verify_ids(const int32_t* tids, const int32_t* draft, int B, int gamma, int32_t* accepted,
+                             int32_t* committed, int32_t* ids, int32_t* next_anchor, const int32_t* lengths,
+                             hipStream_t s) {
+    if (gamma + 1 > 64) return hipErrorInvalidValue;
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL(verify_final_kernel, dim3(B), dim3(64), 0, s, (const float*)nullptr, (const int32_t*)nullptr, 0,
+                       draft, gamma, lengths, accepted, committed, ids, next_anchor, tids);
     return hipGetLastError();
 }
 

@@ -13,6 +13,10 @@ int verify_splits(int V);
 hipError_t launch_verify(const float* logits, const int32_t* draft, int B, int gamma, int V, int32_t* accepted,
                          int32_t* committed, int32_t* ids, int32_t* next_anchor, float* pv, int32_t* pi,
                          hipStream_t s, const int32_t* lengths = nullptr);
+// the same prefix rule from the target's greedy ids tids [B][gamma+1]
+hipError_t launch_verify_ids(const int32_t* tids, const int32_t* draft, int B, int gamma, int32_t* accepted,
+                             int32_t* committed, int32_t* ids, int32_t* next_anchor, const int32_t* lengths,
+                             hipStream_t s);
 
 // One step of the DSpark greedy loop per sequence (see head.hip)
 struct DsparkStepParams {

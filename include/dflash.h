@@ -77,7 +77,18 @@ enum { DFLASH_ACT_GELU_TANH = 0, DFLASH_ACT_SILU = 1 };
  * gamma = block query rows = drafted tokens (the verify width is gamma+1); at
  * most 32 (the block's keys form one 32-key attention unit), and
  * (hq/hkv)*gamma query rows per kv head at most 48 (40 for f32 models): larger
- * blocks are DECLINED. */
+ * blocks are DECLINED.
+ *
+ * The DFlash2 variant (page "Inco Hacks Native: DFlash 2 Speculation",
+ * section 1: a sliding-window drafter) adds two fields; zero in both gives the
+ * plain drafter. The pages fix neither, so both are parameters:
+ *   window      attend to the last `window` context keys of each sequence
+ *               (the block's own keys always); 0 = the whole context.
+ *   rope_theta  rotary positions on Q and K: dims i and i + hd/2 of a head
+ *               turn by the angle position * rope_theta^(-2i/hd); context row
+ *               t sits at position t, block row k at position len + k (len =
+ *               the sequence's context length when the block is drafted).
+ *               Context keys are turned when appended; 0 = no rotation. */
 typedef struct {
     int32_t H;       /* target hidden size (tap width and LM-head width)   */
     int32_t m;       /* number of tapped target layers                      */
@@ -92,6 +103,8 @@ typedef struct {
     float   eps;     /* RMSNorm epsilon                                      */
     int32_t act;     /* DFLASH_ACT_*: activation of the gate branch          */
     int32_t wdtype;  /* DFLASH_F32 / DFLASH_BF16 / DFLASH_INT4G64            */
+    int32_t window;  /* context keys attended, counted from the end; 0 = all */
+    float   rope_theta; /* rotary base; 0 = no rotary positions              */
 } dflash_dims;
 
 typedef struct {
@@ -386,6 +399,24 @@ size_t dflash_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V);
 int dflash_verify_greedy_lengths(const float* target_logits, const int32_t* draft_ids, const int32_t* lengths,
                                  int32_t B, int32_t gamma, int32_t V, int32_t* accepted, int32_t* committed,
                                  int32_t* ids, int32_t* next_anchor, void* ws, size_t ws_bytes, void* stream);
+
+/* Greedy verification from the target's hidden states (the DFlash2 variant:
+ * page "Inco Hacks Native: DFlash 2 Speculation", section 3, the target
+ * verifies the block). The target hands over its final hidden rows (after its
+ * own final norm) at the gamma+1 verify positions; the borrowed LM head scores
+ * them and the greedy rule of dflash_verify_greedy decides:
+ *   t[b, j] = argmax_v target_hidden[b, j] . E_out[v]   (lowest index on ties)
+ * then accepted, committed, ids and next_anchor exactly as there (lengths:
+ * optional, as in dflash_verify_greedy_lengths; NULL = gamma for every row).
+ *   target_hidden: device [B, gamma+1, H], bf16 (bf16 and int4 models) or
+ *                  fp32 (fp32 models), 16-byte aligned; E_out is the model's
+ *                  lm_head. No logits are materialised.
+ * Workspace: at least dflash_verify_hidden_workspace_bytes(dims, B). */
+int dflash_verify_from_hidden(const dflash_model* model, const void* target_hidden, int32_t B,
+                              const int32_t* draft_ids, const int32_t* lengths, int32_t* accepted,
+                              int32_t* committed, int32_t* ids, int32_t* next_anchor, void* ws, size_t ws_bytes,
+                              void* stream);
+size_t dflash_verify_hidden_workspace_bytes(const dflash_dims* dims, int32_t B);
 
 /* For callers that cannot allocate (code under HIP graph capture, serving
  * loops or harnesses that forbid hipMalloc): dflash_verify_greedy without a

@@ -121,9 +121,10 @@ def oracle_prefill(dims, w, lengths, faithful_mode, stream="ctx"):
     for b, L in enumerate(lengths):
         taps = gen.make_taps(dims, 0, int(L), stream=stream, seq=b)
         Hc = O.context_project(taps, w["W_c"], w["ctx_norm"], dims.eps)
+        rot = {"positions": np.arange(int(L)), "theta": dims.rope_theta} if dims.rope_theta else {}
         for i in range(dims.nl):
             K, V = O.context_kv(Hc, w[f"bb.{i}.attn_norm"], w[f"bb.{i}.k"], w[f"bb.{i}.v"], dims.hkv, dims.hd,
-                                dims.eps, faithful_mode)
+                                dims.eps, faithful_mode, **rot)
             ctx.append(i, b, K, V)
         Hs.append(Hc)
         taps_all.append(taps)

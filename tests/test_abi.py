@@ -11,7 +11,7 @@ import re
 import pytest
 
 from block_diffusion_draft_tap_amd import binding as bd
-from synth import TINY, DEFAULT, WIDE, WIDE4, BATCHED, scaled
+from synth import TINY, DEFAULT, WIDE, WIDE4, BATCHED, DFLASH2, scaled
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -36,7 +36,7 @@ def test_status_strings():
     assert "declined" in bd.status_string(1)
 
 
-@pytest.mark.parametrize("cfg", [TINY, DEFAULT, WIDE, WIDE4, BATCHED], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [TINY, DEFAULT, WIDE, WIDE4, BATCHED, DFLASH2], ids=lambda c: c.name)
 def test_query_valid_dims_without_device_declines(cfg):
     # consistent dims: OK on an MI355X, DECLINED where there is no gfx950 device
     rc = bd.dflash_query(cfg)
@@ -203,6 +203,42 @@ def test_dspark_and_length_verify_validation():
     assert lib.dflash_verify_greedy_lengths(P, P, None, 1, 7, 100, P, P, P, None, P, 1 << 20, None) == bd.DFLASH_EINVAL
     assert lib.dflash_verify_greedy_lengths(P, P, P, 1, 70, 100, P, P, P, None, P, 1 << 20, None) == bd.DFLASH_DECLINED
     assert lib.dflash_verify_greedy_lengths(P, P, P, 1, 7, 100, P, P, P, None, P, 4, None) == bd.DFLASH_ENOSPC
+
+
+def test_dflash2_dims_and_hidden_verify_validation():
+    # the variant's fields: a window and a rotary base, zero for the plain drafter
+    for w, theta in ((2048, 1e6), (1, 1e4), (0, 0.0)):
+        d = bd.make_dims(scaled(DFLASH2, window=w, rope_theta=theta))
+        assert bd.lib.dflash_query(ctypes.byref(d)) in (bd.DFLASH_OK, bd.DFLASH_DECLINED)
+    d = bd.make_dims(DFLASH2)
+    d.window = -1
+    assert bd.lib.dflash_query(ctypes.byref(d)) == bd.DFLASH_EINVAL
+    d = bd.make_dims(DFLASH2)
+    d.rope_theta = -1.0
+    assert bd.lib.dflash_query(ctypes.byref(d)) == bd.DFLASH_EINVAL
+    d.rope_theta = float("nan")
+    assert bd.lib.dflash_query(ctypes.byref(d)) == bd.DFLASH_EINVAL
+    # a window shrinks the attention's partial results, never below the plain drafter's need
+    # for short caches
+    plain = bd.make_dims(scaled(DFLASH2, window=0, rope_theta=0.0))
+    assert 0 < bd.lib.dflash_workspace_bytes(ctypes.byref(bd.make_dims(DFLASH2)), 1, 8256) \
+        <= bd.lib.dflash_workspace_bytes(ctypes.byref(plain), 1, 8256)
+    # verify from hidden states: the workspace holds the target ids and the head's partials
+    dims = ctypes.byref(bd.make_dims(DFLASH2))
+    n = bd.lib.dflash_verify_hidden_workspace_bytes(dims, 3)
+    assert n >= 3 * (DFLASH2.gamma + 1) * 4 * 3
+    assert bd.lib.dflash_verify_hidden_workspace_bytes(dims, 0) == 0
+    assert bd.lib.dflash_verify_hidden_workspace_bytes(None, 3) == 0
+    fm = _FakeModel(DFLASH2)
+    P = 1 << 20
+    lib = bd.lib
+    v = lambda hid, B, ws, wsb: lib.dflash_verify_from_hidden(ctypes.byref(fm.c), hid, B, P, None, P, P, P, None, ws,
+                                                               wsb, None)
+    assert v(None, 1, P, n) == bd.DFLASH_EINVAL
+    assert v(P, 0, P, n) == bd.DFLASH_EINVAL
+    assert v(P + 2, 1, P, n) == bd.DFLASH_DECLINED          # hidden rows read as 16-byte vectors
+    assert v(P, 3, P, n - 1) == bd.DFLASH_ENOSPC
+    assert v(P, 3, None, n) == bd.DFLASH_ENOSPC
 
 
 def test_append_and_project_validation():

@@ -77,6 +77,18 @@ GAMMA1 = scaled(GQA_BF16, name="gamma1", gamma=1, B=2)
 EMPTY_CTX = scaled(GQA_BF16, name="empty_ctx", B=3)
 NL0 = scaled(GQA_BF16, name="nl0", nl=0, B=2)
 
+# the DFlash2 variant (rotary positions, a context window): the fp32 drafter with a window
+# shorter than its context (VALU attention); three bf16 GQA sequences of which two are longer
+# than a 100-key window whose first key is not chunk-aligned; a one-key window; the row-split
+# kernel over a 1000-key window of 2100 keys; the int4 wide heads with block 8; and 16
+# sequences on the matrix-core projections with a 64-key window
+D2_TINY = scaled(TINY, name="d2_tiny", window=20, rope_theta=1e4)
+D2_GQA = scaled(GQA_BF16, name="d2_gqa", window=100, rope_theta=1e6)
+D2_W1 = scaled(GQA_BF16, name="d2_w1", window=1, rope_theta=1e6, B=2)
+D2_ROWS = scaled(ROWS_SPLIT64, name="d2_rows", window=1000, rope_theta=1e6)
+D2_WIDE4 = scaled(WIDE4_SMALL, name="d2_wide4", gamma=7, window=256, rope_theta=1e6, verify="hidden")
+D2_BATCHED = scaled(BATCHED_SMALL, name="d2_batched", window=64, rope_theta=1e6)
+
 CASES = {
     "tiny": (TINY, [TINY.L]),
     "gqa_bf16": (GQA_BF16, [200, 77, 131]),
@@ -95,6 +107,12 @@ CASES = {
     "gamma1": (GAMMA1, [200, 77]),
     "empty_ctx": (EMPTY_CTX, [0, 45, 0]),
     "nl0": (NL0, [64, 31]),
+    "d2_tiny": (D2_TINY, [D2_TINY.L]),
+    "d2_gqa": (D2_GQA, [200, 77, 131]),
+    "d2_w1": (D2_W1, [200, 45]),
+    "d2_rows": (D2_ROWS, [2100]),
+    "d2_wide4": (D2_WIDE4, [300, 211]),
+    "d2_batched": (D2_BATCHED, [int(x) for x in gen.context_lengths(D2_BATCHED)]),
 }
 
 _cache = {}
@@ -428,7 +446,8 @@ def test_verify_exhaustive_patterns(V):
 
 
 @pytest.mark.parametrize("name", ["tiny", "gqa_bf16", "gqa_rows42", "default", "wide4_small", "wide4_b1",
-                                  "batched_small", "batched_r140", "gamma1", "empty_ctx"])
+                                  "batched_small", "batched_r140", "gamma1", "empty_ctx", "d2_tiny", "d2_gqa",
+                                  "d2_wide4", "d2_batched"])
 def test_multi_round_loop(name):
     """Rounds of append(committed rows) -> forward -> verify, both sides driven
     by the oracle's schedule (planted logits realise accept lengths; the
@@ -545,7 +564,7 @@ ROUND_FUSED = {"tiny", "default", "gamma1"}
 
 
 @pytest.mark.parametrize("name", ["tiny", "default", "gamma1", "gqa_bf16", "wide4_b1", "batched_small", "nl0",
-                                  "empty_ctx"])
+                                  "empty_ctx", "d2_tiny", "d2_gqa"])
 def test_round_matches_separate_calls(name):
     """One round in one call (the new rows projected, their K/V appended, the
     block drafted) against the three separate calls and the oracle. Where the
