@@ -76,8 +76,10 @@ def dspark_bytes(d, B, r):
 def algorithmic_bytes(d, B, ctx_rows, n_new):
     """Minimum bytes of one round: every weight once (the K/V rows shared by
     the append and the block counted once), the borrowed LM head once, one
-    embedding row per sequence, every layer's context K/V once, the new tap
-    rows and the target logits."""
+    embedding row per sequence, every layer's attended context K/V once
+    (ctx_rows: the rows the attention reads), the new tap rows and the target
+    logits; a verify from the target's hidden states reads those rows instead
+    of logits and streams the head a second time."""
     wb = weight_bytes_per_elem(d.wdtype)
     layer = ((d.hq + 2 * d.hkv) * d.hd * d.d + d.d * d.hq * d.hd + 2 * d.F * d.d + d.d * d.F) * wb
     drafter = d.nl * layer + (d.d * d.m * d.H + d.d * d.H + d.H * d.d) * wb
@@ -85,9 +87,44 @@ def algorithmic_bytes(d, B, ctx_rows, n_new):
     kv_elem = 4 if d.wdtype == "f32" else 2
     kv = d.nl * 2 * d.hkv * d.hd * kv_elem * (ctx_rows + n_new * B)
     act = 4 if d.wdtype == "f32" else 2
-    other = B * (d.gamma + 1) * (d.m * d.H * act + d.V * 4) + B * d.H * wb
+    if d.verify == "hidden":
+        head *= 2
+        other = B * (d.gamma + 1) * (d.m * d.H * act + d.H * act) + B * d.H * wb
+    else:
+        other = B * (d.gamma + 1) * (d.m * d.H * act + d.V * 4) + B * d.H * wb
     return {"weights": drafter, "lm_head": head, "kv": kv, "other": other,
             "total": drafter + head + kv + other}
+
+
+def attended_rows(d, lengths):
+    """Context rows the attention reads: each sequence's, or its window's."""
+    return sum(min(int(L), d.window) if d.window else int(L) for L in lengths)
+
+
+def head_rows(E, tokens):
+    """Rows of the stored head (the generator's formats) as float64, to plant
+    target hidden states along them."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    if isinstance(E, dict):                    # int4-g64: w = scale * q + bias per group of 64
+        codes = E["codes"][tokens]
+        q = (codes[..., None] >> (np.uint32(4) * np.arange(8, dtype=np.uint32))) & np.uint32(15)
+        q = q.reshape(len(tokens), -1).astype(np.float64)
+        sc = np.repeat(gen.bf16_bits_to_f32(E["scales"][tokens]).astype(np.float64), 64, axis=1)
+        bi = np.repeat(gen.bf16_bits_to_f32(E["biases"][tokens]).astype(np.float64), 64, axis=1)
+        return sc * q + bi
+    if E.dtype == np.uint16:
+        return gen.bf16_bits_to_f32(E[tokens]).astype(np.float64)
+    return E[tokens].astype(np.float64)
+
+
+def plant_hidden(d, w, drafts, accept, r):
+    """Target hidden rows [B, gamma+1, H] whose greedy tokens under the head
+    realise the accept plan: each along its planted token's head row (that
+    token's logit exceeds every other by far for random head rows)."""
+    t = gen.plant_target_tokens(d, drafts, accept, r)
+    rows = head_rows(w["E_out"], t.reshape(-1))
+    h = 4.0 * rows / np.linalg.norm(rows, axis=1, keepdims=True)
+    return h.reshape(t.shape + (d.H,)).astype(np.float32)
 
 
 def describe(d, lengths):
@@ -163,8 +200,13 @@ class CpuLeg:
                 ex = {"logits": extra["scores"].reshape(d.gamma, -1)}
             full = np.zeros((d.B, d.gamma), np.int32)
             full[b] = ids[0]
-            T = gen.plant_target_logits(d, full, rr["accept"], r)
-            _, _, _, nxt = O.verify_greedy(T[b:b + 1], ids, lengths=lengths)
+            if d.verify == "hidden":
+                hid = plant_hidden(d, w, full, rr["accept"], r)[b:b + 1].astype(np.float64)
+                hid = hid if d.wdtype == "f32" else O.bf16(hid)
+                _, _, _, nxt = O.verify_from_hidden(hid, w["E_out"], ids, lengths=lengths)
+            else:
+                T = gen.plant_target_logits(d, full, rr["accept"], r)
+                _, _, _, nxt = O.verify_greedy(T[b:b + 1], ids, lengths=lengths)
             self.anchor = nxt
             self.ctx.truncate(0, self.L)
             if self.done < len(self.rounds):
@@ -405,6 +447,7 @@ def main():
     len0 = kv.len.clone()
 
     vws = bd.verify_workspace(B, d.gamma, d.V, dev)
+    hws = dfa.verify_hidden_workspace(d, B, dev) if d.verify == "hidden" else None
     rws = dfa.round_workspace(d, B, kv.cap, dev) if args.one_call else None
     if args.dspark:
         dws = dfa.dspark_workspace(d, d.r, B, kv.cap, dev)
@@ -424,7 +467,8 @@ def main():
             "accept": accept[r],
             "anchors": torch.zeros(B, dtype=torch.int32, device=dev),
             "ids": torch.zeros(B, d.gamma, dtype=torch.int32, device=dev),
-            "T": torch.zeros(B, W, d.V, dtype=torch.float32, device=dev),
+            "T": torch.zeros(B, W, d.V, dtype=torch.float32, device=dev) if d.verify == "logits" else None,
+            "hid": torch.zeros(B, W, d.H, dtype=dm.act_dtype, device=dev) if d.verify == "hidden" else None,
             "acc": torch.zeros(B, dtype=torch.int32, device=dev),
             "com": torch.zeros(B, dtype=torch.int32, device=dev),
             "vids": torch.zeros(B, W, dtype=torch.int32, device=dev),
@@ -437,7 +481,11 @@ def main():
         rounds.append(rr)
 
     def verify_round(rr):
-        if args.dspark:
+        if d.verify == "hidden":
+            bd.check(dfa.dflash_verify_from_hidden(dm, rr["hid"], rr["ids"], rr["acc"], rr["com"], rr["vids"], hws,
+                                                   lengths=rr["lengths"] if args.dspark else None,
+                                                   next_anchor=rr["nxt"]), "verify from hidden")
+        elif args.dspark:
             bd.check(dfa.dflash_verify_greedy_lengths(rr["T"], rr["ids"], rr["lengths"], rr["acc"], rr["com"],
                                                       rr["vids"], vws, next_anchor=rr["nxt"]), "verify lengths")
         else:
@@ -477,7 +525,10 @@ def main():
         ids = rr["ids"].cpu().numpy().copy()
         chain_ids.append(ids)
         chain_y.append(y_chain.float().cpu().numpy())
-        rr["T"].copy_(torch.from_numpy(gen.plant_target_logits(d, ids, accept[r], r)))
+        if d.verify == "hidden":
+            rr["hid"].copy_(torch.from_numpy(plant_hidden(d, w, ids, accept[r], r)))
+        else:
+            rr["T"].copy_(torch.from_numpy(gen.plant_target_logits(d, ids, accept[r], r)))
         verify_round(rr)
         rr["lengths_h"] = rr["lengths"].cpu().numpy().copy()
         rr["accepted_h"] = np.minimum(accept[r], rr["lengths_h"])     # a pruned block proposes fewer
@@ -568,7 +619,10 @@ def main():
     ms_per_step = gpu_ms / args.steps
     blocks_per_s = B * args.steps / (gpu_ms / 1000.0)
     mean_new = float(np.mean([rr["counts_h"].sum() for rr in rounds]))
-    ab = algorithmic_bytes(d, B, sum(lengths), mean_new / B)
+    # context rows the attention reads after each round's append (all of them, or the windows')
+    read_rows = float(np.mean([attended_rows(d, [L + int(c) for L, c in zip(lengths, rr["counts_h"])])
+                               for rr in rounds]))
+    ab = algorithmic_bytes(d, B, read_rows, 0)
     if args.dspark:
         ab["dspark"] = dspark_bytes(d, B, d.r)
         ab["total"] += ab["dspark"]
@@ -608,7 +662,7 @@ def main():
         "round_hbm_frac": round(round_gbs / HBM_PEAK_GBS, 4),
     }
 
-    lengths_after = [sum(lengths) + int(rr["counts_h"].sum()) for rr in rounds]
+    lengths_after = [attended_rows(d, [L + int(c) for L, c in zip(lengths, rr["counts_h"])]) for rr in rounds]
     if trace:
         table = kernel_table(rounds, lengths_after)
         timing = (f"device wall-clock stamps written by the kernel's workgroups (first start to last end per "

@@ -420,7 +420,7 @@ def verify_from_hidden(target_hidden, E_out, draft_ids, lengths=None):
     final hidden rows at the verify positions; the borrowed LM head scores
     them (logits = hidden E_out^T) and the greedy rule above decides."""
     B, W, H = target_hidden.shape
-    logits = dense(target_hidden.reshape(B * W, H)) @ dense(E_out).T
+    _, _, logits = lm_head_argmax(target_hidden.reshape(B * W, H), E_out, want_logits=True)
     return verify_greedy(logits.reshape(B, W, -1), draft_ids, lengths)
 
 

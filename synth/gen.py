@@ -285,6 +285,28 @@ def accept_schedule(dims: Dims, round_idx: int, seed: int = SEED_LOGITS) -> np.n
     return np.minimum((u * (dims.gamma + 1)).astype(np.int64), dims.gamma).astype(np.int32)
 
 
+def plant_target_tokens(dims: Dims, draft_ids: np.ndarray, accept: np.ndarray, round_idx: int,
+                        seed: int = SEED_LOGITS) -> np.ndarray:
+    """The target's greedy tokens [B, gamma+1] that stop the agreement with
+    `draft_ids` after exactly accept[b] tokens (the tokens plant_target_logits
+    raises): the drafts up to accept[b], then a token other than the draft at
+    accept[b], then seeded tokens."""
+    B, G, V = dims.B, dims.gamma, dims.V
+    W = G + 1
+    picks = uniforms(stream_key(seed, "target_pick"), round_idx * B * W, B * W).reshape(B, W)
+    t = np.empty((B, W), dtype=np.int64)
+    for b in range(B):
+        a = int(accept[b])
+        for j in range(W):
+            if j < a:
+                t[b, j] = int(draft_ids[b, j])
+            else:
+                t[b, j] = min(int(picks[b, j] * V), V - 1)
+                if j == a and j < G and t[b, j] == int(draft_ids[b, j]):
+                    t[b, j] = (t[b, j] + 1) % V
+    return t
+
+
 def plant_target_logits(dims: Dims, draft_ids: np.ndarray, accept: np.ndarray, round_idx: int,
                         seed: int = SEED_LOGITS) -> np.ndarray:
     """Target logits [B, gamma+1, V] (float32) whose greedy agreement with
@@ -299,18 +321,10 @@ def plant_target_logits(dims: Dims, draft_ids: np.ndarray, accept: np.ndarray, r
     W = G + 1
     T = normals(seed, "target_logits", B * W * V, start=round_idx * B * W * V)
     T = T.astype(np.float32).reshape(B, W, V)
-    picks = uniforms(stream_key(seed, "target_pick"), round_idx * B * W, B * W).reshape(B, W)
+    t = plant_target_tokens(dims, draft_ids, accept, round_idx, seed)
     for b in range(B):
-        a = int(accept[b])
         for j in range(W):
-            top = np.float32(T[b, j].max()) + np.float32(1.0)
-            if j < a:
-                t = int(draft_ids[b, j])
-            else:
-                t = min(int(picks[b, j] * V), V - 1)
-                if j == a and j < G and t == int(draft_ids[b, j]):
-                    t = (t + 1) % V
-            T[b, j, t] = top
+            T[b, j, t[b, j]] = np.float32(T[b, j].max()) + np.float32(1.0)
     return T
 
 

@@ -5,6 +5,10 @@ each, against the CPU oracle.
             context 4096, gamma 7: every context row, the whole round.
   * wide4   the same drafter with int4-g64 weights on every matrix, context
             8192, gamma 4: every context row, the whole round.
+  * dflash2 the wide geometry in int4-g64 weights with block 8 (gamma 7), a
+            2048-key window over a context of 8192 and rotary positions (base
+            1e6); verification from the target's hidden states, planted along
+            the head rows of the target tokens that realise the accept plan.
   * batched 16 sequences with contexts of 9050-16059 rows (192,011 in all),
             gamma 7. The whole prefill runs as one call per step (the K/V
             prefill with its ~9.8 GB staged workspace, whose offsets exceed
@@ -29,7 +33,7 @@ import block_diffusion_draft_tap_amd as dfa
 from block_diffusion_draft_tap_amd import binding as bd
 from gpu_common import compare_ids, dev, log, rel_err, tol
 from oracle import dflash_oracle as O
-from synth import gen, WIDE, WIDE4, BATCHED, scaled
+from synth import gen, WIDE, WIDE4, BATCHED, DFLASH2, scaled
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -52,11 +56,18 @@ def bits(t):
     return t.cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def oracle_context(d, w, taps, fm):
+def rot(d, positions):
+    """context_kv's rotary arguments for rows at these positions (none without rotation)"""
+    return {"positions": np.asarray(positions), "theta": d.rope_theta} if d.rope_theta else {}
+
+
+def oracle_context(d, w, taps, fm, positions=None):
     Hc = O.context_project(taps, w["W_c"], w["ctx_norm"], d.eps)
     ks, vs = [], []
+    pos = np.arange(Hc.shape[0]) if positions is None else positions
     for i in range(d.nl):
-        K, V = O.context_kv(Hc, w[f"bb.{i}.attn_norm"], w[f"bb.{i}.k"], w[f"bb.{i}.v"], d.hkv, d.hd, d.eps, fm)
+        K, V = O.context_kv(Hc, w[f"bb.{i}.attn_norm"], w[f"bb.{i}.k"], w[f"bb.{i}.v"], d.hkv, d.hd, d.eps, fm,
+                            **rot(d, pos))
         ks.append(K)
         vs.append(V)
     return Hc, ks, vs
@@ -122,7 +133,7 @@ def full_round(d, full_seqs, device_taps, samples_per_seq=20):
         rows[0], rows[-1] = 0, lengths[b] - 1                   # first and last rows always
         rows = np.unique(rows)
         taps_rows = [bits(taps_d[j][s0 + rows]) for j in range(d.m)]
-        Hc, ks, vs = oracle_context(d, w, taps_rows, fm)
+        Hc, ks, vs = oracle_context(d, w, taps_rows, fm, positions=rows)
         e = rel_err(h_ctx[s0 + torch.as_tensor(rows, device="cuda")], Hc)
         assert e <= 1e-4, (b, e)
         worst = max(worst, e)
@@ -173,7 +184,7 @@ def full_round(d, full_seqs, device_taps, samples_per_seq=20):
         assert e <= 1e-4, (b, e)
         for i in range(d.nl):
             K, V = O.context_kv(Hr[:counts[b]], w[f"bb.{i}.attn_norm"], w[f"bb.{i}.k"], w[f"bb.{i}.v"], d.hkv,
-                                d.hd, d.eps, fm)
+                                d.hd, d.eps, fm, **rot(d, lengths[b] + np.arange(counts[b])))
             ctx.append(i, q, K, V)
             rows = np.arange(lengths[b], lengths[b] + counts[b])
             check_kv_rows(kv, i, b, rows, K, V, t, "appended")
@@ -193,14 +204,29 @@ def full_round(d, full_seqs, device_taps, samples_per_seq=20):
     drafts = np.random.default_rng(5).integers(0, d.V, size=(B, d.gamma)).astype(np.int32)
     drafts[sel] = ref_ids
     acc_plan = gen.accept_schedule(d, 0)
-    T = gen.plant_target_logits(d, drafts, acc_plan, 0)
-    acc_o, com_o, ids_o, nxt_o = O.verify_greedy(T, drafts)
-    assert np.array_equal(acc_o, acc_plan)
     acc = torch.empty(B, dtype=torch.int32, device="cuda")
     com, nxt = torch.empty_like(acc), torch.empty_like(acc)
     vid = torch.empty(B, W, dtype=torch.int32, device="cuda")
-    bd.check(dfa.dflash_verify_greedy(torch.from_numpy(T).cuda(), torch.from_numpy(drafts).cuda(), acc, com, vid,
-                                      bd.verify_workspace(B, d.gamma, d.V), next_anchor=nxt), "verify")
+    if d.verify == "hidden":
+        # the target's hidden rows along the head rows of tokens that realise the plan
+        rng = np.random.default_rng(6)
+        tt = np.concatenate([drafts, rng.integers(0, d.V, size=(B, 1))], axis=1).astype(np.int64)
+        for b in range(B):
+            if acc_plan[b] < d.gamma:
+                tt[b, acc_plan[b]] = (drafts[b, acc_plan[b]] + 1 + rng.integers(0, d.V - 1)) % d.V
+        E = O.dense(w["E_out"], rows=tt.reshape(-1))
+        hidden = O.bf16(4.0 * E / np.linalg.norm(E, axis=1, keepdims=True)).reshape(B, W, d.H)
+        acc_o, com_o, ids_o, nxt_o = O.verify_from_hidden(hidden, w["E_out"], drafts)
+        hid_d = torch.from_numpy(hidden.astype(np.float32)).cuda().to(torch.bfloat16)
+        bd.check(dfa.dflash_verify_from_hidden(dm, hid_d, torch.from_numpy(drafts).cuda(), acc, com, vid,
+                                               dfa.verify_hidden_workspace(d, B), next_anchor=nxt),
+                 "verify from hidden")
+    else:
+        T = gen.plant_target_logits(d, drafts, acc_plan, 0)
+        acc_o, com_o, ids_o, nxt_o = O.verify_greedy(T, drafts)
+        bd.check(dfa.dflash_verify_greedy(torch.from_numpy(T).cuda(), torch.from_numpy(drafts).cuda(), acc, com,
+                                          vid, bd.verify_workspace(B, d.gamma, d.V), next_anchor=nxt), "verify")
+    assert np.array_equal(acc_o, acc_plan)
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy(), acc_o) and np.array_equal(com.cpu().numpy(), com_o)
     assert np.array_equal(vid.cpu().numpy(), ids_o) and np.array_equal(nxt.cpu().numpy(), nxt_o)
@@ -221,3 +247,7 @@ def test_batched_full_size():
 
 def test_wide4_full_size():
     full_round(WIDE4, full_seqs=[0], device_taps=set())
+
+
+def test_dflash2_full_size():
+    full_round(DFLASH2, full_seqs=[0], device_taps=set())
