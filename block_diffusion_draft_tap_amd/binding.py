@@ -29,7 +29,7 @@ EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "df
            "dflash_trace_end", "dflash_lm_head_workgroups", "dflash_wall_clock_hz", "dflash_verify_greedy_noalloc",
            "dflash_verify_noalloc_max_bytes", "dflash_dspark_workspace_bytes", "dflash_draft_forward_dspark",
            "dflash_verify_greedy_lengths", "dflash_draft_round", "dflash_round_workspace_bytes",
-           "dflash_verify_from_hidden", "dflash_verify_hidden_workspace_bytes"]
+           "dflash_verify_from_hidden", "dflash_verify_hidden_workspace_bytes", "dflash_lm_head_workspace_bytes_for"]
 DFLASH_TRACE_LM_HEAD, DFLASH_TRACE_ATTENTION, DFLASH_TRACE_PROJECTIONS = 1, 2, 4
 
 
@@ -105,6 +105,8 @@ def _load():
     lib.dflash_lm_head_argmax.restype = ctypes.c_int
     lib.dflash_lm_head_workspace_bytes.argtypes = [I32, I32]
     lib.dflash_lm_head_workspace_bytes.restype = SZ
+    lib.dflash_lm_head_workspace_bytes_for.argtypes = [P(dflash_weight), I32, I32]
+    lib.dflash_lm_head_workspace_bytes_for.restype = SZ
     lib.dflash_verify_greedy.argtypes = [VP, VP, I32, I32, I32, VP, VP, VP, VP, VP, SZ, VP]
     lib.dflash_verify_greedy.restype = ctypes.c_int
     lib.dflash_verify_workspace_bytes.argtypes = [I32, I32, I32]
@@ -446,6 +448,14 @@ def kv_prefill_workspace(dims, n, device="cuda"):
 
 def lm_head_workspace(V, M, device="cuda"):
     return torch.empty(lib.dflash_lm_head_workspace_bytes(V, M), dtype=torch.uint8, device=device)
+
+
+def lm_head_workspace_for(weight, y_dtype, M, device="cuda"):
+    """The workspace for the head's fastest path (its matrix-core path, where it has one)."""
+    cw = weight.c() if isinstance(weight, Weight) else weight
+    ydt = DFLASH_F32 if y_dtype == torch.float32 else DFLASH_BF16
+    return torch.empty(lib.dflash_lm_head_workspace_bytes_for(ctypes.byref(cw), ydt, M), dtype=torch.uint8,
+                       device=device)
 
 
 def dflash_verify_greedy(target_logits, draft_ids, accepted, committed, ids, ws, next_anchor=None, stream=None):

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "dflash")
 LIB = os.path.join(PKG, "libdflash.so")
 
-SOURCES = ["gemv.hip", "gemm.hip", "skinny.hip", "attention.hip", "head.hip", "rope.hip", "noalloc.hip",
+SOURCES = ["gemv.hip", "gemm.hip", "skinny.hip", "attention.hip", "head.hip", "rope.hip", "i4mm.hip", "noalloc.hip",
            "dflash_api.cpp"]
 ARCH = os.environ.get("DFLASH_ARCH", "gfx950")
 

@@ -14,6 +14,7 @@
 #include "gemm.hpp"
 #include "gemv.hpp"
 #include "head.hpp"
+#include "i4mm.hpp"
 #include "rope.hpp"
 #include "skinny.hpp"
 #include "trace.hpp"
@@ -367,6 +368,8 @@ struct Ws {
     uint16_t* an;  // normalised block rows, bf16 [B*gamma][d] (matrix-core path, long rows)
     float* skp;    // matrix-core path: split-K partial sums
     float* rsp;    // GEMV path: split-K partial sums of the residual projections
+    float* i4h;    // int4 LM head on matrix cores: split-K partial logits [splits][B*gamma][V] (else null)
+    size_t i4h_bytes;
     bool skinny;   // the block projections run on matrix cores
     size_t total;
     int nsplit;  // attention workgroups per (sequence, kv head)
@@ -407,12 +410,25 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
         for (int q = 0; q < 5; ++q) {
             if (q >= 2 && !prenorm(d)) break;
             int ns = 1, ks = 0;
-            gemv_split(d, shapes[q][0], (int)rows, &ns, &ks);
+            // int4 weights of up to 16 rows: always partial sums (matrix-core K ranges)
+            const bool i4 = d.wdtype == DFLASH_INT4G64 && i4mm_ok(shapes[q][0], (int)rows);
+            if (i4)
+                i4mm_split(shapes[q][0], &ns, &ks);
+            else
+                gemv_split(d, shapes[q][0], (int)rows, &ns, &ks);
             const size_t b = (size_t)ns * rows * shapes[q][1] * 4;
-            if (ns > 1 && b > rsp_bytes) rsp_bytes = b;
+            if ((ns > 1 || i4) && b > rsp_bytes) rsp_bytes = b;
         }
     }
     const size_t o_rsp = take(rsp_bytes);
+    size_t i4h_bytes = 0;
+    if (d.wdtype == DFLASH_INT4G64 && i4mm_ok(d.H, (int)rows)) {
+        int ns = 1, ks = 0;
+        i4mm_split(d.H, &ns, &ks);
+        i4h_bytes = (size_t)ns * rows * d.V * 4;
+    }
+    const size_t o_i4h = take(i4h_bytes);
+    w.i4h_bytes = i4h_bytes;
     w.total = off;
     // the context append of up to B*cap rows keeps one float per row at the base; the
     // matrix-core context paths of a round's B*(gamma+1) rows use the base as well
@@ -439,6 +455,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
         w.an = reinterpret_cast<uint16_t*>(c + o_an);
         w.skp = reinterpret_cast<float*>(c + o_skp);
         w.rsp = reinterpret_cast<float*>(c + o_rsp);
+        w.i4h = i4h_bytes ? reinterpret_cast<float*>(c + o_i4h) : nullptr;
     }
     return w;
 }
@@ -503,9 +520,14 @@ hipError_t gemv_rows(int wtype, int pro, int epi, GemvParams p, int rows, hipStr
 hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int rows, float* part, hipStream_t s,
                       const void* norm_gain = nullptr, uint16_t* norm_dst = nullptr, bool* normed = nullptr) {
     int ns = 1, ks = p.K;
-    gemv_split(d, p.K, rows, &ns, &ks);
+    // int4 weights of up to 16 bf16 rows: matrix-core K ranges, then the same ordered reduce
+    const bool i4 = wt == W_I4 && !p.src_f32 && i4mm_ok(p.K, rows) && part;
+    if (i4)
+        i4mm_split(p.K, &ns, &ks);
+    else
+        gemv_split(d, p.K, rows, &ns, &ks);
     if (normed) *normed = false;
-    if (ns <= 1) return gemv_rows(wt, PRO_PLAIN, epi, p, rows, s);
+    if (ns <= 1 && !i4) return gemv_rows(wt, PRO_PLAIN, epi, p, rows, s);
     SkinnyParams r;
     std::memset(&r, 0, sizeof(r));
     r.M = rows;
@@ -522,17 +544,35 @@ hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int r
     r.gamma = p.gamma;
     r.hkv = p.hkv;
     r.hd = p.hd;
-    p.ksplit = ns;
-    p.kslice = ks;
-    p.max_wgs = DFL_SMALL_WGS / ns > 0 ? DFL_SMALL_WGS / ns : 1;
-    p.rpw = rpw_for(p.N, d.wdtype);
-    p.out = part;
-    p.out_ld = p.N;
-    p.split_stride = (int64_t)rows * p.N;
-    p.round_out = 0;
-    p.out_bf16 = 0;
-    p.vt = nullptr;
-    const hipError_t e = gemv_rows(wt, PRO_PLAIN, EPI_STORE, p, rows, s);
+    hipError_t e;
+    if (i4) {
+        I4Params q;
+        std::memset(&q, 0, sizeof(q));
+        q.codes = static_cast<const uint32_t*>(p.w[0].data);
+        q.scales = p.w[0].scales;
+        q.biases = p.w[0].biases;
+        q.N = p.N;
+        q.K = p.K;
+        q.a = reinterpret_cast<const uint16_t*>(p.x);
+        q.a_ld = p.x_ld;
+        q.M = rows;
+        q.nsplit = ns;
+        q.kslice = ks;
+        q.part = part;
+        e = launch_i4mm(q, s);
+    } else {
+        p.ksplit = ns;
+        p.kslice = ks;
+        p.max_wgs = DFL_SMALL_WGS / ns > 0 ? DFL_SMALL_WGS / ns : 1;
+        p.rpw = rpw_for(p.N, d.wdtype);
+        p.out = part;
+        p.out_ld = p.N;
+        p.split_stride = (int64_t)rows * p.N;
+        p.round_out = 0;
+        p.out_bf16 = 0;
+        p.vt = nullptr;
+        e = gemv_rows(wt, PRO_PLAIN, EPI_STORE, p, rows, s);
+    }
     if (e != hipSuccess) return e;
     if (epi == EPI_RESID && norm_gain && norm_dst && normed) {
         *normed = true;
@@ -898,7 +938,32 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
 }
 
 int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, int V, int32_t* ids, float* maxl,
-            float* pv, int32_t* pi, hipStream_t s) {
+            float* pv, int32_t* pi, hipStream_t s, float* i4part = nullptr, size_t i4part_bytes = 0) {
+    if (E.dtype == DFLASH_INT4G64 && !y_f32 && i4mm_ok(H, rows) && i4part) {
+        // int4 head on matrix cores: split-K partial logits, then the ordered split argmax
+        int ns = 1, ks = 0;
+        i4mm_split(H, &ns, &ks);
+        if ((size_t)ns * rows * V * 4 <= i4part_bytes) {
+            I4Params q;
+            std::memset(&q, 0, sizeof(q));
+            q.codes = static_cast<const uint32_t*>(E.data);
+            q.scales = static_cast<const uint16_t*>(E.scales);
+            q.biases = static_cast<const uint16_t*>(E.biases);
+            q.N = V;
+            q.K = H;
+            q.a = static_cast<const uint16_t*>(y);
+            q.a_ld = H;
+            q.M = rows;
+            q.nsplit = ns;
+            q.kslice = ks;
+            q.part = i4part;
+            DFL_HIP(launch_i4mm(q, s));
+            const int nb = i4_argmax_blocks(V);
+            DFL_HIP(launch_i4_split_argmax(i4part, ns, rows, V, pv, pi, nb, s));
+            DFL_HIP(launch_argmax_merge(pv, pi, nb, rows, ids, maxl, s));
+            return DFLASH_OK;
+        }
+    }
     if (lm_head_skinny(E.dtype, y_f32, rows, H)) {
         // matrix cores: one pass over the head for all rows, a (max, index) partial per row and tile
         SkinnyParams p = skinny_params(E, static_cast<const uint16_t*>(y), H, V, H, nullptr);
@@ -1579,7 +1644,7 @@ int dflash_draft_forward(const dflash_model* M, const int32_t* anchor_ids, const
     float* y = y_out ? static_cast<float*>(y_out) : w.y;
     DFL_TRY(forward_out(M, B, w, s, an_ready, nullptr, y));
     DFL_TRY(lm_head(M->lm_head, y, d.wdtype == DFLASH_F32, B * d.gamma, d.H, d.V, draft_ids, max_logit, w.lmv, w.lmi,
-                    s));
+                    s, w.i4h, w.i4h_bytes));
     g_invocations++;
     return DFLASH_OK;
 }
@@ -1626,7 +1691,7 @@ int dflash_draft_round(const dflash_model* M, const void* const* taps, int64_t t
     float* y = y_out ? static_cast<float*>(y_out) : w.y;
     DFL_TRY(forward_out(M, B, w, s, an_ready, nullptr, y));
     DFL_TRY(lm_head(M->lm_head, y, d.wdtype == DFLASH_F32, B * d.gamma, d.H, d.V, draft_ids, max_logit, w.lmv, w.lmi,
-                    s));
+                    s, w.i4h, w.i4h_bytes));
     g_invocations++;
     return DFLASH_OK;
 }
@@ -1724,10 +1789,23 @@ int dflash_lm_head_argmax(const dflash_weight* E_out, const void* y, int32_t y_d
     char* c = static_cast<char*>(ws);
     float* pv = reinterpret_cast<float*>(c);
     int32_t* pi = reinterpret_cast<int32_t*>(c + need / 2);
+    // an int4 head with room for its split partial logits past the GEMV need: matrix cores
+    float* i4part = (ws_bytes > need && aligned16(c + need)) ? reinterpret_cast<float*>(c + need) : nullptr;
     DFL_TRY(lm_head(*E_out, y, y_dtype == DFLASH_F32, M, E_out->cols, E_out->rows, ids, max_logit, pv, pi,
-                    static_cast<hipStream_t>(stream)));
+                    static_cast<hipStream_t>(stream), i4part, i4part ? ws_bytes - need : 0));
     g_invocations++;
     return DFLASH_OK;
+}
+
+size_t dflash_lm_head_workspace_bytes_for(const dflash_weight* E_out, int32_t y_dtype, int32_t M) {
+    if (!E_out || E_out->rows <= 0 || E_out->cols <= 0 || M <= 0) return 0;
+    size_t n = dflash_lm_head_workspace_bytes(E_out->rows, M);
+    if (E_out->dtype == DFLASH_INT4G64 && y_dtype == DFLASH_BF16 && i4mm_ok(E_out->cols, M)) {
+        int ns = 1, ks = 0;
+        i4mm_split(E_out->cols, &ns, &ks);
+        n += align_up((size_t)ns * M * E_out->rows * 4);
+    }
+    return n;
 }
 
 size_t dflash_kv_prefill_workspace_bytes(const dflash_dims* dims, int32_t n) {
@@ -1755,10 +1833,18 @@ int dflash_verify_greedy_lengths(const float* target_logits, const int32_t* draf
     return DFLASH_OK;
 }
 
+// the int4 head's partial logits for `rows` rows on matrix cores (0: the GEMV head)
+static size_t i4_head_bytes(const dflash_dims& d, int64_t rows) {
+    if (d.wdtype != DFLASH_INT4G64 || rows > kI4Rows || !i4mm_ok(d.H, (int)rows)) return 0;
+    int ns = 1, ks = 0;
+    i4mm_split(d.H, &ns, &ks);
+    return (size_t)ns * rows * d.V * 4;
+}
+
 size_t dflash_verify_hidden_workspace_bytes(const dflash_dims* dims, int32_t B) {
     if (check_dims(dims) == DFLASH_EINVAL || B <= 0) return 0;
     const size_t rows = (size_t)B * (dims->gamma + 1);
-    return align_up(rows * 4) + 2 * align_up(rows * lm_tiles_max(dims->V) * 4);
+    return align_up(rows * 4) + 2 * align_up(rows * lm_tiles_max(dims->V) * 4) + align_up(i4_head_bytes(*dims, rows));
 }
 
 int dflash_verify_from_hidden(const dflash_model* M, const void* target_hidden, int32_t B, const int32_t* draft_ids,
@@ -1778,8 +1864,10 @@ int dflash_verify_from_hidden(const dflash_model* M, const void* target_hidden, 
     int32_t* tids = reinterpret_cast<int32_t*>(c);
     float* pv = reinterpret_cast<float*>(c + align_up((size_t)rows * 4));
     int32_t* pi = reinterpret_cast<int32_t*>(c + align_up((size_t)rows * 4) + part);
+    float* i4part = reinterpret_cast<float*>(c + align_up((size_t)rows * 4) + 2 * part);
     // the target's greedy token of every verify row: its hidden row scored by the borrowed head
-    DFL_TRY(lm_head(M->lm_head, target_hidden, d.wdtype == DFLASH_F32, rows, d.H, d.V, tids, nullptr, pv, pi, s));
+    DFL_TRY(lm_head(M->lm_head, target_hidden, d.wdtype == DFLASH_F32, rows, d.H, d.V, tids, nullptr, pv, pi, s,
+                    i4part, i4_head_bytes(d, rows)));
     DFL_HIP(launch_verify_ids(tids, draft_ids, B, d.gamma, accepted, committed, ids, next_anchor, lengths, s));
     g_invocations++;
     return DFLASH_OK;

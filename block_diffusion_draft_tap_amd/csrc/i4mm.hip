@@ -1,0 +1,214 @@
+// int4-g64 weights on matrix cores for up to 16 activation rows: the per-round
+// projections and the LM head of the int4 drafters (the Wide4 and DFlash2
+// workloads: 4 and 7 block rows), where the dot-product GEMVs are bound by the
+// code unpack and their activation reads, not by HBM.
+//
+// Products run on v_mfma_f32_16x16x32_bf16 with the activation rows as the A
+// operand (rows past M are zero) and 16 weight rows as the B operand. A weight
+// group (64 columns, one bf16 scale s and bias b) is two MFMA k-steps:
+//   sum_k (s q_k + b) x_k = s sum_k (128 + q_k) x_k + (b - 128 s) sum_k x_k
+// The codes become bf16 (128 + q) with two integer operations per pair (the
+// exponent of 128 or'ed above the 4-bit code), so the B operand costs no float
+// arithmetic; each group's MFMA partial is then scaled and the bias term added
+// with its activation sum, itself an MFMA against a ones operand.
+//
+// Lane (c, g) of a wavefront (c = lane % 16, g = lane / 16) supplies, for k-step
+// j of a 128-column block, the 8 columns 64 (j / 2) + 16 g + 8 (j % 2) .. +8: the
+// codes of weight row c there are one 32-bit word, and the four steps keep every
+// step inside one quantisation group. The two code words a lane needs per block
+// (two 8-byte loads) and the block's scales and biases for its output column
+// are all loaded before the first product; a workgroup (four wavefronts, 64
+// weight rows) takes a K range of up to 8 blocks and stages that range of the
+// activation rows once in LDS.
+//
+// Results are fp32 partial sums per K range; an ordered reduce applies the
+// epilogue (the skinny reduce kernels, or the split argmax below).
+#include "common.hpp"
+#include "i4mm.hpp"
+#include "trace.hpp"
+
+namespace dfl {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mma(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+}
+
+// a word of 8 codes (low nibble first) as bf16 pairs (128 + q_i, 128 + q_(i+4)), i = 0..3
+__device__ __forceinline__ u32x4 codes_bf16(uint32_t c) {
+    u32x4 r;
+    r[0] = (c & 0x000F000Fu) | 0x43004300u;
+    r[1] = ((c >> 4) & 0x000F000Fu) | 0x43004300u;
+    r[2] = ((c >> 8) & 0x000F000Fu) | 0x43004300u;
+    r[3] = ((c >> 12) & 0x000F000Fu) | 0x43004300u;
+    return r;
+}
+
+// 8 consecutive bf16 activations (x0, x1), (x2, x3), (x4, x5), (x6, x7) in the pair
+// order of the codes: (x0, x4), (x1, x5), (x2, x6), (x3, x7)
+__device__ __forceinline__ u32x4 pair_order(const u32x4& x) {
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(x[2], x[0], 0x05040100u);
+    r[1] = __builtin_amdgcn_perm(x[2], x[0], 0x07060302u);
+    r[2] = __builtin_amdgcn_perm(x[3], x[1], 0x05040100u);
+    r[3] = __builtin_amdgcn_perm(x[3], x[1], 0x07060302u);
+    return r;
+}
+
+constexpr int kAld = kI4MaxBlocks * kI4Block + 8;  // LDS activation row (bf16), padded by 16 bytes
+
+__global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
+    __shared__ __align__(16) uint16_t as[kI4Rows * kAld];
+    const uint64_t t_start = trace_start(p.stamps);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int s = blockIdx.y;
+    const int kb = s * p.kslice;
+    const int nblk = min(p.kslice, p.K - kb) / kI4Block;  // 1 .. kI4MaxBlocks
+    const int kw = nblk * kI4Block;
+    const int tile = blockIdx.x * 4 + wave;                // 16 weight rows of this wavefront
+    const int n = min(tile * 16 + col, p.N - 1);           // this lane's weight row and output column
+
+    // the range's activation rows: issued first (loads return in order), rows past M zero
+    constexpr int kChunks = kI4Rows * kI4MaxBlocks * kI4Block / 8 / kBlock;  // 16-byte chunks per thread
+    const int cpr = kw / 8;                                                  // chunks per row
+    u32x4 av[kChunks];
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int idx = min(tid + i * kBlock, kI4Rows * cpr - 1);
+        const int m = idx / cpr, c = idx - m * cpr;
+        av[i] = *reinterpret_cast<const u32x4*>(p.a + (int64_t)min(m, p.M - 1) * p.a_ld + kb + 8 * c);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the weight loads
+
+    // every block's codes, scales and biases (clamped past the range: loaded, never used)
+    const int K8 = p.K / 8, K64 = p.K / 64;
+    const uint32_t* crow = p.codes + (int64_t)n * K8 + kb / 8 + 2 * grp;
+    const uint32_t* srow = reinterpret_cast<const uint32_t*>(p.scales + (int64_t)n * K64 + kb / 64);
+    const uint32_t* brow = reinterpret_cast<const uint32_t*>(p.biases + (int64_t)n * K64 + kb / 64);
+    uint2 c0[kI4MaxBlocks], c1[kI4MaxBlocks];
+    uint32_t sc[kI4MaxBlocks], bi[kI4MaxBlocks];
+#pragma unroll
+    for (int b = 0; b < kI4MaxBlocks; ++b) {
+        const int bb = min(b, nblk - 1);
+        c0[b] = *reinterpret_cast<const uint2*>(crow + 16 * bb);
+        c1[b] = *reinterpret_cast<const uint2*>(crow + 16 * bb + 8);
+        sc[b] = srow[bb];
+        bi[b] = brow[bb];
+    }
+
+    // unconditional stores (threads past the range repeat the last chunk with its value), so
+    // no load is moved into a branch and waited for there
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const int idx = min(tid + i * kBlock, kI4Rows * cpr - 1);
+        const int m = idx / cpr, c = idx - m * cpr;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&as[m * kAld + 8 * c]) = m < p.M ? av[i] : z;
+    }
+    __syncthreads();
+
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = zero;
+#pragma unroll
+    for (int b = 0; b < kI4MaxBlocks; ++b) {
+        if (b < nblk) {
+            // A fragments of the block's four k-steps: activation row col, columns
+            // 128 b + 64 (j / 2) + 16 grp + 8 (j % 2) .. + 8
+            u32x4 af[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                af[j] = pair_order(*reinterpret_cast<const u32x4*>(
+                    &as[col * kAld + kI4Block * b + 64 * (j >> 1) + 16 * grp + 8 * (j & 1)]));
+            // per group: sum_k (128 + q) x over the group's two steps, and sum_k x
+            const f32x4 p0 = mma(af[1], codes_bf16(c0[b].y), mma(af[0], codes_bf16(c0[b].x), zero));
+            const f32x4 p1 = mma(af[3], codes_bf16(c1[b].y), mma(af[2], codes_bf16(c1[b].x), zero));
+            const f32x4 x0 = mma(af[1], ones, mma(af[0], ones, zero));
+            const f32x4 x1 = mma(af[3], ones, mma(af[2], ones, zero));
+            const float s0 = bf16_lo(sc[b]), s1 = bf16_hi(sc[b]);
+            const float b0 = bf16_lo(bi[b]) - 128.0f * s0, b1 = bf16_hi(bi[b]) - 128.0f * s1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += (s0 * p0[e] + b0 * x0[e]) + (s1 * p1[e] + b1 * x1[e]);
+        }
+    }
+
+    // lane holds output column tile * 16 + col of activation rows 4 grp + e
+    const int nout = tile * 16 + col;
+    if (nout < p.N) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 4 * grp + e;
+            if (m < p.M) p.part[((int64_t)s * p.M + m) * p.N + nout] = acc[e];
+        }
+    }
+    trace_end(p.stamps, t_start);
+}
+
+__global__ __launch_bounds__(kBlock) void i4_split_argmax_kernel(const float* part, int nsplit, int M, int N,
+                                                                 float* pv, int32_t* pi, int nblocks) {
+    __shared__ float sv[kBlock / 64];
+    __shared__ int si[kBlock / 64];
+    const int c = blockIdx.x, m = blockIdx.y;
+    const int n0 = c * kI4ArgChunk, n1 = min(N, n0 + kI4ArgChunk);
+    float v = -INFINITY;
+    int idx = 0x7fffffff;
+    for (int n = n0 + threadIdx.x; n < n1; n += kBlock) {
+        float t = 0.f;
+        for (int s = 0; s < nsplit; ++s) t += part[((int64_t)s * M + m) * N + n];
+        argmax_pick(v, idx, t, n);
+    }
+    wave_argmax(v, idx);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { sv[wave] = v; si[wave] = idx; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kBlock / 64; ++w) argmax_pick(v, idx, sv[w], si[w]);
+        pv[(int64_t)m * nblocks + c] = v;
+        pi[(int64_t)m * nblocks + c] = idx;
+    }
+}
+
+}  // namespace
+
+bool i4mm_ok(int K, int M) { return K > 0 && K % kI4Block == 0 && M >= 1 && M <= kI4Rows; }
+
+void i4mm_split(int K, int* nsplit, int* kslice) {
+    const int maxk = kI4MaxBlocks * kI4Block;
+    int ns = (K + maxk - 1) / maxk;
+    int ks = ((K + ns - 1) / ns + kI4Block - 1) / kI4Block * kI4Block;
+    ns = (K + ks - 1) / ks;
+    *nsplit = ns;
+    *kslice = ks;
+}
+
+hipError_t launch_i4mm(I4Params p, hipStream_t s) {
+    if (!i4mm_ok(p.K, p.M) || p.N <= 0 || !p.codes || !p.scales || !p.biases || !p.a || !p.part) return hipErrorInvalidValue;
+    if (p.kslice <= 0 || p.kslice % kI4Block || p.kslice > kI4MaxBlocks * kI4Block || p.a_ld % 8 || p.a_ld < p.K)
+        return hipErrorInvalidValue;
+    if (p.nsplit != (p.K + p.kslice - 1) / p.kslice) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((p.N + 63) / 64), (unsigned)p.nsplit);
+    // instrumentation: algorithmic bytes = int4 weights (codes, scales, biases) + activations + partials
+    const double bytes = (double)p.N * p.K * (0.5 + 4.0 / 64) + (double)p.M * p.K * 2.0 + (double)p.nsplit * p.M * p.N * 4.0;
+    p.stamps = trace_launch(TRACE_PROJECTIONS, "i4mm_kernel", (int64_t)grid.x * grid.y, bytes, 0.0);
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL(i4mm_kernel, grid, dim3(kBlock), 0, s, p);
+    return hipGetLastError();
+}
+
+int i4_argmax_blocks(int N) { return (N + kI4ArgChunk - 1) / kI4ArgChunk; }
+
+hipError_t launch_i4_split_argmax(const float* part, int nsplit, int M, int N, float* pv, int32_t* pi, int nblocks,
+                                  hipStream_t s) {
+    if (M <= 0 || N <= 0 || nsplit < 1 || nblocks != i4_argmax_blocks(N)) return hipErrorInvalidValue;
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL(i4_split_argmax_kernel, dim3((unsigned)nblocks, (unsigned)M), dim3(kBlock), 0, s, part, nsplit, M,
+                       N, pv, pi, nblocks);
+    return hipGetLastError();
+}
+
+}  // namespace dfl

@@ -370,10 +370,16 @@ size_t dflash_round_workspace_bytes(const dflash_dims* dims, int32_t B, int32_t 
  *   y:     [M, H], element type y_dtype (DFLASH_F32 or DFLASH_BF16); rounded
  *          to bf16 before the product unless E_out is f32.
  *   ids:   device int32 [M];  max_logit: optional float [M].
- * Workspace: at least dflash_lm_head_workspace_bytes(E_out->rows, M). */
+ * Workspace: at least dflash_lm_head_workspace_bytes(E_out->rows, M); with
+ * dflash_lm_head_workspace_bytes_for(E_out, y_dtype, M) bytes (more where the
+ * head has a matrix-core path: int4-g64 heads over at most 16 bf16 rows, whose
+ * split partial logits then live in the workspace) the fastest path runs. The
+ * ids are the same either way (the argmax of the same products); the head
+ * sums them in another order, so max_logit may differ in the last bits. */
 int dflash_lm_head_argmax(const dflash_weight* E_out, const void* y, int32_t y_dtype, int32_t M, int32_t* ids,
                           float* max_logit, void* ws, size_t ws_bytes, void* stream);
 size_t dflash_lm_head_workspace_bytes(int32_t V, int32_t M);
+size_t dflash_lm_head_workspace_bytes_for(const dflash_weight* E_out, int32_t y_dtype, int32_t M);
 
 /* Greedy block verification (page "Inco Hacks Native: DFlash 2
  * Speculation", sections 1 and 3: block = 1 verify + gamma proposals;

@@ -61,16 +61,16 @@ def test_dspark_forward(name, r, std):
     a_d = torch.from_numpy(anchors).cuda()
     ws = dfa.dspark_workspace(d, r, s.B, s.kv.cap)
     # thresholds: per step, between the oracle's confidences of that step (so some rows are
-    # cut), at least 2e-3 away from every one of them
+    # cut), at least 2.5e-2 away from every one of them (several times the confidence bound below)
     tok_o, conf_o, _, ex = O.dspark_forward(w, d, s.ctx, anchors, s.fm)
     thr = np.zeros(d.gamma, np.float32)
     for k in range(1, d.gamma):
         c = np.sort(conf_o[:, k])
-        mids = [(c[i] + c[i + 1]) / 2 for i in range(len(c) - 1) if c[i + 1] - c[i] > 4e-3]
+        mids = [(c[i] + c[i + 1]) / 2 for i in range(len(c) - 1) if c[i + 1] - c[i] > 5e-2]
         if mids:
             thr[k] = mids[len(mids) // 2]
         else:                                   # one sequence: cut it half way
-            thr[k] = c[0] + 0.01 if k == d.gamma // 2 else c[0] - 0.01
+            thr[k] = c[0] + 0.05 if k == d.gamma // 2 else c[0] - 0.05
     _, _, len_o, _ = O.dspark_greedy(ex["base"], anchors, hw["markov.w1"], hw["markov.w2"], hw["conf.w"],
                                      hw["conf.b"], ex["block"], thresholds=thr)
     ids = torch.empty(s.B, d.gamma, dtype=torch.int32, device="cuda")
@@ -109,11 +109,17 @@ def test_dspark_forward(name, r, std):
                 assert int(np.argmax(own)) == int(g_ids[b, k]) or own.max() - own[g_ids[b, k]] <= NEAR_TIE, (b, k)
                 explained.append((b, k))
             break                      # the chains condition on different tokens from here on
-    # confidence of the compared steps (same conditioning token), lengths by Alg 1
+    # confidence of the compared steps (same conditioning token), lengths by Alg 1. The GPU's
+    # block rows carry the rounding-order differences Y shows (relative error ey); under a
+    # random-sign model they move z = [block; e1] . conf.w by about ey * |block * conf.w|_2,
+    # and sigma by at most a quarter of that: the bound is 3 such sigmas (fp32: 1e-5)
+    cw = O.dense(hw["conf.w"]).reshape(-1)[:d.d]
     for b in range(s.B):
         same = np.cumprod(np.concatenate([[True], g_ids[b, :-1] == tok_o[b, :-1]])).astype(bool)
-        err = np.max(np.abs(g_conf[b, same] - conf_o[b, same]))
-        assert err <= (1e-5 if d.wdtype == "f32" else 2e-3), (b, err)
+        err = np.abs(g_conf[b, same] - conf_o[b, same])
+        spread = np.linalg.norm(ex["block"][b][same] * cw[None, :], axis=1)
+        bound = 1e-5 if d.wdtype == "f32" else 0.75 * max(ey, 1e-3) * spread
+        assert np.all(err <= bound), (b, err, bound)
     g_len = lengths.cpu().numpy()
     assert np.array_equal(g_len, alg1_lengths(g_conf, thr, 0.0))
     if not explained:

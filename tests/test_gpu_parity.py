@@ -414,6 +414,39 @@ def test_lm_head_argmax_matrix_cores(M, H, V):
     assert rel_err(maxl, best) <= 1e-5
 
 
+@pytest.mark.parametrize("M,H,V", [(1, 256, 1000), (4, 256, 1000), (7, 5120, 3001), (13, 384, 1000),
+                                   (16, 5120, 3001)])
+def test_lm_head_argmax_int4_matrix_cores(M, H, V):
+    """int4-g64 head and bf16 rows, at most 16 of them, with the workspace for
+    the matrix-core path (split partial logits, then the ordered split argmax):
+    ids bit-exact against the oracle at the stated band on identical inputs,
+    planted one-hot rows included; the GEMV path gives the same ids."""
+    dims = scaled(TINY, wdtype="int4g64", H=H, V=V)
+    E = gen.make_weight(dims, "E_out")
+    rng = np.random.default_rng(M * 7 + H)
+    Y = O.bf16(rng.standard_normal((M, H))).astype(np.float32)
+    Y[0] = 0.0
+    Y[0, 17] = 1.0                                  # row 0 selects column 17 of the head
+    W = dfa.Weight(E, torch.device("cuda"))
+    y_d = torch.from_numpy(Y).cuda().to(torch.bfloat16)
+    ws = bd.lm_head_workspace_for(W, torch.bfloat16, M)
+    assert ws.numel() > bd.lm_head_workspace(V, M).numel()      # room for the partial logits
+    ids = torch.empty(M, dtype=torch.int32, device="cuda")
+    maxl = torch.empty(M, dtype=torch.float32, device="cuda")
+    bd.check(dfa.dflash_lm_head_argmax(W, y_d, ids, ws, max_logit=maxl), "lm_head int4 mfma")
+    ref_ids, best, logits = O.lm_head_argmax(Y.astype(np.float64), E, want_logits=True)
+    c = compare_ids(ids, ref_ids, logits, what=f"head int4 mfma M={M}")   # identical inputs: no miss allowed
+    assert rel_err(maxl, best) <= 1e-5
+    assert int(ids[0]) == int(np.argmax(O.dense(E)[:, 17]))
+    ids_g = torch.empty_like(ids)
+    bd.check(dfa.dflash_lm_head_argmax(W, y_d, ids_g, bd.lm_head_workspace(V, M)), "lm_head int4 gemv")
+    torch.cuda.synchronize()
+    s_ = np.sort(logits, axis=1)
+    decided = (s_[:, -1] - s_[:, -2]) >= 1e-3
+    assert np.array_equal(ids.cpu().numpy()[decided], ids_g.cpu().numpy()[decided])
+    log(f"[lm_head int4 mfma M={M} H={H} V={V}] ids decided {c['decided']}/{M}")
+
+
 @pytest.mark.parametrize("V", [5000, 5001, 32768])
 def test_verify_exhaustive_patterns(V):
     """All 2^7 agreement patterns of a block-8 verify in one batch; bit-exact
