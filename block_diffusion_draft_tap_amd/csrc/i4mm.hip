@@ -10,7 +10,7 @@
 // The codes become bf16 (128 + q) with two integer operations per pair (the
 // exponent of 128 or'ed above the 4-bit code), so the B operand costs no float
 // arithmetic; each group's MFMA partial is then scaled and the bias term added
-// with its activation sum, itself an MFMA against a ones operand.
+// with its activation sum (summed once per workgroup while the rows are staged).
 //
 // Lane (c, g) of a wavefront (c = lane % 16, g = lane / 16) supplies, for k-step
 // j of a 128-column block, the 8 columns 64 (j / 2) + 16 g + 8 (j % 2) .. +8: the
@@ -19,10 +19,13 @@
 // (two 8-byte loads) and the block's scales and biases for its output column
 // are all loaded before the first product; a workgroup (four wavefronts, 64
 // weight rows) takes a K range of up to 8 blocks and stages that range of the
-// activation rows once in LDS.
+// activation rows once in LDS, already in the codes' pair order, with each
+// row's per-group sum.
 //
 // Results are fp32 partial sums per K range; an ordered reduce applies the
 // epilogue (the skinny reduce kernels, or the split argmax below).
+#include <cstdio>
+
 #include "common.hpp"
 #include "i4mm.hpp"
 #include "trace.hpp"
@@ -60,26 +63,34 @@ __device__ __forceinline__ u32x4 pair_order(const u32x4& x) {
 }
 
 constexpr int kAld = kI4MaxBlocks * kI4Block + 8;  // LDS activation row (bf16), padded by 16 bytes
+constexpr int kMaxGroups = kI4MaxBlocks * kI4Block / 64;
 
+// MT: activation rows staged (4, 8 or 16; rows past M are zero, MFMA rows past MT too).
+// FULL: every K range is 8 blocks and K/64 a multiple of 16, so a lane's 16 scales (and
+// biases) of its range are two 16-byte loads.
+template <int MT, bool FULL>
 __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
-    __shared__ __align__(16) uint16_t as[kI4Rows * kAld];
+    __shared__ __align__(16) uint16_t as[MT * kAld];            // rows in the codes' pair order
+    __shared__ __align__(16) float xs[kMaxGroups][kI4Rows];     // sum of each row's group (rows past MT: 0)
     const uint64_t t_start = trace_start(p.stamps);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int s = blockIdx.y;
+    // the K ranges of one group of 64 weight rows are consecutive workgroups, so they run
+    // together and share the rows' scale and bias lines in L2
+    const int s = blockIdx.x % p.nsplit;
     const int kb = s * p.kslice;
     const int nblk = min(p.kslice, p.K - kb) / kI4Block;  // 1 .. kI4MaxBlocks
     const int kw = nblk * kI4Block;
-    const int tile = blockIdx.x * 4 + wave;                // 16 weight rows of this wavefront
+    const int tile = (blockIdx.x / p.nsplit) * 4 + wave;   // 16 weight rows of this wavefront
     const int n = min(tile * 16 + col, p.N - 1);           // this lane's weight row and output column
 
-    // the range's activation rows: issued first (loads return in order), rows past M zero
-    constexpr int kChunks = kI4Rows * kI4MaxBlocks * kI4Block / 8 / kBlock;  // 16-byte chunks per thread
-    const int cpr = kw / 8;                                                  // chunks per row
+    // the range's activation rows: issued first (loads return in order)
+    constexpr int kChunks = MT * kI4MaxBlocks * kI4Block / 8 / kBlock;  // 16-byte chunks per thread
+    const int cpr = kw / 8;                                             // chunks per row
     u32x4 av[kChunks];
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-        const int idx = min(tid + i * kBlock, kI4Rows * cpr - 1);
+        const int idx = min(tid + i * kBlock, MT * cpr - 1);
         const int m = idx / cpr, c = idx - m * cpr;
         av[i] = *reinterpret_cast<const u32x4*>(p.a + (int64_t)min(m, p.M - 1) * p.a_ld + kb + 8 * c);
     }
@@ -97,39 +108,75 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
         const int bb = min(b, nblk - 1);
         c0[b] = *reinterpret_cast<const uint2*>(crow + 16 * bb);
         c1[b] = *reinterpret_cast<const uint2*>(crow + 16 * bb + 8);
-        sc[b] = srow[bb];
-        bi[b] = brow[bb];
+    }
+    if constexpr (FULL) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4 sv = *reinterpret_cast<const u32x4*>(srow + 4 * h);
+            const u32x4 bv = *reinterpret_cast<const u32x4*>(brow + 4 * h);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sc[4 * h + q] = sv[q];
+                bi[4 * h + q] = bv[q];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < kI4MaxBlocks; ++b) {
+            const int bb = min(b, nblk - 1);
+            sc[b] = srow[bb];
+            bi[b] = brow[bb];
+        }
     }
 
-    // unconditional stores (threads past the range repeat the last chunk with its value), so
-    // no load is moved into a branch and waited for there
+    // stage the rows in pair order (unconditional stores: threads past the range repeat the
+    // last chunk with its value, so no load is moved into a branch and waited for there)
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-        const int idx = min(tid + i * kBlock, kI4Rows * cpr - 1);
+        const int idx = min(tid + i * kBlock, MT * cpr - 1);
         const int m = idx / cpr, c = idx - m * cpr;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(&as[m * kAld + 8 * c]) = m < p.M ? av[i] : z;
+        *reinterpret_cast<u32x4*>(&as[m * kAld + 8 * c]) = m < p.M ? pair_order(av[i]) : z;
+    }
+    __syncthreads();
+    // each row's group sums (any order of the group's 64 values: a sum)
+    {
+        const int ng = kw / 64;
+        const int m = tid / kMaxGroups, g = tid - m * kMaxGroups;
+        float t = 0.f;
+        if (m < MT && g < ng) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(&as[m * kAld + 64 * g + 8 * q]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t += bf16_lo(v[e]) + bf16_hi(v[e]);
+            }
+        }
+        if (m < kI4Rows) xs[g][m] = t;  // 256 threads: every (group, row) slot written
     }
     __syncthreads();
 
-    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const int arow = min(col, MT - 1);  // A fragment row (zero past MT)
     f32x4 acc = zero;
 #pragma unroll
     for (int b = 0; b < kI4MaxBlocks; ++b) {
         if (b < nblk) {
             // A fragments of the block's four k-steps: activation row col, columns
-            // 128 b + 64 (j / 2) + 16 grp + 8 (j % 2) .. + 8
+            // 128 b + 64 (j / 2) + 16 grp + 8 (j % 2) .. + 8 (already in pair order)
             u32x4 af[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                af[j] = pair_order(*reinterpret_cast<const u32x4*>(
-                    &as[col * kAld + kI4Block * b + 64 * (j >> 1) + 16 * grp + 8 * (j & 1)]));
-            // per group: sum_k (128 + q) x over the group's two steps, and sum_k x
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(
+                    &as[arow * kAld + kI4Block * b + 64 * (j >> 1) + 16 * grp + 8 * (j & 1)]);
+                af[j] = col < MT ? v : zero4;
+            }
+            // per group: sum_k (128 + q) x over the group's two steps
             const f32x4 p0 = mma(af[1], codes_bf16(c0[b].y), mma(af[0], codes_bf16(c0[b].x), zero));
             const f32x4 p1 = mma(af[3], codes_bf16(c1[b].y), mma(af[2], codes_bf16(c1[b].x), zero));
-            const f32x4 x0 = mma(af[1], ones, mma(af[0], ones, zero));
-            const f32x4 x1 = mma(af[3], ones, mma(af[2], ones, zero));
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(&xs[2 * b][4 * grp]);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(&xs[2 * b + 1][4 * grp]);
             const float s0 = bf16_lo(sc[b]), s1 = bf16_hi(sc[b]);
             const float b0 = bf16_lo(bi[b]) - 128.0f * s0, b1 = bf16_hi(bi[b]) - 128.0f * s1;
 #pragma unroll
@@ -191,12 +238,28 @@ hipError_t launch_i4mm(I4Params p, hipStream_t s) {
     if (p.kslice <= 0 || p.kslice % kI4Block || p.kslice > kI4MaxBlocks * kI4Block || p.a_ld % 8 || p.a_ld < p.K)
         return hipErrorInvalidValue;
     if (p.nsplit != (p.K + p.kslice - 1) / p.kslice) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((p.N + 63) / 64), (unsigned)p.nsplit);
+    const dim3 grid((unsigned)(((p.N + 63) / 64) * p.nsplit));
     // instrumentation: algorithmic bytes = int4 weights (codes, scales, biases) + activations + partials
     const double bytes = (double)p.N * p.K * (0.5 + 4.0 / 64) + (double)p.M * p.K * 2.0 + (double)p.nsplit * p.M * p.N * 4.0;
-    p.stamps = trace_launch(TRACE_PROJECTIONS, "i4mm_kernel", (int64_t)grid.x * grid.y, bytes, 0.0);
+    const int mt = p.M <= 4 ? 4 : (p.M <= 8 ? 8 : 16);
+    char name[32];
+    snprintf(name, sizeof name, "i4mm_kernel<%d>", mt);
+    p.stamps = trace_launch(TRACE_PROJECTIONS, name, (int64_t)grid.x, bytes, 0.0);
     (void)hipGetLastError();  // report only this launch's status
-    hipLaunchKernelGGL(i4mm_kernel, grid, dim3(kBlock), 0, s, p);
+    const bool full = p.kslice == kI4MaxBlocks * kI4Block && p.K % p.kslice == 0;
+#define DFL_I4_LAUNCH(MT)                                                                \
+    if (full)                                                                            \
+        hipLaunchKernelGGL((i4mm_kernel<MT, true>), grid, dim3(kBlock), 0, s, p);        \
+    else                                                                                 \
+        hipLaunchKernelGGL((i4mm_kernel<MT, false>), grid, dim3(kBlock), 0, s, p);
+    if (mt == 4) {
+        DFL_I4_LAUNCH(4)
+    } else if (mt == 8) {
+        DFL_I4_LAUNCH(8)
+    } else {
+        DFL_I4_LAUNCH(16)
+    }
+#undef DFL_I4_LAUNCH
     return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ namespace dfl {
 constexpr int kI4Rows = 16;       // activation rows per launch (one MFMA row fragment)
 constexpr int kI4Block = 128;     // K per block: two quantisation groups
 constexpr int kI4MaxBlocks = 8;   // blocks per workgroup K range (1024 columns)
-constexpr int kI4ArgChunk = 4096; // outputs per workgroup of the split argmax
+constexpr int kI4ArgChunk = 1024; // outputs per workgroup of the split argmax
 
 struct I4Params {
     const uint32_t* codes;   // [N, K/8], 8 codes per word, low nibble first
