@@ -346,6 +346,24 @@ size_t kv_append_split_bytes(const dflash_dims& d, int n) {
     const int ns = kv_append_gemv_split(d, n, &ks);
     return kv_append_norm_bytes(d, n) + (ns > 1 ? align_up((size_t)d.nl * ns * n * 2 * d.hkv * d.hd * 4) : 0);
 }
+// int4 context projection of n <= 16 rows on matrix cores: split partials [ns][n][d] (0: not
+// served there; the K ranges must not straddle a tap buffer)
+size_t ctx_i4_bytes(const dflash_dims& d, int n) {
+    if (d.wdtype != DFLASH_INT4G64 || !i4mm_ok(d.m * d.H, n)) return 0;
+    int ns = 1, ks = 0;
+    i4mm_split(d.m * d.H, &ns, &ks);
+    if (d.H % ks) return 0;
+    return align_up((size_t)ns * n * d.d * 4);
+}
+// int4 K/V append of n <= 16 pre-normalised rows on matrix cores: the normalised rows, then
+// split partials [nl][ns][n][2 hkv hd] (0: not served there)
+size_t kv_i4_bytes(const dflash_dims& d, int n) {
+    if (d.wdtype != DFLASH_INT4G64 || !prenorm(d) || d.nl < 1 || !i4mm_ok(d.d, n)) return 0;
+    int ns = 1, ks = 0;
+    i4mm_split(d.d, &ns, &ks);
+    return kv_append_norm_bytes(d, n) + align_up((size_t)d.nl * ns * n * 2 * d.hkv * d.hd * 4);
+}
+
 size_t kv_append_skinny_bytes(const dflash_dims& d, int n) {
     if (!ctx_skinny_rows(d, n) || d.d % kSkinnyK || d.nl < 1) return 0;
     const int N = 2 * d.hkv * d.hd;
@@ -440,6 +458,8 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     if (prenorm(d) && w.total < kv_append_norm_bytes(d, nr)) w.total = kv_append_norm_bytes(d, nr);
     if (prenorm(d) && w.total < kv_append_split_bytes(d, nr < 8 ? nr : 8))
         w.total = kv_append_split_bytes(d, nr < 8 ? nr : 8);
+    if (w.total < ctx_i4_bytes(d, nr)) w.total = ctx_i4_bytes(d, nr);
+    if (w.total < kv_i4_bytes(d, nr)) w.total = kv_i4_bytes(d, nr);
     char* c = static_cast<char*>(base);
     if (c) {
         w.hd = reinterpret_cast<float*>(c + o_hd);
@@ -548,9 +568,10 @@ hipError_t gemv_plain(const dflash_dims& d, int wt, int epi, GemvParams p, int r
     if (i4) {
         I4Params q;
         std::memset(&q, 0, sizeof(q));
-        q.codes = static_cast<const uint32_t*>(p.w[0].data);
-        q.scales = p.w[0].scales;
-        q.biases = p.w[0].biases;
+        q.codes[0] = static_cast<const uint32_t*>(p.w[0].data);
+        q.scales[0] = p.w[0].scales;
+        q.biases[0] = p.w[0].biases;
+        q.layers = 1;
         q.N = p.N;
         q.K = p.K;
         q.a = reinterpret_cast<const uint16_t*>(p.x);
@@ -946,9 +967,10 @@ int lm_head(const dflash_weight& E, const void* y, int y_f32, int rows, int H, i
         if ((size_t)ns * rows * V * 4 <= i4part_bytes) {
             I4Params q;
             std::memset(&q, 0, sizeof(q));
-            q.codes = static_cast<const uint32_t*>(E.data);
-            q.scales = static_cast<const uint16_t*>(E.scales);
-            q.biases = static_cast<const uint16_t*>(E.biases);
+            q.codes[0] = static_cast<const uint32_t*>(E.data);
+            q.scales[0] = static_cast<const uint16_t*>(E.scales);
+            q.biases[0] = static_cast<const uint16_t*>(E.biases);
+            q.layers = 1;
             q.N = V;
             q.K = H;
             q.a = static_cast<const uint16_t*>(y);
@@ -1361,6 +1383,26 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
         g.c_ld = d.d;
         DFL_HIP(launch_gemm(GEMM_A_TAPS, GEMM_EPI_F32, g, 1, s));
         DFL_HIP(launch_rownorm(h_ctx, 1, 0, h_ctx, n, d.d, M->ctx_norm, 0, d.eps, s));
+    } else if (M->w_c.dtype == DFLASH_INT4G64 && ctx_i4_bytes(d, n) > 0 && ws && aligned16(ws) &&
+               ws_bytes >= ctx_i4_bytes(d, n)) {
+        // int4 W_c, up to 16 rows: matrix-core K ranges (each inside one tap buffer), split
+        // partials in ws added in split order by the norm
+        I4Params q;
+        std::memset(&q, 0, sizeof(q));
+        q.codes[0] = static_cast<const uint32_t*>(M->w_c.data);
+        q.scales[0] = static_cast<const uint16_t*>(M->w_c.scales);
+        q.biases[0] = static_cast<const uint16_t*>(M->w_c.biases);
+        q.layers = 1;
+        q.N = d.d;
+        q.K = d.m * d.H;
+        for (int j = 0; j < d.m; ++j) q.a_seg[j] = static_cast<const uint16_t*>(taps[j]);
+        q.seg_k = d.H;
+        q.a_ld = tap_ld;
+        q.M = n;
+        i4mm_split(q.K, &q.nsplit, &q.kslice);
+        q.part = static_cast<float*>(ws);
+        DFL_HIP(launch_i4mm(q, s));
+        DFL_HIP(launch_rownorm(q.part, q.nsplit, (int64_t)n * d.d, h_ctx, n, d.d, M->ctx_norm, 0, d.eps, s));
     } else if (n <= 8 && splits > 1 && ws && ws_bytes >= part_bytes) {
         // few rows: split the long reduction over more workgroups; partials in ws
         p.rpw = 4;
@@ -1567,9 +1609,52 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
     p.cap = kv->cap;
     p.kv_f32 = kv->dtype == DFLASH_F32;
     p.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
+    bool i4w = true;  // every layer's K/V weights int4-g64
+    for (int i = 0; i < d.nl; ++i) i4w = i4w && M->layers[i].w_qkv.dtype == DFLASH_INT4G64;
     int split_ks = 0;
     const int split_ns = pro == PRO_PLAIN ? kv_append_gemv_split(d, n, &split_ks) : 1;
-    if (split_ns > 1 && !p.kv_f32 && ws_bytes >= kv_append_split_bytes(d, n)) {
+    if (pro == PRO_PLAIN && i4w && !p.kv_f32 && kv_i4_bytes(d, n) > 0 && ws_bytes >= kv_i4_bytes(d, n)) {
+        // int4, up to 16 rows: every layer's [K | V] on matrix cores (grid.y = layer) as split
+        // partials, then one reduce over all layers adds them in order and scatters the rows
+        float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + kv_append_norm_bytes(d, n));
+        I4Params q;
+        std::memset(&q, 0, sizeof(q));
+        for (int i = 0; i < d.nl; ++i) {
+            q.codes[i] = static_cast<const uint32_t*>(M->layers[i].w_qkv.data);
+            q.scales[i] = static_cast<const uint16_t*>(M->layers[i].w_qkv.scales);
+            q.biases[i] = static_cast<const uint16_t*>(M->layers[i].w_qkv.biases);
+        }
+        q.w_row0 = (int64_t)d.hq * d.hd;  // the K and V rows of the fused QKV matrix
+        q.layers = d.nl;
+        q.N = p.N;
+        q.K = d.d;
+        q.a = static_cast<const uint16_t*>(ws);  // each layer's normalised rows
+        q.a_ld = d.d;
+        q.a_layer_stride = (int64_t)n * d.d;
+        q.M = n;
+        i4mm_split(q.K, &q.nsplit, &q.kslice);
+        q.part = part;
+        DFL_HIP(launch_i4mm(q, s));
+        SkinnyParams r;
+        std::memset(&r, 0, sizeof(r));
+        r.M = n;
+        r.N = p.N;
+        r.layers = d.nl;
+        r.nsplit = q.nsplit;
+        r.part = part;
+        r.kcache = static_cast<uint16_t*>(kv->k);
+        r.vcache = static_cast<uint16_t*>(kv->v);
+        r.len = kv->len;
+        r.row_offsets = row_offsets;
+        r.counts = counts;
+        r.row_base = 0;
+        r.B = kv->B;
+        r.cap = kv->cap;
+        r.hkv = d.hkv;
+        r.hd = d.hd;
+        r.layer_stride = p.layer_stride;
+        DFL_HIP(launch_split_reduce(SK_KV, r, s));
+    } else if (split_ns > 1 && !p.kv_f32 && ws_bytes >= kv_append_split_bytes(d, n)) {
         // K ranges write fp32 partials (one set per layer), then one reduce over all layers
         // adds them in split order and scatters the rows into the caches
         float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + kv_append_norm_bytes(d, n));

@@ -78,6 +78,7 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
     // the K ranges of one group of 64 weight rows are consecutive workgroups, so they run
     // together and share the rows' scale and bias lines in L2
     const int s = blockIdx.x % p.nsplit;
+    const int layer = blockIdx.y;
     const int kb = s * p.kslice;
     const int nblk = min(p.kslice, p.K - kb) / kI4Block;  // 1 .. kI4MaxBlocks
     const int kw = nblk * kI4Block;
@@ -87,20 +88,24 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
     // the range's activation rows: issued first (loads return in order)
     constexpr int kChunks = MT * kI4MaxBlocks * kI4Block / 8 / kBlock;  // 16-byte chunks per thread
     const int cpr = kw / 8;                                             // chunks per row
+    // the range lies in one column segment (seg_k a multiple of kslice)
+    const uint16_t* abase = p.seg_k > 0 ? p.a_seg[kb / p.seg_k] + kb % p.seg_k
+                                        : p.a + layer * p.a_layer_stride + kb;
     u32x4 av[kChunks];
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
         const int idx = min(tid + i * kBlock, MT * cpr - 1);
         const int m = idx / cpr, c = idx - m * cpr;
-        av[i] = *reinterpret_cast<const u32x4*>(p.a + (int64_t)min(m, p.M - 1) * p.a_ld + kb + 8 * c);
+        av[i] = *reinterpret_cast<const u32x4*>(abase + (int64_t)min(m, p.M - 1) * p.a_ld + 8 * c);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the weight loads
 
     // every block's codes, scales and biases (clamped past the range: loaded, never used)
     const int K8 = p.K / 8, K64 = p.K / 64;
-    const uint32_t* crow = p.codes + (int64_t)n * K8 + kb / 8 + 2 * grp;
-    const uint32_t* srow = reinterpret_cast<const uint32_t*>(p.scales + (int64_t)n * K64 + kb / 64);
-    const uint32_t* brow = reinterpret_cast<const uint32_t*>(p.biases + (int64_t)n * K64 + kb / 64);
+    const int64_t wrow = p.w_row0 + n;
+    const uint32_t* crow = p.codes[layer] + wrow * K8 + kb / 8 + 2 * grp;
+    const uint32_t* srow = reinterpret_cast<const uint32_t*>(p.scales[layer] + wrow * K64 + kb / 64);
+    const uint32_t* brow = reinterpret_cast<const uint32_t*>(p.biases[layer] + wrow * K64 + kb / 64);
     uint2 c0[kI4MaxBlocks], c1[kI4MaxBlocks];
     uint32_t sc[kI4MaxBlocks], bi[kI4MaxBlocks];
 #pragma unroll
@@ -190,7 +195,7 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int m = 4 * grp + e;
-            if (m < p.M) p.part[((int64_t)s * p.M + m) * p.N + nout] = acc[e];
+            if (m < p.M) p.part[(((int64_t)layer * p.nsplit + s) * p.M + m) * p.N + nout] = acc[e];
         }
     }
     trace_end(p.stamps, t_start);
@@ -234,17 +239,28 @@ void i4mm_split(int K, int* nsplit, int* kslice) {
 }
 
 hipError_t launch_i4mm(I4Params p, hipStream_t s) {
-    if (!i4mm_ok(p.K, p.M) || p.N <= 0 || !p.codes || !p.scales || !p.biases || !p.a || !p.part) return hipErrorInvalidValue;
-    if (p.kslice <= 0 || p.kslice % kI4Block || p.kslice > kI4MaxBlocks * kI4Block || p.a_ld % 8 || p.a_ld < p.K)
+    if (!i4mm_ok(p.K, p.M) || p.N <= 0 || !p.part || p.layers < 1 || p.layers > kI4MaxLayers || p.w_row0 < 0)
         return hipErrorInvalidValue;
+    for (int z = 0; z < p.layers; ++z)
+        if (!p.codes[z] || !p.scales[z] || !p.biases[z]) return hipErrorInvalidValue;
+    if (p.kslice <= 0 || p.kslice % kI4Block || p.kslice > kI4MaxBlocks * kI4Block || p.a_ld % 8)
+        return hipErrorInvalidValue;
+    if (p.seg_k > 0) {
+        if (p.seg_k % p.kslice || p.a_ld < p.seg_k || (p.K + p.seg_k - 1) / p.seg_k > kI4MaxSegs) return hipErrorInvalidValue;
+        for (int j = 0; j < (p.K + p.seg_k - 1) / p.seg_k; ++j)
+            if (!p.a_seg[j]) return hipErrorInvalidValue;
+    } else if (!p.a || p.a_ld < p.K) {
+        return hipErrorInvalidValue;
+    }
     if (p.nsplit != (p.K + p.kslice - 1) / p.kslice) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(((p.N + 63) / 64) * p.nsplit));
+    const dim3 grid((unsigned)(((p.N + 63) / 64) * p.nsplit), (unsigned)p.layers);
     // instrumentation: algorithmic bytes = int4 weights (codes, scales, biases) + activations + partials
-    const double bytes = (double)p.N * p.K * (0.5 + 4.0 / 64) + (double)p.M * p.K * 2.0 + (double)p.nsplit * p.M * p.N * 4.0;
+    const double bytes = p.layers * ((double)p.N * p.K * (0.5 + 4.0 / 64) + (double)p.M * p.K * 2.0 +
+                                     (double)p.nsplit * p.M * p.N * 4.0);
     const int mt = p.M <= 4 ? 4 : (p.M <= 8 ? 8 : 16);
     char name[32];
     snprintf(name, sizeof name, "i4mm_kernel<%d>", mt);
-    p.stamps = trace_launch(TRACE_PROJECTIONS, name, (int64_t)grid.x, bytes, 0.0);
+    p.stamps = trace_launch(TRACE_PROJECTIONS, name, (int64_t)grid.x * grid.y, bytes, 0.0);
     (void)hipGetLastError();  // report only this launch's status
     const bool full = p.kslice == kI4MaxBlocks * kI4Block && p.K % p.kslice == 0;
 #define DFL_I4_LAUNCH(MT)                                                                \
