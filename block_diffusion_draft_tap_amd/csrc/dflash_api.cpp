@@ -1402,7 +1402,17 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
         i4mm_split(q.K, &q.nsplit, &q.kslice);
         q.part = static_cast<float*>(ws);
         DFL_HIP(launch_i4mm(q, s));
-        DFL_HIP(launch_rownorm(q.part, q.nsplit, (int64_t)n * d.d, h_ctx, n, d.d, M->ctx_norm, 0, d.eps, s));
+        // the K ranges' sums over many workgroups (split order), then the norm in place
+        SkinnyParams r;
+        std::memset(&r, 0, sizeof(r));
+        r.M = n;
+        r.N = d.d;
+        r.nsplit = q.nsplit;
+        r.part = q.part;
+        r.out = h_ctx;
+        r.out_ld = d.d;
+        DFL_HIP(launch_split_reduce(SK_STORE, r, s));
+        DFL_HIP(launch_rownorm(h_ctx, 1, 0, h_ctx, n, d.d, M->ctx_norm, 0, d.eps, s));
     } else if (n <= 8 && splits > 1 && ws && ws_bytes >= part_bytes) {
         // few rows: split the long reduction over more workgroups; partials in ws
         p.rpw = 4;

@@ -15,12 +15,13 @@
 // Lane (c, g) of a wavefront (c = lane % 16, g = lane / 16) supplies, for k-step
 // j of a 128-column block, the 8 columns 64 (j / 2) + 16 g + 8 (j % 2) .. +8: the
 // codes of weight row c there are one 32-bit word, and the four steps keep every
-// step inside one quantisation group. The two code words a lane needs per block
-// (two 8-byte loads) and the block's scales and biases for its output column
-// are all loaded before the first product; a workgroup (four wavefronts, 64
-// weight rows) takes a K range of up to 8 blocks and stages that range of the
-// activation rows once in LDS, already in the codes' pair order, with each
-// row's per-group sum.
+// step inside one quantisation group. A workgroup (four wavefronts, 64 weight
+// rows) takes a K range of up to 8 blocks: it reads its rows' codes as
+// contiguous 512-byte runs into LDS (loaded fragment by fragment, the codes
+// would come as 16 rows x 32 bytes per instruction, a pattern DRAM serves at
+// about half the rate), stages that range of the activation rows once in LDS,
+// already in the codes' pair order, with each row's per-group sum, and loads
+// its output columns' scales and biases; then the products run from LDS.
 //
 // Results are fp32 partial sums per K range; an ordered reduce applies the
 // epilogue (the skinny reduce kernels, or the split argmax below).
@@ -41,13 +42,21 @@ __device__ __forceinline__ f32x4 mma(const u32x4& a, const u32x4& b, const f32x4
                                                    0, 0);
 }
 
-// a word of 8 codes (low nibble first) as bf16 pairs (128 + q_i, 128 + q_(i+4)), i = 0..3
-__device__ __forceinline__ u32x4 codes_bf16(uint32_t c) {
+// (x & mask) | one in one instruction (the compiler splits it into an and and an or)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t one) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(one));
+    return r;
+}
+
+// a word of 8 codes (low nibble first) as bf16 pairs (128 + q_i, 128 + q_(i+4)), i = 0..3;
+// mask = 0x000F000F and one = 0x43004300 (bf16 128.0 in both halves), held in registers
+__device__ __forceinline__ u32x4 codes_bf16(uint32_t c, uint32_t mask, uint32_t one) {
     u32x4 r;
-    r[0] = (c & 0x000F000Fu) | 0x43004300u;
-    r[1] = ((c >> 4) & 0x000F000Fu) | 0x43004300u;
-    r[2] = ((c >> 8) & 0x000F000Fu) | 0x43004300u;
-    r[3] = ((c >> 12) & 0x000F000Fu) | 0x43004300u;
+    r[0] = and_or(c, mask, one);
+    r[1] = and_or(c >> 4, mask, one);
+    r[2] = and_or(c >> 8, mask, one);
+    r[3] = and_or(c >> 12, mask, one);
     return r;
 }
 
@@ -64,13 +73,16 @@ __device__ __forceinline__ u32x4 pair_order(const u32x4& x) {
 
 constexpr int kAld = kI4MaxBlocks * kI4Block + 8;  // LDS activation row (bf16), padded by 16 bytes
 constexpr int kMaxGroups = kI4MaxBlocks * kI4Block / 64;
+constexpr int kCodeLd = kI4MaxBlocks * kI4Block / 8 + 4;  // LDS code row (32-bit words), padded by 16 bytes
+constexpr int kCodeChunks = 64 * kI4MaxBlocks * kI4Block / 32 / kBlock;  // 16-byte code chunks per thread
 
 // MT: activation rows staged (4, 8 or 16; rows past M are zero, MFMA rows past MT too).
 // FULL: every K range is 8 blocks and K/64 a multiple of 16, so a lane's 16 scales (and
 // biases) of its range are two 16-byte loads.
 template <int MT, bool FULL>
 __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
-    __shared__ __align__(16) uint16_t as[MT * kAld];            // rows in the codes' pair order
+    __shared__ __align__(16) uint16_t as[(MT + 1) * kAld];      // rows in the codes' pair order; row MT zero
+    __shared__ __align__(16) uint32_t cs[64 * kCodeLd];         // the workgroup's 64 weight rows' codes
     __shared__ __align__(16) float xs[kMaxGroups][kI4Rows];     // sum of each row's group (rows past MT: 0)
     const uint64_t t_start = trace_start(p.stamps);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -85,35 +97,40 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
     const int tile = (blockIdx.x / p.nsplit) * 4 + wave;   // 16 weight rows of this wavefront
     const int n = min(tile * 16 + col, p.N - 1);           // this lane's weight row and output column
 
-    // the range's activation rows: issued first (loads return in order)
-    constexpr int kChunks = MT * kI4MaxBlocks * kI4Block / 8 / kBlock;  // 16-byte chunks per thread
-    const int cpr = kw / 8;                                             // chunks per row
+    // the range's activation rows and a zero row: issued first (loads return in order)
+    constexpr int kRowChunks = kI4MaxBlocks * kI4Block / 8;
+    constexpr int kChunks = ((MT + 1) * kRowChunks + kBlock - 1) / kBlock;  // 16-byte chunks per thread
+    const int cpr = FULL ? kRowChunks : kw / 8;                             // chunks per row
     // the range lies in one column segment (seg_k a multiple of kslice)
     const uint16_t* abase = p.seg_k > 0 ? p.a_seg[kb / p.seg_k] + kb % p.seg_k
                                         : p.a + layer * p.a_layer_stride + kb;
     u32x4 av[kChunks];
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-        const int idx = min(tid + i * kBlock, MT * cpr - 1);
+        const int idx = min(tid + i * kBlock, (MT + 1) * cpr - 1);
         const int m = idx / cpr, c = idx - m * cpr;
         av[i] = *reinterpret_cast<const u32x4*>(abase + (int64_t)min(m, p.M - 1) * p.a_ld + 8 * c);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the weight loads
 
-    // every block's codes, scales and biases (clamped past the range: loaded, never used)
+    // the workgroup's codes: its 64 weight rows' K range, read as contiguous runs of each row
+    // (32 threads cover a row's 512 bytes) and staged in LDS; rows past N repeat row N - 1
     const int K8 = p.K / 8, K64 = p.K / 64;
+    const int row0 = (blockIdx.x / p.nsplit) * 64;
+    const int ccr = FULL ? kI4MaxBlocks * kI4Block / 32 : kw / 32;  // 16-byte code chunks per row
+    u32x4 cv[kCodeChunks];
+#pragma unroll
+    for (int i = 0; i < kCodeChunks; ++i) {
+        const int idx = min(tid + i * kBlock, 64 * ccr - 1);
+        const int r = idx / ccr, c = idx - r * ccr;
+        const int64_t grow = p.w_row0 + min(row0 + r, p.N - 1);
+        cv[i] = *reinterpret_cast<const u32x4*>(p.codes[layer] + grow * K8 + kb / 8 + 4 * c);
+    }
+    // this lane's output column's scales and biases (clamped past the range: never used)
     const int64_t wrow = p.w_row0 + n;
-    const uint32_t* crow = p.codes[layer] + wrow * K8 + kb / 8 + 2 * grp;
     const uint32_t* srow = reinterpret_cast<const uint32_t*>(p.scales[layer] + wrow * K64 + kb / 64);
     const uint32_t* brow = reinterpret_cast<const uint32_t*>(p.biases[layer] + wrow * K64 + kb / 64);
-    uint2 c0[kI4MaxBlocks], c1[kI4MaxBlocks];
     uint32_t sc[kI4MaxBlocks], bi[kI4MaxBlocks];
-#pragma unroll
-    for (int b = 0; b < kI4MaxBlocks; ++b) {
-        const int bb = min(b, nblk - 1);
-        c0[b] = *reinterpret_cast<const uint2*>(crow + 16 * bb);
-        c1[b] = *reinterpret_cast<const uint2*>(crow + 16 * bb + 8);
-    }
     if constexpr (FULL) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -138,10 +155,16 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
     // last chunk with its value, so no load is moved into a branch and waited for there)
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-        const int idx = min(tid + i * kBlock, MT * cpr - 1);
+        const int idx = min(tid + i * kBlock, (MT + 1) * cpr - 1);
         const int m = idx / cpr, c = idx - m * cpr;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(&as[m * kAld + 8 * c]) = m < p.M ? pair_order(av[i]) : z;
+        *reinterpret_cast<u32x4*>(&as[m * kAld + 8 * c]) = (m < p.M && m < MT) ? pair_order(av[i]) : z;
+    }
+#pragma unroll
+    for (int i = 0; i < kCodeChunks; ++i) {
+        const int idx = min(tid + i * kBlock, 64 * ccr - 1);
+        const int r = idx / ccr, c = idx - r * ccr;
+        *reinterpret_cast<u32x4*>(&cs[r * kCodeLd + 4 * c]) = cv[i];
     }
     __syncthreads();
     // each row's group sums (any order of the group's 64 values: a sum)
@@ -154,16 +177,16 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
             for (int q = 0; q < 8; ++q) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(&as[m * kAld + 64 * g + 8 * q]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t += bf16_lo(v[e]) + bf16_hi(v[e]);
+                for (int e = 0; e < 4; ++e) t = dot2_bf16(v[e], 0x3F803F80u, t);  // + both halves
             }
         }
         if (m < kI4Rows) xs[g][m] = t;  // 256 threads: every (group, row) slot written
     }
     __syncthreads();
 
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const int arow = min(col, MT - 1);  // A fragment row (zero past MT)
+    const uint16_t* arow = &as[(col < MT ? col : MT) * kAld + 16 * grp];  // A fragment row (the zero row past MT)
+    const uint32_t* crow = &cs[(wave * 16 + col) * kCodeLd + 2 * grp];
     f32x4 acc = zero;
 #pragma unroll
     for (int b = 0; b < kI4MaxBlocks; ++b) {
@@ -172,20 +195,26 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
             // 128 b + 64 (j / 2) + 16 grp + 8 (j % 2) .. + 8 (already in pair order)
             u32x4 af[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(
-                    &as[arow * kAld + kI4Block * b + 64 * (j >> 1) + 16 * grp + 8 * (j & 1)]);
-                af[j] = col < MT ? v : zero4;
-            }
+            for (int j = 0; j < 4; ++j)
+                af[j] = *reinterpret_cast<const u32x4*>(arow + kI4Block * b + 64 * (j >> 1) + 8 * (j & 1));
+            // this lane's codes: weight row wave * 16 + col, words 16 b + 2 grp (+1) and + 8
+            const uint2 c0 = *reinterpret_cast<const uint2*>(crow + 16 * b);
+            const uint2 c1 = *reinterpret_cast<const uint2*>(crow + 16 * b + 8);
             // per group: sum_k (128 + q) x over the group's two steps
-            const f32x4 p0 = mma(af[1], codes_bf16(c0[b].y), mma(af[0], codes_bf16(c0[b].x), zero));
-            const f32x4 p1 = mma(af[3], codes_bf16(c1[b].y), mma(af[2], codes_bf16(c1[b].x), zero));
+            const uint32_t mk = p.nib_mask, one = p.bf16_128;
+            const f32x4 p0 = mma(af[1], codes_bf16(c0.y, mk, one), mma(af[0], codes_bf16(c0.x, mk, one), zero));
+            const f32x4 p1 = mma(af[3], codes_bf16(c1.y, mk, one), mma(af[2], codes_bf16(c1.x, mk, one), zero));
             const f32x4 x0 = *reinterpret_cast<const f32x4*>(&xs[2 * b][4 * grp]);
             const f32x4 x1 = *reinterpret_cast<const f32x4*>(&xs[2 * b + 1][4 * grp]);
             const float s0 = bf16_lo(sc[b]), s1 = bf16_hi(sc[b]);
             const float b0 = bf16_lo(bi[b]) - 128.0f * s0, b1 = bf16_hi(bi[b]) - 128.0f * s1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += (s0 * p0[e] + b0 * x0[e]) + (s1 * p1[e] + b1 * x1[e]);
+            for (int e = 0; e < 4; ++e) {
+                acc[e] = fmaf(s0, p0[e], acc[e]);
+                acc[e] = fmaf(b0, x0[e], acc[e]);
+                acc[e] = fmaf(s1, p1[e], acc[e]);
+                acc[e] = fmaf(b1, x1[e], acc[e]);
+            }
         }
     }
 
@@ -254,6 +283,8 @@ hipError_t launch_i4mm(I4Params p, hipStream_t s) {
     }
     if (p.nsplit != (p.K + p.kslice - 1) / p.kslice) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(((p.N + 63) / 64) * p.nsplit), (unsigned)p.layers);
+    p.nib_mask = 0x000F000Fu;
+    p.bf16_128 = 0x43004300u;
     // instrumentation: algorithmic bytes = int4 weights (codes, scales, biases) + activations + partials
     const double bytes = p.layers * ((double)p.N * p.K * (0.5 + 4.0 / 64) + (double)p.M * p.K * 2.0 +
                                      (double)p.nsplit * p.M * p.N * 4.0);

@@ -34,6 +34,7 @@ struct I4Params {
     int nsplit, kslice;      // K ranges; kslice a multiple of 128, at most 1024
     float* part;             // fp32 partial sums [layers][nsplit][M][N]
     uint64_t* stamps;        // set by the launcher when the launch is traced
+    uint32_t nib_mask, bf16_128;  // set by the launcher: the code unpack's constants
 };
 
 // whether a product of M rows over K columns runs here
