@@ -71,7 +71,7 @@ namespace {
 constexpr int kSW = DFL_SK_WAVES, kSNB = DFL_SK_NB, kST = 64 * kSW;
 constexpr int kSCols = 16 * kSNB * kSW;  // weight rows per workgroup tile
 constexpr int kSKC = kSkinnyK;           // K per chunk
-constexpr int kSLd = kSKC + 8;           // padded LDS row (bf16): 8 lanes of a 16-byte read on distinct banks
+constexpr int kSLd = kSKC + 16;          // padded LDS row (bf16): 72 words, 8 past a multiple of 32 (conflict-free fragment reads)
 constexpr int kSSteps = kSKC / 32;       // MFMA k-steps per chunk
 static_assert(kSNB % 2 == 0, "the gated epilogue pairs gate and up fragments");
 
