@@ -254,6 +254,14 @@ int ctx_splits(const dflash_dims& d) {
 // long rows of a bf16 / int4 drafter: RMSNorm once per row into bf16 rows (norm_rows)
 // instead of two passes over the fp32 row in every GEMV workgroup's prologue
 bool prenorm(const dflash_dims& d) { return d.wdtype != DFLASH_F32 && d.d > kRegNormMaxK; }
+// ... and from this many on drafters with long rows (d, or the head's H, above the register
+// norm's limit): there an 8-row GEMV pass over the long weight rows costs more than one
+// matrix-core pass for all rows (Wide, 7 rows: 675 -> 723 blocks/s); on short rows the
+// GEMVs' latency is lower (Default, 5 rows: 3,335 against 2,665 on matrix cores)
+#ifndef DFL_SKINNY_MIN_ROWS_WIDE
+#define DFL_SKINNY_MIN_ROWS_WIDE 4
+#endif
+int skinny_min_rows(const dflash_dims& d) { return prenorm(d) ? DFL_SKINNY_MIN_ROWS_WIDE : DFL_SKINNY_MIN_ROWS; }
 // split-K of the plain-prologue GEMVs (residual, store and gated epilogues): K ranges
 // of at most this many elements for the 8-row kernels (twice as many for the 4-row
 // int4 kernel), which stage once within the normal LDS budget with several
@@ -275,10 +283,11 @@ void gemv_split(const dflash_dims& d, int K, int rows, int* nsplit, int* kslice)
 }
 
 bool lm_head_skinny(int wdtype, int y_f32, int rows, int H) {
-    return wdtype == DFLASH_BF16 && !y_f32 && rows >= DFL_SKINNY_MIN_ROWS && H % kSkinnyK == 0;
+    return wdtype == DFLASH_BF16 && !y_f32 && H % kSkinnyK == 0 &&
+           rows >= (H > kRegNormMaxK ? DFL_SKINNY_MIN_ROWS_WIDE : DFL_SKINNY_MIN_ROWS);
 }
 bool skinny_ok(const dflash_dims& d, int rows) {
-    return d.wdtype == DFLASH_BF16 && rows >= DFL_SKINNY_MIN_ROWS && d.d % kSkinnyK == 0 && d.F % kSkinnyK == 0 &&
+    return d.wdtype == DFLASH_BF16 && rows >= skinny_min_rows(d) && d.d % kSkinnyK == 0 && d.F % kSkinnyK == 0 &&
            d.H % kSkinnyK == 0;
 }
 // fp32 split-K partials of the skinny launches of a forward (rows in launches of kSkinnyRows)
@@ -321,7 +330,7 @@ size_t skinny_part_bytes(const dflash_dims& d, int rows) {
 // partial sums [nsplit][n][d]. K/V append: each layer's normalised rows, bf16
 // [nl][n][d], then the split-K partials [nl][nsplit][n][2 hkv hd].
 bool ctx_skinny_rows(const dflash_dims& d, int n) {
-    return d.wdtype == DFLASH_BF16 && n >= DFL_SKINNY_MIN_ROWS && n <= kSkinnyRows;
+    return d.wdtype == DFLASH_BF16 && n >= skinny_min_rows(d) && n <= kSkinnyRows;
 }
 size_t ctx_project_skinny_bytes(const dflash_dims& d, int n) {
     if (!ctx_skinny_rows(d, n) || d.H % kSkinnyK || d.m > kMaxTaps) return 0;
