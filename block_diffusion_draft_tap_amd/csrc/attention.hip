@@ -9,16 +9,18 @@
 //
 // bf16 caches: attn_mfma_kernel. Each wavefront of a workgroup is its own
 // split and walks 32-key chunks with no workgroup barriers:
-//   S = Q K^T    v_mfma_f32_16x16x32_bf16; the 16-row Q tiles stay in
-//                registers, K rows are read straight from HBM (one 16-byte
-//                chunk of 8 head dims per lane);
-//   softmax      online per row; a row of a 16x16 score tile lives in one
-//                16-lane DPP row, so its max and sum take four DPP steps;
-//   O += P V     P goes through a per-wavefront LDS tile into the A-operand
-//                layout, split into bf16 high and low parts (two products)
-//                so the probabilities keep ~16 mantissa bits; V is cached
-//                head-dim major, so the B operand (8 consecutive keys of one
-//                dim) is one 16-byte load.
+//   S^T = K Q^T  v_mfma_f32_16x16x32_bf16 with K rows as the A operand (one
+//                16-byte chunk of 8 head dims per lane, straight from HBM) and
+//                the 16-row Q tiles, held in registers, as the B operand;
+//   softmax      online per query row; the 32 keys of a row sit in the four
+//                lanes col, col+16, col+32, col+48 (8 each), so its max and
+//                sum take two row swaps; the reference max moves lazily;
+//   O^T += V^T P^T  P stays in the row's lanes as the B operand, split into
+//                bf16 high and low parts (two products) so the probabilities
+//                keep ~16 mantissa bits; V is cached head-dim major, so the A
+//                operand (8 consecutive keys of one dim) is one 16-byte load.
+// attn_rows_kernel (33..48 query rows, few units) gives each 16-row tile its own
+// wavefront and forms S = Q K^T, passing P through LDS.
 // Lane layout of the 16x16x32 product (lane l): A[l%16][8(l/16)+e],
 // B[8(l/16)+e][l%16] for e < 8; D[4(l/16)+e][l%16] for e < 4.
 //
@@ -76,26 +78,152 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
 
 // ---------------------------------------------------------------------------
 // MFMA kernel (bf16 caches; Q, K_b and V_b arrive as bf16)
+//
+// Scores are formed transposed, S^T = K Q^T (K rows the A operand, Q rows the B
+// operand), and the output as O^T = V^T P^T: the probabilities of a query row then
+// stay in the lanes of that row, from the score accumulator straight into the B
+// operand of the value product, with no trip through LDS. Key tile nt of a unit
+// loads key 8*(c/4) + 4*nt + c%4 into A row c, so lane (col, grp) of the score tiles
+// holds keys 8*grp .. 8*grp + 7 of query row col -- the keys that lane's B operand
+// carries in the value product, whose A operand (V^T, 8 consecutive keys of one
+// head dim per lane) is one 16-byte load of the head-dim-major V cache.
+
+// max and sum over the four lanes col, col + 16, col + 32, col + 48: gfx950's row
+// swaps exchange rows 0/1 and 2/3, then the two halves; every lane ends with the
+// same value (the two operands of each step are the same pair in either order)
+__device__ __forceinline__ float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32_e32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float rows4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// One unit's online softmax for one 16-row query tile held transposed: sc[nt][e] is the
+// score of key 8*grp + 4*nt + e for query row col (raw Q.K). Keys outside [lo, nvalid)
+// take no weight when `ragged`. m is the row's reference max (log2 units) and l its sum
+// of exp2(score - m). The reference moves only when some row of the tile passes it by
+// more than kLazy: until then the probabilities may reach 2^kLazy (fp32 and the two-part
+// bf16 P hold that) and o and l need no rescaling, which on most units saves the pass
+// over o (held in accumulation registers, so each rescale is a read, a multiply and a
+// write per element). When it moves, every row of the tile takes its own max (rows
+// below their reference keep it: exp2(0) = 1 exactly) and o is rescaled when `rescale`
+// (o is still zero on a wavefront's first unit). Returns P = hi + lo as two bf16 B
+// operands (keys 8*grp .. +7 in order), so the product keeps ~16 mantissa bits of P.
+constexpr float kLazy = 8.0f;
+
+template <int DT>
+__device__ __forceinline__ void softmax_tile(const f32x4 (&sc)[2], const bool ragged, const int grp, const int lo,
+                                             const int nvalid, const float sl2, const bool rescale, float& m,
+                                             float& l, f32x4 (&o)[DT], u32x4& ph, u32x4& pl) {
+    float sv[8];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[4 * nt + e] = sc[nt][e];
+    if (ragged) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int key = 8 * grp + j;
+            if (key < lo || key >= nvalid) sv[j] = -INFINITY;
+        }
+    }
+    // finite: a unit holds a valid key
+    const float mt =
+        sl2 * rows4_max(vmax(vmax3(sv[0], sv[1], sv[2]), vmax3(vmax3(sv[3], sv[4], sv[5]), sv[6], sv[7])));
+    if (__builtin_amdgcn_ballot_w64(mt > m + kLazy)) {
+        const float mn = fmaxf(m, mt);
+        const float al = __builtin_amdgcn_exp2f(m - mn);
+        l *= al;
+        m = mn;
+        if (rescale) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[dt] *= al;
+        }
+    }
+    float pv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[j], sl2, -m));
+    l += rows4_sum(((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7])));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t h = pack_bf16x2(pv[2 * q], pv[2 * q + 1]);
+        ph[q] = h;
+        pl[q] = pack_bf16x2(pv[2 * q] - bf16_lo(h), pv[2 * q + 1] - bf16_hi(h));
+    }
+}
+
+// keys past nvalid are zeroed in a V operand (lane keys 8*grp .. +7; P is zero there, the
+// cache may hold anything)
+template <int DT>
+__device__ __forceinline__ void mask_v(u32x4 (&vb)[DT], const int nvalid, const int grp) {
+    const int nk = nvalid - 8 * grp;  // valid keys among this lane's 8
+    u32x4 mk;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mk[q] = (2 * q + 1 < nk) ? 0xFFFFFFFFu : ((2 * q < nk) ? 0x0000FFFFu : 0u);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vb[dt] &= mk;
+}
+
+// Workgroups start in block order, and a sequence's work grows with its length, so the
+// sequences are taken longest first (ties by index): the last workgroups to start are the
+// shortest, which evens out when the compute units run dry. Sequence of rank `pos` in
+// that order; the rank is formed from the lengths on the device (every workgroup alike).
+#ifndef DFL_ATTN_LPT
+#define DFL_ATTN_LPT 1
+#endif
+constexpr int kLptMaxSeqs = 256;
+__device__ __forceinline__ int lpt_sequence(const AttnParams& p, const int pos) {
+    if (!DFL_ATTN_LPT || p.B <= 1 || p.B > kLptMaxSeqs) return pos;
+    __shared__ int chosen;
+    auto len = [&](int j) {
+        const int L = min(max(p.len[j], 0), p.cap);
+        return p.window > 0 ? min(L, p.window) : L;
+    };
+    for (int t = threadIdx.x; t < p.B; t += kBlock) {
+        const int lt = len(t);
+        int rank = 0;
+        for (int j = 0; j < p.B; ++j) {
+            const int lj = len(j);
+            rank += (lj > lt) || (lj == lt && j < t);
+        }
+        if (rank == pos) chosen = t;
+    }
+    __syncthreads();
+    return chosen;
+}
 
 template <int HD, int NRT>
 __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     const uint64_t t_start = trace_start(p.stamps);
-    constexpr int KS = HD / 32;  // k-steps of S = Q K^T
-    constexpr int DT = HD / 16;  // head-dim tiles of O
-    constexpr int PLD = kChunk + 8;  // padded P row (bf16 elements)
-    constexpr int PBYTES = 4 * 2 * NRT * 16 * PLD * 2;  // P tiles, high and low parts, per wavefront
-    constexpr int OBYTES = 4 * NRT * DT * 4 * 64 * 4;   // o of the four wavefronts in register order
-    __shared__ __align__(16) unsigned char lds[PBYTES > OBYTES ? PBYTES : OBYTES];
+    constexpr int KS = HD / 32;  // k-steps of S^T = K Q^T
+    constexpr int DT = HD / 16;  // head-dim tiles of O^T
+    constexpr int OLD = HD + 4;  // padded o row (floats)
+    __shared__ __align__(16) float ob[4][NRT * 16][OLD];  // o of the four wavefronts, row major
     __shared__ float wm[4][NRT * 16], wl[4][NRT * 16], wf[4][NRT * 16];
     __shared__ float rowm[NRT * 16], rowl[NRT * 16];
-    typedef uint16_t PTile[2][NRT][16][PLD];
-    PTile* plds = reinterpret_cast<PTile*>(lds);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int s = blockIdx.x % p.nsplit;
     const int bg = blockIdx.x / p.nsplit;
-    const int g = bg % p.hkv, b = bg / p.hkv;
+    const int g = bg % p.hkv;
+    const int b = lpt_sequence(p, bg / p.hkv);
     const int qpg = p.hq / p.hkv;
     const int R = qpg * p.gamma;
     const int lenb = min(max(p.len[b], 0), p.cap);
@@ -113,28 +241,27 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     const int64_t qkv_ld = p.qkv_ld;
     const uint16_t* qrow0 = static_cast<const uint16_t*>(p.qkv) + (int64_t)b * p.gamma * qkv_ld;
     const int kcol = p.hq * HD + g * HD;
-    const int vcol = p.hq * HD + p.hkv * HD + g * HD;
     const uint16_t* kc = static_cast<const uint16_t*>(p.kcache) + ((int64_t)b * p.hkv + g) * p.cap * HD;
     const uint16_t* vc = static_cast<const uint16_t*>(p.vcache) + ((int64_t)b * p.hkv + g) * HD * (int64_t)p.cap;
     const float sl2 = p.scale * 1.4426950408889634f;  // scores in log2 units
-
     const uint16_t* vblk = p.vblk + ((int64_t)b * p.hkv + g) * HD * kChunk;
 
-    // K rows c0 + nt*16 + col (dims ks*32 + 8*grp ..) and V keys c0 + 8*grp .. +8 of dims
-    // dt*16 + col. Keys past nvalid come from in-bounds rows (cache rows below cap, clamped
-    // block rows): their scores are masked and their values zeroed before use.
-    // The next unit's K goes out as soon as this unit's scores are issued and its V once
-    // the P.V products are, so they land during the softmax and products instead of
-    // after them, with no second register set.
+    // K: A row col of key tile nt is key kq + 4*nt (dims ks*32 + 8*grp ..); V: keys
+    // 8*grp .. +8 of dims dt*16 + col. Keys past nvalid come from in-bounds rows (cache
+    // rows below cap, clamped block rows): their scores are masked and their values zeroed
+    // before use. The next unit's K goes out as soon as this unit's scores are issued and
+    // its V once the value products are, so they land during the softmax and products
+    // instead of after them, with no second register set.
+    const int kq = 8 * (col >> 2) + (col & 3);
     u32x4 kb[2][KS], vb[DT];
     auto load_k = [&](const int u) {
         const uint16_t *k0, *k1;
         if (u != nch) {
-            k0 = kc + (int64_t)(cb + u * kChunk + col) * HD + 8 * grp;
-            k1 = k0 + 16 * HD;
+            k0 = kc + (int64_t)(cb + u * kChunk + kq) * HD + 8 * grp;
+            k1 = k0 + 4 * HD;
         } else {
-            k0 = qrow0 + (int64_t)min(col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
-            k1 = qrow0 + (int64_t)min(16 + col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
+            k0 = qrow0 + (int64_t)min(kq, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
+            k1 = qrow0 + (int64_t)min(kq + 4, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -161,8 +288,8 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         load_v(u_begin);
     }
 
-    // Q tiles as A operands: row = rt*16 + col, dims ks*32 + 8*grp ..; rows past R repeat
-    // row R-1 and are never stored
+    // Q tiles as B operands: query row rt*16 + col, dims ks*32 + 8*grp ..; rows past R
+    // repeat row R-1 and are never stored
     u32x4 qa[NRT][KS];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
@@ -172,14 +299,15 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         for (int ks = 0; ks < KS; ++ks) qa[rt][ks] = *reinterpret_cast<const u32x4*>(src + ks * 32);
     }
 
+    // o[rt][dt]: lane holds dims dt*16 + 4*grp + e of query row rt*16 + col; m, l of that row
     f32x4 o[NRT][DT];
-    float m[NRT][4], l[NRT][4];  // running max (log2 units) and sum per row 4*grp + e
+    float m[NRT], l[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { m[rt][e] = -INFINITY; l[rt][e] = 0.f; }
+        m[rt] = -INFINITY;
+        l[rt] = 0.f;
     }
 
     for (int u = u_begin; u < u_end; ++u) {
@@ -195,80 +323,37 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
             for (int nt = 0; nt < 2; ++nt) {
                 sacc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) sacc[rt][nt] = mfma16(qa[rt][ks], kb[nt][ks], sacc[rt][nt]);
+                for (int ks = 0; ks < KS; ++ks) sacc[rt][nt] = mfma16(kb[nt][ks], qa[rt][ks], sacc[rt][nt]);
             }
         if (u + 1 < u_end) load_k(u + 1);
-        // online softmax; lane holds rows 4*grp+e, keys col and 16+col
-        const bool v0ok = col >= lo && col < nvalid, v1ok = 16 + col >= lo && 16 + col < nvalid;
+        const bool ragged = lo > 0 || nvalid < kChunk;
         const bool rescale = (u != u_begin);  // o is still zero on a wavefront's first unit
+        u32x4 ph[NRT], pl[NRT];
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float s0 = v0ok ? sacc[rt][0][e] * sl2 : -INFINITY;
-                const float s1 = v1ok ? sacc[rt][1][e] * sl2 : -INFINITY;
-                const float mn = fmaxf(m[rt][e], row16_max(fmaxf(s0, s1)));  // finite: a unit holds a valid key
-                const float p0 = __builtin_amdgcn_exp2f(s0 - mn);
-                const float p1 = __builtin_amdgcn_exp2f(s1 - mn);
-                const float al = __builtin_amdgcn_exp2f(m[rt][e] - mn);
-                l[rt][e] = l[rt][e] * al + row16_sum(p0 + p1);
-                m[rt][e] = mn;
-                if (rescale) {
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) o[rt][dt][e] *= al;
-                }
-                // P = hi + lo with both parts bf16: the product keeps ~16 mantissa bits of P
-                const uint32_t hp = pack_bf16x2(p0, p1);
-                const uint32_t lp = pack_bf16x2(p0 - bf16_lo(hp), p1 - bf16_hi(hp));
-                plds[wave][0][rt][4 * grp + e][col] = (uint16_t)hp;
-                plds[wave][0][rt][4 * grp + e][16 + col] = (uint16_t)(hp >> 16);
-                plds[wave][1][rt][4 * grp + e][col] = (uint16_t)lp;
-                plds[wave][1][rt][4 * grp + e][16 + col] = (uint16_t)(lp >> 16);
-            }
-        }
-        // P as A operands (row col, keys 8*grp .. +8); LDS ops of one wavefront are ordered
-        u32x4 pa[NRT], pl[NRT];
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            pa[rt] = *reinterpret_cast<const u32x4*>(&plds[wave][0][rt][col][8 * grp]);
-            pl[rt] = *reinterpret_cast<const u32x4*>(&plds[wave][1][rt][col][8 * grp]);
-        }
-        if (nvalid < kChunk) {
-            // keys past the context are zeroed in V (P is zero there; the cache may hold anything)
-            const int nk = nvalid - 8 * grp;  // valid keys among this lane's 8
-            u32x4 mk;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) mk[q] = (2 * q + 1 < nk) ? 0xFFFFFFFFu : ((2 * q < nk) ? 0x0000FFFFu : 0u);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) vb[dt] &= mk;
-        }
+        for (int rt = 0; rt < NRT; ++rt)
+            softmax_tile<DT>(sacc[rt], ragged, grp, lo, nvalid, sl2, rescale, m[rt], l[rt], o[rt], ph[rt], pl[rt]);
+        if (nvalid < kChunk) mask_v<DT>(vb, nvalid, grp);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) o[rt][dt] = mfma16(pl[rt], vb[dt], mfma16(pa[rt], vb[dt], o[rt][dt]));
+            for (int rt = 0; rt < NRT; ++rt) o[rt][dt] = mfma16(vb[dt], pl[rt], mfma16(vb[dt], ph[rt], o[rt][dt]));
         if (u + 1 < u_end) load_v(u + 1);
     }
 
-    // merge the four wavefronts in LDS: each writes its o; the per-row weights
-    // exp2(m_w - M) and sums L are formed once; then all threads add the four
-    // contributions (wavefront order 0..3) of (row, dim) elements and store them
-    __syncthreads();  // the P tiles are dead; their LDS is reused below
-    if (col == 0) {
+    // merge the four wavefronts in LDS: each writes its o rows; the per-row weights
+    // exp2(m_w - M) and sums L are formed once; then each thread adds the four
+    // contributions (wavefront order 0..3) of four consecutive dims of a row and stores them
+    if (grp == 0) {
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                wm[wave][rt * 16 + 4 * grp + e] = m[rt][e];
-                wl[wave][rt * 16 + 4 * grp + e] = l[rt][e];
-            }
+        for (int rt = 0; rt < NRT; ++rt) {
+            wm[wave][rt * 16 + col] = m[rt];
+            wl[wave][rt * 16 + col] = l[rt];
+        }
     }
-    float* ob = reinterpret_cast<float*>(lds);  // [4][NRT][DT][4][64]
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ob[(((wave * NRT + rt) * DT + dt) * 4 + e) * 64 + lane] = o[rt][dt][e];
+        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(&ob[wave][rt * 16 + col][dt * 16 + 4 * grp]) = o[rt][dt];
     __syncthreads();
     for (int r = threadIdx.x; r < NRT * 16; r += kBlock) {
         const float M = fmaxf(fmaxf(wm[0][r], wm[1][r]), fmaxf(wm[2][r], wm[3][r]));
@@ -283,16 +368,17 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         rowl[r] = L;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < R * HD; idx += kBlock) {
-        const int r = idx / HD, dim = idx - r * HD;
-        const int rt = r >> 4, rr = r & 15, e = rr & 3, ln = (rr >> 2) * 16 + (dim & 15), dt = dim >> 4;
-        float v = 0.f;
+    constexpr int QPR = HD / 4;  // four-dim pieces per row
+    for (int idx = threadIdx.x; idx < R * QPR; idx += kBlock) {
+        const int r = idx / QPR, d4 = (idx - r * QPR) * 4;
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < 4; ++w) v += wf[w][r] * ob[(((w * NRT + rt) * DT + dt) * 4 + e) * 64 + ln];
+        for (int w = 0; w < 4; ++w) v += wf[w][r] * *reinterpret_cast<const f32x4*>(&ob[w][r][d4]);
         const int h = g * qpg + r / p.gamma, i = r % p.gamma;
         float* dst = p.part + ((((int64_t)b * p.hq + h) * p.nparts + s) * p.gamma + i) * (HD + 2);
-        dst[dim] = v;
-        if (dim == 0) {
+        *reinterpret_cast<f32x2*>(dst + d4) = f32x2{v[0], v[1]};
+        *reinterpret_cast<f32x2*>(dst + d4 + 2) = f32x2{v[2], v[3]};
+        if (d4 == 0) {
             dst[HD] = rowm[r] * 0.6931471805599453f;  // natural-log units
             dst[HD + 1] = rowl[r];
         }
