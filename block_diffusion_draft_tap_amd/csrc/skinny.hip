@@ -6,16 +6,20 @@
 //
 // A workgroup of kSW wavefronts owns kSCols consecutive weight rows (output
 // columns) and walks K in chunks of 128. Each wavefront streams its own
-// 16 * kSNB weight rows straight from memory into registers, two chunks ahead
-// of the one it multiplies, already in the B-operand layout of
-// v_mfma_f32_16x16x32_bf16 (lane l: weight row l % 16, k offset 8 (l / 16);
-// one load instruction reads 16 rows x 64 contiguous bytes). The activation
-// chunk (all M rows x 128) is shared by the wavefronts through LDS, double
-// buffered with one barrier per chunk; every workgroup of a launch reads the
-// same activation rows, so they mostly come from L2. Activations are loaded
-// two chunks ahead too, each chunk's before its weights: loads complete in
-// issue order, so the wait for chunk c + 1's activations (before their LDS
-// store) leaves the weights of c + 1 and c + 2 in flight. Lane l holds
+// 16 * kSNB weight rows into registers one chunk ahead of the one it
+// multiplies, reading whole rows: 16 lanes take 256 contiguous bytes of one
+// row (16-row, 64-byte pieces per load, the B-operand layout itself, stream
+// about a fifth slower from HBM). Before the products, each 16-row fragment
+// passes through the wavefront's own LDS tile into the B-operand layout of
+// v_mfma_f32_16x16x32_bf16 (lane l: weight row l % 16, k offset 8 (l / 16)).
+// The activation chunk (all M rows x 128) is shared by the wavefronts through
+// LDS, double buffered with one barrier per chunk; every workgroup of a launch
+// reads the same activation rows, so they mostly come from L2. A chunk's
+// activations are loaded before its weights: loads complete in issue order,
+// so the wait for them (before their LDS store) leaves the weights in flight
+// across the barrier. LDS rows hold 16 pieces of 16 bytes, piece p of row r
+// at slot p ^ (r % 16), so fragment reads (16 rows, one piece each) and row
+// stores both touch every bank once. Lane l holds
 //   A[l % 16][8 (l / 16) + e],  B[8 (l / 16) + e][l % 16]   (e < 8)
 //   D[4 (l / 16) + e][l % 16]                               (e < 4)
 // of each 16 x 16 product, and a wavefront keeps the M x 16 kSNB accumulators
@@ -52,27 +56,21 @@ namespace dfl {
 #ifndef DFL_SK_WGS
 #define DFL_SK_WGS 256
 #endif
-// chunks of activations loaded ahead of the one multiplied (1 or 2; with 2, the wait
-// for chunk c + 1's activations before their LDS store leaves the weights of c + 1 and
-// c + 2 in flight, loads completing in issue order), and the wavefronts per SIMD the
-// kernel is compiled for. Two wavefronts per SIMD (two workgroups per CU, one's LDS and
-// barrier work overlapping the other's weight stream) fit the register budget only with
-// one chunk of activations ahead: with two the kernel spills, and so does the 8-fragment
-// (113 to 128 rows) kernel, which keeps one wavefront per SIMD.
-#ifndef DFL_SK_ADEPTH
-#define DFL_SK_ADEPTH 1
-#endif
+// wavefronts per SIMD the kernel is compiled for: two (two workgroups per CU, one's LDS and
+// barrier work overlapping the other's weight stream); the 8-fragment (113 to 128 rows)
+// kernel keeps one
 #ifndef DFL_SK_OCC
 #define DFL_SK_OCC 2
 #endif
+
 
 namespace {
 
 constexpr int kSW = DFL_SK_WAVES, kSNB = DFL_SK_NB, kST = 64 * kSW;
 constexpr int kSCols = 16 * kSNB * kSW;  // weight rows per workgroup tile
 constexpr int kSKC = kSkinnyK;           // K per chunk
-constexpr int kSLd = kSKC + 16;          // padded LDS row (bf16): 72 words, 8 past a multiple of 32 (conflict-free fragment reads)
 constexpr int kSSteps = kSKC / 32;       // MFMA k-steps per chunk
+static_assert(kSSteps == 4 && kSKC == 128, "a weight row's chunk is 16 lanes x 16 bytes; 16 rows take 4 loads");
 static_assert(kSNB % 2 == 0, "the gated epilogue pairs gate and up fragments");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -125,188 +123,15 @@ __device__ __forceinline__ void store_one(const SkinnyParams& p, int m, int n, f
     }
 }
 
+// ---- epilogue: lane holds rows i*16 + 4*grp + e, columns of fragment f at col. red_v /
+// red_i: [kSW][RED] LDS scratch of the argmax; meta_b / meta_pos: the K/V cache slots of
+// the rows (set before the main loop's barriers)
 template <int MT, int EPI>
-__global__ __launch_bounds__(kST, MT >= 8 ? 1 : DFL_SK_OCC) void skinny_kernel(const SkinnyParams p) {
+__device__ __forceinline__ void skinny_epilogue(const SkinnyParams& p, f32x4 (&acc)[MT][kSNB], const int tile,
+                                                const int split, const int z, const int wave, const int col,
+                                                const int grp, float* red_v, int* red_i, const int* meta_b,
+                                                const int* meta_pos) {
     constexpr int RED = EPI == SK_ARGMAX ? MT * 16 : 1;
-    constexpr int META = EPI == SK_KV ? MT * 16 : 1;
-    __shared__ __align__(16) uint16_t As[2][MT * 16][kSLd];
-    __shared__ float red_v[kSW][RED];
-    __shared__ int red_i[kSW][RED];
-    __shared__ int meta_b[META], meta_pos[META];
-    const uint64_t t_start = trace_start(p.stamps);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 15, grp = lane >> 4;
-    const int tile = blockIdx.x, split = blockIdx.y, z = blockIdx.z;
-    const int kbeg = split * p.kslice;
-    const int nc = (min(p.K, kbeg + p.kslice) - kbeg) / kSKC;
-    // this layer's weights and activations (pointer choices made with compares, so the
-    // pointer arrays stay in kernel-argument registers)
-    const uint16_t* W = p.w[0];
-#pragma unroll
-    for (int q = 1; q < kMaxLayers; ++q)
-        if (z == q) W = p.w[q];
-    const uint16_t* A = p.a + (int64_t)z * p.a_layer_stride;
-
-    if constexpr (EPI == SK_KV) {
-        // cache slot of every row (read after the main loop's barriers)
-        for (int m = threadIdx.x; m < MT * 16; m += kST) {
-            int b = 0, pos = -1;
-            if (m < p.M) kv_slot(p, p.row_base + m, b, pos);
-            meta_b[m] = b;
-            meta_pos[m] = pos;
-        }
-    }
-
-    // weight rows of this wavefront: fragment f, lane row col (rows past the end
-    // read the last row; their outputs are never stored)
-    const uint16_t* wp[kSNB];
-#pragma unroll
-    for (int f = 0; f < kSNB; ++f) {
-        int row;
-        if constexpr (EPI == SK_GATED) {
-            const int j = tile * (kSCols / 2) + wave * 8 * kSNB + (f / 2) * 16 + col;
-            row = (f & 1) * p.F + min(j, p.F - 1);
-        } else {
-            row = min(tile * kSCols + wave * 16 * kSNB + f * 16 + col, p.N - 1);
-        }
-        wp[f] = W + (p.w_row0 + row) * (int64_t)p.K + kbeg + 8 * grp;
-    }
-
-    f32x4 acc[MT][kSNB];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int f = 0; f < kSNB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // three register sets of weights: chunk c lives in set c % 3. Loads past the last
-    // chunk re-read it (never multiplied): unconditional loads let the compiler count the
-    // loads in flight, so waiting for an older load never drains the younger ones
-    u32x4 w0[kSNB][kSSteps], w1[kSNB][kSSteps], w2[kSNB][kSSteps];
-    auto load_w = [&](u32x4 (&wr)[kSNB][kSSteps], int c) {
-        const int cc = min(c, nc - 1);
-#pragma unroll
-        for (int s = 0; s < kSSteps; ++s)
-#pragma unroll
-            for (int f = 0; f < kSNB; ++f)
-                wr[f][s] = *reinterpret_cast<const u32x4*>(wp[f] + cc * kSKC + s * 32);
-    };
-    // the activation chunk: MT*16 rows x 16 pieces of 16 bytes, spread over the threads
-    constexpr int PIECES = MT * 16 * (kSKC / 8);
-    constexpr int APT = (PIECES + kST - 1) / kST;
-    u32x4 ast[APT], ast2[APT];
-    // (past the last chunk it reloads the last one, which is never stored: unconditional
-    // loads keep the staging registers out of scratch memory)
-    auto load_a_into = [&](u32x4 (&dst)[APT], int c) {
-        const int k0 = kbeg + min(c, nc - 1) * kSKC;
-        const uint16_t* src;
-        if (p.seg_k > 0) {  // tap segments: a chunk never straddles two
-            const int j = k0 / p.seg_k;
-            src = p.a_seg[0];
-#pragma unroll
-            for (int q = 1; q < kMaxTaps; ++q)
-                if (j == q) src = p.a_seg[q];
-            src += k0 - j * p.seg_k;
-        } else {
-            src = A + k0;
-        }
-#pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int q = min((int)threadIdx.x + kST * i, PIECES - 1);
-            const int row = min(q >> 4, p.M - 1);  // rows past M: any valid row, never stored
-            dst[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)row * p.a_ld + 8 * (q & 15));
-        }
-    };
-    auto store_a_from = [&](const u32x4 (&srcr)[APT], int buf) {
-#pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int q = threadIdx.x + kST * i;
-            if (PIECES % kST == 0 || q < PIECES) *reinterpret_cast<u32x4*>(&As[buf][q >> 4][8 * (q & 15)]) = srcr[i];
-        }
-    };
-    auto load_a = [&](int c) { load_a_into(ast, c); };
-    auto store_a = [&](int buf) { store_a_from(ast, buf); };
-    auto mma = [&](int buf, const u32x4 (&wr)[kSNB][kSSteps]) {
-#pragma unroll
-        for (int s = 0; s < kSSteps; ++s) {
-#pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                const u32x4 af = *reinterpret_cast<const u32x4*>(&As[buf][i * 16 + col][s * 32 + 8 * grp]);
-#pragma unroll
-                for (int f = 0; f < kSNB; ++f) acc[i][f] = mfma_bf16(af, wr[f][s], acc[i][f]);
-            }
-        }
-    };
-
-    // chunk c multiplies LDS buffer c % 2; the activations of c + 1 are loaded before the
-    // weights of c + 2, so the wait for them before their LDS store leaves the weights in
-    // flight. Whole triples of chunks run without branches (a store into the idle buffer
-    // past the last chunk is never read); the last one or two chunks follow.
-#if DFL_SK_ADEPTH == 2
-    // activations two chunks ahead as well: A(k) sits in staging set k % 2 from its load
-    // (during chunk k - 2) until its LDS store (end of chunk k - 1); six chunks per trip
-    auto stage = [&](int cc, u32x4 (&wc)[kSNB][kSSteps], u32x4 (&wn)[kSNB][kSSteps], u32x4 (&al)[APT],
-                     const u32x4 (&as)[APT]) {
-        load_a_into(al, cc + 2);
-        load_w(wn, cc + 2);
-        mma(cc & 1, wc);
-        store_a_from(as, (cc + 1) & 1);
-        __syncthreads();
-    };
-    load_w(w0, 0);
-    load_w(w1, 1);
-    load_a_into(ast, 0);
-    load_a_into(ast2, 1);
-    store_a_from(ast, 0);
-    __syncthreads();
-    int c = 0;
-    for (; c + 6 <= nc; c += 6) {
-        stage(c, w0, w2, ast, ast2);
-        stage(c + 1, w1, w0, ast2, ast);
-        stage(c + 2, w2, w1, ast, ast2);
-        stage(c + 3, w0, w2, ast2, ast);
-        stage(c + 4, w1, w0, ast, ast2);
-        stage(c + 5, w2, w1, ast2, ast);
-    }
-    if (c < nc) stage(c, w0, w2, ast, ast2);
-    if (c + 1 < nc) stage(c + 1, w1, w0, ast2, ast);
-    if (c + 2 < nc) stage(c + 2, w2, w1, ast, ast2);
-    if (c + 3 < nc) stage(c + 3, w0, w2, ast2, ast);
-    if (c + 4 < nc) stage(c + 4, w1, w0, ast, ast2);
-#else
-    load_w(w0, 0);
-    load_w(w1, 1);
-    load_a(0);
-    store_a(0);
-    __syncthreads();
-    int c = 0;
-    for (; c + 3 <= nc; c += 3) {
-        load_a(c + 1);
-        load_w(w2, c + 2);
-        mma(c & 1, w0);
-        store_a((c + 1) & 1);
-        __syncthreads();
-        load_a(c + 2);
-        load_w(w0, c + 3);
-        mma((c + 1) & 1, w1);
-        store_a(c & 1);
-        __syncthreads();
-        load_a(c + 3);
-        load_w(w1, c + 4);
-        mma(c & 1, w2);
-        store_a((c + 1) & 1);
-        __syncthreads();
-    }
-    if (c < nc) {
-        load_a(c + 1);
-        mma(c & 1, w0);
-        store_a((c + 1) & 1);
-        __syncthreads();
-        if (c + 1 < nc) mma((c + 1) & 1, w1);
-    }
-#endif
-
-
-    // ---- epilogue: lane holds rows i*16 + 4*grp + e, columns of fragment f at col
     if constexpr (EPI == SK_GATED) {
 #pragma unroll
         for (int i = 0; i < MT; ++i)
@@ -347,17 +172,17 @@ __global__ __launch_bounds__(kST, MT >= 8 ? 1 : DFL_SK_OCC) void skinny_kernel(c
                     argmax_pick(v, idx, v2, i2);
                 }
                 if (col == 0) {
-                    red_v[wave][i * 16 + 4 * grp + e] = v;
-                    red_i[wave][i * 16 + 4 * grp + e] = idx;
+                    red_v[wave * RED + i * 16 + 4 * grp + e] = v;
+                    red_i[wave * RED + i * 16 + 4 * grp + e] = idx;
                 }
             }
         __syncthreads();
         const int m = threadIdx.x;
         if (m < p.M) {
-            float v = red_v[0][m];
-            int idx = red_i[0][m];
+            float v = red_v[m];
+            int idx = red_i[m];
 #pragma unroll
-            for (int w = 1; w < kSW; ++w) argmax_pick(v, idx, red_v[w][m], red_i[w][m]);
+            for (int w = 1; w < kSW; ++w) argmax_pick(v, idx, red_v[w * RED + m], red_i[w * RED + m]);
             p.part_val[(int64_t)m * p.nblocks + tile] = v;
             p.part_idx[(int64_t)m * p.nblocks + tile] = idx;
         }
@@ -388,6 +213,319 @@ __global__ __launch_bounds__(kST, MT >= 8 ? 1 : DFL_SK_OCC) void skinny_kernel(c
                 }
             }
     }
+}
+
+template <int MT, int EPI>
+__global__ __launch_bounds__(kST, MT >= 8 ? 1 : DFL_SK_OCC) void skinny_kernel(const SkinnyParams p) {
+    constexpr int RED = EPI == SK_ARGMAX ? MT * 16 : 1;
+    constexpr int META = EPI == SK_KV ? MT * 16 : 1;
+    // LDS tiles, rows of 16 pieces of 16 bytes with piece p of row r at slot p ^ (r % 16): the
+    // 16 lanes of a fragment read (rows col, one piece each) and of a row write (one row,
+    // all pieces) both touch every bank once
+    __shared__ __align__(16) uint16_t As[2][MT * 16][kSKC];  // activation chunk, double buffered
+    __shared__ __align__(16) uint16_t Ws[kSW][16][kSKC];     // a wavefront's weight fragment in transit
+    __shared__ float red_v[kSW][RED];
+    __shared__ int red_i[kSW][RED];
+    __shared__ int meta_b[META], meta_pos[META];
+    const uint64_t t_start = trace_start(p.stamps);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int tile = blockIdx.x, split = blockIdx.y, z = blockIdx.z;
+    const int kbeg = split * p.kslice;
+    const int nc = (min(p.K, kbeg + p.kslice) - kbeg) / kSKC;
+    // this layer's weights and activations (pointer choices made with compares, so the
+    // pointer arrays stay in kernel-argument registers)
+    const uint16_t* W = p.w[0];
+#pragma unroll
+    for (int q = 1; q < kMaxLayers; ++q)
+        if (z == q) W = p.w[q];
+    const uint16_t* A = p.a + (int64_t)z * p.a_layer_stride;
+
+    if constexpr (EPI == SK_KV) {
+        // cache slot of every row (read after the main loop's barriers)
+        for (int m = threadIdx.x; m < MT * 16; m += kST) {
+            int b = 0, pos = -1;
+            if (m < p.M) kv_slot(p, p.row_base + m, b, pos);
+            meta_b[m] = b;
+            meta_pos[m] = pos;
+        }
+    }
+
+    // weight rows of this wavefront: fragment f, row r of the fragment (rows past the end
+    // read the last row; their outputs are never stored). Loads read whole rows: load s of
+    // a fragment gives lane (col, grp) 16 bytes at k offset 8 col of row r = 4 s + grp (16
+    // lanes read 256 contiguous bytes of a row), and the fragment then goes through the
+    // wavefront's LDS tile into the B-operand layout (lane: row col, k offset 8 grp + 32 s)
+    int jrow[kSNB];
+#pragma unroll
+    for (int f = 0; f < kSNB; ++f)
+        jrow[f] = EPI == SK_GATED ? tile * (kSCols / 2) + wave * 8 * kSNB + (f / 2) * 16 + grp
+                                  : tile * kSCols + wave * 16 * kSNB + f * 16 + grp;
+    const uint16_t* wbase = W + p.w_row0 * (int64_t)p.K + kbeg + 8 * col;
+    auto wrow = [&](int f, int s) {
+        if constexpr (EPI == SK_GATED) return (f & 1) * p.F + min(jrow[f] + 4 * s, p.F - 1);
+        return min(jrow[f] + 4 * s, p.N - 1);
+    };
+
+    f32x4 acc[MT][kSNB];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int f = 0; f < kSNB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // two register sets of weights: chunk c lives in set c % 2 from its load (during chunk
+    // c - 1) until its stores into the wavefront's LDS tile. Loads past the last chunk re-read
+    // it (never multiplied): unconditional loads let the compiler count the loads in flight,
+    // so waiting for an older load never drains the younger ones
+    u32x4 w0[kSNB][kSSteps], w1[kSNB][kSSteps];
+    auto load_w = [&](u32x4 (&wr)[kSNB][kSSteps], int c) {
+        const int cc = min(c, nc - 1);
+#pragma unroll
+        for (int f = 0; f < kSNB; ++f)
+#pragma unroll
+            for (int s = 0; s < kSSteps; ++s)
+                wr[f][s] = *reinterpret_cast<const u32x4*>(wbase + (int64_t)wrow(f, s) * p.K + cc * kSKC);
+    };
+    // the activation chunk: MT*16 rows x 16 pieces of 16 bytes, spread over the threads
+    constexpr int PIECES = MT * 16 * (kSKC / 8);
+    constexpr int APT = (PIECES + kST - 1) / kST;
+    u32x4 ast[APT];
+    // (past the last chunk it reloads the last one, which is never stored: unconditional
+    // loads keep the staging registers out of scratch memory)
+    auto load_a_into = [&](u32x4 (&dst)[APT], int c) {
+        const int k0 = kbeg + min(c, nc - 1) * kSKC;
+        const uint16_t* src;
+        if (p.seg_k > 0) {  // tap segments: a chunk never straddles two
+            const int j = k0 / p.seg_k;
+            src = p.a_seg[0];
+#pragma unroll
+            for (int q = 1; q < kMaxTaps; ++q)
+                if (j == q) src = p.a_seg[q];
+            src += k0 - j * p.seg_k;
+        } else {
+            src = A + k0;
+        }
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int q = min((int)threadIdx.x + kST * i, PIECES - 1);
+            const int row = min(q >> 4, p.M - 1);  // rows past M: any valid row, never stored
+            dst[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)row * p.a_ld + 8 * (q & 15));
+        }
+    };
+    auto store_a_from = [&](const u32x4 (&srcr)[APT], int buf) {
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int q = threadIdx.x + kST * i;
+            if (PIECES % kST == 0 || q < PIECES)
+                *reinterpret_cast<u32x4*>(&As[buf][q >> 4][8 * ((q ^ (q >> 4)) & 15)]) = srcr[i];
+        }
+    };
+    auto load_a = [&](int c) { load_a_into(ast, c); };
+    auto store_a = [&](int buf) { store_a_from(ast, buf); };
+    auto mma = [&](int buf, const u32x4 (&wr)[kSNB][kSSteps]) {
+        // the fragments into B operands, one at a time through the wavefront's LDS tile (the
+        // wavefront's LDS accesses complete in order, so the second fragment's stores follow
+        // the first one's loads)
+        u32x4 wb[kSNB][kSSteps];
+#pragma unroll
+        for (int f = 0; f < kSNB; ++f) {
+#pragma unroll
+            for (int s = 0; s < kSSteps; ++s) {
+                const int r = 4 * s + grp;
+                *reinterpret_cast<u32x4*>(&Ws[wave][r][8 * (col ^ r)]) = wr[f][s];
+            }
+#pragma unroll
+            for (int s = 0; s < kSSteps; ++s)
+                wb[f][s] = *reinterpret_cast<const u32x4*>(&Ws[wave][col][8 * ((4 * s + grp) ^ col)]);
+        }
+#pragma unroll
+        for (int s = 0; s < kSSteps; ++s) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const u32x4 af = *reinterpret_cast<const u32x4*>(&As[buf][i * 16 + col][8 * ((4 * s + grp) ^ col)]);
+#pragma unroll
+                for (int f = 0; f < kSNB; ++f) acc[i][f] = mfma_bf16(af, wb[f][s], acc[i][f]);
+            }
+        }
+    };
+
+    // chunk c multiplies LDS buffer c % 2. Chunk c + 1's activations are loaded before its
+    // weights, so the wait for them before their LDS store (after chunk c's products) leaves
+    // the weights in flight across the barrier. Whole pairs of chunks run without branches (a
+    // store into the idle buffer past the last chunk is never read); an odd last one follows.
+    load_w(w0, 0);
+    load_a(0);
+    store_a(0);
+    __syncthreads();
+    int c = 0;
+    for (; c + 2 <= nc; c += 2) {
+        load_a(c + 1);
+        load_w(w1, c + 1);
+        mma(0, w0);
+        store_a(1);
+        __syncthreads();
+        load_a(c + 2);
+        load_w(w0, c + 2);
+        mma(1, w1);
+        store_a(0);
+        __syncthreads();
+    }
+    if (c < nc) mma(0, w0);
+
+    skinny_epilogue<MT, EPI>(p, acc, tile, split, z, wave, col, grp, &red_v[0][0], &red_i[0][0], meta_b, meta_pos);
+    trace_end(p.stamps, t_start);
+}
+
+// Direct-to-LDS variant, for many activation rows: there the products and LDS reads per
+// weight byte are several times those of a few rows, a workgroup's activation tiles take
+// most of a CU's LDS, and weights kept in flight in registers are what the register budget
+// leaves over. Here weights and activations go from memory straight into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the instruction's LDS base + 16 l),
+// with no staging registers, and each wavefront keeps its weight rows kDmaStages chunks deep
+// in its own LDS stages (two chunks ahead of the one it multiplies). The loads choose their
+// sources so that the LDS tiles come out in the slot layout above (piece p of row r at slot
+// p ^ (r % 16)); a row's 16 lanes still read its 256 contiguous bytes.
+//
+// Chunk c's activations are loaded after the barrier that ends chunk c - 1's reads of their
+// buffer, and before chunk c + 1's weights; the wait at the top of chunk c (this wavefront's
+// chunk c weights and activations landed: only chunk c + 1's weights may still be in
+// flight) then a barrier (every wavefront's activation pieces landed) open the products.
+template <int MT>
+constexpr int dma_stages() {
+    return 2 * MT * 16 * kSKC * 2 + kSW * 3 * kSNB * 16 * kSKC * 2 + 4096 <= 163840 ? 3 : 2;
+}
+
+// 16 bytes a lane from src into LDS at lds_base + 16 * lane (lds_base the same in every lane).
+// Written out as the instruction itself: the compiler, seeing the intrinsic's LDS store,
+// would wait for every load in flight before each LDS read and barrier, which is the
+// pipeline this kernel exists for; the waits are explicit here. M0 is taken at issue.
+// (M0 is reserved to the compiler, which warns on the clobber; it keeps no value there in
+// these kernels: M0 appears only in these instructions)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const uint16_t* src, const uint16_t* lds_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// chunk c may start: this wavefront's loads other than the last `keep` (0 or 8) landed, its
+// LDS reads done, then the workgroup barrier (the compiler sees a memory barrier)
+__device__ __forceinline__ void dma_sync(const bool keep8) {
+    if (keep8)
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int MT, int EPI>
+__global__ __launch_bounds__(kST, 1) void skinny_dma_kernel(const SkinnyParams p) {
+    constexpr int RED = EPI == SK_ARGMAX ? MT * 16 : 1;
+    constexpr int META = EPI == SK_KV ? MT * 16 : 1;
+    constexpr int D = dma_stages<MT>();
+    __shared__ __align__(16) uint16_t As[2][MT * 16][kSKC];         // activation chunk, double buffered
+    __shared__ __align__(16) uint16_t Wst[kSW][D][kSNB][16][kSKC];  // each wavefront's weight stages
+    __shared__ float red_v[kSW][RED];
+    __shared__ int red_i[kSW][RED];
+    __shared__ int meta_b[META], meta_pos[META];
+    const uint64_t t_start = trace_start(p.stamps);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int tile = blockIdx.x, split = blockIdx.y, z = blockIdx.z;
+    const int kbeg = split * p.kslice;
+    const int nc = (min(p.K, kbeg + p.kslice) - kbeg) / kSKC;
+    const uint16_t* W = p.w[0];
+#pragma unroll
+    for (int q = 1; q < kMaxLayers; ++q)
+        if (z == q) W = p.w[q];
+    const uint16_t* A = p.a + (int64_t)z * p.a_layer_stride;
+
+    if constexpr (EPI == SK_KV) {
+        for (int m = threadIdx.x; m < MT * 16; m += kST) {
+            int b = 0, pos = -1;
+            if (m < p.M) kv_slot(p, p.row_base + m, b, pos);
+            meta_b[m] = b;
+            meta_pos[m] = pos;
+        }
+    }
+
+    // weight rows: load s of fragment f gives lane (col, grp) row r = 4 s + grp of the
+    // fragment, piece col ^ r (LDS slot col of that row)
+    int jrow[kSNB];
+#pragma unroll
+    for (int f = 0; f < kSNB; ++f)
+        jrow[f] = EPI == SK_GATED ? tile * (kSCols / 2) + wave * 8 * kSNB + (f / 2) * 16 + grp
+                                  : tile * kSCols + wave * 16 * kSNB + f * 16 + grp;
+    const uint16_t* wbase = W + p.w_row0 * (int64_t)p.K + kbeg;
+    auto wrow = [&](int f, int s) {
+        if constexpr (EPI == SK_GATED) return (f & 1) * p.F + min(jrow[f] + 4 * s, p.F - 1);
+        return min(jrow[f] + 4 * s, p.N - 1);
+    };
+    auto load_w = [&](int c) {
+        const int st = c % D;
+#pragma unroll
+        for (int f = 0; f < kSNB; ++f)
+#pragma unroll
+            for (int s = 0; s < kSSteps; ++s) {
+                const int r = 4 * s + grp;
+                lds_dma16(wbase + (int64_t)wrow(f, s) * p.K + c * kSKC + 8 * (col ^ r), &Wst[wave][st][f][4 * s][0]);
+            }
+    };
+    // activations: LDS piece q = kST i + threadIdx.x of the tile is row q / 16, slot q % 16
+    auto load_a = [&](int c) {
+        const int k0 = kbeg + c * kSKC;
+        const uint16_t* src;
+        if (p.seg_k > 0) {  // tap segments: a chunk never straddles two
+            const int j = k0 / p.seg_k;
+            src = p.a_seg[0];
+#pragma unroll
+            for (int q = 1; q < kMaxTaps; ++q)
+                if (j == q) src = p.a_seg[q];
+            src += k0 - j * p.seg_k;
+        } else {
+            src = A + k0;
+        }
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const int q = kST * i + (int)threadIdx.x;
+            const int row = q >> 4;
+            const int piece = (q & 15) ^ (row & 15);
+            lds_dma16(src + (int64_t)min(row, p.M - 1) * p.a_ld + 8 * piece, &As[c & 1][0][0] + (kST * i + 64 * wave) * 8);
+        }
+    };
+
+    f32x4 acc[MT][kSNB];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int f = 0; f < kSNB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    load_a(0);
+    load_w(0);
+    if (D == 3 && nc > 1) load_w(1);
+    for (int c = 0; c < nc; ++c) {
+        // this wavefront's loads after chunk c's activations: chunk c + 1's weights (D = 3)
+        dma_sync(D == 3 && c + 1 < nc);
+        if (c + 1 < nc) load_a(c + 1);          // into the buffer chunk c - 1 read
+        if (c + D - 1 < nc) load_w(c + D - 1);  // into the stage chunk c - 1 used
+        const int st = c % D, buf = c & 1;
+#pragma unroll
+        for (int s = 0; s < kSSteps; ++s) {
+            u32x4 wb[kSNB];
+#pragma unroll
+            for (int f = 0; f < kSNB; ++f)
+                wb[f] = *reinterpret_cast<const u32x4*>(&Wst[wave][st][f][col][8 * ((4 * s + grp) ^ col)]);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const u32x4 af = *reinterpret_cast<const u32x4*>(&As[buf][i * 16 + col][8 * ((4 * s + grp) ^ col)]);
+#pragma unroll
+                for (int f = 0; f < kSNB; ++f) acc[i][f] = mfma_bf16(af, wb[f], acc[i][f]);
+            }
+        }
+    }
+
+    skinny_epilogue<MT, EPI>(p, acc, tile, split, z, wave, col, grp, &red_v[0][0], &red_i[0][0], meta_b, meta_pos);
     trace_end(p.stamps, t_start);
 }
 
@@ -559,14 +697,45 @@ __global__ __launch_bounds__(kRnThreads) void resid_norm_kernel(const float* par
 
 // instrumentation: the stamp slice of one matrix-core launch (algorithmic bytes =
 // weights + activation rows + outputs, per layer)
+// The direct-to-LDS kernel serves launches of at least DFL_SK_DMA_MIN_MT row tiles whose
+// workgroups number at most DFL_SK_DMA_MAX_WGS (about one per CU of the 256-CU part, where
+// its deeper weight stream pays); with more workgroups, two register-path workgroups per CU
+// keep more in flight than its one (measured: the 1187-tile LM head, 444 us direct against
+// 377 us, and the 544-workgroup gate/up product are faster on the register path; the
+// 224-240 workgroup Q/K/V, O, down and K/V launches 14-16% faster direct).
+#ifndef DFL_SK_DMA_MIN_MT
+#define DFL_SK_DMA_MIN_MT 5
+#endif
+#ifndef DFL_SK_DMA_MAX_WGS
+#define DFL_SK_DMA_MAX_WGS 384
+#endif
+
+template <int MT>
+bool use_dma(const SkinnyParams& p, int tiles) {
+    return MT >= DFL_SK_DMA_MIN_MT && (int64_t)tiles * p.nsplit * p.layers <= DFL_SK_DMA_MAX_WGS;
+}
+
 template <int MT, int EPI>
 uint64_t* skinny_trace(const SkinnyParams& p, int tiles) {
     const double nout = EPI == SK_GATED ? p.N / 2 : (EPI == SK_ARGMAX ? 0 : p.N);
     const double bytes = p.layers * ((double)p.N * p.K * 2.0 + (double)p.M * p.K * 2.0 + (double)p.M * nout * 4.0);
     char name[48];
-    snprintf(name, sizeof name, "skinny_kernel<%d, %d>", MT, EPI);
+    snprintf(name, sizeof name, use_dma<MT>(p, tiles) ? "skinny_dma_kernel<%d, %d>" : "skinny_kernel<%d, %d>", MT,
+             EPI);
     return trace_launch(EPI == SK_ARGMAX ? TRACE_LM_HEAD : TRACE_PROJECTIONS, name,
                         (int64_t)tiles * p.nsplit * p.layers, bytes, 0.0);
+}
+
+template <int MT, int EPI>
+void launch_kernel(const SkinnyParams& q, const int tiles, hipStream_t s) {
+    const dim3 grid(tiles, q.nsplit, q.layers);
+    if constexpr (MT >= DFL_SK_DMA_MIN_MT) {
+        if (use_dma<MT>(q, tiles)) {
+            hipLaunchKernelGGL((skinny_dma_kernel<MT, EPI>), grid, dim3(kST), 0, s, q);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((skinny_kernel<MT, EPI>), grid, dim3(kST), 0, s, q);
 }
 
 template <int MT, int EPI>
@@ -577,7 +746,7 @@ hipError_t launch_mt(const SkinnyParams& p, hipStream_t s) {
         if (p.nsplit > 1) {
             SkinnyParams q = p;
             q.stamps = skinny_trace<MT, SK_PARTIAL>(p, tiles);
-            hipLaunchKernelGGL((skinny_kernel<MT, SK_PARTIAL>), dim3(tiles, p.nsplit, p.layers), dim3(kST), 0, s, q);
+            launch_kernel<MT, SK_PARTIAL>(q, tiles, s);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             const int64_t blocks = ((int64_t)p.M * p.N / 4 + kBlock - 1) / kBlock;
@@ -587,7 +756,7 @@ hipError_t launch_mt(const SkinnyParams& p, hipStream_t s) {
     }
     SkinnyParams q = p;
     q.stamps = skinny_trace<MT, EPI>(p, tiles);
-    hipLaunchKernelGGL((skinny_kernel<MT, EPI>), dim3(tiles, p.nsplit, p.layers), dim3(kST), 0, s, q);
+    launch_kernel<MT, EPI>(q, tiles, s);
     return hipGetLastError();
 }
 
