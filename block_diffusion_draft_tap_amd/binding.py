@@ -297,15 +297,17 @@ class DeviceModel:
 
 
 class KVCache:
-    """Retained context K/V: k [nl, B, hkv, cap, hd], v [nl, B, hkv, hd, cap]
-    (head-dim major); len int32 [B]. cap is rounded up to a multiple of 32."""
+    """Retained context K/V: k [nl, B, hkv, cap, hd]; v [nl, B, hkv, cap/32, hd, 32]
+    for bf16 models (32-key chunks, head-dim major inside a chunk), [nl, B, hkv, hd,
+    cap] for f32 models; len int32 [B]. cap is rounded up to a multiple of 32."""
 
     def __init__(self, dims, B, cap, device="cuda"):
         dt = torch.float32 if dims.wdtype == "f32" else torch.bfloat16
         cap = (cap + 31) // 32 * 32
         nl = max(1, dims.nl)
         self.k = torch.zeros((nl, B, dims.hkv, cap, dims.hd), dtype=dt, device=device)
-        self.v = torch.zeros((nl, B, dims.hkv, dims.hd, cap), dtype=dt, device=device)
+        vshape = (nl, B, dims.hkv, dims.hd, cap) if dt == torch.float32 else (nl, B, dims.hkv, cap // 32, dims.hd, 32)
+        self.v = torch.zeros(vshape, dtype=dt, device=device)
         self.len = torch.zeros(B, dtype=torch.int32, device=device)
         self.B, self.cap = B, cap
         self.c = dflash_kv(k=_ptr(self.k), v=_ptr(self.v), len=_ptr(self.len), B=B, cap=cap,

@@ -17,8 +17,10 @@
 //                sum take two row swaps; the reference max moves lazily;
 //   O^T += V^T P^T  P stays in the row's lanes as the B operand, split into
 //                bf16 high and low parts (two products) so the probabilities
-//                keep ~16 mantissa bits; V is cached head-dim major, so the A
-//                operand (8 consecutive keys of one dim) is one 16-byte load.
+//                keep ~16 mantissa bits; V is cached in 32-key chunks of all
+//                head dims ([cap/32][hd][32]), so the A operand (8 consecutive
+//                keys of one dim) is one 16-byte load and a unit's values are
+//                one contiguous 8 KB run (1 KB per load instruction).
 // attn_rows_kernel (33..48 query rows, few units) gives each 16-row tile its own
 // wavefront and forms S = Q K^T, passing P through LDS.
 // Lane layout of the 16x16x32 product (lane l): A[l%16][8(l/16)+e],
@@ -86,7 +88,7 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
 // loads key 8*(c/4) + 4*nt + c%4 into A row c, so lane (col, grp) of the score tiles
 // holds keys 8*grp .. 8*grp + 7 of query row col -- the keys that lane's B operand
 // carries in the value product, whose A operand (V^T, 8 consecutive keys of one
-// head dim per lane) is one 16-byte load of the head-dim-major V cache.
+// head dim per lane) is one 16-byte load of the chunked V cache.
 
 // max and sum over the four lanes col, col + 16, col + 32, col + 48: gfx950's row
 // swaps exchange rows 0/1 and 2/3, then the two halves; every lane ends with the
@@ -195,7 +197,7 @@ __device__ __forceinline__ int lpt_sequence(const AttnParams& p, const int pos) 
         const int L = min(max(p.len[j], 0), p.cap);
         return p.window > 0 ? min(L, p.window) : L;
     };
-    for (int t = threadIdx.x; t < p.B; t += kBlock) {
+    for (int t = threadIdx.x; t < p.B; t += blockDim.x) {
         const int lt = len(t);
         int rank = 0;
         for (int j = 0; j < p.B; ++j) {
@@ -273,8 +275,8 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         const uint16_t* vp;
         int64_t vstride;
         if (u != nch) {
-            vp = vc + (int64_t)col * p.cap + cb + u * kChunk + 8 * grp;
-            vstride = 16 * (int64_t)p.cap;
+            vp = vc + ((int64_t)(cb / kChunk + u) * HD + col) * kChunk + 8 * grp;
+            vstride = 16 * kChunk;
         } else {
             vp = vblk + col * kChunk + 8 * grp;
             vstride = 16 * kChunk;
@@ -387,6 +389,185 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Shared-stage MFMA kernel (bf16 caches, head dim 128, 17..48 query rows per kv head,
+// launches bound by the K/V stream). One wavefront per 16-row query tile, as in the
+// row-split kernel below, but the workgroup's wavefronts share each 32-key unit through
+// LDS: the unit's K rows and V columns go from memory straight into one of kAttnStages
+// LDS stages (global_load_lds_dwordx4, lane l's 16 bytes at the instruction's LDS base +
+// 16 l; the wavefronts split the 16 loads of a unit), kAttnStages - 1 units ahead of the
+// one being multiplied, so each byte is fetched once and no registers hold loads in
+// flight. Scores are transposed as in attn_mfma_kernel (P stays in registers); K and V
+// operands are read from the stage. Stage tiles are swizzled in 16-byte pieces: K row r
+// (a key) holds its piece p at slot p ^ f(r), f(r) = (r & 3) | ((r >> 1) & 12), V row d (a
+// head dim, 4 pieces of 8 keys) holds piece q at slot q ^ ((d >> 2) & 3), so the 16 lanes
+// of an operand read touch every bank once; each lane of a load picks the source piece its
+// slot holds (a row's lanes still read its contiguous bytes).
+#ifndef DFL_ATTN_STAGES
+#define DFL_ATTN_STAGES 4
+#endif
+constexpr int kAttnStages = DFL_ATTN_STAGES;
+static_assert(kAttnStages >= 2 && kAttnStages <= 5, "stage count");
+constexpr int kStageK = kChunk * 128;  // bf16 elements of a unit's K tile (head dim 128)
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes a lane from src into LDS at lds_base + 16 * lane (lds_base uniform). Written as
+// the instruction itself: through the intrinsic the compiler waits for every load in flight
+// before each later LDS read and barrier; the waits here are explicit. M0 is read at issue
+// and appears only in these instructions.
+__device__ __forceinline__ void attn_dma16(const uint16_t* src, const uint16_t* lds_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int NRT>
+__global__ __launch_bounds__(64 * NRT) void attn_lds_kernel(const AttnParams p) {
+    constexpr int HD = 128, KS = HD / 32, DT = HD / 16;
+    constexpr int D = kAttnStages;
+    constexpr int NLOAD = 2 * HD / 16;                 // 1 KB loads per unit (K, then V)
+    constexpr int PER = (NLOAD + NRT - 1) / NRT;      // loads per wavefront per unit (at most)
+    constexpr int LOW = NLOAD / NRT;                  // (at least)
+    __shared__ __align__(16) uint16_t stage[D][2][kStageK];  // [stage][K rows | V rows]
+    const uint64_t t_start = trace_start(p.stamps);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;  // wave = this wavefront's row tile
+    const int col = lane & 15, grp = lane >> 4;
+    const int s = blockIdx.x % p.nsplit;
+    const int bg = blockIdx.x / p.nsplit;
+    const int g = bg % p.hkv;
+    const int b = lpt_sequence(p, bg / p.hkv);
+    const int qpg = p.hq / p.hkv;
+    const int R = qpg * p.gamma;
+    const int lenb = min(max(p.len[b], 0), p.cap);
+    const int kbeg = p.window > 0 ? max(0, lenb - p.window) : 0;
+    const int cb = kbeg & ~(kChunk - 1);
+    const int nch = (lenb - cb + kChunk - 1) / kChunk;
+    const int nunits = nch + 1;
+    const int upw = (nunits + p.nsplit - 1) / p.nsplit;
+    const int u_begin = min(nunits, s * upw);
+    const int u_end = min(nunits, u_begin + upw);
+
+    const int64_t qkv_ld = p.qkv_ld;
+    const uint16_t* qrow0 = static_cast<const uint16_t*>(p.qkv) + (int64_t)b * p.gamma * qkv_ld;
+    const int kcol = p.hq * HD + g * HD;
+    const uint16_t* kc = static_cast<const uint16_t*>(p.kcache) + ((int64_t)b * p.hkv + g) * p.cap * HD;
+    const uint16_t* vc = static_cast<const uint16_t*>(p.vcache) + ((int64_t)b * p.hkv + g) * HD * (int64_t)p.cap;
+    const uint16_t* vblk = p.vblk + ((int64_t)b * p.hkv + g) * HD * kChunk;
+    const float sl2 = p.scale * 1.4426950408889634f;
+
+    // load j of unit u (this wavefront issues j = wave, wave + NRT, ...): j < HD/16 is K rows
+    // 4j .. 4j+3, else V rows (head dims) 16(j - HD/16) .. +15
+    auto issue = [&](const int u, const int j) {
+        uint16_t* dst = &stage[u % D][0][0];
+        const uint16_t* src;
+        if (j < HD / 16) {
+            const int r = 4 * j + (lane >> 4), slot = lane & 15;
+            const int piece = slot ^ ((r & 3) | ((r >> 1) & 12));
+            src = (u != nch) ? kc + (int64_t)(cb + u * kChunk + r) * HD
+                             : qrow0 + (int64_t)min(r, p.gamma - 1) * qkv_ld + kcol;
+            src += 8 * piece;
+            dst += j * 512;
+        } else {
+            const int jj = j - HD / 16;
+            const int d = 16 * jj + (lane >> 2), slot = lane & 3;
+            const int piece = slot ^ ((d >> 2) & 3);
+            src = (u != nch) ? vc + ((int64_t)(cb / kChunk + u) * HD + d) * kChunk : vblk + d * kChunk;
+            src += 8 * piece;
+            dst += kStageK + jj * 512;
+        }
+        attn_dma16(src, dst);
+    };
+    auto issue_unit = [&](const int u) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int j = wave + NRT * q;
+            if (j < NLOAD) issue(u, j);
+        }
+    };
+
+    // this wavefront's Q tile (rows past R repeat row R-1, never stored)
+    u32x4 qa[KS];
+    {
+        const int r = min(wave * 16 + col, R - 1);
+        const uint16_t* src = qrow0 + (int64_t)(r % p.gamma) * qkv_ld + (g * qpg + r / p.gamma) * HD + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = *reinterpret_cast<const u32x4*>(src + ks * 32);
+        // consumed here, before the stage loads go out: the compiler does not count those, and
+        // its wait for Q at the first product would otherwise wait for them too
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qa[ks]));
+    }
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    for (int u = u_begin; u < u_begin + D - 1 && u < u_end; ++u) issue_unit(u);
+    const int kq = 8 * (col >> 2) + (col & 3);
+    for (int u = u_begin; u < u_end; ++u) {
+        // unit u's loads landed (this wavefront's): later units' loads may stay in flight;
+        // the count is the fewest any wavefront issued, so a wavefront with more waits a
+        // little early. Then every wavefront's pieces, and every read of the stage reused next.
+        const int later = min(u_end - 1 - u, D - 2);
+        if (later >= 3)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(3 * LOW) : "memory");
+        else if (later == 2)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOW) : "memory");
+        else if (later == 1)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOW) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (u + D - 1 < u_end) issue_unit(u + D - 1);
+
+        const uint16_t* Kt = &stage[u % D][0][0];
+        const uint16_t* Vt = &stage[u % D][1][0];
+        const int nvalid = (u == nch) ? p.gamma : min(kChunk, lenb - cb - u * kChunk);
+        const int lo = (u == 0 && u != nch) ? kbeg - cb : 0;
+        f32x4 sc[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int r = kq + 4 * nt;
+            const int f = (r & 3) | ((r >> 1) & 12);
+            sc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 ka = *reinterpret_cast<const u32x4*>(Kt + r * HD + 8 * ((4 * ks + grp) ^ f));
+                sc[nt] = mfma16(ka, qa[ks], sc[nt]);
+            }
+        }
+        u32x4 ph, pl;
+        softmax_tile<DT>(sc, lo > 0 || nvalid < kChunk, grp, lo, nvalid, sl2, u != u_begin, m, l, o, ph, pl);
+        u32x4 vb[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int d = 16 * dt + col;
+            vb[dt] = *reinterpret_cast<const u32x4*>(Vt + d * kChunk + 8 * (grp ^ ((d >> 2) & 3)));
+        }
+        if (nvalid < kChunk) mask_v<DT>(vb, nvalid, grp);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = mfma16(vb[dt], pl, mfma16(vb[dt], ph, o[dt]));
+    }
+
+    // this wavefront's rows: lane holds dims dt*16 + 4*grp + e of row wave*16 + col
+    const int r = wave * 16 + col;
+    if (r < R) {
+        const int h = g * qpg + r / p.gamma, i = r % p.gamma;
+        float* dst = p.part + ((((int64_t)b * p.hq + h) * p.nparts + s) * p.gamma + i) * (HD + 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            *reinterpret_cast<f32x2*>(dst + 16 * dt + 4 * grp) = f32x2{o[dt][0], o[dt][1]};
+            *reinterpret_cast<f32x2*>(dst + 16 * dt + 4 * grp + 2) = f32x2{o[dt][2], o[dt][3]};
+        }
+        if (grp == 0) {
+            dst[HD] = m * 0.6931471805599453f;  // natural-log units (-inf without units)
+            dst[HD + 1] = l;
+        }
+    }
+    trace_end(p.stamps, t_start);
+}
+
+// ---------------------------------------------------------------------------
 // Row-split MFMA kernel (bf16 caches, 33..48 query rows per kv head): one
 // wavefront per 16-row tile, every wavefront walking all of the workgroup's
 // units. Each wavefront holds one tile's Q, O and softmax state (about half
@@ -438,8 +619,8 @@ __global__ __launch_bounds__(64 * NRT, 2) void attn_rows_kernel(const AttnParams
         if (u != nch) {
             k0 = kc + (int64_t)(cb + u * kChunk + col) * HD + 8 * grp;
             k1 = k0 + 16 * HD;
-            vp = vc + (int64_t)col * p.cap + cb + u * kChunk + 8 * grp;
-            vstride = 16 * (int64_t)p.cap;
+            vp = vc + ((int64_t)(cb / kChunk + u) * HD + col) * kChunk + 8 * grp;
+            vstride = 16 * kChunk;
         } else {
             k0 = qrow0 + (int64_t)min(col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
             k1 = qrow0 + (int64_t)min(16 + col, p.gamma - 1) * qkv_ld + kcol + 8 * grp;
@@ -780,11 +961,38 @@ static bool use_rows_kernel(int rows, int kv_f32, int pairs, int cap) {
     return !kv_f32 && rows > 32 && rows <= kMaxRows && (int64_t)pairs * units <= DFL_ATTN_ROWS_MAX_UNITS;
 }
 
-void attention_splits(int cap, int gamma, int kv_f32, int pairs, int rows, int* nsplit, int* nparts) {
+// the shared-stage kernel: bf16 caches, head dim 128, two 16-row tiles (Wide4's 20 rows: 77 ->
+// 52 us per round against the all-tiles kernel), where the row-split kernel does not apply.
+// With three tiles (Batched's 35 rows) the all-tiles kernel measured faster (785 against
+// 843 us per round).
+#ifndef DFL_ATTN_LDS_MIN_ROWS
+#define DFL_ATTN_LDS_MIN_ROWS 17
+#endif
+#ifndef DFL_ATTN_LDS_MAX_ROWS
+#define DFL_ATTN_LDS_MAX_ROWS 32
+#endif
+#ifndef DFL_ATTN_LDS_WGS
+#define DFL_ATTN_LDS_WGS 1024
+#endif
+static bool use_lds_kernel(int rows, int kv_f32, int pairs, int cap, int hd) {
+    return !kv_f32 && hd == 128 && rows >= DFL_ATTN_LDS_MIN_ROWS && rows <= DFL_ATTN_LDS_MAX_ROWS &&
+           !use_rows_kernel(rows, kv_f32, pairs, cap);
+}
+
+void attention_splits(int cap, int gamma, int kv_f32, int pairs, int rows, int hd, int* nsplit, int* nparts) {
+    const int units = (cap + kChunk - 1) / kChunk + 1;
+    const int np = pairs > 0 ? pairs : 1;
+    if (use_lds_kernel(rows, kv_f32, pairs, cap, hd)) {
+        // one workgroup walks its run of units with all its wavefronts
+        int ns = (DFL_ATTN_LDS_WGS + np - 1) / np;
+        ns = ns > units ? units : ns;
+        ns = ns < 1 ? 1 : (ns > kMaxSplit ? kMaxSplit : ns);
+        *nsplit = ns;
+        *nparts = ns;
+        return;
+    }
     if (use_rows_kernel(rows, kv_f32, pairs, cap)) {
         // a workgroup walks its units with three wavefronts; enough workgroups to fill the GPU
-        const int units = (cap + kChunk - 1) / kChunk + 1;
-        const int np = pairs > 0 ? pairs : 1;
         int ns = (DFL_ATTN_ROWS_WGS + np - 1) / np;
         ns = ns > units ? units : ns;
         ns = ns < 1 ? 1 : (ns > kMaxSplit ? kMaxSplit : ns);
@@ -801,9 +1009,8 @@ void attention_splits(int cap, int gamma, int kv_f32, int pairs, int rows, int* 
         // one unit per wavefront (cap/32 chunks plus the block) while the launch stays
         // below DFL_ATTN_WGS workgroups; with many (sequence, kv head) pairs, fewer splits
         // of more units each (fewer partial results, and the GPU is full either way)
-        const int units = (cap + kChunk - 1) / kChunk + 1;
         int ns = (units + 3) / 4;
-        const int want = (DFL_ATTN_WGS + (pairs > 0 ? pairs : 1) - 1) / (pairs > 0 ? pairs : 1);
+        const int want = (DFL_ATTN_WGS + np - 1) / np;
         if (ns > want) ns = want;
         ns = ns < 1 ? 1 : (ns > kMaxSplit ? kMaxSplit : ns);
         *nsplit = ns;
@@ -840,10 +1047,26 @@ static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
         }
     } else {
         const int nrt = R <= 16 ? 1 : (R <= 32 ? 2 : 3);
-        const bool rows_kernel = R > 32 && use_rows_kernel(R, 0, p.B * p.hkv, attn_span(p.cap, p.window));
+        const int span = attn_span(p.cap, p.window);
+        const bool rows_kernel = R > 32 && use_rows_kernel(R, 0, p.B * p.hkv, span);
+        const bool lds_kernel = use_lds_kernel(R, 0, p.B * p.hkv, span, HD);
         if (R > kMaxRows) return hipErrorInvalidValue;
-        snprintf(name, sizeof name, rows_kernel ? "attn_rows_kernel<%d, %d>" : "attn_mfma_kernel<%d, %d>", HD, nrt);
+        snprintf(name, sizeof name,
+                 lds_kernel ? "attn_lds_kernel<%d, %d>"
+                            : (rows_kernel ? "attn_rows_kernel<%d, %d>" : "attn_mfma_kernel<%d, %d>"),
+                 HD, nrt);
         q.stamps = trace_launch(TRACE_ATTENTION, name, grid.x, bytes, ctx_row_bytes);
+        if constexpr (HD == 128) {
+            if (lds_kernel) {
+                if (nrt == 2)
+                    hipLaunchKernelGGL((attn_lds_kernel<2>), grid, dim3(128), 0, s, q);
+                else
+                    hipLaunchKernelGGL((attn_lds_kernel<3>), grid, dim3(192), 0, s, q);
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                goto merge;
+            }
+        }
         if (nrt == 1)
             hipLaunchKernelGGL((attn_mfma_kernel<HD, 1>), grid, dim3(kBlock), 0, s, q);
         else if (nrt == 2)
@@ -853,8 +1076,11 @@ static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
         else
             hipLaunchKernelGGL((attn_mfma_kernel<HD, 3>), grid, dim3(kBlock), 0, s, q);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+merge:
     const dim3 mgrid((unsigned)((p.B * p.hq * p.gamma + 3) / 4));
     if (p.nparts <= 32)
         hipLaunchKernelGGL((attn_merge_kernel<HD, 32>), mgrid, dim3(kBlock), 0, s, p);

@@ -17,7 +17,7 @@ struct AttnParams {
     const uint16_t* vblk;  // bf16 caches: block values head-dim major [B][hkv][hd][32], keys < gamma
     int64_t qkv_ld;
     const void* kcache;    // this layer's keys   [B][hkv][cap][hd]
-    const void* vcache;    // this layer's values [B][hkv][hd][cap] (head-dim major)
+    const void* vcache;    // this layer's values [B][hkv][cap/32][hd][32] (bf16; fp32: [B][hkv][hd][cap])
     const int32_t* len;    // [B] context rows per sequence
     int B, hq, hkv, hd, gamma, cap, nsplit, kv_f32;
     int window;            // attend to the last `window` context keys of each sequence; 0 = all
@@ -32,9 +32,9 @@ struct AttnParams {
 
 // Workgroups per (sequence, kv head) and partial results per (sequence, head)
 // for a cache of `cap` rows, `pairs` (sequence, kv head) pairs and `rows` query
-// rows per kv head (one partial per workgroup); the workspace holds
+// rows per kv head at head dim `hd` (one partial per workgroup); the workspace holds
 // B*hq*nparts*gamma*(hd+2) floats.
-void attention_splits(int cap, int gamma, int kv_f32, int pairs, int rows, int* nsplit, int* nparts);
+void attention_splits(int cap, int gamma, int kv_f32, int pairs, int rows, int hd, int* nsplit, int* nparts);
 // context keys a sequence can attend in a cache of `cap` rows under a window (0: cap): the
 // window plus the part of its first 32-key chunk before it; pass it as attention_splits' cap
 int attn_span(int cap, int window);

@@ -130,4 +130,12 @@ __device__ __forceinline__ void load_gain8(const void* g, bool f32, int i, float
     }
 }
 
+// Offset of value (pos, dim) in one (sequence, kv head) slab of the value cache. bf16
+// caches hold each 32-key chunk of all head dims contiguously ([cap/32][hd][32]): a key
+// chunk's values are one contiguous run, read in 1 KB pieces. fp32 caches are head-dim
+// major ([hd][cap]).
+__host__ __device__ inline int64_t v_cache_off(int pos, int dim, int hd, int cap, bool f32) {
+    return f32 ? (int64_t)dim * cap + pos : ((int64_t)(pos >> 5) * hd + dim) * 32 + (pos & 31);
+}
+
 }  // namespace dfl

@@ -408,7 +408,7 @@ Ws ws_layout(const dflash_dims& d, int B, int cap, void* base) {
     const size_t rows = (size_t)B * d.gamma;
     const int qkv_rows = (d.hq + 2 * d.hkv) * d.hd;
     attention_splits(attn_span(cap, d.window), d.gamma, d.wdtype == DFLASH_F32, B * d.hkv, (d.hq / d.hkv) * d.gamma,
-                     &w.nsplit, &w.nparts);
+                     d.hd, &w.nsplit, &w.nparts);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -837,7 +837,7 @@ int run_layer(const dflash_model* M, int i, float* h, const dflash_kv* kv, int B
         p.out_ld = qkv_rows;
         if (d.wdtype != DFLASH_F32) {
             // bf16 models (Q, K_b, V_b are bf16 by the rounding contract): Q and K_b row-major,
-            // V_b head-dim major like the value cache
+            // V_b head-dim major: the layout of one 32-key chunk of the value cache
             p.out_bf16 = 1;
             p.vt = w.vt;
             p.vt_col = (d.hq + d.hkv) * d.hd;

@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
                     const int dim = n - which * kvw - head * p.hd;
                     const int64_t hb = (int64_t)layer * p.layer_stride + ((int64_t)b * p.hkv + head) * p.cap * p.hd;
                     uint16_t* base = static_cast<uint16_t*>(which ? p.vcache : p.kcache);
-                    const int64_t off = hb + (which ? (int64_t)dim * p.cap + pos : (int64_t)pos * p.hd + dim);
+                    const int64_t off = hb + (which ? v_cache_off(pos, dim, p.hd, p.cap, false) : (int64_t)pos * p.hd + dim);
                     base[off] = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
                 }
             }

@@ -40,7 +40,7 @@ struct GemmParams {
     // goes to cache position len[b] + (m - row_offsets[b]) when that row index is
     // below counts[b] (all rows when counts is null) and the position below cap
     void* kcache;  // [nl][B][hkv][cap][hd] bf16
-    void* vcache;  // [nl][B][hkv][hd][cap] bf16
+    void* vcache;  // [nl][B][hkv][cap/32][hd][32] bf16
     const int32_t* len;
     const int32_t* row_offsets;
     const int32_t* counts;

@@ -621,7 +621,7 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
                             const int dim = c - which * kvw - head * p.hd;
                             const int64_t hb = ((int64_t)b * p.hkv + head) * p.cap * p.hd;
                             const int64_t off = (int64_t)layer * p.layer_stride + hb +
-                                                (which ? (int64_t)dim * p.cap + pos : (int64_t)pos * p.hd + dim);
+                                                (which ? v_cache_off(pos, dim, p.hd, p.cap, p.kv_f32) : (int64_t)pos * p.hd + dim);
                             void* base = which ? p.vcache : p.kcache;
                             if (p.kv_f32)
                                 static_cast<float*>(base)[off] = y;
@@ -647,10 +647,10 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(const GemvParams p, const 
                         const int which = n / kvw;
                         const int head = (n - which * kvw) / p.hd;
                         const int dim = n - which * kvw - head * p.hd;
-                        // keys [B][hkv][cap][hd]; values head-dim major [B][hkv][hd][cap]
+                        // keys [B][hkv][cap][hd]; values in the value-cache layout (v_cache_off)
                         const int64_t hb = ((int64_t)b * p.hkv + head) * p.cap * p.hd;
                         const int64_t off = (int64_t)layer * p.layer_stride + hb +
-                                            (which ? (int64_t)dim * p.cap + pos : (int64_t)pos * p.hd + dim);
+                                            (which ? v_cache_off(pos, dim, p.hd, p.cap, p.kv_f32) : (int64_t)pos * p.hd + dim);
                         void* base = which ? p.vcache : p.kcache;
                         if (p.kv_f32)
                             static_cast<float*>(base)[off] = y;

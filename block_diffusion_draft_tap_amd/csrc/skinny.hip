@@ -98,7 +98,8 @@ __device__ __forceinline__ void kv_store(const SkinnyParams& p, int z, int b, in
     const int dim = n - which * kvw - head * p.hd;
     const int64_t hb = (int64_t)z * p.layer_stride + ((int64_t)b * p.hkv + head) * p.cap * p.hd;
     uint16_t* base = which ? p.vcache : p.kcache;
-    base[hb + (which ? (int64_t)dim * p.cap + pos : (int64_t)pos * p.hd + dim)] = (uint16_t)f32_to_bf16_bits(y);
+    base[hb + (which ? v_cache_off(pos, dim, p.hd, p.cap, false) : (int64_t)pos * p.hd + dim)] =
+        (uint16_t)f32_to_bf16_bits(y);
 }
 
 // the SK_STORE / SK_RESID epilogue of one output

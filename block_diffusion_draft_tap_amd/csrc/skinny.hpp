@@ -60,7 +60,7 @@ struct SkinnyParams {
     // and goes to cache position len[b] + (r - row_offsets[b]) when that index is below
     // counts[b] (all rows when counts is null) and the position below cap
     uint16_t* kcache;     // [layers][B][hkv][cap][hd]
-    uint16_t* vcache;     // [layers][B][hkv][hd][cap]
+    uint16_t* vcache;     // [layers][B][hkv][cap/32][hd][32]
     const int32_t* len;
     const int32_t* row_offsets;
     const int32_t* counts;

@@ -144,9 +144,13 @@ typedef struct {
 
 /* Retained per-layer context K/V of B sequences, element type `dtype`
  * (DFLASH_F32 for f32 models, DFLASH_BF16 otherwise):
- *   k: [nl][B][hkv][cap][hd]   (row-major keys)
- *   v: [nl][B][hkv][hd][cap]   (head-dim major values: the attention's
- *                               value operand is 8 consecutive keys of one dim)
+ *   k: [nl][B][hkv][cap][hd]         (row-major keys)
+ *   v: [nl][B][hkv][cap/32][hd][32]  (DFLASH_BF16: values in 32-key chunks,
+ *                                     head-dim major inside a chunk, so the
+ *                                     attention's value operand is 8
+ *                                     consecutive keys of one dim and a chunk's
+ *                                     values are one contiguous run)
+ *      [nl][B][hkv][hd][cap]         (DFLASH_F32: head-dim major)
  * cap must be a multiple of 32 for DFLASH_BF16 caches.
  * len: device int32 [B], rows held per sequence. */
 typedef struct {

@@ -52,6 +52,24 @@ def rel_err(gpu, ref):
     return float(np.max(np.abs(g - r)) / max(1e-30, np.max(np.abs(r))))
 
 
+def dense_v(kv):
+    """The value cache [nl, B, hkv, hd, cap] (head-dim major) whatever its storage: bf16
+    caches hold 32-key chunks [nl, B, hkv, cap/32, hd, 32]."""
+    v = kv.v
+    if v.dim() == 5:
+        return v
+    nl, B, hkv, nc, hd, c = v.shape
+    return v.permute(0, 1, 2, 4, 3, 5).reshape(nl, B, hkv, hd, nc * c)
+
+
+def v_rows(kv, i, b, rows_t):
+    """Values of cache rows `rows_t` (an index tensor) of layer i, sequence b: [rows, hkv, hd]."""
+    v = kv.v[i, b]
+    if v.dim() == 3:                                    # [hkv, hd, cap]
+        return v[:, :, rows_t].permute(2, 0, 1)
+    return v[:, rows_t // 32, :, rows_t % 32]           # [hkv, cap/32, hd, 32] -> [rows, hkv, hd]
+
+
 def dev(a, device="cuda"):
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:

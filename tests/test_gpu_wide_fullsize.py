@@ -31,7 +31,7 @@ import torch
 
 import block_diffusion_draft_tap_amd as dfa
 from block_diffusion_draft_tap_amd import binding as bd
-from gpu_common import compare_ids, dev, log, rel_err, tol
+from gpu_common import compare_ids, dev, log, rel_err, tol, v_rows
 from oracle import dflash_oracle as O
 from synth import gen, WIDE, WIDE4, BATCHED, DFLASH2, scaled
 
@@ -76,7 +76,7 @@ def oracle_context(d, w, taps, fm, positions=None):
 def check_kv_rows(kv, i, b, rows, K, V, t, what):
     rows_t = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=kv.k.device)
     gk = kv.k[i, b][:, rows_t, :].permute(1, 0, 2)          # [rows, hkv, hd]
-    gv = kv.v[i, b][:, :, rows_t].permute(2, 0, 1)
+    gv = v_rows(kv, i, b, rows_t)
     ek, ev = rel_err(gk, K), rel_err(gv, V)
     assert ek <= t and ev <= t, (what, i, b, ek, ev)
     return max(ek, ev)
