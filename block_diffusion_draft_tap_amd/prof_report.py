@@ -12,8 +12,8 @@
       Memory traffic per launch of one kernel from two counter passes
       (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, values in KiB per dispatch).
       Each counter is scaled by what it reads for a calibration kernel that
-      reads and writes N bytes: the last PyTorch kernel dispatched before the
-      first launch of the measured kernel.
+      reads and writes N bytes: the last PyTorch multiply kernel of the run
+      (bench.py's calibration copy); the measured kernel's dispatches after it count.
 
   python -m block_diffusion_draft_tap_amd.prof_report counters <counter_collection.csv>...
       --kernel <name substring> [--command CMD ...]
@@ -68,6 +68,8 @@ def stats_table(path, per=1.0, top=40, per_kernel=None):
              "|---|---:|---:|---:|---:|---:|---:|"]
     for r in rows[:top]:
         name = r["Name"].replace("|", "/")
+        if len(name) > 160:  # template-heavy library kernels: the head of the name says which
+            name = name[:157] + "..."
         calls = int(r["Calls"])
         lines.append(f"| `{name}` | {calls} | {calls / per:.2f} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
@@ -86,15 +88,17 @@ def _dispatches(path):
 
 
 def _split(path, counter, kernel):
+    """The measured kernel's dispatches after the calibration copy (bench.py's scalar
+    multiply, a MulFunctor elementwise kernel: the last one in the run), and the copy."""
     disp = _dispatches(path)
     ids = sorted(disp)
-    targets = [i for i in ids if kernel in disp[i]["name"]]
-    if not targets:
-        raise SystemExit(f"{path}: no dispatch of a kernel containing {kernel!r}")
-    calib = [i for i in ids if i < targets[0] and disp[i]["name"].startswith("void at::native")]
+    calib = [i for i in ids if disp[i]["name"].startswith("void at::native") and "MulFunctor" in disp[i]["name"]]
     if not calib:
-        raise SystemExit(f"{path}: no calibration dispatch before the first {kernel!r}")
+        raise SystemExit(f"{path}: no calibration dispatch (a PyTorch multiply kernel)")
     c = calib[-1]
+    targets = [i for i in ids if i > c and kernel in disp[i]["name"]]
+    if not targets:
+        raise SystemExit(f"{path}: no dispatch of a kernel containing {kernel!r} after the calibration copy")
     vals = [disp[i]["vals"][counter] for i in targets]
     return disp[targets[0]]["name"], vals, disp[c]["name"], disp[c]["vals"][counter]
 
