@@ -297,14 +297,21 @@ def prefill(d, dm, kv, ws, lengths, cpu_seq, dev, reps, up):
                 taps[j][s0:s1] = torch.randn(s1 - s0, d.H, generator=g, device=dev).to(act)
     h = torch.empty(n, d.d, dtype=torch.float32, device=dev)
     offs = torch.from_numpy(offs_h.astype(np.int32)).to(dev)
-    kws = dfa.kv_prefill_workspace(d, n, dev) if (d.wdtype == "bf16" and n >= 64) else ws
+    # bf16: room to stage every layer's normalised rows; int4: room to expand the weights into
+    # bf16 high and low parts for the matrix-core GEMMs (both calls)
+    kws = ws
+    if d.wdtype == "bf16" and n >= 64:
+        kws = dfa.kv_prefill_workspace(d, n, dev)
+    elif d.wdtype == "int4g64" and n >= 64:
+        kws = dfa.int4_prefill_workspace(d, n, dev)
+    pws = kws if d.wdtype == "int4g64" else ws
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     proj_ms, kv_ms = [], []
     for r in range(reps + 1):
         kv.len.zero_()
         torch.cuda.synchronize()
         ev[0].record()
-        bd.check(dfa.dflash_context_project(dm, taps, h, ws), "context_project (prefill)")
+        bd.check(dfa.dflash_context_project(dm, taps, h, pws), "context_project (prefill)")
         ev[1].record()
         bd.check(dfa.dflash_ctx_kv_append(dm, h, offs, None, kv, kws), "append (prefill)")
         ev[2].record()
@@ -313,7 +320,7 @@ def prefill(d, dm, kv, ws, lengths, cpu_seq, dev, reps, up):
             proj_ms.append(ev[0].elapsed_time(ev[1]))
             kv_ms.append(ev[1].elapsed_time(ev[2]))
     assert kv.len.cpu().tolist() == lengths
-    del taps, h, kws
+    del taps, h, kws, pws
     torch.cuda.empty_cache()
     if reps == 0:
         return None

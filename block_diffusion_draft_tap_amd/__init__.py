@@ -12,7 +12,7 @@ _BINDING_NAMES = (
     "dflash_draft_forward", "dflash_lm_head_argmax", "dflash_verify_greedy", "dflash_invocations",
     "dflash_trace_begin", "dflash_trace_end", "DsparkHead", "dspark_workspace",
     "dflash_draft_forward_dspark", "dflash_verify_greedy_lengths", "dflash_draft_round", "round_workspace",
-    "dflash_verify_from_hidden", "verify_hidden_workspace",
+    "dflash_verify_from_hidden", "verify_hidden_workspace", "int4_prefill_workspace",
     "check", "DflashError",
 )
 

@@ -29,7 +29,8 @@ EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "df
            "dflash_trace_end", "dflash_lm_head_workgroups", "dflash_wall_clock_hz", "dflash_verify_greedy_noalloc",
            "dflash_verify_noalloc_max_bytes", "dflash_dspark_workspace_bytes", "dflash_draft_forward_dspark",
            "dflash_verify_greedy_lengths", "dflash_draft_round", "dflash_round_workspace_bytes",
-           "dflash_verify_from_hidden", "dflash_verify_hidden_workspace_bytes", "dflash_lm_head_workspace_bytes_for"]
+           "dflash_verify_from_hidden", "dflash_verify_hidden_workspace_bytes", "dflash_lm_head_workspace_bytes_for",
+           "dflash_int4_prefill_workspace_bytes"]
 DFLASH_TRACE_LM_HEAD, DFLASH_TRACE_ATTENTION, DFLASH_TRACE_PROJECTIONS = 1, 2, 4
 
 
@@ -87,6 +88,8 @@ def _load():
     lib.dflash_workspace_bytes.restype = SZ
     lib.dflash_kv_prefill_workspace_bytes.argtypes = [P(dflash_dims), I32]
     lib.dflash_kv_prefill_workspace_bytes.restype = SZ
+    lib.dflash_int4_prefill_workspace_bytes.argtypes = [P(dflash_dims), I32]
+    lib.dflash_int4_prefill_workspace_bytes.restype = SZ
     lib.dflash_query.argtypes = [P(dflash_dims)]
     lib.dflash_query.restype = ctypes.c_int
     lib.dflash_status_string.argtypes = [ctypes.c_int]
@@ -445,6 +448,15 @@ def kv_prefill_workspace(dims, n, device="cuda"):
     nb = lib.dflash_kv_prefill_workspace_bytes(ctypes.byref(make_dims(dims)), n)
     if nb == 0:
         raise DflashError("invalid dims or row count for a prefill workspace")
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def int4_prefill_workspace(dims, n, device="cuda"):
+    """The workspace with which an int4 model's context projection and K/V append of n >= 64
+    rows run on matrix cores (their weights expanded into bf16 high and low parts)."""
+    nb = lib.dflash_int4_prefill_workspace_bytes(ctypes.byref(make_dims(dims)), n)
+    if nb == 0:
+        raise DflashError("no int4 prefill workspace for these dims or row count")
     return torch.empty(nb, dtype=torch.uint8, device=device)
 
 

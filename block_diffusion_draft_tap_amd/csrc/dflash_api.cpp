@@ -373,6 +373,19 @@ size_t kv_i4_bytes(const dflash_dims& d, int n) {
     return kv_append_norm_bytes(d, n) + align_up((size_t)d.nl * ns * n * 2 * d.hkv * d.hd * 4);
 }
 
+// int4 prefill (n >= DFL_GEMM_MIN_ROWS rows) on matrix cores: the call expands its int4
+// weights into bf16 high and low parts in ws ([N, 2K], one bf16 GEMM against [A | A]); the
+// context projection expands W_c [d, m H], the K/V append every layer's K and V rows
+// [2 hkv hd, d] and keeps the per-row RMS factors after them. 0: not served there.
+size_t i4_prefill_proj_bytes(const dflash_dims& d, int n) {
+    if (d.wdtype != DFLASH_INT4G64 || n < DFL_GEMM_MIN_ROWS || d.H % 64 || d.m > kMaxTaps) return 0;
+    return align_up((size_t)d.d * 2 * d.m * d.H * 2);
+}
+size_t i4_prefill_kv_bytes(const dflash_dims& d, int n) {
+    if (d.wdtype != DFLASH_INT4G64 || n < DFL_GEMM_MIN_ROWS || d.d % 64 || d.nl < 1) return 0;
+    return align_up((size_t)d.nl * 2 * d.hkv * d.hd * 2 * d.d * 2) + align_up((size_t)n * 4);
+}
+
 size_t kv_append_skinny_bytes(const dflash_dims& d, int n) {
     if (!ctx_skinny_rows(d, n) || d.d % kSkinnyK || d.nl < 1) return 0;
     const int N = 2 * d.hkv * d.hd;
@@ -1392,6 +1405,27 @@ int dflash_context_project(const dflash_model* M, const void* const* taps, int64
         g.c_ld = d.d;
         DFL_HIP(launch_gemm(GEMM_A_TAPS, GEMM_EPI_F32, g, 1, s));
         DFL_HIP(launch_rownorm(h_ctx, 1, 0, h_ctx, n, d.d, M->ctx_norm, 0, d.eps, s));
+    } else if (i4_prefill_proj_bytes(d, n) > 0 && ws && aligned16(ws) && ws_bytes >= i4_prefill_proj_bytes(d, n)) {
+        // int4 prefill: W_c expanded into bf16 high and low parts [d, 2 m H] in ws, then
+        // P = [T_1 .. T_m | T_1 .. T_m] [W_hi | W_lo]^T on matrix cores, then the norm in place
+        uint16_t* wx = static_cast<uint16_t*>(ws);
+        DFL_HIP(launch_i4_expand(static_cast<const uint32_t*>(M->w_c.data),
+                                 static_cast<const uint16_t*>(M->w_c.scales),
+                                 static_cast<const uint16_t*>(M->w_c.biases), d.m * d.H, 0, d.d, wx, s));
+        GemmParams g;
+        std::memset(&g, 0, sizeof(g));
+        g.M = n;
+        g.N = d.d;
+        g.K = 2 * d.m * d.H;
+        g.a_period = d.m * d.H;
+        for (int j = 0; j < d.m; ++j) g.a[j] = static_cast<const uint16_t*>(taps[j]);
+        g.a_ld = tap_ld;
+        g.seg_k = d.H;
+        g.b[0] = wx;
+        g.c = h_ctx;
+        g.c_ld = d.d;
+        DFL_HIP(launch_gemm(GEMM_A_TAPS, GEMM_EPI_F32, g, 1, s));
+        DFL_HIP(launch_rownorm(h_ctx, 1, 0, h_ctx, n, d.d, M->ctx_norm, 0, d.eps, s));
     } else if (M->w_c.dtype == DFLASH_INT4G64 && ctx_i4_bytes(d, n) > 0 && ws && aligned16(ws) &&
                ws_bytes >= ctx_i4_bytes(d, n)) {
         // int4 W_c, up to 16 rows: matrix-core K ranges (each inside one tap buffer), split
@@ -1498,6 +1532,51 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
         p.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
         skinny_split(SK_KV, p.N, p.K, p.layers, &p.nsplit, &p.kslice);
         DFL_HIP(launch_skinny(SK_KV, p, s));
+        DFL_TRY(append_done(M, kv, row_offsets, counts, n, s));
+        g_invocations++;
+        return DFLASH_OK;
+    }
+    if (i4_prefill_kv_bytes(d, n) > 0 && ws && aligned16(ws) && aligned16(h_ctx) && ws_bytes >= i4_prefill_kv_bytes(d, n)) {
+        // int4 prefill: every layer's K and V rows expanded into bf16 high and low parts
+        // [2 hkv hd, 2 d] in ws, the per-row RMS factors after them, then every layer's
+        // [K | V] = [N | N] [W_hi | W_lo]^T (N = bf16(RMSNorm(h_ctx; attn_norm_i)) staged on
+        // the fly) as one matrix-core GEMM over all layers, scattered into the cache
+        const int kvr = 2 * d.hkv * d.hd;
+        uint16_t* wx = static_cast<uint16_t*>(ws);
+        const int64_t layer_elems = (int64_t)kvr * 2 * d.d;
+        for (int i = 0; i < d.nl; ++i) {
+            const dflash_weight& w = M->layers[i].w_qkv;
+            DFL_HIP(launch_i4_expand(static_cast<const uint32_t*>(w.data), static_cast<const uint16_t*>(w.scales),
+                                     static_cast<const uint16_t*>(w.biases), d.d, (int64_t)d.hq * d.hd, kvr,
+                                     wx + i * layer_elems, s));
+        }
+        float* rinv = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)d.nl * layer_elems * 2));
+        DFL_HIP(launch_row_rinv(h_ctx, d.d, n, d.d, d.eps, rinv, s));
+        GemmParams g;
+        std::memset(&g, 0, sizeof(g));
+        g.M = n;
+        g.N = kvr;
+        g.K = 2 * d.d;
+        g.a_period = d.d;
+        g.x = h_ctx;
+        g.a_ld = d.d;
+        g.rinv = rinv;
+        g.gain_f32 = 0;
+        for (int i = 0; i < d.nl; ++i) {
+            g.b[i] = wx + i * layer_elems;
+            g.gain[i] = M->layers[i].attn_norm;
+        }
+        g.kcache = kv->k;
+        g.vcache = kv->v;
+        g.len = kv->len;
+        g.row_offsets = row_offsets;
+        g.counts = counts;
+        g.B = kv->B;
+        g.hkv = d.hkv;
+        g.hd = d.hd;
+        g.cap = kv->cap;
+        g.layer_stride = (int64_t)kv->B * d.hkv * kv->cap * d.hd;
+        DFL_HIP(launch_gemm(GEMM_A_NORM, GEMM_EPI_KV, g, d.nl, s));
         DFL_TRY(append_done(M, kv, row_offsets, counts, n, s));
         g_invocations++;
         return DFLASH_OK;
@@ -1915,6 +1994,12 @@ size_t dflash_lm_head_workspace_bytes_for(const dflash_weight* E_out, int32_t y_
 size_t dflash_kv_prefill_workspace_bytes(const dflash_dims* dims, int32_t n) {
     if (check_dims(dims) == DFLASH_EINVAL || n <= 0) return 0;
     return kv_append_norm_bytes(*dims, n);
+}
+
+size_t dflash_int4_prefill_workspace_bytes(const dflash_dims* dims, int32_t n) {
+    if (check_dims(dims) == DFLASH_EINVAL || n <= 0) return 0;
+    const size_t a = i4_prefill_proj_bytes(*dims, n), b = i4_prefill_kv_bytes(*dims, n);
+    return a > b ? a : b;
 }
 
 int dflash_verify_greedy_lengths(const float* target_logits, const int32_t* draft_ids, const int32_t* lengths,

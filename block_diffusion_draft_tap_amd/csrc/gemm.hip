@@ -95,6 +95,7 @@ __device__ __forceinline__ const uint16_t* tap_base(const GemmParams& p, int k0)
 template <int AMODE>
 __device__ __forceinline__ void load_a(const GemmParams& p, int m0, int k0, AStage<AMODE>& st) {
     const int t = threadIdx.x;
+    if (p.a_period > 0) k0 %= p.a_period;
     const uint16_t* abase = nullptr;
     if constexpr (AMODE == GEMM_A_TAPS) abase = tap_base(p, k0);
 #pragma unroll
@@ -116,6 +117,7 @@ template <int AMODE>
 __device__ __forceinline__ void store_a(const GemmParams& p, int k0, const void* gain, const AStage<AMODE>& st,
                                         uint16_t (*As)[kLd]) {
     const int t = threadIdx.x;
+    if (p.a_period > 0) k0 %= p.a_period;
 #pragma unroll
     for (int i = 0; i < kAC; ++i) {
         const int c = t + kThreads * i;
@@ -358,7 +360,9 @@ static hipError_t launch_t(const GemmParams& p, int layers, hipStream_t s) {
 hipError_t launch_gemm(int amode, int epi, const GemmParams& p, int layers, hipStream_t s) {
     if (p.M <= 0 || p.N <= 0 || p.K <= 0 || (p.K % kBK) || layers < 1 || layers > kMaxLayers)
         return hipErrorInvalidValue;
-    if (amode == GEMM_A_TAPS && (p.seg_k <= 0 || (p.seg_k % kBK) || p.K > kMaxTaps * p.seg_k))
+    const int a_cols = p.a_period > 0 ? p.a_period : p.K;  // A's own columns
+    if (p.a_period < 0 || (p.a_period > 0 && (p.a_period % kBK || p.K % p.a_period))) return hipErrorInvalidValue;
+    if (amode == GEMM_A_TAPS && (p.seg_k <= 0 || (p.seg_k % kBK) || a_cols > kMaxTaps * p.seg_k))
         return hipErrorInvalidValue;
     if (amode == GEMM_A_TAPS && epi == GEMM_EPI_F32) return launch_t<GEMM_A_TAPS, GEMM_EPI_F32>(p, layers, s);
     if (amode == GEMM_A_TAPS && epi == GEMM_EPI_KV) return launch_t<GEMM_A_TAPS, GEMM_EPI_KV>(p, layers, s);

@@ -23,6 +23,9 @@ struct GemmParams {
     int64_t a_ld;
     int64_t a_layer_stride;
     int seg_k;
+    // a_period > 0: A's column k is column k % a_period of the rows above (the K of a B
+    // matrix that holds two parts of every weight, [W_hi | W_lo], against [A | A])
+    int a_period;
     // GEMM_A_NORM: A[m, k] = bf16((x[m, k] * rinv[m]) * gain[k]) from fp32 rows
     // x (row stride a_ld); gain per layer (grid.z)
     const float* x;

@@ -321,4 +321,50 @@ hipError_t launch_i4_split_argmax(const float* part, int nsplit, int M, int N, f
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// int4-g64 rows expanded into bf16 high and low parts (the prefill's matrix-core GEMM reads
+// them as one [N, 2K] bf16 matrix against [A | A]); one thread per code word (8 values)
+__global__ __launch_bounds__(256) void i4_expand_kernel(const uint32_t* __restrict__ codes,
+                                                        const uint16_t* __restrict__ scales,
+                                                        const uint16_t* __restrict__ biases, int K, int64_t row0,
+                                                        int N, uint16_t* __restrict__ out) {
+    const int K8 = K / 8;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)N * K8) return;
+    const int64_t n = t / K8;
+    const int w = (int)(t - n * K8);
+    const int64_t row = row0 + n;
+    const uint32_t c = codes[row * K8 + w];
+    const int g = w / 8;  // 64-column group: 8 words
+    const float sc = bf16_lo((uint32_t)scales[row * (K / 64) + g]);
+    const float bi = bf16_lo((uint32_t)biases[row * (K / 64) + g]);
+    float hv[8], lv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float v = fmaf(sc, (float)((c >> (4 * e)) & 15u), bi);
+        const uint32_t h = f32_to_bf16_bits(v);
+        hv[e] = bf16_lo(h);
+        lv[e] = v - hv[e];
+    }
+    u32x4 hi, lo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        hi[q] = pack_bf16x2(hv[2 * q], hv[2 * q + 1]);
+        lo[q] = pack_bf16x2(lv[2 * q], lv[2 * q + 1]);
+    }
+    uint16_t* o = out + n * 2 * (int64_t)K + 8 * (int64_t)w;
+    *reinterpret_cast<u32x4*>(o) = hi;
+    *reinterpret_cast<u32x4*>(o + K) = lo;
+}
+
+hipError_t launch_i4_expand(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int K, int64_t row0,
+                            int N, uint16_t* out, hipStream_t s) {
+    if (!codes || !scales || !biases || !out || K <= 0 || (K % 64) || N <= 0) return hipErrorInvalidValue;
+    const int64_t words = (int64_t)N * (K / 8);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(i4_expand_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, codes, scales, biases,
+                       K, row0, N, out);
+    return hipGetLastError();
+}
+
 }  // namespace dfl

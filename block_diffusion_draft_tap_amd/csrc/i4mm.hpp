@@ -46,6 +46,12 @@ hipError_t launch_i4mm(I4Params p, hipStream_t s);
 // per row m and chunk c of kI4ArgChunk outputs: the (max, lowest index) over n of
 // sum_s part[s][m][n] (split order), into pv / pi [M][nblocks], nblocks = i4_argmax_blocks(N)
 int i4_argmax_blocks(int N);
+// rows row0 .. row0 + N - 1 of an int4-g64 matrix [*, K] expanded into bf16 [N, 2K]: columns
+// [0, K) the high parts bf16(w), [K, 2K) the low parts bf16(w - bf16(w)), w = scale * q + bias
+// formed in fp32 (exact but for the sum's rounding); high + low hold w to about 16 bits, so
+// one bf16 matrix-core product over [A | A] reproduces the int4 product (the prefill GEMM)
+hipError_t launch_i4_expand(const uint32_t* codes, const uint16_t* scales, const uint16_t* biases, int K, int64_t row0,
+                            int N, uint16_t* out, hipStream_t s);
 hipError_t launch_i4_split_argmax(const float* part, int nsplit, int M, int N, float* pv, int32_t* pi, int nblocks,
                                   hipStream_t s);
 

@@ -274,6 +274,21 @@ int dflash_ctx_kv_append(const dflash_model* M, const float* h_ctx, int32_t n, c
  * (layers * n * d * 2, rounded up to 256); 0 for invalid dims or n <= 0. */
 size_t dflash_kv_prefill_workspace_bytes(const dflash_dims* dims, int32_t n);
 
+/* Workspace bytes with which, for an int4-g64 model (Eq 2 and the context
+ * half of Eq 3 on a prompt's rows: page 3, #buildContext and
+ * projectContextRows), dflash_context_project and dflash_ctx_kv_append of
+ * n >= 64 rows run on matrix cores (ws and h_ctx 16-byte aligned): the call
+ * first expands its int4 weights in ws into bf16 high and low parts
+ * (w = scale * q + bias formed in fp32; high = bf16(w), low = bf16(w - high),
+ * which together hold w to about 16 bits), [N, 2K] per matrix, then runs one
+ * bf16 GEMM of [A | A] against [W_high | W_low]: W_c [d, m*H] for the
+ * projection (d * 2*m*H * 2 bytes), every layer's K and V rows [2*hkv*hd, d]
+ * plus 4n bytes of row RMS factors for the append. Returns the larger of the
+ * two (256-byte rounded); 0 for dims that are invalid or not int4, n < 64, or
+ * widths that are not multiples of 64. With a smaller workspace the int4
+ * calls run on the GEMV paths. */
+size_t dflash_int4_prefill_workspace_bytes(const dflash_dims* dims, int32_t n);
+
 /* One drafter layer on the block (page 3, #layer, Eq 3), in place:
  *   n = RMSNorm(H; attn_norm), Q/K_b/V_b = n W^T,
  *   O = softmax(hd^-1/2 Q [K_ctx[0:len[b]] ; K_b]^T) [V_ctx ; V_b]  (no mask),

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_functions():
     src = open(os.path.join(ROOT, "include", "dflash.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dflash_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported():

@@ -255,6 +255,45 @@ def test_kv_prefill_staged(name):
             assert float((a - c).abs().max()) <= t * float(a.abs().max()), (i, b)
 
 
+@pytest.mark.parametrize("name", ["wide4_small", "wide4_b1", "d2_wide4"])
+def test_int4_prefill_matrix_cores(name):
+    """The int4 prefill on matrix cores (page 3, #buildContext and projectContextRows on a
+    prompt's rows): with dflash_int4_prefill_workspace_bytes of workspace the projection and
+    the K/V append expand their int4 weights into bf16 high and low parts and run one bf16
+    GEMM each. H_ctx and every layer's K/V (rotated for d2_wide4) against the oracle, and
+    against the GEMV path of the same calls (the fixture's); lengths advanced by every row."""
+    s = get(name)
+    d = s.dims
+    n = sum(s.lengths)
+    assert n >= 64 and d.wdtype == "int4g64"
+    ws = dfa.int4_prefill_workspace(d, n)
+    assert ws.numel() >= d.d * 2 * d.m * d.H * 2
+    t = tol(d)
+    h = torch.empty(n, d.d, dtype=torch.float32, device="cuda")
+    bd.check(dfa.dflash_context_project(s.dm, s.taps_d, h, ws), "int4 prefill projection")
+    torch.cuda.synchronize()
+    err = rel_err(h, np.concatenate(s.Hs))
+    gap = float((h - s.h_ctx).abs().max()) / float(s.h_ctx.abs().max())
+    log(f"[{name}] int4 prefill projection of {n} rows: H_ctx rel err {err:.3e}, against the GEMV path {gap:.3e}")
+    assert err <= t and gap <= t
+    kv2 = dfa.KVCache(d, s.B, s.cap)
+    bd.check(dfa.dflash_ctx_kv_append(s.dm, s.h_ctx, s.offs_d, None, kv2, ws), "int4 prefill append")
+    torch.cuda.synchronize()
+    assert kv2.len.cpu().tolist() == s.lengths
+    worst = 0.0
+    for i in range(d.nl):
+        for b, L in enumerate(s.lengths):
+            ek = rel_err(kv2.k[i, b, :, :L].permute(1, 0, 2), s.ctx.k[i][b])
+            ev = rel_err(dense_v(kv2)[i, b, :, :, :L].permute(2, 0, 1), s.ctx.v[i][b])
+            worst = max(worst, ek, ev)
+            assert ek <= t and ev <= t, (i, b, ek, ev)
+            # the same rows through the GEMV path: equal but for bf16 ties of the K/V rounding
+            a = kv2.k[i, b, :, :L].float()
+            c = s.kv.k[i, b, :, :L].float()
+            assert float((a - c).abs().max()) <= t * float(c.abs().max()), (i, b)
+    log(f"[{name}] int4 prefill K/V ({n} rows, ws {ws.numel()} B): worst rel err {worst:.3e}")
+
+
 @pytest.mark.parametrize("name", ["gqa_bf16", "batched_small"])
 def test_kv_prefill_two_stages(name):
     """The matrix-core K/V append at non-zero cache lengths and with counts:

@@ -20,15 +20,20 @@ def test_traffic_scaling(tmp_path):
     copy = 1 << 20  # calibration kernel reads and writes 1 MiB
     fetch = tmp_path / "f.csv"
     write = tmp_path / "w.csv"
-    # the fill is not the calibration kernel: the last PyTorch dispatch before the target is
-    _counter_csv(fetch, "FETCH_SIZE", [("void at::native::fill", 0.0), ("void at::native::copy", 512.0),
-                                       ("void dfl::head", 100.0), ("void dfl::head", 102.0)])
-    _counter_csv(write, "WRITE_SIZE", [("void at::native::fill", 1024.0), ("void at::native::copy", 1024.0),
-                                       ("void dfl::head", 1.0), ("void dfl::head", 1.0)])
+    mul = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<float, float, float, MulFunctor>"
+    # the calibration copy is the last PyTorch multiply; the measured kernel's launches before it
+    # (a warm-up) and the fills after it do not count
+    _counter_csv(fetch, "FETCH_SIZE", [("void dfl::head", 50.0), ("void at::native::fill", 0.0), (mul, 512.0),
+                                       ("void at::native::fill", 3.0), ("void dfl::head", 100.0),
+                                       ("void dfl::head", 102.0)])
+    _counter_csv(write, "WRITE_SIZE", [("void dfl::head", 9.0), ("void at::native::fill", 1024.0), (mul, 1024.0),
+                                       ("void at::native::fill", 1.0), ("void dfl::head", 1.0),
+                                       ("void dfl::head", 1.0)])
     v = prof_report.traffic_summary(str(fetch), str(write), "dfl::head", copy, 200 * 1024)
     # fetch counter reads half the true bytes -> scale 2; write exact -> scale 1
     assert v["fetch scale"] == "2.00000" and v["write scale"] == "1.00000"
     assert int(v["bytes per launch"]) == (101.0 * 2 + 1.0) * 1024
+    assert v["launches"] == "2 (fetch pass), 2 (write pass)"
     assert v["kernel sources sha256[:16]"] == prof_report.kernel_sources_hash()
 
 
