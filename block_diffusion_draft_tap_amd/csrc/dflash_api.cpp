@@ -321,7 +321,9 @@ size_t skinny_part_bytes(const dflash_dims& d, int rows) {
     }
     int ns = 1, ks = 0;
     skinny_gated_split(2 * d.F, d.d, &ns, &ks);
-    const size_t g = ns > 1 ? (size_t)ns * r * 2 * d.F * 4 : 0;
+    size_t g = ns > 1 ? (size_t)ns * r * 2 * d.F * 4 : 0;
+    const size_t bal = skinny_gated_balanced_floats(r) * 4;  // the balanced gated launch's tail partials
+    if (bal > g) g = bal;
     return g > most ? g : most;
 }
 
@@ -652,10 +654,31 @@ hipError_t skinny_rows(int epi, SkinnyParams p, int rows, hipStream_t s) {
 hipError_t skinny_gated(SkinnyParams p, int rows, hipStream_t s) {
     int ns = 1, ks = p.K;
     skinny_gated_split(p.N, p.K, &ns, &ks);
-    if (ns <= 1) return skinny_rows(SK_GATED, p, rows, s);
     for (int r0 = 0; r0 < rows; r0 += kSkinnyRows) {
+        const int m = rows - r0 < kSkinnyRows ? rows - r0 : kSkinnyRows;
+        if (p.part && skinny_gated_balanced(m, p.N, p.K)) {
+            // 5+ row tiles and more column tiles than CUs: whole tiles spread over the CUs on
+            // the direct-to-LDS kernel, the remainder split in K (partials in p.part)
+            SkinnyParams q = p;
+            q.M = m;
+            q.a = p.a + (int64_t)r0 * p.a_ld;
+            q.out = static_cast<uint16_t*>(p.out) + (size_t)r0 * p.out_ld;
+            q.nblocks = skinny_tiles(SK_GATED, p.N);
+            const hipError_t e = launch_skinny_gated_balanced(q, s);
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        if (ns <= 1) {
+            SkinnyParams q = p;
+            q.M = m;
+            q.a = p.a + (int64_t)r0 * p.a_ld;
+            q.out = static_cast<uint16_t*>(p.out) + (size_t)r0 * p.out_ld;
+            const hipError_t e = skinny_rows(SK_GATED, q, m, s);
+            if (e != hipSuccess) return e;
+            continue;
+        }
         SkinnyParams q = p;
-        q.M = rows - r0 < kSkinnyRows ? rows - r0 : kSkinnyRows;
+        q.M = m;
         q.a = p.a + (int64_t)r0 * p.a_ld;
         q.nsplit = ns;
         q.kslice = ks;

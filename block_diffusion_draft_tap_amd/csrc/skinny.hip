@@ -433,9 +433,7 @@ __global__ __launch_bounds__(kST, 1) void skinny_dma_kernel(const SkinnyParams p
     const uint64_t t_start = trace_start(p.stamps);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int tile = blockIdx.x, split = blockIdx.y, z = blockIdx.z;
-    const int kbeg = split * p.kslice;
-    const int nc = (min(p.K, kbeg + p.kslice) - kbeg) / kSKC;
+    const int z = blockIdx.z;
     const uint16_t* W = p.w[0];
 #pragma unroll
     for (int q = 1; q < kMaxLayers; ++q)
@@ -451,81 +449,129 @@ __global__ __launch_bounds__(kST, 1) void skinny_dma_kernel(const SkinnyParams p
         }
     }
 
-    // weight rows: load s of fragment f gives lane (col, grp) row r = 4 s + grp of the
-    // fragment, piece col ^ r (LDS slot col of that row)
-    int jrow[kSNB];
-#pragma unroll
-    for (int f = 0; f < kSNB; ++f)
-        jrow[f] = EPI == SK_GATED ? tile * (kSCols / 2) + wave * 8 * kSNB + (f / 2) * 16 + grp
-                                  : tile * kSCols + wave * 16 * kSNB + f * 16 + grp;
-    const uint16_t* wbase = W + p.w_row0 * (int64_t)p.K + kbeg;
-    auto wrow = [&](int f, int s) {
-        if constexpr (EPI == SK_GATED) return (f & 1) * p.F + min(jrow[f] + 4 * s, p.F - 1);
-        return min(jrow[f] + 4 * s, p.N - 1);
-    };
-    auto load_w = [&](int c) {
-        const int st = c % D;
+    f32x4 acc[MT][kSNB];
+    // the products of one work item: column tile `tile` over chunks [kbeg, kbeg + 128 nc)
+    auto item = [&](const int tile, const int kbeg, const int nc) {
+        // weight rows: load s of fragment f gives lane (col, grp) row r = 4 s + grp of the
+        // fragment, piece col ^ r (LDS slot col of that row)
+        int jrow[kSNB];
 #pragma unroll
         for (int f = 0; f < kSNB; ++f)
-#pragma unroll
-            for (int s = 0; s < kSSteps; ++s) {
-                const int r = 4 * s + grp;
-                lds_dma16(wbase + (int64_t)wrow(f, s) * p.K + c * kSKC + 8 * (col ^ r), &Wst[wave][st][f][4 * s][0]);
-            }
-    };
-    // activations: LDS piece q = kST i + threadIdx.x of the tile is row q / 16, slot q % 16
-    auto load_a = [&](int c) {
-        const int k0 = kbeg + c * kSKC;
-        const uint16_t* src;
-        if (p.seg_k > 0) {  // tap segments: a chunk never straddles two
-            const int j = k0 / p.seg_k;
-            src = p.a_seg[0];
-#pragma unroll
-            for (int q = 1; q < kMaxTaps; ++q)
-                if (j == q) src = p.a_seg[q];
-            src += k0 - j * p.seg_k;
-        } else {
-            src = A + k0;
-        }
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int q = kST * i + (int)threadIdx.x;
-            const int row = q >> 4;
-            const int piece = (q & 15) ^ (row & 15);
-            lds_dma16(src + (int64_t)min(row, p.M - 1) * p.a_ld + 8 * piece, &As[c & 1][0][0] + (kST * i + 64 * wave) * 8);
-        }
-    };
-
-    f32x4 acc[MT][kSNB];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int f = 0; f < kSNB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    load_a(0);
-    load_w(0);
-    if (D == 3 && nc > 1) load_w(1);
-    for (int c = 0; c < nc; ++c) {
-        // this wavefront's loads after chunk c's activations: chunk c + 1's weights (D = 3)
-        dma_sync(D == 3 && c + 1 < nc);
-        if (c + 1 < nc) load_a(c + 1);          // into the buffer chunk c - 1 read
-        if (c + D - 1 < nc) load_w(c + D - 1);  // into the stage chunk c - 1 used
-        const int st = c % D, buf = c & 1;
-#pragma unroll
-        for (int s = 0; s < kSSteps; ++s) {
-            u32x4 wb[kSNB];
+            jrow[f] = EPI == SK_GATED ? tile * (kSCols / 2) + wave * 8 * kSNB + (f / 2) * 16 + grp
+                                      : tile * kSCols + wave * 16 * kSNB + f * 16 + grp;
+        const uint16_t* wbase = W + p.w_row0 * (int64_t)p.K + kbeg;
+        auto wrow = [&](int f, int s) {
+            if constexpr (EPI == SK_GATED) return (f & 1) * p.F + min(jrow[f] + 4 * s, p.F - 1);
+            return min(jrow[f] + 4 * s, p.N - 1);
+        };
+        auto load_w = [&](int c) {
+            const int st = c % D;
 #pragma unroll
             for (int f = 0; f < kSNB; ++f)
-                wb[f] = *reinterpret_cast<const u32x4*>(&Wst[wave][st][f][col][8 * ((4 * s + grp) ^ col)]);
+#pragma unroll
+                for (int s = 0; s < kSSteps; ++s) {
+                    const int r = 4 * s + grp;
+                    lds_dma16(wbase + (int64_t)wrow(f, s) * p.K + c * kSKC + 8 * (col ^ r), &Wst[wave][st][f][4 * s][0]);
+                }
+        };
+        // activations: LDS piece q = kST i + threadIdx.x of the tile is row q / 16, slot q % 16
+        auto load_a = [&](int c) {
+            const int k0 = kbeg + c * kSKC;
+            const uint16_t* src;
+            if (p.seg_k > 0) {  // tap segments: a chunk never straddles two
+                const int j = k0 / p.seg_k;
+                src = p.a_seg[0];
+#pragma unroll
+                for (int q = 1; q < kMaxTaps; ++q)
+                    if (j == q) src = p.a_seg[q];
+                src += k0 - j * p.seg_k;
+            } else {
+                src = A + k0;
+            }
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
-                const u32x4 af = *reinterpret_cast<const u32x4*>(&As[buf][i * 16 + col][8 * ((4 * s + grp) ^ col)]);
+                const int q = kST * i + (int)threadIdx.x;
+                const int row = q >> 4;
+                const int piece = (q & 15) ^ (row & 15);
+                lds_dma16(src + (int64_t)min(row, p.M - 1) * p.a_ld + 8 * piece,
+                          &As[c & 1][0][0] + (kST * i + 64 * wave) * 8);
+            }
+        };
+
 #pragma unroll
-                for (int f = 0; f < kSNB; ++f) acc[i][f] = mfma_bf16(af, wb[f], acc[i][f]);
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int f = 0; f < kSNB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        load_a(0);
+        load_w(0);
+        if (D == 3 && nc > 1) load_w(1);
+        for (int c = 0; c < nc; ++c) {
+            // this wavefront's loads after chunk c's activations: chunk c + 1's weights (D = 3)
+            dma_sync(D == 3 && c + 1 < nc);
+            if (c + 1 < nc) load_a(c + 1);          // into the buffer chunk c - 1 read
+            if (c + D - 1 < nc) load_w(c + D - 1);  // into the stage chunk c - 1 used
+            const int st = c % D, buf = c & 1;
+#pragma unroll
+            for (int s = 0; s < kSSteps; ++s) {
+                u32x4 wb[kSNB];
+#pragma unroll
+                for (int f = 0; f < kSNB; ++f)
+                    wb[f] = *reinterpret_cast<const u32x4*>(&Wst[wave][st][f][col][8 * ((4 * s + grp) ^ col)]);
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    const u32x4 af =
+                        *reinterpret_cast<const u32x4*>(&As[buf][i * 16 + col][8 * ((4 * s + grp) ^ col)]);
+#pragma unroll
+                    for (int f = 0; f < kSNB; ++f) acc[i][f] = mfma_bf16(af, wb[f], acc[i][f]);
+                }
             }
         }
-    }
+    };
 
+    if constexpr (EPI == SK_GATED) {
+        if (p.bal_main > 0) {
+            // balanced launch: whole tiles blockIdx.x, + gridDim.x, ... below bal_main, then at
+            // most one K range of a tail tile, whose partial sums of the gate and up rows go to
+            // bal_part [split][M][2 Ft] (gate columns [0, Ft), up [Ft, 2 Ft), Ft the tail's
+            // gate rows) for the gated reduce. Before each item after the first, every
+            // wavefront's reads of the LDS tiles end (the next item's loads refill them).
+            bool first = true;
+            for (int t = blockIdx.x; t < p.bal_main; t += gridDim.x) {
+                if (!first) dma_sync(false);
+                first = false;
+                item(t, 0, p.K / kSKC);
+                skinny_epilogue<MT, EPI>(p, acc, t, 0, z, wave, col, grp, &red_v[0][0], &red_i[0][0], meta_b,
+                                         meta_pos);
+            }
+            const int q = blockIdx.x;
+            if (q < p.bal_items) {
+                if (!first) dma_sync(false);
+                const int t = p.bal_main + q / p.bal_splits, sp = q % p.bal_splits;
+                const int kb = sp * p.bal_kslice;
+                item(t, kb, (min(p.K, kb + p.bal_kslice) - kb) / kSKC);
+                const int j0 = p.bal_main * (kSCols / 2), Ft = p.F - j0;
+                float* part = p.bal_part + (int64_t)sp * p.M * 2 * Ft;
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = i * 16 + 4 * grp + e;
+                        if (m >= p.M) continue;
+#pragma unroll
+                        for (int f = 0; f < kSNB; ++f) {
+                            const int j = t * (kSCols / 2) + wave * 8 * kSNB + (f / 2) * 16 + col;
+                            if (j < p.F) part[(int64_t)m * 2 * Ft + (f & 1) * Ft + (j - j0)] = acc[i][f][e];
+                        }
+                    }
+            }
+            trace_end(p.stamps, t_start);
+            return;
+        }
+    }
+    const int tile = blockIdx.x, split = blockIdx.y;
+    const int kbeg = split * p.kslice;
+    item(tile, kbeg, (min(p.K, kbeg + p.kslice) - kbeg) / kSKC);
     skinny_epilogue<MT, EPI>(p, acc, tile, split, z, wave, col, grp, &red_v[0][0], &red_i[0][0], meta_b, meta_pos);
     trace_end(p.stamps, t_start);
 }
@@ -776,6 +822,81 @@ hipError_t launch_epi(const SkinnyParams& p, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+// The gated product balanced over the CUs on the direct-to-LDS kernel (one workgroup per
+// CU): with T column tiles and G CUs, each workgroup takes T / G whole tiles and the rest
+// (T mod G tiles) is split into K ranges of nearly equal length, at most one per workgroup,
+// whose partial sums the gated reduce adds in range order. A plain launch of T > G tiles at
+// one workgroup per CU would take a second full round of the chip for the last T mod G.
+constexpr int kMaxCus = 512;  // bound of the tail partials' size (devices up to this many CUs)
+
+int device_cus() {
+    static int cus[16] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 256;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n < kMaxCus ? n : kMaxCus;
+    }
+    return cus[dev];
+}
+
+struct GatedPlan {
+    int main, rem, splits, kslice, items;
+};
+
+bool gated_plan(int M, int N2, int K, GatedPlan* g) {
+    const int MT = (M + 15) / 16;
+    if (MT < DFL_SK_DMA_MIN_MT || MT > 8 || (N2 % 8) || (K % kSKC)) return false;
+    const int F = N2 / 2, T = skinny_tiles(SK_GATED, N2), G = device_cus(), nc = K / kSKC;
+    if (T <= G || (F % 4)) return false;
+    g->main = (T / G) * G;
+    g->rem = T - g->main;
+    g->splits = 0;
+    g->kslice = K;
+    g->items = 0;
+    if (g->rem > 0) {
+        int kch = (nc * g->rem + G - 1) / G;
+        while (g->rem * ((nc + kch - 1) / kch) > G) ++kch;
+        g->splits = (nc + kch - 1) / kch;
+        g->kslice = kch * kSKC;
+        g->items = g->rem * g->splits;
+    }
+    return true;
+}
+
+template <int MT>
+hipError_t launch_gated_balanced(SkinnyParams q, const GatedPlan& g, hipStream_t s) {
+    q.bal_main = g.main;
+    q.bal_items = g.items;
+    q.bal_splits = g.splits > 0 ? g.splits : 1;
+    q.bal_kslice = g.kslice;
+    q.bal_part = q.part;
+    q.nsplit = 1;
+    q.kslice = q.K;
+    const int G = device_cus();
+    const dim3 grid((unsigned)G, 1, 1);
+    char name[48];
+    snprintf(name, sizeof name, "skinny_dma_kernel<%d, %d>", MT, SK_GATED);
+    const double bytes = (double)q.N * q.K * 2.0 + (double)q.M * q.K * 2.0 + (double)q.M * (q.N / 2) * 2.0;
+    q.stamps = trace_launch(TRACE_PROJECTIONS, name, G, bytes, 0.0);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((skinny_dma_kernel<MT, SK_GATED>), grid, dim3(kST), 0, s, q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || g.items == 0) return e;
+    // the tail's gate and up partial sums, added in range order, then the activation
+    const int j0 = g.main * (kSCols / 2), Ft = q.F - j0;
+    SkinnyParams r = q;
+    r.N = Ft;
+    r.part = q.bal_part;
+    r.nsplit = g.splits;
+    r.out = static_cast<uint16_t*>(q.out) + j0;
+    r.layers = 1;
+    const int64_t blocks = ((int64_t)r.M * r.N / 4 + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL((skinny_reduce_kernel<SK_GATED>), dim3((unsigned)blocks, 1), dim3(kBlock), 0, s, r);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int skinny_tiles(int epi, int N) {
@@ -793,6 +914,26 @@ void skinny_split(int epi, int N, int K, int layers, int* nsplit, int* kslice) {
     const int per = chunks > 0 ? (chunks + s - 1) / s : 1;
     *kslice = per * kSKC;
     *nsplit = chunks > 0 ? (chunks + per - 1) / per : 1;
+}
+
+size_t skinny_gated_balanced_floats(int M) { return (size_t)M * 2 * (kSCols / 2) * kMaxCus; }
+
+bool skinny_gated_balanced(int M, int N, int K) {
+    GatedPlan g;
+    return gated_plan(M, N, K, &g);
+}
+
+hipError_t launch_skinny_gated_balanced(const SkinnyParams& p, hipStream_t s) {
+    GatedPlan g;
+    if (p.layers != 1 || p.F * 2 != p.N || !p.part || !p.out || !gated_plan(p.M, p.N, p.K, &g))
+        return hipErrorInvalidValue;
+    switch ((p.M + 15) / 16) {
+        case 5: return launch_gated_balanced<5>(p, g, s);
+        case 6: return launch_gated_balanced<6>(p, g, s);
+        case 7: return launch_gated_balanced<7>(p, g, s);
+        case 8: return launch_gated_balanced<8>(p, g, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_skinny(int epi, const SkinnyParams& p, hipStream_t s) {

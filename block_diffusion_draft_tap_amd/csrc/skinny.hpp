@@ -39,6 +39,12 @@ struct SkinnyParams {
     // split order and applies the epilogue, for SK_PARTIAL the caller consumes them
     int nsplit, kslice;
     float* part;
+    // SK_GATED on the direct-to-LDS kernel, balanced over the CUs (bal_main > 0): whole
+    // tiles [0, bal_main) spread evenly over the workgroups, the remaining tiles split into
+    // bal_items K ranges of bal_kslice (bal_splits per tile, at most one per workgroup) whose
+    // partial sums go to bal_part [bal_splits][M][2 (F - bal_main 64)] (gate then up)
+    int bal_main, bal_items, bal_splits, bal_kslice;
+    float* bal_part;
     // SK_STORE: out[m, n] = y, fp32 or (out_bf16) bf16; with vt, bf16 columns n >= vt_col go
     //   head-dim major to vt[b][head][dim][32], b = (row_base + m) / gamma, key = its remainder
     // SK_RESID: out[m, n] += y (fp32)
@@ -77,6 +83,15 @@ void skinny_split(int epi, int N, int K, int layers, int* nsplit, int* kslice);
 // the functions above (part holds layers * nsplit * M * N floats when nsplit > 1 or
 // for SK_PARTIAL)
 hipError_t launch_skinny(int epi, const SkinnyParams& p, hipStream_t s);
+
+// The gated product (N = 2F, one layer) balanced over the CUs on the direct-to-LDS kernel:
+// whole column tiles spread evenly, the remaining tiles split into K ranges at most one per
+// workgroup, their partial sums in part (at most skinny_gated_balanced_floats(M) floats)
+// added in range order by the gated reduce. skinny_gated_balanced says whether a launch of
+// M rows over N x K takes this path (5 to 8 row tiles, more column tiles than CUs).
+bool skinny_gated_balanced(int M, int N, int K);
+size_t skinny_gated_balanced_floats(int M);
+hipError_t launch_skinny_gated_balanced(const SkinnyParams& p, hipStream_t s);
 
 // The split-K sum and epilogue alone (SK_STORE / SK_RESID / SK_GATED, one layer; SK_KV,
 // p.layers layers of partials [layers][nsplit][M][N] into bf16 caches): adds the nsplit

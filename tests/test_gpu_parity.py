@@ -62,6 +62,9 @@ BATCHED_SMALL = scaled(BATCHED, name="batched_small", H=256, m=2, d=256, hq=4, h
 # fragments, ragged) and 20 x 7 = 140 rows (a launch of 128 rows and one of 12)
 BATCHED_R21 = scaled(BATCHED_SMALL, name="batched_r21", B=3, L=150, L_max=150)
 BATCHED_R140 = scaled(BATCHED_SMALL, name="batched_r140", B=20, V=3001, L=40, L_max=120)
+# the gated product of 112 block rows over more column tiles than the GPU has CUs (17408
+# gate/up pairs: 272 tiles), which runs balanced over the CUs with a split tail
+BATCHED_FFN = scaled(BATCHED_SMALL, name="batched_ffn", F=17408, nl=1)
 
 # 35 query rows per kv head over many long sequences (64 x 2 kv heads, ~2100 keys: more
 # key units in all than the row-split attention kernel takes, so the kernel whose
@@ -103,6 +106,7 @@ CASES = {
     "batched_small": (BATCHED_SMALL, [int(x) for x in gen.context_lengths(BATCHED_SMALL)]),
     "batched_r21": (BATCHED_R21, [150, 33, 97]),
     "batched_r140": (BATCHED_R140, [int(x) for x in gen.context_lengths(BATCHED_R140)]),
+    "batched_ffn": (BATCHED_FFN, [int(x) for x in gen.context_lengths(BATCHED_FFN)]),
     "rows35_many": (ROWS35_MANY, [int(x) for x in gen.context_lengths(ROWS35_MANY)]),
     "gamma1": (GAMMA1, [200, 77]),
     "empty_ctx": (EMPTY_CTX, [0, 45, 0]),
