@@ -255,8 +255,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     // its V once the value products are, so they land during the softmax and products
     // instead of after them, with no second register set.
     const int kq = 8 * (col >> 2) + (col & 3);
-    u32x4 kb[2][KS], vb[DT];
-    auto load_k = [&](const int u) {
+    auto load_k = [&](const int u, u32x4 (&kb)[2][KS]) {
         const uint16_t *k0, *k1;
         if (u != nch) {
             k0 = kc + (int64_t)(cb + u * kChunk + kq) * HD + 8 * grp;
@@ -271,23 +270,20 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
             kb[1][ks] = *reinterpret_cast<const u32x4*>(k1 + ks * 32);
         }
     };
-    auto load_v = [&](const int u) {
+    auto load_v = [&](const int u, u32x4 (&vb)[DT]) {
         const uint16_t* vp;
-        int64_t vstride;
-        if (u != nch) {
+        if (u != nch)
             vp = vc + ((int64_t)(cb / kChunk + u) * HD + col) * kChunk + 8 * grp;
-            vstride = 16 * kChunk;
-        } else {
+        else
             vp = vblk + col * kChunk + 8 * grp;
-            vstride = 16 * kChunk;
-        }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vb[dt] = *reinterpret_cast<const u32x4*>(vp + dt * vstride);
+        for (int dt = 0; dt < DT; ++dt) vb[dt] = *reinterpret_cast<const u32x4*>(vp + dt * 16 * kChunk);
     };
+    u32x4 kA[2][KS], vA[DT];
     // the first unit's loads go out together with Q's
     if (u_begin < u_end) {
-        load_k(u_begin);
-        load_v(u_begin);
+        load_k(u_begin, kA);
+        load_v(u_begin, vA);
     }
 
     // Q tiles as B operands: query row rt*16 + col, dims ks*32 + 8*grp ..; rows past R
@@ -312,7 +308,9 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         l[rt] = 0.f;
     }
 
-    for (int u = u_begin; u < u_end; ++u) {
+    // one unit from register set (kb, vb); the set's K then V are reloaded with unit `next`
+    // (if `reload`) as soon as the products that read them are issued
+    auto unit = [&](const int u, u32x4 (&kb)[2][KS], u32x4 (&vb)[DT], const int next, const bool reload) {
         const int nvalid = (u == nch) ? p.gamma : min(kChunk, lenb - cb - u * kChunk);
         // keys of the first chunk before the window's first key take no weight (they are
         // held context rows: their values are finite and meet zero probabilities)
@@ -327,7 +325,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) sacc[rt][nt] = mfma16(kb[nt][ks], qa[rt][ks], sacc[rt][nt]);
             }
-        if (u + 1 < u_end) load_k(u + 1);
+        if (reload) load_k(next, kb);
         const bool ragged = lo > 0 || nvalid < kChunk;
         const bool rescale = (u != u_begin);  // o is still zero on a wavefront's first unit
         u32x4 ph[NRT], pl[NRT];
@@ -339,8 +337,9 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) o[rt][dt] = mfma16(vb[dt], pl[rt], mfma16(vb[dt], ph[rt], o[rt][dt]));
-        if (u + 1 < u_end) load_v(u + 1);
-    }
+        if (reload) load_v(next, vb);
+    };
+    for (int u = u_begin; u < u_end; ++u) unit(u, kA, vA, u + 1, u + 1 < u_end);
 
     // merge the four wavefronts in LDS: each writes its o rows; the per-row weights
     // exp2(m_w - M) and sums L are formed once; then each thread adds the four

@@ -65,6 +65,10 @@ BATCHED_R140 = scaled(BATCHED_SMALL, name="batched_r140", B=20, V=3001, L=40, L_
 # the gated product of 112 block rows over more column tiles than the GPU has CUs (17408
 # gate/up pairs: 272 tiles), which runs balanced over the CUs with a split tail
 BATCHED_FFN = scaled(BATCHED_SMALL, name="batched_ffn", F=17408, nl=1)
+# 5 and 6 row tiles of block rows (10 x 7 = 70, 12 x 7 = 84): the direct-to-LDS projections'
+# other instantiations
+BATCHED_R70 = scaled(BATCHED_SMALL, name="batched_r70", B=10, L=60, L_max=90)
+BATCHED_R84 = scaled(BATCHED_SMALL, name="batched_r84", B=12, L=60, L_max=90)
 
 # 35 query rows per kv head over many long sequences (64 x 2 kv heads, ~2100 keys: more
 # key units in all than the row-split attention kernel takes, so the kernel whose
@@ -107,6 +111,8 @@ CASES = {
     "batched_r21": (BATCHED_R21, [150, 33, 97]),
     "batched_r140": (BATCHED_R140, [int(x) for x in gen.context_lengths(BATCHED_R140)]),
     "batched_ffn": (BATCHED_FFN, [int(x) for x in gen.context_lengths(BATCHED_FFN)]),
+    "batched_r70": (BATCHED_R70, [int(x) for x in gen.context_lengths(BATCHED_R70)]),
+    "batched_r84": (BATCHED_R84, [int(x) for x in gen.context_lengths(BATCHED_R84)]),
     "rows35_many": (ROWS35_MANY, [int(x) for x in gen.context_lengths(ROWS35_MANY)]),
     "gamma1": (GAMMA1, [200, 77]),
     "empty_ctx": (EMPTY_CTX, [0, 45, 0]),
