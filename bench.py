@@ -683,6 +683,8 @@ def main():
                                     for k in table[:8]]
         traced = sum(k["us_per_round"] for k in table)
         res["traced_ms_per_step"] = round(traced_ms / args.steps, 5)
+        res["wall_clock_hz"] = {"measured": round(bd.dflash_wall_clock_hz(), 1),
+                                "runtime_reported": round(bd.dflash_wall_clock_hz_reported(), 1)}
         res["traced_share_of_round"] = round(traced / (traced_ms / args.steps * 1e3), 4)
     res["prefill"] = pre
     res["wall_s_timed"] = round(wall, 4)

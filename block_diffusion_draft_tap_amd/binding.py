@@ -26,7 +26,7 @@ EXPORTS = ["dflash_workspace_bytes", "dflash_query", "dflash_status_string", "df
            "dflash_context_project", "dflash_ctx_kv_append", "dflash_draft_layer", "dflash_draft_forward",
            "dflash_lm_head_argmax", "dflash_lm_head_workspace_bytes", "dflash_verify_greedy",
            "dflash_verify_workspace_bytes", "dflash_kv_prefill_workspace_bytes", "dflash_trace_begin",
-           "dflash_trace_end", "dflash_lm_head_workgroups", "dflash_wall_clock_hz", "dflash_verify_greedy_noalloc",
+           "dflash_trace_end", "dflash_lm_head_workgroups", "dflash_wall_clock_hz", "dflash_wall_clock_hz_reported", "dflash_verify_greedy_noalloc",
            "dflash_verify_noalloc_max_bytes", "dflash_dspark_workspace_bytes", "dflash_draft_forward_dspark",
            "dflash_verify_greedy_lengths", "dflash_draft_round", "dflash_round_workspace_bytes",
            "dflash_verify_from_hidden", "dflash_verify_hidden_workspace_bytes", "dflash_lm_head_workspace_bytes_for",
@@ -143,6 +143,8 @@ def _load():
     lib.dflash_lm_head_workgroups.restype = ctypes.c_int32
     lib.dflash_wall_clock_hz.argtypes = []
     lib.dflash_wall_clock_hz.restype = ctypes.c_double
+    lib.dflash_wall_clock_hz_reported.argtypes = []
+    lib.dflash_wall_clock_hz_reported.restype = ctypes.c_double
     return lib
 
 
@@ -521,6 +523,10 @@ def dflash_lm_head_workgroups(V, H, dtype, M, y_dtype=None):
 
 def dflash_wall_clock_hz():
     return lib.dflash_wall_clock_hz()
+
+
+def dflash_wall_clock_hz_reported():
+    return lib.dflash_wall_clock_hz_reported()
 
 
 def traced_durations_s(stamps, records):

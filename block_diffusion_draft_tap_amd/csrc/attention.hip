@@ -862,9 +862,10 @@ __global__ __launch_bounds__(kBlock) void attn_valu_kernel(const AttnParams p) {
 // One wavefront per (b, head, block row), four rows per workgroup, no barriers:
 // combine the nparts partials (o, m, l) of the row. The (m, l) of the first 64
 // partials (one per lane) and the values of the first MR go out in one batch, so
-// up to MR partials cost one round trip (MR = 32 up to 32 partials, else 64: the
-// wider batch measured slower where fewer partials suffice). M = max m_s, weights
-// w_s = exp(m_s - M) (lane s, read back uniformly), L = sum w_s l_s, and each lane
+// up to MR partials cost one round trip (MR = 8, 32 or 64, the smallest that holds
+// the partials: a wider batch issues loads of clamped indexes whose values go
+// unused). M = max m_s, weights w_s = exp(m_s - M) (lane s, read back uniformly),
+// L = sum w_s l_s, and each lane
 // sums its HD/64 head-dim columns over the partials in order s = 0, 1, ...
 template <int HD, int MR>
 __global__ __launch_bounds__(kBlock) void attn_merge_kernel(const AttnParams p) {
@@ -1081,7 +1082,9 @@ static hipError_t launch_hd(const AttnParams& p, hipStream_t s) {
     }
 merge:
     const dim3 mgrid((unsigned)((p.B * p.hq * p.gamma + 3) / 4));
-    if (p.nparts <= 32)
+    if (p.nparts <= 8)
+        hipLaunchKernelGGL((attn_merge_kernel<HD, 8>), mgrid, dim3(kBlock), 0, s, p);
+    else if (p.nparts <= 32)
         hipLaunchKernelGGL((attn_merge_kernel<HD, 32>), mgrid, dim3(kBlock), 0, s, p);
     else
         hipLaunchKernelGGL((attn_merge_kernel<HD, 64>), mgrid, dim3(kBlock), 0, s, p);

@@ -1,10 +1,12 @@
 // C ABI of libdflash.so (declared in include/dflash.h): argument validation on
 // the host, workspace layout, and the kernel sequence of each call.
 #include <atomic>
+#include <chrono>
 #include <cstdlib>
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <thread>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -1361,7 +1363,35 @@ int32_t dflash_lm_head_workgroups(int32_t V, int32_t H, int32_t dtype, int32_t M
     return lm_nblocks(V, H, wtype_of(dtype), M < 8 ? M : 8);
 }
 
+// The rate is measured: two readings of the device clock 100 ms apart on the host's steady
+// clock (the runtime's reported rate has disagreed with the counter on some devices). Once
+// per device and process; the readings run on the null stream and synchronise the device.
 double dflash_wall_clock_hz(void) {
+    static std::mutex mu;
+    static double rate[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0.0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (rate[dev] > 0.0) return rate[dev];
+    uint64_t* buf = nullptr;
+    if (hipMalloc(&buf, 2 * sizeof(uint64_t)) != hipSuccess) return 0.0;
+    uint64_t ticks[2] = {0, 0};
+    double secs = 0.0;
+    bool ok = launch_wall_clock(buf, nullptr) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+    const auto t0 = std::chrono::steady_clock::now();
+    if (ok) {
+        std::this_thread::sleep_for(std::chrono::milliseconds(100));
+        secs = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+        ok = launch_wall_clock(buf + 1, nullptr) == hipSuccess && hipDeviceSynchronize() == hipSuccess &&
+             hipMemcpy(ticks, buf, sizeof(ticks), hipMemcpyDeviceToHost) == hipSuccess;
+    }
+    (void)hipFree(buf);
+    if (!ok || ticks[1] <= ticks[0] || secs <= 0.0) return 0.0;
+    rate[dev] = (double)(ticks[1] - ticks[0]) / secs;
+    return rate[dev];
+}
+
+double dflash_wall_clock_hz_reported(void) {
     int dev = 0, khz = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0.0;
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0.0;

@@ -6,7 +6,7 @@
 //   dspark_step_kernel    one step of the DSpark greedy loop (previous token, Markov operand,
 //                         confidence, pruning length)
 //   rownorm_kernel        RMSNorm of fp32 rows (sum of split partials) with a gain (Eq 2)
-//   rownorm1_kernel       the same for rows from a single source, read once
+//   rownorm1_kernel       the same on 16-byte chunks (rows of a multiple of 4 values)
 //   gather_rows_kernel    bf16 table rows by id (the anchors' embeddings)
 //   block_fill_kernel     block rows around a stored anchor product (Eq 3 block init)
 //   advance_len_kernel    len[b] += appended rows (retained context grows)
@@ -231,12 +231,15 @@ __global__ __launch_bounds__(kBlock) void rownorm_kernel(const float* src, int n
     }
 }
 
-// single-source rows (no split partials): each 16-byte chunk of the row is read once into
-// registers, the sum of squares reduced across the workgroup, then scaled and written
-// (in place when src == dst: every thread writes only the chunks it read)
+// rows of 16-byte-aligned chunks: each chunk of the row is the sum of the split partials
+// in split order (one partial: the row itself), read into registers (the splits in
+// batches of kZB, every load of a batch issued before the first add), the sum of squares
+// reduced across the workgroup while the gains load, then scaled and written (in place
+// when src == dst and nsplit == 1: every thread writes only the chunks it read)
 template <int KP4>
-__global__ __launch_bounds__(kBlock) void rownorm1_kernel(const float* src, float* dst, int d, const void* gain,
-                                                          int gain_f32, float eps) {
+__global__ __launch_bounds__(kBlock) void rownorm1_kernel(const float* src, int nsplit, int64_t split_stride,
+                                                          float* dst, int d, const void* gain, int gain_f32,
+                                                          float eps) {
     __shared__ float sv[4];
     const int64_t roff = (int64_t)blockIdx.x * d;
     const int tid = threadIdx.x, n4 = d / 4;
@@ -244,10 +247,38 @@ __global__ __launch_bounds__(kBlock) void rownorm1_kernel(const float* src, floa
 #pragma unroll
     for (int j = 0; j < KP4; ++j)
         v[j] = *reinterpret_cast<const f32x4*>(src + roff + 4 * min(tid + j * kBlock, n4 - 1));
-    float s = 0.f;
+    for (int z0 = 1; z0 < nsplit; z0 += kZB) {
+        f32x4 t[kZB][KP4];
 #pragma unroll
-    for (int j = 0; j < KP4; ++j)
+        for (int zb = 0; zb < kZB; ++zb) {
+            const int64_t zo = (int64_t)min(z0 + zb, nsplit - 1) * split_stride + roff;
+#pragma unroll
+            for (int j = 0; j < KP4; ++j)
+                t[zb][j] = *reinterpret_cast<const f32x4*>(src + zo + 4 * min(tid + j * kBlock, n4 - 1));
+        }
+#pragma unroll
+        for (int zb = 0; zb < kZB; ++zb)
+            if (z0 + zb < nsplit) {
+#pragma unroll
+                for (int j = 0; j < KP4; ++j) {
+                    v[j].x += t[zb][j].x;
+                    v[j].y += t[zb][j].y;
+                    v[j].z += t[zb][j].z;
+                    v[j].w += t[zb][j].w;
+                }
+            }
+    }
+    float s = 0.f;
+    f32x4 g[KP4];
+#pragma unroll
+    for (int j = 0; j < KP4; ++j) {
+        const int k = 4 * min(tid + j * kBlock, n4 - 1);
+        g[j].x = load_gain(gain, gain_f32, k);
+        g[j].y = load_gain(gain, gain_f32, k + 1);
+        g[j].z = load_gain(gain, gain_f32, k + 2);
+        g[j].w = load_gain(gain, gain_f32, k + 3);
         if (tid + j * kBlock < n4) s += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    }
     s = wave_sum(s);
     if ((tid & 63) == 0) sv[tid >> 6] = s;
     __syncthreads();
@@ -257,13 +288,12 @@ __global__ __launch_bounds__(kBlock) void rownorm1_kernel(const float* src, floa
     for (int j = 0; j < KP4; ++j) {
         const int q = tid + j * kBlock;
         if (q < n4) {
-            const int k = 4 * q;
             f32x4 o;
-            o.x = v[j].x * r * load_gain(gain, gain_f32, k);
-            o.y = v[j].y * r * load_gain(gain, gain_f32, k + 1);
-            o.z = v[j].z * r * load_gain(gain, gain_f32, k + 2);
-            o.w = v[j].w * r * load_gain(gain, gain_f32, k + 3);
-            *reinterpret_cast<f32x4*>(dst + roff + k) = o;
+            o.x = v[j].x * r * g[j].x;
+            o.y = v[j].y * r * g[j].y;
+            o.z = v[j].z * r * g[j].z;
+            o.w = v[j].w * r * g[j].w;
+            *reinterpret_cast<f32x4*>(dst + roff + 4 * q) = o;
         }
     }
 }
@@ -291,6 +321,11 @@ __global__ __launch_bounds__(kBlock) void block_fill_kernel(float* h, int gamma,
         row[n] += load_gain(block_pos, gain_f32, n);
     else
         row[n] = load_gain(mask_emb, gain_f32, (k - 1) * d + n) + load_gain(block_pos, gain_f32, k * d + n);
+}
+
+// one reading of the device wall clock (the tick counter of the launch stamps)
+__global__ void wall_clock_kernel(uint64_t* out) {
+    if (threadIdx.x == 0) out[0] = (uint64_t)wall_clock64();
 }
 
 __global__ void advance_len_kernel(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap,
@@ -356,17 +391,22 @@ hipError_t launch_verify_ids(const int32_t* tids, const int32_t* draft, int B, i
 hipError_t launch_rownorm(const float* src, int nsplit, int64_t split_stride, float* dst, int rows, int d,
                           const void* gain, int gain_f32, float eps, hipStream_t s) {
     (void)hipGetLastError();  // report only this launch's status
-    const bool vec = nsplit == 1 && d % 4 == 0 && ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+    // in place only without partials (rows are read whole before they are written)
+    const bool vec = d % 4 == 0 && (nsplit == 1 || (split_stride % 4 == 0 && src != dst)) &&
+                     ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
     if (vec && d <= 4 * kBlock) {
-        hipLaunchKernelGGL(rownorm1_kernel<1>, dim3(rows), dim3(kBlock), 0, s, src, dst, d, gain, gain_f32, eps);
+        hipLaunchKernelGGL(rownorm1_kernel<1>, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
+                           gain_f32, eps);
         return hipGetLastError();
     }
     if (vec && d <= 8 * kBlock) {
-        hipLaunchKernelGGL(rownorm1_kernel<2>, dim3(rows), dim3(kBlock), 0, s, src, dst, d, gain, gain_f32, eps);
+        hipLaunchKernelGGL(rownorm1_kernel<2>, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
+                           gain_f32, eps);
         return hipGetLastError();
     }
     if (vec && d <= 32 * kBlock) {
-        hipLaunchKernelGGL(rownorm1_kernel<8>, dim3(rows), dim3(kBlock), 0, s, src, dst, d, gain, gain_f32, eps);
+        hipLaunchKernelGGL(rownorm1_kernel<8>, dim3(rows), dim3(kBlock), 0, s, src, nsplit, split_stride, dst, d, gain,
+                           gain_f32, eps);
         return hipGetLastError();
     }
     if (d <= 4 * kBlock)
@@ -398,6 +438,12 @@ hipError_t launch_block_fill(float* h, int B, int gamma, int d, const void* bloc
     (void)hipGetLastError();  // report only this launch's status
     hipLaunchKernelGGL(block_fill_kernel, dim3((unsigned)((d + kBlock - 1) / kBlock), (unsigned)B, (unsigned)gamma),
                        dim3(kBlock), 0, s, h, gamma, d, block_pos, mask_emb, gain_f32);
+    return hipGetLastError();
+}
+
+hipError_t launch_wall_clock(uint64_t* out, hipStream_t s) {
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL(wall_clock_kernel, dim3(1), dim3(64), 0, s, out);
     return hipGetLastError();
 }
 

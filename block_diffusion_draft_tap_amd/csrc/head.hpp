@@ -45,6 +45,8 @@ hipError_t launch_gather_rows(const uint16_t* table, int table_rows, const int32
 hipError_t launch_block_fill(float* h, int B, int gamma, int d, const void* block_pos, const void* mask_emb,
                              int gain_f32, hipStream_t s);
 // len[b] += the appended rows of b (capped at cap); with save, the lengths before go to save[b]
+// out[0] = the device wall clock (one workgroup)
+hipError_t launch_wall_clock(uint64_t* out, hipStream_t s);
 hipError_t launch_advance_len(int32_t* len, const int32_t* row_offsets, const int32_t* counts, int B, int cap,
                               hipStream_t s, int32_t* save = nullptr);
 hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);

@@ -224,9 +224,15 @@ int32_t dflash_trace_end(dflash_trace_record* records, int32_t capacity);
  * arguments (launches may be NULL). */
 int32_t dflash_lm_head_workgroups(int32_t V, int32_t H, int32_t dtype, int32_t M, int32_t y_dtype, int32_t* launches);
 
-/* Tick rate of the wall clock the stamps use, for the current device, in Hz
- * (0 when the runtime cannot report it). */
+/* Tick rate of the wall clock the stamps use, for the current device, in Hz:
+ * measured on the first call per device (two readings of the device clock
+ * about 100 ms apart on the host's steady clock; the call allocates 16 bytes
+ * of device memory for it, synchronises the device and sleeps), then cached;
+ * 0 on failure. Not to be called while a stream is being captured. */
 double dflash_wall_clock_hz(void);
+/* The rate the runtime reports for that clock (hipDeviceAttributeWallClockRate),
+ * in Hz, 0 when it reports none; for comparison with the measured rate. */
+double dflash_wall_clock_hz_reported(void);
 
 /* Eq 2 (page 3, #buildContext): h_ctx[r] = RMSNorm(sum_j T_j[r] W_c[:, jH:(j+1)H]^T; ctx_norm).
  *   taps:   HOST array of m device pointers; tap j is [n, H] with row stride
