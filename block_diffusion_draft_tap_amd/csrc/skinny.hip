@@ -420,13 +420,52 @@ __device__ __forceinline__ void dma_sync(const bool keep8) {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The 64-wide pipeline (DFL_SK_DMA_K64, for row tiles where the 128-wide one fits only two
+// weight stages: 128 rows): K chunks of 64, four activation buffers and five weight stages,
+// so a chunk's activations load three chunks ahead and its weights four (1.5 and 2 chunks
+// of 128; measured at 128 rows 51.0 -> 47.7 us per context launch, at 112 rows, where the
+// 128-wide pipeline keeps three weight stages, 25.6 -> 26.8 us per projection). Rows
+// of 64 hold 8 pieces of 16 bytes, piece p of row r at slot p ^ ((r >> 1) & 7): a fragment
+// read (16 rows, one piece each) touches every bank once. A chunk's activation pieces are
+// padded to whole instructions (the padding lanes write slots past the tile, from clamped
+// sources), so every wavefront issues the same loads.
+#ifndef DFL_SK_DMA_K64
+#define DFL_SK_DMA_K64 1
+#endif
+constexpr int kDK = 64, kDA64 = 4, kDW64 = 5;
+template <int MT>
+constexpr int k64_nai() {  // activation loads per thread per chunk
+    return (MT * 16 * (kDK / 8) + kST - 1) / kST;
+}
+
+// chunk c may start (64-wide pipeline): this wavefront's loads other than the last keep
+// landed, its LDS reads done, then the workgroup barrier; keep is one of four values known
+// at compile time (three, two, one or no later chunks issued)
+template <int K3, int K2, int K1>
+__device__ __forceinline__ void dma_sync64(const int later) {
+    if (later >= 3)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(K3) : "memory");
+    else if (later == 2)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(K2) : "memory");
+    else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(K1) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int MT, int EPI>
 __global__ __launch_bounds__(kST, 1) void skinny_dma_kernel(const SkinnyParams p) {
     constexpr int RED = EPI == SK_ARGMAX ? MT * 16 : 1;
     constexpr int META = EPI == SK_KV ? MT * 16 : 1;
     constexpr int D = dma_stages<MT>();
-    __shared__ __align__(16) uint16_t As[2][MT * 16][kSKC];         // activation chunk, double buffered
-    __shared__ __align__(16) uint16_t Wst[kSW][D][kSNB][16][kSKC];  // each wavefront's weight stages
+    constexpr bool K64 = DFL_SK_DMA_K64 && D < 3;
+    constexpr int NAI = k64_nai<MT>();
+    // 128-wide pipeline: activation chunk double buffered, each wavefront's weight stages
+    __shared__ __align__(16) uint16_t As[K64 ? 1 : 2][K64 ? 1 : MT * 16][K64 ? 8 : kSKC];
+    __shared__ __align__(16) uint16_t Wst[K64 ? 1 : kSW][K64 ? 1 : D][kSNB][16][K64 ? 8 : kSKC];
+    // 64-wide pipeline: activation buffers (NAI * kST pieces each) and weight stages
+    __shared__ __align__(16) uint16_t As64[K64 ? kDA64 : 1][K64 ? NAI * kST * 8 : 8];
+    __shared__ __align__(16) uint16_t Wst64[K64 ? kSW : 1][K64 ? kDW64 : 1][kSNB][16][K64 ? kDK : 8];
     __shared__ float red_v[kSW][RED];
     __shared__ int red_i[kSW][RED];
     __shared__ int meta_b[META], meta_pos[META];
@@ -450,8 +489,100 @@ __global__ __launch_bounds__(kST, 1) void skinny_dma_kernel(const SkinnyParams p
     }
 
     f32x4 acc[MT][kSNB];
+    // 64-wide pipeline: the products of column tile `tile` over K [kbeg, kbeg + 64 nc)
+    auto item64 = [&](const int tile, const int kbeg, const int nc) __attribute__((always_inline)) {
+        // weight loads: instruction t of fragment f gives lane l row r = 8 t + (l >> 3) of the
+        // fragment and LDS slot l & 7, which holds piece (l & 7) ^ ((r >> 1) & 7)
+        const int lr = lane >> 3, lq = lane & 7;
+        int jrow[kSNB];
+#pragma unroll
+        for (int f = 0; f < kSNB; ++f)
+            jrow[f] = EPI == SK_GATED ? tile * (kSCols / 2) + wave * 8 * kSNB + (f / 2) * 16 + lr
+                                      : tile * kSCols + wave * 16 * kSNB + f * 16 + lr;
+        const uint16_t* wbase = W + p.w_row0 * (int64_t)p.K + kbeg;
+        auto wrow = [&](int f, int t) {
+            if constexpr (EPI == SK_GATED) return (f & 1) * p.F + min(jrow[f] + 8 * t, p.F - 1);
+            return min(jrow[f] + 8 * t, p.N - 1);
+        };
+        auto load_w = [&](int c) {
+            const int st = c % kDW64;
+#pragma unroll
+            for (int f = 0; f < kSNB; ++f)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int r = 8 * t + lr;
+                    lds_dma16(wbase + (int64_t)wrow(f, t) * p.K + c * kDK + 8 * (lq ^ ((r >> 1) & 7)),
+                              &Wst64[wave][st][f][8 * t][0]);
+                }
+        };
+        // activations: piece q = kST i + threadIdx.x of the chunk is row q / 8, slot q % 8
+        auto load_a = [&](int c) {
+            const int k0 = kbeg + c * kDK;
+            const uint16_t* src;
+            if (p.seg_k > 0) {  // tap segments (multiples of 128): a chunk never straddles two
+                const int j = k0 / p.seg_k;
+                src = p.a_seg[0];
+#pragma unroll
+                for (int q = 1; q < kMaxTaps; ++q)
+                    if (j == q) src = p.a_seg[q];
+                src += k0 - j * p.seg_k;
+            } else {
+                src = A + k0;
+            }
+#pragma unroll
+            for (int i = 0; i < NAI; ++i) {
+                const int q = min(kST * i + (int)threadIdx.x, MT * 16 * 8 - 1);
+                const int row = q >> 3;
+                const int piece = (q & 7) ^ ((row >> 1) & 7);
+                lds_dma16(src + (int64_t)min(row, p.M - 1) * p.a_ld + 8 * piece,
+                          &As64[c % kDA64][0] + (kST * i + 64 * wave) * 8);
+            }
+        };
+
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int f = 0; f < kSNB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // chunk j's weights go out with chunk j - 1's activations (activations three chunks
+        // ahead, weights four): at the top of chunk c only chunks c + 1 .. c + 3's loads after
+        // chunk c's activations may be in flight
+        constexpr int nW = 2 * kSNB;
+        load_w(0);
+#pragma unroll
+        for (int j = 0; j < kDA64 - 1; ++j) {
+            if (j < nc) load_a(j);
+            if (j + 1 < nc) load_w(j + 1);
+        }
+        const int sw = (col >> 1) & 7;  // slot swizzle of the fragment rows this lane reads
+        for (int c = 0; c < nc; ++c) {
+            dma_sync64<3 * nW + 2 * NAI, 2 * nW + 2 * NAI, nW + NAI>(min(nc - 1 - c, 3));
+            if (c + kDA64 - 1 < nc) load_a(c + kDA64 - 1);  // into the buffer chunk c - 1 read
+            if (c + kDW64 - 1 < nc) load_w(c + kDW64 - 1);  // into the stage chunk c - 1 used
+            const int st = c % kDW64, buf = c % kDA64;
+#pragma unroll
+            for (int s = 0; s < kDK / 32; ++s) {
+                const int slot = (4 * s + grp) ^ sw;
+                u32x4 wb[kSNB];
+#pragma unroll
+                for (int f = 0; f < kSNB; ++f)
+                    wb[f] = *reinterpret_cast<const u32x4*>(&Wst64[wave][st][f][col][8 * slot]);
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    const u32x4 af = *reinterpret_cast<const u32x4*>(&As64[buf][(i * 16 + col) * kDK + 8 * slot]);
+#pragma unroll
+                    for (int f = 0; f < kSNB; ++f) acc[i][f] = mfma_bf16(af, wb[f], acc[i][f]);
+                }
+            }
+        }
+    };
+
     // the products of one work item: column tile `tile` over chunks [kbeg, kbeg + 128 nc)
-    auto item = [&](const int tile, const int kbeg, const int nc) {
+    auto item = [&](const int tile, const int kbeg, const int nc) __attribute__((always_inline)) {
+        if constexpr (K64) {
+            item64(tile, kbeg, 2 * nc);
+            return;
+        }
         // weight rows: load s of fragment f gives lane (col, grp) row r = 4 s + grp of the
         // fragment, piece col ^ r (LDS slot col of that row)
         int jrow[kSNB];
