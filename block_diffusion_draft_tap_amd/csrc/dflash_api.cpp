@@ -1067,20 +1067,33 @@ int forward_backbone(const dflash_model* M, const int32_t* anchor_ids, const dfl
                      hipStream_t s, bool* an_ready, const CtxRows* ctx = nullptr) {
     const dflash_dims& d = M->dims;
     const int wt = wtype_of(d.wdtype);
+    bool an_init = false;
     const bool init_sk = w.skinny && d.wdtype == DFLASH_BF16 && M->embed_in.dtype == DFLASH_BF16 &&
                          M->tok_proj.dtype == DFLASH_BF16 && B >= DFL_SKINNY_MIN_ROWS && d.H % kSkinnyK == 0 &&
                          (int64_t)d.gamma * d.d >= d.H;
     if (init_sk) {
         // 16 or more sequences on matrix cores: the anchors' embeddings gathered into w.an
-        // (B rows of H; it holds B * gamma rows of d), their tok_proj product stored as row 0
-        // of each block, then the block positions added and the mask rows written
+        // (B rows of H; it holds B * gamma rows of d), their tok_proj product as row 0 of each
+        // block, the block positions added and the mask rows written
         DFL_HIP(launch_gather_rows(static_cast<const uint16_t*>(M->embed_in.data), M->embed_in.rows, anchor_ids, B,
                                    d.H, w.an, s));
         SkinnyParams p = skinny_params(M->tok_proj, w.an, d.H, d.d, d.H, w.skp);
-        p.out = w.hd;
-        p.out_ld = (int64_t)d.gamma * d.d;
-        DFL_HIP(skinny_rows(SK_STORE, p, B, s));
-        DFL_HIP(launch_block_fill(w.hd, B, d.gamma, d.d, M->block_pos, M->mask_emb, 0, s));
+        if (B <= kSkinnyRows && d.d % 4 == 0 && d.d <= kNormMaxK) {
+            // the product's split partials, then one kernel for the block rows and the first
+            // layer's RMSNorm (the norm of the out projection when there are no layers)
+            int ns = 1, ks = 0;
+            skinny_split(SK_PARTIAL, d.d, d.H, 1, &ns, &ks);
+            DFL_HIP(skinny_rows(SK_PARTIAL, p, B, s));
+            DFL_HIP(launch_block_norm(w.skp, ns, B, d.gamma, d.d, w.hd, static_cast<const uint16_t*>(M->block_pos),
+                                      static_cast<const uint16_t*>(M->mask_emb),
+                                      d.nl > 0 ? M->layers[0].attn_norm : M->out_norm, 0, d.eps, w.an, s));
+            an_init = true;
+        } else {
+            p.out = w.hd;
+            p.out_ld = (int64_t)d.gamma * d.d;
+            DFL_HIP(skinny_rows(SK_STORE, p, B, s));
+            DFL_HIP(launch_block_fill(w.hd, B, d.gamma, d.d, M->block_pos, M->mask_emb, 0, s));
+        }
     } else {  // block rows: E_in[anchor] tok_proj^T + block_pos[0]; mask_emb[k-1] + block_pos[k]
         GemvParams p = base_params(d);
         p.w[0] = wptr(M->tok_proj);
@@ -1098,7 +1111,7 @@ int forward_backbone(const dflash_model* M, const int32_t* anchor_ids, const dfl
         p.seq_base = 0;
         DFL_HIP(gemv_rows(wt, PRO_GATHER, EPI_BLOCKINIT, p, B, s));
     }
-    *an_ready = false;  // w.an holds the next projection's normalised rows
+    *an_ready = an_init;  // w.an holds the next projection's normalised rows
     for (int i = 0; i < d.nl; ++i)
         DFL_TRY(run_layer(M, i, w.hd, kv, B, w, s, i + 1 < d.nl ? M->layers[i + 1].attn_norm : M->out_norm,
                           an_ready, ctx));

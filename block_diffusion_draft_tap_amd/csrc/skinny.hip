@@ -873,6 +873,77 @@ __global__ __launch_bounds__(kRnThreads) void resid_norm_kernel(const float* par
     }
 }
 
+// the block rows of B sequences (row r = b gamma + j) with the first layer's RMSNorm:
+// j = 0: v = sum_s part[s][b] (split order) + block_pos[0], the anchor's token projection
+// from its split partials; j > 0: v = mask_emb[j - 1] + block_pos[j]. h[r] = v (fp32),
+// dst[r] = bf16(v (mean v^2 + eps)^-1/2 gain). One workgroup per row, as resid_norm_kernel
+__global__ __launch_bounds__(kRnThreads) void block_norm_kernel(const float* part, int nsplit, int B, int gamma, int N,
+                                                                float* h, const uint16_t* block_pos,
+                                                                const uint16_t* mask_emb, const void* gain,
+                                                                int gain_f32, float eps, uint16_t* dst) {
+    constexpr int kBlock = kRnThreads;
+    constexpr int U = kNormMaxK / (4 * kBlock);
+    __shared__ float red[kBlock / kWave];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int b = r / gamma, j = r - b * gamma;
+    const int64_t bn = (int64_t)B * N;
+    float* hr = h + (int64_t)r * N;
+    float4 v[U];
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k = (tid + u * kBlock) * 4;
+        if (k < N) {
+            const uint2 bp = *reinterpret_cast<const uint2*>(block_pos + (int64_t)j * N + k);
+            float4 a;
+            if (j == 0) {
+                const float* src = part + (int64_t)b * N + k;
+                a = *reinterpret_cast<const float4*>(src);
+#pragma unroll 8
+                for (int sp = 1; sp < nsplit; ++sp) {
+                    const float4 t = *reinterpret_cast<const float4*>(src + sp * bn);
+                    a.x += t.x;
+                    a.y += t.y;
+                    a.z += t.z;
+                    a.w += t.w;
+                }
+            } else {
+                const uint2 me = *reinterpret_cast<const uint2*>(mask_emb + (int64_t)(j - 1) * N + k);
+                a = make_float4(bf16_lo(me.x), bf16_hi(me.x), bf16_lo(me.y), bf16_hi(me.y));
+            }
+            v[u] = make_float4(a.x + bf16_lo(bp.x), a.y + bf16_hi(bp.x), a.z + bf16_lo(bp.y), a.w + bf16_hi(bp.y));
+            *reinterpret_cast<float4*>(hr + k) = v[u];
+            ss += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
+        }
+    }
+    ss = wave_sum(ss);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kBlock / kWave; ++w) tot += red[w];
+    const float rs = 1.0f / sqrtf(tot / (float)N + eps);
+    uint16_t* o = dst + (int64_t)r * N;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k = (tid + u * kBlock) * 4;
+        if (k < N) {
+            float g[4];
+            if (gain_f32) {
+                const float4 gv = *reinterpret_cast<const float4*>(static_cast<const float*>(gain) + k);
+                g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
+            } else {
+                const uint2 gv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(gain) + k);
+                g[0] = bf16_lo(gv.x); g[1] = bf16_hi(gv.x); g[2] = bf16_lo(gv.y); g[3] = bf16_hi(gv.y);
+            }
+            uint2 q;
+            q.x = pack_bf16x2(v[u].x * rs * g[0], v[u].y * rs * g[1]);
+            q.y = pack_bf16x2(v[u].z * rs * g[2], v[u].w * rs * g[3]);
+            *reinterpret_cast<uint2*>(o + k) = q;
+        }
+    }
+}
+
 // instrumentation: the stamp slice of one matrix-core launch (algorithmic bytes =
 // weights + activation rows + outputs, per layer)
 // The direct-to-LDS kernel serves launches of at least DFL_SK_DMA_MIN_MT row tiles whose
@@ -1122,6 +1193,17 @@ hipError_t launch_resid_norm(const float* part, int nsplit, int M, int N, float*
     (void)hipGetLastError();  // report only this launch's status
     hipLaunchKernelGGL(resid_norm_kernel, dim3((unsigned)M), dim3(kRnThreads), 0, s, part, nsplit, M, N, h, h_ld, gain,
                        gain_f32, eps, dst, dst_ld);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_norm(const float* part, int nsplit, int B, int gamma, int N, float* h,
+                             const uint16_t* block_pos, const uint16_t* mask_emb, const void* gain, int gain_f32,
+                             float eps, uint16_t* dst, hipStream_t s) {
+    if (B <= 0 || gamma <= 0) return hipSuccess;
+    if (N <= 0 || (N % 4) || N > kNormMaxK || nsplit < 1) return hipErrorInvalidValue;
+    (void)hipGetLastError();  // report only this launch's status
+    hipLaunchKernelGGL(block_norm_kernel, dim3((unsigned)(B * gamma)), dim3(kRnThreads), 0, s, part, nsplit, B, gamma,
+                       N, h, block_pos, mask_emb, gain, gain_f32, eps, dst);
     return hipGetLastError();
 }
 

@@ -106,6 +106,15 @@ hipError_t launch_split_reduce(int epi, const SkinnyParams& p, hipStream_t s);
 hipError_t launch_resid_norm(const float* part, int nsplit, int M, int N, float* h, int64_t h_ld, const void* gain,
                              int gain_f32, float eps, uint16_t* dst, int64_t dst_ld, hipStream_t s);
 
+// The block rows of B sequences (row r = b gamma + j, N values each) and their RMSNorm with
+// `gain`: row j = 0 of sequence b is the sum of the split partials part[s][b] (nsplit
+// partials [nsplit][B][N], split order) + block_pos[0], row j > 0 is mask_emb[j - 1] +
+// block_pos[j] (bf16 tables [gamma][N], [gamma - 1][N]); h[r] = the row (fp32), dst[r] =
+// bf16(row (mean row^2 + eps)^-1/2 gain). N a multiple of 4, at most 8192
+hipError_t launch_block_norm(const float* part, int nsplit, int B, int gamma, int N, float* h,
+                             const uint16_t* block_pos, const uint16_t* mask_emb, const void* gain, int gain_f32,
+                             float eps, uint16_t* dst, hipStream_t s);
+
 // dst + z * dst_layer_stride: rows r of bf16(x[r, k] * (mean_k x[r, k]^2 + eps)^-1/2 * gain[z][k])
 // for rows of K fp32 values (K a multiple of 8, at most 8192), z < layers (grid.y)
 struct NormRowsParams {
