@@ -83,6 +83,10 @@ ROWS35_MANY = scaled(BATCHED, name="rows35_many", H=128, m=2, d=640, hq=10, hkv=
 GAMMA1 = scaled(GQA_BF16, name="gamma1", gamma=1, B=2)
 EMPTY_CTX = scaled(GQA_BF16, name="empty_ctx", B=3)
 NL0 = scaled(GQA_BF16, name="nl0", nl=0, B=2)
+# the same on the matrix-core block init of 16 sequences (the block rows' kernel then
+# normalises with the out projection's gain, or its rows are only the anchors)
+NL0_BATCHED = scaled(BATCHED_SMALL, name="nl0_batched", nl=0)
+GAMMA1_BATCHED = scaled(BATCHED_SMALL, name="gamma1_batched", gamma=1)
 
 # the DFlash2 variant (rotary positions, a context window): the fp32 drafter with a window
 # shorter than its context (VALU attention); three bf16 GQA sequences of which two are longer
@@ -117,6 +121,8 @@ CASES = {
     "gamma1": (GAMMA1, [200, 77]),
     "empty_ctx": (EMPTY_CTX, [0, 45, 0]),
     "nl0": (NL0, [64, 31]),
+    "nl0_batched": (NL0_BATCHED, [int(x) for x in gen.context_lengths(NL0_BATCHED)]),
+    "gamma1_batched": (GAMMA1_BATCHED, [int(x) for x in gen.context_lengths(GAMMA1_BATCHED)]),
     "d2_tiny": (D2_TINY, [D2_TINY.L]),
     "d2_gqa": (D2_GQA, [200, 77, 131]),
     "d2_w1": (D2_W1, [200, 45]),
