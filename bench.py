@@ -53,7 +53,7 @@ HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, GB/s (published)
 MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix peak (published)
 METRIC = "draft blocks/sec (drafter fwd+verify) at 1 MI355X; % HBM/MFMA roofline"
 NEAR_TIE = 1e-3                   # draft ids are compared where the oracle's top-2 gap is at least this
-FLUSH_BYTES = 1 << 30             # MALL flush between rounds: a 1 GiB write (the MALL holds 256 MB)
+FLUSH_BYTES = 1 << 30             # MALL flush between rounds: a 1 GiB read (the MALL holds 256 MB)
 STAMP_ENTRIES = 1 << 20           # per round: room for every traced workgroup's (start, end)
 
 
@@ -689,14 +689,15 @@ def main():
     res["prefill"] = pre
     res["wall_s_timed"] = round(wall, 4)
 
-    # rounds one by one, each after a write that evicts the MALL (a decode loop runs the
-    # target model between drafter rounds)
+    # rounds one by one, each after a 1 GiB read that evicts the MALL (a decode loop runs the
+    # target model between drafter rounds, streaming its weights; a read leaves the cache
+    # clean, where a write would leave dirty lines for the round to write back)
     if args.flush_steps > 0:
-        junk = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        junk = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fl = []
         for i in range(args.flush_steps):
-            junk.fill_(float(i))
+            junk.sum()
             e0.record()
             step(nxt + i)
             e1.record()
