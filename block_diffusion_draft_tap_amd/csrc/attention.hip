@@ -210,6 +210,9 @@ __device__ __forceinline__ int lpt_sequence(const AttnParams& p, const int pos) 
     return chosen;
 }
 
+// K/V cache loads (streamed: each byte read once a launch)
+__device__ __forceinline__ u32x4 kv_load(const uint16_t* p) { return stream_load(reinterpret_cast<const u32x4*>(p)); }
+
 template <int HD, int NRT>
 __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
     const uint64_t t_start = trace_start(p.stamps);
@@ -266,8 +269,8 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            kb[0][ks] = *reinterpret_cast<const u32x4*>(k0 + ks * 32);
-            kb[1][ks] = *reinterpret_cast<const u32x4*>(k1 + ks * 32);
+            kb[0][ks] = kv_load(k0 + ks * 32);
+            kb[1][ks] = kv_load(k1 + ks * 32);
         }
     };
     auto load_v = [&](const int u, u32x4 (&vb)[DT]) {
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(kBlock) void attn_mfma_kernel(const AttnParams p) {
         else
             vp = vblk + col * kChunk + 8 * grp;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vb[dt] = *reinterpret_cast<const u32x4*>(vp + dt * 16 * kChunk);
+        for (int dt = 0; dt < DT; ++dt) vb[dt] = kv_load(vp + dt * 16 * kChunk);
     };
     u32x4 kA[2][KS], vA[DT];
     // the first unit's loads go out together with Q's
@@ -417,7 +420,11 @@ constexpr int kStageK = kChunk * 128;  // bf16 elements of a unit's K tile (head
 __device__ __forceinline__ void attn_dma16(const uint16_t* src, const uint16_t* lds_base) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base);
+#if DFL_STREAM_NT
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds) : "memory", "m0");
+#else
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+#endif
 }
 #pragma clang diagnostic pop
 
@@ -628,11 +635,11 @@ __global__ __launch_bounds__(64 * NRT, 2) void attn_rows_kernel(const AttnParams
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            kb[0][ks] = *reinterpret_cast<const u32x4*>(k0 + ks * 32);
-            kb[1][ks] = *reinterpret_cast<const u32x4*>(k1 + ks * 32);
+            kb[0][ks] = kv_load(k0 + ks * 32);
+            kb[1][ks] = kv_load(k1 + ks * 32);
         }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vb[dt] = *reinterpret_cast<const u32x4*>(vp + dt * vstride);
+        for (int dt = 0; dt < DT; ++dt) vb[dt] = kv_load(vp + dt * vstride);
     };
     const bool any = u_begin < u_end;
     if (any) load_unit(u_begin, kA, vA);

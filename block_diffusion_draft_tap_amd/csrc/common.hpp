@@ -113,6 +113,35 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 }
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
+// Loads of data each launch reads once (weights, the K/V cache, target logits) carry the
+// non-temporal hint, so the stream does not displace what the workgroups re-read from the
+// caches (activation chunks, query tiles, partial sums)
+#ifndef DFL_STREAM_NT
+#define DFL_STREAM_NT 1
+#endif
+__device__ __forceinline__ u32x4 stream_load(const u32x4* p) {
+#if DFL_STREAM_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ f32x4 stream_load(const f32x4* p) {
+#if DFL_STREAM_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+    const u32x4 v = stream_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float4 stream_load(const float4* p) {
+    const f32x4 v = stream_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float load_gain(const void* g, bool f32, int i) {
     return f32 ? static_cast<const float*>(g)[i] : bf16_bits_to_f32(static_cast<const uint16_t*>(g)[i]);
 }

@@ -58,13 +58,13 @@ template <> struct WChunk<W_I4> { uint4 c; float s, b; };
 template <int WT>
 __device__ __forceinline__ void wload(WChunk<WT>& w, const WeightPtr& W, int64_t row, int K, int k) {
     if constexpr (WT == W_BF16) {
-        w.v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W.data) + row * K + k);
+        w.v = stream_load(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W.data) + row * K + k));
     } else if constexpr (WT == W_F32) {
         const float* src = static_cast<const float*>(W.data) + row * K + k;
-        w.a = *reinterpret_cast<const float4*>(src);
-        w.b = *reinterpret_cast<const float4*>(src + 4);
+        w.a = stream_load(reinterpret_cast<const float4*>(src));
+        w.b = stream_load(reinterpret_cast<const float4*>(src + 4));
     } else {
-        w.c = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(W.data) + row * (K / 8) + k / 8);
+        w.c = stream_load(reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(W.data) + row * (K / 8) + k / 8));
         const int64_t g = row * (K / 64) + k / 64;
         w.s = bf16_bits_to_f32(W.scales[g]);
         w.b = bf16_bits_to_f32(W.biases[g]);

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kBlock) void verify_partial_kernel(const float* log
     if ((V & 3) == 0) {
 #pragma unroll 4
         for (int j = v0 + 4 * threadIdx.x; j < v1; j += 4 * blockDim.x) {
-            const float4 a = *reinterpret_cast<const float4*>(src + j);
+            const float4 a = stream_load(reinterpret_cast<const float4*>(src + j));
             argmax_pick(v, i, a.x, j);
             argmax_pick(v, i, a.y, j + 1);
             argmax_pick(v, i, a.z, j + 2);

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
         const int idx = min(tid + i * kBlock, 64 * ccr - 1);
         const int r = idx / ccr, c = idx - r * ccr;
         const int64_t grow = p.w_row0 + min(row0 + r, p.N - 1);
-        cv[i] = *reinterpret_cast<const u32x4*>(p.codes[layer] + grow * K8 + kb / 8 + 4 * c);
+        cv[i] = stream_load(reinterpret_cast<const u32x4*>(p.codes[layer] + grow * K8 + kb / 8 + 4 * c));
     }
     // this lane's output column's scales and biases (clamped past the range: never used)
     const int64_t wrow = p.w_row0 + n;

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kST, MT >= 8 ? 1 : DFL_SK_OCC) void skinny_kernel(c
         for (int f = 0; f < kSNB; ++f)
 #pragma unroll
             for (int s = 0; s < kSSteps; ++s)
-                wr[f][s] = *reinterpret_cast<const u32x4*>(wbase + (int64_t)wrow(f, s) * p.K + cc * kSKC);
+                wr[f][s] = stream_load(reinterpret_cast<const u32x4*>(wbase + (int64_t)wrow(f, s) * p.K + cc * kSKC));
     };
     // the activation chunk: MT*16 rows x 16 pieces of 16 bytes, spread over the threads
     constexpr int PIECES = MT * 16 * (kSKC / 8);
@@ -409,6 +409,16 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, const uint16_t* l
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
+// the same with the non-temporal hint of streamed data (the weights)
+__device__ __forceinline__ void lds_dma16_nt(const uint16_t* src, const uint16_t* lds_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base);
+#if DFL_STREAM_NT
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds) : "memory", "m0");
+#else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+#endif
+}
 #pragma clang diagnostic pop
 
 // chunk c may start: this wavefront's loads other than the last `keep` (0 or 8) landed, its
@@ -511,7 +521,7 @@ __global__ __launch_bounds__(kST, 1) void skinny_dma_kernel(const SkinnyParams p
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int r = 8 * t + lr;
-                    lds_dma16(wbase + (int64_t)wrow(f, t) * p.K + c * kDK + 8 * (lq ^ ((r >> 1) & 7)),
+                    lds_dma16_nt(wbase + (int64_t)wrow(f, t) * p.K + c * kDK + 8 * (lq ^ ((r >> 1) & 7)),
                               &Wst64[wave][st][f][8 * t][0]);
                 }
         };
@@ -602,7 +612,7 @@ __global__ __launch_bounds__(kST, 1) void skinny_dma_kernel(const SkinnyParams p
 #pragma unroll
                 for (int s = 0; s < kSSteps; ++s) {
                     const int r = 4 * s + grp;
-                    lds_dma16(wbase + (int64_t)wrow(f, s) * p.K + c * kSKC + 8 * (col ^ r), &Wst[wave][st][f][4 * s][0]);
+                    lds_dma16_nt(wbase + (int64_t)wrow(f, s) * p.K + c * kSKC + 8 * (col ^ r), &Wst[wave][st][f][4 * s][0]);
                 }
         };
         // activations: LDS piece q = kST i + threadIdx.x of the tile is row q / 16, slot q % 16
