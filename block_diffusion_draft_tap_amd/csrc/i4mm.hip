@@ -4,24 +4,31 @@
 // code unpack and their activation reads, not by HBM.
 //
 // Products run on v_mfma_f32_16x16x32_bf16 with the activation rows as the A
-// operand (rows past M are zero) and 16 weight rows as the B operand. A weight
-// group (64 columns, one bf16 scale s and bias b) is two MFMA k-steps:
+// operand (rows past M are zero) and 16 weight rows as the B operand. Over a
+// weight group (64 columns, one bf16 scale s and bias b):
 //   sum_k (s q_k + b) x_k = s sum_k (128 + q_k) x_k + (b - 128 s) sum_k x_k
 // The codes become bf16 (128 + q) with two integer operations per pair (the
 // exponent of 128 or'ed above the 4-bit code), so the B operand costs no float
 // arithmetic; each group's MFMA partial is then scaled and the bias term added
 // with its activation sum (summed once per workgroup while the rows are staged).
 //
-// Lane (c, g) of a wavefront (c = lane % 16, g = lane / 16) supplies, for k-step
-// j of a 128-column block, the 8 columns 64 (j / 2) + 16 g + 8 (j % 2) .. +8: the
-// codes of weight row c there are one 32-bit word, and the four steps keep every
-// step inside one quantisation group. A workgroup (four wavefronts, 64 weight
-// rows) takes a K range of up to 8 blocks: it reads its rows' codes as
-// contiguous 512-byte runs into LDS (loaded fragment by fragment, the codes
-// would come as 16 rows x 32 bytes per instruction, a pattern DRAM serves at
-// about half the rate), stages that range of the activation rows once in LDS,
-// already in the codes' pair order, with each row's per-group sum, and loads
-// its output columns' scales and biases; then the products run from LDS.
+// With M <= 4 or 8 activation rows, an MFMA's 16 rows hold 4 or 2 slots of the
+// rows: slot h's rows see only the k columns taken from one quantisation group
+// (zero A elsewhere; slot h takes groups 16 h / kG + t over the sets t), so one
+// MFMA output holds the partials of kG groups and each lane scales one group
+// per set, not every group (the
+// scaling was most of the kernel's VALU work at few rows). Lane (c, g) of a
+// wavefront (c = lane % 16, g = lane / 16) supplies k-chunk g of every MFMA: 8
+// consecutive columns of one group, so the codes of weight row c there are one
+// 32-bit word, and the lane's words of a group set are consecutive. The slots'
+// sums meet in one lane by cross-lane adds at the end. A workgroup (four
+// wavefronts, 64 weight rows) takes a K range of up to 8 blocks of 128 columns:
+// it reads its rows' codes as contiguous 512-byte runs into LDS (loaded fragment
+// by fragment, the codes would come as 16 rows x 32 bytes per instruction, a
+// pattern DRAM serves at about half the rate), stages that range of the
+// activation rows once in LDS, already in the codes' pair order, with each row's
+// per-group sum, and loads its output columns' scales and biases; then the
+// products run from LDS.
 //
 // Results are fp32 partial sums per K range; an ordered reduce applies the
 // epilogue (the skinny reduce kernels, or the split argmax below).
@@ -81,6 +88,14 @@ constexpr int kCodeChunks = 64 * kI4MaxBlocks * kI4Block / 32 / kBlock;  // 16-b
 // biases) of its range are two 16-byte loads.
 template <int MT, bool FULL>
 __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
+    // An MFMA's 16 rows are kG = 16 / MT slots of MT activation rows; slot h takes 32 / kG
+    // of its 32 k columns from quantisation group kSets h + t (group set t), so one MFMA
+    // output holds kG groups' partials and every lane scales one group per set.
+    constexpr int kG = 16 / MT;                // 4, 2, 1
+    constexpr int kCPG = 4 / kG;               // 8-column k-chunks per slot
+    constexpr int kSteps = 8 / kCPG;           // k-steps per group
+    constexpr int kSets = kMaxGroups / kG;     // group sets of a 1024-column range
+    static_assert(kG * MT == 16 && kSets * kG == kMaxGroups, "slot layout");
     __shared__ __align__(16) uint16_t as[(MT + 1) * kAld];      // rows in the codes' pair order; row MT zero
     __shared__ __align__(16) uint32_t cs[64 * kCodeLd];         // the workgroup's 64 weight rows' codes
     __shared__ __align__(16) float xs[kMaxGroups][kI4Rows];     // sum of each row's group (rows past MT: 0)
@@ -126,28 +141,40 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
         const int64_t grow = p.w_row0 + min(row0 + r, p.N - 1);
         cv[i] = stream_load(reinterpret_cast<const u32x4*>(p.codes[layer] + grow * K8 + kb / 8 + 4 * c));
     }
-    // this lane's output column's scales and biases (clamped past the range: never used)
+    // this lane's output column's scales and biases, for the groups of its output slot: the
+    // kSets consecutive groups kSets slot + t (one or two 16-byte loads or one 8-byte load;
+    // for a shorter range, loads clamped to it: its products and sums are zero past it)
+    const int slot = grp / kCPG;
+    const int ng = kw / 64;
     const int64_t wrow = p.w_row0 + n;
-    const uint32_t* srow = reinterpret_cast<const uint32_t*>(p.scales[layer] + wrow * K64 + kb / 64);
-    const uint32_t* brow = reinterpret_cast<const uint32_t*>(p.biases[layer] + wrow * K64 + kb / 64);
-    uint32_t sc[kI4MaxBlocks], bi[kI4MaxBlocks];
+    const uint16_t* srow = p.scales[layer] + wrow * K64 + kb / 64;
+    const uint16_t* brow = p.biases[layer] + wrow * K64 + kb / 64;
+    const int g0 = kSets * slot;
+    uint32_t sc[kSets / 2], bi[kSets / 2];  // bf16 pairs: groups g0 + 2i (low), g0 + 2i + 1 (high)
     if constexpr (FULL) {
+        if constexpr (kSets == 4) {
+            const uint2 sv = *reinterpret_cast<const uint2*>(srow + g0);
+            const uint2 bv = *reinterpret_cast<const uint2*>(brow + g0);
+            sc[0] = sv.x; sc[1] = sv.y;
+            bi[0] = bv.x; bi[1] = bv.y;
+        } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const u32x4 sv = *reinterpret_cast<const u32x4*>(srow + 4 * h);
-            const u32x4 bv = *reinterpret_cast<const u32x4*>(brow + 4 * h);
+            for (int h = 0; h < kSets / 8; ++h) {
+                const u32x4 sv = *reinterpret_cast<const u32x4*>(srow + g0 + 8 * h);
+                const u32x4 bv = *reinterpret_cast<const u32x4*>(brow + g0 + 8 * h);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sc[4 * h + q] = sv[q];
-                bi[4 * h + q] = bv[q];
+                for (int q = 0; q < 4; ++q) {
+                    sc[4 * h + q] = sv[q];
+                    bi[4 * h + q] = bv[q];
+                }
             }
         }
     } else {
 #pragma unroll
-        for (int b = 0; b < kI4MaxBlocks; ++b) {
-            const int bb = min(b, nblk - 1);
-            sc[b] = srow[bb];
-            bi[b] = brow[bb];
+        for (int i = 0; i < kSets / 2; ++i) {
+            const int ga = min(g0 + 2 * i, ng - 1), gb = min(g0 + 2 * i + 1, ng - 1);
+            sc[i] = (uint32_t)srow[ga] | ((uint32_t)srow[gb] << 16);
+            bi[i] = (uint32_t)brow[ga] | ((uint32_t)brow[gb] << 16);
         }
     }
 
@@ -169,7 +196,6 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
     __syncthreads();
     // each row's group sums (any order of the group's 64 values: a sum)
     {
-        const int ng = kw / 64;
         const int m = tid / kMaxGroups, g = tid - m * kMaxGroups;
         float t = 0.f;
         if (m < MT && g < ng) {
@@ -184,43 +210,67 @@ __global__ __launch_bounds__(kBlock) void i4mm_kernel(const I4Params p) {
     }
     __syncthreads();
 
+    // Lane (col, grp) supplies k-chunk grp of every MFMA: chunk c = grp % kCPG of slot
+    // `slot`, i.e. the columns 8 (c kSteps + j) .. + 8 of group g0 + t at k-step j of set t.
+    // Its A fragment is activation row col % MT when col lies in that slot's rows, else the
+    // zero row; its B fragment is weight row col's codes there, kSteps consecutive words.
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* arow = &as[(col < MT ? col : MT) * kAld + 16 * grp];  // A fragment row (the zero row past MT)
-    const uint32_t* crow = &cs[(wave * 16 + col) * kCodeLd + 2 * grp];
+    const int chunk = grp % kCPG;
+    const bool areal = col / MT == slot;
+    const uint16_t* arow = &as[(areal ? col % MT : MT) * kAld + 64 * g0 + 8 * kSteps * chunk];
+    const uint16_t* azero = &as[MT * kAld];
+    const uint32_t* crow = &cs[(wave * 16 + col) * kCodeLd + 8 * g0 + kSteps * chunk];
+    const uint32_t mk = p.nib_mask, one = p.bf16_128;
     f32x4 acc = zero;
 #pragma unroll
-    for (int b = 0; b < kI4MaxBlocks; ++b) {
-        if (b < nblk) {
-            // A fragments of the block's four k-steps: activation row col, columns
-            // 128 b + 64 (j / 2) + 16 grp + 8 (j % 2) .. + 8 (already in pair order)
-            u32x4 af[4];
+    for (int t = 0; t < kSets; ++t) {
+        if (FULL || t < ng) {
+            // past the range (slots whose group t lies beyond it) the A fragments are the zero row
+            const uint16_t* ap = (FULL || g0 + t < ng) ? arow + 64 * t : azero;
+            uint32_t cw[kSteps];
+            if constexpr (kSteps == 8) {
+                const u32x4 c0 = *reinterpret_cast<const u32x4*>(crow + 8 * t);
+                const u32x4 c1 = *reinterpret_cast<const u32x4*>(crow + 8 * t + 4);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                af[j] = *reinterpret_cast<const u32x4*>(arow + kI4Block * b + 64 * (j >> 1) + 8 * (j & 1));
-            // this lane's codes: weight row wave * 16 + col, words 16 b + 2 grp (+1) and + 8
-            const uint2 c0 = *reinterpret_cast<const uint2*>(crow + 16 * b);
-            const uint2 c1 = *reinterpret_cast<const uint2*>(crow + 16 * b + 8);
-            // per group: sum_k (128 + q) x over the group's two steps
-            const uint32_t mk = p.nib_mask, one = p.bf16_128;
-            const f32x4 p0 = mma(af[1], codes_bf16(c0.y, mk, one), mma(af[0], codes_bf16(c0.x, mk, one), zero));
-            const f32x4 p1 = mma(af[3], codes_bf16(c1.y, mk, one), mma(af[2], codes_bf16(c1.x, mk, one), zero));
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(&xs[2 * b][4 * grp]);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(&xs[2 * b + 1][4 * grp]);
-            const float s0 = bf16_lo(sc[b]), s1 = bf16_hi(sc[b]);
-            const float b0 = bf16_lo(bi[b]) - 128.0f * s0, b1 = bf16_hi(bi[b]) - 128.0f * s1;
+                for (int q = 0; q < 4; ++q) { cw[q] = c0[q]; cw[4 + q] = c1[q]; }
+            } else if constexpr (kSteps == 4) {
+                const u32x4 c0 = *reinterpret_cast<const u32x4*>(crow + 8 * t);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cw[q] = c0[q];
+            } else {
+                const uint2 c0 = *reinterpret_cast<const uint2*>(crow + 8 * t);
+                cw[0] = c0.x;
+                cw[1] = c0.y;
+            }
+            // the slots' group partials: sum_k (128 + q) x over this lane's output group
+            f32x4 pg = zero;
+#pragma unroll
+            for (int j = 0; j < kSteps; ++j)
+                pg = mma(*reinterpret_cast<const u32x4*>(ap + 8 * j), codes_bf16(cw[j], mk, one), pg);
+            // rows (4 grp) % MT + e of group g0 + t (its activation sums: zero past the range)
+            const f32x4 xg = *reinterpret_cast<const f32x4*>(&xs[g0 + t][(4 * grp) % MT]);
+            const float sg = (t & 1) ? bf16_hi(sc[t / 2]) : bf16_lo(sc[t / 2]);
+            const float bg = ((t & 1) ? bf16_hi(bi[t / 2]) : bf16_lo(bi[t / 2])) - 128.0f * sg;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[e] = fmaf(s0, p0[e], acc[e]);
-                acc[e] = fmaf(b0, x0[e], acc[e]);
-                acc[e] = fmaf(s1, p1[e], acc[e]);
-                acc[e] = fmaf(b1, x1[e], acc[e]);
+                acc[e] = fmaf(sg, pg[e], acc[e]);
+                acc[e] = fmaf(bg, xg[e], acc[e]);
             }
         }
     }
+    // the slots of one row block: lanes 16 apart (kG = 4) and 32 apart (kG >= 2)
+    if constexpr (kG >= 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 32, kWave);
+    }
+    if constexpr (kG == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], 16, kWave);
+    }
 
-    // lane holds output column tile * 16 + col of activation rows 4 grp + e
+    // slot 0's lanes hold output column tile * 16 + col of activation rows 4 grp + e
     const int nout = tile * 16 + col;
-    if (nout < p.N) {
+    if (nout < p.N && slot == 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int m = 4 * grp + e;

@@ -469,8 +469,8 @@ def test_lm_head_argmax_matrix_cores(M, H, V):
     assert rel_err(maxl, best) <= 1e-5
 
 
-@pytest.mark.parametrize("M,H,V", [(1, 256, 1000), (4, 256, 1000), (7, 5120, 3001), (13, 384, 1000),
-                                   (16, 5120, 3001)])
+@pytest.mark.parametrize("M,H,V", [(1, 256, 1000), (4, 256, 1000), (3, 384, 1000), (7, 5120, 3001), (8, 640, 1000),
+                                   (13, 384, 1000), (16, 5120, 3001)])
 def test_lm_head_argmax_int4_matrix_cores(M, H, V):
     """int4-g64 head and bf16 rows, at most 16 of them, with the workspace for
     the matrix-core path (split partial logits, then the ordered split argmax):
