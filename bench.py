@@ -380,7 +380,8 @@ def roofline_entry(k, d, timing):
         # counter-derived bytes per launch, valid only for the kernel sources they were taken with
         from block_diffusion_draft_tap_amd import prof_report
         vals = prof_report.read_summary(tfile)
-        if vals.get("kernel sources sha256[:16]") == prof_report.kernel_sources_hash() and "bytes per launch" in vals:
+        if (vals.get("kernel sources sha256[:16]") == prof_report.kernel_sources_hash(vals.get("kernel", k["kernel"]))
+                and "bytes per launch" in vals):
             entry["traffic"] = float(vals["bytes per launch"])
     return entry
 

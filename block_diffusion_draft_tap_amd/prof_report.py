@@ -21,27 +21,51 @@
       `--pmc` passes, with the share of LDS-active cycles lost to bank
       conflicts when both SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE are there.
 
-The traffic summary records a hash of the kernel sources it was measured with
-(kernel_sources_hash); a reader of the summary compares it with the current
-sources and ignores the figure once they differ.
+The traffic summary records a hash of the sources that decide the measured
+kernel (kernel_sources_hash: its own .hip file, the headers and the host launch
+code, not the files of other kernels); a reader of the summary compares it with
+the current sources and ignores the figure once they differ.
 """
 
 import argparse
 import csv
 import hashlib
 import os
+import re
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-def kernel_sources():
-    """Every source that decides the kernels' code and launch shapes."""
+def _kernel_files():
+    """{kernel function name: the .hip file that defines it}"""
     d = os.path.join(HERE, "csrc")
-    return sorted(os.path.join("csrc", f) for f in os.listdir(d) if f.endswith((".hip", ".hpp", ".cpp")))
+    out = {}
+    for f in sorted(os.listdir(d)):
+        if f.endswith(".hip"):
+            with open(os.path.join(d, f)) as fh:
+                for name in re.findall(r"\bvoid\s+([A-Za-z0-9_]+_kernel)\b", fh.read()):
+                    out.setdefault(name, os.path.join("csrc", f))
+    return out
 
 
-def kernel_sources_hash():
+def kernel_sources(kernel=None):
+    """The sources that decide a kernel's code and launch shapes: the .hip file that defines
+    it and every source that defines no other kernel (headers, the host code that sizes the
+    launches). Without a kernel, or for one not found: every source."""
+    d = os.path.join(HERE, "csrc")
+    every = sorted(os.path.join("csrc", f) for f in os.listdir(d) if f.endswith((".hip", ".hpp", ".cpp")))
+    if not kernel:
+        return every
+    files = _kernel_files()
+    own = {f for n, f in files.items() if re.search(r"\b" + n + r"\b", kernel)}
+    if not own:
+        return every
+    others = set(files.values()) - own
+    return [rel for rel in every if rel not in others]
+
+
+def kernel_sources_hash(kernel=None):
     h = hashlib.sha256()
-    for rel in kernel_sources():
+    for rel in kernel_sources(kernel):
         with open(os.path.join(HERE, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -125,7 +149,8 @@ def traffic_summary(fetch_csv, write_csv, kernel, copy_bytes, algorithmic_bytes)
         "bytes per launch": f"{bytes_per:.0f}",
         "algorithmic bytes per launch": f"{algorithmic_bytes}",
         "traffic / algorithmic": f"{bytes_per / algorithmic_bytes:.4f}",
-        "kernel sources sha256[:16]": kernel_sources_hash(),
+        "kernel sources sha256[:16]": kernel_sources_hash(name),
+        "kernel sources hashed": " ".join(kernel_sources(name)),
     }
 
 

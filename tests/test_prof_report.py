@@ -37,6 +37,21 @@ def test_traffic_scaling(tmp_path):
     assert v["kernel sources sha256[:16]"] == prof_report.kernel_sources_hash()
 
 
+def test_kernel_sources_per_kernel():
+    """A kernel's hash covers its own .hip file and the shared sources (headers, host launch
+    code), not the files of other kernels; an unknown name covers every source."""
+    every = prof_report.kernel_sources()
+    attn = prof_report.kernel_sources("void dfl::attn_mfma_kernel<128, 3>(dfl::AttnParams)")
+    assert "csrc/attention.hip" in attn and "csrc/dflash_api.cpp" in attn and "csrc/common.hpp" in attn
+    assert "csrc/i4mm.hip" not in attn and "csrc/skinny.hip" not in attn and "csrc/gemv.hip" not in attn
+    assert all(h in attn for h in every if h.endswith(".hpp"))
+    sk = prof_report.kernel_sources("void dfl::(anonymous namespace)::skinny_kernel<1, 3>(dfl::SkinnyParams)")
+    assert "csrc/skinny.hip" in sk and "csrc/attention.hip" not in sk
+    assert prof_report.kernel_sources("not a kernel") == every
+    assert prof_report.kernel_sources_hash("not a kernel") == prof_report.kernel_sources_hash()
+    assert prof_report.kernel_sources_hash("attn_mfma_kernel<128, 3>") != prof_report.kernel_sources_hash()
+
+
 def test_summary_parser_keeps_colons_in_keys(tmp_path):
     p = tmp_path / "s.md"
     p.write_text("# t\n\n- kernel sources sha256[:16]: abc\n- bytes per launch: 12\nnot a field: x\n")
