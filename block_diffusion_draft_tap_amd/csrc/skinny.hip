@@ -959,9 +959,10 @@ __global__ __launch_bounds__(kRnThreads) void block_norm_kernel(const float* par
 // The direct-to-LDS kernel serves launches of at least DFL_SK_DMA_MIN_MT row tiles whose
 // workgroups number at most DFL_SK_DMA_MAX_WGS (about one per CU of the 256-CU part, where
 // its deeper weight stream pays); with more workgroups, two register-path workgroups per CU
-// keep more in flight than its one (measured: the 1187-tile LM head, 444 us direct against
-// 377 us, and the 544-workgroup gate/up product are faster on the register path; the
-// 224-240 workgroup Q/K/V, O, down and K/V launches 14-16% faster direct).
+// keep more in flight than its one (measured: the 2374-tile LM head of 112 rows, 361 us
+// direct against 335 us per round with the non-temporal weight loads on both, 444 against
+// 377 before them, and the 544-workgroup gate/up product are faster on the register path;
+// the 224-240 workgroup Q/K/V, O, down and K/V launches 14-16% faster direct).
 #ifndef DFL_SK_DMA_MIN_MT
 #define DFL_SK_DMA_MIN_MT 5
 #endif
